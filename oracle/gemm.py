@@ -1,0 +1,145 @@
+"""Dense quantized-GEMM oracles (test infrastructure only).
+
+Each oracle is the definition written out: unpack the codes one nibble at a
+time, dequantise each weight exactly in float64, and form C = A . W_deq^T with
+a float64 matrix product.  No blocking, fusion or reordering beyond that.
+
+Sources.  Humming: open-source kernel library for quantized inference
+(news.ditty.ir), summary: weights, scales and zero points are described as
+separate parameters of one unified format, and the library covers WnA16 and
+W4A8 (including W4A8-MXFP4, where FP8 activations meet MXFP4 weights).
+cocoloop.cn (vi/fr), format section: MXFP4 is a supported weight format.
+The arithmetic of each format comes from its specification (formats.py).
+
+Readings where the pages are silent:
+
+* Dequantisation is w = (q - z) * s with the integer zero point subtracted
+  before scaling; group g covers k in [G*g, G*g + G) for every row n.
+* Scales and zero points are row-major [N, K/G], n-major like the codes.
+* A symmetric INT4 weight (fixed zero 8) stands for q - 8 in [-8, 7].
+* W4A8-INT: the int32 accumulator of one group is
+  P[m,n,g] = sum_{k in g} a_q[m,k] * (q[n,k] - 8), and
+  C = s_a[m] * sum_g s[n,g] * P[m,n,g].
+* W4A8-MXFP4: C = s_a[m] * sum_k e4m3(a_q[m,k]) * e2m1(q[n,k]) * 2^(E[n,k/32]-127).
+  The inner sum is a sum of multiples of 2^-18 below 2^21 in magnitude at
+  these sizes, so it is exact in float64 in any order.
+* Tolerance per output: tau = 1e-2 * (sum_k |a*w|) / K * sqrt(K), plus half
+  an output ulp (the rounding of the result to fp16/bf16 that every
+  implementation, this oracle included, must incur).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import e2m1_value, e4m3_value, e8m0_value, int8_value, rne, ulp, unpack_u4
+
+
+def dequant_int4(codes, scales, zeros, group: int = 128) -> np.ndarray:
+    """Exact float64 weights w[n,k] = (q[n,k] - z[n,k//G]) * s[n,k//G].
+
+    codes  int32 [N, K/8] (canonical packing)
+    scales float array-like [N, K/G] (the fp16/bf16 values, widened exactly)
+    zeros  None -> 8 (symmetric), an int -> that fixed zero, or an integer
+           array [N, K/G] of per-group zero points.
+    """
+    q = unpack_u4(codes).astype(np.int64)
+    N, K = q.shape
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    s = np.asarray(scales, dtype=np.float64)
+    if zeros is None:
+        z = np.full(s.shape, 8, dtype=np.int64)
+    elif np.isscalar(zeros):
+        z = np.full(s.shape, int(zeros), dtype=np.int64)
+    else:
+        z = np.asarray(zeros).astype(np.int64)
+    w = np.empty((N, K), dtype=np.float64)
+    for g in range(K // group):
+        ks = slice(g * group, (g + 1) * group)
+        w[:, ks] = (q[:, ks] - z[:, g : g + 1]) * s[:, g : g + 1]
+    return w
+
+
+def tolerance(a, w) -> np.ndarray:
+    """tau[m,n] = 1e-2 * (sum_k |a[m,k] w[n,k]|) / K * sqrt(K), in float64."""
+    a = np.asarray(a, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    K = a.shape[1]
+    return 1e-2 * (np.abs(a) @ np.abs(w).T) / K * np.sqrt(K)
+
+
+def check(c_gpu, c64, tau, out_fmt: str):
+    """Per-output pass mask: |c_gpu - c64| <= tau + ulp_out(max(|c_gpu|,|c64|))/2.
+
+    Returns (ok, literal_ok, err_over_tau).  ``literal_ok`` is the bare
+    |err| <= tau check, reported alongside.
+    """
+    c_gpu = np.asarray(c_gpu, dtype=np.float64)
+    err = np.abs(c_gpu - c64)
+    half = 0.5 * ulp(np.maximum(np.abs(c_gpu), np.abs(c64)), out_fmt)
+    ok = err <= tau + half
+    ok &= np.isfinite(c_gpu)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(tau > 0, err / tau, np.where(err == 0, 0.0, np.inf))
+    return ok, err <= tau, ratio
+
+
+def gemm_w4a16(a, codes, scales, zeros=None, group: int = 128, out_fmt: str = "f16"):
+    """Dense W4A16: C = A . ((q - z) * s)^T, float64 accumulate.
+
+    a  float array [M, K] holding the fp16/bf16 activation values exactly.
+    Returns dict(c64, c_out (rounded to out_fmt), tau).
+    """
+    a = np.asarray(a, dtype=np.float64)
+    w = dequant_int4(codes, scales, zeros, group)
+    c64 = a @ w.T
+    return {"c64": c64, "c_out": rne(c64, out_fmt), "tau": tolerance(a, w), "w": w}
+
+
+def mxfp4_weights(codes, e8m0, block: int = 32) -> np.ndarray:
+    """w[n,k] = e2m1(q[n,k]) * 2^(E[n, k//32] - 127), exact in float64."""
+    q = unpack_u4(codes)
+    N, K = q.shape
+    scale = e8m0_value(np.asarray(e8m0))
+    if scale.shape != (N, K // block):
+        raise ValueError("E8M0 scales must be [N, K/32]")
+    w = e2m1_value(q)
+    for b in range(K // block):
+        w[:, b * block : (b + 1) * block] *= scale[:, b : b + 1]
+    return w
+
+
+def gemm_mxfp4_fp8(a_codes, a_scale, w_codes, e8m0, out_fmt: str = "bf16"):
+    """W4A8-MXFP4: C[m,n] = s_a[m] * sum_k e4m3(a_q[m,k]) * w[n,k]."""
+    a = e4m3_value(np.asarray(a_codes))
+    sa = np.asarray(a_scale, dtype=np.float64)
+    w = mxfp4_weights(w_codes, e8m0)
+    inner = a @ w.T  # exact: see module docstring
+    c64 = sa[:, None] * inner
+    a_val = a * sa[:, None]
+    return {"c64": c64, "c_out": rne(c64, out_fmt), "tau": tolerance(a_val, w), "w": w}
+
+
+def int_accumulators(a_codes, w_codes, group: int = 128) -> np.ndarray:
+    """P[m,n,g] = sum_{k in g} a_q[m,k] * (q[n,k] - 8), exact int64."""
+    a = int8_value(np.asarray(a_codes)).astype(np.int64)
+    wq = unpack_u4(w_codes).astype(np.int64) - 8
+    M, K = a.shape
+    N = wq.shape[0]
+    G = K // group
+    P = np.zeros((M, N, G), dtype=np.int64)
+    for g in range(G):
+        ks = slice(g * group, (g + 1) * group)
+        P[:, :, g] = a[:, ks] @ wq[:, ks].T
+    return P
+
+
+def gemm_int4_int8(a_codes, a_scale, w_codes, scales, group: int = 128, out_fmt: str = "bf16"):
+    """W4A8-INT: exact per-group int accumulators, then the float epilogue."""
+    P = int_accumulators(a_codes, w_codes, group)
+    s = np.asarray(scales, dtype=np.float64)  # [N, G]
+    sa = np.asarray(a_scale, dtype=np.float64)
+    c64 = sa[:, None] * np.einsum("mng,ng->mn", P.astype(np.float64), s)
+    a_val = int8_value(np.asarray(a_codes)) * sa[:, None]
+    w = dequant_int4(w_codes, scales, 8, group)
+    return {"P": P, "c64": c64, "c_out": rne(c64, out_fmt), "tau": tolerance(a_val, w), "w": w}
