@@ -1,0 +1,283 @@
+"""Python binding of the MI355X quantized GEMM library (libhq.so).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/hq.h``.  PyTorch supplies the
+device memory (tensors) and the stream (the current HIP stream); there is no
+CPU fallback, and every entry point raises if the library is not built or a
+tensor is not on the GPU.
+
+Quick use::
+
+    import bit_quantized_gemm_repack_amd as hq
+    plan = hq.Plan(n=4096, k=4096, quant=hq.w4a16(act="bf16", zp="u4"), max_m=64)
+    w, meta = plan.repack(codes, scales, zeros)        # canonical -> device layout
+    out = plan.gemm(a, w, meta)                         # [m, n] bf16
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhq.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "hq.h")
+
+# ------------------------------------------------------------------ enums --
+HQ_OK, HQ_ERR_INVALID_ARG, HQ_ERR_UNSUPPORTED, HQ_ERR_WORKSPACE, HQ_ERR_HIP, HQ_ERR_INTERNAL = range(6)
+F16, BF16, F32, FP8_E4M3, INT8, U4, FP4_E2M1, E8M0, I32 = range(9)
+ZP_NONE, ZP_FIXED, ZP_PER_GROUP_U4 = range(3)
+ASCALE_NONE, ASCALE_PER_TOKEN_F32 = range(2)
+GEMM_DENSE, GEMM_GROUPED = range(2)
+EPI_NONE, EPI_SILU_MUL, EPI_SILU_MUL_QFP8, EPI_TOPK_COMBINE, EPI_I32_ACC = range(5)
+
+_DT = {"f16": F16, "bf16": BF16, "fp8": FP8_E4M3, "int8": INT8}
+_EPI = {"none": EPI_NONE, "silu_mul": EPI_SILU_MUL, "silu_mul_qfp8": EPI_SILU_MUL_QFP8,
+        "topk_combine": EPI_TOPK_COMBINE, "i32_acc": EPI_I32_ACC}
+
+
+class HQError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_status_name(status)}: {msg}")
+        self.status = status
+
+
+def _status_name(s: int) -> str:
+    names = ["HQ_OK", "HQ_ERR_INVALID_ARG", "HQ_ERR_UNSUPPORTED", "HQ_ERR_WORKSPACE", "HQ_ERR_HIP",
+             "HQ_ERR_INTERNAL"]
+    return names[s] if 0 <= s < len(names) else f"HQ_ERR_{s}"
+
+
+# ------------------------------------------------------------- structures --
+class QuantDesc(ctypes.Structure):
+    _fields_ = [("w_elem", ctypes.c_int), ("w_bits", ctypes.c_int), ("group_size", ctypes.c_int),
+                ("scale", ctypes.c_int), ("zp", ctypes.c_int), ("zp_value", ctypes.c_int),
+                ("act", ctypes.c_int), ("act_scale", ctypes.c_int), ("out", ctypes.c_int)]
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("k", ctypes.c_int64), ("num_experts", ctypes.c_int),
+                ("q", QuantDesc)]
+
+
+class Compute(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int), ("epi", ctypes.c_int)]
+
+
+class Tuning(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int), ("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int),
+                ("waves", ctypes.c_int), ("split_k", ctypes.c_int), ("stages", ctypes.c_int),
+                ("mfma", ctypes.c_int)]
+
+
+def w4a16(act: str = "f16", scale: Optional[str] = None, zp="fixed", zp_value: int = 8,
+          out: Optional[str] = None) -> QuantDesc:
+    """INT4 (group 128) weights x fp16/bf16 activations.  zp: 'fixed' or 'u4'."""
+    return QuantDesc(U4, 4, 128, _DT[scale or act], ZP_FIXED if zp == "fixed" else ZP_PER_GROUP_U4,
+                     zp_value, _DT[act], ASCALE_NONE, _DT[out or act])
+
+
+def w4a8_int(scale: str = "f16", out: str = "bf16") -> QuantDesc:
+    """INT4 (group 128, zero 8) weights x int8 per-token activations."""
+    return QuantDesc(U4, 4, 128, _DT[scale], ZP_FIXED, 8, INT8, ASCALE_PER_TOKEN_F32, _DT[out])
+
+
+def w4a8_fp8(scale: str = "f16", zp="fixed", zp_value: int = 8, out: str = "bf16") -> QuantDesc:
+    """INT4 (group 128) weights x fp8 e4m3 per-token activations."""
+    return QuantDesc(U4, 4, 128, _DT[scale], ZP_FIXED if zp == "fixed" else ZP_PER_GROUP_U4, zp_value,
+                     FP8_E4M3, ASCALE_PER_TOKEN_F32, _DT[out])
+
+
+def w4a8_mxfp4(out: str = "bf16") -> QuantDesc:
+    """MXFP4 (E2M1 + E8M0 per 32) weights x fp8 e4m3 per-token activations."""
+    return QuantDesc(FP4_E2M1, 4, 32, E8M0, ZP_NONE, 0, FP8_E4M3, ASCALE_PER_TOKEN_F32, _DT[out])
+
+
+# ---------------------------------------------------------------- library --
+_lib = None
+
+_SIGS = {
+    "hq_abi_version": (ctypes.c_int, []),
+    "hq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "hq_last_error": (ctypes.c_char_p, []),
+    "hq_plan_create": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTER(Compute), ctypes.c_int64,
+                                      ctypes.POINTER(Tuning), ctypes.POINTER(ctypes.c_void_p)]),
+    "hq_plan_destroy": (ctypes.c_int, [ctypes.c_void_p]),
+    "hq_plan_describe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_char_p, ctypes.c_size_t]),
+    "hq_plan_workspace_bytes": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64,
+                                               ctypes.POINTER(ctypes.c_size_t)]),
+    "hq_repacked_bytes": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t),
+                                         ctypes.POINTER(ctypes.c_size_t)]),
+    "hq_repack": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 5 + [ctypes.c_void_p]),
+    "hq_repack_host": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 5),
+    "hq_time_next_launch": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
+    "hq_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                               ctypes.c_size_t, ctypes.c_void_p]),
+}
+
+
+def lib():
+    """Load libhq.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def header_functions(path: str = HEADER_PATH):
+    """Names of the functions declared in include/hq.h."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*(hq_[a-z0-9_]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def _check(status: int):
+    if status != HQ_OK:
+        raise HQError(status, lib().hq_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream_ptr(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+_TORCH_OUT = {F16: torch.float16, BF16: torch.bfloat16}
+
+
+# ------------------------------------------------------------------ plan --
+class Plan:
+    """A layer description + execution choice (owns an hq_plan)."""
+
+    def __init__(self, n: int, k: int, quant: QuantDesc, max_m: int, epi: str = "none",
+                 kind: str = "dense", num_experts: int = 1, tuning: Optional[dict] = None):
+        L = lib()
+        self.n, self.k, self.max_m, self.num_experts = int(n), int(k), int(max_m), int(num_experts)
+        self.quant = quant
+        self.epi = _EPI[epi]
+        layer = LayerDesc(self.n, self.k, self.num_experts, quant)
+        comp = Compute(GEMM_DENSE if kind == "dense" else GEMM_GROUPED, self.epi)
+        tun = None
+        if tuning:
+            tun = Tuning(**{key: int(v) for key, v in tuning.items()})
+        handle = ctypes.c_void_p()
+        _check(L.hq_plan_create(ctypes.byref(layer), ctypes.byref(comp), self.max_m,
+                                ctypes.byref(tun) if tun is not None else None, ctypes.byref(handle)))
+        self._h = handle
+        self._ws = {}
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.hq_plan_destroy(h)
+            self._h = None
+
+    # -- sizes ----------------------------------------------------------
+    def repacked_bytes(self):
+        w, m = ctypes.c_size_t(), ctypes.c_size_t()
+        _check(lib().hq_repacked_bytes(self._h, ctypes.byref(w), ctypes.byref(m)))
+        return w.value, m.value
+
+    def workspace_bytes(self, m: int) -> int:
+        b = ctypes.c_size_t()
+        _check(lib().hq_plan_workspace_bytes(self._h, int(m), ctypes.byref(b)))
+        return b.value
+
+    def describe(self, m: int) -> str:
+        buf = ctypes.create_string_buffer(512)
+        _check(lib().hq_plan_describe(self._h, int(m), buf, 512))
+        return buf.value.decode()
+
+    def workspace(self, m: int, device) -> Optional[torch.Tensor]:
+        """A zero-initialised workspace kept per device (reused across calls;
+        the kernels leave it ready for the next call on the same stream)."""
+        need = self.workspace_bytes(m)
+        if need == 0:
+            return None
+        dev = torch.device(device)
+        ws = self._ws.get(dev)
+        if ws is None or ws.numel() < need:
+            ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+            self._ws[dev] = ws
+        return ws
+
+    # -- repack ---------------------------------------------------------
+    def _repack_outputs(self, device):
+        wb, mb = self.repacked_bytes()
+        w = torch.empty(wb, dtype=torch.uint8, device=device)
+        meta = torch.empty(max(mb, 16), dtype=torch.uint8, device=device)
+        return w, meta
+
+    def repack(self, codes: torch.Tensor, scales: Optional[torch.Tensor] = None,
+               zeros: Optional[torch.Tensor] = None, e8m0: Optional[torch.Tensor] = None):
+        """Canonical device tensors -> (w, meta) device-layout tensors (GPU kernel)."""
+        _dev(codes, "codes")
+        for t, nm in ((scales, "scales"), (zeros, "zeros"), (e8m0, "e8m0")):
+            if t is not None:
+                _dev(t, nm)
+        w, meta = self._repack_outputs(codes.device)
+        zx = e8m0 if e8m0 is not None else zeros
+        _check(lib().hq_repack(self._h, _ptr(codes), _ptr(scales), _ptr(zx), _ptr(w), _ptr(meta),
+                               _stream_ptr(codes.device)))
+        return w, meta
+
+    def repack_host(self, codes: torch.Tensor, scales: Optional[torch.Tensor] = None,
+                    zeros: Optional[torch.Tensor] = None, e8m0: Optional[torch.Tensor] = None):
+        """The same permutation on CPU tensors (offline preparation)."""
+        ts = [t.contiguous() if t is not None else None for t in (codes, scales, zeros, e8m0)]
+        for t in ts:
+            if t is not None and t.is_cuda:
+                raise ValueError("repack_host takes CPU tensors")
+        codes, scales, zeros, e8m0 = ts
+        w, meta = self._repack_outputs("cpu")
+        zx = e8m0 if e8m0 is not None else zeros
+        _check(lib().hq_repack_host(self._h, _ptr(codes), _ptr(scales), _ptr(zx), _ptr(w), _ptr(meta)))
+        return w, meta
+
+    # -- GEMM -----------------------------------------------------------
+    def gemm(self, a: torch.Tensor, w: torch.Tensor, meta: torch.Tensor, a_scale: Optional[torch.Tensor] = None,
+             out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """out[m, n] = A . W_deq^T (see include/hq.h, hq_gemm)."""
+        _dev(a, "a"), _dev(w, "w"), _dev(meta, "meta")
+        if a_scale is not None:
+            _dev(a_scale, "a_scale")
+            if a_scale.dtype != torch.float32:
+                raise ValueError("a_scale must be float32")
+        m = a.shape[0]
+        if a.dim() != 2 or a.shape[1] != self.k:
+            raise ValueError(f"a must be [m, {self.k}]")
+        if out is None:
+            if self.epi == EPI_I32_ACC:
+                out = torch.empty((m, self.n, self.k // 128), dtype=torch.int32, device=a.device)
+            else:
+                out = torch.empty((m, self.n), dtype=_TORCH_OUT[self.quant.out], device=a.device)
+        _dev(out, "out")
+        if ws is None:
+            ws = self.workspace(m, a.device)
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+        _check(lib().hq_gemm(self._h, m, _ptr(a), _ptr(a_scale), _ptr(w), _ptr(meta), _ptr(out), _ptr(ws),
+                             ws_bytes, _stream_ptr(a.device)))
+        return out

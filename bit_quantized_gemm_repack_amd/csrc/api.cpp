@@ -1,0 +1,415 @@
+// C ABI of the quantized GEMM library: descriptors, validation, the
+// execution-choice heuristic and kernel dispatch.
+//
+// The split between a quantisation description (what the bits mean) and an
+// execution choice (tile shape, pipeline depth, matrix instruction), chosen
+// by a rule-based heuristic that a caller may override, follows the Humming
+// page on news.ditty.ir (summary: layer / compute / tuning configs; the
+// heuristic is rule-based) and cocoloop.cn (limits section: tuning is
+// heuristic, not autotuned).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "hq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local hq::TimingEvents g_timing{nullptr, nullptr};
+
+hq_status fail(hq_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+hq_status fail(hq_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+hq_status ok() {
+  g_last_error.clear();
+  return HQ_OK;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Map a quantisation description to a kernel format, or fail.
+hq_status classify(const hq_quant_desc& q, int* fmt) {
+  if (q.w_bits != 4) return fail(HQ_ERR_UNSUPPORTED, "only 4-bit weights are implemented (w_bits=%d)", q.w_bits);
+  if (q.out != HQ_F16 && q.out != HQ_BF16)
+    return fail(HQ_ERR_UNSUPPORTED, "output dtype must be fp16 or bf16");
+  if (q.w_elem == HQ_U4) {
+    if (q.group_size != 128) return fail(HQ_ERR_UNSUPPORTED, "INT4 weights need group_size 128 (got %d)", q.group_size);
+    if (q.scale != HQ_F16 && q.scale != HQ_BF16)
+      return fail(HQ_ERR_UNSUPPORTED, "INT4 group scales must be fp16 or bf16");
+    if (q.zp == HQ_ZP_FIXED) {
+      if (q.zp_value < 0 || q.zp_value > 15) return fail(HQ_ERR_INVALID_ARG, "fixed zero point must be 0..15");
+    } else if (q.zp != HQ_ZP_PER_GROUP_U4) {
+      return fail(HQ_ERR_UNSUPPORTED, "INT4 weights need a fixed or per-group zero point");
+    }
+    switch (q.act) {
+      case HQ_F16:
+      case HQ_BF16:
+        if (q.act_scale != HQ_ASCALE_NONE) return fail(HQ_ERR_UNSUPPORTED, "16-bit activations take no scale");
+        *fmt = q.act == HQ_F16 ? hq::FMT_W16F16 : hq::FMT_W16BF16;
+        return HQ_OK;
+      case HQ_INT8:
+        if (q.act_scale != HQ_ASCALE_PER_TOKEN_F32)
+          return fail(HQ_ERR_UNSUPPORTED, "int8 activations need per-token fp32 scales");
+        if (q.zp != HQ_ZP_FIXED || q.zp_value != 8)
+          return fail(HQ_ERR_UNSUPPORTED, "INT4 x INT8 needs the symmetric zero point 8");
+        *fmt = hq::FMT_I8;
+        return HQ_OK;
+      case HQ_FP8_E4M3:
+        if (q.act_scale != HQ_ASCALE_PER_TOKEN_F32)
+          return fail(HQ_ERR_UNSUPPORTED, "fp8 activations need per-token fp32 scales");
+        *fmt = hq::FMT_Q8;
+        return HQ_OK;
+      default:
+        return fail(HQ_ERR_UNSUPPORTED, "unsupported activation dtype %d for INT4 weights", (int)q.act);
+    }
+  }
+  if (q.w_elem == HQ_FP4_E2M1) {
+    if (q.group_size != 32) return fail(HQ_ERR_UNSUPPORTED, "MXFP4 needs block size 32");
+    if (q.scale != HQ_E8M0) return fail(HQ_ERR_UNSUPPORTED, "MXFP4 needs E8M0 block scales");
+    if (q.zp != HQ_ZP_NONE) return fail(HQ_ERR_UNSUPPORTED, "MXFP4 has no zero point");
+    if (q.act != HQ_FP8_E4M3 || q.act_scale != HQ_ASCALE_PER_TOKEN_F32)
+      return fail(HQ_ERR_UNSUPPORTED, "MXFP4 weights are implemented with fp8 e4m3 per-token activations");
+    *fmt = hq::FMT_F4;
+    return HQ_OK;
+  }
+  return fail(HQ_ERR_UNSUPPORTED, "unsupported weight element type %d", (int)q.w_elem);
+}
+
+const char* fmt_name(int fmt) {
+  switch (fmt) {
+    case hq::FMT_W16F16: return "w4a16-f16";
+    case hq::FMT_W16BF16: return "w4a16-bf16";
+    case hq::FMT_I8: return "w4a8-int8";
+    case hq::FMT_Q8: return "w4a8-fp8";
+    case hq::FMT_F4: return "w4a8-mxfp4";
+  }
+  return "?";
+}
+
+bool valid_pow(int v) { return v == 1 || v == 2 || v == 4; }
+
+}  // namespace
+
+namespace hq {
+
+TimingEvents take_timing() {
+  TimingEvents t = g_timing;
+  g_timing = TimingEvents{nullptr, nullptr};
+  return t;
+}
+
+Exec choose_exec(const hq_plan* p, int64_t m) {
+  Exec e{};
+  e.kernel = KER_SKINNY;
+  const int64_t N = p->layer.n;
+  const int64_t G = p->layer.k / kFragK;
+  const hq_tuning& u = p->user;
+  SkinnyCfg c{};
+  c.mb = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
+  const bool act16 = p->fmt == FMT_W16F16 || p->fmt == FMT_W16BF16;
+  c.nb = (m > 4 && N % 32 == 0 && !(c.mb == 4 && act16)) ? 2 : 1;
+  c.waves = 4;
+  c.stages = 2;
+  if (u.tile_m) c.mb = u.tile_m / 16;
+  if (u.tile_n) c.nb = u.tile_n / 16;
+  if (u.waves) c.waves = u.waves;
+  if (u.stages) c.stages = u.stages;
+  const int64_t ntiles = N / (16 * c.nb);
+  const int64_t mch = cdiv(m > 0 ? m : 1, 16 * c.mb);
+  int64_t split = 1;
+  // enough workgroups to cover the chip twice, while every wave keeps work
+  while (ntiles * mch * split < 512 && G / (split * 2) >= 2 * c.waves) split *= 2;
+  if (u.split_k) split = u.split_k;
+  c.split = (int)split;
+  e.sk = c;
+  e.tiles_m = mch;
+  e.tiles_n = ntiles;
+  e.ws_counter_bytes = align256((size_t)(N / 16) * (size_t)cdiv(p->max_m > 0 ? p->max_m : 1, 16) * 4);
+  e.ws_bytes = 0;
+  if (c.split > 1 && p->compute.epi != HQ_EPI_I32_ACC)
+    e.ws_bytes = e.ws_counter_bytes + align256((size_t)c.split * (size_t)m * (size_t)N * 4);
+  return e;
+}
+
+}  // namespace hq
+
+namespace {
+
+hq_status check_exec(const hq_plan* p, const hq::Exec& e) {
+  const hq::SkinnyCfg& c = e.sk;
+  if (!valid_pow(c.mb)) return fail(HQ_ERR_INVALID_ARG, "tile_m must be 16, 32 or 64");
+  if (!valid_pow(c.nb)) return fail(HQ_ERR_INVALID_ARG, "tile_n must be 16, 32 or 64");
+  if (p->layer.n % (16 * c.nb)) return fail(HQ_ERR_INVALID_ARG, "N must be a multiple of tile_n");
+  if (c.waves < 1 || c.waves > 8) return fail(HQ_ERR_INVALID_ARG, "waves must be 1..8");
+  if (c.stages != 2 && c.stages != 4) return fail(HQ_ERR_INVALID_ARG, "stages must be 2 or 4");
+  if (c.split < 1 || c.split > 64) return fail(HQ_ERR_INVALID_ARG, "split_k must be 1..64");
+  if ((size_t)c.waves * c.mb * c.nb * 4 * 64 * 4 > 32768)
+    return fail(HQ_ERR_INVALID_ARG, "waves * tile_m * tile_n too large for the reduction buffer");
+  // register budget: these shapes would spill at two waves per SIMD
+  const bool act16 = p->fmt == hq::FMT_W16F16 || p->fmt == hq::FMT_W16BF16;
+  if (c.mb * c.nb * c.stages > 16 || c.mb * c.stages > 8 || (c.mb == 4 && c.nb == 2 && act16))
+    return fail(HQ_ERR_INVALID_ARG, "tile_m/tile_n/stages combination exceeds the register budget");
+  return HQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hq_abi_version(void) { return HQ_ABI_VERSION; }
+
+const char* hq_status_str(hq_status s) {
+  switch (s) {
+    case HQ_OK: return "HQ_OK";
+    case HQ_ERR_INVALID_ARG: return "HQ_ERR_INVALID_ARG";
+    case HQ_ERR_UNSUPPORTED: return "HQ_ERR_UNSUPPORTED";
+    case HQ_ERR_WORKSPACE: return "HQ_ERR_WORKSPACE";
+    case HQ_ERR_HIP: return "HQ_ERR_HIP";
+    case HQ_ERR_INTERNAL: return "HQ_ERR_INTERNAL";
+  }
+  return "HQ_ERR_UNKNOWN";
+}
+
+const char* hq_last_error(void) { return g_last_error.c_str(); }
+
+hq_status hq_time_next_launch(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(HQ_ERR_INVALID_ARG, "give both events or neither");
+  g_timing = hq::TimingEvents{start_event, stop_event};
+  return ok();
+}
+
+hq_status hq_plan_create(const hq_layer_desc* layer, const hq_compute* compute, int64_t max_m,
+                         const hq_tuning* tuning, hq_plan** out) {
+  try {
+    if (!layer || !compute || !out) return fail(HQ_ERR_INVALID_ARG, "null argument");
+    *out = nullptr;
+    if (layer->n <= 0 || layer->k <= 0) return fail(HQ_ERR_INVALID_ARG, "n and k must be positive");
+    if (layer->n % 16) return fail(HQ_ERR_UNSUPPORTED, "N must be a multiple of 16 (got %lld)", (long long)layer->n);
+    if (layer->k % 128) return fail(HQ_ERR_UNSUPPORTED, "K must be a multiple of 128 (got %lld)", (long long)layer->k);
+    if (layer->n > (1 << 24) || layer->k > (1 << 24)) return fail(HQ_ERR_UNSUPPORTED, "N or K too large");
+    if (max_m < 0 || max_m > (1 << 20)) return fail(HQ_ERR_INVALID_ARG, "max_m out of range");
+    if (layer->num_experts < 1) return fail(HQ_ERR_INVALID_ARG, "num_experts must be >= 1");
+    if (compute->kind != HQ_GEMM_DENSE && compute->kind != HQ_GEMM_GROUPED)
+      return fail(HQ_ERR_INVALID_ARG, "unknown GEMM kind");
+    if (compute->kind == HQ_GEMM_DENSE && layer->num_experts != 1)
+      return fail(HQ_ERR_INVALID_ARG, "a dense plan has exactly one expert");
+    int fmt = 0;
+    hq_status s = classify(layer->q, &fmt);
+    if (s != HQ_OK) return s;
+    switch (compute->epi) {
+      case HQ_EPI_NONE: break;
+      case HQ_EPI_I32_ACC:
+        if (fmt != hq::FMT_I8 || compute->kind != HQ_GEMM_DENSE)
+          return fail(HQ_ERR_UNSUPPORTED, "int32 accumulator output needs a dense INT4 x INT8 plan");
+        break;
+      case HQ_EPI_SILU_MUL:
+      case HQ_EPI_SILU_MUL_QFP8:
+      case HQ_EPI_TOPK_COMBINE:
+        return fail(HQ_ERR_UNSUPPORTED, "grouped epilogues are not available on dense plans");
+      default:
+        return fail(HQ_ERR_INVALID_ARG, "unknown epilogue");
+    }
+    if (compute->kind == HQ_GEMM_GROUPED) return fail(HQ_ERR_UNSUPPORTED, "grouped GEMM is not implemented yet");
+    hq_plan* p = new (std::nothrow) hq_plan();
+    if (!p) return fail(HQ_ERR_INTERNAL, "out of host memory");
+    p->layer = *layer;
+    p->compute = *compute;
+    p->max_m = max_m;
+    if (tuning) p->user = *tuning;
+    p->fmt = fmt;
+    const int64_t N = layer->n, K = layer->k, G = K / 128;
+    p->w_bytes_per_expert = (size_t)(N * K / 2);
+    if (fmt == hq::FMT_F4) {
+      p->scale_region_bytes = 0;
+      p->meta_bytes_per_expert = (size_t)(N * K / 32);
+    } else {
+      p->scale_region_bytes = (size_t)(N * G * 2);
+      p->meta_bytes_per_expert = p->scale_region_bytes;
+      if (layer->q.zp == HQ_ZP_PER_GROUP_U4) p->meta_bytes_per_expert += (size_t)((N / 16) * G * 8);
+    }
+    hq::Exec e = hq::choose_exec(p, max_m > 0 ? max_m : 1);
+    s = check_exec(p, e);
+    if (s != HQ_OK) {
+      delete p;
+      return s;
+    }
+    *out = p;
+    return ok();
+  } catch (...) {
+    return fail(HQ_ERR_INTERNAL, "exception in hq_plan_create");
+  }
+}
+
+hq_status hq_plan_destroy(hq_plan* plan) {
+  delete plan;
+  return ok();
+}
+
+hq_status hq_plan_describe(const hq_plan* p, int64_t m, char* buf, size_t len) {
+  if (!p || !buf || len == 0) return fail(HQ_ERR_INVALID_ARG, "null argument");
+  if (m < 1) m = 1;
+  hq::Exec e = hq::choose_exec(p, m);
+  snprintf(buf, len,
+           "kernel=skinny fmt=%s m=%lld n=%lld k=%lld tile_m=%d tile_n=%d waves=%d split_k=%d stages=%d "
+           "grid=%lldx%dx%lld ws=%zu",
+           fmt_name(p->fmt), (long long)m, (long long)p->layer.n, (long long)p->layer.k, 16 * e.sk.mb,
+           16 * e.sk.nb, e.sk.waves, e.sk.split, e.sk.stages, (long long)e.tiles_n, e.sk.split,
+           (long long)e.tiles_m, e.ws_bytes);
+  return ok();
+}
+
+hq_status hq_plan_workspace_bytes(const hq_plan* p, int64_t m, size_t* bytes) {
+  if (!p || !bytes) return fail(HQ_ERR_INVALID_ARG, "null argument");
+  if (m < 0 || m > p->max_m) return fail(HQ_ERR_INVALID_ARG, "m out of range [0, max_m]");
+  *bytes = m == 0 ? 0 : hq::choose_exec(p, m).ws_bytes;
+  return ok();
+}
+
+hq_status hq_repacked_bytes(const hq_plan* p, size_t* w_bytes, size_t* meta_bytes) {
+  if (!p || !w_bytes || !meta_bytes) return fail(HQ_ERR_INVALID_ARG, "null argument");
+  *w_bytes = p->w_bytes_per_expert * (size_t)p->layer.num_experts;
+  *meta_bytes = p->meta_bytes_per_expert * (size_t)p->layer.num_experts;
+  return ok();
+}
+
+static hq_status check_repack_args(const hq_plan* p, const void* codes, const void* scales, const void* zx,
+                                   const void* w_out, const void* meta_out) {
+  if (!p || !codes || !w_out || !meta_out) return fail(HQ_ERR_INVALID_ARG, "null argument");
+  if (p->fmt == hq::FMT_F4) {
+    if (!zx) return fail(HQ_ERR_INVALID_ARG, "MXFP4 repack needs the E8M0 scales");
+  } else {
+    if (!scales) return fail(HQ_ERR_INVALID_ARG, "INT4 repack needs the group scales");
+    if (p->layer.q.zp == HQ_ZP_PER_GROUP_U4 && !zx)
+      return fail(HQ_ERR_INVALID_ARG, "per-group zero points missing");
+  }
+  return HQ_OK;
+}
+
+hq_status hq_repack(const hq_plan* p, const void* codes, const void* scales, const void* zx, void* w_out,
+                    void* meta_out, void* stream) {
+  try {
+    hq_status s = check_repack_args(p, codes, scales, zx, w_out, meta_out);
+    if (s != HQ_OK) return s;
+    if (!aligned16(codes) || !aligned16(w_out) || !aligned16(meta_out))
+      return fail(HQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+    int err = hq::launch_repack(p, codes, scales, zx, w_out, meta_out, stream);
+    if (err != hipSuccess) return fail(HQ_ERR_HIP, "repack launch: %s", hipGetErrorString((hipError_t)err));
+    return ok();
+  } catch (...) {
+    return fail(HQ_ERR_INTERNAL, "exception in hq_repack");
+  }
+}
+
+hq_status hq_repack_host(const hq_plan* p, const void* codes, const void* scales, const void* zx, void* w_out,
+                         void* meta_out) {
+  try {
+    hq_status s = check_repack_args(p, codes, scales, zx, w_out, meta_out);
+    if (s != HQ_OK) return s;
+    const int64_t N = p->layer.n, K = p->layer.k, E = p->layer.num_experts, G = K / 128;
+    const int64_t wpe = N * K / 8;
+    const uint32_t* cw = static_cast<const uint32_t*>(codes);
+    uint32_t* wo = static_cast<uint32_t*>(w_out);
+    for (int64_t e = 0; e < E; ++e)
+      for (int64_t i = 0; i < wpe; ++i) wo[e * wpe + i] = hq::repack_word(cw + e * wpe, K, p->fmt, i);
+    uint8_t* meta = static_cast<uint8_t*>(meta_out);
+    if (p->fmt == hq::FMT_F4) {
+      const int64_t per = N * K / 32;
+      const uint8_t* src = static_cast<const uint8_t*>(zx);
+      for (int64_t e = 0; e < E; ++e)
+        for (int64_t i = 0; i < per; ++i) meta[e * per + i] = src[e * per + hq::e8m0_src_index(K, i)];
+      return ok();
+    }
+    const int64_t sper = N * G;
+    const uint16_t* ss = static_cast<const uint16_t*>(scales);
+    uint16_t* so = reinterpret_cast<uint16_t*>(meta);
+    for (int64_t e = 0; e < E; ++e)
+      for (int64_t i = 0; i < sper; ++i) so[e * sper + i] = ss[e * sper + hq::scale_src_index(G, i)];
+    if (p->layer.q.zp == HQ_ZP_PER_GROUP_U4) {
+      const int64_t zwpe = (N / 16) * G * 2;
+      const uint8_t* zs = static_cast<const uint8_t*>(zx);
+      uint32_t* zo = reinterpret_cast<uint32_t*>(meta + p->scale_region_bytes * E);
+      for (int64_t e = 0; e < E; ++e)
+        for (int64_t i = 0; i < zwpe; ++i) zo[e * zwpe + i] = hq::zeros_word(zs + e * N * G, G, i);
+    }
+    return ok();
+  } catch (...) {
+    return fail(HQ_ERR_INTERNAL, "exception in hq_repack_host");
+  }
+}
+
+hq_status hq_gemm(const hq_plan* p, int64_t m, const void* a, const float* a_scale, const void* w,
+                  const void* meta, void* out, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    if (!p) return fail(HQ_ERR_INVALID_ARG, "null plan");
+    if (p->compute.kind != HQ_GEMM_DENSE) return fail(HQ_ERR_INVALID_ARG, "hq_gemm needs a dense plan");
+    if (m < 0 || m > p->max_m) return fail(HQ_ERR_INVALID_ARG, "m=%lld out of range [0, %lld]", (long long)m,
+                                           (long long)p->max_m);
+    if (m == 0) return ok();
+    if (!a || !w || !meta || !out) return fail(HQ_ERR_INVALID_ARG, "null device pointer");
+    if (!aligned16(a) || !aligned16(w) || !aligned16(meta) || !aligned16(out))
+      return fail(HQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+    const bool act8 = p->fmt == hq::FMT_I8 || p->fmt == hq::FMT_Q8 || p->fmt == hq::FMT_F4;
+    if (act8 && !a_scale) return fail(HQ_ERR_INVALID_ARG, "8-bit activations need a_scale");
+    if (!act8 && a_scale) return fail(HQ_ERR_INVALID_ARG, "16-bit activations take no a_scale");
+    hq::Exec e = hq::choose_exec(p, m);
+    hq_status s = check_exec(p, e);
+    if (s != HQ_OK) return s;
+    if (e.ws_bytes > 0) {
+      if (!ws) return fail(HQ_ERR_WORKSPACE, "this call needs %zu workspace bytes", e.ws_bytes);
+      if (ws_bytes < e.ws_bytes)
+        return fail(HQ_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, e.ws_bytes);
+      if (!aligned16(ws)) return fail(HQ_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    }
+    const int64_t N = p->layer.n, K = p->layer.k, G = K / 128;
+    if (m * K > (int64_t(1) << 40)) return fail(HQ_ERR_UNSUPPORTED, "problem too large");
+    hq::SkinnyArgs args{};
+    args.a = a;
+    args.a_scale = a_scale;
+    args.w = w;
+    if (p->fmt == hq::FMT_F4) {
+      args.e8m0 = static_cast<const uint8_t*>(meta);
+    } else {
+      args.scales = meta;
+      if (p->layer.q.zp == HQ_ZP_PER_GROUP_U4)
+        args.zeros = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(meta) + p->scale_region_bytes);
+    }
+    args.out = out;
+    if (e.ws_bytes > 0) {
+      args.counter = static_cast<uint32_t*>(ws);
+      args.part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + e.ws_counter_bytes);
+    }
+    args.M = (int)m;
+    args.N = (int)N;
+    args.K = (int)K;
+    args.G = (int)G;
+    args.zp_fixed = p->layer.q.zp == HQ_ZP_FIXED ? p->layer.q.zp_value : -1;
+    args.scale_bf16 = p->layer.q.scale == HQ_BF16;
+    args.out_bf16 = p->layer.q.out == HQ_BF16;
+    args.i32_out = p->compute.epi == HQ_EPI_I32_ACC;
+    args.gps = (int)cdiv(G, e.sk.split);
+    int err = hq::launch_skinny(p->fmt, e.sk, args, stream);
+    if (err != hipSuccess) return fail(HQ_ERR_HIP, "gemm launch: %s", hipGetErrorString((hipError_t)err));
+    return ok();
+  } catch (...) {
+    return fail(HQ_ERR_INTERNAL, "exception in hq_gemm");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,205 @@
+// Internal definitions shared by the host library and the gfx950 kernels.
+//
+// Device weight layout ("fragment" layout)
+// ----------------------------------------
+// The weight [N, K] is cut into fragments of 16 columns (n) x 128 k.  One
+// fragment is exactly what one wavefront consumes with a single 16-byte load
+// per lane: 64 lanes x 16 B = 1 KiB = 16 x 128 4-bit codes.  Fragments are
+// stored n-block major: fragment (nb, g) sits at byte ((nb * K/128) + g) * 1024,
+// so one wave walking along K reads one contiguous stream.
+//
+// Lane l of a fragment holds column c = l % 16 and the 32 consecutive k of
+// its quarter kq = l / 16:  k in [128 g + 32 kq, 128 g + 32 kq + 32).  The
+// activation operand of every MFMA used here takes row m = l % 16 and the
+// same k range in lane l, so a lane's A data is one contiguous run of the
+// activation row.  Inside the lane's four 32-bit words (word t covers the
+// 8 k at 32 kq + 8 t), the order of the 8 nibbles depends on the matrix
+// instruction that will consume them, so that one mask (plus one shift)
+// yields a ready operand register:
+//
+//   NIB_W16  (fp16 / bf16 MFMA 16x16x32): nibble p holds k-offset
+//            {0,2,4,6,1,3,5,7}[p]; (w >> 4r) & 0x000F000F puts the codes of
+//            k-offsets 2r and 2r+1 in the two 16-bit halves.
+//   NIB_B8   (8-bit operands: int8 MFMA 16x16x64, fp8 scaled MFMA): byte b
+//            of the word holds k-offset b in its low nibble and b+4 in its
+//            high nibble, so w & 0x0F0F0F0F / (w >> 4) & 0x0F0F0F0F (or the
+//            0xF0F0F0F0 forms) give four consecutive k as four bytes.
+//   NIB_NAT  (MXFP4, fp4 operand of the scaled MFMA): nibble p holds
+//            k-offset p, the operand order of E2M1 data.
+//
+// For the int8 MFMA the stored nibble is q ^ 8, the two's-complement int4 of
+// q - 8: placed in the high half of a byte it reads as the int8 16 * (q - 8).
+//
+// Scales, zero points, E8M0: per (n-block, group) records in the order the
+// lanes read them: scales [N/16][K/128][16] (2 B each), zero points as
+// nibbles [N/16][K/128][16 x 4 bit] (8 B), E8M0 [N/16][K/128][64 lanes].
+// A grouped (MoE) weight is E such layouts one after the other.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/hq.h"
+
+#if defined(__HIPCC__)
+#define HQ_HD __host__ __device__
+#else
+#define HQ_HD
+#endif
+
+namespace hq {
+
+constexpr int kFragN = 16;
+constexpr int kFragK = 128;
+constexpr int kFragBytes = 1024;
+
+// Kernel-side format of the weight x activation pair.
+enum Fmt : int {
+  FMT_W16F16 = 0,  // INT4 weight, fp16 activation, fp16 MFMA
+  FMT_W16BF16 = 1, // INT4 weight, bf16 activation, bf16 MFMA
+  FMT_I8 = 2,      // INT4 weight, int8 activation, int8 MFMA (exact int32)
+  FMT_Q8 = 3,      // INT4 weight, fp8 activation, scaled fp8 MFMA
+  FMT_F4 = 4       // MXFP4 weight, fp8 activation, scaled fp8 x fp4 MFMA
+};
+
+enum NibOrder : int { NIB_W16 = 0, NIB_B8 = 1, NIB_NAT = 2 };
+
+HQ_HD inline int nib_order_of(int fmt) {
+  return (fmt == FMT_W16F16 || fmt == FMT_W16BF16) ? NIB_W16 : (fmt == FMT_F4 ? NIB_NAT : NIB_B8);
+}
+HQ_HD inline uint32_t nib_xor_of(int fmt) { return fmt == FMT_I8 ? 8u : 0u; }
+
+// k-offset (0..7, within the 8 k of one word) held by nibble p.
+HQ_HD inline int nib_koff(int order, int p) {
+  if (order == NIB_W16) return (p < 4) ? 2 * p : 2 * (p - 4) + 1;
+  if (order == NIB_B8) return (p & 1) ? 4 + (p >> 1) : (p >> 1);
+  return p;
+}
+
+// Canonical 4-bit code (n, k) of a row-major int32 [N, K/8] code matrix.
+HQ_HD inline uint32_t canon_code(const uint32_t* codes, int64_t K, int64_t n, int64_t k) {
+  return (codes[n * (K / 8) + (k >> 3)] >> (4 * (k & 7))) & 0xFu;
+}
+
+// One 32-bit word of the device layout: word index widx counts 32-bit words
+// from the start of one expert's code region.
+HQ_HD inline uint32_t repack_word(const uint32_t* codes, int64_t K, int fmt, int64_t widx) {
+  const int64_t G = K / kFragK;
+  const int t = (int)(widx & 3);
+  const int lane = (int)((widx >> 2) & 63);
+  const int64_t frag = widx >> 8;
+  const int64_t g = frag % G;
+  const int64_t nb = frag / G;
+  const int64_t n = nb * kFragN + (lane & 15);
+  const int64_t kbase = g * kFragK + 32 * (lane >> 4) + 8 * t;
+  const int order = nib_order_of(fmt);
+  const uint32_t x = nib_xor_of(fmt);
+  uint32_t w = 0;
+  for (int p = 0; p < 8; ++p) w |= (canon_code(codes, K, n, kbase + nib_koff(order, p)) ^ x) << (4 * p);
+  return w;
+}
+
+// Element eidx of the scale region [N/16][G][16] <- canonical [N][G].
+HQ_HD inline int64_t scale_src_index(int64_t G, int64_t eidx) {
+  const int64_t c = eidx & 15;
+  const int64_t g = (eidx >> 4) % G;
+  const int64_t nb = (eidx >> 4) / G;
+  return (nb * kFragN + c) * G + g;
+}
+
+// 32-bit word widx of the zero-point region [N/16][G][2 words] (16 nibbles,
+// column c at bits 4*(c%8) of word c/8) <- canonical uint8 [N][G].
+HQ_HD inline uint32_t zeros_word(const uint8_t* zeros, int64_t G, int64_t widx) {
+  const int half = (int)(widx & 1);
+  const int64_t g = (widx >> 1) % G;
+  const int64_t nb = (widx >> 1) / G;
+  uint32_t w = 0;
+  for (int i = 0; i < 8; ++i) {
+    const int64_t n = nb * kFragN + half * 8 + i;
+    w |= (uint32_t)(zeros[n * G + g] & 0xF) << (4 * i);
+  }
+  return w;
+}
+
+// Byte eidx of the E8M0 region [N/16][G][64 lanes] <- canonical [N][K/32].
+HQ_HD inline int64_t e8m0_src_index(int64_t K, int64_t eidx) {
+  const int64_t G = K / kFragK;
+  const int lane = (int)(eidx & 63);
+  const int64_t g = (eidx >> 6) % G;
+  const int64_t nb = (eidx >> 6) / G;
+  const int64_t n = nb * kFragN + (lane & 15);
+  return n * (K / 32) + 4 * g + (lane >> 4);
+}
+
+// ---------------------------------------------------------------------------
+// Plan
+// ---------------------------------------------------------------------------
+
+enum KernelKind : int { KER_SKINNY = 1, KER_TILED = 2 };
+
+struct SkinnyCfg {
+  int mb;      // 16-row blocks per workgroup (1, 2, 4)
+  int nb;      // 16-column blocks per workgroup (1, 2, 4)
+  int waves;   // wavefronts per workgroup (split K inside the workgroup)
+  int split;   // workgroups along K (1 = no cross-workgroup reduction)
+  int stages;  // groups in flight per wave
+};
+
+}  // namespace hq
+
+struct hq_plan {
+  hq_layer_desc layer;
+  hq_compute compute;
+  int64_t max_m;
+  hq_tuning user;  // user overrides (zero = auto)
+  int fmt;         // hq::Fmt
+  size_t w_bytes_per_expert;
+  size_t meta_bytes_per_expert;
+  size_t scale_region_bytes;  // per expert, before the zero / e8m0 region
+};
+
+namespace hq {
+
+// Resolved execution choice for one call with m rows.
+struct Exec {
+  int kernel;
+  SkinnyCfg sk;
+  int64_t tiles_m, tiles_n;
+  size_t ws_bytes;  // total workspace
+  size_t ws_counter_bytes;
+};
+
+Exec choose_exec(const hq_plan* p, int64_t m);
+
+// Kernel launchers (defined in the .hip files).  Return a hipError_t as int.
+struct SkinnyArgs {
+  const void* a;
+  const float* a_scale;
+  const void* w;
+  const void* scales;
+  const uint32_t* zeros;  // nibble-packed, or null
+  const uint8_t* e8m0;
+  void* out;
+  float* part;       // [split][M][N] fp32 partials (split > 1)
+  uint32_t* counter; // one per output tile (split > 1)
+  int M, N, K, G;
+  int zp_fixed;      // fixed zero point, or -1 for per-group zeros
+  int scale_bf16;    // scale dtype: 1 bf16, 0 fp16
+  int out_bf16;      // output dtype: 1 bf16, 0 fp16
+  int i32_out;       // write per-group int32 accumulators instead of C
+  int gps;           // groups per split
+};
+
+int launch_skinny(int fmt, const SkinnyCfg& cfg, const SkinnyArgs& a, void* stream);
+
+// Pending timing events for the next launch on this thread (see
+// hq_time_next_launch); take_timing() returns and clears them.
+struct TimingEvents {
+  void* start;
+  void* stop;
+};
+TimingEvents take_timing();
+int launch_repack(const hq_plan* p, const void* codes, const void* scales, const void* zx,
+                  void* w_out, void* meta_out, void* stream);
+
+}  // namespace hq

@@ -1,0 +1,405 @@
+// Small-M quantized GEMM for gfx950 ("skinny" kernel): the weight-bandwidth
+// bound regime (decode, M <= 64 per launch slice).
+//
+// Operation (Humming page on news.ditty.ir, summary: weights, scales and zero
+// points are separate parameters; W4A16 and W4A8 including MXFP4 x FP8):
+//   C[m,n] = s_a[m] * sum_g s[n,g] * sum_{k in g} a[m,k] * (q[n,k] - z[n,g])
+// or, for MXFP4, C[m,n] = s_a[m] * sum_k a[m,k] * e2m1(q[n,k]) * 2^(X[n,k/32]-127).
+//
+// Work decomposition
+//   * A workgroup owns NB blocks of 16 output columns and MB blocks of 16 rows
+//     and a contiguous range of 128-k groups (its split).  Its W wavefronts
+//     take the groups of that range round-robin, so at any time the waves of a
+//     workgroup stream neighbouring 1 KiB weight fragments.
+//   * Weights go straight from HBM to registers with one 16-byte load per
+//     lane per fragment (fully coalesced, no LDS: no other wave needs them).
+//     Each wave keeps STAGES groups of loads in flight ahead of its math.
+//   * Activations are read per lane as one contiguous 32 / 64-byte run of a
+//     row (L2 / L1 resident; rows beyond M are clamped, their results dropped).
+//   * Per group the 4-bit codes become MFMA operands with one mask (+ one
+//     shift) per register and no float arithmetic: the MFMA sees the exact
+//     integers (OFF + q) (16-bit formats: OFF = 1024 for fp16, 128 for bf16),
+//     q (fp8, via the e4m3 codes 0x00..0x0F = q * 2^-9, undone by the MFMA's
+//     block scale 2^9) or 16 (q - 8) (int8).  The zero point and the offset
+//     are removed with the row sums of A over the group, obtained from one
+//     extra MFMA chain against a ones operand (shared by all column blocks):
+//       acc += s[n,g] * (P[m,n,g] - (OFF + z[n,g]) * rowsum_g(a[m, :]))
+//     so the group scale is applied once per output in fp32 and the weights
+//     are never rounded.  MXFP4 needs no conversion at all: its codes and
+//     E8M0 scales feed the scaled MFMA directly.
+//   * The W partial accumulators are summed in LDS in a fixed order; with a
+//     split > 1 every workgroup stores its fp32 partial tile, and the last one
+//     to arrive (device-scope counter) sums the splits in index order and
+//     writes the output, then re-arms the counter.  Results are therefore
+//     deterministic run to run.
+#include <hip/hip_ext.h>
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "hq_internal.h"
+
+namespace hq {
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef int i4_t __attribute__((ext_vector_type(4)));
+typedef int i8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+
+__device__ inline float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ inline float f16_bits_to_float(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+// Round-to-nearest-even fp32 -> bf16 bits (NaN kept quiet).
+__device__ inline uint16_t float_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ inline uint16_t float_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);  // RNE conversion
+}
+
+template <int FMT>
+struct FmtInfo {
+  static constexpr bool kAct16 = (FMT == FMT_W16F16 || FMT == FMT_W16BF16);
+  static constexpr int kAVec = kAct16 ? 4 : 2;  // 16-byte loads per lane per group
+  static constexpr bool kRowSum = (FMT == FMT_W16F16 || FMT == FMT_W16BF16 || FMT == FMT_Q8);
+  static constexpr bool kActScale = !kAct16;
+};
+
+template <int FMT, int MB, int NB>
+struct Stage {
+  u4_t a[MB][FmtInfo<FMT>::kAVec];
+  u4_t b[NB];
+  uint32_t meta[NB];
+};
+
+template <int FMT>
+__device__ inline f4_t mfma16(u4_t a, u4_t b, f4_t c) {
+  if constexpr (FMT == FMT_W16F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, a),
+                                                  __builtin_bit_cast(h8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8_t, a),
+                                                   __builtin_bit_cast(b8_t, b), c, 0, 0, 0);
+}
+
+__device__ inline i8_t cat8(u4_t x, u4_t y) {
+  i8_t r;
+  r[0] = x[0]; r[1] = x[1]; r[2] = x[2]; r[3] = x[3];
+  r[4] = y[0]; r[5] = y[1]; r[6] = y[2]; r[7] = y[3];
+  return r;
+}
+
+template <int FMT, int MB, int NB, int STAGES>
+__global__ void __launch_bounds__(512) qgemm_skinny(SkinnyArgs p) {
+  using FI = FmtInfo<FMT>;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int W = blockDim.x >> 6;
+  const int c = lane & 15;
+  const int kq = lane >> 4;
+  const int nt = blockIdx.x;
+  const int split = blockIdx.y;
+  const int m0 = blockIdx.z * 16 * MB;
+  const int G = p.G;
+  const int K = p.K;
+
+  const int g_beg = split * p.gps;
+  const int g_end = min(G, g_beg + p.gps);
+  const int my_first = g_beg + wave;
+  const int n_it = (my_first < g_end) ? (g_end - my_first + W - 1) / W : 0;
+
+  // Row each lane loads for each m-block (clamped into [0, M)).
+  int arow[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) arow[mb] = min(m0 + 16 * mb + c, p.M - 1);
+
+  const u4_t* wfr = reinterpret_cast<const u4_t*>(p.w);
+
+  auto load = [&](Stage<FMT, MB, NB>& st, int g) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int64_t frag = (int64_t)(nt * NB + nb) * G + g;
+      st.b[nb] = __builtin_nontemporal_load(wfr + frag * 64 + lane);
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      if constexpr (FI::kAct16) {
+        const u4_t* ap = reinterpret_cast<const u4_t*>(
+            static_cast<const uint16_t*>(p.a) + (int64_t)arow[mb] * K + g * 128 + 32 * kq);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) st.a[mb][v] = ap[v];
+      } else {
+        const u4_t* ap = reinterpret_cast<const u4_t*>(
+            static_cast<const uint8_t*>(p.a) + (int64_t)arow[mb] * K + g * 128 + 32 * kq);
+        st.a[mb][0] = ap[0];
+        st.a[mb][1] = ap[1];
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int64_t rec = (int64_t)(nt * NB + nb) * G + g;
+      if constexpr (FMT == FMT_F4) {
+        st.meta[nb] = p.e8m0[rec * 64 + lane];
+      } else {
+        uint32_t s = static_cast<const uint16_t*>(p.scales)[rec * 16 + c];
+        uint32_t z = (uint32_t)p.zp_fixed;
+        if (p.zp_fixed < 0) z = (p.zeros[rec * 2 + (c >> 3)] >> (4 * (c & 7))) & 0xFu;
+        st.meta[nb] = s | (z << 16);
+      }
+    }
+  };
+
+  f4_t acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const Stage<FMT, MB, NB>& st, int g) {
+    [[maybe_unused]] f4_t rs[MB];
+    if constexpr (FMT == FMT_W16F16 || FMT == FMT_W16BF16) {
+      const uint32_t one2 = (FMT == FMT_W16F16) ? 0x3C003C00u : 0x3F803F80u;
+      const u4_t ones = u4_t{one2, one2, one2, one2};
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        rs[mb] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) rs[mb] = mfma16<FMT>(st.a[mb][t], ones, rs[mb]);
+      }
+    } else if constexpr (FMT == FMT_Q8) {
+      const i8_t ones = i8_t{0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                             0x38383838, 0x38383838, 0x38383838, 0x38383838};
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        rs[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            cat8(st.a[mb][0], st.a[mb][1]), ones, f4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+    }
+
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const u4_t w = st.b[nb];
+      if constexpr (FMT == FMT_W16F16 || FMT == FMT_W16BF16) {
+        const uint32_t magic = (FMT == FMT_W16F16) ? 0x64006400u : 0x43004300u;
+        const float off = (FMT == FMT_W16F16) ? 1024.f : 128.f;
+        f4_t P[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) P[mb] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t x = w[t];
+          const u4_t bop = u4_t{(x & 0x000F000Fu) | magic, ((x >> 4) & 0x000F000Fu) | magic,
+                                ((x >> 8) & 0x000F000Fu) | magic, ((x >> 12) & 0x000F000Fu) | magic};
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) P[mb] = mfma16<FMT>(st.a[mb][t], bop, P[mb]);
+        }
+        const uint32_t meta = st.meta[nb];
+        const float s = p.scale_bf16 ? bf16_bits_to_float(meta & 0xFFFFu) : f16_bits_to_float(meta & 0xFFFFu);
+        const float cz = off + (float)(meta >> 16);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[mb][nb][r] += s * (P[mb][r] - cz * rs[mb][r]);
+      } else if constexpr (FMT == FMT_I8) {
+        const i4_t b0 = i4_t{(int)((w[0] << 4) & 0xF0F0F0F0u), (int)(w[0] & 0xF0F0F0F0u),
+                             (int)((w[1] << 4) & 0xF0F0F0F0u), (int)(w[1] & 0xF0F0F0F0u)};
+        const i4_t b1 = i4_t{(int)((w[2] << 4) & 0xF0F0F0F0u), (int)(w[2] & 0xF0F0F0F0u),
+                             (int)((w[3] << 4) & 0xF0F0F0F0u), (int)(w[3] & 0xF0F0F0F0u)};
+        const uint32_t meta = st.meta[nb];
+        const float s16 = 0.0625f * (p.scale_bf16 ? bf16_bits_to_float(meta & 0xFFFFu)
+                                                  : f16_bits_to_float(meta & 0xFFFFu));
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          i4_t P = i4_t{0, 0, 0, 0};
+          P = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i4_t, st.a[mb][0]), b0, P, 0, 0, 0);
+          P = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i4_t, st.a[mb][1]), b1, P, 0, 0, 0);
+          if (p.i32_out) {
+            const int n = (nt * NB + nb) * 16 + c;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int m = m0 + 16 * mb + 4 * kq + r;
+              if (m < p.M) static_cast<int32_t*>(p.out)[((int64_t)m * p.N + n) * G + g] = P[r] >> 4;
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[mb][nb][r] += s16 * (float)P[r];
+        }
+      } else if constexpr (FMT == FMT_Q8) {
+        const i8_t bop = i8_t{(int)(w[0] & 0x0F0F0F0Fu), (int)((w[0] >> 4) & 0x0F0F0F0Fu),
+                              (int)(w[1] & 0x0F0F0F0Fu), (int)((w[1] >> 4) & 0x0F0F0F0Fu),
+                              (int)(w[2] & 0x0F0F0F0Fu), (int)((w[2] >> 4) & 0x0F0F0F0Fu),
+                              (int)(w[3] & 0x0F0F0F0Fu), (int)((w[3] >> 4) & 0x0F0F0F0Fu)};
+        const uint32_t meta = st.meta[nb];
+        const float s = p.scale_bf16 ? bf16_bits_to_float(meta & 0xFFFFu) : f16_bits_to_float(meta & 0xFFFFu);
+        const float z = (float)(meta >> 16);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          // codes 0x00..0x0F are q * 2^-9 in e4m3; block scale 2^9 (E8M0 136) undoes it
+          const f4_t P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              cat8(st.a[mb][0], st.a[mb][1]), bop, f4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 136);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[mb][nb][r] += s * (P[r] - z * rs[mb][r]);
+        }
+      } else {  // FMT_F4
+        const i8_t bop = i8_t{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+        const int sb = (int)st.meta[nb];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              cat8(st.a[mb][0], st.a[mb][1]), bop, acc[mb][nb], 0, 4, 0, 127, 0, sb);
+      }
+    }
+    (void)g;
+  };
+
+  // Software pipeline: STAGES groups of loads in flight ahead of the math.
+  Stage<FMT, MB, NB> st[STAGES];
+#pragma unroll
+  for (int d = 0; d < STAGES; ++d)
+    if (d < n_it) load(st[d], my_first + d * W);
+  for (int i = 0; i < n_it; i += STAGES) {
+#pragma unroll
+    for (int d = 0; d < STAGES; ++d) {
+      if (i + d < n_it) {
+        const int g = my_first + (i + d) * W;
+        compute(st[d], g);
+        if (i + d + STAGES < n_it) load(st[d], g + STAGES * W);
+      }
+    }
+  }
+
+  if (p.i32_out) return;  // per-group accumulators already written
+
+  // ---- reduce the W partial accumulators of this workgroup (fixed order) ----
+  constexpr int E = MB * NB * 4;
+  extern __shared__ float red[];  // [W][E][64]
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[(wave * E + (mb * NB + nb) * 4 + r) * 64 + lane] = acc[mb][nb][r];
+  __syncthreads();
+
+  const int S = gridDim.y;
+  const int nthreads = blockDim.x;
+  for (int e = threadIdx.x; e < E * 64; e += nthreads) {
+    float v = 0.f;
+    for (int w = 0; w < W; ++w) v += red[w * E * 64 + e];
+    const int l = e & 63;
+    const int idx = e >> 6;
+    const int r = idx & 3;
+    const int nb = (idx >> 2) % NB;
+    const int mb = (idx >> 2) / NB;
+    const int m = m0 + 16 * mb + 4 * (l >> 4) + r;
+    const int n = (nt * NB + nb) * 16 + (l & 15);
+    if (m >= p.M) continue;
+    if (S == 1) {
+      if (FI::kActScale) v *= p.a_scale[m];
+      const uint16_t o = p.out_bf16 ? float_to_bf16_bits(v) : float_to_f16_bits(v);
+      static_cast<uint16_t*>(p.out)[(int64_t)m * p.N + n] = o;
+    } else {
+      p.part[((int64_t)split * p.M + m) * p.N + n] = v;
+    }
+  }
+  if (S == 1) return;
+
+  // ---- cross-workgroup split-K: the last workgroup to arrive finishes ----
+  __shared__ int is_last;
+  __threadfence();
+  __syncthreads();
+  const int tile = blockIdx.z * gridDim.x + nt;
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(p.counter + tile, 1u, __ATOMIC_ACQ_REL,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    is_last = (old == (uint32_t)(S - 1));
+  }
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+  for (int e = threadIdx.x; e < E * 64; e += nthreads) {
+    const int l = e & 63;
+    const int idx = e >> 6;
+    const int r = idx & 3;
+    const int nb = (idx >> 2) % NB;
+    const int mb = (idx >> 2) / NB;
+    const int m = m0 + 16 * mb + 4 * (l >> 4) + r;
+    const int n = (nt * NB + nb) * 16 + (l & 15);
+    if (m >= p.M) continue;
+    float v = 0.f;
+    for (int s = 0; s < S; ++s) v += __builtin_nontemporal_load(p.part + ((int64_t)s * p.M + m) * p.N + n);
+    if (FI::kActScale) v *= p.a_scale[m];
+    const uint16_t o = p.out_bf16 ? float_to_bf16_bits(v) : float_to_f16_bits(v);
+    static_cast<uint16_t*>(p.out)[(int64_t)m * p.N + n] = o;
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(p.counter + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// dispatch
+// ---------------------------------------------------------------------------
+
+template <typename Kern>
+static hipError_t launch_kernel(Kern kern, dim3 grid, dim3 block, size_t lds, hipStream_t s, const SkinnyArgs& a) {
+  const TimingEvents ev = take_timing();
+  if (ev.start) {
+    hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)lds, s, static_cast<hipEvent_t>(ev.start),
+                          static_cast<hipEvent_t>(ev.stop), 0, a);
+  } else {
+    hipLaunchKernelGGL(kern, grid, block, lds, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <int FMT, int MB, int NB>
+static hipError_t launch_t(const SkinnyCfg& cfg, const SkinnyArgs& a, dim3 grid, dim3 block, size_t lds,
+                           hipStream_t s) {
+  if (cfg.stages <= 2) return launch_kernel(qgemm_skinny<FMT, MB, NB, 2>, grid, block, lds, s, a);
+  return launch_kernel(qgemm_skinny<FMT, MB, NB, 4>, grid, block, lds, s, a);
+}
+
+template <int FMT, int MB>
+static hipError_t launch_nb(const SkinnyCfg& cfg, const SkinnyArgs& a, dim3 grid, dim3 block, size_t lds,
+                            hipStream_t s) {
+  switch (cfg.nb) {
+    case 1: return launch_t<FMT, MB, 1>(cfg, a, grid, block, lds, s);
+    case 2: return launch_t<FMT, MB, 2>(cfg, a, grid, block, lds, s);
+    case 4: return launch_t<FMT, MB, 4>(cfg, a, grid, block, lds, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int FMT>
+static hipError_t launch_mb(const SkinnyCfg& cfg, const SkinnyArgs& a, dim3 grid, dim3 block, size_t lds,
+                            hipStream_t s) {
+  switch (cfg.mb) {
+    case 1: return launch_nb<FMT, 1>(cfg, a, grid, block, lds, s);
+    case 2: return launch_nb<FMT, 2>(cfg, a, grid, block, lds, s);
+    case 4: return launch_nb<FMT, 4>(cfg, a, grid, block, lds, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+int launch_skinny(int fmt, const SkinnyCfg& cfg, const SkinnyArgs& a, void* stream) {
+  const int ntiles = a.N / (16 * cfg.nb);
+  const int mchunks = (a.M + 16 * cfg.mb - 1) / (16 * cfg.mb);
+  dim3 grid(ntiles, cfg.split, mchunks);
+  dim3 block(64 * cfg.waves);
+  const size_t lds = (size_t)cfg.waves * cfg.mb * cfg.nb * 4 * 64 * sizeof(float);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (fmt) {
+    case FMT_W16F16: return (int)launch_mb<FMT_W16F16>(cfg, a, grid, block, lds, s);
+    case FMT_W16BF16: return (int)launch_mb<FMT_W16BF16>(cfg, a, grid, block, lds, s);
+    case FMT_I8: return (int)launch_mb<FMT_I8>(cfg, a, grid, block, lds, s);
+    case FMT_Q8: return (int)launch_mb<FMT_Q8>(cfg, a, grid, block, lds, s);
+    case FMT_F4: return (int)launch_mb<FMT_F4>(cfg, a, grid, block, lds, s);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+}  // namespace hq

@@ -1,0 +1,227 @@
+/*
+ * hq.h -- C ABI of the MI355X (gfx950) quantized GEMM library.
+ *
+ * The library multiplies activations by packed 4-bit weights that are
+ * dequantised inside the kernel, in a dense form and in a grouped
+ * mixture-of-experts (MoE) form.  Every entry point returns an hq_status;
+ * nothing throws across this boundary, and a thread-local message
+ * (hq_last_error) explains the last failure.
+ *
+ * What is computed (the Humming pages describe it in prose only):
+ *   - "Humming: open-source kernel library for quantized inference"
+ *     (news.ditty.ir), summary: every supported weight format is converted
+ *     into one standard description in which the weight codes, the scales
+ *     and the zero points are separate parameters; a layer is described by
+ *     a layer config (shapes, data types), a compute config (which GEMM) and
+ *     a tuning config (tile size, pipeline stages, matrix instruction),
+ *     chosen by a heuristic; W4A16, W4A8 (including MXFP4 weights with FP8
+ *     activations) and a grouped MoE path are supported.
+ *   - cocoloop.cn (vi / fr), format section and speed-up table: WnA16,
+ *     W4A8 and MXFP4 formats; dense single-layer GEMMs and MoE layers.
+ *   - aube.news (pt): INT4 stores one weight in 4 bits; dense and MoE layers.
+ *
+ * Number formats follow the OCP Microscaling (MX) v1.0 specification (E2M1
+ * elements, E8M0 shared scales, 32-element blocks) and the OCP 8-bit
+ * floating-point specification (E4M3, "fn" variant: no infinities).
+ *
+ * Conventions that hold for every function below
+ * -----------------------------------------------
+ *   * Pointers named "device" point to memory the caller allocated on the
+ *     GPU (hipMalloc, or a torch tensor's data_ptr()); "host" pointers point
+ *     to CPU memory.  The library never allocates, frees or synchronises on
+ *     the hq_gemm / hq_moe_* paths; work is queued on `stream` (a
+ *     hipStream_t, passed as void* so this header needs no HIP headers;
+ *     NULL is the default stream) and returns before it finishes.
+ *   * Argument validation happens before any launch; a rejected call
+ *     touches no memory.  A launch failure reported by the runtime returns
+ *     HQ_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ *     synchronisation, as for any asynchronous GPU work.
+ *   * Device buffers must be 16-byte aligned.
+ *   * Canonical (user-facing) weight layout, row-major, n-major:
+ *       codes   int32 [N, K/8]: eight 4-bit codes per word along K; code
+ *               k = 8j+i sits in bits [4i, 4i+4) of word j (low nibble
+ *               first); the word is a bit container, its sign is irrelevant.
+ *       scales  fp16 or bf16 [N, K/G] (INT4, G = 128): group g covers
+ *               k in [G*g, G*g+G).
+ *       zeros   uint8 [N, K/G] holding 0..15 (only with HQ_ZP_PER_GROUP_U4).
+ *       e8m0    uint8 [N, K/32] (MXFP4): scale 2^(X-127) per 32 k.
+ *     INT4 dequantisation is w = (q - z) * s; MXFP4 is
+ *     w = e2m1(q) * 2^(X-127).
+ *   * Activations: row-major [M, K] fp16 / bf16, or 8-bit codes (fp8 e4m3
+ *     or int8) with one fp32 scale per row (value = code * scale[m]).
+ *   * Output: row-major [M, N] fp16 / bf16, rounded to nearest even from
+ *     the fp32 accumulator.  Outputs are fully overwritten (no beta).
+ */
+#ifndef HQ_H
+#define HQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HQ_ABI_VERSION 1
+
+typedef enum hq_status {
+  HQ_OK = 0,
+  HQ_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, ...     */
+  HQ_ERR_UNSUPPORTED = 2, /* valid request this library does not implement */
+  HQ_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required    */
+  HQ_ERR_HIP = 4,         /* the HIP runtime reported an error             */
+  HQ_ERR_INTERNAL = 5     /* unexpected failure inside the library         */
+} hq_status;
+
+typedef enum hq_dtype {
+  HQ_F16 = 0,
+  HQ_BF16 = 1,
+  HQ_F32 = 2,
+  HQ_FP8_E4M3 = 3, /* OCP e4m3fn */
+  HQ_INT8 = 4,
+  HQ_U4 = 5,       /* unsigned 4-bit integer code 0..15 */
+  HQ_FP4_E2M1 = 6, /* OCP MX FP4 element */
+  HQ_E8M0 = 7,     /* OCP MX shared scale */
+  HQ_I32 = 8
+} hq_dtype;
+
+typedef enum hq_zp_mode {
+  HQ_ZP_NONE = 0,        /* no zero point (MXFP4)                        */
+  HQ_ZP_FIXED = 1,       /* one integer zero point for every group       */
+  HQ_ZP_PER_GROUP_U4 = 2 /* uint4 zero point per (n, group)              */
+} hq_zp_mode;
+
+typedef enum hq_ascale_mode {
+  HQ_ASCALE_NONE = 0,         /* 16-bit activations, no scale        */
+  HQ_ASCALE_PER_TOKEN_F32 = 1 /* 8-bit codes with one fp32 per row   */
+} hq_ascale_mode;
+
+/* The unified quantisation description: weight codes, scales, zero points
+ * and activation type as separate parameters (Humming page on
+ * news.ditty.ir, summary).  Supported combinations:
+ *   W4A16      w_elem U4, group 128, scale F16|BF16, zp FIXED|PER_GROUP_U4,
+ *              act F16|BF16, act_scale NONE, out F16|BF16
+ *   W4A8-INT   w_elem U4, group 128, scale F16|BF16, zp FIXED (8),
+ *              act INT8, act_scale PER_TOKEN_F32, out F16|BF16
+ *   W4A8-FP8   w_elem U4, group 128, scale F16|BF16, zp FIXED|PER_GROUP_U4,
+ *              act FP8_E4M3, act_scale PER_TOKEN_F32, out F16|BF16
+ *   W4A8-MXFP4 w_elem FP4_E2M1, group 32, scale E8M0, zp NONE,
+ *              act FP8_E4M3, act_scale PER_TOKEN_F32, out F16|BF16
+ * Anything else returns HQ_ERR_UNSUPPORTED from hq_plan_create. */
+typedef struct hq_quant_desc {
+  hq_dtype w_elem;
+  int w_bits;     /* 4 */
+  int group_size; /* 128 (INT4) or 32 (MXFP4) */
+  hq_dtype scale;
+  hq_zp_mode zp;
+  int zp_value;   /* HQ_ZP_FIXED: the zero point, 0..15 */
+  hq_dtype act;
+  hq_ascale_mode act_scale;
+  hq_dtype out;
+} hq_quant_desc;
+
+/* Layer config: the weight's shape; num_experts > 1 for the grouped form. */
+typedef struct hq_layer_desc {
+  int64_t n, k;
+  int num_experts;
+  hq_quant_desc q;
+} hq_layer_desc;
+
+typedef enum hq_gemm_kind { HQ_GEMM_DENSE = 0, HQ_GEMM_GROUPED = 1 } hq_gemm_kind;
+
+typedef enum hq_epilogue {
+  HQ_EPI_NONE = 0,          /* plain output                                */
+  HQ_EPI_SILU_MUL = 1,      /* grouped gate_up: SiLU(h[:, :N/2]) * h[:, N/2:] */
+  HQ_EPI_SILU_MUL_QFP8 = 2, /* as above, then per-row fp8 e4m3 requant    */
+  HQ_EPI_TOPK_COMBINE = 3,  /* grouped down: * topk weight, sum per token  */
+  HQ_EPI_I32_ACC = 4        /* W4A8-INT debug: per-group int32 accumulators */
+} hq_epilogue;
+
+/* Compute config: which GEMM and which epilogue. */
+typedef struct hq_compute {
+  hq_gemm_kind kind;
+  hq_epilogue epi;
+} hq_compute;
+
+/* Tuning config (execution choice, kept apart from the description).
+ * Zero in any field means "let the heuristic choose". */
+typedef struct hq_tuning {
+  int kernel;  /* 0 auto, 1 skinny (small M, split-K), 2 tiled (large M)  */
+  int tile_m;  /* skinny: rows per workgroup (16, 32, 64); tiled: 64/128/256 */
+  int tile_n;  /* skinny: columns per workgroup (16, 32, 64)              */
+  int waves;   /* wavefronts per workgroup                                 */
+  int split_k; /* skinny: workgroups sharing one output tile along K      */
+  int stages;  /* groups of 128 k kept in flight per wave                  */
+  int mfma;    /* 16 (16x16 MFMA); reserved for 32                         */
+} hq_tuning;
+
+typedef struct hq_plan hq_plan;
+
+int hq_abi_version(void);
+const char* hq_status_str(hq_status s);
+/* Message of the last failed call on this thread ("" if none). */
+const char* hq_last_error(void);
+
+/* Validate a layer + compute description and pick an execution choice.
+ * max_m bounds the rows (tokens) a later call may pass.  `tuning` may be
+ * NULL (heuristic, the rule-based selection the pages describe); non-zero
+ * fields override it.  On success *out owns a host object released with
+ * hq_plan_destroy.  A plan is immutable and may be used from several
+ * streams and threads at once (each call with its own workspace). */
+hq_status hq_plan_create(const hq_layer_desc* layer, const hq_compute* compute, int64_t max_m,
+                         const hq_tuning* tuning, hq_plan** out);
+hq_status hq_plan_destroy(hq_plan* plan);
+/* Human-readable description of the plan's execution choice. */
+hq_status hq_plan_describe(const hq_plan* plan, int64_t m, char* buf, size_t len);
+
+/* Workspace a call with m rows needs, in bytes (0 if none).  A workspace
+ * must be zero-filled once before its first use; every call leaves it in a
+ * state valid for the next call.  Two calls that overlap in time must not
+ * share one workspace. */
+hq_status hq_plan_workspace_bytes(const hq_plan* plan, int64_t m, size_t* bytes);
+
+/* Sizes of the repacked (device-layout) weight: w_bytes for the codes,
+ * meta_bytes for scales + zero points (or E8M0 scales).  For a grouped
+ * plan both cover all experts. */
+hq_status hq_repacked_bytes(const hq_plan* plan, size_t* w_bytes, size_t* meta_bytes);
+
+/* Offline repack (the format conversion into the library's standard
+ * layout): canonical codes / scales / zeros-or-e8m0 (see above; for a
+ * grouped plan each is stacked [E, ...]) -> the device layout, which places
+ * the 4-bit codes in gfx950 MFMA operand order.  All pointers are device
+ * pointers; the work is a kernel on `stream`.  `zeros_or_e8m0` is NULL for
+ * HQ_ZP_FIXED.  The output is a private layout: only hq_gemm / hq_moe_gemm
+ * of a plan with the same layer description and activation type read it. */
+hq_status hq_repack(const hq_plan* plan, const void* codes, const void* scales,
+                    const void* zeros_or_e8m0, void* w_out, void* meta_out, void* stream);
+/* The same permutation on host memory (for preparing weights offline on a
+ * machine without a GPU).  Produces bytes identical to hq_repack. */
+hq_status hq_repack_host(const hq_plan* plan, const void* codes, const void* scales,
+                         const void* zeros_or_e8m0, void* w_out, void* meta_out);
+
+/* Dense GEMM: out[M, N] = A[M, K] . W_deq^T.
+ *   a        device [m, K] activations (act dtype of the plan)
+ *   a_scale  device fp32 [m] per-row scales for 8-bit activations, else NULL
+ *   w, meta  device, produced by hq_repack
+ *   out      device [m, N] in the plan's out dtype; with HQ_EPI_I32_ACC
+ *            (W4A8-INT only) int32 [m, N, K/128] holding
+ *            P[m,n,g] = sum_{k in group g} a_q[m,k] * (q[n,k] - 8), exactly
+ *   ws       device workspace of hq_plan_workspace_bytes(plan, m) bytes
+ *            (may be NULL when that is 0)
+ * m = 0 is a no-op; m > max_m is HQ_ERR_INVALID_ARG. */
+hq_status hq_gemm(const hq_plan* plan, int64_t m, const void* a, const float* a_scale,
+                  const void* w, const void* meta, void* out, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/* Kernel timing: the next GEMM kernel this thread launches records `start`
+ * and `stop` (hipEvent_t, created by the caller with timing enabled) around
+ * its own execution (the dispatch's start and end, without launch gaps), so
+ * hipEventElapsedTime gives the kernel's duration.  The request is consumed
+ * by that launch; passing NULL, NULL cancels a pending request. */
+hq_status hq_time_next_launch(void* start_event, void* stop_event);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HQ_H */

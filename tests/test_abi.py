@@ -1,0 +1,249 @@
+"""C-ABI checks that need no GPU.
+
+* The built library loads and exports every function include/hq.h declares.
+* Host-side validation rejects bad descriptions, tunings and call arguments
+  before any launch (every call below fails validation, so nothing reaches a
+  device on any machine).
+* The host repack (hq_repack_host; the device repack is checked against it
+  on the GPU) produces the operand order each matrix instruction needs.  The
+  requirement is restated here from the MFMA operand definitions, not from the
+  library's code: lane l of the 16 x 128 fragment (nb, g) serves column
+  16 nb + l % 16 and the k range [128 g + 32 (l // 16), +32); every extracted
+  operand register must hold the codes of the k its activation partner holds.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_gemm_repack_amd as hq
+import datagen
+from oracle.formats import unpack_u4
+
+
+def _plan(n=256, k=512, quant=None, max_m=64, epi="none", tuning=None):
+    return hq.Plan(n, k, quant if quant is not None else hq.w4a16(), max_m=max_m, epi=epi, tuning=tuning)
+
+
+def test_library_exports_every_header_function():
+    L = hq.lib()
+    names = hq.header_functions()
+    assert {"hq_plan_create", "hq_repack", "hq_gemm", "hq_last_error"} <= set(names)
+    for name in names:
+        assert hasattr(L, name), f"{name} declared in include/hq.h but not exported"
+
+
+def test_abi_version_and_status_strings():
+    L = hq.lib()
+    assert L.hq_abi_version() == 1
+    assert L.hq_status_str(0) == b"HQ_OK"
+    assert L.hq_status_str(3) == b"HQ_ERR_WORKSPACE"
+
+
+@pytest.mark.parametrize("kw, status", [
+    (dict(k=500), hq.HQ_ERR_UNSUPPORTED),          # K not a multiple of 128
+    (dict(n=250), hq.HQ_ERR_UNSUPPORTED),          # N not a multiple of 16
+    (dict(max_m=-1), hq.HQ_ERR_INVALID_ARG),
+    (dict(quant=hq.QuantDesc(hq.U4, 3, 128, hq.F16, hq.ZP_FIXED, 8, hq.F16, 0, hq.F16)), hq.HQ_ERR_UNSUPPORTED),
+    (dict(quant=hq.QuantDesc(hq.U4, 4, 64, hq.F16, hq.ZP_FIXED, 8, hq.F16, 0, hq.F16)), hq.HQ_ERR_UNSUPPORTED),
+    (dict(quant=hq.QuantDesc(hq.U4, 4, 128, hq.F16, hq.ZP_FIXED, 16, hq.F16, 0, hq.F16)), hq.HQ_ERR_INVALID_ARG),
+    (dict(quant=hq.QuantDesc(hq.U4, 4, 128, hq.F16, hq.ZP_PER_GROUP_U4, 0, hq.INT8, 1, hq.BF16)),
+     hq.HQ_ERR_UNSUPPORTED),                       # INT4 x INT8 needs zero 8
+    (dict(quant=hq.QuantDesc(hq.FP4_E2M1, 4, 32, hq.E8M0, hq.ZP_NONE, 0, hq.BF16, 0, hq.BF16)),
+     hq.HQ_ERR_UNSUPPORTED),                       # MXFP4 x bf16 not implemented
+    (dict(quant=hq.QuantDesc(hq.U4, 4, 128, hq.F16, hq.ZP_FIXED, 8, hq.INT8, 0, hq.BF16)),
+     hq.HQ_ERR_UNSUPPORTED),                       # int8 activations without scales
+    (dict(epi="i32_acc"), hq.HQ_ERR_UNSUPPORTED),  # int32 accumulators need INT4 x INT8
+    (dict(tuning=dict(tile_m=48)), hq.HQ_ERR_INVALID_ARG),
+    (dict(tuning=dict(tile_n=128)), hq.HQ_ERR_INVALID_ARG),
+    (dict(tuning=dict(waves=9)), hq.HQ_ERR_INVALID_ARG),
+    (dict(tuning=dict(stages=3)), hq.HQ_ERR_INVALID_ARG),
+    (dict(tuning=dict(tile_m=64, tile_n=64, stages=4)), hq.HQ_ERR_INVALID_ARG),  # register budget
+])
+def test_plan_validation(kw, status):
+    with pytest.raises(hq.HQError) as e:
+        _plan(**kw)
+    assert e.value.status == status
+    assert hq.lib().hq_last_error().decode()
+
+
+def test_grouped_epilogue_on_dense_plan_rejected():
+    with pytest.raises(hq.HQError) as e:
+        _plan(epi="silu_mul")
+    assert e.value.status == hq.HQ_ERR_UNSUPPORTED
+
+
+def test_null_arguments_rejected():
+    L = hq.lib()
+    h = ctypes.c_void_p()
+    assert L.hq_plan_create(None, None, 1, None, ctypes.byref(h)) == hq.HQ_ERR_INVALID_ARG
+    b = ctypes.c_size_t()
+    assert L.hq_plan_workspace_bytes(None, 1, ctypes.byref(b)) == hq.HQ_ERR_INVALID_ARG
+    assert L.hq_gemm(None, 1, None, None, None, None, None, None, 0, None) == hq.HQ_ERR_INVALID_ARG
+
+
+# Fake, never-dereferenced device addresses: every call below is rejected by
+# validation before any launch.
+_A16 = 0x10000
+
+
+def _gemm_status(plan, m, a=_A16, a_scale=None, w=_A16, meta=_A16, out=_A16, ws=None, ws_bytes=0):
+    return hq.lib().hq_gemm(plan._h, m, a, a_scale, w, meta, out, ws, ws_bytes, None)
+
+
+def test_gemm_argument_validation():
+    p = _plan(max_m=16)
+    assert _gemm_status(p, 17) == hq.HQ_ERR_INVALID_ARG             # m > max_m
+    assert _gemm_status(p, -1) == hq.HQ_ERR_INVALID_ARG
+    assert _gemm_status(p, 0) == hq.HQ_OK                            # m = 0 is a no-op
+    assert _gemm_status(p, 4, a=None) == hq.HQ_ERR_INVALID_ARG       # null
+    assert _gemm_status(p, 4, w=_A16 + 4) == hq.HQ_ERR_INVALID_ARG  # misaligned
+    assert _gemm_status(p, 4, a_scale=_A16) == hq.HQ_ERR_INVALID_ARG  # 16-bit A takes no scale
+    p8 = _plan(quant=hq.w4a8_int(), max_m=16)
+    assert _gemm_status(p8, 4) == hq.HQ_ERR_INVALID_ARG              # int8 A needs scales
+
+
+def test_workspace_validation():
+    # force a cross-workgroup split so that a workspace is required
+    p = _plan(n=256, k=4096, max_m=16, tuning=dict(split_k=4))
+    need = p.workspace_bytes(16)
+    assert need > 0
+    assert _gemm_status(p, 16, ws=None) == hq.HQ_ERR_WORKSPACE
+    assert _gemm_status(p, 16, ws=_A16, ws_bytes=need - 1) == hq.HQ_ERR_WORKSPACE
+    assert _plan(n=256, k=4096, max_m=16, tuning=dict(split_k=1)).workspace_bytes(16) == 0
+
+
+def test_describe_and_sizes():
+    p = _plan(n=4096, k=4096, quant=hq.w4a16("bf16", zp="u4"), max_m=64)
+    s = p.describe(16)
+    assert "w4a16-bf16" in s and "split_k" in s
+    w, m = p.repacked_bytes()
+    assert w == 4096 * 4096 // 2
+    assert m == 4096 * 32 * 2 + (4096 // 16) * 32 * 8
+    pm = _plan(n=4096, k=7168, quant=hq.w4a8_mxfp4(), max_m=16)
+    assert pm.repacked_bytes() == (4096 * 7168 // 2, 4096 * 7168 // 32)
+
+
+# ---------------------------------------------------------------- layout ----
+
+N, K = 48, 384  # three column blocks, three groups
+
+
+def _codes(seed=0):
+    rng = np.random.default_rng(seed)
+    q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    return q, datagen.pack_u4(q)
+
+
+def _frag_words(w: np.ndarray):
+    """Device bytes -> words[nb, g, lane, t]."""
+    return w.view(np.uint32).reshape(N // 16, K // 128, 64, 4)
+
+
+def _lane_k(g, lane):
+    return 128 * g + 32 * (lane // 16)
+
+
+def test_repack_w16_operand_order():
+    q, codes = _codes(1)
+    p = _plan(N, K, hq.w4a16("f16"), max_m=16)
+    w, _ = p.repack_host(torch.from_numpy(codes), torch.ones(N, K // 128, dtype=torch.float16))
+    fw = _frag_words(w.numpy())
+    for nb in range(N // 16):
+        for g in range(K // 128):
+            for lane in range(64):
+                n, k0 = 16 * nb + lane % 16, _lane_k(g, lane)
+                for t in range(4):
+                    x = int(fw[nb, g, lane, t])
+                    for r in range(4):  # operand register r: 16-bit halves = k-offsets 2r, 2r+1
+                        v = (x >> (4 * r)) & 0x000F000F
+                        assert v & 0xF == q[n, k0 + 8 * t + 2 * r]
+                        assert v >> 16 == q[n, k0 + 8 * t + 2 * r + 1]
+
+
+def test_repack_int8_operand_order():
+    q, codes = _codes(2)
+    p = _plan(N, K, hq.w4a8_int(), max_m=16)
+    w, _ = p.repack_host(torch.from_numpy(codes), torch.ones(N, K // 128, dtype=torch.float16))
+    fw = _frag_words(w.numpy())
+    for nb in range(N // 16):
+        for g in range(K // 128):
+            for lane in range(64):
+                n, k0 = 16 * nb + lane % 16, _lane_k(g, lane)
+                for step in range(2):  # int8 MFMA 16x16x64: 16 k per lane per step
+                    w0, w1 = int(fw[nb, g, lane, 2 * step]), int(fw[nb, g, lane, 2 * step + 1])
+                    regs = [(w0 << 4) & 0xF0F0F0F0, w0 & 0xF0F0F0F0, (w1 << 4) & 0xF0F0F0F0, w1 & 0xF0F0F0F0]
+                    for j, reg in enumerate(regs):
+                        for b in range(4):
+                            byte = (reg >> (8 * b)) & 0xFF
+                            val = byte - 256 if byte >= 128 else byte
+                            assert val == 16 * (int(q[n, k0 + 16 * step + 4 * j + b]) - 8)
+
+
+def test_repack_fp8_operand_order():
+    q, codes = _codes(3)
+    p = _plan(N, K, hq.w4a8_fp8(), max_m=16)
+    w, _ = p.repack_host(torch.from_numpy(codes), torch.ones(N, K // 128, dtype=torch.float16))
+    fw = _frag_words(w.numpy())
+    for nb in range(N // 16):
+        for g in range(K // 128):
+            for lane in range(64):
+                n, k0 = 16 * nb + lane % 16, _lane_k(g, lane)
+                for t in range(4):  # operand registers 2t, 2t+1 of the 8-register fp8 operand
+                    x = int(fw[nb, g, lane, t])
+                    for h, reg in enumerate((x & 0x0F0F0F0F, (x >> 4) & 0x0F0F0F0F)):
+                        for b in range(4):
+                            assert (reg >> (8 * b)) & 0xFF == q[n, k0 + 8 * t + 4 * h + b]
+
+
+def test_repack_mxfp4_operand_order_and_e8m0():
+    q, codes = _codes(4)
+    rng = np.random.default_rng(5)
+    e8 = rng.integers(119, 124, size=(N, K // 32), dtype=np.uint8)
+    p = _plan(N, K, hq.w4a8_mxfp4(), max_m=16)
+    w, meta = p.repack_host(torch.from_numpy(codes), e8m0=torch.from_numpy(e8))
+    wb = w.numpy().reshape(N // 16, K // 128, 64, 16)
+    mb = meta.numpy().reshape(N // 16, K // 128, 64)
+    for nb in range(N // 16):
+        for g in range(K // 128):
+            for lane in range(64):
+                n, k0 = 16 * nb + lane % 16, _lane_k(g, lane)
+                nib = np.stack([wb[nb, g, lane] & 0xF, wb[nb, g, lane] >> 4], axis=1).reshape(-1)
+                assert np.array_equal(nib, q[n, k0:k0 + 32])  # element j: byte j/2, low nibble first
+                assert mb[nb, g, lane] == e8[n, k0 // 32]
+
+
+def test_repack_scales_and_zeros():
+    q, codes = _codes(6)
+    rng = np.random.default_rng(7)
+    scales = torch.from_numpy(rng.uniform(0.005, 0.02, size=(N, K // 128))).to(torch.bfloat16)
+    zeros = rng.integers(0, 16, size=(N, K // 128), dtype=np.uint8)
+    p = _plan(N, K, hq.w4a16("bf16", zp="u4"), max_m=16)
+    w, meta = p.repack_host(torch.from_numpy(codes), scales, torch.from_numpy(zeros))
+    G = K // 128
+    sreg = meta[: N * G * 2].view(torch.bfloat16).reshape(N // 16, G, 16)
+    zreg = meta[N * G * 2:].numpy().view(np.uint32).reshape(N // 16, G, 2)
+    for nb in range(N // 16):
+        for g in range(G):
+            for c in range(16):
+                n = 16 * nb + c
+                assert sreg[nb, g, c].item() == scales[n, g].item()
+                assert (int(zreg[nb, g, c // 8]) >> (4 * (c % 8))) & 0xF == zeros[n, g]
+
+
+def test_repack_is_a_bijection_on_codes():
+    # every canonical nibble appears exactly once in the device layout
+    for quant in (hq.w4a16("f16"), hq.w4a8_fp8(), hq.w4a8_mxfp4()):
+        q = np.zeros((N, K), dtype=np.uint8)
+        p = _plan(N, K, quant, max_m=16)
+        for bit in range(4):
+            q[:] = 0
+            rng = np.random.default_rng(bit)
+            q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+            codes = torch.from_numpy(datagen.pack_u4(q))
+            kw = dict(e8m0=torch.zeros(N, K // 32, dtype=torch.uint8)) if quant.w_elem == hq.FP4_E2M1 else \
+                dict(scales=torch.ones(N, K // 128, dtype=torch.float16))
+            w, _ = p.repack_host(codes, **kw)
+            dev = unpack_u4(w.numpy().view(np.int32).reshape(1, -1))[0]
+            assert np.array_equal(np.bincount(dev, minlength=16), np.bincount(q.reshape(-1), minlength=16))
