@@ -115,6 +115,8 @@ _SIGS = {
     "hq_repack": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 5 + [ctypes.c_void_p]),
     "hq_repack_host": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 5),
     "hq_time_next_launch": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
+    "hq_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.c_void_p]),
     "hq_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_size_t, ctypes.c_void_p]),
@@ -281,3 +283,10 @@ class Plan:
         _check(lib().hq_gemm(self._h, m, _ptr(a), _ptr(a_scale), _ptr(w), _ptr(meta), _ptr(out), _ptr(ws),
                              ws_bytes, _stream_ptr(a.device)))
         return out
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int, nbytes: Optional[int] = None):
+    """Bandwidth probe: read `nbytes` (default all) of `buf` once (see hq_stream_read)."""
+    _dev(buf, "buf"), _dev(sink, "sink")
+    n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    _check(lib().hq_stream_read(_ptr(buf), n, _ptr(sink), int(workgroups), _stream_ptr(buf.device)))

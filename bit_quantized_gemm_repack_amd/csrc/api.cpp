@@ -12,6 +12,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <new>
 #include <string>
 
@@ -120,27 +121,49 @@ Exec choose_exec(const hq_plan* p, int64_t m) {
   const int64_t N = p->layer.n;
   const int64_t G = p->layer.k / kFragK;
   const hq_tuning& u = p->user;
+  e.ws_counter_bytes = align256((size_t)(N / 16) * (size_t)cdiv(p->max_m > 0 ? p->max_m : 1, 16) * 4);
+  // Large M: the MFMA-bound tiled kernel (needs whole 128/256-column tiles).
+  const bool tiled_ok = p->compute.epi != HQ_EPI_I32_ACC && N % 128 == 0;
+  if (tiled_ok && (u.kernel == KER_TILED || (u.kernel == 0 && m > 64))) {
+    e.kernel = KER_TILED;
+    e.tl.bm = m >= 512 ? 128 : 64;
+    e.tl.nbw = (N % 256 == 0 && !(p->fmt == FMT_W16BF16 && e.tl.bm == 128)) ? 4 : 2;
+    if (u.tile_m) e.tl.bm = u.tile_m;
+    if (u.tile_n) e.tl.nbw = u.tile_n / 64;
+    e.tiles_m = cdiv(m > 0 ? m : 1, e.tl.bm);
+    e.tiles_n = e.tl.nbw > 0 ? N / (64 * e.tl.nbw) : 0;
+    e.ws_bytes = 0;
+    return e;
+  }
   SkinnyCfg c{};
   c.mb = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
-  const bool act16 = p->fmt == FMT_W16F16 || p->fmt == FMT_W16BF16;
-  c.nb = (m > 4 && N % 32 == 0 && !(c.mb == 4 && act16)) ? 2 : 1;
-  c.waves = 4;
-  c.stages = 2;
+  c.nb = 1;
+  if (c.mb == 1) {
+    // one column block per workgroup, K split over up to 16 waves, every
+    // group of a wave in flight at once (stages >= groups per wave)
+    c.waves = (int)std::min<int64_t>(16, std::max<int64_t>(1, G / 2));
+    c.stages = cdiv(G, c.waves) <= 2 ? 2 : 4;
+  } else {
+    c.waves = 8;
+    c.stages = c.mb == 2 ? 4 : 2;
+  }
   if (u.tile_m) c.mb = u.tile_m / 16;
   if (u.tile_n) c.nb = u.tile_n / 16;
   if (u.waves) c.waves = u.waves;
   if (u.stages) c.stages = u.stages;
+  // 16-wave workgroups exist for one 16 x 16 block per wave only
+  if (!u.waves && c.waves > 8 && !(c.mb == 1 && c.nb == 1 && c.stages <= 4)) c.waves = 8;
   const int64_t ntiles = N / (16 * c.nb);
   const int64_t mch = cdiv(m > 0 ? m : 1, 16 * c.mb);
+  // Splitting K over workgroups needs a device-wide release/acquire per
+  // workgroup (an L2 write-back + invalidate on this chip), so it is only
+  // used when asked for.
   int64_t split = 1;
-  // enough workgroups to cover the chip twice, while every wave keeps work
-  while (ntiles * mch * split < 512 && G / (split * 2) >= 2 * c.waves) split *= 2;
   if (u.split_k) split = u.split_k;
   c.split = (int)split;
   e.sk = c;
   e.tiles_m = mch;
   e.tiles_n = ntiles;
-  e.ws_counter_bytes = align256((size_t)(N / 16) * (size_t)cdiv(p->max_m > 0 ? p->max_m : 1, 16) * 4);
   e.ws_bytes = 0;
   if (c.split > 1 && p->compute.epi != HQ_EPI_I32_ACC)
     e.ws_bytes = e.ws_counter_bytes + align256((size_t)c.split * (size_t)m * (size_t)N * 4);
@@ -152,18 +175,28 @@ Exec choose_exec(const hq_plan* p, int64_t m) {
 namespace {
 
 hq_status check_exec(const hq_plan* p, const hq::Exec& e) {
+  if (e.kernel == hq::KER_TILED) {
+    if (e.tl.bm != 64 && e.tl.bm != 128) return fail(HQ_ERR_INVALID_ARG, "tiled kernel: tile_m must be 64 or 128");
+    if (e.tl.nbw != 2 && e.tl.nbw != 4) return fail(HQ_ERR_INVALID_ARG, "tiled kernel: tile_n must be 128 or 256");
+    if (p->layer.n % (64 * e.tl.nbw)) return fail(HQ_ERR_INVALID_ARG, "tiled kernel: N must be a multiple of tile_n");
+    if (e.tiles_m * e.tiles_n > (int64_t(1) << 31) - 1) return fail(HQ_ERR_UNSUPPORTED, "too many tiles");
+    return HQ_OK;
+  }
   const hq::SkinnyCfg& c = e.sk;
   if (!valid_pow(c.mb)) return fail(HQ_ERR_INVALID_ARG, "tile_m must be 16, 32 or 64");
   if (!valid_pow(c.nb)) return fail(HQ_ERR_INVALID_ARG, "tile_n must be 16, 32 or 64");
   if (p->layer.n % (16 * c.nb)) return fail(HQ_ERR_INVALID_ARG, "N must be a multiple of tile_n");
-  if (c.waves < 1 || c.waves > 8) return fail(HQ_ERR_INVALID_ARG, "waves must be 1..8");
-  if (c.stages != 2 && c.stages != 4) return fail(HQ_ERR_INVALID_ARG, "stages must be 2 or 4");
+  if (c.waves < 1 || c.waves > 16) return fail(HQ_ERR_INVALID_ARG, "waves must be 1..16");
+  if (c.waves > 8 && (c.mb != 1 || c.nb != 1 || c.stages > 4))
+    return fail(HQ_ERR_INVALID_ARG, "more than 8 waves needs tile_m=16, tile_n=16 and stages <= 4");
+  if (c.stages != 2 && c.stages != 4 && c.stages != 8) return fail(HQ_ERR_INVALID_ARG, "stages must be 2, 4 or 8");
+  if (c.stages == 8 && (c.mb != 1 || c.nb > 2)) return fail(HQ_ERR_INVALID_ARG, "stages=8 needs tile_m=16, tile_n<=32");
   if (c.split < 1 || c.split > 64) return fail(HQ_ERR_INVALID_ARG, "split_k must be 1..64");
   if ((size_t)c.waves * c.mb * c.nb * 4 * 64 * 4 > 32768)
     return fail(HQ_ERR_INVALID_ARG, "waves * tile_m * tile_n too large for the reduction buffer");
   // register budget: these shapes would spill at two waves per SIMD
   const bool act16 = p->fmt == hq::FMT_W16F16 || p->fmt == hq::FMT_W16BF16;
-  if (c.mb * c.nb * c.stages > 16 || c.mb * c.stages > 8 || (c.mb == 4 && c.nb == 2 && act16))
+  if ((c.stages < 8 && c.mb * c.nb * c.stages > 16) || c.mb * c.stages > 8 || (c.mb == 4 && c.nb == 2 && act16))
     return fail(HQ_ERR_INVALID_ARG, "tile_m/tile_n/stages combination exceeds the register budget");
   return HQ_OK;
 }
@@ -266,6 +299,12 @@ hq_status hq_plan_describe(const hq_plan* p, int64_t m, char* buf, size_t len) {
   if (!p || !buf || len == 0) return fail(HQ_ERR_INVALID_ARG, "null argument");
   if (m < 1) m = 1;
   hq::Exec e = hq::choose_exec(p, m);
+  if (e.kernel == hq::KER_TILED) {
+    snprintf(buf, len, "kernel=tiled fmt=%s m=%lld n=%lld k=%lld tile_m=%d tile_n=%d waves=4 grid=%lld ws=0",
+             fmt_name(p->fmt), (long long)m, (long long)p->layer.n, (long long)p->layer.k, e.tl.bm, 64 * e.tl.nbw,
+             (long long)(e.tiles_m * e.tiles_n));
+    return ok();
+  }
   snprintf(buf, len,
            "kernel=skinny fmt=%s m=%lld n=%lld k=%lld tile_m=%d tile_n=%d waves=%d split_k=%d stages=%d "
            "grid=%lldx%dx%lld ws=%zu",
@@ -379,6 +418,32 @@ hq_status hq_gemm(const hq_plan* p, int64_t m, const void* a, const float* a_sca
     }
     const int64_t N = p->layer.n, K = p->layer.k, G = K / 128;
     if (m * K > (int64_t(1) << 40)) return fail(HQ_ERR_UNSUPPORTED, "problem too large");
+    const uint32_t* zeros = p->layer.q.zp == HQ_ZP_PER_GROUP_U4
+                                ? reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(meta) +
+                                                                    p->scale_region_bytes)
+                                : nullptr;
+    if (e.kernel == hq::KER_TILED) {
+      hq::TiledArgs t{};
+      t.a = a;
+      t.a_scale = a_scale;
+      t.w = w;
+      if (p->fmt == hq::FMT_F4) t.e8m0 = static_cast<const uint8_t*>(meta);
+      else t.scales = meta;
+      t.zeros = zeros;
+      t.out = out;
+      t.M = (int)m;
+      t.N = (int)N;
+      t.K = (int)K;
+      t.G = (int)G;
+      t.zp_fixed = p->layer.q.zp == HQ_ZP_FIXED ? p->layer.q.zp_value : -1;
+      t.scale_bf16 = p->layer.q.scale == HQ_BF16;
+      t.out_bf16 = p->layer.q.out == HQ_BF16;
+      t.tiles_m = (int)e.tiles_m;
+      t.tiles_n = (int)e.tiles_n;
+      int err = hq::launch_tiled(p->fmt, e.tl, t, stream);
+      if (err != hipSuccess) return fail(HQ_ERR_HIP, "gemm launch: %s", hipGetErrorString((hipError_t)err));
+      return ok();
+    }
     hq::SkinnyArgs args{};
     args.a = a;
     args.a_scale = a_scale;
@@ -387,8 +452,7 @@ hq_status hq_gemm(const hq_plan* p, int64_t m, const void* a, const float* a_sca
       args.e8m0 = static_cast<const uint8_t*>(meta);
     } else {
       args.scales = meta;
-      if (p->layer.q.zp == HQ_ZP_PER_GROUP_U4)
-        args.zeros = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(meta) + p->scale_region_bytes);
+      args.zeros = zeros;
     }
     args.out = out;
     if (e.ws_bytes > 0) {
@@ -410,6 +474,15 @@ hq_status hq_gemm(const hq_plan* p, int64_t m, const void* a, const float* a_sca
   } catch (...) {
     return fail(HQ_ERR_INTERNAL, "exception in hq_gemm");
   }
+}
+
+hq_status hq_stream_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups, void* stream) {
+  if (!buf || !sink) return fail(HQ_ERR_INVALID_ARG, "null argument");
+  if (bytes % 16 || !aligned16(buf)) return fail(HQ_ERR_INVALID_ARG, "buffer must be 16-byte aligned and sized");
+  if (workgroups < 1 || workgroups > (1 << 20)) return fail(HQ_ERR_INVALID_ARG, "workgroups out of range");
+  int err = hq::launch_stream_read(buf, bytes, sink, workgroups, stream);
+  if (err != hipSuccess) return fail(HQ_ERR_HIP, "stream read launch: %s", hipGetErrorString((hipError_t)err));
+  return ok();
 }
 
 }  // extern "C"

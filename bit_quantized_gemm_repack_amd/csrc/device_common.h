@@ -1,0 +1,82 @@
+// Device helpers shared by the gfx950 GEMM kernels: operand vector types,
+// 16-bit conversions, and the 4-bit code -> MFMA operand expansions that the
+// fragment layout (hq_internal.h) was designed for.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace hq {
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef int i4_t __attribute__((ext_vector_type(4)));
+typedef int i8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+
+__device__ inline float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ inline float f16_bits_to_float(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (a NaN stays a quiet NaN).
+__device__ inline uint16_t float_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+// Round-to-nearest-even fp32 -> fp16 bits (the hardware conversion).
+__device__ inline uint16_t float_to_f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+__device__ inline i8_t cat8(u4_t x, u4_t y) {
+  i8_t r;
+  r[0] = x[0]; r[1] = x[1]; r[2] = x[2]; r[3] = x[3];
+  r[4] = y[0]; r[5] = y[1]; r[6] = y[2]; r[7] = y[3];
+  return r;
+}
+
+// One word of NIB_W16 codes -> the 16-bit operand (8 values, k-offsets 0..7)
+// holding MAGIC + q exactly: fp16 0x6400 = 1024, bf16 0x4300 = 128.
+__device__ inline u4_t w16_operand(uint32_t x, uint32_t magic) {
+  return u4_t{(x & 0x000F000Fu) | magic, ((x >> 4) & 0x000F000Fu) | magic, ((x >> 8) & 0x000F000Fu) | magic,
+              ((x >> 12) & 0x000F000Fu) | magic};
+}
+
+// Two words of NIB_B8 codes stored as q ^ 8 -> the int8 operand (16 values)
+// holding 16 * (q - 8) exactly.
+__device__ inline i4_t i8_operand(uint32_t w0, uint32_t w1) {
+  return i4_t{(int)((w0 << 4) & 0xF0F0F0F0u), (int)(w0 & 0xF0F0F0F0u), (int)((w1 << 4) & 0xF0F0F0F0u),
+              (int)(w1 & 0xF0F0F0F0u)};
+}
+
+// Four words of NIB_B8 codes -> the fp8 operand (32 values): the e4m3 codes
+// 0x00..0x0F, i.e. q * 2^-9 exactly (subnormal and first normal binade share
+// the spacing 2^-9).
+__device__ inline i8_t q8_operand(u4_t w) {
+  return i8_t{(int)(w[0] & 0x0F0F0F0Fu), (int)((w[0] >> 4) & 0x0F0F0F0Fu), (int)(w[1] & 0x0F0F0F0Fu),
+              (int)((w[1] >> 4) & 0x0F0F0F0Fu), (int)(w[2] & 0x0F0F0F0Fu), (int)((w[2] >> 4) & 0x0F0F0F0Fu),
+              (int)(w[3] & 0x0F0F0F0Fu), (int)((w[3] >> 4) & 0x0F0F0F0Fu)};
+}
+
+template <bool F16>
+__device__ inline f4_t mfma_16x16x32(u4_t a, u4_t b, f4_t c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, a), __builtin_bit_cast(h8_t, b), c, 0,
+                                                  0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8_t, a), __builtin_bit_cast(b8_t, b), c,
+                                                   0, 0, 0);
+}
+
+__device__ inline float load_scale(const void* scales, int64_t idx, int bf16) {
+  const uint32_t s = static_cast<const uint16_t*>(scales)[idx];
+  return bf16 ? bf16_bits_to_float(s) : f16_bits_to_float(s);
+}
+
+__device__ inline void store_out(void* out, int64_t idx, float v, int bf16) {
+  static_cast<uint16_t*>(out)[idx] = bf16 ? float_to_bf16_bits(v) : float_to_f16_bits(v);
+}
+
+}  // namespace hq

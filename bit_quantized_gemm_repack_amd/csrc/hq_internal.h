@@ -137,6 +137,11 @@ HQ_HD inline int64_t e8m0_src_index(int64_t K, int64_t eidx) {
 
 enum KernelKind : int { KER_SKINNY = 1, KER_TILED = 2 };
 
+struct TiledCfgRt {
+  int bm;   // rows per workgroup tile (64, 128)
+  int nbw;  // 16-column blocks per wave (2, 4); tile width = 64 * nbw
+};
+
 struct SkinnyCfg {
   int mb;      // 16-row blocks per workgroup (1, 2, 4)
   int nb;      // 16-column blocks per workgroup (1, 2, 4)
@@ -164,6 +169,7 @@ namespace hq {
 struct Exec {
   int kernel;
   SkinnyCfg sk;
+  TiledCfgRt tl;
   int64_t tiles_m, tiles_n;
   size_t ws_bytes;  // total workspace
   size_t ws_counter_bytes;
@@ -191,6 +197,24 @@ struct SkinnyArgs {
 };
 
 int launch_skinny(int fmt, const SkinnyCfg& cfg, const SkinnyArgs& a, void* stream);
+
+struct TiledArgs {
+  const void* a;
+  const float* a_scale;
+  const void* w;
+  const void* scales;
+  const uint32_t* zeros;
+  const uint8_t* e8m0;
+  void* out;
+  int M, N, K, G;
+  int zp_fixed;
+  int scale_bf16;
+  int out_bf16;
+  int tiles_m, tiles_n;
+};
+
+int launch_tiled(int fmt, const TiledCfgRt& cfg, const TiledArgs& a, void* stream);
+int launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups, void* stream);
 
 // Pending timing events for the next launch on this thread (see
 // hq_time_next_launch); take_timing() returns and clears them.

@@ -36,31 +36,10 @@
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
+#include "device_common.h"
 #include "hq_internal.h"
 
 namespace hq {
-
-typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
-typedef float f4_t __attribute__((ext_vector_type(4)));
-typedef int i4_t __attribute__((ext_vector_type(4)));
-typedef int i8_t __attribute__((ext_vector_type(8)));
-typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
-
-__device__ inline float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
-__device__ inline float f16_bits_to_float(uint32_t b) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
-}
-// Round-to-nearest-even fp32 -> bf16 bits (NaN kept quiet).
-__device__ inline uint16_t float_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-__device__ inline uint16_t float_to_f16_bits(float f) {
-  return __builtin_bit_cast(uint16_t, (_Float16)f);  // RNE conversion
-}
 
 template <int FMT>
 struct FmtInfo {
@@ -79,23 +58,11 @@ struct Stage {
 
 template <int FMT>
 __device__ inline f4_t mfma16(u4_t a, u4_t b, f4_t c) {
-  if constexpr (FMT == FMT_W16F16)
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, a),
-                                                  __builtin_bit_cast(h8_t, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8_t, a),
-                                                   __builtin_bit_cast(b8_t, b), c, 0, 0, 0);
+  return mfma_16x16x32<FMT == FMT_W16F16>(a, b, c);
 }
 
-__device__ inline i8_t cat8(u4_t x, u4_t y) {
-  i8_t r;
-  r[0] = x[0]; r[1] = x[1]; r[2] = x[2]; r[3] = x[3];
-  r[4] = y[0]; r[5] = y[1]; r[6] = y[2]; r[7] = y[3];
-  return r;
-}
-
-template <int FMT, int MB, int NB, int STAGES>
-__global__ void __launch_bounds__(512) qgemm_skinny(SkinnyArgs p) {
+template <int FMT, int MB, int NB, int STAGES, int MAXT>
+__global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   using FI = FmtInfo<FMT>;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -134,10 +101,12 @@ __global__ void __launch_bounds__(512) qgemm_skinny(SkinnyArgs p) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) st.a[mb][v] = ap[v];
       } else {
-        const u4_t* ap = reinterpret_cast<const u4_t*>(
-            static_cast<const uint8_t*>(p.a) + (int64_t)arow[mb] * K + g * 128 + 32 * kq);
-        st.a[mb][0] = ap[0];
-        st.a[mb][1] = ap[1];
+        // int8 / fp8 x fp8: the lane's 32 contiguous k.  fp8 x fp4 (MXFP4):
+        // the fp8 operand's registers 0-3 hold k 16 kq + [0,16) and
+        // registers 4-7 hold k 64 + 16 kq + [0,16).
+        const uint8_t* arow8 = static_cast<const uint8_t*>(p.a) + (int64_t)arow[mb] * K + g * 128;
+        st.a[mb][0] = *reinterpret_cast<const u4_t*>(arow8 + (FMT == FMT_F4 ? 16 * kq : 32 * kq));
+        st.a[mb][1] = *reinterpret_cast<const u4_t*>(arow8 + (FMT == FMT_F4 ? 64 + 16 * kq : 32 * kq + 16));
       }
     }
 #pragma unroll
@@ -356,11 +325,23 @@ static hipError_t launch_kernel(Kern kern, dim3 grid, dim3 block, size_t lds, hi
   return hipGetLastError();
 }
 
+// Instantiated shapes: up to 8 waves per workgroup (256 VGPRs per lane) for
+// every (tile_m, tile_n, stages), and 16 waves (128 VGPRs per lane) for one
+// column block of up to 16 rows.
 template <int FMT, int MB, int NB>
 static hipError_t launch_t(const SkinnyCfg& cfg, const SkinnyArgs& a, dim3 grid, dim3 block, size_t lds,
                            hipStream_t s) {
-  if (cfg.stages <= 2) return launch_kernel(qgemm_skinny<FMT, MB, NB, 2>, grid, block, lds, s, a);
-  return launch_kernel(qgemm_skinny<FMT, MB, NB, 4>, grid, block, lds, s, a);
+  if (cfg.waves > 8) {
+    if constexpr (MB == 1 && NB == 1) {
+      if (cfg.stages <= 2) return launch_kernel(qgemm_skinny<FMT, 1, 1, 2, 1024>, grid, block, lds, s, a);
+      return launch_kernel(qgemm_skinny<FMT, 1, 1, 4, 1024>, grid, block, lds, s, a);
+    }
+    return hipErrorInvalidValue;
+  }
+  if (cfg.stages <= 2) return launch_kernel(qgemm_skinny<FMT, MB, NB, 2, 512>, grid, block, lds, s, a);
+  if (cfg.stages <= 4) return launch_kernel(qgemm_skinny<FMT, MB, NB, 4, 512>, grid, block, lds, s, a);
+  if constexpr (MB == 1 && NB <= 2) return launch_kernel(qgemm_skinny<FMT, MB, NB, 8, 512>, grid, block, lds, s, a);
+  return hipErrorInvalidValue;
 }
 
 template <int FMT, int MB>

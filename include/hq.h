@@ -147,8 +147,8 @@ typedef struct hq_compute {
  * Zero in any field means "let the heuristic choose". */
 typedef struct hq_tuning {
   int kernel;  /* 0 auto, 1 skinny (small M, split-K), 2 tiled (large M)  */
-  int tile_m;  /* skinny: rows per workgroup (16, 32, 64); tiled: 64/128/256 */
-  int tile_n;  /* skinny: columns per workgroup (16, 32, 64)              */
+  int tile_m;  /* skinny: rows per workgroup (16, 32, 64); tiled: 64 or 128     */
+  int tile_n;  /* skinny: columns per workgroup (16, 32, 64); tiled: 128, 256 */
   int waves;   /* wavefronts per workgroup                                 */
   int split_k; /* skinny: workgroups sharing one output tile along K      */
   int stages;  /* groups of 128 k kept in flight per wave                  */
@@ -219,6 +219,12 @@ hq_status hq_gemm(const hq_plan* plan, int64_t m, const void* a, const float* a_
  * hipEventElapsedTime gives the kernel's duration.  The request is consumed
  * by that launch; passing NULL, NULL cancels a pending request. */
 hq_status hq_time_next_launch(void* start_event, void* stop_event);
+
+/* Bandwidth probe (measurement helper, not part of the GEMM): read `bytes`
+ * (a multiple of 16) of the device buffer `buf` once with 16-byte loads on
+ * `workgroups` workgroups of 256 threads; `sink` is a device uint32 that is
+ * practically never written.  Honours hq_time_next_launch. */
+hq_status hq_stream_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups, void* stream);
 
 #ifdef __cplusplus
 }

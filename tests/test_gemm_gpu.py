@@ -159,13 +159,14 @@ def test_w4a8_int_accumulators_exact_and_output(M):
     _assert_ok(out.double().cpu().numpy()[rows], ref, "bf16", f"w4a8-int M={M}")
 
 
+@pytest.mark.parametrize("kernel", [1, 2])
 @pytest.mark.parametrize("M", [1, 16, 128, 1024])
-def test_w4a8_mxfp4(M):
+def test_w4a8_mxfp4(M, kernel):
     N, K = 4096, 7168
-    _log(f"w4a8-mxfp4 M={M} N={N} K={K}")
+    _log(f"w4a8-mxfp4 M={M} N={N} K={K} kernel={kernel}")
     d = datagen.w4a8_mxfp4(M, N, K)
     rows = _sample_rows(M)
-    plan = hq.Plan(N, K, hq.w4a8_mxfp4(), max_m=M)
+    plan = hq.Plan(N, K, hq.w4a8_mxfp4(), max_m=M, tuning=dict(kernel=kernel))
     w, meta = plan.repack(torch.from_numpy(d["codes"]).to(DEV), e8m0=torch.from_numpy(d["e8m0"]).to(DEV))
     out = plan.gemm(d["a_codes"].to(DEV), w, meta, a_scale=d["a_scale"].to(DEV))
     torch.cuda.synchronize()
@@ -221,3 +222,61 @@ def test_int8_activation_extremes():
     ref = og.int_accumulators(a.view(np.uint8), codes)
     assert np.array_equal(P.cpu().numpy().astype(np.int64), ref)
     assert int8_value(np.array([128], np.uint8))[0] == -128
+
+
+# --------------------------------------------------------- tiled kernel --
+
+def _w4a16_sampled(M, N, K, act, zp, tuning=None, key=(3,)):
+    _log(f"w4a16 sampled M={M} N={N} K={K} act={act} zp={zp} tuning={tuning}")
+    d = datagen.dense_w4a16(M, N, K, act=act, zp=zp, key=key)
+    rows = _sample_rows(M)
+    zeros = d["zeros"] if zp == "u4" else 8
+    plan = hq.Plan(N, K, hq.w4a16(act=act, zp=zp), max_m=M, tuning=tuning)
+    w, meta = plan.repack(torch.from_numpy(d["codes"]).to(DEV), d["scales"].to(DEV),
+                          torch.from_numpy(d["zeros"]).to(DEV) if zp == "u4" else None)
+    out = plan.gemm(d["a"].to(DEV), w, meta)
+    torch.cuda.synchronize()
+    ref = og.gemm_w4a16(d["a"].double().numpy()[rows], d["codes"], d["scales"].double().numpy(), zeros,
+                        out_fmt=act)
+    return plan.describe(M), _assert_ok(out.double().cpu().numpy()[rows], ref, act, f"w4a16 M={M}")
+
+
+@pytest.mark.parametrize("M", [1024, 4096])
+def test_prefill_fp16_symmetric(M):
+    # M in {1024, 4096}, N = K = 8192, fp16, zero point 8 (sampled rows)
+    desc, _ = _w4a16_sampled(M, 8192, 8192, "f16", "fixed")
+    assert "kernel=tiled" in desc
+
+
+@pytest.mark.parametrize("tuning", [dict(kernel=2, tile_m=64, tile_n=128), dict(kernel=2, tile_m=64, tile_n=256),
+                                    dict(kernel=2, tile_m=128, tile_n=128), dict(kernel=2, tile_m=128, tile_n=256)])
+@pytest.mark.parametrize("act,zp", [("f16", "fixed"), ("bf16", "u4"), ("f16", "u4"), ("bf16", "fixed")])
+def test_tiled_w4a16_shapes(tuning, act, zp):
+    for (M, N, K) in [(200, 512, 1024), (1, 256, 128), (129, 768, 384)]:
+        run_w4a16(M, N, K, act=act, zp=zp, tuning=tuning)
+
+
+@pytest.mark.parametrize("tuning", [dict(kernel=2, tile_m=64, tile_n=256), dict(kernel=2, tile_m=128, tile_n=256),
+                                    dict(kernel=2, tile_m=128, tile_n=128)])
+def test_tiled_w4a8(tuning):
+    M, N, K = 300, 512, 1024
+    _log(f"tiled w4a8 {tuning}")
+    # INT4 x INT8
+    d = datagen.w4a8_int(M, N, K)
+    plan = hq.Plan(N, K, hq.w4a8_int(), max_m=M, tuning=tuning)
+    w, meta = plan.repack(torch.from_numpy(d["codes"]).to(DEV), d["scales"].to(DEV))
+    out = plan.gemm(d["a_codes"].to(DEV), w, meta, a_scale=d["a_scale"].to(DEV))
+    torch.cuda.synchronize()
+    assert "kernel=tiled" in plan.describe(M)
+    ref = og.gemm_int4_int8(d["a_codes"].numpy(), d["a_scale"].numpy(), d["codes"], d["scales"].double().numpy())
+    _assert_ok(out.double().cpu().numpy(), ref, "bf16", "tiled w4a8-int")
+    # INT4 x fp8
+    rng = np.random.default_rng(5)
+    a_codes, a_scale = datagen.quant_per_token(torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)), "fp8")
+    zeros = rng.integers(0, 16, size=(N, K // 128), dtype=np.uint8)
+    plan = hq.Plan(N, K, hq.w4a8_fp8(zp="u4"), max_m=M, tuning=tuning)
+    w, meta = plan.repack(torch.from_numpy(d["codes"]).to(DEV), d["scales"].to(DEV), torch.from_numpy(zeros).to(DEV))
+    out = plan.gemm(a_codes.to(DEV), w, meta, a_scale=a_scale.to(DEV))
+    torch.cuda.synchronize()
+    ref = _fp8_oracle(a_codes.numpy(), a_scale.numpy(), d["codes"], d["scales"].double().numpy(), zeros)
+    _assert_ok(out.double().cpu().numpy(), ref, "bf16", "tiled w4a8-fp8")
