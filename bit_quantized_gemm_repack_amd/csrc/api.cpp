@@ -122,12 +122,14 @@ Exec choose_exec(const hq_plan* p, int64_t m) {
   const int64_t G = p->layer.k / kFragK;
   const hq_tuning& u = p->user;
   e.ws_counter_bytes = align256((size_t)(N / 16) * (size_t)cdiv(p->max_m > 0 ? p->max_m : 1, 16) * 4);
-  // Large M: the MFMA-bound tiled kernel (needs whole 128/256-column tiles).
+  // Large M: the MFMA-bound tiled kernel (needs whole 128/256-column tiles);
+  // also for 33..64 rows when the layer is wide enough to fill the chip.
   const bool tiled_ok = p->compute.epi != HQ_EPI_I32_ACC && N % 128 == 0;
-  if (tiled_ok && (u.kernel == KER_TILED || (u.kernel == 0 && m > 64))) {
+  const bool tiled_auto = m > 64 || (m > 32 && N >= 8192);
+  if (tiled_ok && (u.kernel == KER_TILED || (u.kernel == 0 && tiled_auto))) {
     e.kernel = KER_TILED;
     e.tl.bm = m >= 512 ? 128 : 64;
-    e.tl.nbw = (N % 256 == 0 && !(p->fmt == FMT_W16BF16 && e.tl.bm == 128)) ? 4 : 2;
+    e.tl.nbw = (N % 256 == 0 && m >= 512 && p->fmt != FMT_W16BF16) ? 4 : 2;
     if (u.tile_m) e.tl.bm = u.tile_m;
     if (u.tile_n) e.tl.nbw = u.tile_n / 64;
     e.tiles_m = cdiv(m > 0 ? m : 1, e.tl.bm);
@@ -138,15 +140,22 @@ Exec choose_exec(const hq_plan* p, int64_t m) {
   SkinnyCfg c{};
   c.mb = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
   c.nb = 1;
+  // Rules from a sweep of the decode shapes on MI355X (kernel durations):
+  //   wide layers (>= 512 column blocks): 4 column blocks x 8 waves;
+  //   otherwise one column block per workgroup with K split over 8 waves,
+  //   16 for long K at <= 4 rows; two groups of loads in flight per wave.
+  c.stages = 2;
   if (c.mb == 1) {
-    // one column block per workgroup, K split over up to 16 waves, every
-    // group of a wave in flight at once (stages >= groups per wave)
-    c.waves = (int)std::min<int64_t>(16, std::max<int64_t>(1, G / 2));
-    c.stages = cdiv(G, c.waves) <= 2 ? 2 : 4;
+    if (N / 16 >= 512 && N % 64 == 0) {
+      c.nb = 4;
+      c.waves = 8;
+    } else {
+      c.waves = (G >= 64 && m <= 4) ? 16 : 8;
+    }
   } else {
     c.waves = 8;
-    c.stages = c.mb == 2 ? 4 : 2;
   }
+  c.waves = (int)std::min<int64_t>(c.waves, std::max<int64_t>(1, G));
   if (u.tile_m) c.mb = u.tile_m / 16;
   if (u.tile_n) c.nb = u.tile_n / 16;
   if (u.waves) c.waves = u.waves;

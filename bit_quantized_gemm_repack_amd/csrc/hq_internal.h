@@ -8,24 +8,27 @@
 // stored n-block major: fragment (nb, g) sits at byte ((nb * K/128) + g) * 1024,
 // so one wave walking along K reads one contiguous stream.
 //
-// Lane l of a fragment holds column c = l % 16 and the 32 consecutive k of
-// its quarter kq = l / 16:  k in [128 g + 32 kq, 128 g + 32 kq + 32).  The
-// activation operand of every MFMA used here takes row m = l % 16 and the
-// same k range in lane l, so a lane's A data is one contiguous run of the
-// activation row.  Inside the lane's four 32-bit words (word t covers the
-// 8 k at 32 kq + 8 t), the order of the 8 nibbles depends on the matrix
-// instruction that will consume them, so that one mask (plus one shift)
-// yields a ready operand register:
+// Lane l of a fragment holds column c = l % 16 and 32 of the fragment's 128 k,
+// split in pieces so that, for every load instruction of the activation
+// operand (which takes row m = l % 16 in lane l), the four lanes of one row
+// read one contiguous 64-byte run:
 //
-//   NIB_W16  (fp16 / bf16 MFMA 16x16x32): nibble p holds k-offset
-//            {0,2,4,6,1,3,5,7}[p]; (w >> 4r) & 0x000F000F puts the codes of
-//            k-offsets 2r and 2r+1 in the two 16-bit halves.
-//   NIB_B8   (8-bit operands: int8 MFMA 16x16x64, fp8 scaled MFMA): byte b
-//            of the word holds k-offset b in its low nibble and b+4 in its
-//            high nibble, so w & 0x0F0F0F0F / (w >> 4) & 0x0F0F0F0F (or the
-//            0xF0F0F0F0 forms) give four consecutive k as four bytes.
-//   NIB_NAT  (MXFP4, fp4 operand of the scaled MFMA): nibble p holds
-//            k-offset p, the operand order of E2M1 data.
+//   NIB_W16  (fp16 / bf16 MFMA 16x16x32, 4 steps of 32 k): word t (8 codes)
+//            holds k = 32 t + 8 kq + [0, 8), kq = l / 16; nibble p holds the
+//            k-offset {0,2,4,6,1,3,5,7}[p], so (w >> 4r) & 0x000F000F puts the
+//            codes of k-offsets 2r and 2r+1 in the two 16-bit halves.
+//   NIB_B8   (8-bit operands: int8 MFMA 16x16x64, fp8 scaled MFMA): two
+//            pieces of 16 k, piece h = k 64 h + 16 kq + [0, 16) in words 2h,
+//            2h+1; byte b of word 2h+u holds k-offset 8u + b in its low nibble
+//            and 8u + 4 + b in its high nibble, so w & 0x0F0F0F0F /
+//            (w >> 4) & 0x0F0F0F0F (or the 0xF0F0F0F0 forms) give four
+//            consecutive k as four bytes.
+//   NIB_NAT  (MXFP4, fp4 operand of the scaled MFMA): the 32 consecutive k
+//            [32 kq, 32 kq + 32) of the E8M0 block kq, nibble p of word t
+//            holding k-offset 8 t + p (E2M1 operand order).  The fp8
+//            activation operand of that instruction takes k 16 kq + [0, 16)
+//            in registers 0-3 and 64 + 16 kq + [0, 16) in registers 4-7,
+//            i.e. the same two pieces as NIB_B8.
 //
 // For the int8 MFMA the stored nibble is q ^ 8, the two's-complement int4 of
 // q - 8: placed in the high half of a byte it reads as the int8 16 * (q - 8).
@@ -81,6 +84,13 @@ HQ_HD inline uint32_t canon_code(const uint32_t* codes, int64_t K, int64_t n, in
   return (codes[n * (K / 8) + (k >> 3)] >> (4 * (k & 7))) & 0xFu;
 }
 
+// First k (within the fragment's 128) of word t of the lane quarter kq.
+HQ_HD inline int word_kbase(int order, int kq, int t) {
+  if (order == NIB_W16) return 32 * t + 8 * kq;
+  if (order == NIB_B8) return 64 * (t >> 1) + 16 * kq + 8 * (t & 1);
+  return 32 * kq + 8 * t;
+}
+
 // One 32-bit word of the device layout: word index widx counts 32-bit words
 // from the start of one expert's code region.
 HQ_HD inline uint32_t repack_word(const uint32_t* codes, int64_t K, int fmt, int64_t widx) {
@@ -91,8 +101,8 @@ HQ_HD inline uint32_t repack_word(const uint32_t* codes, int64_t K, int fmt, int
   const int64_t g = frag % G;
   const int64_t nb = frag / G;
   const int64_t n = nb * kFragN + (lane & 15);
-  const int64_t kbase = g * kFragK + 32 * (lane >> 4) + 8 * t;
   const int order = nib_order_of(fmt);
+  const int64_t kbase = g * kFragK + word_kbase(order, lane >> 4, t);
   const uint32_t x = nib_xor_of(fmt);
   uint32_t w = 0;
   for (int p = 0; p < 8; ++p) w |= (canon_code(codes, K, n, kbase + nib_koff(order, p)) ^ x) << (4 * p);

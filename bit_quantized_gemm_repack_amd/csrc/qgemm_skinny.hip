@@ -53,7 +53,8 @@ template <int FMT, int MB, int NB>
 struct Stage {
   u4_t a[MB][FmtInfo<FMT>::kAVec];
   u4_t b[NB];
-  uint32_t meta[NB];
+  uint32_t sraw[NB];  // scale bits, or the E8M0 byte
+  uint32_t zraw[NB];  // zero-point word (8 nibbles), unused with a fixed zero
 };
 
 template <int FMT>
@@ -86,6 +87,8 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   for (int mb = 0; mb < MB; ++mb) arow[mb] = min(m0 + 16 * mb + c, p.M - 1);
 
   const u4_t* wfr = reinterpret_cast<const u4_t*>(p.w);
+  // zero points, or (fixed zero) any readable word array of at least the same size
+  const uint32_t* zsrc = p.zeros ? p.zeros : static_cast<const uint32_t*>(p.scales);
 
   auto load = [&](Stage<FMT, MB, NB>& st, int g) {
 #pragma unroll
@@ -95,32 +98,34 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
+      // Step t of the 16-bit operand: k = 32 t + 8 kq + [0,8); piece h of the
+      // 8-bit operand: k = 64 h + 16 kq + [0,16).  Per load instruction the
+      // four lanes of one row read 64 contiguous bytes.
       if constexpr (FI::kAct16) {
-        const u4_t* ap = reinterpret_cast<const u4_t*>(
-            static_cast<const uint16_t*>(p.a) + (int64_t)arow[mb] * K + g * 128 + 32 * kq);
+        const uint16_t* arow16 = static_cast<const uint16_t*>(p.a) + (int64_t)arow[mb] * K + g * 128 + 8 * kq;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) st.a[mb][v] = ap[v];
+        for (int t = 0; t < 4; ++t) st.a[mb][t] = *reinterpret_cast<const u4_t*>(arow16 + 32 * t);
       } else {
-        // int8 / fp8 x fp8: the lane's 32 contiguous k.  fp8 x fp4 (MXFP4):
-        // the fp8 operand's registers 0-3 hold k 16 kq + [0,16) and
-        // registers 4-7 hold k 64 + 16 kq + [0,16).
-        const uint8_t* arow8 = static_cast<const uint8_t*>(p.a) + (int64_t)arow[mb] * K + g * 128;
-        st.a[mb][0] = *reinterpret_cast<const u4_t*>(arow8 + (FMT == FMT_F4 ? 16 * kq : 32 * kq));
-        st.a[mb][1] = *reinterpret_cast<const u4_t*>(arow8 + (FMT == FMT_F4 ? 64 + 16 * kq : 32 * kq + 16));
+        const uint8_t* arow8 = static_cast<const uint8_t*>(p.a) + (int64_t)arow[mb] * K + g * 128 + 16 * kq;
+        st.a[mb][0] = *reinterpret_cast<const u4_t*>(arow8);
+        st.a[mb][1] = *reinterpret_cast<const u4_t*>(arow8 + 64);
       }
     }
+    // Metadata loads are unconditional and decoded only at compute time, so
+    // that no wait is needed until the stage's math.
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int64_t rec = (int64_t)(nt * NB + nb) * G + g;
       if constexpr (FMT == FMT_F4) {
-        st.meta[nb] = p.e8m0[rec * 64 + lane];
+        st.sraw[nb] = p.e8m0[rec * 64 + lane];
       } else {
-        uint32_t s = static_cast<const uint16_t*>(p.scales)[rec * 16 + c];
-        uint32_t z = (uint32_t)p.zp_fixed;
-        if (p.zp_fixed < 0) z = (p.zeros[rec * 2 + (c >> 3)] >> (4 * (c & 7))) & 0xFu;
-        st.meta[nb] = s | (z << 16);
+        st.sraw[nb] = static_cast<const uint16_t*>(p.scales)[rec * 16 + c];
+        st.zraw[nb] = zsrc[rec * 2 + (c >> 3)];
       }
     }
+  };
+  auto zero_of = [&](const Stage<FMT, MB, NB>& st, int nb) -> uint32_t {
+    return p.zp_fixed < 0 ? (st.zraw[nb] >> (4 * (c & 7))) & 0xFu : (uint32_t)p.zp_fixed;
   };
 
   f4_t acc[MB][NB];
@@ -166,9 +171,8 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) P[mb] = mfma16<FMT>(st.a[mb][t], bop, P[mb]);
         }
-        const uint32_t meta = st.meta[nb];
-        const float s = p.scale_bf16 ? bf16_bits_to_float(meta & 0xFFFFu) : f16_bits_to_float(meta & 0xFFFFu);
-        const float cz = off + (float)(meta >> 16);
+        const float s = p.scale_bf16 ? bf16_bits_to_float(st.sraw[nb]) : f16_bits_to_float(st.sraw[nb]);
+        const float cz = off + (float)zero_of(st, nb);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -178,9 +182,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
                              (int)((w[1] << 4) & 0xF0F0F0F0u), (int)(w[1] & 0xF0F0F0F0u)};
         const i4_t b1 = i4_t{(int)((w[2] << 4) & 0xF0F0F0F0u), (int)(w[2] & 0xF0F0F0F0u),
                              (int)((w[3] << 4) & 0xF0F0F0F0u), (int)(w[3] & 0xF0F0F0F0u)};
-        const uint32_t meta = st.meta[nb];
-        const float s16 = 0.0625f * (p.scale_bf16 ? bf16_bits_to_float(meta & 0xFFFFu)
-                                                  : f16_bits_to_float(meta & 0xFFFFu));
+        const float s16 = 0.0625f * (p.scale_bf16 ? bf16_bits_to_float(st.sraw[nb]) : f16_bits_to_float(st.sraw[nb]));
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           i4_t P = i4_t{0, 0, 0, 0};
@@ -202,9 +204,8 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
                               (int)(w[1] & 0x0F0F0F0Fu), (int)((w[1] >> 4) & 0x0F0F0F0Fu),
                               (int)(w[2] & 0x0F0F0F0Fu), (int)((w[2] >> 4) & 0x0F0F0F0Fu),
                               (int)(w[3] & 0x0F0F0F0Fu), (int)((w[3] >> 4) & 0x0F0F0F0Fu)};
-        const uint32_t meta = st.meta[nb];
-        const float s = p.scale_bf16 ? bf16_bits_to_float(meta & 0xFFFFu) : f16_bits_to_float(meta & 0xFFFFu);
-        const float z = (float)(meta >> 16);
+        const float s = p.scale_bf16 ? bf16_bits_to_float(st.sraw[nb]) : f16_bits_to_float(st.sraw[nb]);
+        const float z = (float)zero_of(st, nb);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           // codes 0x00..0x0F are q * 2^-9 in e4m3; block scale 2^9 (E8M0 136) undoes it
@@ -215,7 +216,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
         }
       } else {  // FMT_F4
         const i8_t bop = i8_t{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
-        const int sb = (int)st.meta[nb];
+        const int sb = (int)st.sraw[nb];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
           acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -226,18 +227,19 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   };
 
   // Software pipeline: STAGES groups of loads in flight ahead of the math.
+  // Loads are issued without branches (a load past the end of this wave's
+  // range re-reads group g_dummy, an in-range fragment that stays hot in L2)
+  // so that the wait before each stage's math counts only that stage's loads.
+  const int g_dummy = min(g_beg, G - 1);
+  auto group_of = [&](int it) { return it < n_it ? my_first + it * W : g_dummy; };
   Stage<FMT, MB, NB> st[STAGES];
 #pragma unroll
-  for (int d = 0; d < STAGES; ++d)
-    if (d < n_it) load(st[d], my_first + d * W);
+  for (int d = 0; d < STAGES; ++d) load(st[d], group_of(d));
   for (int i = 0; i < n_it; i += STAGES) {
 #pragma unroll
     for (int d = 0; d < STAGES; ++d) {
-      if (i + d < n_it) {
-        const int g = my_first + (i + d) * W;
-        compute(st[d], g);
-        if (i + d + STAGES < n_it) load(st[d], g + STAGES * W);
-      }
+      if (i + d < n_it) compute(st[d], my_first + (i + d) * W);
+      load(st[d], group_of(i + d + STAGES));
     }
   }
 

@@ -108,7 +108,10 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
   // ---- weight fragments + group metadata of this wave -----------------------
   const u4_t* wfr = reinterpret_cast<const u4_t*>(p.w);
   u4_t braw[2][NBW];
-  uint32_t bmeta[2][NBW];
+  uint32_t sraw[2][NBW], zraw[2][NBW];
+  // zero points, or (fixed zero) any readable word array of at least the same size
+  const uint32_t* zsrc = p.zeros ? p.zeros : static_cast<const uint32_t*>(p.scales);
+  // Loads are unconditional and decoded only in the math (no early waits).
   auto load_b = [&](auto slot_c, int g) {
     constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
@@ -116,14 +119,15 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
       const int64_t rec = (int64_t)(nblk0 + j) * G + g;
       braw[slot][j] = __builtin_nontemporal_load(wfr + rec * 64 + lane);
       if constexpr (FMT == FMT_F4) {
-        bmeta[slot][j] = p.e8m0[rec * 64 + lane];
+        sraw[slot][j] = p.e8m0[rec * 64 + lane];
       } else {
-        uint32_t s = static_cast<const uint16_t*>(p.scales)[rec * 16 + c];
-        uint32_t z = (uint32_t)p.zp_fixed;
-        if (p.zp_fixed < 0) z = (p.zeros[rec * 2 + (c >> 3)] >> (4 * (c & 7))) & 0xFu;
-        bmeta[slot][j] = s | (z << 16);
+        sraw[slot][j] = static_cast<const uint16_t*>(p.scales)[rec * 16 + c];
+        zraw[slot][j] = zsrc[rec * 2 + (c >> 3)];
       }
     }
+  };
+  auto zero_of = [&](uint32_t zw) -> uint32_t {
+    return p.zp_fixed < 0 ? (zw >> (4 * (c & 7))) & 0xFu : (uint32_t)p.zp_fixed;
   };
 
   f4_t acc[C::MB][NBW];
@@ -133,24 +137,20 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
     for (int j = 0; j < NBW; ++j) acc[mb][j] = f4_t{0.f, 0.f, 0.f, 0.f};
 
   // Operand fetch of m-block mb from LDS stage `buf`: this lane's row
-  // r = 16 mb + c and its 32 k (64 B for 16-bit, 32 B for 8-bit activations).
+  // r = 16 mb + c.  16-bit: step t takes k = 32 t + 8 kq + [0,8) (16-byte
+  // chunk 4 t + kq of the row); 8-bit: piece h takes k = 64 h + 16 kq + [0,16)
+  // (chunk 4 h + kq).
   auto read_a16 = [&](int buf, int mb, u4_t (&a)[4]) {
     const int r = 16 * mb + c;
     const uint8_t* base = lds + buf * C::STAGE_BYTES + r * C::ROWB;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const u4_t*>(base + swz<true>(r, 4 * kq + t) * 16);
+    for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const u4_t*>(base + swz<true>(r, 4 * t + kq) * 16);
   };
-  // 8-bit operands: the int8 and fp8 x fp8 MFMAs pair A byte j with B byte j
-  // of the same lane, so a lane takes its 32 contiguous k; with an fp4 B
-  // operand the fp8 A registers 0-3 hold k 16 kq + [0,16) and registers 4-7
-  // hold k 64 + 16 kq + [0,16) (16-byte chunks kq and 4 + kq of the row).
   auto read_a8 = [&](int buf, int mb, u4_t (&a)[2]) {
     const int r = 16 * mb + c;
     const uint8_t* base = lds + buf * C::STAGE_BYTES + r * C::ROWB;
-    const int c0 = FMT == FMT_F4 ? kq : 2 * kq;
-    const int c1 = FMT == FMT_F4 ? 4 + kq : 2 * kq + 1;
-    a[0] = *reinterpret_cast<const u4_t*>(base + swz<false>(r, c0) * 16);
-    a[1] = *reinterpret_cast<const u4_t*>(base + swz<false>(r, c1) * 16);
+    a[0] = *reinterpret_cast<const u4_t*>(base + swz<false>(r, kq) * 16);
+    a[1] = *reinterpret_cast<const u4_t*>(base + swz<false>(r, 4 + kq) * 16);
   };
 
   auto compute = [&](auto slot_c) {
@@ -160,9 +160,8 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
       u4_t bop[NBW][4];
 #pragma unroll
       for (int j = 0; j < NBW; ++j) {
-        const uint32_t meta = bmeta[slot][j];
-        const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)(meta & 0xFFFFu));
-        const _Float16 cz = -(_Float16)(1024 + (int)(meta >> 16));
+        const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)sraw[slot][j]);
+        const _Float16 cz = -(_Float16)(1024 + (int)zero_of(zraw[slot][j]));
         const h2_t s2 = h2_t{s, s};
         const h2_t c2 = h2_t{cz, cz};
 #pragma unroll
@@ -192,9 +191,8 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
       float sj[NBW], cj[NBW];
 #pragma unroll
       for (int j = 0; j < NBW; ++j) {
-        const uint32_t meta = bmeta[slot][j];
-        sj[j] = p.scale_bf16 ? bf16_bits_to_float(meta & 0xFFFFu) : f16_bits_to_float(meta & 0xFFFFu);
-        cj[j] = 128.f + (float)(meta >> 16);
+        sj[j] = p.scale_bf16 ? bf16_bits_to_float(sraw[slot][j]) : f16_bits_to_float(sraw[slot][j]);
+        cj[j] = 128.f + (float)zero_of(zraw[slot][j]);
 #pragma unroll
         for (int t = 0; t < 4; ++t) bop[j][t] = w16_operand(braw[slot][j][t], 0x43004300u);
       }
@@ -220,8 +218,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
       float sj[NBW];
 #pragma unroll
       for (int j = 0; j < NBW; ++j) {
-        const uint32_t meta = bmeta[slot][j];
-        sj[j] = 0.0625f * (p.scale_bf16 ? bf16_bits_to_float(meta & 0xFFFFu) : f16_bits_to_float(meta & 0xFFFFu));
+        sj[j] = 0.0625f * (p.scale_bf16 ? bf16_bits_to_float(sraw[slot][j]) : f16_bits_to_float(sraw[slot][j]));
         bop[j][0] = i8_operand(braw[slot][j][0], braw[slot][j][1]);
         bop[j][1] = i8_operand(braw[slot][j][2], braw[slot][j][3]);
       }
@@ -243,9 +240,8 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
       float sj[NBW], zj[NBW];
 #pragma unroll
       for (int j = 0; j < NBW; ++j) {
-        const uint32_t meta = bmeta[slot][j];
-        sj[j] = p.scale_bf16 ? bf16_bits_to_float(meta & 0xFFFFu) : f16_bits_to_float(meta & 0xFFFFu);
-        zj[j] = (float)(meta >> 16);
+        sj[j] = p.scale_bf16 ? bf16_bits_to_float(sraw[slot][j]) : f16_bits_to_float(sraw[slot][j]);
+        zj[j] = (float)zero_of(zraw[slot][j]);
         bop[j] = q8_operand(braw[slot][j]);
       }
       const i8_t ones = i8_t{0x38383838, 0x38383838, 0x38383838, 0x38383838,
@@ -276,7 +272,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
           const u4_t w = braw[slot][j];
           const i8_t bv = i8_t{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
           acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mb][j], 0, 4, 0, 127, 0,
-                                                                        (int)bmeta[slot][j]);
+                                                                        (int)sraw[slot][j]);
         }
       }
     }
@@ -286,16 +282,17 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
   // that every register array is indexed with compile-time constants --------
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
+  // The next group's loads are issued without a branch (the last step
+  // re-reads group G-1, which is in L2) so that the waits inside the math
+  // count only LDS traffic, not the loads in flight.
   auto step = [&](auto slot_c, int g) {
     constexpr int cur = decltype(slot_c)::value;
     using Next = std::integral_constant<int, 1 - cur>;
-    const bool more = (g + 1) < G;
-    if (more) {
-      load_a(g + 1);
-      load_b(Next{}, g + 1);
-    }
+    const int gn = min(g + 1, G - 1);
+    load_a(gn);
+    load_b(Next{}, gn);
     compute(slot_c);
-    if (more) store_a(1 - cur);
+    store_a(1 - cur);
     __syncthreads();
   };
   load_a(0);

@@ -8,8 +8,10 @@
   on the GPU) produces the operand order each matrix instruction needs.  The
   requirement is restated here from the MFMA operand definitions, not from the
   library's code: lane l of the 16 x 128 fragment (nb, g) serves column
-  16 nb + l % 16 and the k range [128 g + 32 (l // 16), +32); every extracted
-  operand register must hold the codes of the k its activation partner holds.
+  16 nb + l % 16, and every extracted operand register must hold the codes of
+  the k its activation partner in the same lane holds (16-bit step t:
+  k = 32 t + 8 (l // 16) + [0, 8); 8-bit piece h: k = 64 h + 16 (l // 16) +
+  [0, 16)); MXFP4 lanes hold the E8M0 block [128 g + 32 (l // 16), +32).
 """
 import ctypes
 
@@ -145,6 +147,16 @@ def _lane_k(g, lane):
     return 128 * g + 32 * (lane // 16)
 
 
+# k of each activation-operand piece, per lane quarter kq = lane // 16:
+# 16-bit MFMA step t: 32 t + 8 kq + [0, 8); 8-bit piece h: 64 h + 16 kq + [0, 16)
+def _k16(g, lane, t):
+    return 128 * g + 32 * t + 8 * (lane // 16)
+
+
+def _k8(g, lane, h):
+    return 128 * g + 64 * h + 16 * (lane // 16)
+
+
 def test_repack_w16_operand_order():
     q, codes = _codes(1)
     p = _plan(N, K, hq.w4a16("f16"), max_m=16)
@@ -153,13 +165,14 @@ def test_repack_w16_operand_order():
     for nb in range(N // 16):
         for g in range(K // 128):
             for lane in range(64):
-                n, k0 = 16 * nb + lane % 16, _lane_k(g, lane)
+                n = 16 * nb + lane % 16
                 for t in range(4):
                     x = int(fw[nb, g, lane, t])
+                    k0 = _k16(g, lane, t)
                     for r in range(4):  # operand register r: 16-bit halves = k-offsets 2r, 2r+1
                         v = (x >> (4 * r)) & 0x000F000F
-                        assert v & 0xF == q[n, k0 + 8 * t + 2 * r]
-                        assert v >> 16 == q[n, k0 + 8 * t + 2 * r + 1]
+                        assert v & 0xF == q[n, k0 + 2 * r]
+                        assert v >> 16 == q[n, k0 + 2 * r + 1]
 
 
 def test_repack_int8_operand_order():
@@ -170,15 +183,16 @@ def test_repack_int8_operand_order():
     for nb in range(N // 16):
         for g in range(K // 128):
             for lane in range(64):
-                n, k0 = 16 * nb + lane % 16, _lane_k(g, lane)
+                n = 16 * nb + lane % 16
                 for step in range(2):  # int8 MFMA 16x16x64: 16 k per lane per step
+                    k0 = _k8(g, lane, step)
                     w0, w1 = int(fw[nb, g, lane, 2 * step]), int(fw[nb, g, lane, 2 * step + 1])
                     regs = [(w0 << 4) & 0xF0F0F0F0, w0 & 0xF0F0F0F0, (w1 << 4) & 0xF0F0F0F0, w1 & 0xF0F0F0F0]
                     for j, reg in enumerate(regs):
                         for b in range(4):
                             byte = (reg >> (8 * b)) & 0xFF
                             val = byte - 256 if byte >= 128 else byte
-                            assert val == 16 * (int(q[n, k0 + 16 * step + 4 * j + b]) - 8)
+                            assert val == 16 * (int(q[n, k0 + 4 * j + b]) - 8)
 
 
 def test_repack_fp8_operand_order():
@@ -189,12 +203,13 @@ def test_repack_fp8_operand_order():
     for nb in range(N // 16):
         for g in range(K // 128):
             for lane in range(64):
-                n, k0 = 16 * nb + lane % 16, _lane_k(g, lane)
+                n = 16 * nb + lane % 16
                 for t in range(4):  # operand registers 2t, 2t+1 of the 8-register fp8 operand
                     x = int(fw[nb, g, lane, t])
+                    k0 = _k8(g, lane, t // 2) + 8 * (t % 2)
                     for h, reg in enumerate((x & 0x0F0F0F0F, (x >> 4) & 0x0F0F0F0F)):
                         for b in range(4):
-                            assert (reg >> (8 * b)) & 0xFF == q[n, k0 + 8 * t + 4 * h + b]
+                            assert (reg >> (8 * b)) & 0xFF == q[n, k0 + 4 * h + b]
 
 
 def test_repack_mxfp4_operand_order_and_e8m0():
