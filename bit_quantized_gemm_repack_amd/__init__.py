@@ -115,6 +115,15 @@ _SIGS = {
     "hq_repack": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 5 + [ctypes.c_void_p]),
     "hq_repack_host": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 5),
     "hq_time_next_launch": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
+    "hq_moe_block_m": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]),
+    "hq_moe_max_padded": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.POINTER(ctypes.c_int64)]),
+    "hq_moe_align": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int] +
+                     [ctypes.c_void_p] * 5),
+    "hq_moe_workspace_bytes": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                              ctypes.POINTER(ctypes.c_size_t)]),
+    "hq_moe_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int] + [ctypes.c_void_p] * 11 +
+                    [ctypes.c_size_t, ctypes.c_void_p]),
     "hq_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
                                       ctypes.c_void_p]),
     "hq_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
@@ -290,3 +299,80 @@ def stream_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int, nbytes: 
     _dev(buf, "buf"), _dev(sink, "sink")
     n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
     _check(lib().hq_stream_read(_ptr(buf), n, _ptr(sink), int(workgroups), _stream_ptr(buf.device)))
+
+
+# ------------------------------------------------------------------- MoE --
+def moe_max_padded(t: int, topk: int, num_experts: int, block_m: int) -> int:
+    v = ctypes.c_int64()
+    _check(lib().hq_moe_max_padded(int(t), int(topk), int(num_experts), int(block_m), ctypes.byref(v)))
+    return v.value
+
+
+def moe_align(topk_ids: torch.Tensor, num_experts: int, block_m: int):
+    """Token sort / align by expert (see hq_moe_align).  topk_ids: int32 [t, topk] on the GPU.
+    Returns (sorted_ids, block_expert, num_padded) device int32 tensors."""
+    _dev(topk_ids, "topk_ids")
+    if topk_ids.dtype != torch.int32 or topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be int32 [t, topk]")
+    t, topk = topk_ids.shape
+    mp = moe_max_padded(t, topk, num_experts, block_m)
+    dev = topk_ids.device
+    sorted_ids = torch.empty(mp, dtype=torch.int32, device=dev)
+    block_expert = torch.empty(max(mp // block_m, 1), dtype=torch.int32, device=dev)
+    num_padded = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(lib().hq_moe_align(t, topk, int(num_experts), int(block_m), _ptr(topk_ids), _ptr(sorted_ids),
+                              _ptr(block_expert), _ptr(num_padded), _stream_ptr(dev)))
+    return sorted_ids, block_expert, num_padded
+
+
+class MoePlan(Plan):
+    """A grouped plan: num_experts weights of [n, k]; epi one of 'silu_mul',
+    'silu_mul_qfp8' (gate_up), 'topk_combine' (down) or 'none'."""
+
+    def __init__(self, n: int, k: int, quant: QuantDesc, num_experts: int, max_t: int, epi: str,
+                 tuning: Optional[dict] = None):
+        super().__init__(n, k, quant, max_m=max_t, epi=epi, kind="grouped", num_experts=num_experts, tuning=tuning)
+
+    def block_m(self, t: int, topk: int) -> int:
+        v = ctypes.c_int()
+        _check(lib().hq_moe_block_m(self._h, int(t), int(topk), ctypes.byref(v)))
+        return v.value
+
+    def moe_workspace(self, t: int, topk: int, device) -> Optional[torch.Tensor]:
+        b = ctypes.c_size_t()
+        _check(lib().hq_moe_workspace_bytes(self._h, int(t), int(topk), ctypes.byref(b)))
+        if b.value == 0:
+            return None
+        dev = torch.device(device)
+        ws = self._ws.get(dev)
+        if ws is None or ws.numel() < b.value:
+            ws = torch.zeros(b.value, dtype=torch.uint8, device=dev)
+            self._ws[dev] = ws
+        return ws
+
+    def moe_gemm(self, a: torch.Tensor, t: int, topk: int, sorted_ids: torch.Tensor, block_expert: torch.Tensor,
+                 num_padded: torch.Tensor, w: torch.Tensor, meta: torch.Tensor, a_scale=None, topk_w=None,
+                 out=None, out_scale=None, ws=None):
+        for x, nm in ((a, "a"), (sorted_ids, "sorted_ids"), (block_expert, "block_expert"),
+                      (num_padded, "num_padded"), (w, "w"), (meta, "meta")):
+            _dev(x, nm)
+        dev = a.device
+        mp = sorted_ids.numel()
+        if out is None:
+            if self.epi == EPI_TOPK_COMBINE:
+                out = torch.empty((t, self.n), dtype=_TORCH_OUT[self.quant.out], device=dev)
+            elif self.epi == EPI_SILU_MUL_QFP8:
+                out = torch.empty((mp, self.n // 2), dtype=torch.uint8, device=dev)
+            elif self.epi == EPI_SILU_MUL:
+                out = torch.empty((mp, self.n // 2), dtype=_TORCH_OUT[self.quant.out], device=dev)
+            else:
+                out = torch.empty((mp, self.n), dtype=_TORCH_OUT[self.quant.out], device=dev)
+        if self.epi == EPI_SILU_MUL_QFP8 and out_scale is None:
+            out_scale = torch.empty(mp, dtype=torch.float32, device=dev)
+        if ws is None:
+            ws = self.moe_workspace(t, topk, dev)
+        ws_bytes = 0 if ws is None else ws.numel()
+        _check(lib().hq_moe_gemm(self._h, int(t), int(topk), _ptr(a), _ptr(a_scale), _ptr(sorted_ids),
+                                 _ptr(block_expert), _ptr(num_padded), _ptr(topk_w), _ptr(w), _ptr(meta), _ptr(out),
+                                 _ptr(out_scale), _ptr(ws), ws_bytes, _stream_ptr(dev)))
+        return (out, out_scale) if self.epi == EPI_SILU_MUL_QFP8 else out

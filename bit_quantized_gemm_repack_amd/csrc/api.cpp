@@ -264,11 +264,20 @@ hq_status hq_plan_create(const hq_layer_desc* layer, const hq_compute* compute, 
       case HQ_EPI_SILU_MUL:
       case HQ_EPI_SILU_MUL_QFP8:
       case HQ_EPI_TOPK_COMBINE:
-        return fail(HQ_ERR_UNSUPPORTED, "grouped epilogues are not available on dense plans");
+        if (compute->kind != HQ_GEMM_GROUPED)
+          return fail(HQ_ERR_UNSUPPORTED, "grouped epilogues are not available on dense plans");
+        break;
       default:
         return fail(HQ_ERR_INVALID_ARG, "unknown epilogue");
     }
-    if (compute->kind == HQ_GEMM_GROUPED) return fail(HQ_ERR_UNSUPPORTED, "grouped GEMM is not implemented yet");
+    if (compute->kind == HQ_GEMM_GROUPED) {
+      if (fmt != hq::FMT_W16F16 && fmt != hq::FMT_W16BF16 && fmt != hq::FMT_Q8)
+        return fail(HQ_ERR_UNSUPPORTED, "grouped GEMM supports INT4 weights with fp16/bf16/fp8 activations");
+      if ((compute->epi == HQ_EPI_SILU_MUL || compute->epi == HQ_EPI_SILU_MUL_QFP8) && layer->n % 32)
+        return fail(HQ_ERR_UNSUPPORTED, "SiLU * mul needs n (gate + up) a multiple of 32");
+      if (compute->epi == HQ_EPI_TOPK_COMBINE && layer->n % 64)
+        return fail(HQ_ERR_UNSUPPORTED, "the combining down GEMM needs n a multiple of 64");
+    }
     hq_plan* p = new (std::nothrow) hq_plan();
     if (!p) return fail(HQ_ERR_INTERNAL, "out of host memory");
     p->layer = *layer;
@@ -287,7 +296,7 @@ hq_status hq_plan_create(const hq_layer_desc* layer, const hq_compute* compute, 
       if (layer->q.zp == HQ_ZP_PER_GROUP_U4) p->meta_bytes_per_expert += (size_t)((N / 16) * G * 8);
     }
     hq::Exec e = hq::choose_exec(p, max_m > 0 ? max_m : 1);
-    s = check_exec(p, e);
+    s = compute->kind == HQ_GEMM_GROUPED ? HQ_OK : check_exec(p, e);
     if (s != HQ_OK) {
       delete p;
       return s;
@@ -482,6 +491,175 @@ hq_status hq_gemm(const hq_plan* p, int64_t m, const void* a, const float* a_sca
     return ok();
   } catch (...) {
     return fail(HQ_ERR_INTERNAL, "exception in hq_gemm");
+  }
+}
+
+// ---------------------------------------------------------------------------
+// grouped (MoE)
+// ---------------------------------------------------------------------------
+
+static int64_t moe_max_padded(int64_t t, int topk, int E, int bm) {
+  const int64_t raw = t * topk + (int64_t)E * (bm - 1);
+  return (raw + bm - 1) / bm * bm;
+}
+
+static int moe_block_m(const hq_plan* p) { return p->user.tile_m ? p->user.tile_m : 16; }
+
+static hq::SkinnyCfg moe_cfg(const hq_plan* p) {
+  hq::SkinnyCfg c{};
+  c.mb = 1;
+  c.nb = (p->compute.epi == HQ_EPI_TOPK_COMBINE || p->compute.epi == HQ_EPI_NONE) ? 4 : 2;
+  if (p->compute.epi == HQ_EPI_NONE && p->layer.n % 64) c.nb = 1;
+  const int64_t G = p->layer.k / 128;
+  c.waves = (int)std::min<int64_t>(8, std::max<int64_t>(1, G));
+  c.stages = 2;
+  c.split = 1;
+  return c;
+}
+
+hq_status hq_moe_block_m(const hq_plan* p, int64_t t, int topk, int* block_m) {
+  if (!p || !block_m) return fail(HQ_ERR_INVALID_ARG, "null argument");
+  if (p->compute.kind != HQ_GEMM_GROUPED) return fail(HQ_ERR_INVALID_ARG, "not a grouped plan");
+  (void)t;
+  (void)topk;
+  *block_m = moe_block_m(p);
+  return ok();
+}
+
+hq_status hq_moe_max_padded(int64_t t, int topk, int num_experts, int block_m, int64_t* max_padded) {
+  if (!max_padded) return fail(HQ_ERR_INVALID_ARG, "null argument");
+  if (t < 0 || topk < 1 || num_experts < 1 || block_m < 1) return fail(HQ_ERR_INVALID_ARG, "bad sizes");
+  *max_padded = moe_max_padded(t, topk, num_experts, block_m);
+  return ok();
+}
+
+hq_status hq_moe_align(int64_t t, int topk, int num_experts, int block_m, const int32_t* topk_ids,
+                       int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded, void* stream) {
+  try {
+    if (!topk_ids || !sorted_ids || !block_expert || !num_padded) return fail(HQ_ERR_INVALID_ARG, "null pointer");
+    if (t < 1 || topk < 1 || num_experts < 1 || block_m < 1) return fail(HQ_ERR_INVALID_ARG, "bad sizes");
+    if (t * topk > (int64_t(1) << 20)) return fail(HQ_ERR_UNSUPPORTED, "t * topk above 2^20");
+    if (num_experts > 4096) return fail(HQ_ERR_UNSUPPORTED, "more than 4096 experts");
+    if (block_m % 16) return fail(HQ_ERR_INVALID_ARG, "block_m must be a multiple of 16");
+    int err = hq::launch_moe_align(t, topk, num_experts, block_m, topk_ids, sorted_ids, block_expert, num_padded,
+                                   stream);
+    if (err != hipSuccess) return fail(HQ_ERR_HIP, "align launch: %s", hipGetErrorString((hipError_t)err));
+    return ok();
+  } catch (...) {
+    return fail(HQ_ERR_INTERNAL, "exception in hq_moe_align");
+  }
+}
+
+struct MoeWs {
+  size_t act32, amax, y32, total;
+};
+
+static MoeWs moe_ws(const hq_plan* p, int64_t t, int topk) {
+  MoeWs w{};
+  const int64_t mp = moe_max_padded(t, topk, p->layer.num_experts, moe_block_m(p));
+  if (p->compute.epi == HQ_EPI_SILU_MUL_QFP8) {
+    w.act32 = align256((size_t)mp * (size_t)(p->layer.n / 2) * 4);
+    w.amax = align256((size_t)mp * 4);
+  }
+  if (p->compute.epi == HQ_EPI_TOPK_COMBINE) w.y32 = align256((size_t)t * (size_t)p->layer.n * 4);
+  w.total = w.act32 + w.amax + w.y32;
+  return w;
+}
+
+hq_status hq_moe_workspace_bytes(const hq_plan* p, int64_t t, int topk, size_t* bytes) {
+  if (!p || !bytes) return fail(HQ_ERR_INVALID_ARG, "null argument");
+  if (p->compute.kind != HQ_GEMM_GROUPED) return fail(HQ_ERR_INVALID_ARG, "not a grouped plan");
+  if (t < 0 || t > p->max_m || topk < 1) return fail(HQ_ERR_INVALID_ARG, "t out of range [0, max_m]");
+  *bytes = moe_ws(p, t, topk).total;
+  return ok();
+}
+
+hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, const float* a_scale,
+                      const int32_t* sorted_ids, const int32_t* block_expert, const int32_t* num_padded,
+                      const float* topk_w, const void* w, const void* meta, void* out, float* out_scale, void* ws,
+                      size_t ws_bytes, void* stream) {
+  try {
+    if (!p) return fail(HQ_ERR_INVALID_ARG, "null plan");
+    if (p->compute.kind != HQ_GEMM_GROUPED) return fail(HQ_ERR_INVALID_ARG, "hq_moe_gemm needs a grouped plan");
+    if (t < 0 || t > p->max_m) return fail(HQ_ERR_INVALID_ARG, "t out of range [0, max_m]");
+    if (topk < 1 || topk > 64) return fail(HQ_ERR_INVALID_ARG, "topk must be 1..64");
+    if (t == 0) return ok();
+    if (!a || !sorted_ids || !block_expert || !num_padded || !w || !meta || !out)
+      return fail(HQ_ERR_INVALID_ARG, "null device pointer");
+    if (!aligned16(a) || !aligned16(w) || !aligned16(meta) || !aligned16(out))
+      return fail(HQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+    const bool act8 = p->fmt == hq::FMT_Q8;
+    if (act8 && !a_scale) return fail(HQ_ERR_INVALID_ARG, "8-bit activations need a_scale");
+    if (!act8 && a_scale) return fail(HQ_ERR_INVALID_ARG, "16-bit activations take no a_scale");
+    const int epi = p->compute.epi;
+    if (epi == HQ_EPI_TOPK_COMBINE && !topk_w) return fail(HQ_ERR_INVALID_ARG, "the combine needs topk_w");
+    if (epi == HQ_EPI_SILU_MUL_QFP8 && !out_scale) return fail(HQ_ERR_INVALID_ARG, "fp8 requant needs out_scale");
+    const MoeWs mw = moe_ws(p, t, topk);
+    if (mw.total > 0) {
+      if (!ws) return fail(HQ_ERR_WORKSPACE, "this call needs %zu workspace bytes", mw.total);
+      if (ws_bytes < mw.total) return fail(HQ_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, mw.total);
+      if (!aligned16(ws)) return fail(HQ_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    }
+    const int64_t N = p->layer.n, K = p->layer.k, G = K / 128;
+    const int bm = moe_block_m(p);
+    const int64_t mp = moe_max_padded(t, topk, p->layer.num_experts, bm);
+    hq::SkinnyCfg c = moe_cfg(p);
+    hq::SkinnyArgs s{};
+    s.a = a;
+    s.a_scale = a_scale;
+    s.w = w;
+    s.scales = meta;
+    s.zeros = p->layer.q.zp == HQ_ZP_PER_GROUP_U4
+                  ? reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(meta) +
+                                                      p->scale_region_bytes * (size_t)p->layer.num_experts)
+                  : nullptr;
+    s.out = out;
+    s.M = (int)mp;
+    s.N = (int)N;
+    s.K = (int)K;
+    s.G = (int)G;
+    s.zp_fixed = p->layer.q.zp == HQ_ZP_FIXED ? p->layer.q.zp_value : -1;
+    s.scale_bf16 = p->layer.q.scale == HQ_BF16;
+    s.out_bf16 = p->layer.q.out == HQ_BF16;
+    s.gps = (int)G;
+    s.sorted_ids = sorted_ids;
+    s.block_expert = block_expert;
+    s.num_padded = num_padded;
+    s.topk_w = topk_w;
+    s.topk = topk;
+    s.n_slots = (int)(t * topk);
+    s.half_nblk = (int)(N / 2 / 16);
+    s.w_expert = (int64_t)p->w_bytes_per_expert;
+    s.s_expert = (int64_t)(N * G);
+    s.z_expert = (int64_t)((N / 16) * G * 2);
+    s.e8_expert = (int64_t)(N * K / 32);
+    uint8_t* wsb = static_cast<uint8_t*>(ws);
+    int mode = hq::GRP_GATHER;
+    switch (epi) {
+      case HQ_EPI_NONE: s.epi = hq::GEPI_PLAIN; break;
+      case HQ_EPI_SILU_MUL: s.epi = hq::GEPI_SILU; break;
+      case HQ_EPI_SILU_MUL_QFP8:
+        s.epi = hq::GEPI_SILU_F32;
+        s.f32_out = reinterpret_cast<float*>(wsb);
+        s.row_amax = reinterpret_cast<uint32_t*>(wsb + mw.act32);
+        break;
+      case HQ_EPI_TOPK_COMBINE:
+        s.epi = hq::GEPI_COMBINE;
+        mode = hq::GRP_SORTED;
+        s.f32_out = reinterpret_cast<float*>(wsb);
+        break;
+      default: return fail(HQ_ERR_INVALID_ARG, "unsupported grouped epilogue");
+    }
+    int err = hq::launch_skinny_grouped(p->fmt, mode, c, s, mp / 16, stream);
+    if (err == hipSuccess && epi == HQ_EPI_SILU_MUL_QFP8)
+      err = hq::launch_moe_requant(s.f32_out, s.row_amax, sorted_ids, num_padded, s.n_slots, (int)(N / 2), mp,
+                                   static_cast<uint8_t*>(out), out_scale, stream);
+    if (err == hipSuccess && epi == HQ_EPI_TOPK_COMBINE)
+      err = hq::launch_moe_finalize(s.f32_out, out, t * N, s.out_bf16, stream);
+    if (err != hipSuccess) return fail(HQ_ERR_HIP, "grouped gemm launch: %s", hipGetErrorString((hipError_t)err));
+    return ok();
+  } catch (...) {
+    return fail(HQ_ERR_INTERNAL, "exception in hq_moe_gemm");
   }
 }
 

@@ -204,9 +204,38 @@ struct SkinnyArgs {
   int out_bf16;      // output dtype: 1 bf16, 0 fp16
   int i32_out;       // write per-group int32 accumulators instead of C
   int gps;           // groups per split
+  // ---- grouped (MoE) mode ----
+  const int32_t* sorted_ids;    // aligned slot ids (sentinel n_slots)
+  const int32_t* block_expert;  // expert of each aligned block
+  const int32_t* num_padded;    // used length of sorted_ids
+  const float* topk_w;          // [t, topk] routing weights (combine)
+  int topk;
+  int n_slots;                  // t * topk
+  int epi;                      // EPI_* below
+  int half_nblk;                // (n / 2) / 16: first up-projection column block
+  int64_t w_expert;             // repacked code bytes per expert
+  int64_t s_expert;             // scale elements per expert
+  int64_t z_expert;             // zero-point words per expert
+  int64_t e8_expert;            // E8M0 bytes per expert
+  float* f32_out;               // gate_up fp32 act (QFP8) or down fp32 token accumulators
+  uint32_t* row_amax;           // gate_up QFP8: per aligned row max |act| (float bits)
 };
 
+// Grouped epilogues (SkinnyArgs::epi / TiledArgs::epi).
+enum GroupedEpi : int { GEPI_PLAIN = 0, GEPI_SILU = 1, GEPI_SILU_F32 = 2, GEPI_COMBINE = 3 };
+// Grouped kernel modes (template parameter): 0 dense, 1 rows gathered by
+// token (gate_up), 2 rows in aligned order (down).
+enum GroupedMode : int { GRP_DENSE = 0, GRP_GATHER = 1, GRP_SORTED = 2 };
+
 int launch_skinny(int fmt, const SkinnyCfg& cfg, const SkinnyArgs& a, void* stream);
+// Grouped launch: grid.z = blocks of the aligned array (max_padded / (16 mb)).
+int launch_skinny_grouped(int fmt, int mode, const SkinnyCfg& cfg, const SkinnyArgs& a, int64_t blocks,
+                          void* stream);
+int launch_moe_align(int64_t t, int topk, int num_experts, int block_m, const int32_t* ids, int32_t* sorted_ids,
+                     int32_t* block_expert, int32_t* num_padded, void* stream);
+int launch_moe_requant(const float* act32, uint32_t* row_amax, const int32_t* sorted_ids, const int32_t* num_padded,
+                       int n_slots, int inter, int64_t max_rows, uint8_t* codes, float* scales, void* stream);
+int launch_moe_finalize(float* y32, void* y, int64_t elems, int out_bf16, void* stream);
 
 struct TiledArgs {
   const void* a;

@@ -62,7 +62,11 @@ __device__ inline f4_t mfma16(u4_t a, u4_t b, f4_t c) {
   return mfma_16x16x32<FMT == FMT_W16F16>(a, b, c);
 }
 
-template <int FMT, int MB, int NB, int STAGES, int MAXT>
+// GRP selects the row / weight indexing: GRP_DENSE (rows 0..M-1, one weight),
+// GRP_GATHER (MoE gate_up: block z of the expert-aligned slot array, rows are
+// the slots' tokens, weights of the block's expert) or GRP_SORTED (MoE down:
+// rows are the aligned slots themselves).
+template <int FMT, int MB, int NB, int STAGES, int MAXT, int GRP>
 __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   using FI = FmtInfo<FMT>;
   const int lane = threadIdx.x & 63;
@@ -76,24 +80,62 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   const int G = p.G;
   const int K = p.K;
 
+  // Grouped mode: skip blocks past the aligned length; point at this block's
+  // expert.  gate_up pairs gate column block j with up column block
+  // half_nblk + j inside one workgroup (first NB/2 blocks gate, rest up).
+  const uint8_t* wbytes = static_cast<const uint8_t*>(p.w);
+  const uint16_t* scales16 = static_cast<const uint16_t*>(p.scales);
+  const uint32_t* zeros32 = p.zeros;
+  const uint8_t* e8 = p.e8m0;
+  [[maybe_unused]] bool paired = false;
+  if constexpr (GRP != GRP_DENSE) {
+    if (m0 >= *p.num_padded) return;
+    const int64_t ex = p.block_expert[blockIdx.z];
+    wbytes += ex * p.w_expert;
+    if constexpr (FMT == FMT_F4) {
+      e8 += ex * p.e8_expert;
+    } else {
+      scales16 += ex * p.s_expert;
+      if (zeros32) zeros32 += ex * p.z_expert;
+    }
+    paired = GRP == GRP_GATHER && (p.epi == GEPI_SILU || p.epi == GEPI_SILU_F32);
+  }
+  auto nblk = [&](int nb) -> int {
+    if constexpr (GRP == GRP_GATHER) {
+      if (paired) return nb < NB / 2 ? nt * (NB / 2) + nb : p.half_nblk + nt * (NB / 2) + (nb - NB / 2);
+    }
+    return nt * NB + nb;
+  };
+
   const int g_beg = split * p.gps;
   const int g_end = min(G, g_beg + p.gps);
   const int my_first = g_beg + wave;
   const int n_it = (my_first < g_end) ? (g_end - my_first + W - 1) / W : 0;
 
-  // Row each lane loads for each m-block (clamped into [0, M)).
+  // Row each lane loads for each m-block: dense rows clamped into [0, M);
+  // gathered slots read their token (padding slots read token 0, their
+  // results are dropped); aligned rows read themselves.
   int arow[MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) arow[mb] = min(m0 + 16 * mb + c, p.M - 1);
+  for (int mb = 0; mb < MB; ++mb) {
+    if constexpr (GRP == GRP_DENSE) {
+      arow[mb] = min(m0 + 16 * mb + c, p.M - 1);
+    } else if constexpr (GRP == GRP_GATHER) {
+      const int id = p.sorted_ids[m0 + 16 * mb + c];
+      arow[mb] = id < p.n_slots ? id / p.topk : 0;
+    } else {
+      arow[mb] = m0 + 16 * mb + c;
+    }
+  }
 
-  const u4_t* wfr = reinterpret_cast<const u4_t*>(p.w);
+  const u4_t* wfr = reinterpret_cast<const u4_t*>(wbytes);
   // zero points, or (fixed zero) any readable word array of at least the same size
-  const uint32_t* zsrc = p.zeros ? p.zeros : static_cast<const uint32_t*>(p.scales);
+  const uint32_t* zsrc = zeros32 ? zeros32 : reinterpret_cast<const uint32_t*>(scales16);
 
   auto load = [&](Stage<FMT, MB, NB>& st, int g) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int64_t frag = (int64_t)(nt * NB + nb) * G + g;
+      const int64_t frag = (int64_t)nblk(nb) * G + g;
       st.b[nb] = __builtin_nontemporal_load(wfr + frag * 64 + lane);
     }
 #pragma unroll
@@ -115,11 +157,11 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
     // that no wait is needed until the stage's math.
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int64_t rec = (int64_t)(nt * NB + nb) * G + g;
+      const int64_t rec = (int64_t)nblk(nb) * G + g;
       if constexpr (FMT == FMT_F4) {
-        st.sraw[nb] = p.e8m0[rec * 64 + lane];
+        st.sraw[nb] = e8[rec * 64 + lane];
       } else {
-        st.sraw[nb] = static_cast<const uint16_t*>(p.scales)[rec * 16 + c];
+        st.sraw[nb] = scales16[rec * 16 + c];
         st.zraw[nb] = zsrc[rec * 2 + (c >> 3)];
       }
     }
@@ -267,7 +309,36 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
     const int nb = (idx >> 2) % NB;
     const int mb = (idx >> 2) / NB;
     const int m = m0 + 16 * mb + 4 * (l >> 4) + r;
-    const int n = (nt * NB + nb) * 16 + (l & 15);
+    const int n = nblk(nb) * 16 + (l & 15);
+    if constexpr (GRP != GRP_DENSE) {
+      // m is the row of the aligned slot array; padding slots are dropped
+      const int id = p.sorted_ids[m];
+      if (id >= p.n_slots) continue;
+      const int tok = id / p.topk;
+      if constexpr (GRP == GRP_GATHER) {
+        const float sa = FI::kActScale ? p.a_scale[tok] : 1.f;
+        if (paired) {
+          if (nb >= NB / 2) continue;
+          float u = 0.f;  // the up projection of the same row and column
+          for (int w = 0; w < W; ++w) u += red[w * E * 64 + e + (NB / 2) * 4 * 64];
+          const float gv = v * sa;
+          const float act = gv / (1.f + expf(-gv)) * (u * sa);  // SiLU(gate) * up
+          const int half = p.N / 2;
+          if (p.epi == GEPI_SILU) {
+            store_out(p.out, (int64_t)m * half + n, act, p.out_bf16);
+          } else {
+            p.f32_out[(int64_t)m * half + n] = act;
+            atomicMax(p.row_amax + m, __float_as_uint(fabsf(act)));
+          }
+        } else {
+          store_out(p.out, (int64_t)m * p.N + n, v * sa, p.out_bf16);
+        }
+      } else {
+        const float sa = FI::kActScale ? p.a_scale[m] : 1.f;
+        atomicAdd(p.f32_out + (int64_t)tok * p.N + n, v * sa * p.topk_w[id]);
+      }
+      continue;
+    }
     if (m >= p.M) continue;
     if (S == 1) {
       if (FI::kActScale) v *= p.a_scale[m];
@@ -277,7 +348,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
       p.part[((int64_t)split * p.M + m) * p.N + n] = v;
     }
   }
-  if (S == 1) return;
+  if (GRP != GRP_DENSE || S == 1) return;
 
   // ---- cross-workgroup split-K: the last workgroup to arrive finishes ----
   __shared__ int is_last;
@@ -335,14 +406,15 @@ static hipError_t launch_t(const SkinnyCfg& cfg, const SkinnyArgs& a, dim3 grid,
                            hipStream_t s) {
   if (cfg.waves > 8) {
     if constexpr (MB == 1 && NB == 1) {
-      if (cfg.stages <= 2) return launch_kernel(qgemm_skinny<FMT, 1, 1, 2, 1024>, grid, block, lds, s, a);
-      return launch_kernel(qgemm_skinny<FMT, 1, 1, 4, 1024>, grid, block, lds, s, a);
+      if (cfg.stages <= 2) return launch_kernel(qgemm_skinny<FMT, 1, 1, 2, 1024, GRP_DENSE>, grid, block, lds, s, a);
+      return launch_kernel(qgemm_skinny<FMT, 1, 1, 4, 1024, GRP_DENSE>, grid, block, lds, s, a);
     }
     return hipErrorInvalidValue;
   }
-  if (cfg.stages <= 2) return launch_kernel(qgemm_skinny<FMT, MB, NB, 2, 512>, grid, block, lds, s, a);
-  if (cfg.stages <= 4) return launch_kernel(qgemm_skinny<FMT, MB, NB, 4, 512>, grid, block, lds, s, a);
-  if constexpr (MB == 1 && NB <= 2) return launch_kernel(qgemm_skinny<FMT, MB, NB, 8, 512>, grid, block, lds, s, a);
+  if (cfg.stages <= 2) return launch_kernel(qgemm_skinny<FMT, MB, NB, 2, 512, GRP_DENSE>, grid, block, lds, s, a);
+  if (cfg.stages <= 4) return launch_kernel(qgemm_skinny<FMT, MB, NB, 4, 512, GRP_DENSE>, grid, block, lds, s, a);
+  if constexpr (MB == 1 && NB <= 2)
+    return launch_kernel(qgemm_skinny<FMT, MB, NB, 8, 512, GRP_DENSE>, grid, block, lds, s, a);
   return hipErrorInvalidValue;
 }
 
@@ -366,6 +438,41 @@ static hipError_t launch_mb(const SkinnyCfg& cfg, const SkinnyArgs& a, dim3 grid
     case 4: return launch_nb<FMT, 4>(cfg, a, grid, block, lds, s);
   }
   return hipErrorInvalidValue;
+}
+
+// Grouped instantiations: 16-row expert blocks, 2 (gate_up pair) or 4
+// column blocks, two groups of loads in flight, up to 8 waves.
+template <int FMT, int GRP>
+static hipError_t launch_grouped_t(const SkinnyCfg& cfg, const SkinnyArgs& a, dim3 grid, dim3 block, size_t lds,
+                                   hipStream_t s) {
+  if (cfg.mb != 1 || cfg.stages != 2 || cfg.waves > 8) return hipErrorInvalidValue;
+  if (cfg.nb == 2) return launch_kernel(qgemm_skinny<FMT, 1, 2, 2, 512, GRP>, grid, block, lds, s, a);
+  if (cfg.nb == 4) return launch_kernel(qgemm_skinny<FMT, 1, 4, 2, 512, GRP>, grid, block, lds, s, a);
+  return hipErrorInvalidValue;
+}
+
+template <int FMT>
+static hipError_t launch_grouped_f(int mode, const SkinnyCfg& cfg, const SkinnyArgs& a, dim3 grid, dim3 block,
+                                   size_t lds, hipStream_t s) {
+  if (mode == GRP_GATHER) return launch_grouped_t<FMT, GRP_GATHER>(cfg, a, grid, block, lds, s);
+  if (mode == GRP_SORTED) return launch_grouped_t<FMT, GRP_SORTED>(cfg, a, grid, block, lds, s);
+  return hipErrorInvalidValue;
+}
+
+int launch_skinny_grouped(int fmt, int mode, const SkinnyCfg& cfg, const SkinnyArgs& a, int64_t blocks,
+                          void* stream) {
+  const bool paired = mode == GRP_GATHER && (a.epi == GEPI_SILU || a.epi == GEPI_SILU_F32);
+  const int ntiles = paired ? (a.N / 2) / (16 * (cfg.nb / 2)) : a.N / (16 * cfg.nb);
+  dim3 grid(ntiles, 1, (unsigned)blocks);
+  dim3 block(64 * cfg.waves);
+  const size_t lds = (size_t)cfg.waves * cfg.mb * cfg.nb * 4 * 64 * sizeof(float);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (fmt) {
+    case FMT_W16F16: return (int)launch_grouped_f<FMT_W16F16>(mode, cfg, a, grid, block, lds, s);
+    case FMT_W16BF16: return (int)launch_grouped_f<FMT_W16BF16>(mode, cfg, a, grid, block, lds, s);
+    case FMT_Q8: return (int)launch_grouped_f<FMT_Q8>(mode, cfg, a, grid, block, lds, s);
+  }
+  return (int)hipErrorInvalidValue;
 }
 
 int launch_skinny(int fmt, const SkinnyCfg& cfg, const SkinnyArgs& a, void* stream) {

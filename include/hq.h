@@ -213,6 +213,59 @@ hq_status hq_gemm(const hq_plan* plan, int64_t m, const void* a, const float* a_
                   const void* w, const void* meta, void* out, void* ws, size_t ws_bytes,
                   void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Grouped (mixture-of-experts) path.  The pages describe a separate MoE
+ * backend with its own "Grouped" GEMM path run with W4A16 or W4A8 weights
+ * (Humming page on news.ditty.ir, summary; cocoloop.cn speed-up table).  A
+ * layer is: routing ids -> hq_moe_align -> gate_up GEMM (+ SiLU * mul, or +
+ * per-row fp8 requant) -> down GEMM (+ top-k weighted combine into tokens).
+ * ------------------------------------------------------------------------- */
+
+/* Rows per expert block that a grouped plan's kernels use for `t` tokens;
+ * hq_moe_align must be called with this block_m. */
+hq_status hq_moe_block_m(const hq_plan* plan, int64_t t, int topk, int* block_m);
+
+/* Size of the aligned slot array for `t` tokens: the largest possible
+ * sum over experts of count_e rounded up to block_m, i.e.
+ * t*topk + num_experts*(block_m - 1) rounded up to block_m. */
+hq_status hq_moe_max_padded(int64_t t, int topk, int num_experts, int block_m, int64_t* max_padded);
+
+/* Token sort / align by expert.  topk_ids: device int32 [t, topk], each in
+ * [0, num_experts).  Outputs (device, int32): sorted_ids[max_padded]: flat
+ * slot indices t*topk + j grouped by expert, each expert's segment padded to
+ * a multiple of block_m with the sentinel t*topk (order inside a segment is
+ * unspecified); block_expert[max_padded / block_m]: the expert of each block;
+ * num_padded[1]: the used length.  One workgroup; t * topk <= 2^20. */
+hq_status hq_moe_align(int64_t t, int topk, int num_experts, int block_m, const int32_t* topk_ids,
+                       int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded, void* stream);
+
+/* Grouped GEMM over the aligned blocks (plan kind HQ_GEMM_GROUPED, layer n x k
+ * per expert, num_experts experts, weights repacked by hq_repack).
+ *   epi HQ_EPI_SILU_MUL       gate_up: row r of the aligned array takes token
+ *                             sorted_ids[r] / topk of `a` [t, k];
+ *                             out[max_padded, n/2] (plan out dtype) =
+ *                             SiLU(h[:, :n/2]) * h[:, n/2:].
+ *   epi HQ_EPI_SILU_MUL_QFP8  as above, then per-row fp8 e4m3 requant:
+ *                             out = uint8 codes [max_padded, n/2], out_scale =
+ *                             fp32 [max_padded], s = max|act| / 448 (1 for an
+ *                             all-zero row), codes = RNE(act / s).
+ *   epi HQ_EPI_TOPK_COMBINE   down: row r of `a` [max_padded, k] is the
+ *                             intermediate of slot sorted_ids[r];
+ *                             out = y [t, n] (plan out dtype),
+ *                             y[tok] = sum_j topk_w[tok, j] * (a_row . W_e^T)
+ *                             accumulated in fp32.
+ *   epi HQ_EPI_NONE           gate_up rows without the activation: out
+ *                             [max_padded, n] (plan out dtype).
+ * a_scale: per-row fp32 scales of 8-bit activations (per token for gate_up,
+ * per aligned row for down), else NULL.  topk_w: device fp32 [t, topk]
+ * (TOPK_COMBINE only).  Rows of padding slots are left unwritten.  ws: the
+ * workspace of hq_moe_workspace_bytes, zero-filled once before first use. */
+hq_status hq_moe_workspace_bytes(const hq_plan* plan, int64_t t, int topk, size_t* bytes);
+hq_status hq_moe_gemm(const hq_plan* plan, int64_t t, int topk, const void* a, const float* a_scale,
+                      const int32_t* sorted_ids, const int32_t* block_expert, const int32_t* num_padded,
+                      const float* topk_w, const void* w, const void* meta, void* out, float* out_scale,
+                      void* ws, size_t ws_bytes, void* stream);
+
 /* Kernel timing: the next GEMM kernel this thread launches records `start`
  * and `stop` (hipEvent_t, created by the caller with timing enabled) around
  * its own execution (the dispatch's start and end, without launch gaps), so

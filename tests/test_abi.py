@@ -262,3 +262,57 @@ def test_repack_is_a_bijection_on_codes():
             w, _ = p.repack_host(codes, **kw)
             dev = unpack_u4(w.numpy().view(np.int32).reshape(1, -1))[0]
             assert np.array_equal(np.bincount(dev, minlength=16), np.bincount(q.reshape(-1), minlength=16))
+
+
+# ------------------------------------------------------------------- MoE ----
+
+def test_moe_plan_validation():
+    with pytest.raises(hq.HQError) as e:   # grouped + INT4 x INT8 not implemented
+        hq.MoePlan(512, 7168, hq.w4a8_int(), 256, 64, "silu_mul")
+    assert e.value.status == hq.HQ_ERR_UNSUPPORTED
+    with pytest.raises(hq.HQError) as e:   # gate + up must pair 16-column blocks
+        hq.MoePlan(48, 256, hq.w4a16("bf16"), 4, 64, "silu_mul")
+    assert e.value.status == hq.HQ_ERR_UNSUPPORTED
+    with pytest.raises(hq.HQError):         # combine epilogue on a dense plan
+        hq.Plan(512, 256, hq.w4a16("bf16"), max_m=4, epi="topk_combine")
+    p = hq.MoePlan(512, 7168, hq.w4a16("bf16", scale="f16"), 256, 64, "silu_mul")
+    assert p.block_m(32, 8) == 16
+    assert p.repacked_bytes() == (256 * 512 * 7168 // 2, 256 * 512 * 56 * 2)
+
+
+def test_moe_sizes_and_workspace():
+    assert hq.moe_max_padded(1, 8, 256, 16) == 8 + 256 * 15 + 8  # rounded up to 16
+    assert hq.moe_max_padded(4096, 8, 256, 16) == 32768 + 256 * 15
+    pq = hq.MoePlan(512, 7168, hq.w4a8_fp8(), 256, 4096, "silu_mul_qfp8")
+    b = ctypes.c_size_t()
+    assert hq.lib().hq_moe_workspace_bytes(pq._h, 32, 8, ctypes.byref(b)) == 0
+    mp = hq.moe_max_padded(32, 8, 256, 16)
+    assert b.value >= mp * 256 * 4 + mp * 4
+    pc = hq.MoePlan(7168, 256, hq.w4a16("bf16", scale="f16"), 256, 4096, "topk_combine")
+    assert hq.lib().hq_moe_workspace_bytes(pc._h, 32, 8, ctypes.byref(b)) == 0 and b.value >= 32 * 7168 * 4
+
+
+def test_moe_call_validation():
+    L = hq.lib()
+    A = 0x10000
+    assert L.hq_moe_align(0, 8, 256, 16, A, A, A, A, None) == hq.HQ_ERR_INVALID_ARG
+    assert L.hq_moe_align(4, 8, 256, 10, A, A, A, A, None) == hq.HQ_ERR_INVALID_ARG   # block_m % 16
+    assert L.hq_moe_align(4, 8, 256, 16, None, A, A, A, None) == hq.HQ_ERR_INVALID_ARG
+    p = hq.MoePlan(7168, 256, hq.w4a16("bf16", scale="f16"), 256, 64, "topk_combine")
+    # pointer arguments: a, a_scale, sorted_ids, block_expert, num_padded, topk_w, w, meta, out, out_scale, ws
+    def args(**kw):
+        names = ["a", "a_scale", "sorted_ids", "block_expert", "num_padded", "topk_w", "w", "meta", "out",
+                 "out_scale", "ws"]
+        d = {n: A for n in names}
+        d["a_scale"] = None
+        d["out_scale"] = None
+        d.update(kw)
+        return [d[n] for n in names]
+    assert L.hq_moe_gemm(p._h, 4, 8, *args(topk_w=None), 1 << 30, None) == hq.HQ_ERR_INVALID_ARG
+    assert L.hq_moe_gemm(p._h, 4, 8, *args(a_scale=A), 1 << 30, None) == hq.HQ_ERR_INVALID_ARG
+    assert L.hq_moe_gemm(p._h, 4, 8, *args(), 16, None) == hq.HQ_ERR_WORKSPACE   # workspace too small
+    assert L.hq_moe_gemm(p._h, 4, 8, *args(ws=None), 1 << 30, None) == hq.HQ_ERR_WORKSPACE
+    assert L.hq_moe_gemm(p._h, 65, 8, *args(), 1 << 30, None) == hq.HQ_ERR_INVALID_ARG  # t > max_t
+    assert L.hq_moe_gemm(p._h, 4, 8, *args(w=A + 8), 1 << 30, None) == hq.HQ_ERR_INVALID_ARG  # misaligned
+    pq = hq.MoePlan(512, 7168, hq.w4a8_fp8(), 256, 64, "silu_mul_qfp8")
+    assert L.hq_moe_gemm(pq._h, 4, 8, *args(a_scale=A), 1 << 30, None) == hq.HQ_ERR_INVALID_ARG  # no out_scale

@@ -1,0 +1,165 @@
+"""MoE parity on the GPU: hq_moe_align, the grouped gate_up (+ SiLU * mul, or
++ per-row fp8 requant) and the grouped down + top-k combine, each checked on
+the GPU's own input to that stage against the CPU oracle (oracle/moe.py).
+
+Layer: one GPU's tensor-parallel share of a DeepSeek-style layer -- 256
+experts, top-8 of softmax(router logits ~ N(0,1)), hidden 7168, expert
+intermediate 256 (gate_up N=512 K=7168; down N=7168 K=256), INT4 weights with
+group 128, fp16 scales and zero point 8, activations bf16 or fp8 e4m3 with
+per-token scales -- for T in {1, 32, 512, 4096} tokens (sampled tokens at the
+larger T), plus a small layer checked on every token.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_gemm_repack_amd as hq
+import datagen
+from oracle import gemm as og
+from oracle import moe as om
+from oracle.formats import e4m3_value
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+E_FULL, H_FULL, I_FULL, TOPK = 256, 7168, 256, 8
+
+
+def _log(msg):
+    print(f"[gpu case] {msg}", flush=True)
+
+
+# ------------------------------------------------------------------ align --
+
+@pytest.mark.parametrize("T", [1, 32, 512, 4096])
+def test_align_invariants(T):
+    _log(f"moe align T={T}")
+    r = datagen.moe_routing(T)
+    ids = torch.from_numpy(r["topk_ids"]).to(DEV)
+    sid, bexp, npad = hq.moe_align(ids, E_FULL, 16)
+    torch.cuda.synchronize()
+    om.check_align(r["topk_ids"], E_FULL, 16, sid.cpu().numpy(), bexp.cpu().numpy(), npad.cpu().numpy())
+
+
+def test_align_degenerate_cases():
+    _log("moe align degenerate")
+    # every slot on one expert; one expert only; block of 64
+    ids = np.full((100, 4), 3, dtype=np.int32)
+    sid, bexp, npad = hq.moe_align(torch.from_numpy(ids).to(DEV), 8, 16)
+    torch.cuda.synchronize()
+    om.check_align(ids, 8, 16, sid.cpu().numpy(), bexp.cpu().numpy(), npad.cpu().numpy())
+    ids1 = np.zeros((7, 1), dtype=np.int32)
+    sid, bexp, npad = hq.moe_align(torch.from_numpy(ids1).to(DEV), 1, 64)
+    torch.cuda.synchronize()
+    om.check_align(ids1, 1, 64, sid.cpu().numpy(), bexp.cpu().numpy(), npad.cpu().numpy())
+
+
+# --------------------------------------------------------- layer pipeline --
+
+def _quant(act):
+    return hq.w4a16("bf16", scale="f16") if act == "bf16" else hq.w4a8_fp8(scale="f16")
+
+
+class Layer:
+    """Weights on the GPU (repacked for both activation types) + host copies."""
+
+    def __init__(self, E, H, I, key):
+        self.E, self.H, self.I = E, H, I
+        wts = datagen.moe_weights(E, H, I, key=key)
+        self.w = wts
+        self.dev = {}
+        for act in ("bf16", "fp8"):
+            p1 = hq.MoePlan(2 * I, H, _quant(act), E, 4096, "silu_mul" if act == "bf16" else "silu_mul_qfp8")
+            p2 = hq.MoePlan(H, I, _quant(act), E, 4096, "topk_combine")
+            w1, m1 = p1.repack(torch.from_numpy(wts["w1"]).to(DEV), wts["s1"].to(DEV))
+            w2, m2 = p2.repack(torch.from_numpy(wts["w2"]).to(DEV), wts["s2"].to(DEV))
+            self.dev[act] = (p1, p2, w1, m1, w2, m2)
+        torch.cuda.synchronize()
+
+
+def run_layer(layer, T, act, topk, key=(5,), sample=None):
+    """Run align -> gate_up -> down on the GPU; check every stage on sampled tokens."""
+    E, H, I = layer.E, layer.H, layer.I
+    _log(f"moe layer E={E} H={H} I={I} T={T} topk={topk} act={act}")
+    r = datagen.moe_routing(T, E=E, topk=topk, key=key)
+    x = datagen.moe_activations(T, H=H, act=act, key=key)
+    p1, p2, w1, m1, w2, m2 = layer.dev[act]
+    ids = torch.from_numpy(r["topk_ids"]).to(DEV)
+    bm = p1.block_m(T, topk)
+    sid, bexp, npad = hq.moe_align(ids, E, bm)
+    if act == "bf16":
+        a = x["x"].to(DEV)
+        act_out = p1.moe_gemm(a, T, topk, sid, bexp, npad, w1, m1)
+        y = p2.moe_gemm(act_out, T, topk, sid, bexp, npad, w2, m2, topk_w=torch.from_numpy(r["topk_w"]).to(DEV))
+    else:
+        a = x["x_codes"].to(DEV)
+        codes, scl = p1.moe_gemm(a, T, topk, sid, bexp, npad, w1, m1, a_scale=x["x_scale"].to(DEV))
+        y = p2.moe_gemm(codes, T, topk, sid, bexp, npad, w2, m2, a_scale=scl,
+                        topk_w=torch.from_numpy(r["topk_w"]).to(DEV))
+    torch.cuda.synchronize()
+    sid_h, bexp_h, npad_h = sid.cpu().numpy(), bexp.cpu().numpy(), int(npad.cpu().numpy()[0])
+    om.check_align(r["topk_ids"], E, bm, sid_h, bexp_h, np.array([npad_h]))
+
+    toks = np.arange(T) if sample is None or T <= sample else \
+        np.sort(np.random.default_rng(T).choice(T, sample, replace=False))
+    tokset = set(int(t) for t in toks)
+    rows = [i for i in range(npad_h) if sid_h[i] < T * topk and int(sid_h[i]) // topk in tokset]
+    rows = np.array(rows, dtype=np.int64)
+    slot = sid_h[rows]
+    row_tok = slot // topk
+    row_exp = bexp_h[rows // bm]
+    assert np.array_equal(row_exp, r["topk_ids"].reshape(-1)[slot])
+
+    # gate_up: oracle on the GPU's stage input (the same x)
+    if act == "bf16":
+        xa = x["x"].double().numpy()[row_tok]
+    else:
+        xa = e4m3_value(x["x_codes"].numpy()[row_tok]) * x["x_scale"].numpy()[row_tok, None].astype(np.float64)
+    gu = om.gate_up(xa, row_exp, layer.w["w1"], layer.w["s1"].double().numpy(), I)
+    if act == "bf16":
+        act_gpu = act_out.double().cpu().numpy()[rows]
+        ok, _, ratio = og.check(act_gpu, gu["act"], gu["tau_act"], "bf16")
+        assert ok.all(), f"gate_up act: {(~ok).sum()} bad, max err/tau {ratio.max():.3g}"
+        act_rows = act_gpu
+    else:
+        dq = e4m3_value(codes.cpu().numpy()[rows]) * scl.cpu().numpy()[rows, None].astype(np.float64)
+        bound = om.fp8_rows_bound(dq, scl.cpu().numpy()[rows], gu["act"], gu["tau_act"])
+        err = np.abs(dq - gu["act"])
+        assert (err <= bound).all(), f"fp8 requant: {(err > bound).sum()} bad"
+        act_rows = dq
+    # down + combine: oracle on the GPU's act rows, for the sampled tokens
+    dc = om.down_combine(act_rows, row_tok, r["topk_w"].reshape(-1)[slot], row_exp, layer.w["w2"],
+                         layer.w["s2"].double().numpy(), T)
+    y_gpu = y.double().cpu().numpy()[toks]
+    ok, _, ratio = og.check(y_gpu, dc["y64"][toks], dc["tau_y"][toks], "bf16")
+    assert ok.all(), f"down+combine: {(~ok).sum()} bad, max err/tau {ratio.max():.3g}"
+    return ratio.max()
+
+
+@pytest.fixture(scope="module")
+def small_layer():
+    return Layer(8, 512, 128, key=(7,))
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp8"])
+@pytest.mark.parametrize("T,topk", [(1, 2), (37, 2), (200, 3), (5, 8)])
+def test_small_layer_all_tokens(small_layer, T, topk, act):
+    run_layer(small_layer, T, act, topk, key=(11,))
+
+
+def test_small_layer_repeat_calls_reuse_workspace(small_layer):
+    # the fp32 combine accumulators and row maxima re-arm themselves: calls
+    # in a row on the same workspace all pass
+    for act in ("fp8", "bf16", "fp8"):
+        run_layer(small_layer, 64, act, 2, key=(13,))
+
+
+@pytest.fixture(scope="module")
+def full_layer():
+    _log("generating the 256-expert layer")
+    return Layer(E_FULL, H_FULL, I_FULL, key=(5,))
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp8"])
+@pytest.mark.parametrize("T", [1, 32, 512, 4096])
+def test_full_layer(full_layer, T, act):
+    run_layer(full_layer, T, act, TOPK, sample=12)
