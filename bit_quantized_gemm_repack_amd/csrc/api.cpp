@@ -650,10 +650,14 @@ hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, cons
         break;
       default: return fail(HQ_ERR_INVALID_ARG, "unsupported grouped epilogue");
     }
-    int err = hq::launch_skinny_grouped(p->fmt, mode, c, s, mp / 16, stream);
+    // Non-empty blocks: each holds at least one slot, so at most t * topk of
+    // them exist whatever the routing; the grid covers min(that, all blocks).
+    const int64_t blocks = std::min<int64_t>(mp / 16, t * topk);
+    int err = hq::launch_skinny_grouped(p->fmt, mode, c, s, blocks, stream);
     if (err == hipSuccess && epi == HQ_EPI_SILU_MUL_QFP8)
-      err = hq::launch_moe_requant(s.f32_out, s.row_amax, sorted_ids, num_padded, s.n_slots, (int)(N / 2), mp,
-                                   static_cast<uint8_t*>(out), out_scale, stream);
+      err = hq::launch_moe_requant(s.f32_out, s.row_amax, sorted_ids, num_padded, s.n_slots, (int)(N / 2),
+                                   std::min<int64_t>(mp, 16 * t * topk), static_cast<uint8_t*>(out), out_scale,
+                                   stream);
     if (err == hipSuccess && epi == HQ_EPI_TOPK_COMBINE)
       err = hq::launch_moe_finalize(s.f32_out, out, t * N, s.out_bf16, stream);
     if (err != hipSuccess) return fail(HQ_ERR_HIP, "grouped gemm launch: %s", hipGetErrorString((hipError_t)err));

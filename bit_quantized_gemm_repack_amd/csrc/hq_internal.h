@@ -250,9 +250,24 @@ struct TiledArgs {
   int scale_bf16;
   int out_bf16;
   int tiles_m, tiles_n;
+  // ---- grouped (MoE) mode: the same fields as SkinnyArgs ----
+  const int32_t* sorted_ids;
+  const int32_t* block_expert;
+  const int32_t* num_padded;
+  const float* topk_w;
+  int topk;
+  int n_slots;
+  int epi;
+  int half_nblk;
+  int64_t w_expert, s_expert, z_expert, e8_expert;
+  float* f32_out;
+  uint32_t* row_amax;
 };
 
 int launch_tiled(int fmt, const TiledCfgRt& cfg, const TiledArgs& a, void* stream);
+// Grouped launch: grid (n tiles, aligned blocks of bm rows).
+int launch_tiled_grouped(int fmt, int mode, const TiledCfgRt& cfg, const TiledArgs& a, int64_t blocks,
+                         void* stream);
 int launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups, void* stream);
 
 // Pending timing events for the next launch on this thread (see

@@ -1,18 +1,24 @@
 // Large-M quantized GEMM for gfx950 ("tiled" kernel): the MFMA-bound regime
-// (prefill-sized M), same operation and fragment layout as the skinny kernel.
+// (prefill-sized M, and the grouped MoE GEMM with many tokens per expert).
+// Same operation and fragment layout as the skinny kernel.
 //
 // Work decomposition
-//   * A workgroup of 4 wavefronts computes a BM x BN output tile with
-//     BN = 4 * NBW * 16: wave w owns the NBW column blocks 4*?.. of its slice
-//     and all BM rows, so every weight is dequantised exactly once per tile.
-//   * The k loop advances one 128-k group per iteration.  The activation tile
-//     (BM rows x 128 k) is staged through LDS (double buffered, XOR-swizzled so
-//     that the 16 rows read by one MFMA operand fetch hit distinct banks) and
-//     shared by the 4 waves; weight fragments go from HBM straight to the
-//     registers of the one wave that uses them (one 16-byte load per lane per
-//     fragment).  The next group's loads are issued before the current group's
-//     math, and one barrier per group separates the LDS write of group g+1
-//     from the reads of group g.
+//   * A workgroup of 4 wavefronts computes a BM x BN output tile,
+//     BN = 64 * NBW: wave w owns NBW 16-column blocks and all BM rows, so every
+//     weight is dequantised exactly once per tile.
+//   * The k loop advances one 128-k group per step through a 3-slot pipeline:
+//       - activations (BM rows x 128 k) go from HBM straight into an LDS slot
+//         with the direct global->LDS 16-byte load (no staging registers);
+//         the 16-byte chunks are XOR-swizzled so that the 16 rows of one MFMA
+//         operand fetch hit distinct banks;
+//       - weight fragments go to a 3-slot register ring of the one wave that
+//         uses them (one 16-byte load per lane per fragment), metadata beside;
+//       - step g: wait until only the loads of step g+1 are still in flight,
+//         one barrier (every wave's loads of step g have landed, and every
+//         wave has finished reading the slot of step g-1), issue the loads of
+//         step g+2 into that freed slot, then the math of step g.
+//     Loads are issued without branches (past the end they re-read the last
+//     group), so the number of loads in flight at every wait is exact.
 //   * fp16 activations: the weights are dequantised to fp16 in registers,
 //     w = ((1024 + q) - (1024 + z)) * s with packed fp16 arithmetic (the
 //     subtraction is exact; one rounding in the product), and the MFMA
@@ -21,9 +27,12 @@
 //     with the row-sum correction of the offset 128 + z; int8: exact int32
 //     per group; fp8: the row-sum correction of z), and MXFP4 feeds codes and
 //     E8M0 block scales to the scaled MFMA directly.
-//   * Tiles are ordered so that the workgroups the hardware places on one XCD
-//     (consecutive workgroup ids modulo 8) share the same activation rows,
-//     which then stay in that XCD's L2.
+//   * Dense tiles are ordered so that the workgroups the hardware places on
+//     one XCD (consecutive ids modulo 8) share the same activation rows.
+//   * Grouped mode (MoE): grid y walks the expert-aligned blocks of BM slots,
+//     rows are gathered by token (gate_up) or taken in aligned order (down);
+//     epilogues as in the skinny kernel (SiLU * mul, fp32 + row max for the
+//     fp8 requant, weighted atomic combine into tokens).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -43,92 +52,161 @@ struct TCfg {
   static constexpr bool ACT16 = (FMT == FMT_W16F16 || FMT == FMT_W16BF16);
   static constexpr int ROWB = ACT16 ? 256 : 128;  // A bytes per row per group
   static constexpr int CHUNKS = ROWB / 16;        // 16-byte chunks per row
-  static constexpr int LOADS = BM * CHUNKS / THREADS;
+  static constexpr int RPS = 1024 / ROWB;         // rows per 1 KiB load segment
+  static constexpr int NSEG = BM * ROWB / 1024;   // global->LDS loads per step (workgroup)
+  static constexpr int SEGW = NSEG / WAVES;       // ... per wave
+  static constexpr int STAGES = 3;
   static constexpr int STAGE_BYTES = BM * ROWB;
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
-  static_assert(LOADS * THREADS == BM * CHUNKS, "tile rows must fill the loaders");
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int META = (FMT == FMT_F4) ? 1 : 2;  // metadata loads per fragment
+  static constexpr int LPS = SEGW + NBW + META * NBW;   // vector-memory loads per step per wave
+  static_assert(SEGW * WAVES == NSEG, "tile rows must fill the loaders");
+  static_assert(LPS < 64, "loads in flight exceed the counter");
 };
 
-// Physical 16-byte chunk of logical chunk c in row r (bank-conflict-free
-// operand reads: the 16 rows of one MFMA operand fetch land on 16 distinct
-// 16-byte bank groups).
+// Physical 16-byte chunk of logical chunk c in row r.
 template <bool ACT16>
 __device__ inline int swz(int r, int c) {
   return ACT16 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
 }
 
-template <int FMT, int BM, int NBW>
+// s_waitcnt: at most N (< 64) vector-memory loads of this wave still in
+// flight, and every LDS read of this wave completed (so that the barrier
+// that follows also orders all reads of a slot before the loads that refill it).
+template <int N>
+__device__ inline void wait_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+}
+
+// Makes `x` look redefined here, so that no use of the value can be moved
+// above this point (it pins the uses of a ring slot below the step barrier).
+template <typename T>
+__device__ inline void pin(T& x) {
+  asm volatile("; pin %0" : "+v"(x));
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int FMT, int BM, int NBW, int GRP>
 __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
   using C = TCfg<FMT, BM, NBW>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int c = lane & 15;
+  const int c16 = lane & 15;
   const int kq = lane >> 4;
   const int G = p.G;
   const int K = p.K;
 
-  // XCD-aware tile order: the hardware deals workgroup ids round-robin to the
-  // 8 XCDs; give the ids of one XCD consecutive logical tiles (same rows).
-  const int nwg = gridDim.x;
-  int lid = blockIdx.x;
-  if ((nwg & 7) == 0) lid = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
-  const int tm = lid / p.tiles_n;
-  const int tn = lid - tm * p.tiles_n;
+  int tm, tn;
+  if constexpr (GRP == GRP_DENSE) {
+    // XCD-aware order: ids dealt round-robin to the 8 XCDs get consecutive
+    // logical tiles (same rows) on each XCD.
+    const int nwg = gridDim.x;
+    int lid = blockIdx.x;
+    if ((nwg & 7) == 0) lid = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+    tm = lid / p.tiles_n;
+    tn = lid - tm * p.tiles_n;
+  } else {
+    tn = blockIdx.x;
+    tm = blockIdx.y;
+  }
   const int m0 = tm * BM;
-  const int nblk0 = tn * (C::BN / 16) + wave * NBW;  // first 16-column block of this wave
 
-  // ---- activation loader: rows / chunks this thread stages ------------------
+  const uint8_t* wbytes = static_cast<const uint8_t*>(p.w);
+  const uint16_t* scales16 = static_cast<const uint16_t*>(p.scales);
+  const uint32_t* zeros32 = p.zeros;
+  const uint8_t* e8 = p.e8m0;
+  [[maybe_unused]] bool paired = false;
+  if constexpr (GRP != GRP_DENSE) {
+    if (m0 >= *p.num_padded) return;
+    const int64_t ex = p.block_expert[tm];
+    wbytes += ex * p.w_expert;
+    if constexpr (FMT == FMT_F4) {
+      e8 += ex * p.e8_expert;
+    } else {
+      scales16 += ex * p.s_expert;
+      if (zeros32) zeros32 += ex * p.z_expert;
+    }
+    paired = GRP == GRP_GATHER && (p.epi == GEPI_SILU || p.epi == GEPI_SILU_F32);
+  }
+  // 16-column block of this wave's fragment j (gate_up pairs gate block b
+  // with up block half_nblk + b: fragments j < NBW/2 gate, the rest up).
+  auto nblk = [&](int j) -> int {
+    if constexpr (GRP == GRP_GATHER) {
+      if (paired) {
+        const int b0 = tn * (C::BN / 32) + wave * (NBW / 2);
+        return j < NBW / 2 ? b0 + j : p.half_nblk + b0 + (j - NBW / 2);
+      }
+    }
+    return tn * (C::BN / 16) + wave * NBW + j;
+  };
+
+  // ---- activation sources of this wave's global->LDS loads ------------------
+  // Segment seg (1 KiB of the slot) holds rows seg*RPS .. seg*RPS+RPS-1; lane l
+  // writes physical chunk l % CHUNKS of row seg*RPS + l / CHUNKS, so it loads
+  // the logical chunk the swizzle places there (the XOR is its own inverse).
   const uint8_t* a_bytes = static_cast<const uint8_t*>(p.a);
   const int64_t a_pitch = (int64_t)K * (C::ACT16 ? 2 : 1);
-  const uint8_t* a_src[C::LOADS];
-  int lds_off[C::LOADS];
+  const uint8_t* dsrc[C::SEGW];
 #pragma unroll
-  for (int i = 0; i < C::LOADS; ++i) {
-    const int idx = tid + i * C::THREADS;
-    const int r = idx / C::CHUNKS;
-    const int ch = idx - r * C::CHUNKS;
-    const int row = min(m0 + r, p.M - 1);
-    a_src[i] = a_bytes + row * a_pitch + ch * 16;
-    lds_off[i] = r * C::ROWB + swz<C::ACT16>(r, ch) * 16;
+  for (int s = 0; s < C::SEGW; ++s) {
+    const int seg = wave + C::WAVES * s;
+    const int r = seg * C::RPS + lane / C::CHUNKS;
+    const int lchunk = swz<C::ACT16>(r, lane % C::CHUNKS);
+    int row;
+    if constexpr (GRP == GRP_DENSE) {
+      row = min(m0 + r, p.M - 1);
+    } else if constexpr (GRP == GRP_GATHER) {
+      const int id = p.sorted_ids[m0 + r];
+      row = id < p.n_slots ? id / p.topk : 0;
+    } else {
+      row = m0 + r;
+    }
+    dsrc[s] = a_bytes + row * a_pitch + lchunk * 16;
   }
-  u4_t a_stage[C::LOADS];
-  auto load_a = [&](int g) {
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i)
-      a_stage[i] = *reinterpret_cast<const u4_t*>(a_src[i] + (int64_t)g * C::ROWB);
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i)
-      *reinterpret_cast<u4_t*>(lds + buf * C::STAGE_BYTES + lds_off[i]) = a_stage[i];
-  };
 
-  // ---- weight fragments + group metadata of this wave -----------------------
-  const u4_t* wfr = reinterpret_cast<const u4_t*>(p.w);
-  u4_t braw[2][NBW];
-  uint32_t sraw[2][NBW], zraw[2][NBW];
-  // zero points, or (fixed zero) any readable word array of at least the same size
-  const uint32_t* zsrc = p.zeros ? p.zeros : static_cast<const uint32_t*>(p.scales);
-  // Loads are unconditional and decoded only in the math (no early waits).
-  auto load_b = [&](auto slot_c, int g) {
+  // ---- weight fragments + metadata of this wave, 3-slot ring ----------------
+  const u4_t* wfr = reinterpret_cast<const u4_t*>(wbytes);
+  const uint32_t* zsrc = zeros32 ? zeros32 : reinterpret_cast<const uint32_t*>(scales16);
+  u4_t braw[C::STAGES][NBW];
+  uint32_t sraw[C::STAGES][NBW];
+  [[maybe_unused]] uint32_t zraw[C::STAGES][NBW];
+
+  auto issue = [&](auto slot_c, int g) {
     constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
+    for (int s = 0; s < C::SEGW; ++s) {
+      const int seg = wave + C::WAVES * s;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(dsrc[s] + (int64_t)g * C::ROWB),
+                                       (lds_ptr_t)(lds + slot * C::STAGE_BYTES + seg * 1024), 16, 0, 0);
+    }
+#pragma unroll
     for (int j = 0; j < NBW; ++j) {
-      const int64_t rec = (int64_t)(nblk0 + j) * G + g;
+      const int64_t rec = (int64_t)nblk(j) * G + g;
       braw[slot][j] = __builtin_nontemporal_load(wfr + rec * 64 + lane);
+    }
+    // Metadata comes in as whole 32-bit words and the lane's byte / half-word
+    // is taken out in the math: a narrow load would be zero-extended where the
+    // ring is carried round the loop, which forces a wait for every load there.
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+      const int64_t rec = (int64_t)nblk(j) * G + g;
       if constexpr (FMT == FMT_F4) {
-        sraw[slot][j] = p.e8m0[rec * 64 + lane];
+        sraw[slot][j] = reinterpret_cast<const uint32_t*>(e8)[(rec * 64 + lane) >> 2];
       } else {
-        sraw[slot][j] = static_cast<const uint16_t*>(p.scales)[rec * 16 + c];
-        zraw[slot][j] = zsrc[rec * 2 + (c >> 3)];
+        sraw[slot][j] = reinterpret_cast<const uint32_t*>(scales16)[(rec * 16 + c16) >> 1];
+        zraw[slot][j] = zsrc[rec * 2 + (c16 >> 3)];
       }
     }
   };
   auto zero_of = [&](uint32_t zw) -> uint32_t {
-    return p.zp_fixed < 0 ? (zw >> (4 * (c & 7))) & 0xFu : (uint32_t)p.zp_fixed;
+    return p.zp_fixed < 0 ? (zw >> (4 * (c16 & 7))) & 0xFu : (uint32_t)p.zp_fixed;
   };
+  auto scale_bits = [&](uint32_t w) -> uint32_t { return (w >> (16 * (c16 & 1))) & 0xFFFFu; };
+  auto e8m0_of = [&](uint32_t w) -> int { return (int)((w >> (8 * (lane & 3))) & 0xFFu); };
 
   f4_t acc[C::MB][NBW];
 #pragma unroll
@@ -136,31 +214,29 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 #pragma unroll
     for (int j = 0; j < NBW; ++j) acc[mb][j] = f4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Operand fetch of m-block mb from LDS stage `buf`: this lane's row
-  // r = 16 mb + c.  16-bit: step t takes k = 32 t + 8 kq + [0,8) (16-byte
-  // chunk 4 t + kq of the row); 8-bit: piece h takes k = 64 h + 16 kq + [0,16)
-  // (chunk 4 h + kq).
-  auto read_a16 = [&](int buf, int mb, u4_t (&a)[4]) {
-    const int r = 16 * mb + c;
-    const uint8_t* base = lds + buf * C::STAGE_BYTES + r * C::ROWB;
+  // Operand fetch of m-block mb from `slot`: row r = 16 mb + c16.
+  // 16-bit: step t takes k = 32 t + 8 kq + [0,8) (chunk 4 t + kq);
+  // 8-bit: piece h takes k = 64 h + 16 kq + [0,16) (chunk 4 h + kq).
+  auto read_a16 = [&](int slot, int mb, u4_t (&a)[4]) {
+    const int r = 16 * mb + c16;
+    const uint8_t* base = lds + slot * C::STAGE_BYTES + r * C::ROWB;
 #pragma unroll
     for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const u4_t*>(base + swz<true>(r, 4 * t + kq) * 16);
   };
-  auto read_a8 = [&](int buf, int mb, u4_t (&a)[2]) {
-    const int r = 16 * mb + c;
-    const uint8_t* base = lds + buf * C::STAGE_BYTES + r * C::ROWB;
+  auto read_a8 = [&](int slot, int mb, u4_t (&a)[2]) {
+    const int r = 16 * mb + c16;
+    const uint8_t* base = lds + slot * C::STAGE_BYTES + r * C::ROWB;
     a[0] = *reinterpret_cast<const u4_t*>(base + swz<false>(r, kq) * 16);
     a[1] = *reinterpret_cast<const u4_t*>(base + swz<false>(r, 4 + kq) * 16);
   };
 
   auto compute = [&](auto slot_c) {
     constexpr int slot = decltype(slot_c)::value;
-    constexpr int buf = slot;
     if constexpr (FMT == FMT_W16F16) {
       u4_t bop[NBW][4];
 #pragma unroll
       for (int j = 0; j < NBW; ++j) {
-        const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)sraw[slot][j]);
+        const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)scale_bits(sraw[slot][j]));
         const _Float16 cz = -(_Float16)(1024 + (int)zero_of(zraw[slot][j]));
         const h2_t s2 = h2_t{s, s};
         const h2_t c2 = h2_t{cz, cz};
@@ -180,7 +256,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) {
         u4_t a[4];
-        read_a16(buf, mb, a);
+        read_a16(slot, mb, a);
 #pragma unroll
         for (int j = 0; j < NBW; ++j)
 #pragma unroll
@@ -191,7 +267,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
       float sj[NBW], cj[NBW];
 #pragma unroll
       for (int j = 0; j < NBW; ++j) {
-        sj[j] = p.scale_bf16 ? bf16_bits_to_float(sraw[slot][j]) : f16_bits_to_float(sraw[slot][j]);
+        sj[j] = p.scale_bf16 ? bf16_bits_to_float(scale_bits(sraw[slot][j])) : f16_bits_to_float(scale_bits(sraw[slot][j]));
         cj[j] = 128.f + (float)zero_of(zraw[slot][j]);
 #pragma unroll
         for (int t = 0; t < 4; ++t) bop[j][t] = w16_operand(braw[slot][j][t], 0x43004300u);
@@ -200,7 +276,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) {
         u4_t a[4];
-        read_a16(buf, mb, a);
+        read_a16(slot, mb, a);
         f4_t rs = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 4; ++t) rs = mfma_16x16x32<false>(a[t], ones, rs);
@@ -218,14 +294,14 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
       float sj[NBW];
 #pragma unroll
       for (int j = 0; j < NBW; ++j) {
-        sj[j] = 0.0625f * (p.scale_bf16 ? bf16_bits_to_float(sraw[slot][j]) : f16_bits_to_float(sraw[slot][j]));
+        sj[j] = 0.0625f * (p.scale_bf16 ? bf16_bits_to_float(scale_bits(sraw[slot][j])) : f16_bits_to_float(scale_bits(sraw[slot][j])));
         bop[j][0] = i8_operand(braw[slot][j][0], braw[slot][j][1]);
         bop[j][1] = i8_operand(braw[slot][j][2], braw[slot][j][3]);
       }
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) {
         u4_t a[2];
-        read_a8(buf, mb, a);
+        read_a8(slot, mb, a);
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
           i4_t P = i4_t{0, 0, 0, 0};
@@ -240,7 +316,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
       float sj[NBW], zj[NBW];
 #pragma unroll
       for (int j = 0; j < NBW; ++j) {
-        sj[j] = p.scale_bf16 ? bf16_bits_to_float(sraw[slot][j]) : f16_bits_to_float(sraw[slot][j]);
+        sj[j] = p.scale_bf16 ? bf16_bits_to_float(scale_bits(sraw[slot][j])) : f16_bits_to_float(scale_bits(sraw[slot][j]));
         zj[j] = (float)zero_of(zraw[slot][j]);
         bop[j] = q8_operand(braw[slot][j]);
       }
@@ -249,7 +325,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) {
         u4_t a[2];
-        read_a8(buf, mb, a);
+        read_a8(slot, mb, a);
         const i8_t av = cat8(a[0], a[1]);
         const f4_t rs = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, ones, f4_t{0.f, 0.f, 0.f, 0.f}, 0, 0,
                                                                          0, 127, 0, 127);
@@ -265,44 +341,52 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) {
         u4_t a[2];
-        read_a8(buf, mb, a);
+        read_a8(slot, mb, a);
         const i8_t av = cat8(a[0], a[1]);
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
           const u4_t w = braw[slot][j];
           const i8_t bv = i8_t{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
           acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mb][j], 0, 4, 0, 127, 0,
-                                                                        (int)sraw[slot][j]);
+                                                                        e8m0_of(sraw[slot][j]));
         }
       }
     }
   };
 
-  // ---- main loop: one 128-k group per step, unrolled by the two buffers so
-  // that every register array is indexed with compile-time constants --------
+  // ---- main loop: 3-slot pipeline, one barrier per 128-k group ---------------
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  // The next group's loads are issued without a branch (the last step
-  // re-reads group G-1, which is in L2) so that the waits inside the math
-  // count only LDS traffic, not the loads in flight.
+  using S2 = std::integral_constant<int, 2>;
+  auto gclamp = [&](int g) { return g < G ? g : G - 1; };
   auto step = [&](auto slot_c, int g) {
     constexpr int cur = decltype(slot_c)::value;
-    using Next = std::integral_constant<int, 1 - cur>;
-    const int gn = min(g + 1, G - 1);
-    load_a(gn);
-    load_b(Next{}, gn);
-    compute(slot_c);
-    store_a(1 - cur);
-    __syncthreads();
+    using Ahead = std::integral_constant<int, (cur + 2) % 3>;
+    __builtin_amdgcn_sched_barrier(0);  // keeps the last step's loads above the count below
+    wait_vm_lds<C::LPS>();  // this wave's loads of step g have landed (step g+1's may not)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+      pin(braw[cur][j]);
+      pin(sraw[cur][j]);
+      if constexpr (FMT != FMT_F4) pin(zraw[cur][j]);
+    }
+    issue(Ahead{}, gclamp(g + 2));  // into the slot every wave finished reading at step g-1
+    if (g < G) compute(slot_c);
   };
-  load_a(0);
-  load_b(S0{}, 0);
-  store_a(0);
-  __syncthreads();
-  for (int g = 0; g < G; g += 2) {
+  // The wait count above assumes every load of a step is issued after every
+  // load of the step before, so no scheduling across these two.
+  issue(S0{}, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(S1{}, gclamp(1));
+  __builtin_amdgcn_sched_barrier(0);
+  for (int g = 0; g < G; g += 3) {
     step(S0{}, g);
-    if (g + 1 < G) step(S1{}, g + 1);
+    step(S1{}, g + 1);
+    step(S2{}, g + 2);
   }
+  __builtin_amdgcn_s_waitcnt(0);  // no load into LDS may outlive the workgroup
 
   // ---- epilogue ---------------------------------------------------------------
   constexpr bool ACT_SCALE = !C::ACT16;
@@ -311,12 +395,43 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = m0 + 16 * mb + 4 * kq + r;
-      if (m >= p.M) continue;
-      const float sa = ACT_SCALE ? p.a_scale[m] : 1.f;
+      if constexpr (GRP == GRP_DENSE) {
+        if (m >= p.M) continue;
+        const float sa = ACT_SCALE ? p.a_scale[m] : 1.f;
 #pragma unroll
-      for (int j = 0; j < NBW; ++j) {
-        const int n = (nblk0 + j) * 16 + c;
-        store_out(p.out, (int64_t)m * p.N + n, acc[mb][j][r] * sa, p.out_bf16);
+        for (int j = 0; j < NBW; ++j)
+          store_out(p.out, (int64_t)m * p.N + nblk(j) * 16 + c16, acc[mb][j][r] * sa, p.out_bf16);
+      } else {
+        const int id = p.sorted_ids[m];
+        if (id >= p.n_slots) continue;
+        const int tok = id / p.topk;
+        if constexpr (GRP == GRP_GATHER) {
+          const float sa = ACT_SCALE ? p.a_scale[tok] : 1.f;
+          if (paired) {
+            const int half = p.N / 2;
+#pragma unroll
+            for (int j = 0; j < NBW / 2; ++j) {
+              const float gv = acc[mb][j][r] * sa;
+              const float act = gv / (1.f + expf(-gv)) * (acc[mb][j + NBW / 2][r] * sa);
+              const int64_t o = (int64_t)m * half + nblk(j) * 16 + c16;
+              if (p.epi == GEPI_SILU) {
+                store_out(p.out, o, act, p.out_bf16);
+              } else {
+                p.f32_out[o] = act;
+                atomicMax(p.row_amax + m, __float_as_uint(fabsf(act)));
+              }
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < NBW; ++j)
+              store_out(p.out, (int64_t)m * p.N + nblk(j) * 16 + c16, acc[mb][j][r] * sa, p.out_bf16);
+          }
+        } else {
+          const float sa = (ACT_SCALE ? p.a_scale[m] : 1.f) * p.topk_w[id];
+#pragma unroll
+          for (int j = 0; j < NBW; ++j)
+            atomicAdd(p.f32_out + (int64_t)tok * p.N + nblk(j) * 16 + c16, acc[mb][j][r] * sa);
+        }
       }
     }
   }
@@ -326,10 +441,10 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 // dispatch
 // ---------------------------------------------------------------------------
 
-template <int FMT, int BM, int NBW>
-static hipError_t launch_tiled_t(const TiledArgs& a, hipStream_t s) {
+template <int FMT, int BM, int NBW, int GRP>
+static hipError_t launch_tiled_t(const TiledArgs& a, dim3 grid, hipStream_t s) {
   using C = TCfg<FMT, BM, NBW>;
-  auto kern = qgemm_tiled<FMT, BM, NBW>;
+  auto kern = qgemm_tiled<FMT, BM, NBW, GRP>;
   static bool attr_done = false;  // raise the dynamic LDS limit once per instantiation
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -337,33 +452,56 @@ static hipError_t launch_tiled_t(const TiledArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_done = true;
   }
-  const int tiles = a.tiles_m * a.tiles_n;
   const TimingEvents ev = take_timing();
   if (ev.start)
-    hipExtLaunchKernelGGL(kern, dim3(tiles), dim3(C::THREADS), (uint32_t)C::LDS_BYTES, s,
+    hipExtLaunchKernelGGL(kern, grid, dim3(C::THREADS), (uint32_t)C::LDS_BYTES, s,
                           static_cast<hipEvent_t>(ev.start), static_cast<hipEvent_t>(ev.stop), 0, a);
   else
-    hipLaunchKernelGGL(kern, dim3(tiles), dim3(C::THREADS), C::LDS_BYTES, s, a);
+    hipLaunchKernelGGL(kern, grid, dim3(C::THREADS), C::LDS_BYTES, s, a);
   return hipGetLastError();
 }
 
-template <int FMT>
-static hipError_t launch_tiled_f(const TiledCfgRt& cfg, const TiledArgs& a, hipStream_t s) {
-  if (cfg.bm == 128 && cfg.nbw == 4) return launch_tiled_t<FMT, 128, 4>(a, s);
-  if (cfg.bm == 64 && cfg.nbw == 4) return launch_tiled_t<FMT, 64, 4>(a, s);
-  if (cfg.bm == 128 && cfg.nbw == 2) return launch_tiled_t<FMT, 128, 2>(a, s);
-  if (cfg.bm == 64 && cfg.nbw == 2) return launch_tiled_t<FMT, 64, 2>(a, s);
+template <int FMT, int GRP>
+static hipError_t launch_tiled_f(const TiledCfgRt& cfg, const TiledArgs& a, dim3 grid, hipStream_t s) {
+  if (cfg.bm == 128 && cfg.nbw == 4) return launch_tiled_t<FMT, 128, 4, GRP>(a, grid, s);
+  if (cfg.bm == 64 && cfg.nbw == 4) return launch_tiled_t<FMT, 64, 4, GRP>(a, grid, s);
+  if (cfg.bm == 128 && cfg.nbw == 2) return launch_tiled_t<FMT, 128, 2, GRP>(a, grid, s);
+  if (cfg.bm == 64 && cfg.nbw == 2) return launch_tiled_t<FMT, 64, 2, GRP>(a, grid, s);
   return hipErrorInvalidValue;
 }
 
 int launch_tiled(int fmt, const TiledCfgRt& cfg, const TiledArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)(a.tiles_m * a.tiles_n));
   switch (fmt) {
-    case FMT_W16F16: return (int)launch_tiled_f<FMT_W16F16>(cfg, a, s);
-    case FMT_W16BF16: return (int)launch_tiled_f<FMT_W16BF16>(cfg, a, s);
-    case FMT_I8: return (int)launch_tiled_f<FMT_I8>(cfg, a, s);
-    case FMT_Q8: return (int)launch_tiled_f<FMT_Q8>(cfg, a, s);
-    case FMT_F4: return (int)launch_tiled_f<FMT_F4>(cfg, a, s);
+    case FMT_W16F16: return (int)launch_tiled_f<FMT_W16F16, GRP_DENSE>(cfg, a, grid, s);
+    case FMT_W16BF16: return (int)launch_tiled_f<FMT_W16BF16, GRP_DENSE>(cfg, a, grid, s);
+    case FMT_I8: return (int)launch_tiled_f<FMT_I8, GRP_DENSE>(cfg, a, grid, s);
+    case FMT_Q8: return (int)launch_tiled_f<FMT_Q8, GRP_DENSE>(cfg, a, grid, s);
+    case FMT_F4: return (int)launch_tiled_f<FMT_F4, GRP_DENSE>(cfg, a, grid, s);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_tiled_grouped(int fmt, int mode, const TiledCfgRt& cfg, const TiledArgs& a, int64_t blocks,
+                         void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool paired = mode == GRP_GATHER && (a.epi == GEPI_SILU || a.epi == GEPI_SILU_F32);
+  const int bn = 64 * cfg.nbw;
+  const int ntiles = paired ? (a.N / 2) / (bn / 2) : a.N / bn;
+  const dim3 grid((unsigned)ntiles, (unsigned)blocks);
+  if (mode == GRP_GATHER) {
+    switch (fmt) {
+      case FMT_W16F16: return (int)launch_tiled_f<FMT_W16F16, GRP_GATHER>(cfg, a, grid, s);
+      case FMT_W16BF16: return (int)launch_tiled_f<FMT_W16BF16, GRP_GATHER>(cfg, a, grid, s);
+      case FMT_Q8: return (int)launch_tiled_f<FMT_Q8, GRP_GATHER>(cfg, a, grid, s);
+    }
+  } else if (mode == GRP_SORTED) {
+    switch (fmt) {
+      case FMT_W16F16: return (int)launch_tiled_f<FMT_W16F16, GRP_SORTED>(cfg, a, grid, s);
+      case FMT_W16BF16: return (int)launch_tiled_f<FMT_W16BF16, GRP_SORTED>(cfg, a, grid, s);
+      case FMT_Q8: return (int)launch_tiled_f<FMT_Q8, GRP_SORTED>(cfg, a, grid, s);
+    }
   }
   return (int)hipErrorInvalidValue;
 }
