@@ -357,6 +357,11 @@ class MoePlan(Plan):
                       (num_padded, "num_padded"), (w, "w"), (meta, "meta")):
             _dev(x, nm)
         dev = a.device
+        bm = self.block_m(t, topk)
+        need = moe_max_padded(t, topk, self.num_experts, bm)
+        if sorted_ids.numel() < need or block_expert.numel() < max(need // bm, 1):
+            raise ValueError(f"sorted_ids / block_expert are smaller than an alignment with block_m={bm} "
+                             f"for t={t}, topk={topk} needs ({need}, {need // bm}); align with block_m(t, topk)")
         mp = sorted_ids.numel()
         if out is None:
             if self.epi == EPI_TOPK_COMBINE:

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libhq.so")
 ARCH = os.environ.get("HQ_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"), "-Wno-unused-command-line-argument"]
+COMMON = ["-O3", "-std=c++20", "-fPIC", "-I", os.path.join(ROOT, "include"), "-Wno-unused-command-line-argument"]
 DEVICE = [f"--offload-arch={ARCH}", "-mcode-object-version=5", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 

@@ -109,6 +109,8 @@ bool valid_pow(int v) { return v == 1 || v == 2 || v == 4; }
 
 namespace hq {
 
+void arm_timing(TimingEvents t) { g_timing = t; }
+
 TimingEvents take_timing() {
   TimingEvents t = g_timing;
   g_timing = TimingEvents{nullptr, nullptr};
@@ -121,20 +123,31 @@ Exec choose_exec(const hq_plan* p, int64_t m) {
   const int64_t N = p->layer.n;
   const int64_t G = p->layer.k / kFragK;
   const hq_tuning& u = p->user;
-  e.ws_counter_bytes = align256((size_t)(N / 16) * (size_t)cdiv(p->max_m > 0 ? p->max_m : 1, 16) * 4);
+  const int64_t mm = m > 0 ? m : 1;
   // Large M: the MFMA-bound tiled kernel (needs whole 128/256-column tiles);
-  // also for 33..64 rows when the layer is wide enough to fill the chip.
+  // from 33 rows on, the activation tile in LDS is shared by the four waves
+  // instead of being re-read by every 16-column workgroup.
   const bool tiled_ok = p->compute.epi != HQ_EPI_I32_ACC && N % 128 == 0;
-  const bool tiled_auto = m > 64 || (m > 32 && N >= 8192);
+  const bool tiled_auto = m > 32;
   if (tiled_ok && (u.kernel == KER_TILED || (u.kernel == 0 && tiled_auto))) {
     e.kernel = KER_TILED;
     e.tl.bm = m >= 512 ? 128 : 64;
     e.tl.nbw = (N % 256 == 0 && m >= 512 && p->fmt != FMT_W16BF16) ? 4 : 2;
     if (u.tile_m) e.tl.bm = u.tile_m;
     if (u.tile_n) e.tl.nbw = u.tile_n / 64;
-    e.tiles_m = cdiv(m > 0 ? m : 1, e.tl.bm);
+    e.tiles_m = cdiv(mm, e.tl.bm);
     e.tiles_n = e.tl.nbw > 0 ? N / (64 * e.tl.nbw) : 0;
-    e.ws_bytes = 0;
+    // Too few tiles to fill the 256 CUs: split K over workgroups (each split
+    // at least two groups), partial tiles summed by a second kernel.
+    int64_t split = 1;
+    const int64_t tiles = e.tiles_m * e.tiles_n;
+    if (u.split_k) split = u.split_k;
+    else if (tiles > 0 && tiles < 256) split = std::min<int64_t>(cdiv(256, tiles), std::max<int64_t>(1, G / 2));
+    split = std::max<int64_t>(1, std::min<int64_t>(split, G));
+    split = cdiv(G, cdiv(G, split));  // no empty split
+    e.tl.split = (int)split;
+    e.tl.stages = u.stages ? u.stages : 3;
+    e.ws_bytes = split > 1 ? align256((size_t)split * (size_t)mm * (size_t)N * 4) : 0;
     return e;
   }
   SkinnyCfg c{};
@@ -163,19 +176,18 @@ Exec choose_exec(const hq_plan* p, int64_t m) {
   // 16-wave workgroups exist for one 16 x 16 block per wave only
   if (!u.waves && c.waves > 8 && !(c.mb == 1 && c.nb == 1 && c.stages <= 4)) c.waves = 8;
   const int64_t ntiles = N / (16 * c.nb);
-  const int64_t mch = cdiv(m > 0 ? m : 1, 16 * c.mb);
-  // Splitting K over workgroups needs a device-wide release/acquire per
-  // workgroup (an L2 write-back + invalidate on this chip), so it is only
-  // used when asked for.
+  const int64_t mch = cdiv(mm, 16 * c.mb);
   int64_t split = 1;
   if (u.split_k) split = u.split_k;
+  split = std::max<int64_t>(1, std::min<int64_t>(split, G));
+  split = cdiv(G, cdiv(G, split));  // no empty split
   c.split = (int)split;
   e.sk = c;
   e.tiles_m = mch;
   e.tiles_n = ntiles;
   e.ws_bytes = 0;
   if (c.split > 1 && p->compute.epi != HQ_EPI_I32_ACC)
-    e.ws_bytes = e.ws_counter_bytes + align256((size_t)c.split * (size_t)m * (size_t)N * 4);
+    e.ws_bytes = align256((size_t)c.split * (size_t)mm * (size_t)N * 4);
   return e;
 }
 
@@ -184,11 +196,23 @@ Exec choose_exec(const hq_plan* p, int64_t m) {
 namespace {
 
 hq_status check_exec(const hq_plan* p, const hq::Exec& e) {
+  if (p->user.split_k < 0 || p->user.split_k > 64) return fail(HQ_ERR_INVALID_ARG, "split_k must be 1..64");
   if (e.kernel == hq::KER_TILED) {
     if (e.tl.bm != 64 && e.tl.bm != 128) return fail(HQ_ERR_INVALID_ARG, "tiled kernel: tile_m must be 64 or 128");
     if (e.tl.nbw != 2 && e.tl.nbw != 4) return fail(HQ_ERR_INVALID_ARG, "tiled kernel: tile_n must be 128 or 256");
     if (p->layer.n % (64 * e.tl.nbw)) return fail(HQ_ERR_INVALID_ARG, "tiled kernel: N must be a multiple of tile_n");
     if (e.tiles_m * e.tiles_n > (int64_t(1) << 31) - 1) return fail(HQ_ERR_UNSUPPORTED, "too many tiles");
+    if (e.tl.split < 1 || e.tl.split > 64) return fail(HQ_ERR_INVALID_ARG, "split_k must be 1..64");
+    {
+      // load pipeline: stages x (tile_m rows x one group of A) in LDS, and the
+      // loads of stages - 2 groups in flight within the 6-bit wait counter
+      const bool act16 = p->fmt == hq::FMT_W16F16 || p->fmt == hq::FMT_W16BF16;
+      const int rowb = act16 ? 256 : 128;
+      const int lps = e.tl.bm * rowb / 1024 / 4 + e.tl.nbw * (p->fmt == hq::FMT_F4 ? 2 : 3);
+      if (e.tl.stages < 3 || e.tl.stages > 5) return fail(HQ_ERR_INVALID_ARG, "tiled kernel: stages must be 3..5");
+      if (e.tl.stages * e.tl.bm * rowb > 160 * 1024 || lps * (e.tl.stages - 2) >= 64)
+        return fail(HQ_ERR_INVALID_ARG, "tiled kernel: too many stages for this tile");
+    }
     return HQ_OK;
   }
   const hq::SkinnyCfg& c = e.sk;
@@ -277,6 +301,18 @@ hq_status hq_plan_create(const hq_layer_desc* layer, const hq_compute* compute, 
         return fail(HQ_ERR_UNSUPPORTED, "SiLU * mul needs n (gate + up) a multiple of 32");
       if (compute->epi == HQ_EPI_TOPK_COMBINE && layer->n % 64)
         return fail(HQ_ERR_UNSUPPORTED, "the combining down GEMM needs n a multiple of 64");
+      if (tuning) {
+        const int tm = tuning->tile_m, tn = tuning->tile_n;
+        if (tm != 0 && tm != 16 && tm != 64 && tm != 128)
+          return fail(HQ_ERR_UNSUPPORTED, "grouped tile_m must be 16 (skinny), 64 or 128 (tiled)");
+        if (tuning->kernel == hq::KER_SKINNY && tm > 16)
+          return fail(HQ_ERR_UNSUPPORTED, "the skinny grouped kernel uses 16-row blocks");
+        if (tuning->kernel == hq::KER_TILED && tm == 16)
+          return fail(HQ_ERR_UNSUPPORTED, "the tiled grouped kernel uses 64- or 128-row blocks");
+        if (tn != 0 && tn != 128 && tn != 256)
+          return fail(HQ_ERR_UNSUPPORTED, "grouped tile_n must be 128 or 256");
+        if (tn != 0 && layer->n % tn) return fail(HQ_ERR_UNSUPPORTED, "n must be a multiple of tile_n");
+      }
     }
     hq_plan* p = new (std::nothrow) hq_plan();
     if (!p) return fail(HQ_ERR_INTERNAL, "out of host memory");
@@ -318,9 +354,10 @@ hq_status hq_plan_describe(const hq_plan* p, int64_t m, char* buf, size_t len) {
   if (m < 1) m = 1;
   hq::Exec e = hq::choose_exec(p, m);
   if (e.kernel == hq::KER_TILED) {
-    snprintf(buf, len, "kernel=tiled fmt=%s m=%lld n=%lld k=%lld tile_m=%d tile_n=%d waves=4 grid=%lld ws=0",
+    snprintf(buf, len,
+             "kernel=tiled fmt=%s m=%lld n=%lld k=%lld tile_m=%d tile_n=%d waves=4 split_k=%d grid=%lldx%d ws=%zu",
              fmt_name(p->fmt), (long long)m, (long long)p->layer.n, (long long)p->layer.k, e.tl.bm, 64 * e.tl.nbw,
-             (long long)(e.tiles_m * e.tiles_n));
+             e.tl.split, (long long)(e.tiles_m * e.tiles_n), e.tl.split, e.ws_bytes);
     return ok();
   }
   snprintf(buf, len,
@@ -413,6 +450,7 @@ hq_status hq_repack_host(const hq_plan* p, const void* codes, const void* scales
 
 hq_status hq_gemm(const hq_plan* p, int64_t m, const void* a, const float* a_scale, const void* w,
                   const void* meta, void* out, void* ws, size_t ws_bytes, void* stream) {
+  const hq::TimingEvents ev = hq::take_timing();  // consumed by this call whatever happens
   try {
     if (!p) return fail(HQ_ERR_INVALID_ARG, "null plan");
     if (p->compute.kind != HQ_GEMM_DENSE) return fail(HQ_ERR_INVALID_ARG, "hq_gemm needs a dense plan");
@@ -458,7 +496,15 @@ hq_status hq_gemm(const hq_plan* p, int64_t m, const void* a, const float* a_sca
       t.out_bf16 = p->layer.q.out == HQ_BF16;
       t.tiles_m = (int)e.tiles_m;
       t.tiles_n = (int)e.tiles_n;
+      t.gps = (int)cdiv(G, e.tl.split);
+      t.part = e.tl.split > 1 ? static_cast<float*>(ws) : nullptr;
+      hq::arm_timing({ev.start, e.tl.split > 1 ? nullptr : ev.stop});
       int err = hq::launch_tiled(p->fmt, e.tl, t, stream);
+      if (err == hipSuccess && e.tl.split > 1) {
+        hq::arm_timing({nullptr, ev.stop});
+        err = hq::launch_splitk_reduce(t.part, e.tl.split, m * N, out, t.out_bf16, stream);
+      }
+      hq::arm_timing({nullptr, nullptr});
       if (err != hipSuccess) return fail(HQ_ERR_HIP, "gemm launch: %s", hipGetErrorString((hipError_t)err));
       return ok();
     }
@@ -473,10 +519,7 @@ hq_status hq_gemm(const hq_plan* p, int64_t m, const void* a, const float* a_sca
       args.zeros = zeros;
     }
     args.out = out;
-    if (e.ws_bytes > 0) {
-      args.counter = static_cast<uint32_t*>(ws);
-      args.part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + e.ws_counter_bytes);
-    }
+    if (e.ws_bytes > 0) args.part = static_cast<float*>(ws);
     args.M = (int)m;
     args.N = (int)N;
     args.K = (int)K;
@@ -486,7 +529,14 @@ hq_status hq_gemm(const hq_plan* p, int64_t m, const void* a, const float* a_sca
     args.out_bf16 = p->layer.q.out == HQ_BF16;
     args.i32_out = p->compute.epi == HQ_EPI_I32_ACC;
     args.gps = (int)cdiv(G, e.sk.split);
+    const bool reduce = e.ws_bytes > 0;
+    hq::arm_timing({ev.start, reduce ? nullptr : ev.stop});
     int err = hq::launch_skinny(p->fmt, e.sk, args, stream);
+    if (err == hipSuccess && reduce) {
+      hq::arm_timing({nullptr, ev.stop});
+      err = hq::launch_splitk_reduce(args.part, e.sk.split, m * N, out, args.out_bf16, stream);
+    }
+    hq::arm_timing({nullptr, nullptr});
     if (err != hipSuccess) return fail(HQ_ERR_HIP, "gemm launch: %s", hipGetErrorString((hipError_t)err));
     return ok();
   } catch (...) {
@@ -503,26 +553,58 @@ static int64_t moe_max_padded(int64_t t, int topk, int E, int bm) {
   return (raw + bm - 1) / bm * bm;
 }
 
-static int moe_block_m(const hq_plan* p) { return p->user.tile_m ? p->user.tile_m : 16; }
+// Kernel choice for one grouped call.  Few slots per expert (decode-sized T)
+// leave the weight stream as the cost: the skinny kernel with 16-row blocks
+// reads every active expert's weights about once.  Many slots per expert make
+// the GEMM MFMA-bound: the tiled kernel with 64- or 128-row blocks reuses each
+// dequantised weight fragment over the whole block.
+struct MoeChoice {
+  bool tiled;
+  int bm;  // alignment block = rows per workgroup
+  hq::SkinnyCfg sk;
+  hq::TiledCfgRt tl;
+};
 
-static hq::SkinnyCfg moe_cfg(const hq_plan* p) {
-  hq::SkinnyCfg c{};
-  c.mb = 1;
-  c.nb = (p->compute.epi == HQ_EPI_TOPK_COMBINE || p->compute.epi == HQ_EPI_NONE) ? 4 : 2;
-  if (p->compute.epi == HQ_EPI_NONE && p->layer.n % 64) c.nb = 1;
-  const int64_t G = p->layer.k / 128;
-  c.waves = (int)std::min<int64_t>(8, std::max<int64_t>(1, G));
-  c.stages = 2;
-  c.split = 1;
+static MoeChoice moe_choice(const hq_plan* p, int64_t t, int topk) {
+  MoeChoice c{};
+  const hq_tuning& u = p->user;
+  const int64_t N = p->layer.n;
+  const double per_expert = (double)t * topk / p->layer.num_experts;
+  bool tiled;
+  if (u.kernel == hq::KER_TILED) tiled = true;
+  else if (u.kernel == hq::KER_SKINNY) tiled = false;
+  else if (u.tile_m) tiled = u.tile_m >= 64;
+  else tiled = per_expert >= 48.0;
+  if (tiled && N % 128) tiled = false;  // the tiled grid needs whole 128-column tiles
+  c.tiled = tiled;
+  if (!tiled) {
+    c.bm = 16;
+    c.sk.mb = 1;
+    c.sk.nb = (p->compute.epi == HQ_EPI_TOPK_COMBINE || p->compute.epi == HQ_EPI_NONE) ? 4 : 2;
+    if (p->compute.epi == HQ_EPI_NONE && N % 64) c.sk.nb = 1;
+    const int64_t G = p->layer.k / 128;
+    c.sk.waves = (int)std::min<int64_t>(8, std::max<int64_t>(1, G));
+    c.sk.stages = 2;
+    c.sk.split = 1;
+    return c;
+  }
+  c.bm = u.tile_m >= 64 ? u.tile_m : (per_expert >= 192.0 ? 128 : 64);
+  int nbw;
+  if (u.tile_n) nbw = u.tile_n / 64;
+  else nbw = (N % 256 == 0 && N >= 2048 && p->fmt != hq::FMT_W16BF16) ? 4 : 2;
+  if (N % (64 * nbw)) nbw = 2;
+  c.tl.bm = c.bm;
+  c.tl.nbw = nbw;
+  c.tl.split = 1;
+  c.tl.stages = 3;
   return c;
 }
 
 hq_status hq_moe_block_m(const hq_plan* p, int64_t t, int topk, int* block_m) {
   if (!p || !block_m) return fail(HQ_ERR_INVALID_ARG, "null argument");
   if (p->compute.kind != HQ_GEMM_GROUPED) return fail(HQ_ERR_INVALID_ARG, "not a grouped plan");
-  (void)t;
-  (void)topk;
-  *block_m = moe_block_m(p);
+  if (t < 0 || topk < 1) return fail(HQ_ERR_INVALID_ARG, "bad sizes");
+  *block_m = moe_choice(p, t, topk).bm;
   return ok();
 }
 
@@ -556,7 +638,7 @@ struct MoeWs {
 
 static MoeWs moe_ws(const hq_plan* p, int64_t t, int topk) {
   MoeWs w{};
-  const int64_t mp = moe_max_padded(t, topk, p->layer.num_experts, moe_block_m(p));
+  const int64_t mp = moe_max_padded(t, topk, p->layer.num_experts, moe_choice(p, t, topk).bm);
   if (p->compute.epi == HQ_EPI_SILU_MUL_QFP8) {
     w.act32 = align256((size_t)mp * (size_t)(p->layer.n / 2) * 4);
     w.amax = align256((size_t)mp * 4);
@@ -578,6 +660,7 @@ hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, cons
                       const int32_t* sorted_ids, const int32_t* block_expert, const int32_t* num_padded,
                       const float* topk_w, const void* w, const void* meta, void* out, float* out_scale, void* ws,
                       size_t ws_bytes, void* stream) {
+  const hq::TimingEvents ev = hq::take_timing();  // consumed by this call whatever happens
   try {
     if (!p) return fail(HQ_ERR_INVALID_ARG, "null plan");
     if (p->compute.kind != HQ_GEMM_GROUPED) return fail(HQ_ERR_INVALID_ARG, "hq_moe_gemm needs a grouped plan");
@@ -601,65 +684,110 @@ hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, cons
       if (!aligned16(ws)) return fail(HQ_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
     }
     const int64_t N = p->layer.n, K = p->layer.k, G = K / 128;
-    const int bm = moe_block_m(p);
+    const MoeChoice mc = moe_choice(p, t, topk);
+    const int bm = mc.bm;
     const int64_t mp = moe_max_padded(t, topk, p->layer.num_experts, bm);
-    hq::SkinnyCfg c = moe_cfg(p);
-    hq::SkinnyArgs s{};
-    s.a = a;
-    s.a_scale = a_scale;
-    s.w = w;
-    s.scales = meta;
-    s.zeros = p->layer.q.zp == HQ_ZP_PER_GROUP_U4
-                  ? reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(meta) +
-                                                      p->scale_region_bytes * (size_t)p->layer.num_experts)
-                  : nullptr;
-    s.out = out;
-    s.M = (int)mp;
-    s.N = (int)N;
-    s.K = (int)K;
-    s.G = (int)G;
-    s.zp_fixed = p->layer.q.zp == HQ_ZP_FIXED ? p->layer.q.zp_value : -1;
-    s.scale_bf16 = p->layer.q.scale == HQ_BF16;
-    s.out_bf16 = p->layer.q.out == HQ_BF16;
-    s.gps = (int)G;
-    s.sorted_ids = sorted_ids;
-    s.block_expert = block_expert;
-    s.num_padded = num_padded;
-    s.topk_w = topk_w;
-    s.topk = topk;
-    s.n_slots = (int)(t * topk);
-    s.half_nblk = (int)(N / 2 / 16);
-    s.w_expert = (int64_t)p->w_bytes_per_expert;
-    s.s_expert = (int64_t)(N * G);
-    s.z_expert = (int64_t)((N / 16) * G * 2);
-    s.e8_expert = (int64_t)(N * K / 32);
+    const uint32_t* zeros = p->layer.q.zp == HQ_ZP_PER_GROUP_U4
+                                ? reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(meta) +
+                                                                    p->scale_region_bytes *
+                                                                        (size_t)p->layer.num_experts)
+                                : nullptr;
     uint8_t* wsb = static_cast<uint8_t*>(ws);
-    int mode = hq::GRP_GATHER;
+    int mode = hq::GRP_GATHER, gepi = hq::GEPI_PLAIN;
+    float* f32_out = nullptr;
+    uint32_t* row_amax = nullptr;
     switch (epi) {
-      case HQ_EPI_NONE: s.epi = hq::GEPI_PLAIN; break;
-      case HQ_EPI_SILU_MUL: s.epi = hq::GEPI_SILU; break;
+      case HQ_EPI_NONE: gepi = hq::GEPI_PLAIN; break;
+      case HQ_EPI_SILU_MUL: gepi = hq::GEPI_SILU; break;
       case HQ_EPI_SILU_MUL_QFP8:
-        s.epi = hq::GEPI_SILU_F32;
-        s.f32_out = reinterpret_cast<float*>(wsb);
-        s.row_amax = reinterpret_cast<uint32_t*>(wsb + mw.act32);
+        gepi = hq::GEPI_SILU_F32;
+        f32_out = reinterpret_cast<float*>(wsb);
+        row_amax = reinterpret_cast<uint32_t*>(wsb + mw.act32);
         break;
       case HQ_EPI_TOPK_COMBINE:
-        s.epi = hq::GEPI_COMBINE;
+        gepi = hq::GEPI_COMBINE;
         mode = hq::GRP_SORTED;
-        s.f32_out = reinterpret_cast<float*>(wsb);
+        f32_out = reinterpret_cast<float*>(wsb);
         break;
       default: return fail(HQ_ERR_INVALID_ARG, "unsupported grouped epilogue");
     }
     // Non-empty blocks: each holds at least one slot, so at most t * topk of
     // them exist whatever the routing; the grid covers min(that, all blocks).
-    const int64_t blocks = std::min<int64_t>(mp / 16, t * topk);
-    int err = hq::launch_skinny_grouped(p->fmt, mode, c, s, blocks, stream);
+    const int64_t blocks = std::min<int64_t>(mp / bm, t * topk);
+    const int n_slots = (int)(t * topk);
+    int err;
+    const bool second = epi == HQ_EPI_SILU_MUL_QFP8 || epi == HQ_EPI_TOPK_COMBINE;
+    hq::arm_timing({ev.start, second ? nullptr : ev.stop});
+    if (mc.tiled) {
+      hq::TiledArgs s{};
+      s.a = a;
+      s.a_scale = a_scale;
+      s.w = w;
+      s.scales = meta;
+      s.zeros = zeros;
+      s.out = out;
+      s.M = (int)mp;
+      s.N = (int)N;
+      s.K = (int)K;
+      s.G = (int)G;
+      s.gps = (int)G;  // grouped launches do not split K
+      s.zp_fixed = p->layer.q.zp == HQ_ZP_FIXED ? p->layer.q.zp_value : -1;
+      s.scale_bf16 = p->layer.q.scale == HQ_BF16;
+      s.out_bf16 = p->layer.q.out == HQ_BF16;
+      s.sorted_ids = sorted_ids;
+      s.block_expert = block_expert;
+      s.num_padded = num_padded;
+      s.topk_w = topk_w;
+      s.topk = topk;
+      s.n_slots = n_slots;
+      s.epi = gepi;
+      s.half_nblk = (int)(N / 2 / 16);
+      s.w_expert = (int64_t)p->w_bytes_per_expert;
+      s.s_expert = (int64_t)(N * G);
+      s.z_expert = (int64_t)((N / 16) * G * 2);
+      s.f32_out = f32_out;
+      s.row_amax = row_amax;
+      err = hq::launch_tiled_grouped(p->fmt, mode, mc.tl, s, blocks, stream);
+    } else {
+      hq::SkinnyArgs s{};
+      s.a = a;
+      s.a_scale = a_scale;
+      s.w = w;
+      s.scales = meta;
+      s.zeros = zeros;
+      s.out = out;
+      s.M = (int)mp;
+      s.N = (int)N;
+      s.K = (int)K;
+      s.G = (int)G;
+      s.zp_fixed = p->layer.q.zp == HQ_ZP_FIXED ? p->layer.q.zp_value : -1;
+      s.scale_bf16 = p->layer.q.scale == HQ_BF16;
+      s.out_bf16 = p->layer.q.out == HQ_BF16;
+      s.gps = (int)G;
+      s.sorted_ids = sorted_ids;
+      s.block_expert = block_expert;
+      s.num_padded = num_padded;
+      s.topk_w = topk_w;
+      s.topk = topk;
+      s.n_slots = n_slots;
+      s.epi = gepi;
+      s.half_nblk = (int)(N / 2 / 16);
+      s.w_expert = (int64_t)p->w_bytes_per_expert;
+      s.s_expert = (int64_t)(N * G);
+      s.z_expert = (int64_t)((N / 16) * G * 2);
+      s.e8_expert = (int64_t)(N * K / 32);
+      s.f32_out = f32_out;
+      s.row_amax = row_amax;
+      err = hq::launch_skinny_grouped(p->fmt, mode, mc.sk, s, blocks, stream);
+    }
+    hq::arm_timing({nullptr, ev.stop});
     if (err == hipSuccess && epi == HQ_EPI_SILU_MUL_QFP8)
-      err = hq::launch_moe_requant(s.f32_out, s.row_amax, sorted_ids, num_padded, s.n_slots, (int)(N / 2),
-                                   std::min<int64_t>(mp, 16 * t * topk), static_cast<uint8_t*>(out), out_scale,
-                                   stream);
+      err = hq::launch_moe_requant(f32_out, row_amax, sorted_ids, num_padded, n_slots, (int)(N / 2),
+                                   std::min<int64_t>(mp, (int64_t)bm * t * topk), static_cast<uint8_t*>(out),
+                                   out_scale, stream);
     if (err == hipSuccess && epi == HQ_EPI_TOPK_COMBINE)
-      err = hq::launch_moe_finalize(s.f32_out, out, t * N, s.out_bf16, stream);
+      err = hq::launch_moe_finalize(f32_out, out, t * N, p->layer.q.out == HQ_BF16, stream);
+    hq::arm_timing({nullptr, nullptr});
     if (err != hipSuccess) return fail(HQ_ERR_HIP, "grouped gemm launch: %s", hipGetErrorString((hipError_t)err));
     return ok();
   } catch (...) {
@@ -671,7 +799,8 @@ hq_status hq_stream_read(const void* buf, size_t bytes, uint32_t* sink, int work
   if (!buf || !sink) return fail(HQ_ERR_INVALID_ARG, "null argument");
   if (bytes % 16 || !aligned16(buf)) return fail(HQ_ERR_INVALID_ARG, "buffer must be 16-byte aligned and sized");
   if (workgroups < 1 || workgroups > (1 << 20)) return fail(HQ_ERR_INVALID_ARG, "workgroups out of range");
-  int err = hq::launch_stream_read(buf, bytes, sink, workgroups, stream);
+  int err = hq::launch_stream_read(buf, bytes, sink, workgroups, stream);  // takes the armed events
+  hq::arm_timing({nullptr, nullptr});
   if (err != hipSuccess) return fail(HQ_ERR_HIP, "stream read launch: %s", hipGetErrorString((hipError_t)err));
   return ok();
 }

@@ -7,6 +7,7 @@
 
 #include "device_common.h"
 #include "hq_internal.h"
+#include "launch.h"
 
 namespace hq {
 
@@ -32,15 +33,8 @@ __global__ void __launch_bounds__(256) stream_read_kernel(const u4_t* __restrict
 
 int launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups, void* stream) {
   const int64_t n16 = (int64_t)(bytes / 16);
-  const TimingEvents ev = take_timing();
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (ev.start)
-    hipExtLaunchKernelGGL(stream_read_kernel, dim3(workgroups), dim3(256), 0, s, static_cast<hipEvent_t>(ev.start),
-                          static_cast<hipEvent_t>(ev.stop), 0, static_cast<const u4_t*>(buf), n16, sink);
-  else
-    hipLaunchKernelGGL(stream_read_kernel, dim3(workgroups), dim3(256), 0, s, static_cast<const u4_t*>(buf), n16,
-                       sink);
-  return (int)hipGetLastError();
+  return (int)launch_timed(stream_read_kernel, dim3(workgroups), dim3(256), 0, static_cast<hipStream_t>(stream),
+                           static_cast<const u4_t*>(buf), n16, sink);
 }
 
 }  // namespace hq

@@ -148,8 +148,10 @@ HQ_HD inline int64_t e8m0_src_index(int64_t K, int64_t eidx) {
 enum KernelKind : int { KER_SKINNY = 1, KER_TILED = 2 };
 
 struct TiledCfgRt {
-  int bm;   // rows per workgroup tile (64, 128)
-  int nbw;  // 16-column blocks per wave (2, 4); tile width = 64 * nbw
+  int bm;     // rows per workgroup tile (64, 128)
+  int nbw;    // 16-column blocks per wave (2, 4); tile width = 64 * nbw
+  int split;   // K split over workgroups (dense; partials + reduce kernel)
+  int stages;  // groups in the load pipeline (3; dense also 4, 5)
 };
 
 struct SkinnyCfg {
@@ -181,8 +183,7 @@ struct Exec {
   SkinnyCfg sk;
   TiledCfgRt tl;
   int64_t tiles_m, tiles_n;
-  size_t ws_bytes;  // total workspace
-  size_t ws_counter_bytes;
+  size_t ws_bytes;  // total workspace: the fp32 split-K partials
 };
 
 Exec choose_exec(const hq_plan* p, int64_t m);
@@ -197,7 +198,6 @@ struct SkinnyArgs {
   const uint8_t* e8m0;
   void* out;
   float* part;       // [split][M][N] fp32 partials (split > 1)
-  uint32_t* counter; // one per output tile (split > 1)
   int M, N, K, G;
   int zp_fixed;      // fixed zero point, or -1 for per-group zeros
   int scale_bf16;    // scale dtype: 1 bf16, 0 fp16
@@ -250,6 +250,8 @@ struct TiledArgs {
   int scale_bf16;
   int out_bf16;
   int tiles_m, tiles_n;
+  int gps;      // groups per split (dense)
+  float* part;  // [split][M][N] fp32 partials, or null (no split)
   // ---- grouped (MoE) mode: the same fields as SkinnyArgs ----
   const int32_t* sorted_ids;
   const int32_t* block_expert;
@@ -268,6 +270,8 @@ int launch_tiled(int fmt, const TiledCfgRt& cfg, const TiledArgs& a, void* strea
 // Grouped launch: grid (n tiles, aligned blocks of bm rows).
 int launch_tiled_grouped(int fmt, int mode, const TiledCfgRt& cfg, const TiledArgs& a, int64_t blocks,
                          void* stream);
+// out[i] = round(sum_s part[s * mn + i]) in index order (fp16 / bf16 out).
+int launch_splitk_reduce(const float* part, int splits, int64_t mn, void* out, int out_bf16, void* stream);
 int launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups, void* stream);
 
 // Pending timing events for the next launch on this thread (see
@@ -277,6 +281,8 @@ struct TimingEvents {
   void* stop;
 };
 TimingEvents take_timing();
+// Arms the events the next launch takes (either may be null).
+void arm_timing(TimingEvents t);
 int launch_repack(const hq_plan* p, const void* codes, const void* scales, const void* zx,
                   void* w_out, void* meta_out, void* stream);
 

@@ -11,6 +11,7 @@
 
 #include "device_common.h"
 #include "hq_internal.h"
+#include "launch.h"
 
 namespace hq {
 
@@ -132,18 +133,17 @@ int launch_moe_align(int64_t t, int topk, int num_experts, int block_m, const in
 int launch_moe_requant(const float* act32, uint32_t* row_amax, const int32_t* sorted_ids, const int32_t* num_padded,
                        int n_slots, int inter, int64_t max_rows, uint8_t* codes, float* scales, void* stream) {
   const int64_t blocks = (max_rows + 3) / 4;
-  hipLaunchKernelGGL(moe_requant_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     act32, row_amax, sorted_ids, num_padded, n_slots, inter, max_rows, codes, scales);
-  return (int)hipGetLastError();
+  return (int)launch_timed(moe_requant_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                           static_cast<hipStream_t>(stream), act32, row_amax, sorted_ids, num_padded, n_slots, inter,
+                           max_rows, codes, scales);
 }
 
 int launch_moe_finalize(float* y32, void* y, int64_t elems, int out_bf16, void* stream) {
   int64_t blocks = (elems + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(moe_finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     y32, y, elems, out_bf16);
-  return (int)hipGetLastError();
+  return (int)launch_timed(moe_finalize_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                           static_cast<hipStream_t>(stream), y32, y, elems, out_bf16);
 }
 
 }  // namespace hq

@@ -28,16 +28,16 @@
 //     are never rounded.  MXFP4 needs no conversion at all: its codes and
 //     E8M0 scales feed the scaled MFMA directly.
 //   * The W partial accumulators are summed in LDS in a fixed order; with a
-//     split > 1 every workgroup stores its fp32 partial tile, and the last one
-//     to arrive (device-scope counter) sums the splits in index order and
-//     writes the output, then re-arms the counter.  Results are therefore
-//     deterministic run to run.
+//     split > 1 every workgroup stores its fp32 partial tile (times the row
+//     scale) and a second kernel sums the splits in index order.  Results are
+//     therefore deterministic run to run.
 #include <hip/hip_ext.h>
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
 #include "hq_internal.h"
+#include "launch.h"
 
 namespace hq {
 
@@ -340,46 +340,14 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
       continue;
     }
     if (m >= p.M) continue;
+    if (FI::kActScale) v *= p.a_scale[m];
     if (S == 1) {
-      if (FI::kActScale) v *= p.a_scale[m];
       const uint16_t o = p.out_bf16 ? float_to_bf16_bits(v) : float_to_f16_bits(v);
       static_cast<uint16_t*>(p.out)[(int64_t)m * p.N + n] = o;
     } else {
       p.part[((int64_t)split * p.M + m) * p.N + n] = v;
     }
   }
-  if (GRP != GRP_DENSE || S == 1) return;
-
-  // ---- cross-workgroup split-K: the last workgroup to arrive finishes ----
-  __shared__ int is_last;
-  __threadfence();
-  __syncthreads();
-  const int tile = blockIdx.z * gridDim.x + nt;
-  if (threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(p.counter + tile, 1u, __ATOMIC_ACQ_REL,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    is_last = (old == (uint32_t)(S - 1));
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  for (int e = threadIdx.x; e < E * 64; e += nthreads) {
-    const int l = e & 63;
-    const int idx = e >> 6;
-    const int r = idx & 3;
-    const int nb = (idx >> 2) % NB;
-    const int mb = (idx >> 2) / NB;
-    const int m = m0 + 16 * mb + 4 * (l >> 4) + r;
-    const int n = (nt * NB + nb) * 16 + (l & 15);
-    if (m >= p.M) continue;
-    float v = 0.f;
-    for (int s = 0; s < S; ++s) v += __builtin_nontemporal_load(p.part + ((int64_t)s * p.M + m) * p.N + n);
-    if (FI::kActScale) v *= p.a_scale[m];
-    const uint16_t o = p.out_bf16 ? float_to_bf16_bits(v) : float_to_f16_bits(v);
-    static_cast<uint16_t*>(p.out)[(int64_t)m * p.N + n] = o;
-  }
-  if (threadIdx.x == 0)
-    __hip_atomic_store(p.counter + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -388,14 +356,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
 
 template <typename Kern>
 static hipError_t launch_kernel(Kern kern, dim3 grid, dim3 block, size_t lds, hipStream_t s, const SkinnyArgs& a) {
-  const TimingEvents ev = take_timing();
-  if (ev.start) {
-    hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)lds, s, static_cast<hipEvent_t>(ev.start),
-                          static_cast<hipEvent_t>(ev.stop), 0, a);
-  } else {
-    hipLaunchKernelGGL(kern, grid, block, lds, s, a);
-  }
-  return hipGetLastError();
+  return launch_timed(kern, grid, block, lds, s, a);
 }
 
 // Instantiated shapes: up to 8 waves per workgroup (256 VGPRs per lane) for
@@ -461,6 +422,7 @@ static hipError_t launch_grouped_f(int mode, const SkinnyCfg& cfg, const SkinnyA
 
 int launch_skinny_grouped(int fmt, int mode, const SkinnyCfg& cfg, const SkinnyArgs& a, int64_t blocks,
                           void* stream) {
+  if (a.G < 1 || a.gps != a.G || cfg.split != 1) return (int)hipErrorInvalidValue;
   const bool paired = mode == GRP_GATHER && (a.epi == GEPI_SILU || a.epi == GEPI_SILU_F32);
   const int ntiles = paired ? (a.N / 2) / (16 * (cfg.nb / 2)) : a.N / (16 * cfg.nb);
   dim3 grid(ntiles, 1, (unsigned)blocks);
@@ -476,6 +438,9 @@ int launch_skinny_grouped(int fmt, int mode, const SkinnyCfg& cfg, const SkinnyA
 }
 
 int launch_skinny(int fmt, const SkinnyCfg& cfg, const SkinnyArgs& a, void* stream) {
+  // every split holds at least one group, and the splits cover K
+  if (a.G < 1 || a.gps < 1 || (int64_t)(cfg.split - 1) * a.gps >= a.G || (int64_t)cfg.split * a.gps < a.G)
+    return (int)hipErrorInvalidValue;
   const int ntiles = a.N / (16 * cfg.nb);
   const int mchunks = (a.M + 16 * cfg.mb - 1) / (16 * cfg.mb);
   dim3 grid(ntiles, cfg.split, mchunks);

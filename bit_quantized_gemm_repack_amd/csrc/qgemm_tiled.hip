@@ -27,6 +27,9 @@
 //     with the row-sum correction of the offset 128 + z; int8: exact int32
 //     per group; fp8: the row-sum correction of z), and MXFP4 feeds codes and
 //     E8M0 block scales to the scaled MFMA directly.
+//   * Split K (dense, for M too small to fill the chip with tiles): grid y
+//     takes a contiguous range of groups and stores its fp32 partial tile
+//     (times the row scale); a second kernel sums the splits in index order.
 //   * Dense tiles are ordered so that the workgroups the hardware places on
 //     one XCD (consecutive ids modulo 8) share the same activation rows.
 //   * Grouped mode (MoE): grid y walks the expert-aligned blocks of BM slots,
@@ -37,13 +40,15 @@
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "device_common.h"
 #include "hq_internal.h"
+#include "launch.h"
 
 namespace hq {
 
-template <int FMT, int BM, int NBW>
+template <int FMT, int BM, int NBW, int ST>
 struct TCfg {
   static constexpr int WAVES = 4;
   static constexpr int THREADS = 64 * WAVES;
@@ -55,13 +60,14 @@ struct TCfg {
   static constexpr int RPS = 1024 / ROWB;         // rows per 1 KiB load segment
   static constexpr int NSEG = BM * ROWB / 1024;   // global->LDS loads per step (workgroup)
   static constexpr int SEGW = NSEG / WAVES;       // ... per wave
-  static constexpr int STAGES = 3;
+  static constexpr int STAGES = ST;  // groups in the pipeline (ST - 1 ahead of the math)
   static constexpr int STAGE_BYTES = BM * ROWB;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static constexpr int META = (FMT == FMT_F4) ? 1 : 2;  // metadata loads per fragment
   static constexpr int LPS = SEGW + NBW + META * NBW;   // vector-memory loads per step per wave
   static_assert(SEGW * WAVES == NSEG, "tile rows must fill the loaders");
-  static_assert(LPS < 64, "loads in flight exceed the counter");
+  static_assert(LPS * (ST - 2) < 64, "loads in flight exceed the counter");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds the workgroup limit");
 };
 
 // Physical 16-byte chunk of logical chunk c in row r.
@@ -88,9 +94,9 @@ __device__ inline void pin(T& x) {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int FMT, int BM, int NBW, int GRP>
+template <int FMT, int BM, int NBW, int GRP, int ST>
 __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
-  using C = TCfg<FMT, BM, NBW>;
+  using C = TCfg<FMT, BM, NBW, ST>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -99,6 +105,11 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
   const int kq = lane >> 4;
   const int G = p.G;
   const int K = p.K;
+  // Split K (dense only): grid y picks a range of p.gps groups; the fp32
+  // partial tiles are summed by a second kernel.
+  const int split = (GRP == GRP_DENSE) ? (int)blockIdx.y : 0;
+  const int gb = split * p.gps;                   // first group of this split
+  const int Gl = min(G - gb, p.gps);              // groups of this split (>= 1)
 
   int tm, tn;
   if constexpr (GRP == GRP_DENSE) {
@@ -180,12 +191,12 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 #pragma unroll
     for (int s = 0; s < C::SEGW; ++s) {
       const int seg = wave + C::WAVES * s;
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(dsrc[s] + (int64_t)g * C::ROWB),
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(dsrc[s] + (int64_t)(gb + g) * C::ROWB),
                                        (lds_ptr_t)(lds + slot * C::STAGE_BYTES + seg * 1024), 16, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
-      const int64_t rec = (int64_t)nblk(j) * G + g;
+      const int64_t rec = (int64_t)nblk(j) * G + gb + g;
       braw[slot][j] = __builtin_nontemporal_load(wfr + rec * 64 + lane);
     }
     // Metadata comes in as whole 32-bit words and the lane's byte / half-word
@@ -193,7 +204,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
     // ring is carried round the loop, which forces a wait for every load there.
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
-      const int64_t rec = (int64_t)nblk(j) * G + g;
+      const int64_t rec = (int64_t)nblk(j) * G + gb + g;
       if constexpr (FMT == FMT_F4) {
         sraw[slot][j] = reinterpret_cast<const uint32_t*>(e8)[(rec * 64 + lane) >> 2];
       } else {
@@ -233,34 +244,63 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
   auto compute = [&](auto slot_c) {
     constexpr int slot = decltype(slot_c)::value;
     if constexpr (FMT == FMT_W16F16) {
-      u4_t bop[NBW][4];
+      // Per k-step t: the MB x NBW MFMAs of step t, with the dequantisation
+      // of step t+1's weights interleaved between them (the MFMA pipe runs
+      // 16 cycles per op; the 4-cycle VALU ops fill the gaps), then t+1.
+      h2_t s2[NBW], c2[NBW];
 #pragma unroll
       for (int j = 0; j < NBW; ++j) {
         const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)scale_bits(sraw[slot][j]));
         const _Float16 cz = -(_Float16)(1024 + (int)zero_of(zraw[slot][j]));
-        const h2_t s2 = h2_t{s, s};
-        const h2_t c2 = h2_t{cz, cz};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const u4_t x = w16_operand(braw[slot][j][t], 0x64006400u);
-          uint32_t y[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            h2_t v = __builtin_bit_cast(h2_t, (uint32_t)x[r]);
-            v = (v + c2) * s2;  // exact integer q - z, then one rounding
-            y[r] = __builtin_bit_cast(uint32_t, v);
-          }
-          bop[j][t] = u4_t{y[0], y[1], y[2], y[3]};
-        }
+        s2[j] = h2_t{s, s};
+        c2[j] = h2_t{cz, cz};
       }
+      auto deq = [&](int j, int t) -> u4_t {
+        const u4_t x = w16_operand(braw[slot][j][t], 0x64006400u);
+        uint32_t y[4];
 #pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb) {
-        u4_t a[4];
-        read_a16(slot, mb, a);
+        for (int r = 0; r < 4; ++r) {
+          h2_t v = __builtin_bit_cast(h2_t, (uint32_t)x[r]);
+          v = (v + c2[j]) * s2[j];  // exact integer q - z, then one rounding
+          y[r] = __builtin_bit_cast(uint32_t, v);
+        }
+        return u4_t{y[0], y[1], y[2], y[3]};
+      };
+      auto read_a16t = [&](int mb, int t) -> u4_t {
+        const int r = 16 * mb + c16;
+        const uint8_t* base = lds + slot * C::STAGE_BYTES + r * C::ROWB;
+        return *reinterpret_cast<const u4_t*>(base + swz<true>(r, 4 * t + kq) * 16);
+      };
+      u4_t b[2][NBW];
+      u4_t a[2][C::MB];
 #pragma unroll
-        for (int j = 0; j < NBW; ++j)
+      for (int j = 0; j < NBW; ++j) b[0][j] = deq(j, 0);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) acc[mb][j] = mfma_16x16x32<true>(a[t], bop[j][t], acc[mb][j]);
+      for (int mb = 0; mb < C::MB; ++mb) a[0][mb] = read_a16t(mb, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // One scheduling region per k-step: the next step's LDS reads first,
+      // then each MFMA followed by up to three VALU ops of the next step's
+      // dequantisation (the 16-cycle MFMA leaves room for three 4-cycle ops).
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int cb = t & 1, nb = cb ^ 1;
+        if (t < 3) {
+#pragma unroll
+          for (int mb = 0; mb < C::MB; ++mb) a[nb][mb] = read_a16t(mb, t + 1);
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) b[nb][j] = deq(j, t + 1);
+        }
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) acc[mb][j] = mfma_16x16x32<true>(a[cb][mb], b[cb][j], acc[mb][j]);
+        if (t < 3) __builtin_amdgcn_sched_group_barrier(0x100, C::MB, 0);
+#pragma unroll
+        for (int i = 0; i < C::MB * NBW; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     } else if constexpr (FMT == FMT_W16BF16) {
       u4_t bop[NBW][4];
@@ -354,16 +394,13 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
     }
   };
 
-  // ---- main loop: 3-slot pipeline, one barrier per 128-k group ---------------
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  auto gclamp = [&](int g) { return g < G ? g : G - 1; };
+  // ---- main loop: ST-slot pipeline, one barrier per 128-k group --------------
+  auto gclamp = [&](int g) { return g < Gl ? g : Gl - 1; };
   auto step = [&](auto slot_c, int g) {
     constexpr int cur = decltype(slot_c)::value;
-    using Ahead = std::integral_constant<int, (cur + 2) % 3>;
+    using Ahead = std::integral_constant<int, (cur + ST - 1) % ST>;
     __builtin_amdgcn_sched_barrier(0);  // keeps the last step's loads above the count below
-    wait_vm_lds<C::LPS>();  // this wave's loads of step g have landed (step g+1's may not)
+    wait_vm_lds<C::LPS * (ST - 2)>();   // this wave's loads of step g have landed (later ones may not)
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -372,19 +409,18 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
       pin(sraw[cur][j]);
       if constexpr (FMT != FMT_F4) pin(zraw[cur][j]);
     }
-    issue(Ahead{}, gclamp(g + 2));  // into the slot every wave finished reading at step g-1
-    if (g < G) compute(slot_c);
+    issue(Ahead{}, gclamp(g + ST - 1));  // into the slot every wave finished reading at step g-1
+    if (g < Gl) compute(slot_c);
   };
   // The wait count above assumes every load of a step is issued after every
-  // load of the step before, so no scheduling across these two.
-  issue(S0{}, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  issue(S1{}, gclamp(1));
-  __builtin_amdgcn_sched_barrier(0);
-  for (int g = 0; g < G; g += 3) {
-    step(S0{}, g);
-    step(S1{}, g + 1);
-    step(S2{}, g + 2);
+  // load of the step before, so no scheduling across the prologue's steps.
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    ((issue(std::integral_constant<int, I>{}, gclamp(I)), __builtin_amdgcn_sched_barrier(0)), ...);
+  }(std::make_integer_sequence<int, ST - 1>{});
+  for (int g = 0; g < Gl; g += ST) {
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (step(std::integral_constant<int, I>{}, g + I), ...);
+    }(std::make_integer_sequence<int, ST>{});
   }
   __builtin_amdgcn_s_waitcnt(0);  // no load into LDS may outlive the workgroup
 
@@ -398,6 +434,12 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
       if constexpr (GRP == GRP_DENSE) {
         if (m >= p.M) continue;
         const float sa = ACT_SCALE ? p.a_scale[m] : 1.f;
+        if (p.part) {
+          float* prow = p.part + ((int64_t)split * p.M + m) * p.N;
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) prow[nblk(j) * 16 + c16] = acc[mb][j][r] * sa;
+          continue;
+        }
 #pragma unroll
         for (int j = 0; j < NBW; ++j)
           store_out(p.out, (int64_t)m * p.N + nblk(j) * 16 + c16, acc[mb][j][r] * sa, p.out_bf16);
@@ -441,10 +483,10 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 // dispatch
 // ---------------------------------------------------------------------------
 
-template <int FMT, int BM, int NBW, int GRP>
+template <int FMT, int BM, int NBW, int GRP, int ST>
 static hipError_t launch_tiled_t(const TiledArgs& a, dim3 grid, hipStream_t s) {
-  using C = TCfg<FMT, BM, NBW>;
-  auto kern = qgemm_tiled<FMT, BM, NBW, GRP>;
+  using C = TCfg<FMT, BM, NBW, ST>;
+  auto kern = qgemm_tiled<FMT, BM, NBW, GRP, ST>;
   static bool attr_done = false;  // raise the dynamic LDS limit once per instantiation
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -452,27 +494,40 @@ static hipError_t launch_tiled_t(const TiledArgs& a, dim3 grid, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_done = true;
   }
-  const TimingEvents ev = take_timing();
-  if (ev.start)
-    hipExtLaunchKernelGGL(kern, grid, dim3(C::THREADS), (uint32_t)C::LDS_BYTES, s,
-                          static_cast<hipEvent_t>(ev.start), static_cast<hipEvent_t>(ev.stop), 0, a);
-  else
-    hipLaunchKernelGGL(kern, grid, dim3(C::THREADS), C::LDS_BYTES, s, a);
-  return hipGetLastError();
+  return launch_timed(kern, grid, dim3(C::THREADS), (size_t)C::LDS_BYTES, s, a);
+}
+
+template <int FMT, int BM, int NBW, int GRP>
+static hipError_t launch_tiled_s(const TiledCfgRt& cfg, const TiledArgs& a, dim3 grid, hipStream_t s) {
+  if constexpr (GRP == GRP_DENSE) {
+    if (cfg.stages == 4) return launch_tiled_t<FMT, BM, NBW, GRP, 4>(a, grid, s);
+    if constexpr (TCfg<FMT, BM, NBW, 5>::LDS_BYTES <= 160 * 1024 && TCfg<FMT, BM, NBW, 5>::LPS * 3 < 64)
+      if (cfg.stages == 5) return launch_tiled_t<FMT, BM, NBW, GRP, 5>(a, grid, s);
+  }
+  if (cfg.stages == 3 || cfg.stages == 0) return launch_tiled_t<FMT, BM, NBW, GRP, 3>(a, grid, s);
+  return hipErrorInvalidValue;
 }
 
 template <int FMT, int GRP>
 static hipError_t launch_tiled_f(const TiledCfgRt& cfg, const TiledArgs& a, dim3 grid, hipStream_t s) {
-  if (cfg.bm == 128 && cfg.nbw == 4) return launch_tiled_t<FMT, 128, 4, GRP>(a, grid, s);
-  if (cfg.bm == 64 && cfg.nbw == 4) return launch_tiled_t<FMT, 64, 4, GRP>(a, grid, s);
-  if (cfg.bm == 128 && cfg.nbw == 2) return launch_tiled_t<FMT, 128, 2, GRP>(a, grid, s);
-  if (cfg.bm == 64 && cfg.nbw == 2) return launch_tiled_t<FMT, 64, 2, GRP>(a, grid, s);
+  if (cfg.bm == 128 && cfg.nbw == 4) return launch_tiled_s<FMT, 128, 4, GRP>(cfg, a, grid, s);
+  if (cfg.bm == 64 && cfg.nbw == 4) return launch_tiled_s<FMT, 64, 4, GRP>(cfg, a, grid, s);
+  if (cfg.bm == 128 && cfg.nbw == 2) return launch_tiled_s<FMT, 128, 2, GRP>(cfg, a, grid, s);
+  if (cfg.bm == 64 && cfg.nbw == 2) return launch_tiled_s<FMT, 64, 2, GRP>(cfg, a, grid, s);
   return hipErrorInvalidValue;
 }
 
+// Every split must hold at least one group: the kernel's loads clamp group
+// indices into [first group of the split, last group of the split].
+static bool splits_cover_k(const TiledCfgRt& cfg, const TiledArgs& a, bool dense) {
+  const int splits = (dense && a.part) ? cfg.split : 1;
+  return a.G >= 1 && a.gps >= 1 && (int64_t)(splits - 1) * a.gps < a.G && (int64_t)splits * a.gps >= a.G;
+}
+
 int launch_tiled(int fmt, const TiledCfgRt& cfg, const TiledArgs& a, void* stream) {
+  if (!splits_cover_k(cfg, a, true)) return (int)hipErrorInvalidValue;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)(a.tiles_m * a.tiles_n));
+  const dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)(a.part ? cfg.split : 1));
   switch (fmt) {
     case FMT_W16F16: return (int)launch_tiled_f<FMT_W16F16, GRP_DENSE>(cfg, a, grid, s);
     case FMT_W16BF16: return (int)launch_tiled_f<FMT_W16BF16, GRP_DENSE>(cfg, a, grid, s);
@@ -485,6 +540,7 @@ int launch_tiled(int fmt, const TiledCfgRt& cfg, const TiledArgs& a, void* strea
 
 int launch_tiled_grouped(int fmt, int mode, const TiledCfgRt& cfg, const TiledArgs& a, int64_t blocks,
                          void* stream) {
+  if (!splits_cover_k(cfg, a, false) || a.part) return (int)hipErrorInvalidValue;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool paired = mode == GRP_GATHER && (a.epi == GEPI_SILU || a.epi == GEPI_SILU_F32);
   const int bn = 64 * cfg.nbw;

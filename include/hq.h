@@ -174,9 +174,10 @@ hq_status hq_plan_destroy(hq_plan* plan);
 /* Human-readable description of the plan's execution choice. */
 hq_status hq_plan_describe(const hq_plan* plan, int64_t m, char* buf, size_t len);
 
-/* Workspace a call with m rows needs, in bytes (0 if none).  A workspace
- * must be zero-filled once before its first use; every call leaves it in a
- * state valid for the next call.  Two calls that overlap in time must not
+/* Workspace a call with m rows needs, in bytes (0 if none): the fp32 partial
+ * tiles [split][m][n] when K is split over workgroups (a second kernel of the
+ * same call sums them in split order, so results are deterministic).  Its
+ * contents need no initialisation.  Two calls that overlap in time must not
  * share one workspace. */
 hq_status hq_plan_workspace_bytes(const hq_plan* plan, int64_t m, size_t* bytes);
 
@@ -221,8 +222,15 @@ hq_status hq_gemm(const hq_plan* plan, int64_t m, const void* a, const float* a_
  * per-row fp8 requant) -> down GEMM (+ top-k weighted combine into tokens).
  * ------------------------------------------------------------------------- */
 
-/* Rows per expert block that a grouped plan's kernels use for `t` tokens;
- * hq_moe_align must be called with this block_m. */
+/* Rows per expert block that a grouped plan's kernels use for `t` tokens
+ * routed to `topk` experts each: 16 when few slots land on each expert (the
+ * weight-streaming kernel), 64 or 128 when many do (the MFMA-tiled kernel), or
+ * what the plan's tuning fixes.  hq_moe_align must be called with this
+ * block_m, and hq_moe_gemm with the same t and topk: the GEMM reads
+ * sorted_ids and block_expert as laid out for this block size (a different
+ * block size reads past their end).  The gate_up and down plans of one layer
+ * share one alignment, so they must give the same block_m (true for
+ * equal tuning). */
 hq_status hq_moe_block_m(const hq_plan* plan, int64_t t, int topk, int* block_m);
 
 /* Size of the aligned slot array for `t` tokens: the largest possible
@@ -266,11 +274,13 @@ hq_status hq_moe_gemm(const hq_plan* plan, int64_t t, int topk, const void* a, c
                       const float* topk_w, const void* w, const void* meta, void* out, float* out_scale,
                       void* ws, size_t ws_bytes, void* stream);
 
-/* Kernel timing: the next GEMM kernel this thread launches records `start`
- * and `stop` (hipEvent_t, created by the caller with timing enabled) around
- * its own execution (the dispatch's start and end, without launch gaps), so
- * hipEventElapsedTime gives the kernel's duration.  The request is consumed
- * by that launch; passing NULL, NULL cancels a pending request. */
+/* Kernel timing: the next hq_gemm, hq_moe_gemm or hq_stream_read call on this
+ * thread records `start` (hipEvent_t, created by the caller with timing
+ * enabled) when its first kernel starts and `stop` when its last kernel ends
+ * (the split-K reduce, the fp8 requant or the combine's final pass included;
+ * dispatch times, so no host launch overhead), and hipEventElapsedTime gives
+ * the call's device duration.  The request is consumed by that call; passing
+ * NULL, NULL cancels a pending request. */
 hq_status hq_time_next_launch(void* start_event, void* stop_event);
 
 /* Bandwidth probe (measurement helper, not part of the GEMM): read `bytes`

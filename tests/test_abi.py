@@ -58,10 +58,12 @@ def test_abi_version_and_status_strings():
      hq.HQ_ERR_UNSUPPORTED),                       # int8 activations without scales
     (dict(epi="i32_acc"), hq.HQ_ERR_UNSUPPORTED),  # int32 accumulators need INT4 x INT8
     (dict(tuning=dict(tile_m=48)), hq.HQ_ERR_INVALID_ARG),
-    (dict(tuning=dict(tile_n=128)), hq.HQ_ERR_INVALID_ARG),
-    (dict(tuning=dict(waves=9)), hq.HQ_ERR_INVALID_ARG),
-    (dict(tuning=dict(stages=3)), hq.HQ_ERR_INVALID_ARG),
-    (dict(tuning=dict(tile_m=64, tile_n=64, stages=4)), hq.HQ_ERR_INVALID_ARG),  # register budget
+    (dict(tuning=dict(kernel=1, tile_n=128)), hq.HQ_ERR_INVALID_ARG),
+    (dict(tuning=dict(kernel=2, tile_n=192)), hq.HQ_ERR_INVALID_ARG),
+    (dict(tuning=dict(kernel=2, split_k=65)), hq.HQ_ERR_INVALID_ARG),
+    (dict(tuning=dict(kernel=1, waves=9)), hq.HQ_ERR_INVALID_ARG),
+    (dict(tuning=dict(kernel=1, stages=3)), hq.HQ_ERR_INVALID_ARG),
+    (dict(tuning=dict(kernel=1, tile_m=64, tile_n=64, stages=4)), hq.HQ_ERR_INVALID_ARG),  # register budget
 ])
 def test_plan_validation(kw, status):
     with pytest.raises(hq.HQError) as e:
@@ -278,6 +280,30 @@ def test_moe_plan_validation():
     p = hq.MoePlan(512, 7168, hq.w4a16("bf16", scale="f16"), 256, 64, "silu_mul")
     assert p.block_m(32, 8) == 16
     assert p.repacked_bytes() == (256 * 512 * 7168 // 2, 256 * 512 * 56 * 2)
+
+
+def test_moe_block_choice():
+    """Host logic: the block size follows the slots per expert, or the tuning."""
+    q = hq.w4a16("bf16", scale="f16")
+    p = hq.MoePlan(512, 7168, q, 256, 1 << 16, "silu_mul")
+    assert p.block_m(1, 8) == 16         # 0.03 slots per expert: weight streaming
+    assert p.block_m(512, 8) == 16       # 16 per expert
+    assert p.block_m(4096, 8) == 64      # 128 per expert: MFMA tiles
+    assert p.block_m(16384, 8) == 128    # 512 per expert
+    assert hq.MoePlan(512, 7168, q, 256, 64, "silu_mul", tuning=dict(tile_m=128)).block_m(1, 8) == 128
+    assert hq.MoePlan(512, 7168, q, 256, 64, "silu_mul", tuning=dict(kernel=2)).block_m(1, 8) == 64
+    assert hq.MoePlan(512, 7168, q, 256, 8192, "silu_mul", tuning=dict(kernel=1)).block_m(4096, 8) == 16
+    for bad in (dict(tile_m=32), dict(kernel=1, tile_m=64), dict(kernel=2, tile_m=16), dict(tile_n=64),
+                dict(tile_n=256, tile_m=64)):
+        n = 384 if bad.get("tile_n") == 256 else 512
+        with pytest.raises(hq.HQError) as e:
+            hq.MoePlan(n, 7168, q, 256, 64, "silu_mul", tuning=bad)
+        assert e.value.status == hq.HQ_ERR_UNSUPPORTED, bad
+    # the workspace follows the block size of the call
+    pq = hq.MoePlan(512, 7168, hq.w4a8_fp8(), 256, 8192, "silu_mul_qfp8")
+    b = ctypes.c_size_t()
+    assert hq.lib().hq_moe_workspace_bytes(pq._h, 4096, 8, ctypes.byref(b)) == 0
+    assert b.value >= hq.moe_max_padded(4096, 8, 256, 64) * (256 * 4 + 4)
 
 
 def test_moe_sizes_and_workspace():

@@ -99,7 +99,7 @@ def test_m_zero_is_noop_and_calls_repeat():
     a = d["a"].to(DEV)
     empty = plan.gemm(a[:0], w, meta)
     assert empty.shape == (0, N)
-    outs = [plan.gemm(a, w, meta) for _ in range(3)]  # the split-K counters re-arm themselves
+    outs = [plan.gemm(a, w, meta) for _ in range(3)]  # every call rewrites its partials
     torch.cuda.synchronize()
     for o in outs:
         assert torch.equal(o, outs[0])  # deterministic reduction order
@@ -254,6 +254,47 @@ def test_prefill_fp16_symmetric(M):
 def test_tiled_w4a16_shapes(tuning, act, zp):
     for (M, N, K) in [(200, 512, 1024), (1, 256, 128), (129, 768, 384)]:
         run_w4a16(M, N, K, act=act, zp=zp, tuning=tuning)
+
+
+@pytest.mark.parametrize("stages", [4, 5])
+@pytest.mark.parametrize("tuning", [dict(kernel=2, tile_m=64, tile_n=128), dict(kernel=2, tile_m=128, tile_n=256),
+                                    dict(kernel=2, tile_m=64, tile_n=256, split_k=3)])
+@pytest.mark.parametrize("act,zp", [("f16", "fixed"), ("bf16", "u4")])
+def test_tiled_deeper_pipeline(stages, tuning, act, zp):
+    # 4- and 5-group load pipelines (G = 1, 3, 8, 11 groups: shorter than,
+    # equal to and longer than the pipeline)
+    for (M, N, K) in [(70, 512, 128), (130, 256, 384), (64, 512, 1024), (200, 256, 1408)]:
+        run_w4a16(M, N, K, act=act, zp=zp, tuning=dict(tuning, stages=stages))
+
+
+@pytest.mark.parametrize("split", [2, 3, 5, 8])
+@pytest.mark.parametrize("act,zp", [("f16", "fixed"), ("bf16", "u4")])
+def test_tiled_split_k(split, act, zp):
+    # K split over workgroups + the second-pass reduce: an even split, uneven
+    # ones (G = 16 or 10 groups), ragged M, both tile widths
+    for (M, N, K, tn) in [(64, 512, 2048, 128), (40, 256, 1280, 256), (97, 384, 2048, 128)]:
+        run_w4a16(M, N, K, act=act, zp=zp, tuning=dict(kernel=2, tile_m=64, tile_n=tn, split_k=split))
+
+
+def test_tiled_split_k_w4a8_formats():
+    M, N, K = 48, 256, 2048
+    for tun in (dict(kernel=2, tile_m=64, tile_n=128, split_k=4), dict(kernel=2, tile_m=128, tile_n=256, split_k=3)):
+        _log(f"tiled split w4a8 {tun}")
+        d = datagen.w4a8_int(M, N, K)
+        plan = hq.Plan(N, K, hq.w4a8_int(), max_m=M, tuning=tun)
+        assert "split_k=" + str(tun["split_k"]) in plan.describe(M)
+        w, meta = plan.repack(torch.from_numpy(d["codes"]).to(DEV), d["scales"].to(DEV))
+        out = plan.gemm(d["a_codes"].to(DEV), w, meta, a_scale=d["a_scale"].to(DEV))
+        torch.cuda.synchronize()
+        ref = og.gemm_int4_int8(d["a_codes"].numpy(), d["a_scale"].numpy(), d["codes"], d["scales"].double().numpy())
+        _assert_ok(out.double().cpu().numpy(), ref, "bf16", "split w4a8-int")
+        d = datagen.w4a8_mxfp4(M, N, K)
+        plan = hq.Plan(N, K, hq.w4a8_mxfp4(), max_m=M, tuning=tun)
+        w, meta = plan.repack(torch.from_numpy(d["codes"]).to(DEV), e8m0=torch.from_numpy(d["e8m0"]).to(DEV))
+        out = plan.gemm(d["a_codes"].to(DEV), w, meta, a_scale=d["a_scale"].to(DEV))
+        torch.cuda.synchronize()
+        ref = og.gemm_mxfp4_fp8(d["a_codes"].numpy(), d["a_scale"].numpy(), d["codes"], d["e8m0"])
+        _assert_ok(out.double().cpu().numpy(), ref, "bf16", "split w4a8-mxfp4")
 
 
 @pytest.mark.parametrize("tuning", [dict(kernel=2, tile_m=64, tile_n=256), dict(kernel=2, tile_m=128, tile_n=256),

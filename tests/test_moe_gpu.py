@@ -60,16 +60,18 @@ def _quant(act):
 
 
 class Layer:
-    """Weights on the GPU (repacked for both activation types) + host copies."""
+    """Weights on the GPU (repacked for both activation types) + host copies.
+    `tuning` (same for both GEMMs) forces a kernel / block size."""
 
-    def __init__(self, E, H, I, key):
+    def __init__(self, E, H, I, key, tuning=None):
         self.E, self.H, self.I = E, H, I
         wts = datagen.moe_weights(E, H, I, key=key)
         self.w = wts
         self.dev = {}
         for act in ("bf16", "fp8"):
-            p1 = hq.MoePlan(2 * I, H, _quant(act), E, 4096, "silu_mul" if act == "bf16" else "silu_mul_qfp8")
-            p2 = hq.MoePlan(H, I, _quant(act), E, 4096, "topk_combine")
+            p1 = hq.MoePlan(2 * I, H, _quant(act), E, 4096, "silu_mul" if act == "bf16" else "silu_mul_qfp8",
+                            tuning=tuning)
+            p2 = hq.MoePlan(H, I, _quant(act), E, 4096, "topk_combine", tuning=tuning)
             w1, m1 = p1.repack(torch.from_numpy(wts["w1"]).to(DEV), wts["s1"].to(DEV))
             w2, m2 = p2.repack(torch.from_numpy(wts["w2"]).to(DEV), wts["s2"].to(DEV))
             self.dev[act] = (p1, p2, w1, m1, w2, m2)
@@ -79,12 +81,13 @@ class Layer:
 def run_layer(layer, T, act, topk, key=(5,), sample=None):
     """Run align -> gate_up -> down on the GPU; check every stage on sampled tokens."""
     E, H, I = layer.E, layer.H, layer.I
-    _log(f"moe layer E={E} H={H} I={I} T={T} topk={topk} act={act}")
+    _log(f"moe layer E={E} H={H} I={I} T={T} topk={topk} act={act} block_m={layer.dev[act][0].block_m(T, topk)}")
     r = datagen.moe_routing(T, E=E, topk=topk, key=key)
     x = datagen.moe_activations(T, H=H, act=act, key=key)
     p1, p2, w1, m1, w2, m2 = layer.dev[act]
     ids = torch.from_numpy(r["topk_ids"]).to(DEV)
     bm = p1.block_m(T, topk)
+    assert p2.block_m(T, topk) == bm
     sid, bexp, npad = hq.moe_align(ids, E, bm)
     if act == "bf16":
         a = x["x"].to(DEV)
@@ -146,6 +149,24 @@ def test_small_layer_all_tokens(small_layer, T, topk, act):
     run_layer(small_layer, T, act, topk, key=(11,))
 
 
+# the MFMA-tiled grouped kernel on every token: 64- and 128-row blocks, 128-
+# and 256-column tiles (gate_up n = 256: one or two paired tiles; down K = 128:
+# a single k group), mostly-empty blocks at small T
+TILED = [dict(kernel=2, tile_m=64, tile_n=128), dict(kernel=2, tile_m=128, tile_n=128),
+         dict(kernel=2, tile_m=64, tile_n=256)]
+
+
+@pytest.fixture(scope="module", params=range(len(TILED)), ids=["bm64_bn128", "bm128_bn128", "bm64_bn256"])
+def small_layer_tiled(request):
+    return Layer(8, 512, 128, key=(7,), tuning=TILED[request.param])
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp8"])
+@pytest.mark.parametrize("T,topk", [(3, 2), (200, 3), (700, 2)])
+def test_small_layer_tiled(small_layer_tiled, T, topk, act):
+    run_layer(small_layer_tiled, T, act, topk, key=(17,))
+
+
 def test_small_layer_repeat_calls_reuse_workspace(small_layer):
     # the fp32 combine accumulators and row maxima re-arm themselves: calls
     # in a row on the same workspace all pass
@@ -163,3 +184,19 @@ def full_layer():
 @pytest.mark.parametrize("T", [1, 32, 512, 4096])
 def test_full_layer(full_layer, T, act):
     run_layer(full_layer, T, act, TOPK, sample=12)
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp8"])
+def test_full_layer_tiled_128_rows(full_layer, act):
+    # T = 4096 again with the other tiled block size (and 256-column tiles)
+    tl = Layer.__new__(Layer)
+    tl.E, tl.H, tl.I, tl.w = full_layer.E, full_layer.H, full_layer.I, full_layer.w
+    tl.dev = {}
+    for a in ("bf16", "fp8"):
+        _, _, w1, m1, w2, m2 = full_layer.dev[a]
+        tun = dict(kernel=2, tile_m=128, tile_n=256)
+        p1 = hq.MoePlan(2 * tl.I, tl.H, _quant(a), tl.E, 4096, "silu_mul" if a == "bf16" else "silu_mul_qfp8",
+                        tuning=tun)
+        p2 = hq.MoePlan(tl.H, tl.I, _quant(a), tl.E, 4096, "topk_combine", tuning=tun)
+        tl.dev[a] = (p1, p2, w1, m1, w2, m2)
+    run_layer(tl, 4096, act, TOPK, sample=12)
