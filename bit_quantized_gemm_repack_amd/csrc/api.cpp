@@ -548,8 +548,10 @@ hq_status hq_gemm(const hq_plan* p, int64_t m, const void* a, const float* a_sca
 // grouped (MoE)
 // ---------------------------------------------------------------------------
 
+// Longest possible aligned slot array: every expert's segment, plus the one
+// for out-of-range ids, padded up to whole blocks.
 static int64_t moe_max_padded(int64_t t, int topk, int E, int bm) {
-  const int64_t raw = t * topk + (int64_t)E * (bm - 1);
+  const int64_t raw = t * topk + (int64_t)(E + 1) * (bm - 1);
   return (raw + bm - 1) / bm * bm;
 }
 
@@ -633,7 +635,7 @@ hq_status hq_moe_align(int64_t t, int topk, int num_experts, int block_m, const 
 }
 
 struct MoeWs {
-  size_t act32, amax, y32, total;
+  size_t act32, amax, rows, total;
 };
 
 static MoeWs moe_ws(const hq_plan* p, int64_t t, int topk) {
@@ -643,8 +645,8 @@ static MoeWs moe_ws(const hq_plan* p, int64_t t, int topk) {
     w.act32 = align256((size_t)mp * (size_t)(p->layer.n / 2) * 4);
     w.amax = align256((size_t)mp * 4);
   }
-  if (p->compute.epi == HQ_EPI_TOPK_COMBINE) w.y32 = align256((size_t)t * (size_t)p->layer.n * 4);
-  w.total = w.act32 + w.amax + w.y32;
+  if (p->compute.epi == HQ_EPI_TOPK_COMBINE) w.rows = align256((size_t)t * topk * (size_t)p->layer.n * 4);
+  w.total = w.act32 + w.amax + w.rows;
   return w;
 }
 
@@ -786,7 +788,7 @@ hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, cons
                                    std::min<int64_t>(mp, (int64_t)bm * t * topk), static_cast<uint8_t*>(out),
                                    out_scale, stream);
     if (err == hipSuccess && epi == HQ_EPI_TOPK_COMBINE)
-      err = hq::launch_moe_finalize(f32_out, out, t * N, p->layer.q.out == HQ_BF16, stream);
+      err = hq::launch_moe_combine(f32_out, topk, t, N, out, p->layer.q.out == HQ_BF16, stream);
     hq::arm_timing({nullptr, nullptr});
     if (err != hipSuccess) return fail(HQ_ERR_HIP, "grouped gemm launch: %s", hipGetErrorString((hipError_t)err));
     return ok();

@@ -217,7 +217,7 @@ struct SkinnyArgs {
   int64_t s_expert;             // scale elements per expert
   int64_t z_expert;             // zero-point words per expert
   int64_t e8_expert;            // E8M0 bytes per expert
-  float* f32_out;               // gate_up fp32 act (QFP8) or down fp32 token accumulators
+  float* f32_out;               // gate_up fp32 act (QFP8) or down weighted slot rows [n_slots][N]
   uint32_t* row_amax;           // gate_up QFP8: per aligned row max |act| (float bits)
 };
 
@@ -235,7 +235,8 @@ int launch_moe_align(int64_t t, int topk, int num_experts, int block_m, const in
                      int32_t* block_expert, int32_t* num_padded, void* stream);
 int launch_moe_requant(const float* act32, uint32_t* row_amax, const int32_t* sorted_ids, const int32_t* num_padded,
                        int n_slots, int inter, int64_t max_rows, uint8_t* codes, float* scales, void* stream);
-int launch_moe_finalize(float* y32, void* y, int64_t elems, int out_bf16, void* stream);
+// y[t][n] = RNE(sum over the token's topk weighted slot rows), rows [t*topk][n] fp32
+int launch_moe_combine(const float* rows, int topk, int64_t t, int64_t n, void* y, int out_bf16, void* stream);
 
 struct TiledArgs {
   const void* a;

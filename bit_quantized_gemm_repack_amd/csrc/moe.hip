@@ -1,6 +1,6 @@
 // Mixture-of-experts helpers around the grouped GEMM: the token sort / align
 // by expert, the per-row fp8 requantisation of the gate_up activation, and
-// the final fp32 -> bf16/fp16 conversion of the combined down projection.
+// the top-k combine of the down projection's weighted slot rows.
 //
 // The pages describe a dedicated MoE backend whose "Grouped" GEMM path is run
 // with W4A16 or W4A8 weights (Humming page on news.ditty.ir, summary;
@@ -17,53 +17,69 @@ namespace hq {
 
 // One workgroup: histogram of expert ids in LDS, padded exclusive prefix
 // sum, sentinel fill, block -> expert table, then the scatter of slot ids.
-// Slot ids outside [0, E) are ignored (left out of every segment).
+// Slot ids outside [0, E) go to one trailing segment (pseudo-expert E) whose
+// blocks are marked block_expert = -1: the GEMMs give those slots no output
+// (gate_up) or a zero row (down), so they add nothing to the combine.
 __global__ void __launch_bounds__(1024) moe_align_kernel(const int32_t* __restrict__ ids, int n_slots, int E,
                                                          int bm, int32_t* __restrict__ sorted_ids,
                                                          int32_t* __restrict__ block_expert,
                                                          int32_t* __restrict__ num_padded) {
   extern __shared__ int sh[];
-  int* cnt = sh;           // [E]
-  int* off = sh + E;       // [E + 1] padded segment starts
-  int* cur = sh + 2 * E + 1;  // [E] scatter cursors
+  const int S = E + 1;         // segments: the experts, then the out-of-range slots
+  int* cnt = sh;               // [S]
+  int* off = sh + S;           // [S + 1] padded segment starts
+  int* cur = sh + 2 * S + 1;   // [S] scatter cursors
   const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += blockDim.x) {
+  for (int e = tid; e < S; e += blockDim.x) {
     cnt[e] = 0;
     cur[e] = 0;
   }
   __syncthreads();
   for (int i = tid; i < n_slots; i += blockDim.x) {
     const int e = ids[i];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    atomicAdd(&cnt[(e >= 0 && e < E) ? e : E], 1);
   }
   __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int e = 0; e < E; ++e) {
+  // padded sizes, then an inclusive scan over the segments by the first wave
+  // (each lane owns a contiguous run of segments)
+  if (tid < 64) {
+    const int per = (S + 63) / 64;
+    const int b0 = tid * per, b1 = min(S, b0 + per);
+    int run = 0;
+    for (int e = b0; e < b1; ++e) run += (cnt[e] + bm - 1) / bm * bm;
+    int incl = run;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d, 64);
+      if (tid >= d) incl += o;
+    }
+    int acc = incl - run;  // exclusive start of this lane's run
+    for (int e = b0; e < b1; ++e) {
       off[e] = acc;
       acc += (cnt[e] + bm - 1) / bm * bm;
     }
-    off[E] = acc;
-    *num_padded = acc;
+    if (tid == 63) {
+      off[S] = incl;
+      *num_padded = incl;
+    }
   }
   __syncthreads();
-  const int total = off[E];
+  const int total = off[S];
   for (int i = tid; i < total; i += blockDim.x) sorted_ids[i] = n_slots;
   for (int b = tid; b < total / bm; b += blockDim.x) {
-    // the expert whose padded segment contains row b * bm
-    int lo = 0, hi = E;  // off[lo] <= b*bm < off[hi]
+    // the segment that contains row b * bm
+    int lo = 0, hi = S;  // off[lo] <= b*bm < off[hi]
     const int row = b * bm;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (off[mid] <= row) lo = mid;
       else hi = mid;
     }
-    block_expert[b] = lo;
+    block_expert[b] = lo < E ? lo : -1;
   }
   __syncthreads();  // sentinel fill (global) before the scatter in this workgroup
   for (int i = tid; i < n_slots; i += blockDim.x) {
-    const int e = ids[i];
-    if (e < 0 || e >= E) continue;
+    const int e0 = ids[i];
+    const int e = (e0 >= 0 && e0 < E) ? e0 : E;
     const int pos = off[e] + atomicAdd(&cur[e], 1);
     sorted_ids[pos] = i;
   }
@@ -113,18 +129,33 @@ __global__ void __launch_bounds__(256) moe_requant_kernel(const float* __restric
   }
 }
 
-// y = RNE(y32) in the output dtype, and y32 back to zero for the next call.
-__global__ void __launch_bounds__(256) moe_finalize_kernel(float* __restrict__ y32, void* __restrict__ y,
-                                                           int64_t elems, int out_bf16) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < elems; i += (int64_t)gridDim.x * blockDim.x) {
-    store_out(y, i, y32[i], out_bf16);
-    y32[i] = 0.f;
+// The combine: y[t, n] = RNE(sum_j rows[t * topk + j][n]) over the token's
+// topk slot rows (each already weighted), summed in slot order; four outputs
+// per thread (n is a multiple of 64).
+__global__ void __launch_bounds__(256) moe_combine_kernel(const float4* __restrict__ rows, int topk, int64_t n4,
+                                                          int64_t elems4, uint2* __restrict__ y, int out_bf16) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < elems4; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / n4, c = i - t * n4;
+    const float4* r = rows + t * topk * n4 + c;
+    float4 v = r[0];
+    for (int j = 1; j < topk; ++j) {
+      const float4 w = r[(int64_t)j * n4];
+      v.x += w.x;
+      v.y += w.y;
+      v.z += w.z;
+      v.w += w.w;
+    }
+    const uint32_t h0 = out_bf16 ? float_to_bf16_bits(v.x) : float_to_f16_bits(v.x);
+    const uint32_t h1 = out_bf16 ? float_to_bf16_bits(v.y) : float_to_f16_bits(v.y);
+    const uint32_t h2 = out_bf16 ? float_to_bf16_bits(v.z) : float_to_f16_bits(v.z);
+    const uint32_t h3 = out_bf16 ? float_to_bf16_bits(v.w) : float_to_f16_bits(v.w);
+    y[i] = uint2{h0 | (h1 << 16), h2 | (h3 << 16)};
   }
 }
 
 int launch_moe_align(int64_t t, int topk, int num_experts, int block_m, const int32_t* ids, int32_t* sorted_ids,
                      int32_t* block_expert, int32_t* num_padded, void* stream) {
-  const size_t lds = (size_t)(3 * num_experts + 1) * sizeof(int);
+  const size_t lds = (size_t)(3 * (num_experts + 1) + 1) * sizeof(int);
   hipLaunchKernelGGL(moe_align_kernel, dim3(1), dim3(1024), lds, static_cast<hipStream_t>(stream), ids,
                      (int)(t * topk), num_experts, block_m, sorted_ids, block_expert, num_padded);
   return (int)hipGetLastError();
@@ -138,12 +169,14 @@ int launch_moe_requant(const float* act32, uint32_t* row_amax, const int32_t* so
                            max_rows, codes, scales);
 }
 
-int launch_moe_finalize(float* y32, void* y, int64_t elems, int out_bf16, void* stream) {
-  int64_t blocks = (elems + 255) / 256;
+int launch_moe_combine(const float* rows, int topk, int64_t t, int64_t n, void* y, int out_bf16, void* stream) {
+  const int64_t elems4 = t * n / 4;
+  int64_t blocks = (elems4 + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;
-  return (int)launch_timed(moe_finalize_kernel, dim3((unsigned)blocks), dim3(256), 0,
-                           static_cast<hipStream_t>(stream), y32, y, elems, out_bf16);
+  return (int)launch_timed(moe_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                           reinterpret_cast<const float4*>(rows), topk, n / 4, elems4, static_cast<uint2*>(y),
+                           out_bf16);
 }
 
 }  // namespace hq

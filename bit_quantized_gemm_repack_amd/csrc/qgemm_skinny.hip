@@ -91,6 +91,18 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   if constexpr (GRP != GRP_DENSE) {
     if (m0 >= *p.num_padded) return;
     const int64_t ex = p.block_expert[blockIdx.z];
+    if (ex < 0) {
+      // slots whose expert id is out of range: no gate_up output; the down
+      // GEMM writes their (weighted) slot rows as zeros for the combine
+      if constexpr (GRP == GRP_SORTED) {
+        for (int e = threadIdx.x; e < 16 * MB * NB * 16; e += blockDim.x) {
+          const int r = e / (NB * 16), cc = e - r * (NB * 16);
+          const int id = p.sorted_ids[m0 + r];
+          if (id < p.n_slots) p.f32_out[(int64_t)id * p.N + (nt * NB + cc / 16) * 16 + (cc & 15)] = 0.f;
+        }
+      }
+      return;
+    }
     wbytes += ex * p.w_expert;
     if constexpr (FMT == FMT_F4) {
       e8 += ex * p.e8_expert;
@@ -335,7 +347,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
         }
       } else {
         const float sa = FI::kActScale ? p.a_scale[m] : 1.f;
-        atomicAdd(p.f32_out + (int64_t)tok * p.N + n, v * sa * p.topk_w[id]);
+        p.f32_out[(int64_t)id * p.N + n] = v * sa * p.topk_w[id];  // this slot's weighted row
       }
       continue;
     }

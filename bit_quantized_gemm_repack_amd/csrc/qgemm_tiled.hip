@@ -134,6 +134,18 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
   if constexpr (GRP != GRP_DENSE) {
     if (m0 >= *p.num_padded) return;
     const int64_t ex = p.block_expert[tm];
+    if (ex < 0) {
+      // slots whose expert id is out of range: no gate_up output; the down
+      // GEMM writes their (weighted) slot rows as zeros for the combine
+      if constexpr (GRP == GRP_SORTED) {
+        for (int e = tid; e < BM * C::BN; e += C::THREADS) {
+          const int r = e / C::BN, cc = e - r * C::BN;
+          const int id = p.sorted_ids[m0 + r];
+          if (id < p.n_slots) p.f32_out[(int64_t)id * p.N + tn * C::BN + cc] = 0.f;
+        }
+      }
+      return;
+    }
     wbytes += ex * p.w_expert;
     if constexpr (FMT == FMT_F4) {
       e8 += ex * p.e8_expert;
@@ -470,9 +482,9 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
           }
         } else {
           const float sa = (ACT_SCALE ? p.a_scale[m] : 1.f) * p.topk_w[id];
+          float* row = p.f32_out + (int64_t)id * p.N;  // this slot's weighted row
 #pragma unroll
-          for (int j = 0; j < NBW; ++j)
-            atomicAdd(p.f32_out + (int64_t)tok * p.N + nblk(j) * 16 + c16, acc[mb][j][r] * sa);
+          for (int j = 0; j < NBW; ++j) row[nblk(j) * 16 + c16] = acc[mb][j][r] * sa;
         }
       }
     }

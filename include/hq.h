@@ -233,16 +233,19 @@ hq_status hq_gemm(const hq_plan* plan, int64_t m, const void* a, const float* a_
  * equal tuning). */
 hq_status hq_moe_block_m(const hq_plan* plan, int64_t t, int topk, int* block_m);
 
-/* Size of the aligned slot array for `t` tokens: the largest possible
- * sum over experts of count_e rounded up to block_m, i.e.
- * t*topk + num_experts*(block_m - 1) rounded up to block_m. */
+/* Size of the aligned slot array for `t` tokens: the largest possible sum
+ * over the num_experts + 1 segments (the experts, then out-of-range ids) of
+ * count rounded up to block_m, i.e. t*topk + (num_experts + 1)*(block_m - 1)
+ * rounded up to block_m. */
 hq_status hq_moe_max_padded(int64_t t, int topk, int num_experts, int block_m, int64_t* max_padded);
 
-/* Token sort / align by expert.  topk_ids: device int32 [t, topk], each in
- * [0, num_experts).  Outputs (device, int32): sorted_ids[max_padded]: flat
- * slot indices t*topk + j grouped by expert, each expert's segment padded to
- * a multiple of block_m with the sentinel t*topk (order inside a segment is
- * unspecified); block_expert[max_padded / block_m]: the expert of each block;
+/* Token sort / align by expert.  topk_ids: device int32 [t, topk].  Outputs
+ * (device, int32): sorted_ids[max_padded]: flat slot indices t*topk + j
+ * grouped by expert in increasing expert order, each expert's segment padded
+ * to a multiple of block_m with the sentinel t*topk (order inside a segment
+ * is unspecified); slots whose id is outside [0, num_experts) (for example
+ * experts masked with -1) form one last segment; block_expert[max_padded /
+ * block_m]: the expert of each block, -1 for the out-of-range segment;
  * num_padded[1]: the used length.  One workgroup; t * topk <= 2^20. */
 hq_status hq_moe_align(int64_t t, int topk, int num_experts, int block_m, const int32_t* topk_ids,
                        int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded, void* stream);
@@ -260,14 +263,21 @@ hq_status hq_moe_align(int64_t t, int topk, int num_experts, int block_m, const 
  *   epi HQ_EPI_TOPK_COMBINE   down: row r of `a` [max_padded, k] is the
  *                             intermediate of slot sorted_ids[r];
  *                             out = y [t, n] (plan out dtype),
- *                             y[tok] = sum_j topk_w[tok, j] * (a_row . W_e^T)
- *                             accumulated in fp32.
+ *                             y[tok] = sum_j topk_w[tok, j] * (a_row . W_e^T):
+ *                             each slot's weighted fp32 row goes to the
+ *                             workspace, then a second kernel sums a token's
+ *                             topk rows in slot order and rounds once, so the
+ *                             result is deterministic.  Slots with an
+ *                             out-of-range expert id contribute zero.
  *   epi HQ_EPI_NONE           gate_up rows without the activation: out
  *                             [max_padded, n] (plan out dtype).
  * a_scale: per-row fp32 scales of 8-bit activations (per token for gate_up,
  * per aligned row for down), else NULL.  topk_w: device fp32 [t, topk]
- * (TOPK_COMBINE only).  Rows of padding slots are left unwritten.  ws: the
- * workspace of hq_moe_workspace_bytes, zero-filled once before first use. */
+ * (TOPK_COMBINE only).  Rows of padding slots (and, for gate_up, of slots
+ * with an out-of-range expert id) are left unwritten.  ws: the workspace of
+ * hq_moe_workspace_bytes (the fp8 requant's fp32 rows and row maxima, or the
+ * combine's t*topk weighted slot rows), zero-filled once before first use
+ * (the row maxima are re-armed by every call). */
 hq_status hq_moe_workspace_bytes(const hq_plan* plan, int64_t t, int topk, size_t* bytes);
 hq_status hq_moe_gemm(const hq_plan* plan, int64_t t, int topk, const void* a, const float* a_scale,
                       const int32_t* sorted_ids, const int32_t* block_expert, const int32_t* num_padded,

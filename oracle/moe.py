@@ -39,19 +39,23 @@ def check_align(topk_ids, num_experts: int, block_m: int, sorted_ids, block_expe
 
     Valid means: the non-sentinel entries of sorted_ids[:num_padded] are a
     permutation of the flat slots 0..T*topk-1; every block holds slots of one
-    expert only (block_expert[b]); expert e's slots occupy exactly
-    ceil(count_e / block_m) consecutive blocks, experts in increasing order;
-    every other entry in [0, num_padded) is the sentinel T*topk.
+    segment only; the segments are the experts 0..E-1 in increasing order and
+    then one segment for ids outside [0, E) (block_expert -1); a segment with
+    c slots occupies exactly ceil(c / block_m) consecutive blocks; every other
+    entry in [0, num_padded) is the sentinel T*topk.  (The pages do not
+    describe the routing data structures; this is the layout the grouped GEMM
+    needs: each expert's slots contiguous and padded to whole row blocks.)
     """
     ids = np.asarray(topk_ids).astype(np.int64)
     T, topk = ids.shape
     flat = ids.reshape(-1)
+    seg = np.where((flat >= 0) & (flat < num_experts), flat, num_experts)  # segment of each slot
     sentinel = T * topk
     npad = int(np.asarray(num_padded).reshape(-1)[0])
     sid = np.asarray(sorted_ids).astype(np.int64)[:npad]
     bexp = np.asarray(block_expert).astype(np.int64)
     assert npad % block_m == 0, "num_padded is not a multiple of block_m"
-    counts = np.bincount(flat, minlength=num_experts)
+    counts = np.bincount(seg, minlength=num_experts + 1)
     expect_blocks = -(-counts // block_m)
     assert npad == int(expect_blocks.sum()) * block_m, "num_padded is not the minimum padded length"
     valid = sid[sid != sentinel]
@@ -60,17 +64,15 @@ def check_align(topk_ids, num_experts: int, block_m: int, sorted_ids, block_expe
         "sorted ids are not a permutation of the slots"
     nb = npad // block_m
     b = 0
-    for e in range(num_experts):
+    for e in range(num_experts + 1):
         for _ in range(int(expect_blocks[e])):
-            assert bexp[b] == e, f"block {b} should belong to expert {e}"
+            want = e if e < num_experts else -1
+            assert bexp[b] == want, f"block {b} should belong to segment {want}"
             rows = sid[b * block_m : (b + 1) * block_m]
             rows = rows[rows != sentinel]
-            assert np.all(flat[rows] == e), f"block {b} holds slots of another expert"
+            assert np.all(seg[rows] == e), f"block {b} holds slots of another segment"
             b += 1
     assert b == nb
-    # each expert's valid rows come first within its segment? not required;
-    # only that the segment holds exactly count_e valid slots (checked above
-    # through the permutation + per-block expert test).
     return True
 
 

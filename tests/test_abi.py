@@ -307,15 +307,18 @@ def test_moe_block_choice():
 
 
 def test_moe_sizes_and_workspace():
-    assert hq.moe_max_padded(1, 8, 256, 16) == 8 + 256 * 15 + 8  # rounded up to 16
-    assert hq.moe_max_padded(4096, 8, 256, 16) == 32768 + 256 * 15
+    # every expert's segment + the out-of-range segment, padded, rounded up to 16
+    assert hq.moe_max_padded(1, 8, 256, 16) == 8 + 257 * 15 + 9
+    assert hq.moe_max_padded(4096, 8, 256, 16) == 32768 + 257 * 15 + 1
+    assert hq.moe_max_padded(4096, 8, 256, 64) == 32768 + 257 * 63 + 1
     pq = hq.MoePlan(512, 7168, hq.w4a8_fp8(), 256, 4096, "silu_mul_qfp8")
     b = ctypes.c_size_t()
     assert hq.lib().hq_moe_workspace_bytes(pq._h, 32, 8, ctypes.byref(b)) == 0
     mp = hq.moe_max_padded(32, 8, 256, 16)
     assert b.value >= mp * 256 * 4 + mp * 4
     pc = hq.MoePlan(7168, 256, hq.w4a16("bf16", scale="f16"), 256, 4096, "topk_combine")
-    assert hq.lib().hq_moe_workspace_bytes(pc._h, 32, 8, ctypes.byref(b)) == 0 and b.value >= 32 * 7168 * 4
+    # the combine's weighted slot rows: t * topk rows of n fp32
+    assert hq.lib().hq_moe_workspace_bytes(pc._h, 32, 8, ctypes.byref(b)) == 0 and b.value >= 32 * 8 * 7168 * 4
 
 
 def test_moe_call_validation():

@@ -40,6 +40,15 @@ def test_align_invariants(T):
     om.check_align(r["topk_ids"], E_FULL, 16, sid.cpu().numpy(), bexp.cpu().numpy(), npad.cpu().numpy())
 
 
+def test_align_out_of_range_ids():
+    _log("moe align out-of-range ids")
+    ids = np.array([[0, -1], [3, 4], [2, 0], [-1, 7], [1, 1], [9, 9]], dtype=np.int32)
+    for bm in (16, 64):
+        sid, bexp, npad = hq.moe_align(torch.from_numpy(ids).to(DEV), 4, bm)
+        torch.cuda.synchronize()
+        om.check_align(ids, 4, bm, sid.cpu().numpy(), bexp.cpu().numpy(), npad.cpu().numpy())
+
+
 def test_align_degenerate_cases():
     _log("moe align degenerate")
     # every slot on one expert; one expert only; block of 64
@@ -78,11 +87,20 @@ class Layer:
         torch.cuda.synchronize()
 
 
-def run_layer(layer, T, act, topk, key=(5,), sample=None):
-    """Run align -> gate_up -> down on the GPU; check every stage on sampled tokens."""
+def run_layer(layer, T, act, topk, key=(5,), sample=None, masked=0.0):
+    """Run align -> gate_up -> down on the GPU; check every stage on sampled tokens.
+    `masked`: fraction of slots whose expert id is replaced by an out-of-range
+    one (-1 or E + 3); those slots must add nothing to y."""
     E, H, I = layer.E, layer.H, layer.I
-    _log(f"moe layer E={E} H={H} I={I} T={T} topk={topk} act={act} block_m={layer.dev[act][0].block_m(T, topk)}")
+    _log(f"moe layer E={E} H={H} I={I} T={T} topk={topk} act={act} block_m={layer.dev[act][0].block_m(T, topk)} "
+         f"masked={masked}")
     r = datagen.moe_routing(T, E=E, topk=topk, key=key)
+    if masked:
+        rng = np.random.default_rng(99)
+        ids = r["topk_ids"].copy()
+        hit = rng.random(ids.shape) < masked
+        ids[hit] = np.where(rng.random(ids.shape) < 0.5, -1, E + 3)[hit]
+        r = dict(r, topk_ids=ids)
     x = datagen.moe_activations(T, H=H, act=act, key=key)
     p1, p2, w1, m1, w2, m2 = layer.dev[act]
     ids = torch.from_numpy(r["topk_ids"]).to(DEV)
@@ -108,9 +126,12 @@ def run_layer(layer, T, act, topk, key=(5,), sample=None):
     rows = [i for i in range(npad_h) if sid_h[i] < T * topk and int(sid_h[i]) // topk in tokset]
     rows = np.array(rows, dtype=np.int64)
     slot = sid_h[rows]
+    flat = r["topk_ids"].reshape(-1)
+    in_range = (flat[slot] >= 0) & (flat[slot] < E)
+    assert np.array_equal(bexp_h[rows // bm], np.where(in_range, flat[slot], -1))
+    rows, slot = rows[in_range], slot[in_range]  # out-of-range slots: no gate_up row, nothing in y
     row_tok = slot // topk
     row_exp = bexp_h[rows // bm]
-    assert np.array_equal(row_exp, r["topk_ids"].reshape(-1)[slot])
 
     # gate_up: oracle on the GPU's stage input (the same x)
     if act == "bf16":
@@ -165,6 +186,13 @@ def small_layer_tiled(request):
 @pytest.mark.parametrize("T,topk", [(3, 2), (200, 3), (700, 2)])
 def test_small_layer_tiled(small_layer_tiled, T, topk, act):
     run_layer(small_layer_tiled, T, act, topk, key=(17,))
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp8"])
+@pytest.mark.parametrize("T,topk,tiled", [(40, 3, False), (300, 2, True)])
+def test_small_layer_masked_experts(small_layer, small_layer_tiled, T, topk, tiled, act):
+    # slots routed to -1 or past the last expert: dropped from the combine
+    run_layer(small_layer_tiled if tiled else small_layer, T, act, topk, key=(19,), masked=0.15)
 
 
 def test_small_layer_repeat_calls_reuse_workspace(small_layer):

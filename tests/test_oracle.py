@@ -325,13 +325,28 @@ def test_moe_combine_matches_per_token_loop():
 def _align_ref(ids, E, bm):
     flat = ids.reshape(-1)
     sid, bexp = [], []
-    for e in range(E):
-        rows = list(np.nonzero(flat == e)[0])
+    for e in range(E + 1):  # the experts, then the out-of-range ids
+        sel = (flat == e) if e < E else ((flat < 0) | (flat >= E))
+        rows = list(np.nonzero(sel)[0])
         nb = -(-len(rows) // bm)
         rows += [flat.size] * (nb * bm - len(rows))
         sid += rows
-        bexp += [e] * nb
+        bexp += [e if e < E else -1] * nb
     return np.array(sid), np.array(bexp), np.array([len(sid)])
+
+
+def test_align_out_of_range_ids_form_the_last_segment():
+    ids = np.array([[0, -1], [3, 4], [2, 0], [-1, 7], [1, 1]])  # E = 4: -1, 4 and 7 are out of range
+    sid, bexp, npad = _align_ref(ids, 4, 2)
+    assert MO.check_align(ids, 4, 2, sid, bexp, npad)
+    assert list(bexp[-2:]) == [-1, -1] and sorted(sid[-4:]) == [1, 3, 6, 7]
+    be = bexp.copy()
+    be[-1] = 3  # the out-of-range block labelled as an expert
+    with pytest.raises(AssertionError):
+        MO.check_align(ids, 4, 2, sid, be, npad)
+    # dropping the out-of-range segment is not a valid alignment
+    with pytest.raises(AssertionError):
+        MO.check_align(ids, 4, 2, sid[:-4], bexp[:-2], npad - 4)
 
 
 def test_align_invariants_accept_and_reject():
