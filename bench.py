@@ -14,9 +14,13 @@ Timings
   * ms_per_step: K steps replayed as HIP graphs (one graph per pool rotation),
     bracketed by synchronisations, timed with events on the launch stream.
     `value` = algorithmic bytes of the sweep / ms_per_step (GB/s).
-  * roofline: the same K steps launched eagerly, each kernel bracketed by HIP
-    events recorded around its own dispatch (hq_time_next_launch); achieved =
-    algorithmic bytes per launch / mean kernel duration.
+  * roofline: the same K steps launched eagerly, each hq_gemm call bracketed
+    by HIP events recorded at the start of its first dispatch and the end of
+    its last (hq_time_next_launch; a call is one GEMM kernel, plus the
+    split-K reduce where K is split); achieved = algorithmic bytes per call /
+    mean call duration.  traffic: HBM bytes per call from the committed
+    FETCH_SIZE / WRITE_SIZE counter summary, used only while the kernel
+    sources it was taken on are unchanged (source hash), else null.
   * cpu_baseline: the CPU oracle (oracle/, float64 dequantise + GEMM) on a
     bounded sample of the same points, on this host's cores.
 
@@ -47,6 +51,35 @@ BF16_PEAK_TFLOPS = 2500.0
 METRIC = "quantized GEMM TFLOPS and effective HBM GB/s (% of roofline) vs M"
 WORKLOAD = ("dense W4A16 decode sweep: M in {1,4,16,64} x (N,K) in {(4096,4096),(14336,4096),(4096,14336)}, "
             "bf16 activations, uint4 weights (group 128, bf16 scales, uint4 zero points), bf16 output")
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qgemm_decode_sweep_traffic.json")
+
+
+def kernel_source_hash():
+    """sha256 over the library's kernel and host sources (sorted by name)."""
+    import hashlib
+
+    csrc = os.path.join(ROOT, "bit_quantized_gemm_repack_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".cpp", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per call from the counter summary, if taken on these sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_call")
 
 
 def algo_bytes(M, N, K):
@@ -292,8 +325,9 @@ def main():
                    "weight_pool_rotations": R, "timing": "HIP graph replay per step; kernel durations from "
                                                          "dispatch-bracketing HIP events"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "hq::qgemm_skinny (all instantiations of the sweep)",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "kernel": "hq_gemm calls of the sweep: hq::qgemm_skinny / hq::qgemm_tiled "
+                               "(+ hq::splitk_reduce_kernel where K is split)",
                      "mean_kernel_us": round(mean_kernel_us, 3), "mean_algorithmic_bytes": int(mean_bytes)},
         "cpu_baseline": cpu,
         "points": per_point,

@@ -169,6 +169,15 @@ Exec choose_exec(const hq_plan* p, int64_t m) {
     c.waves = 8;
   }
   c.waves = (int)std::min<int64_t>(c.waves, std::max<int64_t>(1, G));
+  // 5..16 rows and long K: the activation block is re-read by every
+  // column-block workgroup; 4 column blocks per workgroup cut that 4x, and
+  // a 4-way K split keeps 4x the workgroups (partials summed by the reduce).
+  int64_t auto_split = 1;
+  if (c.mb == 1 && m > 4 && G >= 64 && N % 64 == 0 && N / 64 >= 32) {
+    c.nb = 4;
+    c.waves = 8;
+    auto_split = 4;
+  }
   if (u.tile_m) c.mb = u.tile_m / 16;
   if (u.tile_n) c.nb = u.tile_n / 16;
   if (u.waves) c.waves = u.waves;
@@ -177,8 +186,9 @@ Exec choose_exec(const hq_plan* p, int64_t m) {
   if (!u.waves && c.waves > 8 && !(c.mb == 1 && c.nb == 1 && c.stages <= 4)) c.waves = 8;
   const int64_t ntiles = N / (16 * c.nb);
   const int64_t mch = cdiv(mm, 16 * c.mb);
-  int64_t split = 1;
+  int64_t split = (u.tile_m || u.tile_n || u.waves) ? 1 : auto_split;
   if (u.split_k) split = u.split_k;
+  if (p->compute.epi == HQ_EPI_I32_ACC) split = u.split_k ? u.split_k : 1;
   split = std::max<int64_t>(1, std::min<int64_t>(split, G));
   split = cdiv(G, cdiv(G, split));  // no empty split
   c.split = (int)split;
