@@ -131,8 +131,21 @@ Exec choose_exec(const hq_plan* p, int64_t m) {
   const bool tiled_auto = m > 32;
   if (tiled_ok && (u.kernel == KER_TILED || (u.kernel == 0 && tiled_auto))) {
     e.kernel = KER_TILED;
+    // tile shapes from a sweep on MI355X (N = 4096..8192): 16-bit activations
+    // 128 x 256 at m >= 512; MXFP4 128 x 128 with a 4-group pipeline; int8
+    // and fp8 x INT4 64 x 128 with a 2-group pipeline
+    const bool act16 = p->fmt == FMT_W16F16 || p->fmt == FMT_W16BF16;
     e.tl.bm = m >= 512 ? 128 : 64;
-    e.tl.nbw = (N % 256 == 0 && m >= 512 && p->fmt != FMT_W16BF16) ? 4 : 2;
+    e.tl.nbw = (N % 256 == 0 && m >= 512 && p->fmt == FMT_W16F16) ? 4 : 2;
+    int stages = 3;
+    if (!act16 && m >= 512) {
+      if (p->fmt == FMT_F4) {
+        stages = 4;
+      } else {
+        e.tl.bm = 64;
+        stages = 2;
+      }
+    }
     if (u.tile_m) e.tl.bm = u.tile_m;
     if (u.tile_n) e.tl.nbw = u.tile_n / 64;
     e.tiles_m = cdiv(mm, e.tl.bm);
@@ -146,7 +159,7 @@ Exec choose_exec(const hq_plan* p, int64_t m) {
     split = std::max<int64_t>(1, std::min<int64_t>(split, G));
     split = cdiv(G, cdiv(G, split));  // no empty split
     e.tl.split = (int)split;
-    e.tl.stages = u.stages ? u.stages : 3;
+    e.tl.stages = u.stages ? u.stages : ((u.tile_m || u.tile_n) ? 3 : stages);
     e.ws_bytes = split > 1 ? align256((size_t)split * (size_t)mm * (size_t)N * 4) : 0;
     return e;
   }
@@ -219,7 +232,7 @@ hq_status check_exec(const hq_plan* p, const hq::Exec& e) {
       const bool act16 = p->fmt == hq::FMT_W16F16 || p->fmt == hq::FMT_W16BF16;
       const int rowb = act16 ? 256 : 128;
       const int lps = e.tl.bm * rowb / 1024 / 4 + e.tl.nbw * (p->fmt == hq::FMT_F4 ? 2 : 3);
-      if (e.tl.stages < 3 || e.tl.stages > 5) return fail(HQ_ERR_INVALID_ARG, "tiled kernel: stages must be 3..5");
+      if (e.tl.stages < 2 || e.tl.stages > 5) return fail(HQ_ERR_INVALID_ARG, "tiled kernel: stages must be 2..5");
       if (e.tl.stages * e.tl.bm * rowb > 160 * 1024 || lps * (e.tl.stages - 2) >= 64)
         return fail(HQ_ERR_INVALID_ARG, "tiled kernel: too many stages for this tile");
     }
@@ -313,11 +326,11 @@ hq_status hq_plan_create(const hq_layer_desc* layer, const hq_compute* compute, 
         return fail(HQ_ERR_UNSUPPORTED, "the combining down GEMM needs n a multiple of 64");
       if (tuning) {
         const int tm = tuning->tile_m, tn = tuning->tile_n;
-        if (tm != 0 && tm != 16 && tm != 64 && tm != 128)
-          return fail(HQ_ERR_UNSUPPORTED, "grouped tile_m must be 16 (skinny), 64 or 128 (tiled)");
-        if (tuning->kernel == hq::KER_SKINNY && tm > 16)
-          return fail(HQ_ERR_UNSUPPORTED, "the skinny grouped kernel uses 16-row blocks");
-        if (tuning->kernel == hq::KER_TILED && tm == 16)
+        if (tm != 0 && tm != 16 && tm != 32 && tm != 64 && tm != 128)
+          return fail(HQ_ERR_UNSUPPORTED, "grouped tile_m must be 16 or 32 (skinny), 64 or 128 (tiled)");
+        if (tuning->kernel == hq::KER_SKINNY && tm > 32)
+          return fail(HQ_ERR_UNSUPPORTED, "the skinny grouped kernel uses 16- or 32-row blocks");
+        if (tuning->kernel == hq::KER_TILED && (tm == 16 || tm == 32))
           return fail(HQ_ERR_UNSUPPORTED, "the tiled grouped kernel uses 64- or 128-row blocks");
         if (tn != 0 && tn != 128 && tn != 256)
           return fail(HQ_ERR_UNSUPPORTED, "grouped tile_n must be 128 or 256");
@@ -590,8 +603,10 @@ static MoeChoice moe_choice(const hq_plan* p, int64_t t, int topk) {
   if (tiled && N % 128) tiled = false;  // the tiled grid needs whole 128-column tiles
   c.tiled = tiled;
   if (!tiled) {
-    c.bm = 16;
-    c.sk.mb = 1;
+    // 16-row blocks (32 by tuning: fewer weight re-reads at ~16 slots per
+    // expert, but measured slower on MI355X at T = 512)
+    c.bm = (u.tile_m == 16 || u.tile_m == 32) ? u.tile_m : 16;
+    c.sk.mb = c.bm / 16;
     c.sk.nb = (p->compute.epi == HQ_EPI_TOPK_COMBINE || p->compute.epi == HQ_EPI_NONE) ? 4 : 2;
     if (p->compute.epi == HQ_EPI_NONE && N % 64) c.sk.nb = 1;
     const int64_t G = p->layer.k / 128;

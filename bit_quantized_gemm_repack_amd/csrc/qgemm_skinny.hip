@@ -418,9 +418,11 @@ static hipError_t launch_mb(const SkinnyCfg& cfg, const SkinnyArgs& a, dim3 grid
 template <int FMT, int GRP>
 static hipError_t launch_grouped_t(const SkinnyCfg& cfg, const SkinnyArgs& a, dim3 grid, dim3 block, size_t lds,
                                    hipStream_t s) {
-  if (cfg.mb != 1 || cfg.stages != 2 || cfg.waves > 8) return hipErrorInvalidValue;
-  if (cfg.nb == 2) return launch_kernel(qgemm_skinny<FMT, 1, 2, 2, 512, GRP>, grid, block, lds, s, a);
-  if (cfg.nb == 4) return launch_kernel(qgemm_skinny<FMT, 1, 4, 2, 512, GRP>, grid, block, lds, s, a);
+  if (cfg.stages != 2 || cfg.waves > 8) return hipErrorInvalidValue;
+  if (cfg.mb == 1 && cfg.nb == 2) return launch_kernel(qgemm_skinny<FMT, 1, 2, 2, 512, GRP>, grid, block, lds, s, a);
+  if (cfg.mb == 1 && cfg.nb == 4) return launch_kernel(qgemm_skinny<FMT, 1, 4, 2, 512, GRP>, grid, block, lds, s, a);
+  if (cfg.mb == 2 && cfg.nb == 2) return launch_kernel(qgemm_skinny<FMT, 2, 2, 2, 512, GRP>, grid, block, lds, s, a);
+  if (cfg.mb == 2 && cfg.nb == 4) return launch_kernel(qgemm_skinny<FMT, 2, 4, 2, 512, GRP>, grid, block, lds, s, a);
   return hipErrorInvalidValue;
 }
 

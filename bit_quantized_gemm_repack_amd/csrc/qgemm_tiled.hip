@@ -66,7 +66,7 @@ struct TCfg {
   static constexpr int META = (FMT == FMT_F4) ? 1 : 2;  // metadata loads per fragment
   static constexpr int LPS = SEGW + NBW + META * NBW;   // vector-memory loads per step per wave
   static_assert(SEGW * WAVES == NSEG, "tile rows must fill the loaders");
-  static_assert(LPS * (ST - 2) < 64, "loads in flight exceed the counter");
+  static_assert(ST >= 2 && LPS * (ST - 2) < 64, "loads in flight exceed the counter");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds the workgroup limit");
 };
 
@@ -512,6 +512,7 @@ static hipError_t launch_tiled_t(const TiledArgs& a, dim3 grid, hipStream_t s) {
 template <int FMT, int BM, int NBW, int GRP>
 static hipError_t launch_tiled_s(const TiledCfgRt& cfg, const TiledArgs& a, dim3 grid, hipStream_t s) {
   if constexpr (GRP == GRP_DENSE) {
+    if (cfg.stages == 2) return launch_tiled_t<FMT, BM, NBW, GRP, 2>(a, grid, s);
     if (cfg.stages == 4) return launch_tiled_t<FMT, BM, NBW, GRP, 4>(a, grid, s);
     if constexpr (TCfg<FMT, BM, NBW, 5>::LDS_BYTES <= 160 * 1024 && TCfg<FMT, BM, NBW, 5>::LPS * 3 < 64)
       if (cfg.stages == 5) return launch_tiled_t<FMT, BM, NBW, GRP, 5>(a, grid, s);

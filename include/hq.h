@@ -150,8 +150,9 @@ typedef struct hq_tuning {
   int tile_m;  /* skinny: rows per workgroup (16, 32, 64); tiled: 64 or 128     */
   int tile_n;  /* skinny: columns per workgroup (16, 32, 64); tiled: 128, 256 */
   int waves;   /* wavefronts per workgroup                                 */
-  int split_k; /* skinny: workgroups sharing one output tile along K      */
-  int stages;  /* groups of 128 k kept in flight per wave                  */
+  int split_k; /* workgroups sharing one output tile along K (dense)     */
+  int stages;  /* skinny: 128-k groups in flight per wave (2, 4, 8);
+                  tiled: groups in the LDS / register ring (2..5)          */
   int mfma;    /* 16 (16x16 MFMA); reserved for 32                         */
 } hq_tuning;
 

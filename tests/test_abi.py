@@ -287,13 +287,15 @@ def test_moe_block_choice():
     q = hq.w4a16("bf16", scale="f16")
     p = hq.MoePlan(512, 7168, q, 256, 1 << 16, "silu_mul")
     assert p.block_m(1, 8) == 16         # 0.03 slots per expert: weight streaming
+    assert p.block_m(32, 8) == 16        # 1 per expert
     assert p.block_m(512, 8) == 16       # 16 per expert
     assert p.block_m(4096, 8) == 64      # 128 per expert: MFMA tiles
     assert p.block_m(16384, 8) == 128    # 512 per expert
     assert hq.MoePlan(512, 7168, q, 256, 64, "silu_mul", tuning=dict(tile_m=128)).block_m(1, 8) == 128
     assert hq.MoePlan(512, 7168, q, 256, 64, "silu_mul", tuning=dict(kernel=2)).block_m(1, 8) == 64
     assert hq.MoePlan(512, 7168, q, 256, 8192, "silu_mul", tuning=dict(kernel=1)).block_m(4096, 8) == 16
-    for bad in (dict(tile_m=32), dict(kernel=1, tile_m=64), dict(kernel=2, tile_m=16), dict(tile_n=64),
+    assert hq.MoePlan(512, 7168, q, 256, 8192, "silu_mul", tuning=dict(tile_m=32)).block_m(4096, 8) == 32
+    for bad in (dict(tile_m=48), dict(kernel=1, tile_m=64), dict(kernel=2, tile_m=32), dict(tile_n=64),
                 dict(tile_n=256, tile_m=64)):
         n = 384 if bad.get("tile_n") == 256 else 512
         with pytest.raises(hq.HQError) as e:

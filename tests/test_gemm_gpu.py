@@ -256,13 +256,13 @@ def test_tiled_w4a16_shapes(tuning, act, zp):
         run_w4a16(M, N, K, act=act, zp=zp, tuning=tuning)
 
 
-@pytest.mark.parametrize("stages", [4, 5])
+@pytest.mark.parametrize("stages", [2, 4, 5])
 @pytest.mark.parametrize("tuning", [dict(kernel=2, tile_m=64, tile_n=128), dict(kernel=2, tile_m=128, tile_n=256),
                                     dict(kernel=2, tile_m=64, tile_n=256, split_k=3)])
 @pytest.mark.parametrize("act,zp", [("f16", "fixed"), ("bf16", "u4")])
 def test_tiled_deeper_pipeline(stages, tuning, act, zp):
-    # 4- and 5-group load pipelines (G = 1, 3, 8, 11 groups: shorter than,
-    # equal to and longer than the pipeline)
+    # 2-, 4- and 5-group load pipelines (G = 1, 3, 8, 11 groups: shorter
+    # than, equal to and longer than the pipeline)
     for (M, N, K) in [(70, 512, 128), (130, 256, 384), (64, 512, 1024), (200, 256, 1408)]:
         run_w4a16(M, N, K, act=act, zp=zp, tuning=dict(tuning, stages=stages))
 

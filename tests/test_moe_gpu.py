@@ -170,6 +170,18 @@ def test_small_layer_all_tokens(small_layer, T, topk, act):
     run_layer(small_layer, T, act, topk, key=(11,))
 
 
+@pytest.fixture(scope="module")
+def small_layer_32():
+    return Layer(8, 512, 128, key=(7,), tuning=dict(kernel=1, tile_m=32))
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp8"])
+@pytest.mark.parametrize("T,topk", [(1, 2), (37, 2), (150, 3)])
+def test_small_layer_32_row_blocks(small_layer_32, T, topk, act):
+    # the weight-streaming kernel with two 16-row blocks per workgroup
+    run_layer(small_layer_32, T, act, topk, key=(23,))
+
+
 # the MFMA-tiled grouped kernel on every token: 64- and 128-row blocks, 128-
 # and 256-column tiles (gate_up n = 256: one or two paired tiles; down K = 128:
 # a single k group), mostly-empty blocks at small T
