@@ -599,7 +599,7 @@ static MoeChoice moe_choice(const hq_plan* p, int64_t t, int topk) {
   if (u.kernel == hq::KER_TILED) tiled = true;
   else if (u.kernel == hq::KER_SKINNY) tiled = false;
   else if (u.tile_m) tiled = u.tile_m >= 64;
-  else tiled = per_expert >= 48.0;
+  else tiled = per_expert >= 12.0;  // measured crossover on MI355X (H = 7168, I = 256)
   if (tiled && N % 128) tiled = false;  // the tiled grid needs whole 128-column tiles
   c.tiled = tiled;
   if (!tiled) {
@@ -618,7 +618,7 @@ static MoeChoice moe_choice(const hq_plan* p, int64_t t, int topk) {
   c.bm = u.tile_m >= 64 ? u.tile_m : (per_expert >= 192.0 ? 128 : 64);
   int nbw;
   if (u.tile_n) nbw = u.tile_n / 64;
-  else nbw = (N % 256 == 0 && N >= 2048 && p->fmt != hq::FMT_W16BF16) ? 4 : 2;
+  else nbw = (N % 256 == 0) ? 4 : 2;
   if (N % (64 * nbw)) nbw = 2;
   c.tl.bm = c.bm;
   c.tl.nbw = nbw;
@@ -745,7 +745,39 @@ hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, cons
     int err;
     const bool second = epi == HQ_EPI_SILU_MUL_QFP8 || epi == HQ_EPI_TOPK_COMBINE;
     hq::arm_timing({ev.start, second ? nullptr : ev.stop});
-    if (mc.tiled) {
+    // the down projection with a short K: activations resident in registers,
+    // weights streamed over all columns (16- and 64-row blocks)
+    const bool smallk = epi == HQ_EPI_TOPK_COMBINE && p->user.kernel == 0 &&
+                        hq::smallk_supported(p->fmt, bm / 16, (int)G) && (bm == 16 || bm == 64);
+    if (smallk) {
+      hq::SkinnyArgs s{};
+      s.a = a;
+      s.a_scale = a_scale;
+      s.w = w;
+      s.scales = meta;
+      s.zeros = zeros;
+      s.out = out;
+      s.M = (int)mp;
+      s.N = (int)N;
+      s.K = (int)K;
+      s.G = (int)G;
+      s.gps = (int)G;
+      s.zp_fixed = p->layer.q.zp == HQ_ZP_FIXED ? p->layer.q.zp_value : -1;
+      s.scale_bf16 = p->layer.q.scale == HQ_BF16;
+      s.out_bf16 = p->layer.q.out == HQ_BF16;
+      s.sorted_ids = sorted_ids;
+      s.block_expert = block_expert;
+      s.num_padded = num_padded;
+      s.topk_w = topk_w;
+      s.topk = topk;
+      s.n_slots = n_slots;
+      s.epi = gepi;
+      s.w_expert = (int64_t)p->w_bytes_per_expert;
+      s.s_expert = (int64_t)(N * G);
+      s.z_expert = (int64_t)((N / 16) * G * 2);
+      s.f32_out = f32_out;
+      err = hq::launch_smallk_grouped(p->fmt, bm / 16, s, blocks, stream);
+    } else if (mc.tiled) {
       hq::TiledArgs s{};
       s.a = a;
       s.a_scale = a_scale;

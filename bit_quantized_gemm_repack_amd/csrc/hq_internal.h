@@ -228,6 +228,11 @@ enum GroupedEpi : int { GEPI_PLAIN = 0, GEPI_SILU = 1, GEPI_SILU_F32 = 2, GEPI_C
 enum GroupedMode : int { GRP_DENSE = 0, GRP_GATHER = 1, GRP_SORTED = 2 };
 
 int launch_skinny(int fmt, const SkinnyCfg& cfg, const SkinnyArgs& a, void* stream);
+// Grouped down GEMM for short K (K = 128 G): blocks of 16 mb aligned rows,
+// combine rows out.  Supported: fp16 / bf16 / fp8 activations, mb 1 with
+// G <= 4 (1, 2, 4), mb 4 with G <= 2.
+bool smallk_supported(int fmt, int mb, int G);
+int launch_smallk_grouped(int fmt, int mb, const SkinnyArgs& a, int64_t blocks, void* stream);
 // Grouped launch: grid.z = blocks of the aligned array (max_padded / (16 mb)).
 int launch_skinny_grouped(int fmt, int mode, const SkinnyCfg& cfg, const SkinnyArgs& a, int64_t blocks,
                           void* stream);

@@ -288,7 +288,8 @@ def test_moe_block_choice():
     p = hq.MoePlan(512, 7168, q, 256, 1 << 16, "silu_mul")
     assert p.block_m(1, 8) == 16         # 0.03 slots per expert: weight streaming
     assert p.block_m(32, 8) == 16        # 1 per expert
-    assert p.block_m(512, 8) == 16       # 16 per expert
+    assert p.block_m(256, 8) == 16       # 8 per expert
+    assert p.block_m(512, 8) == 64       # 16 per expert: MFMA tiles
     assert p.block_m(4096, 8) == 64      # 128 per expert: MFMA tiles
     assert p.block_m(16384, 8) == 128    # 512 per expert
     assert hq.MoePlan(512, 7168, q, 256, 64, "silu_mul", tuning=dict(tile_m=128)).block_m(1, 8) == 128
