@@ -37,6 +37,16 @@ __device__ inline i8_t cat8(u4_t x, u4_t y) {
   return r;
 }
 
+// A value the compiler cannot see through (kept in a VGPR).  Passing the
+// magic exponent of w16_operand this way lets each register be one
+// v_and_or_b32 (mask from an SGPR, magic from a VGPR): with both constants
+// literal the compiler emits a separate AND and OR, as one VOP3 instruction
+// cannot hold two literals.
+__device__ inline uint32_t opaque_vgpr(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // One word of NIB_W16 codes -> the 16-bit operand (8 values, k-offsets 0..7)
 // holding MAGIC + q exactly: fp16 0x6400 = 1024, bf16 0x4300 = 128.
 __device__ inline u4_t w16_operand(uint32_t x, uint32_t magic) {

@@ -96,6 +96,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 template <int FMT, int BM, int NBW, int GRP, int ST>
 __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the body uses device-only builtins; the host pass needs only the stub
   using C = TCfg<FMT, BM, NBW, ST>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x;
@@ -167,13 +168,29 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
     return tn * (C::BN / 16) + wave * NBW + j;
   };
 
-  // ---- activation sources of this wave's global->LDS loads ------------------
-  // Segment seg (1 KiB of the slot) holds rows seg*RPS .. seg*RPS+RPS-1; lane l
-  // writes physical chunk l % CHUNKS of row seg*RPS + l / CHUNKS, so it loads
-  // the logical chunk the swizzle places there (the XOR is its own inverse).
-  const uint8_t* a_bytes = static_cast<const uint8_t*>(p.a);
-  const int64_t a_pitch = (int64_t)K * (C::ACT16 ? 2 : 1);
-  const uint8_t* dsrc[C::SEGW];
+  // ---- buffer resources and this lane's byte offsets -------------------------
+  // Every load goes through a buffer resource (base + byte range): the lane's
+  // offset is fixed for the whole loop and the per-group advance is a scalar
+  // offset, so a step spends no vector instructions on addresses.  Loads
+  // outside a range return zero (the host keeps every range below 2 GiB).
+  auto rsrc = [](const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+  };
+  const int a_rowb = K * (C::ACT16 ? 2 : 1);
+  const int a_rows = (GRP == GRP_GATHER) ? p.n_slots / p.topk : p.M;
+  const auto ra = rsrc(p.a, (int64_t)a_rows * a_rowb);
+  const int64_t nfrag = (int64_t)(p.N / 16) * G;  // fragments of this weight (one expert)
+  const auto rw = rsrc(wbytes, nfrag * 1024);
+  [[maybe_unused]] const auto rs = rsrc(scales16, nfrag * 32);
+  [[maybe_unused]] const auto rz = rsrc(zeros32 ? static_cast<const void*>(zeros32) : static_cast<const void*>(scales16),
+                                        zeros32 ? nfrag * 8 : nfrag * 32);
+  [[maybe_unused]] const auto re = rsrc(e8, nfrag * 64);
+
+  // Activation segment s (1 KiB of the slot) holds rows seg*RPS .. +RPS-1;
+  // lane l writes physical chunk l % CHUNKS of row seg*RPS + l / CHUNKS, so it
+  // loads the logical chunk the swizzle places there (the XOR is its own
+  // inverse).
+  int aoff[C::SEGW];
 #pragma unroll
   for (int s = 0; s < C::SEGW; ++s) {
     const int seg = wave + C::WAVES * s;
@@ -188,40 +205,44 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
     } else {
       row = m0 + r;
     }
-    dsrc[s] = a_bytes + row * a_pitch + lchunk * 16;
+    aoff[s] = row * a_rowb + lchunk * 16;
+  }
+  int woff[NBW], soff[NBW], zoff[NBW];
+#pragma unroll
+  for (int j = 0; j < NBW; ++j) {
+    const int f0 = nblk(j) * G;  // first fragment of this column block
+    woff[j] = (f0 * 64 + lane) * 16;
+    soff[j] = (FMT == FMT_F4) ? f0 * 64 + (lane & ~3) : f0 * 32 + (c16 >> 1) * 4;
+    zoff[j] = f0 * 8 + (c16 >> 3) * 4;
   }
 
-  // ---- weight fragments + metadata of this wave, 3-slot ring ----------------
-  const u4_t* wfr = reinterpret_cast<const u4_t*>(wbytes);
-  const uint32_t* zsrc = zeros32 ? zeros32 : reinterpret_cast<const uint32_t*>(scales16);
+  // ---- weight fragments + metadata of this wave, register ring ---------------
   u4_t braw[C::STAGES][NBW];
   uint32_t sraw[C::STAGES][NBW];
   [[maybe_unused]] uint32_t zraw[C::STAGES][NBW];
 
   auto issue = [&](auto slot_c, int g) {
     constexpr int slot = decltype(slot_c)::value;
+    const int gg = gb + g;  // uniform
 #pragma unroll
     for (int s = 0; s < C::SEGW; ++s) {
       const int seg = wave + C::WAVES * s;
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(dsrc[s] + (int64_t)(gb + g) * C::ROWB),
-                                       (lds_ptr_t)(lds + slot * C::STAGE_BYTES + seg * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(lds + slot * C::STAGE_BYTES + seg * 1024), 16, aoff[s],
+                                               gg * C::ROWB, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < NBW; ++j) {
-      const int64_t rec = (int64_t)nblk(j) * G + gb + g;
-      braw[slot][j] = __builtin_nontemporal_load(wfr + rec * 64 + lane);
-    }
+    for (int j = 0; j < NBW; ++j)
+      braw[slot][j] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[j], gg * 1024, 2));
     // Metadata comes in as whole 32-bit words and the lane's byte / half-word
     // is taken out in the math: a narrow load would be zero-extended where the
     // ring is carried round the loop, which forces a wait for every load there.
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
-      const int64_t rec = (int64_t)nblk(j) * G + gb + g;
       if constexpr (FMT == FMT_F4) {
-        sraw[slot][j] = reinterpret_cast<const uint32_t*>(e8)[(rec * 64 + lane) >> 2];
+        sraw[slot][j] = __builtin_amdgcn_raw_buffer_load_b32(re, soff[j], gg * 64, 0);
       } else {
-        sraw[slot][j] = reinterpret_cast<const uint32_t*>(scales16)[(rec * 16 + c16) >> 1];
-        zraw[slot][j] = zsrc[rec * 2 + (c16 >> 3)];
+        sraw[slot][j] = __builtin_amdgcn_raw_buffer_load_b32(rs, soff[j], gg * 32, 0);
+        zraw[slot][j] = __builtin_amdgcn_raw_buffer_load_b32(rz, zoff[j], gg * 8, 0);
       }
     }
   };
@@ -236,6 +257,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
   for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
     for (int j = 0; j < NBW; ++j) acc[mb][j] = f4_t{0.f, 0.f, 0.f, 0.f};
+  [[maybe_unused]] const uint32_t magic_v = opaque_vgpr(FMT == FMT_W16F16 ? 0x64006400u : 0x43004300u);
 
   // Operand fetch of m-block mb from `slot`: row r = 16 mb + c16.
   // 16-bit: step t takes k = 32 t + 8 kq + [0,8) (chunk 4 t + kq);
@@ -268,7 +290,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
         c2[j] = h2_t{cz, cz};
       }
       auto deq = [&](int j, int t) -> u4_t {
-        const u4_t x = w16_operand(braw[slot][j][t], 0x64006400u);
+        const u4_t x = w16_operand(braw[slot][j][t], magic_v);
         uint32_t y[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -322,7 +344,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
         sj[j] = p.scale_bf16 ? bf16_bits_to_float(scale_bits(sraw[slot][j])) : f16_bits_to_float(scale_bits(sraw[slot][j]));
         cj[j] = 128.f + (float)zero_of(zraw[slot][j]);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) bop[j][t] = w16_operand(braw[slot][j][t], 0x43004300u);
+        for (int t = 0; t < 4; ++t) bop[j][t] = w16_operand(braw[slot][j][t], magic_v);
       }
       const u4_t ones = u4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 #pragma unroll
@@ -489,6 +511,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
       }
     }
   }
+#endif
 }
 
 // ---------------------------------------------------------------------------

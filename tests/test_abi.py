@@ -36,6 +36,16 @@ def test_library_exports_every_header_function():
         assert hasattr(L, name), f"{name} declared in include/hq.h but not exported"
 
 
+def test_library_has_no_undefined_internal_symbols():
+    # every kernel launched from host code must have its host stub in the
+    # library (a kernel body the host pass cannot instantiate drops the stub
+    # without a diagnostic, and the library then fails to load on a GPU host)
+    import subprocess
+    r = subprocess.run(["nm", "-D", "--undefined-only", hq.lib()._name], capture_output=True, text=True, check=True)
+    bad = [l.split()[-1] for l in r.stdout.splitlines() if "_ZN2hq" in l]
+    assert not bad, f"undefined library symbols: {bad[:5]}"
+
+
 def test_abi_version_and_status_strings():
     L = hq.lib()
     assert L.hq_abi_version() == 1
