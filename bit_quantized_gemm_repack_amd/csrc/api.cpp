@@ -501,11 +501,13 @@ hq_status hq_gemm(const hq_plan* p, int64_t m, const void* a, const float* a_sca
                                 ? reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(meta) +
                                                                     p->scale_region_bytes)
                                 : nullptr;
-    if (e.kernel == hq::KER_TILED) {
-      // the tiled kernel addresses A and W through 32-bit buffer ranges
+    {
+      // the kernels address A and W through 32-bit buffer ranges
       const int64_t act_bytes = (p->fmt == hq::FMT_W16F16 || p->fmt == hq::FMT_W16BF16) ? 2 : 1;
       if (m * K * act_bytes >= (int64_t(1) << 31) || N * K / 2 >= (int64_t(1) << 31))
-        return fail(HQ_ERR_UNSUPPORTED, "tiled kernel: activations and weights must each stay below 2 GiB");
+        return fail(HQ_ERR_UNSUPPORTED, "activations and weights must each stay below 2 GiB");
+    }
+    if (e.kernel == hq::KER_TILED) {
       hq::TiledArgs t{};
       t.a = a;
       t.a_scale = a_scale;
@@ -718,6 +720,12 @@ hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, cons
     const MoeChoice mc = moe_choice(p, t, topk);
     const int bm = mc.bm;
     const int64_t mp = moe_max_padded(t, topk, p->layer.num_experts, bm);
+    {
+      // the kernels address A and one expert's W through 32-bit buffer ranges
+      const int64_t act_bytes = (p->fmt == hq::FMT_W16F16 || p->fmt == hq::FMT_W16BF16) ? 2 : 1;
+      if (std::max<int64_t>(mp, t) * K * act_bytes >= (int64_t(1) << 31) || N * K / 2 >= (int64_t(1) << 31))
+        return fail(HQ_ERR_UNSUPPORTED, "activations and one expert's weights must each stay below 2 GiB");
+    }
     const uint32_t* zeros = p->layer.q.zp == HQ_ZP_PER_GROUP_U4
                                 ? reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(meta) +
                                                                     p->scale_region_bytes *
@@ -782,9 +790,6 @@ hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, cons
       s.f32_out = f32_out;
       err = hq::launch_smallk_grouped(p->fmt, bm / 16, s, blocks, stream);
     } else if (mc.tiled) {
-      const int64_t act_bytes = (p->fmt == hq::FMT_W16F16 || p->fmt == hq::FMT_W16BF16) ? 2 : 1;
-      if (std::max<int64_t>(mp, t) * K * act_bytes >= (int64_t(1) << 31) || N * K / 2 >= (int64_t(1) << 31))
-        return fail(HQ_ERR_UNSUPPORTED, "tiled kernel: activations and weights must each stay below 2 GiB");
       hq::TiledArgs s{};
       s.a = a;
       s.a_scale = a_scale;

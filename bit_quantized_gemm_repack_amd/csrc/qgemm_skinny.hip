@@ -68,9 +68,10 @@ __device__ inline f4_t mfma16(u4_t a, u4_t b, f4_t c) {
 // rows are the aligned slots themselves).
 template <int FMT, int MB, int NB, int STAGES, int MAXT, int GRP>
 __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the body uses device-only builtins; the host pass needs only the stub
   using FI = FmtInfo<FMT>;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar group offsets
   const int W = blockDim.x >> 6;
   const int c = lane & 15;
   const int kq = lane >> 4;
@@ -124,59 +125,84 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   const int my_first = g_beg + wave;
   const int n_it = (my_first < g_end) ? (g_end - my_first + W - 1) / W : 0;
 
-  // Row each lane loads for each m-block: dense rows clamped into [0, M);
-  // gathered slots read their token (padding slots read token 0, their
-  // results are dropped); aligned rows read themselves.
-  int arow[MB];
+  // ---- buffer resources and this lane's byte offsets -------------------------
+  // Every load goes through a buffer resource: the lane's offset is fixed and
+  // the group advance is a scalar offset.  A lane whose row holds no output
+  // (past M, or a padding slot) gets an offset outside the activation range:
+  // the load returns zero without touching memory, so the activation loads of
+  // a 1..15-row block fetch only the rows that exist.
+  auto rsrc = [](const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+  };
+  const int a_rowb = K * (FI::kAct16 ? 2 : 1);
+  const int a_rows = (GRP == GRP_GATHER) ? p.n_slots / p.topk : p.M;
+  const auto ra = rsrc(p.a, (int64_t)a_rows * a_rowb);
+  const int64_t nfrag = (int64_t)(p.N / 16) * G;
+  const auto rw = rsrc(wbytes, nfrag * 1024);
+  [[maybe_unused]] const auto rsc = rsrc(scales16, nfrag * 32);
+  [[maybe_unused]] const auto rz = rsrc(zeros32 ? static_cast<const void*>(zeros32) : static_cast<const void*>(scales16),
+                                        zeros32 ? nfrag * 8 : nfrag * 32);
+  [[maybe_unused]] const auto re = rsrc(e8, nfrag * 64);
+  // at or above 2^31: past every range (ranges stay below 2 GiB), and adding
+  // the group offset cannot wrap
+  constexpr int kOutOfRange = INT32_MIN;
+  int aoff[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
+    const int m = m0 + 16 * mb + c;
+    int row = -1;
     if constexpr (GRP == GRP_DENSE) {
-      arow[mb] = min(m0 + 16 * mb + c, p.M - 1);
-    } else if constexpr (GRP == GRP_GATHER) {
-      const int id = p.sorted_ids[m0 + 16 * mb + c];
-      arow[mb] = id < p.n_slots ? id / p.topk : 0;
+      row = m < p.M ? m : -1;
     } else {
-      arow[mb] = m0 + 16 * mb + c;
+      const int id = p.sorted_ids[m];
+      if (id < p.n_slots) row = (GRP == GRP_GATHER) ? id / p.topk : m;
     }
+    // 16-bit step t: bytes 256 g + 64 t + 16 kq; 8-bit piece h: 128 g + 64 h + 16 kq
+    aoff[mb] = row >= 0 ? row * a_rowb + 16 * kq : kOutOfRange;
   }
-
-  const u4_t* wfr = reinterpret_cast<const u4_t*>(wbytes);
-  // zero points, or (fixed zero) any readable word array of at least the same size
-  const uint32_t* zsrc = zeros32 ? zeros32 : reinterpret_cast<const uint32_t*>(scales16);
+  int woff[NB], soff[NB], zoff[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int f0 = nblk(nb) * G;
+    woff[nb] = (f0 * 64 + lane) * 16;
+    soff[nb] = (FMT == FMT_F4) ? f0 * 64 + (lane & ~3) : f0 * 32 + (c >> 1) * 4;
+    zoff[nb] = f0 * 8 + (c >> 3) * 4;
+  }
 
   auto load = [&](Stage<FMT, MB, NB>& st, int g) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int64_t frag = (int64_t)nblk(nb) * G + g;
-      st.b[nb] = __builtin_nontemporal_load(wfr + frag * 64 + lane);
-    }
+    for (int nb = 0; nb < NB; ++nb)
+      st.b[nb] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[nb], g * 1024, 2));
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       // Step t of the 16-bit operand: k = 32 t + 8 kq + [0,8); piece h of the
       // 8-bit operand: k = 64 h + 16 kq + [0,16).  Per load instruction the
       // four lanes of one row read 64 contiguous bytes.
       if constexpr (FI::kAct16) {
-        const uint16_t* arow16 = static_cast<const uint16_t*>(p.a) + (int64_t)arow[mb] * K + g * 128 + 8 * kq;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) st.a[mb][t] = *reinterpret_cast<const u4_t*>(arow16 + 32 * t);
+        for (int t = 0; t < 4; ++t)
+          st.a[mb][t] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[mb] + 64 * t, g * 256, 0));
       } else {
-        const uint8_t* arow8 = static_cast<const uint8_t*>(p.a) + (int64_t)arow[mb] * K + g * 128 + 16 * kq;
-        st.a[mb][0] = *reinterpret_cast<const u4_t*>(arow8);
-        st.a[mb][1] = *reinterpret_cast<const u4_t*>(arow8 + 64);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          st.a[mb][h] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[mb] + 64 * h, g * 128, 0));
       }
     }
-    // Metadata loads are unconditional and decoded only at compute time, so
+    // Metadata comes in as whole dwords, decoded only at compute time, so
     // that no wait is needed until the stage's math.
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int64_t rec = (int64_t)nblk(nb) * G + g;
       if constexpr (FMT == FMT_F4) {
-        st.sraw[nb] = e8[rec * 64 + lane];
+        st.sraw[nb] = __builtin_amdgcn_raw_buffer_load_b32(re, soff[nb], g * 64, 0);
       } else {
-        st.sraw[nb] = scales16[rec * 16 + c];
-        st.zraw[nb] = zsrc[rec * 2 + (c >> 3)];
+        st.sraw[nb] = __builtin_amdgcn_raw_buffer_load_b32(rsc, soff[nb], g * 32, 0);
+        st.zraw[nb] = __builtin_amdgcn_raw_buffer_load_b32(rz, zoff[nb], g * 8, 0);
       }
     }
+  };
+  // the lane's 16-bit scale / E8M0 byte out of its metadata dword
+  auto sbits = [&](const Stage<FMT, MB, NB>& st, int nb) -> uint32_t {
+    return (FMT == FMT_F4) ? (st.sraw[nb] >> (8 * (lane & 3))) & 0xFFu : (st.sraw[nb] >> (16 * (c & 1))) & 0xFFFFu;
   };
   auto zero_of = [&](const Stage<FMT, MB, NB>& st, int nb) -> uint32_t {
     return p.zp_fixed < 0 ? (st.zraw[nb] >> (4 * (c & 7))) & 0xFu : (uint32_t)p.zp_fixed;
@@ -225,7 +251,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) P[mb] = mfma16<FMT>(st.a[mb][t], bop, P[mb]);
         }
-        const float s = p.scale_bf16 ? bf16_bits_to_float(st.sraw[nb]) : f16_bits_to_float(st.sraw[nb]);
+        const float s = p.scale_bf16 ? bf16_bits_to_float(sbits(st, nb)) : f16_bits_to_float(sbits(st, nb));
         const float cz = off + (float)zero_of(st, nb);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -236,7 +262,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
                              (int)((w[1] << 4) & 0xF0F0F0F0u), (int)(w[1] & 0xF0F0F0F0u)};
         const i4_t b1 = i4_t{(int)((w[2] << 4) & 0xF0F0F0F0u), (int)(w[2] & 0xF0F0F0F0u),
                              (int)((w[3] << 4) & 0xF0F0F0F0u), (int)(w[3] & 0xF0F0F0F0u)};
-        const float s16 = 0.0625f * (p.scale_bf16 ? bf16_bits_to_float(st.sraw[nb]) : f16_bits_to_float(st.sraw[nb]));
+        const float s16 = 0.0625f * (p.scale_bf16 ? bf16_bits_to_float(sbits(st, nb)) : f16_bits_to_float(sbits(st, nb)));
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           i4_t P = i4_t{0, 0, 0, 0};
@@ -258,7 +284,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
                               (int)(w[1] & 0x0F0F0F0Fu), (int)((w[1] >> 4) & 0x0F0F0F0Fu),
                               (int)(w[2] & 0x0F0F0F0Fu), (int)((w[2] >> 4) & 0x0F0F0F0Fu),
                               (int)(w[3] & 0x0F0F0F0Fu), (int)((w[3] >> 4) & 0x0F0F0F0Fu)};
-        const float s = p.scale_bf16 ? bf16_bits_to_float(st.sraw[nb]) : f16_bits_to_float(st.sraw[nb]);
+        const float s = p.scale_bf16 ? bf16_bits_to_float(sbits(st, nb)) : f16_bits_to_float(sbits(st, nb));
         const float z = (float)zero_of(st, nb);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -270,7 +296,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
         }
       } else {  // FMT_F4
         const i8_t bop = i8_t{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
-        const int sb = (int)st.sraw[nb];
+        const int sb = (int)sbits(st, nb);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
           acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -286,9 +312,15 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   // so that the wait before each stage's math counts only that stage's loads.
   const int g_dummy = min(g_beg, G - 1);
   auto group_of = [&](int it) { return it < n_it ? my_first + it * W : g_dummy; };
+  // The prologue issues the stages in order (no scheduling across the
+  // barriers): the wait before stage d's math then counts the loads of the
+  // later stages, on the first pass as in the loop.
   Stage<FMT, MB, NB> st[STAGES];
 #pragma unroll
-  for (int d = 0; d < STAGES; ++d) load(st[d], group_of(d));
+  for (int d = 0; d < STAGES; ++d) {
+    load(st[d], group_of(d));
+    __builtin_amdgcn_sched_barrier(0);
+  }
   for (int i = 0; i < n_it; i += STAGES) {
 #pragma unroll
     for (int d = 0; d < STAGES; ++d) {
@@ -360,6 +392,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
       p.part[((int64_t)split * p.M + m) * p.N + n] = v;
     }
   }
+#endif
 }
 
 // ---------------------------------------------------------------------------

@@ -210,7 +210,9 @@ hq_status hq_repack_host(const hq_plan* plan, const void* codes, const void* sca
  *            P[m,n,g] = sum_{k in group g} a_q[m,k] * (q[n,k] - 8), exactly
  *   ws       device workspace of hq_plan_workspace_bytes(plan, m) bytes
  *            (may be NULL when that is 0)
- * m = 0 is a no-op; m > max_m is HQ_ERR_INVALID_ARG. */
+ * m = 0 is a no-op; m > max_m is HQ_ERR_INVALID_ARG.  The kernels address
+ * `a` and `w` through 32-bit buffer ranges: an `a` of 2 GiB or more, or a `w`
+ * of 2 GiB or more, is HQ_ERR_UNSUPPORTED. */
 hq_status hq_gemm(const hq_plan* plan, int64_t m, const void* a, const float* a_scale,
                   const void* w, const void* meta, void* out, void* ws, size_t ws_bytes,
                   void* stream);
@@ -278,7 +280,8 @@ hq_status hq_moe_align(int64_t t, int topk, int num_experts, int block_m, const 
  * with an out-of-range expert id) are left unwritten.  ws: the workspace of
  * hq_moe_workspace_bytes (the fp8 requant's fp32 rows and row maxima, or the
  * combine's t*topk weighted slot rows), zero-filled once before first use
- * (the row maxima are re-armed by every call). */
+ * (the row maxima are re-armed by every call).  As for hq_gemm, activations
+ * or one expert's weights of 2 GiB or more are HQ_ERR_UNSUPPORTED. */
 hq_status hq_moe_workspace_bytes(const hq_plan* plan, int64_t t, int topk, size_t* bytes);
 hq_status hq_moe_gemm(const hq_plan* plan, int64_t t, int topk, const void* a, const float* a_scale,
                       const int32_t* sorted_ids, const int32_t* block_expert, const int32_t* num_padded,
