@@ -35,8 +35,11 @@ gemm     dense W4A16, W4A8 (MXFP4 x FP8 and INT4 x INT8) oracles and the
          per-output tolerance.
 moe      the grouped MoE layer: align invariants, gate_up + SiLU*mul (+ fp8
          requant), down + top-k combine.
+quant    the per-token (per-row) activation quantiser that feeds W4A8:
+         s = max|x| / Q, codes = RNE(x / s) as fp8 e4m3 or int8.
 
-Parity status: every function is pinned by tests/test_oracle.py against
+Parity status: every function is pinned by tests/test_oracle.py and
+tests/test_quant_oracle.py against
 hand-worked examples (tests/golden), code tables derived from the format
 definitions, torch's fp8 decoders, exact rational brute force and
 invariants.  No function is "parity unpinned".

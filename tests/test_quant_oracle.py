@@ -1,0 +1,135 @@
+"""Pins of the per-token activation quantiser oracle (CPU only).
+
+The oracle (oracle/quant.py) is checked against a hand-worked fixture
+(tests/golden/quant_per_token.json), torch's float8_e4m3fn cast, a brute-force
+nearest-value search over the code grids, and invariants that hold for any
+correct symmetric per-row quantiser.  The last test plants plausible mistakes
+in a copy of the rule and checks that these pins reject each one.
+"""
+import json
+import os
+
+import numpy as np
+import torch
+
+from oracle import formats as F
+from oracle import quant as QZ
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold():
+    with open(os.path.join(GOLD, "quant_per_token.json")) as f:
+        return json.load(f)
+
+
+def _rows(seed, m=24, k=200, dtype=torch.bfloat16):
+    """fp16/bf16-valued rows with different magnitudes, signs and outliers."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((m, k)) * 10.0 ** rng.integers(-3, 4, size=(m, 1))
+    x[::5, rng.integers(0, k)] *= -40.0                      # a negative outlier on some rows
+    x[3] = 0.0                                               # an all-zero row
+    x[4, :] = 0.0
+    x[4, 7] = -3.0                                           # a single negative entry
+    return torch.from_numpy(x).to(dtype).float().numpy()
+
+
+def _brute_e4m3(v):
+    """Nearest e4m3 code by exhaustive search over the 127 non-negative finite
+    codes; ties go to the even code; negative values take the sign bit
+    (a value that rounds to zero gives code 0)."""
+    vals = F.e4m3_value(np.arange(127))
+    out = np.empty(v.shape, dtype=np.uint8)
+    for i, x in np.ndenumerate(v):
+        d = np.abs(vals - abs(x))
+        cand = np.flatnonzero(d == d.min())
+        c = int(cand[0]) if len(cand) == 1 else int(cand[cand % 2 == 0][0])
+        out[i] = c | 0x80 if (x < 0 and c != 0) else c
+    return out
+
+
+def _brute_int(v):
+    """Nearest integer by comparison of floor and floor+1; ties to even."""
+    lo = np.floor(v)
+    hi = lo + 1
+    dlo, dhi = v - lo, hi - v
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    return np.clip(pick, -127, 127)
+
+
+def test_quant_hand_examples():
+    g = _gold()
+    c, s = QZ.quantize_rows(np.array(g["fp8"]["x"], np.float32), "fp8")
+    assert s.tolist() == g["fp8"]["scales"]
+    assert c.tolist() == [[int(h, 16) for h in row] for row in g["fp8"]["codes_hex"]]
+    c, s = QZ.quantize_rows(np.array(g["int8"]["x"], np.float32), "int8")
+    assert s.tolist() == g["int8"]["scales"]
+    assert c.tolist() == g["int8"]["codes"]
+
+
+def test_quant_fp8_codes_match_torch_cast_and_brute_force():
+    x = _rows(11)
+    codes, s = QZ.quantize_rows(x, "fp8")
+    v = (x / s[:, None]).astype(np.float32)                    # the float32 quotient the rule rounds
+    ref = torch.from_numpy(np.clip(v, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    neg_zero = (ref == 0x80)
+    assert np.array_equal(codes, np.where(neg_zero, 0, ref))
+    sub = v[:6, :40]
+    assert np.array_equal(codes[:6, :40], _brute_e4m3(np.clip(sub.astype(np.float64), -448, 448)))
+
+
+def test_quant_int8_codes_match_brute_force():
+    x = _rows(12, dtype=torch.float16)
+    codes, s = QZ.quantize_rows(x, "int8")
+    v = (x / s[:, None]).astype(np.float32).astype(np.float64)
+    assert np.array_equal(codes.astype(np.int64), _brute_int(v).astype(np.int64))
+
+
+def test_quant_invariants():
+    x = _rows(13)
+    for out, q in (("fp8", 448.0), ("int8", 127.0)):
+        codes, s = QZ.quantize_rows(x, out)
+        val = QZ.dequantize_rows(codes, np.ones_like(s), out)
+        nz = np.abs(x).max(1) > 0
+        # the largest magnitude of a non-zero row lands exactly on +-Q
+        assert np.all(np.abs(val[nz]).max(1) == q)
+        assert np.all(np.abs(val) <= q)
+        # all-zero rows: scale 1, codes 0
+        assert np.all(s[~nz] == 1.0) and np.all(val[~nz] == 0)
+        # every element within half a code step of x (times s)
+        err = np.abs(QZ.dequantize_rows(codes, s, out) - x)
+        assert np.all(err <= QZ.step_bound(x, s, out))
+        # sign symmetry
+        c2, s2 = QZ.quantize_rows(-x, out)
+        assert np.array_equal(s2, s)
+        assert np.array_equal(QZ.dequantize_rows(c2, s2, out), -QZ.dequantize_rows(codes, s, out))
+        # scaling by a power of two moves only the scale (of the non-zero rows)
+        c3, s3 = QZ.quantize_rows(x * np.float32(8.0), out)
+        assert np.array_equal(c3, codes)
+        assert np.array_equal(s3[nz], s[nz] * np.float32(8.0)) and np.all(s3[~nz] == 1.0)
+
+
+def test_quant_planted_mistakes_are_caught():
+    g = _gold()
+    xf = np.array(g["fp8"]["x"], np.float32)
+    xi = np.array(g["int8"]["x"], np.float32)
+    want_f = [[int(h, 16) for h in row] for row in g["fp8"]["codes_hex"]]
+    want_i = g["int8"]["codes"]
+
+    def rule(x, out, q=None, absmax=True, rnd=np.rint):
+        q = np.float32(q if q is not None else (448.0 if out == "fp8" else 127.0))
+        m = np.max(np.abs(x) if absmax else x, axis=1)
+        s = np.where(m > 0, m / q, np.float32(1)).astype(np.float32)
+        v = np.clip((x / s[:, None]).astype(np.float64), -float(q), float(q))
+        if out == "fp8":
+            return F.e4m3_encode(v).tolist()
+        return np.clip(rnd(v), -127, 127).astype(np.int64).tolist()
+
+    assert rule(xf, "fp8") == want_f and rule(xi, "int8") == want_i
+    assert rule(xi, "int8", q=128.0) != want_i                 # int8 range taken as 128
+    assert rule(xi, "int8", rnd=lambda v: np.floor(v + 0.5)) != want_i   # ties away from zero / up
+    assert rule(xi, "int8", rnd=np.trunc) != want_i            # truncation
+    assert rule(xf, "fp8", q=240.0) != want_f                  # e4m3 "fnuz"-style range
+    neg = np.array([[-896, 1, -2, 0.5, 0, 0, 0, 0]], np.float32)
+    c, s = QZ.quantize_rows(neg, "fp8")
+    assert s.tolist() == [2.0] and rule(neg, "fp8", absmax=False) != c.tolist()   # max without abs
