@@ -70,7 +70,8 @@ def test_quant_hand_examples():
 def test_quant_fp8_codes_match_torch_cast_and_brute_force():
     x = _rows(11)
     codes, s = QZ.quantize_rows(x, "fp8")
-    v = (x / s[:, None]).astype(np.float32)                    # the float32 quotient the rule rounds
+    inv = (np.float32(1) / s).astype(np.float32)
+    v = (x * inv[:, None]).astype(np.float32)                  # the float32 product the rule rounds
     ref = torch.from_numpy(np.clip(v, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     neg_zero = (ref == 0x80)
     assert np.array_equal(codes, np.where(neg_zero, 0, ref))
@@ -81,7 +82,7 @@ def test_quant_fp8_codes_match_torch_cast_and_brute_force():
 def test_quant_int8_codes_match_brute_force():
     x = _rows(12, dtype=torch.float16)
     codes, s = QZ.quantize_rows(x, "int8")
-    v = (x / s[:, None]).astype(np.float32).astype(np.float64)
+    v = (x * (np.float32(1) / s)[:, None]).astype(np.float32).astype(np.float64)
     assert np.array_equal(codes.astype(np.int64), _brute_int(v).astype(np.int64))
 
 
@@ -120,7 +121,7 @@ def test_quant_planted_mistakes_are_caught():
         q = np.float32(q if q is not None else (448.0 if out == "fp8" else 127.0))
         m = np.max(np.abs(x) if absmax else x, axis=1)
         s = np.where(m > 0, m / q, np.float32(1)).astype(np.float32)
-        v = np.clip((x / s[:, None]).astype(np.float64), -float(q), float(q))
+        v = np.clip((x * (np.float32(1) / s)[:, None]).astype(np.float64), -float(q), float(q))
         if out == "fp8":
             return F.e4m3_encode(v).tolist()
         return np.clip(rnd(v), -127, 127).astype(np.int64).tolist()
