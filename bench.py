@@ -26,6 +26,12 @@ Timings
 
 Algorithmic bytes per GEMM: N*K/2 (codes) + 2*N*K/128 (bf16 scales) +
 N*K/256 (4-bit zeros) + 2*M*K (A) + 2*M*N (C).  Flops: 2*M*N*K.
+
+`--workload quant` measures the per-token activation quantiser instead (the
+step before the W4A8 GEMMs): x bf16 [M, 7168] for M in {1, 16, 128, 1024},
+fp8 and int8 codes, inputs rotated over 16 copies; algorithmic bytes per
+launch 2*M*K (x) + M*K (codes) + 4*M (scales).  The default run is the decode
+sweep.
 """
 from __future__ import annotations
 
@@ -205,6 +211,135 @@ def cpu_baseline(budget_s: float):
                       f"(the dequantise step is single-threaded numpy)"}
 
 
+QUANT_M = (1, 16, 128, 1024)
+QUANT_K = 7168
+QUANT_METRIC = "per-token activation quantiser effective HBM GB/s vs M"
+QUANT_WORKLOAD = ("per-token activation quantiser (the W4A8 GEMMs' input step): x bf16 [M, 7168], "
+                  "M in {1,16,128,1024}, fp8 e4m3 and int8 codes + fp32 row scales")
+
+
+def quant_bytes(M, K):
+    return 2 * M * K + M * K + 4 * M
+
+
+def run_quant(args):
+    """The quantiser workload: one step = 8 launches (each M, fp8 and int8)."""
+    import bit_quantized_gemm_repack_amd as hq
+
+    dev = torch.device("cuda:0")
+    hip = Hip()
+    L = hq.lib()
+    # enough input copies that a step's rotation does not fit the 256 MB last-level cache
+    R = max(args.rotations, 16)
+    pts = []
+    for M in QUANT_M:
+        g = torch.Generator().manual_seed(M)
+        x = torch.randn((M, QUANT_K), generator=g).to(torch.bfloat16)
+        xs = [x.to(dev) for _ in range(R)]
+        for out in ("fp8", "int8"):
+            codes = torch.empty((M, QUANT_K), dtype=torch.uint8 if out == "fp8" else torch.int8, device=dev)
+            scales = torch.empty(M, dtype=torch.float32, device=dev)
+            pts.append(dict(M=M, out=out, xs=xs, codes=codes, scales=scales, bytes=quant_bytes(M, QUANT_K)))
+    step_bytes = sum(p["bytes"] for p in pts)
+
+    def step(r):
+        for p in pts:
+            hq.quantize_per_token(p["xs"][r], p["out"], codes=p["codes"], scales=p["scales"])
+
+    for i in range(max(1, args.warmup)):
+        step(i % R)
+    torch.cuda.synchronize()
+
+    graphs = []
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(0)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for r in range(R):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            step(r)
+        graphs.append(gr)
+    for i in range(args.warmup):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        graphs[i % R].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] graph steps: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+
+    n = len(pts)
+    evs = [(hip.event(), hip.event()) for _ in range(args.steps * n)]
+    for i in range(args.steps):
+        for j, p in enumerate(pts):
+            hq._check(L.hq_time_next_launch(*evs[i * n + j]))
+            hq.quantize_per_token(p["xs"][i % R], p["out"], codes=p["codes"], scales=p["scales"])
+    torch.cuda.synchronize()
+    per_point, tot = [], 0.0
+    for j, p in enumerate(pts):
+        ms = [hip.elapsed_ms(*evs[i * n + j]) for i in range(args.steps)]
+        tot += float(np.sum(ms))
+        us = float(np.mean(ms)) * 1e3
+        per_point.append({"M": p["M"], "K": QUANT_K, "out": p["out"], "kernel_us": round(us, 3),
+                          "GBps": round(p["bytes"] / (us * 1e-6) / 1e9, 1),
+                          "hbm_frac": round(p["bytes"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+    mean_us = tot / (args.steps * n) * 1e3
+    achieved = step_bytes / n / (mean_us * 1e-6) / 1e9
+
+    cpu = None
+    if not args.no_cpu:
+        # the CPU oracle leg: a spot check of the last timed launches' output, then its timing
+        from oracle import quant as QZ
+
+        for p in pts[-2:]:
+            ref_c, ref_s = QZ.quantize_rows(p["xs"][(args.steps - 1) % R].float().cpu().numpy(), p["out"])
+            if not (np.array_equal(p["codes"].cpu().numpy(), ref_c)
+                    and np.array_equal(p["scales"].cpu().numpy(), ref_s)):
+                raise SystemExit(f"bench: quantiser output check failed (M={p['M']} {p['out']})")
+        print("[bench] spot check against the oracle ok (codes and scales bit-exact); timing the CPU oracle",
+              file=sys.stderr, flush=True)
+        done, secs, runs = 0, 0.0, 0
+        while secs < args.cpu_budget:
+            for M in QUANT_M:
+                x = torch.randn((M, QUANT_K), generator=torch.Generator().manual_seed(M)).to(torch.bfloat16)
+                xf = x.float().numpy()
+                for out in ("fp8", "int8"):
+                    t0 = time.perf_counter()
+                    QZ.quantize_rows(xf, out)
+                    secs += time.perf_counter() - t0
+                    done += quant_bytes(M, QUANT_K)
+                    runs += 1
+        cpu = {"value": done / secs / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{runs} oracle runs over the 8 points of the workload (numpy float32 division, "
+                         f"float64 rounding to the code grid), {secs:.1f} s total, single-threaded numpy"}
+
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    line = {
+        "metric": QUANT_METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": QUANT_WORKLOAD, "launches_per_step": n, "step_bytes": step_bytes,
+                   "input_rotations": R, "timing": "HIP graph replay per step; kernel durations from "
+                                                   "dispatch-bracketing HIP events"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "hq::quantize_rows_kernel", "mean_kernel_us": round(mean_us, 3),
+                     "mean_algorithmic_bytes": int(step_bytes / n)},
+        "cpu_baseline": cpu,
+        "points": per_point,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,11 +348,16 @@ def main():
     ap.add_argument("--rotations", type=int, default=4)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--workload", choices=("decode", "quant"), default="decode",
+                    help="decode: the dense W4A16 decode sweep (default); quant: the per-token quantiser")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); the sharded "
               "form is a design note, not a measured path", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "quant":
+        run_quant(args)
+        return
 
     import bit_quantized_gemm_repack_amd as hq
 
@@ -235,8 +375,6 @@ def main():
     for i in range(max(1, args.warmup)):
         run_step(points, i % R)
     torch.cuda.synchronize()
-    max_ratio = check_point(points, shapes)
-    print(f"[bench] spot check ok (max err/tau {max_ratio:.3g})", file=sys.stderr, flush=True)
 
     # --- graphs: one per rotation -------------------------------------------
     graphs = []
@@ -303,8 +441,12 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        # the CPU oracle leg: a spot check of the timed launches' output, then its timing
+        max_ratio = check_point(points, shapes)
+        print(f"[bench] spot check against the oracle ok (max err/tau {max_ratio:.3g}); timing the CPU oracle",
+              file=sys.stderr, flush=True)
         cpu = cpu_baseline(args.cpu_budget)
+        cpu["spot_check_max_err_over_tau"] = round(max_ratio, 4)
 
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     line = {

@@ -126,6 +126,8 @@ _SIGS = {
                     [ctypes.c_size_t, ctypes.c_void_p]),
     "hq_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
                                       ctypes.c_void_p]),
+    "hq_quantize_per_token": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int] +
+                              [ctypes.c_void_p] * 4),
     "hq_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_size_t, ctypes.c_void_p]),
@@ -299,6 +301,32 @@ def stream_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int, nbytes: 
     _dev(buf, "buf"), _dev(sink, "sink")
     n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
     _check(lib().hq_stream_read(_ptr(buf), n, _ptr(sink), int(workgroups), _stream_ptr(buf.device)))
+
+
+def quantize_per_token(x: torch.Tensor, out: str = "fp8", codes: Optional[torch.Tensor] = None,
+                       scales: Optional[torch.Tensor] = None):
+    """Per-row 8-bit quantisation of fp16 / bf16 activations [m, k] (see
+    hq_quantize_per_token): scales = max|row| / Q, codes = RNE(x / scale).
+    out "fp8" gives uint8 e4m3 codes (Q = 448), "int8" int8 codes (Q = 127).
+    Returns (codes [m, k], scales fp32 [m]), the (a, a_scale) of a W4A8 GEMM."""
+    _dev(x, "x")
+    if x.dim() != 2 or x.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("x must be fp16 / bf16 [m, k]")
+    if out not in ("fp8", "int8"):
+        raise ValueError("out must be 'fp8' or 'int8'")
+    m, k = x.shape
+    cdt = torch.uint8 if out == "fp8" else torch.int8
+    if codes is None:
+        codes = torch.empty((m, k), dtype=cdt, device=x.device)
+    if scales is None:
+        scales = torch.empty(m, dtype=torch.float32, device=x.device)
+    _dev(codes, "codes"), _dev(scales, "scales")
+    if codes.shape != (m, k) or codes.element_size() != 1 or scales.numel() != m or scales.dtype != torch.float32:
+        raise ValueError("codes must be 1-byte [m, k] and scales fp32 [m]")
+    _check(lib().hq_quantize_per_token(m, k, BF16 if x.dtype == torch.bfloat16 else F16,
+                                       FP8_E4M3 if out == "fp8" else INT8, _ptr(x), _ptr(codes), _ptr(scales),
+                                       _stream_ptr(x.device)))
+    return codes, scales
 
 
 # ------------------------------------------------------------------- MoE --

@@ -866,6 +866,24 @@ hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, cons
   }
 }
 
+hq_status hq_quantize_per_token(int64_t m, int64_t k, hq_dtype in, hq_dtype out, const void* x, void* codes,
+                                float* scales, void* stream) {
+  const hq::TimingEvents ev = hq::take_timing();  // consumed by this call whatever happens
+  if (in != HQ_F16 && in != HQ_BF16) return fail(HQ_ERR_UNSUPPORTED, "input must be fp16 or bf16");
+  if (out != HQ_FP8_E4M3 && out != HQ_INT8) return fail(HQ_ERR_UNSUPPORTED, "codes must be fp8 e4m3 or int8");
+  if (m < 0 || m > (int64_t(1) << 24)) return fail(HQ_ERR_INVALID_ARG, "m out of range [0, 2^24]");
+  if (k < 8 || k % 8 || k > (int64_t(1) << 24)) return fail(HQ_ERR_INVALID_ARG, "k must be a multiple of 8 in [8, 2^24]");
+  if (m == 0) return ok();
+  if (!x || !codes || !scales) return fail(HQ_ERR_INVALID_ARG, "null device pointer");
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales))
+    return fail(HQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  hq::arm_timing(ev);
+  const int err = hq::launch_quantize_rows(m, k, in == HQ_BF16, out == HQ_FP8_E4M3, x, codes, scales, stream);
+  hq::arm_timing({nullptr, nullptr});
+  if (err != hipSuccess) return fail(HQ_ERR_HIP, "quantize launch: %s", hipGetErrorString((hipError_t)err));
+  return ok();
+}
+
 hq_status hq_stream_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups, void* stream) {
   if (!buf || !sink) return fail(HQ_ERR_INVALID_ARG, "null argument");
   if (bytes % 16 || !aligned16(buf)) return fail(HQ_ERR_INVALID_ARG, "buffer must be 16-byte aligned and sized");

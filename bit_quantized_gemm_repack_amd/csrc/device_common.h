@@ -30,6 +30,26 @@ __device__ inline uint16_t float_to_bf16_bits(float f) {
 // Round-to-nearest-even fp32 -> fp16 bits (the hardware conversion).
 __device__ inline uint16_t float_to_f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
+// Round-to-nearest-even fp32 -> OCP e4m3 (fn) code, saturating at 448; -0
+// gives code 0.  Below 2^-5 the subnormal and first normal binade share the
+// spacing 2^-9, so the code is the integer rint(|x| * 2^9); above it the
+// 23-bit mantissa is rounded to 3 bits (a carry moves into the exponent).
+__device__ inline uint32_t e4m3_code_rne(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fminf(fabsf(x), 448.f);
+  uint32_t code;
+  if (a < 0.03125f) {
+    code = (uint32_t)__builtin_rintf(a * 512.f);
+  } else {
+    const uint32_t bits = __float_as_uint(a);
+    const uint32_t exp = (bits >> 23) - 127u + 7u;
+    const uint32_t mant = bits & 0x7FFFFFu;
+    const uint32_t r = (mant + 0x7FFFFu + ((mant >> 20) & 1u)) >> 20;  // 0..8
+    code = (exp << 3) + r;
+  }
+  return code == 0 ? 0u : (sign | code);
+}
+
 __device__ inline i8_t cat8(u4_t x, u4_t y) {
   i8_t r;
   r[0] = x[0]; r[1] = x[1]; r[2] = x[2]; r[3] = x[3];

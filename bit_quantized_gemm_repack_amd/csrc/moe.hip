@@ -85,26 +85,6 @@ __global__ void __launch_bounds__(1024) moe_align_kernel(const int32_t* __restri
   }
 }
 
-// Round-to-nearest-even fp32 -> OCP e4m3 code for |x| <= 448.  Below 2^-5 the
-// subnormal and first normal binade share the spacing 2^-9, so the code is
-// the integer rint(|x| * 2^9); above it the 23-bit mantissa is rounded to 3
-// bits (a carry moves into the exponent field).
-__device__ inline uint32_t e4m3_code_rne(float x) {
-  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  const float a = fminf(fabsf(x), 448.f);
-  uint32_t code;
-  if (a < 0.03125f) {
-    code = (uint32_t)__builtin_rintf(a * 512.f);
-  } else {
-    const uint32_t bits = __float_as_uint(a);
-    const uint32_t exp = (bits >> 23) - 127u + 7u;
-    const uint32_t mant = bits & 0x7FFFFFu;
-    const uint32_t r = (mant + 0x7FFFFu + ((mant >> 20) & 1u)) >> 20;  // 0..8
-    code = (exp << 3) + r;
-  }
-  return code == 0 ? 0u : (sign | code);
-}
-
 // One wave per aligned row: s = max|act| / 448 (1 for an all-zero row),
 // codes = RNE_e4m3(act / s).  Resets the row maximum for the next call.
 __global__ void __launch_bounds__(256) moe_requant_kernel(const float* __restrict__ act32,

@@ -288,12 +288,37 @@ hq_status hq_moe_gemm(const hq_plan* plan, int64_t t, int topk, const void* a, c
                       const float* topk_w, const void* w, const void* meta, void* out, float* out_scale,
                       void* ws, size_t ws_bytes, void* stream);
 
-/* Kernel timing: the next hq_gemm, hq_moe_gemm or hq_stream_read call on this
- * thread records `start` (hipEvent_t, created by the caller with timing
- * enabled) when its first kernel starts and `stop` when its last kernel ends
- * (the split-K reduce, the fp8 requant or the combine's final pass included;
- * dispatch times, so no host launch overhead), and hipEventElapsedTime gives
- * the call's device duration.  The request is consumed by that call; passing
+/* ---------------------------------------------------------------------------
+ * Per-token activation quantiser: the step before a W4A8 GEMM, which takes
+ * 8-bit activations with one fp32 scale per row (W4A8: INT8 or FP8
+ * activations, FP8 for MXFP4 weights -- Humming page on news.ditty.ir,
+ * summary; cocoloop.cn, format section).  The pages do not say how the
+ * activations are quantised; this is the plain symmetric per-row rule, with
+ * the quotient taken as a product with the reciprocal scale:
+ *   scales[r]  = max_j |x[r, j]| / Q, computed in fp32 (1 for an all-zero row)
+ *   codes[r,j] = x[r, j] * (1 / scales[r]), reciprocal and product in fp32
+ *                (each correctly rounded), rounded to nearest even and
+ *                saturated to +-Q
+ * with Q = 448 and OCP e4m3fn codes (out = HQ_FP8_E4M3; -0 gives code 0) or
+ * Q = 127 and two's-complement int8 codes (out = HQ_INT8; -128 is never
+ * produced).  The (codes, scales) pair is what hq_gemm takes as (a, a_scale).
+ *   x       device [m, k] fp16 / bf16 (in = HQ_F16 / HQ_BF16), finite values
+ *           (non-finite inputs give unspecified codes, no fault)
+ *   codes   device [m, k] bytes, fully overwritten
+ *   scales  device fp32 [m], fully overwritten
+ * k must be a positive multiple of 8 (at most 2^24), m at most 2^24; m = 0
+ * is a no-op.  x, codes and scales must not overlap.  Honours
+ * hq_time_next_launch (one kernel).  The MoE gate_up GEMM has the same
+ * quantisation fused into its epilogue (HQ_EPI_SILU_MUL_QFP8). */
+hq_status hq_quantize_per_token(int64_t m, int64_t k, hq_dtype in, hq_dtype out, const void* x, void* codes,
+                                float* scales, void* stream);
+
+/* Kernel timing: the next hq_gemm, hq_moe_gemm, hq_quantize_per_token or
+ * hq_stream_read call on this thread records `start` (hipEvent_t, created by
+ * the caller with timing enabled) when its first kernel starts and `stop`
+ * when its last kernel ends (the split-K reduce, the fp8 requant or the
+ * combine's final pass included; dispatch times, so no host launch
+ * overhead), and hipEventElapsedTime gives the call's device duration.  The request is consumed by that call; passing
  * NULL, NULL cancels a pending request. */
 hq_status hq_time_next_launch(void* start_event, void* stop_event);
 

@@ -358,3 +358,22 @@ def test_moe_call_validation():
     assert L.hq_moe_gemm(p._h, 4, 8, *args(w=A + 8), 1 << 30, None) == hq.HQ_ERR_INVALID_ARG  # misaligned
     pq = hq.MoePlan(512, 7168, hq.w4a8_fp8(), 256, 64, "silu_mul_qfp8")
     assert L.hq_moe_gemm(pq._h, 4, 8, *args(a_scale=A), 1 << 30, None) == hq.HQ_ERR_INVALID_ARG  # no out_scale
+
+
+def test_quantize_call_validation():
+    """Argument checks of hq_quantize_per_token run before any launch (no GPU needed)."""
+    L = hq.lib()
+    fake = 1 << 20  # 16-byte aligned address that is never dereferenced: every call below is rejected
+    q = L.hq_quantize_per_token
+    assert q(4, 64, hq.F32, hq.FP8_E4M3, fake, fake, fake, None) == hq.HQ_ERR_UNSUPPORTED
+    assert q(4, 64, hq.BF16, hq.BF16, fake, fake, fake, None) == hq.HQ_ERR_UNSUPPORTED
+    assert q(-1, 64, hq.BF16, hq.INT8, fake, fake, fake, None) == hq.HQ_ERR_INVALID_ARG
+    assert q((1 << 24) + 1, 64, hq.BF16, hq.INT8, fake, fake, fake, None) == hq.HQ_ERR_INVALID_ARG
+    for k in (0, 4, 12, (1 << 24) + 8):
+        assert q(4, k, hq.BF16, hq.INT8, fake, fake, fake, None) == hq.HQ_ERR_INVALID_ARG
+    assert q(4, 64, hq.F16, hq.FP8_E4M3, None, fake, fake, None) == hq.HQ_ERR_INVALID_ARG
+    assert q(4, 64, hq.F16, hq.FP8_E4M3, fake, None, fake, None) == hq.HQ_ERR_INVALID_ARG
+    assert q(4, 64, hq.F16, hq.FP8_E4M3, fake, fake, None, None) == hq.HQ_ERR_INVALID_ARG
+    assert q(4, 64, hq.F16, hq.FP8_E4M3, fake + 8, fake, fake, None) == hq.HQ_ERR_INVALID_ARG
+    assert b"aligned" in L.hq_last_error()
+    assert q(0, 64, hq.F16, hq.FP8_E4M3, None, None, None, None) == hq.HQ_OK  # m = 0: no-op
