@@ -62,22 +62,28 @@ WORKLOAD = ("dense W4A16 decode sweep: M in {1,4,16,64} x (N,K) in {(4096,4096),
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qgemm_decode_sweep_traffic.json")
 
 
+# sources of the kernels a decode-sweep call runs (GEMM, split-K reduce, their
+# shared headers and launch helper); the plan strings cover the host heuristic
+DECODE_KERNEL_SOURCES = ("qgemm_skinny.hip", "qgemm_tiled.hip", "splitk_reduce.hip", "device_common.h",
+                         "hq_internal.h", "launch.h")
+
+
 def kernel_source_hash():
-    """sha256 over the library's kernel and host sources (sorted by name)."""
+    """sha256 over the sources of the decode-sweep kernels."""
     import hashlib
 
     csrc = os.path.join(ROOT, "bit_quantized_gemm_repack_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".cpp", ".h")):
-            h.update(name.encode())
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(f.read())
+    for name in DECODE_KERNEL_SOURCES:
+        h.update(name.encode())
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per call from the counter summary, if taken on these sources."""
+def measured_traffic(plans=None):
+    """HBM bytes per call from the counter summary, if it was taken on these
+    kernel sources and (when given) with these per-point plans."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -85,7 +91,125 @@ def measured_traffic():
         return None
     if t.get("source_sha256") != kernel_source_hash():
         return None
+    if plans is not None and [q.get("plan") for q in t.get("points", [])] != list(plans):
+        return None
     return t.get("hbm_bytes_per_call")
+
+
+def write_profiles(run_dir):
+    """Summaries under profiles/ from the rocprofv3 outputs of the decode bench
+    in run_dir (CPU only; the GPU commands are listed in the files written):
+      prof_bench/bench_kernel_{stats,trace}.csv  --kernel-trace --stats run
+      pmc_fetch/f_counter_collection.csv         --pmc FETCH_SIZE run
+      pmc_write/w_counter_collection.csv         --pmc WRITE_SIZE run
+      bench.json                                 a default bench run (last line)."""
+    import collections
+    import csv
+
+    def rows(path):
+        with open(os.path.join(run_dir, path)) as f:
+            return list(csv.DictReader(f))
+
+    n = len(SWEEP_M) * len(SWEEP_NK)
+    pts = [(M, N, K) for M in SWEEP_M for (N, K) in SWEEP_NK]
+    with open(os.path.join(run_dir, "bench.json")) as f:
+        b = json.loads(f.read().strip().splitlines()[-1])
+    plans = [p["plan"] for p in b["points"]]
+
+    # --- traffic: FETCH_SIZE / WRITE_SIZE per call (GEMM + its reduce) -------
+    fetch, write = rows("pmc_fetch/f_counter_collection.csv"), rows("pmc_write/w_counter_collection.csv")
+    wr = {r["Dispatch_Id"]: float(r["Counter_Value"]) for r in write}
+    # calibration: the runtime's copy kernels (the weight-pool clones) read what they write
+    cf = [(float(r["Counter_Value"]), wr[r["Dispatch_Id"]]) for r in fetch if "copyBuffer" in r["Kernel_Name"]]
+    fetch_scale = sum(w for _, w in cf) / sum(f for f, _ in cf)
+    calls, cur = [], None
+    for r in fetch:
+        k = r["Kernel_Name"]
+        if "qgemm" in k:
+            cur = {"kernel": k.split("(")[0], "fetch": float(r["Counter_Value"]), "write": wr[r["Dispatch_Id"]]}
+            calls.append(cur)
+        elif "splitk_reduce" in k and cur is not None:
+            cur["fetch"] += float(r["Counter_Value"])
+            cur["write"] += wr[r["Dispatch_Id"]]
+            cur["reduce"] = True
+    per = collections.defaultdict(list)
+    for i, c in enumerate(calls):
+        per[i % n].append(c)
+    tpoints, tot = [], 0.0
+    for j in range(n):
+        cs = per[j]
+        fb = sum(c["fetch"] for c in cs) / len(cs) * 1024 * fetch_scale
+        wb = sum(c["write"] for c in cs) / len(cs) * 1024
+        M, N, K = pts[j]
+        alg = algo_bytes(M, N, K)
+        tpoints.append(dict(M=M, N=N, K=K, kernel=cs[0]["kernel"], reduce=bool(cs[0].get("reduce")),
+                            hbm_read=int(fb), hbm_write=int(wb), algorithmic=alg, ratio=round((fb + wb) / alg, 3),
+                            plan=plans[j]))
+        tot += fb + wb
+    cmd = "cd /tmp && rocprofv3 --pmc {c} --output-format csv -d <repo>/gpurun_out/{d} -o {o} -- " \
+          "python3 <repo>/bench.py --steps 3 --warmup 1 --no-cpu"
+    traffic = {"source_sha256": kernel_source_hash(), "hbm_bytes_per_call": int(tot / n),
+               "algorithmic_bytes_per_call": int(sum(algo_bytes(*p) for p in pts) / n),
+               "fetch_scale": round(fetch_scale, 4), "write_scale": 1.0,
+               "calibration": "FETCH_SIZE (KiB per dispatch) scaled by written/fetched of the runtime's copy kernels "
+                              "in the same runs (a plain copy reads what it writes); WRITE_SIZE taken as is",
+               "commands": [cmd.format(c="FETCH_SIZE", d="pmc_fetch", o="f"),
+                            cmd.format(c="WRITE_SIZE", d="pmc_write", o="w"),
+                            "python3 bench.py --write-profiles gpurun_out   (this summary, on the CPU)"],
+               "points": tpoints}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(traffic, f, indent=1)
+
+    # --- kernel trace: per-kernel stats and per-call durations ---------------
+    stats, trace = rows("prof_bench/bench_kernel_stats.csv"), rows("prof_bench/bench_kernel_trace.csv")
+    calls, cur = [], None
+    for r in trace:
+        k = r["Kernel_Name"]
+        st, en = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        if "qgemm" in k:
+            cur = [st, en]
+            calls.append(cur)
+        elif "splitk_reduce" in k and cur is not None:
+            cur[1] = en
+    dur = [(c[1] - c[0]) / 1e3 for c in calls]
+    timed = dur[-20 * n:]
+    graph = dur[-40 * n:-20 * n]
+    mean_timed = sum(timed) / len(timed)
+    L = ["# qgemm -- dense W4A16 decode sweep, bf16, uint4 zero points (skinny / tiled + split-K reduce)", "",
+         "Workload: M in {1,4,16,64} x (N,K) in {(4096,4096),(14336,4096),(4096,14336)}, group 128, bf16 scales,",
+         "uint4 zero points, bf16 output; every call reads its own copy of the weights from a rotating pool (> 1 GB).",
+         "", "Kernel trace (from the repository root on the GPU host):", "", "```",
+         "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <repo>/gpurun_out/prof_bench -o bench -- \\",
+         "    python3 <repo>/bench.py --steps 20 --warmup 5 --no-cpu",
+         "python3 bench.py --write-profiles gpurun_out      # this file and the traffic summary, on the CPU", "```", "",
+         "`bench_kernel_stats.csv`, library kernels (every dispatch of the run: eager warm-up, graph replays, "
+         "event-timed pass):", "", "| kernel | calls | total ns | average ns | min ns | max ns |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        if "hq::" in r["Name"]:
+            L.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {r['TotalDurationNs']} | {float(r['AverageNs']):.0f} | "
+                     f"{r['MinNs']} | {r['MaxNs']} |")
+    L += ["", f"hq_gemm calls in the trace (GEMM dispatch start to the end of its split-K reduce, where there is one): "
+              f"the traced run's event-timed pass (its last {len(timed)} calls) averages {mean_timed:.2f} us per call, "
+              f"its graph replays {sum(graph) / len(graph):.2f} us, all {len(calls)} calls {sum(dur) / len(dur):.2f} us "
+              f"(the first passes run on cold caches and workspaces).  The bench's own dispatch-bracketing events in "
+              f"the default run (below) give {b['roofline']['mean_kernel_us']:.2f} us per call "
+              f"({100 * (b['roofline']['mean_kernel_us'] / mean_timed - 1):+.1f} % against the traced timed pass, "
+              f"which carries the profiler's overhead).", "",
+          f"Bench line (default `python3 bench.py`): {b['value']} GB/s over the step ({b['ms_per_step'] * 1e3:.1f} us "
+          f"per step of {n} graph-replayed calls); roofline achieved {b['roofline']['achieved']} GB/s = "
+          f"{100 * b['roofline']['frac']:.1f} % of 8 TB/s; CPU oracle {b['cpu_baseline']['value']:.3f} GB/s on "
+          f"{b['cpu_baseline']['cores']} BLAS threads.", "",
+          "| M | N | K | us | GB/s | % of 8 TB/s | HBM bytes / algorithmic | plan |", "|---|---|---|---|---|---|---|---|"]
+    for p, t in zip(b["points"], tpoints):
+        L.append(f"| {p['M']} | {p['N']} | {p['K']} | {p['kernel_us']:.2f} | {p['GBps']:.0f} | "
+                 f"{100 * p['hbm_frac']:.1f} | {t['ratio']:.2f} | {p['plan']} |")
+    L += ["", f"HBM traffic per call (`qgemm_decode_sweep_traffic.json`): FETCH_SIZE and WRITE_SIZE from two `--pmc` "
+              f"runs of the same bench (commands in that file), FETCH scaled by {traffic['fetch_scale']} (the copy "
+              f"kernels' written/fetched ratio), WRITE by 1.0: {traffic['hbm_bytes_per_call'] / 1e6:.2f} MB per call "
+              f"against {traffic['algorithmic_bytes_per_call'] / 1e6:.2f} MB algorithmic."]
+    with open(os.path.join(ROOT, "profiles", "qgemm_decode_sweep_w4a16_bf16.md"), "w") as f:
+        f.write("\n".join(L) + "\n")
+    print(f"wrote {TRAFFIC_FILE} and profiles/qgemm_decode_sweep_w4a16_bf16.md")
 
 
 def algo_bytes(M, N, K):
@@ -340,6 +464,280 @@ def run_quant(args):
     print(json.dumps(line), flush=True)
 
 
+# ----------------------------------------------------------------------------
+# Further workloads (non-default): each point is a list of library calls; a
+# point's time is the sum of its calls' durations (dispatch-bracketing events),
+# its roofline t_roof = max(flops / MFMA peak of its dtype, bytes / 8 TB/s).
+# ----------------------------------------------------------------------------
+FP16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
+
+
+def _prefill_points(dev):
+    import bit_quantized_gemm_repack_amd as hq
+    import datagen
+
+    N = K = 8192
+    pts = []
+    for M in (1024, 4096):
+        d = datagen.dense_w4a16(M, N, K, act="f16", zp="fixed", key=(3,))
+        plan = hq.Plan(N, K, hq.w4a16("f16"), max_m=M)
+        w, meta = plan.repack(torch.from_numpy(d["codes"]).to(dev), d["scales"].to(dev))
+        R = 32  # 32 weight copies of 33.6 MB: > 1 GB
+        ws_ = [(w.clone(), meta.clone()) for _ in range(R)]
+        a_ = [d["a"].to(dev) for _ in range(4)]
+        out = torch.empty((M, N), dtype=torch.float16, device=dev)
+        ws = plan.workspace(M, dev)
+        byt = N * K // 2 + 2 * N * (K // 128) + 2 * M * K + 2 * M * N
+        pts.append(dict(name=f"M={M} N={N} K={K}", R=R, bytes=byt, flops=2 * M * N * K, peak=FP16_PEAK_TFLOPS,
+                        plan=plan.describe(M),
+                        calls=lambda r, plan=plan, ws_=ws_, a_=a_, out=out, ws=ws:
+                        [lambda: plan.gemm(a_[r % 4], ws_[r][0], ws_[r][1], out=out, ws=ws)]))
+    return pts, "quantized GEMM TFLOPS vs M (dense W4A16 prefill)", \
+        "dense W4A16 prefill: M in {1024,4096}, N = K = 8192, fp16 activations, uint4 weights (group 128, fp16 " \
+        "scales, zero point 8), fp16 output", "f16"
+
+
+def _w4a8_points(dev):
+    import bit_quantized_gemm_repack_amd as hq
+    import datagen
+
+    N, K = 4096, 7168
+    pts = []
+    for kind in ("mxfp4", "int"):
+        for M in (1, 16, 128, 1024):
+            d = datagen.w4a8_mxfp4(M, N, K) if kind == "mxfp4" else datagen.w4a8_int(M, N, K)
+            plan = hq.Plan(N, K, hq.w4a8_mxfp4() if kind == "mxfp4" else hq.w4a8_int(), max_m=M)
+            if kind == "mxfp4":
+                w, meta = plan.repack(torch.from_numpy(d["codes"]).to(dev), e8m0=torch.from_numpy(d["e8m0"]).to(dev))
+            else:
+                w, meta = plan.repack(torch.from_numpy(d["codes"]).to(dev), d["scales"].to(dev))
+            R = 64  # 64 copies of ~15.6 MB: > 1 GB
+            ws_ = [(w.clone(), meta.clone()) for _ in range(R)]
+            a, sa = d["a_codes"].to(dev), d["a_scale"].to(dev)
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            ws = plan.workspace(M, dev)
+            meta_b = N * K // 32 if kind == "mxfp4" else 2 * N * (K // 128)
+            byt = N * K // 2 + meta_b + M * K + 4 * M + 2 * M * N
+            pts.append(dict(name=f"{kind} M={M} N={N} K={K}", R=R, bytes=byt, flops=2 * M * N * K,
+                            peak=FP8_PEAK_TFLOPS, plan=plan.describe(M),
+                            calls=lambda r, plan=plan, ws_=ws_, a=a, sa=sa, out=out, ws=ws:
+                            [lambda: plan.gemm(a, ws_[r][0], ws_[r][1], a_scale=sa, out=out, ws=ws)]))
+        del d
+    return pts, "quantized GEMM TFLOPS and effective HBM GB/s vs M (W4A8)", \
+        "dense W4A8: M in {1,16,128,1024}, N = 4096, K = 7168; MXFP4 weights (E8M0 scales) x fp8 e4m3 " \
+        "activations, and INT4 weights (fp16 scales, zero point 8) x int8 activations; bf16 output", "f8/i8"
+
+
+def _moe_points(dev):
+    import bit_quantized_gemm_repack_amd as hq
+    import datagen
+
+    E, H, I, topk = 256, 7168, 256, 8
+    wts = datagen.moe_weights(E, H, I, key=(5,))
+    pts = []
+    for act in ("bf16", "fp8"):
+        q = hq.w4a16("bf16", scale="f16") if act == "bf16" else hq.w4a8_fp8(scale="f16")
+        p1 = hq.MoePlan(2 * I, H, q, E, 4096, "silu_mul" if act == "bf16" else "silu_mul_qfp8")
+        p2 = hq.MoePlan(H, I, q, E, 4096, "topk_combine")
+        w1, m1 = p1.repack(torch.from_numpy(wts["w1"]).to(dev), wts["s1"].to(dev))
+        w2, m2 = p2.repack(torch.from_numpy(wts["w2"]).to(dev), wts["s2"].to(dev))
+        R = 2  # two copies of the 727 MB expert weights: > 1 GB
+        cp = [(w1, m1, w2, m2)] + [(w1.clone(), m1.clone(), w2.clone(), m2.clone()) for _ in range(R - 1)]
+        for T in (1, 32, 512, 4096):
+            rt = datagen.moe_routing(T)
+            x = datagen.moe_activations(T, act=act)
+            ids = torch.from_numpy(rt["topk_ids"]).to(dev)
+            tw = torch.from_numpy(rt["topk_w"]).to(dev)
+            xa = (x["x"] if act == "bf16" else x["x_codes"]).to(dev)
+            xs = None if act == "bf16" else x["x_scale"].to(dev)
+            bm = p1.block_m(T, topk)
+            mp = hq.moe_max_padded(T, topk, E, bm)
+            sid = torch.empty(mp, dtype=torch.int32, device=dev)
+            bex = torch.empty(max(mp // bm, 1), dtype=torch.int32, device=dev)
+            npad = torch.empty(1, dtype=torch.int32, device=dev)
+            inter = torch.empty((mp, I), dtype=torch.bfloat16 if act == "bf16" else torch.uint8, device=dev)
+            iscale = None if act == "bf16" else torch.empty(mp, dtype=torch.float32, device=dev)
+            y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+            ws1, ws2 = p1.moe_workspace(T, topk, dev), p2.moe_workspace(T, topk, dev)
+            hit = int(np.unique(rt["topk_ids"]).size)
+            wbytes = hit * (2 * I * H // 2 + 2 * (2 * I) * (H // 128) + H * I // 2 + 2 * H * (I // 128))
+            abytes = 2 if act == "bf16" else 1
+            # A once (+ scale), the intermediate written once and read once, y once
+            byt = wbytes + T * H * abytes + (4 * T if act == "fp8" else 0) + 2 * T * topk * I * abytes + 2 * T * H
+            flops = 2 * T * topk * (2 * I * H + H * I)
+
+            def calls(r, cp=cp, ids=ids, tw=tw, xa=xa, xs=xs, bm=bm, sid=sid, bex=bex, npad=npad, inter=inter,
+                      iscale=iscale, y=y, ws1=ws1, ws2=ws2, T=T, p1=p1, p2=p2, act=act):
+                w1_, m1_, w2_, m2_ = cp[r]
+                L = hq.lib()
+
+                def align():
+                    hq._check(L.hq_moe_align(T, topk, E, bm, hq._ptr(ids), hq._ptr(sid), hq._ptr(bex),
+                                             hq._ptr(npad), hq._stream_ptr(ids.device)))
+
+                def gate_up():
+                    p1.moe_gemm(xa, T, topk, sid, bex, npad, w1_, m1_, a_scale=xs, out=inter, out_scale=iscale,
+                                ws=ws1)
+
+                def down():
+                    p2.moe_gemm(inter, T, topk, sid, bex, npad, w2_, m2_, a_scale=iscale, topk_w=tw, out=y, ws=ws2)
+
+                return [align, gate_up, down]
+
+            pts.append(dict(name=f"{act} T={T} (experts hit {hit})", R=R, bytes=byt, flops=flops,
+                            peak=FP16_PEAK_TFLOPS if act == "bf16" else FP8_PEAK_TFLOPS,
+                            plan=f"block_m={bm} gate_up: {p1.describe(T)} | down: {p2.describe(T)}", calls=calls))
+    return pts, "MoE layer TFLOPS and effective HBM GB/s vs T", \
+        "MoE layer on one GPU's tensor-parallel share: 256 experts, top-8, hidden 7168, intermediate 256; " \
+        "align + gate_up (SiLU * up; bf16, or fp8 requant for W4A8-FP8) + down with the top-k combine; INT4 " \
+        "weights (group 128, fp16 scales, zero point 8); T in {1,32,512,4096}", "bf16/f8"
+
+
+def run_points_workload(args, builder):
+    import bit_quantized_gemm_repack_amd as hq
+
+    dev = torch.device("cuda:0")
+    hip = Hip()
+    L = hq.lib()
+    print(f"[bench] preparing the {args.workload} workload", file=sys.stderr, flush=True)
+    pts, metric, workload, dtype = builder(dev)
+    R = max(p["R"] for p in pts)
+
+    def step(r):
+        for p in pts:
+            for c in p["calls"](r % p["R"]):
+                c()
+
+    for i in range(max(1, args.warmup)):
+        step(i)
+    torch.cuda.synchronize()
+    graphs = []
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        step(0)
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    for r in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(r)
+        graphs.append(g)
+    for i in range(args.warmup):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        graphs[i % R].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] graph steps: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+
+    # per-point durations: the sum of the point's calls, each bracketed by events
+    times = {j: [] for j in range(len(pts))}
+    for i in range(args.steps):
+        pend = []
+        for j, p in enumerate(pts):
+            for c in p["calls"](i % p["R"]):
+                a, b = hip.event(), hip.event()
+                hq._check(L.hq_time_next_launch(a, b))
+                c()
+                pend.append((j, i, a, b))
+        torch.cuda.synchronize()
+        per = {}
+        for j, _, a, b in pend:
+            per[j] = per.get(j, 0.0) + hip.elapsed_ms(a, b)
+            hip.destroy(a)
+            hip.destroy(b)
+        for j, v in per.items():
+            times[j].append(v)
+    points, shares = [], []
+    for j, p in enumerate(pts):
+        ms = np.array(times[j])
+        us = float(np.median(ms)) * 1e3
+        t_hbm = p["bytes"] / (HBM_PEAK_GBS * 1e3)
+        t_mfma = p["flops"] / (p["peak"] * 1e6)
+        bound = "hbm" if t_hbm >= t_mfma else "mfma"
+        points.append({"point": p["name"], "kernel_us": round(us, 3),
+                       "kernel_us_p10": round(float(np.percentile(ms, 10)) * 1e3, 3),
+                       "kernel_us_p90": round(float(np.percentile(ms, 90)) * 1e3, 3),
+                       "GBps": round(p["bytes"] / us / 1e3, 1), "TFLOPS": round(p["flops"] / us / 1e6, 2),
+                       "bound": bound, "roofline_frac": round(max(t_hbm, t_mfma) / us, 4),
+                       "mfma_frac": round(t_mfma / us, 4), "hbm_frac": round(t_hbm / us, 4), "plan": p["plan"]})
+        shares.append(us)
+    step_bytes = sum(p["bytes"] for p in pts)
+    step_flops = sum(p["flops"] for p in pts)
+    dom = int(np.argmax(shares))
+    dp, dq = points[dom], pts[dom]
+    if dp["bound"] == "mfma":
+        roof = {"bound": "mfma", "achieved": dp["TFLOPS"], "peak": dq["peak"], "unit": "TFLOP/s",
+                "frac": dp["mfma_frac"]}
+    else:
+        roof = {"bound": "hbm", "achieved": dp["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dp["hbm_frac"]}
+    roof.update({"traffic": None, "point": dp["point"], "kernel_us": dp["kernel_us"]})
+
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = _cpu_sample(args.workload, args.cpu_budget)
+    line = {"metric": metric, "value": round(step_flops / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+            "config": {"workload": workload, "points_per_step": len(pts), "step_bytes": step_bytes,
+                       "step_flops": step_flops, "gbps_per_step_time": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+                       "timing": "HIP graph replay per step; per-point time = sum of its calls' "
+                                 "dispatch-bracketing HIP events, median over the steps"},
+            "roofline": roof, "cpu_baseline": cpu, "points": points}
+    print(json.dumps(line), flush=True)
+
+
+def _cpu_sample(workload, budget):
+    """The oracle on a row sample of the workload, in TFLOP/s of oracle work."""
+    import datagen
+    from oracle import gemm as og
+
+    flops, secs, runs = 0, 0.0, 0
+    while secs < budget:
+        if workload == "prefill":
+            M, N, K = 8, 8192, 8192
+            d = datagen.dense_w4a16(M, N, K, act="f16", zp="fixed", key=(3,))
+            t0 = time.perf_counter()
+            og.gemm_w4a16(d["a"].double().numpy(), d["codes"], d["scales"].double().numpy(), 8, out_fmt="f16")
+            what = "dense W4A16 M=8 rows of N = K = 8192"
+        elif workload == "w4a8":
+            M, N, K = 16, 4096, 7168
+            d = datagen.w4a8_mxfp4(M, N, K)
+            t0 = time.perf_counter()
+            og.gemm_mxfp4_fp8(d["a_codes"].numpy(), d["a_scale"].numpy(), d["codes"], d["e8m0"])
+            what = "W4A8-MXFP4 M=16 N=4096 K=7168"
+        else:
+            from oracle import moe as om
+
+            M, N, K = 8, 512, 7168  # one token's 8 gate_up rows, each through its own expert
+            rt = datagen.moe_routing(1)
+            wts = datagen.moe_weights(256, 7168, 256, key=(5,), experts=rt["topk_ids"][0])
+            x = datagen.moe_activations(1)["x"].double().numpy()
+            rows = np.repeat(x, 8, axis=0)
+            t0 = time.perf_counter()
+            om.gate_up(rows, rt["topk_ids"][0], wts["w1"], wts["s1"].double().numpy(), 256)
+            what = "MoE gate_up of one token (8 experts, N = 512, K = 7168)"
+        secs += time.perf_counter() - t0
+        flops += 2 * M * N * K
+        runs += 1
+    try:
+        import threadpoolctl
+
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{runs} oracle runs of {what} (unpack + float64 dequantise + float64 GEMM), {secs:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -348,15 +746,24 @@ def main():
     ap.add_argument("--rotations", type=int, default=4)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--workload", choices=("decode", "quant"), default="decode",
-                    help="decode: the dense W4A16 decode sweep (default); quant: the per-token quantiser")
+    ap.add_argument("--workload", choices=("decode", "quant", "prefill", "w4a8", "moe"), default="decode",
+                    help="decode: the dense W4A16 decode sweep (default); quant: the per-token quantiser; "
+                         "prefill / w4a8 / moe: the other GEMM workloads")
+    ap.add_argument("--write-profiles", metavar="RUN_DIR",
+                    help="CPU only: write the profiles/ summaries from rocprofv3 outputs in RUN_DIR and exit")
     args = ap.parse_args()
+    if args.write_profiles:
+        write_profiles(args.write_profiles)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); the sharded "
               "form is a design note, not a measured path", file=sys.stderr)
         sys.exit(2)
     if args.workload == "quant":
         run_quant(args)
+        return
+    if args.workload in ("prefill", "w4a8", "moe"):
+        run_points_workload(args, {"prefill": _prefill_points, "w4a8": _w4a8_points, "moe": _moe_points}[args.workload])
         return
 
     import bit_quantized_gemm_repack_amd as hq
@@ -467,7 +874,8 @@ def main():
                    "weight_pool_rotations": R, "timing": "HIP graph replay per step; kernel durations from "
                                                          "dispatch-bracketing HIP events"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic([p["plan"] for p in per_point]),
                      "kernel": "hq_gemm calls of the sweep: hq::qgemm_skinny / hq::qgemm_tiled "
                                "(+ hq::splitk_reduce_kernel where K is split)",
                      "mean_kernel_us": round(mean_kernel_us, 3), "mean_algorithmic_bytes": int(mean_bytes)},

@@ -650,14 +650,17 @@ hq_status hq_moe_max_padded(int64_t t, int topk, int num_experts, int block_m, i
 
 hq_status hq_moe_align(int64_t t, int topk, int num_experts, int block_m, const int32_t* topk_ids,
                        int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded, void* stream) {
+  const hq::TimingEvents ev = hq::take_timing();  // consumed by this call whatever happens
   try {
     if (!topk_ids || !sorted_ids || !block_expert || !num_padded) return fail(HQ_ERR_INVALID_ARG, "null pointer");
     if (t < 1 || topk < 1 || num_experts < 1 || block_m < 1) return fail(HQ_ERR_INVALID_ARG, "bad sizes");
     if (t * topk > (int64_t(1) << 20)) return fail(HQ_ERR_UNSUPPORTED, "t * topk above 2^20");
     if (num_experts > 4096) return fail(HQ_ERR_UNSUPPORTED, "more than 4096 experts");
     if (block_m % 16) return fail(HQ_ERR_INVALID_ARG, "block_m must be a multiple of 16");
+    hq::arm_timing(ev);
     int err = hq::launch_moe_align(t, topk, num_experts, block_m, topk_ids, sorted_ids, block_expert, num_padded,
                                    stream);
+    hq::arm_timing({nullptr, nullptr});
     if (err != hipSuccess) return fail(HQ_ERR_HIP, "align launch: %s", hipGetErrorString((hipError_t)err));
     return ok();
   } catch (...) {

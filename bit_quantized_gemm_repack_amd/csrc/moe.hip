@@ -136,9 +136,8 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(const float4* __restri
 int launch_moe_align(int64_t t, int topk, int num_experts, int block_m, const int32_t* ids, int32_t* sorted_ids,
                      int32_t* block_expert, int32_t* num_padded, void* stream) {
   const size_t lds = (size_t)(3 * (num_experts + 1) + 1) * sizeof(int);
-  hipLaunchKernelGGL(moe_align_kernel, dim3(1), dim3(1024), lds, static_cast<hipStream_t>(stream), ids,
-                     (int)(t * topk), num_experts, block_m, sorted_ids, block_expert, num_padded);
-  return (int)hipGetLastError();
+  return (int)launch_timed(moe_align_kernel, dim3(1), dim3(1024), lds, static_cast<hipStream_t>(stream), ids,
+                           (int)(t * topk), num_experts, block_m, sorted_ids, block_expert, num_padded);
 }
 
 int launch_moe_requant(const float* act32, uint32_t* row_amax, const int32_t* sorted_ids, const int32_t* num_padded,

@@ -313,13 +313,14 @@ hq_status hq_moe_gemm(const hq_plan* plan, int64_t t, int topk, const void* a, c
 hq_status hq_quantize_per_token(int64_t m, int64_t k, hq_dtype in, hq_dtype out, const void* x, void* codes,
                                 float* scales, void* stream);
 
-/* Kernel timing: the next hq_gemm, hq_moe_gemm, hq_quantize_per_token or
- * hq_stream_read call on this thread records `start` (hipEvent_t, created by
- * the caller with timing enabled) when its first kernel starts and `stop`
- * when its last kernel ends (the split-K reduce, the fp8 requant or the
- * combine's final pass included; dispatch times, so no host launch
- * overhead), and hipEventElapsedTime gives the call's device duration.  The request is consumed by that call; passing
- * NULL, NULL cancels a pending request. */
+/* Kernel timing: the next hq_gemm, hq_moe_align, hq_moe_gemm,
+ * hq_quantize_per_token or hq_stream_read call on this thread records
+ * `start` (hipEvent_t, created by the caller with timing enabled) when its
+ * first kernel starts and `stop` when its last kernel ends (the split-K
+ * reduce, the fp8 requant or the combine's final pass included; dispatch
+ * times, so no host launch overhead), and hipEventElapsedTime gives the
+ * call's device duration.  The request is consumed by that call (also when
+ * it fails); passing NULL, NULL cancels a pending request. */
 hq_status hq_time_next_launch(void* start_event, void* stop_event);
 
 /* Bandwidth probe (measurement helper, not part of the GEMM): read `bytes`
