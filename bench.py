@@ -210,6 +210,67 @@ def write_profiles(run_dir):
     with open(os.path.join(ROOT, "profiles", "qgemm_decode_sweep_w4a16_bf16.md"), "w") as f:
         f.write("\n".join(L) + "\n")
     print(f"wrote {TRAFFIC_FILE} and profiles/qgemm_decode_sweep_w4a16_bf16.md")
+    _write_workload_profiles(run_dir, rows)
+
+
+_WORKLOAD_PROFILES = {
+    "quant": ("quantize_rows_per_token_k7168.md", "per-token activation quantiser, x bf16 [M, 7168], "
+              "M in {1,16,128,1024}, fp8 and int8 codes"),
+    "prefill": ("qgemm_tiled_prefill_w4a16_f16.md", "dense W4A16 prefill, M in {1024,4096}, N = K = 8192, fp16"),
+    "w4a8": ("qgemm_w4a8_mxfp4_int8_n4096_k7168.md", "dense W4A8, M in {1,16,128,1024}, N = 4096, K = 7168, "
+             "MXFP4 x fp8 and INT4 x int8"),
+    "moe": ("moe_layer_e256_top8_h7168_i256.md", "MoE layer, 256 experts, top-8, hidden 7168, intermediate 256, "
+            "T in {1,32,512,4096}, bf16 and fp8 activations"),
+}
+
+
+def _write_workload_profiles(run_dir, rows):
+    """profiles/<kernel>_<workload>.md for each workload traced in run_dir:
+    prof_<w>/<w>_kernel_stats.csv (--kernel-trace --stats) and, if present,
+    bench_<w>.log (the workload's bench line)."""
+    for w, (fname, what) in _WORKLOAD_PROFILES.items():
+        path = os.path.join(run_dir, f"prof_{w}", f"{w}_kernel_stats.csv")
+        if not os.path.exists(path):
+            continue
+        stats = rows(f"prof_{w}/{w}_kernel_stats.csv")
+        L = [f"# {what}", "", "Kernel trace (from the repository root on the GPU host):", "", "```",
+             f"cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <repo>/gpurun_out/prof_{w} -o {w} -- \\",
+             f"    python3 <repo>/bench.py --workload {w} --steps 10 --warmup 2 --no-cpu",
+             "python3 bench.py --write-profiles gpurun_out      # this summary, on the CPU", "```", "",
+             f"`{w}_kernel_stats.csv`, library kernels (every dispatch of the run: eager warm-up, graph replays, "
+             "event-timed pass; averages mix the workload's points where one kernel serves several):", "",
+             "| kernel | calls | total ns | average ns | min ns | max ns |", "|---|---|---|---|---|---|"]
+        for r in stats:
+            if "hq::" in r["Name"]:
+                L.append(f"| `{r['Name'][:100]}` | {r['Calls']} | {r['TotalDurationNs']} | {float(r['AverageNs']):.0f} | "
+                         f"{r['MinNs']} | {r['MaxNs']} |")
+        log = os.path.join(run_dir, f"bench_{w}.log")
+        if os.path.exists(log):
+            with open(log) as f:
+                lines = [x for x in f if x.startswith("{")]
+            if lines:
+                b = json.loads(lines[-1])
+                cmd = f"python3 bench.py --workload {w}" + (" --steps 20 --warmup 3 --cpu-budget 8" if w != "quant"
+                                                             else " --cpu-budget 5")
+                L += ["", f"Bench line (`{cmd}`): value {b['value']} {b['unit']} ({b['ms_per_step'] * 1e3:.1f} us per "
+                          f"step); roofline {json.dumps(b['roofline'])}; CPU oracle "
+                          f"{b['cpu_baseline']['value']:.4g} {b['cpu_baseline']['unit']} "
+                          f"({b['cpu_baseline']['sample']}).", ""]
+                if w == "quant":
+                    L += ["| M | codes | us | GB/s | % of 8 TB/s |", "|---|---|---|---|---|"]
+                    for p in b["points"]:
+                        L.append(f"| {p['M']} | {p['out']} | {p['kernel_us']:.2f} | {p['GBps']:.0f} | "
+                                 f"{100 * p['hbm_frac']:.1f} |")
+                else:
+                    L += ["| point | us (median) | p10 | p90 | GB/s | TFLOP/s | bound | % of bound | plan |",
+                          "|---|---|---|---|---|---|---|---|---|"]
+                    for p in b["points"]:
+                        L.append(f"| {p['point']} | {p['kernel_us']:.1f} | {p['kernel_us_p10']:.1f} | "
+                                 f"{p['kernel_us_p90']:.1f} | {p['GBps']:.0f} | {p['TFLOPS']:.1f} | {p['bound']} | "
+                                 f"{100 * p['roofline_frac']:.1f} | {p['plan']} |")
+        with open(os.path.join(ROOT, "profiles", fname), "w") as f:
+            f.write("\n".join(L) + "\n")
+        print(f"wrote profiles/{fname}")
 
 
 def algo_bytes(M, N, K):
