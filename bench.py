@@ -117,7 +117,8 @@ def write_profiles(run_dir):
     plans = [p["plan"] for p in b["points"]]
 
     # --- traffic: FETCH_SIZE / WRITE_SIZE per call (GEMM + its reduce) -------
-    fetch, write = rows("pmc_fetch/f_counter_collection.csv"), rows("pmc_write/w_counter_collection.csv")
+    fetch = sorted(rows("pmc_fetch/f_counter_collection.csv"), key=lambda r: int(r["Dispatch_Id"]))
+    write = rows("pmc_write/w_counter_collection.csv")
     wr = {r["Dispatch_Id"]: float(r["Counter_Value"]) for r in write}
     # calibration: the runtime's copy kernels (the weight-pool clones) read what they write
     cf = [(float(r["Counter_Value"]), wr[r["Dispatch_Id"]]) for r in fetch if "copyBuffer" in r["Kernel_Name"]]
@@ -161,7 +162,8 @@ def write_profiles(run_dir):
         json.dump(traffic, f, indent=1)
 
     # --- kernel trace: per-kernel stats and per-call durations ---------------
-    stats, trace = rows("prof_bench/bench_kernel_stats.csv"), rows("prof_bench/bench_kernel_trace.csv")
+    stats = rows("prof_bench/bench_kernel_stats.csv")
+    trace = sorted(rows("prof_bench/bench_kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
     calls, cur = [], None
     for r in trace:
         k = r["Kernel_Name"]
@@ -203,6 +205,14 @@ def write_profiles(run_dir):
     for p, t in zip(b["points"], tpoints):
         L.append(f"| {p['M']} | {p['N']} | {p['K']} | {p['kernel_us']:.2f} | {p['GBps']:.0f} | "
                  f"{100 * p['hbm_frac']:.1f} | {t['ratio']:.2f} | {p['plan']} |")
+    L += ["", "Per point, the bench's events against the trace (mean over the traced run's event-timed pass and its "
+              "graph replays; the profiler widens the gap between a split-K GEMM and its reduce):", "",
+          "| M | N | K | bench events us | trace, timed pass us | trace, graph replays us |", "|---|---|---|---|---|---|"]
+    for j, p in enumerate(b["points"]):
+        tj = [timed[i] for i in range(j, len(timed), n)]
+        gj = [graph[i] for i in range(j, len(graph), n)]
+        L.append(f"| {p['M']} | {p['N']} | {p['K']} | {p['kernel_us']:.2f} | {sum(tj) / len(tj):.2f} | "
+                 f"{sum(gj) / len(gj):.2f} |")
     L += ["", f"HBM traffic per call (`qgemm_decode_sweep_traffic.json`): FETCH_SIZE and WRITE_SIZE from two `--pmc` "
               f"runs of the same bench (commands in that file), FETCH scaled by {traffic['fetch_scale']} (the copy "
               f"kernels' written/fetched ratio), WRITE by 1.0: {traffic['hbm_bytes_per_call'] / 1e6:.2f} MB per call "
