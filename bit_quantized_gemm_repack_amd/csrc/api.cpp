@@ -167,17 +167,14 @@ Exec choose_exec(const hq_plan* p, int64_t m) {
   c.mb = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
   c.nb = 1;
   // Rules from a sweep of the decode shapes on MI355X (kernel durations):
-  //   wide layers (>= 512 column blocks): 4 column blocks x 8 waves;
-  //   otherwise one column block per workgroup with K split over 8 waves,
-  //   16 for long K at <= 4 rows; two groups of loads in flight per wave.
+  //   wide layers (>= 512 column blocks): 4 column blocks per workgroup;
+  //   otherwise one column block per workgroup with K split over the waves;
+  //   8 waves for <= 4 rows, 4 for 5..16 rows (each wave's activation loads
+  //   grow with the rows); two groups of loads in flight per wave.
   c.stages = 2;
   if (c.mb == 1) {
-    if (N / 16 >= 512 && N % 64 == 0) {
-      c.nb = 4;
-      c.waves = 8;
-    } else {
-      c.waves = (G >= 64 && m <= 4) ? 16 : 8;
-    }
+    c.waves = m <= 4 ? 8 : 4;
+    if (N / 16 >= 512 && N % 64 == 0) c.nb = 4;
   } else {
     c.waves = 8;
   }
@@ -188,7 +185,6 @@ Exec choose_exec(const hq_plan* p, int64_t m) {
   int64_t auto_split = 1;
   if (c.mb == 1 && m > 4 && G >= 64 && N % 64 == 0 && N / 64 >= 32) {
     c.nb = 4;
-    c.waves = 8;
     auto_split = 4;
   }
   if (u.tile_m) c.mb = u.tile_m / 16;
