@@ -31,12 +31,13 @@ Modules
 -------
 formats  code-value tables (E2M1, E8M0, E4M3), nibble unpack, exact
          round-to-nearest-even to fp16 / bf16 / e4m3.
-gemm     dense W4A16, W4A8 (MXFP4 x FP8 and INT4 x INT8) oracles and the
-         per-output tolerance.
+gemm     dense W4A16, W4A8 (MXFP4 x FP8 and INT4 x INT8), W4A4 (MXFP4 x
+         MXFP4) oracles and the per-output tolerance.
 moe      the grouped MoE layer: align invariants, gate_up + SiLU*mul (+ fp8
          requant), down + top-k combine.
 quant    the per-token (per-row) activation quantiser that feeds W4A8:
-         s = max|x| / Q, codes = RNE(x / s) as fp8 e4m3 or int8.
+         s = max|x| / Q, codes = RNE(x * (1/s)) as fp8 e4m3 or int8; and the
+         MXFP4 block quantiser (OCP MX v1.0) of W4A4 activations.
 
 Parity status: every function is pinned by tests/test_oracle.py and
 tests/test_quant_oracle.py against

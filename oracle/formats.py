@@ -88,6 +88,7 @@ _FMT = {
     "f16": (11, -14),
     "bf16": (8, -126),
     "e4m3": (4, -6),
+    "e2m1": (2, 0),
     "f32": (24, -126),
 }
 
@@ -115,6 +116,22 @@ def ulp(x, fmt: str) -> np.ndarray:
     _, E = np.frexp(np.abs(np.asarray(x, dtype=np.float64)))
     e = np.maximum(E - 1, emin)
     return np.ldexp(1.0, e - (p - 1))
+
+
+def e2m1_encode(x) -> np.ndarray:
+    """Code of RNE_e2m1(x) for finite |x| <= 6 (callers clamp first); a value
+    that rounds to zero gives code 0 (no -0)."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(np.abs(x) > 6.0) or np.any(np.isnan(x)):
+        raise ValueError("e2m1_encode expects finite values with |x| <= 6")
+    r = rne(x, "e2m1")
+    pos = e2m1_value(np.arange(8))  # 0, 0.5, 1, 1.5, 2, 3, 4, 6: increasing
+    idx = np.searchsorted(pos, np.abs(r))
+    if not np.all(pos[np.minimum(idx, 7)] == np.abs(r)):
+        raise AssertionError("rounded value is not an e2m1 value")
+    code = idx.astype(np.int64)
+    code = np.where(np.signbit(r) & (r != 0), code | 0x8, code)
+    return code.astype(np.uint8)
 
 
 def e4m3_encode(x) -> np.ndarray:

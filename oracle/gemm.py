@@ -120,6 +120,19 @@ def gemm_mxfp4_fp8(a_codes, a_scale, w_codes, e8m0, out_fmt: str = "bf16"):
     return {"c64": c64, "c_out": rne(c64, out_fmt), "tau": tolerance(a_val, w), "w": w}
 
 
+def gemm_mxfp4_mxfp4(a_codes, a_e8m0, w_codes, w_e8m0, out_fmt: str = "bf16"):
+    """W4A4-MXFP4: C[m,n] = sum_k e2m1(qa[m,k]) 2^(Xa[m,k/32]-127) * e2m1(qw[n,k]) 2^(Xw[n,k/32]-127).
+
+    a_codes int32 [M, K/8] (canonical packing, like the weights), a_e8m0
+    uint8 [M, K/32].  Every product is a multiple of 2^(Xa+Xw-256) below
+    2^(Xa+Xw-248) in magnitude; with the scale ranges of these workloads the
+    float64 sum is exact in any order."""
+    a = mxfp4_weights(a_codes, a_e8m0)  # the activation block format is the weights' one
+    w = mxfp4_weights(w_codes, w_e8m0)
+    c64 = a @ w.T
+    return {"c64": c64, "c_out": rne(c64, out_fmt), "tau": tolerance(a, w), "w": w}
+
+
 def int_accumulators(a_codes, w_codes, group: int = 128) -> np.ndarray:
     """P[m,n,g] = sum_{k in g} a_q[m,k] * (q[n,k] - 8), exact int64."""
     a = int8_value(np.asarray(a_codes)).astype(np.int64)

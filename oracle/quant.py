@@ -32,7 +32,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import e4m3_encode, e4m3_value, int8_value, ulp
+from .formats import e2m1_encode, e2m1_value, e4m3_encode, e4m3_value, e8m0_value, int8_value, ulp
 
 Q_FP8 = 448.0
 Q_INT8 = 127.0
@@ -74,3 +74,48 @@ def step_bound(x, scales, out: str) -> np.ndarray:
     v = np.abs(np.asarray(x, dtype=np.float64)) / s
     half = 0.5 * ulp(np.minimum(v, Q_FP8), "e4m3") if out == "fp8" else np.full_like(v, 0.5)
     return (half + 2.0 ** -22 * v) * s
+
+
+# ----------------------------------------------------------------------------
+# MXFP4 activations (for W4A4: MXFP4 weights x MXFP4 activations)
+# ----------------------------------------------------------------------------
+#
+# Source: the OCP Microscaling (MX) v1.0 specification, section on converting
+# a vector of scalars to an MX block: the shared exponent of a block of 32 is
+# floor(log2(max |v|)) minus the element format's largest exponent (2 for
+# E2M1, whose largest value is 6 = 1.5 * 2^2), stored as the E8M0 code
+# X + 127; each element is v / 2^X rounded to E2M1 (ties to even), saturated
+# to +-6.  The pages list MXFP4 among the weight formats (cocoloop.cn, format
+# section) and W4A4 is the survey's next row; the rule for activations is the
+# specification's.  Readings: an all-zero block takes X = 0 (code 127) with
+# zero elements; X is clamped to [-127, 127]; a value that rounds to zero
+# gives code 0.  Division by 2^X is exact, so no float32 decision is involved.
+
+E2M1_EMAX = 2
+
+
+def mx_quantize_rows(x, block: int = 32):
+    """MXFP4 quantisation of the rows of x (float array [m, k], k % 32 == 0).
+
+    Returns (codes uint8 [m, k] holding 0..15, e8m0 uint8 [m, k/32])."""
+    x = np.asarray(x, dtype=np.float64)
+    m, k = x.shape
+    if k % block:
+        raise ValueError("k must be a multiple of the block size")
+    xb = x.reshape(m, k // block, block)
+    amax = np.max(np.abs(xb), axis=2)
+    safe = np.where(amax > 0, amax, 1.0)
+    _, E = np.frexp(safe)                          # amax = f * 2^E, f in [0.5, 1): floor(log2) = E - 1
+    X = np.where(amax > 0, (E - 1) - E2M1_EMAX, 0)
+    X = np.clip(X, -127, 127).astype(np.int64)
+    v = xb / np.ldexp(1.0, X)[:, :, None]          # exact: a power-of-two scaling
+    codes = e2m1_encode(np.clip(v, -6.0, 6.0)).reshape(m, k)
+    return codes, (X + 127).astype(np.uint8)
+
+
+def mx_values(codes, e8m0, block: int = 32) -> np.ndarray:
+    """e2m1(code) * 2^(X - 127) in float64 ([m, k] codes, [m, k/32] scales)."""
+    c = np.asarray(codes)
+    val = e2m1_value(c)
+    sc = e8m0_value(np.asarray(e8m0))
+    return val * np.repeat(sc, block, axis=1)

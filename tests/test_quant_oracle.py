@@ -134,3 +134,97 @@ def test_quant_planted_mistakes_are_caught():
     neg = np.array([[-896, 1, -2, 0.5, 0, 0, 0, 0]], np.float32)
     c, s = QZ.quantize_rows(neg, "fp8")
     assert s.tolist() == [2.0] and rule(neg, "fp8", absmax=False) != c.tolist()   # max without abs
+
+
+# ------------------------------------------------------------- MXFP4 (W4A4) --
+
+import datagen  # noqa: E402
+from oracle import gemm as OG  # noqa: E402
+
+
+def _mx_fixture():
+    with open(os.path.join(GOLD, "mx_w4a4.json")) as f:
+        g = json.load(f)
+    x = np.zeros((2, 32))
+    x[:, :8] = g["x_first8"]
+    a = np.zeros((2, 32), np.uint8)
+    a[:, :8] = g["a_codes_first8"]
+    w = np.zeros((2, 32), np.uint8)
+    w[:, :8] = g["w_codes_first8"]
+    return g, x, a, w
+
+
+def test_e2m1_encode_inverts_the_table():
+    vals = F.e2m1_value(np.arange(16))
+    codes = F.e2m1_encode(vals)
+    assert codes.tolist() == [c if c != 8 else 0 for c in range(16)]   # -0 encodes as +0
+
+
+def test_mx_quantize_hand_example():
+    g, x, a, _ = _mx_fixture()
+    codes, e8 = QZ.mx_quantize_rows(x)
+    assert codes.tolist() == a.tolist()
+    assert e8[:, 0].tolist() == g["a_e8m0"]
+
+
+def _brute_e2m1(v):
+    vals = F.e2m1_value(np.arange(8))
+    out = np.empty(v.shape, dtype=np.uint8)
+    for i, x in np.ndenumerate(v):
+        d = np.abs(vals - abs(x))
+        cand = np.flatnonzero(d == d.min())
+        c = int(cand[0]) if len(cand) == 1 else int(cand[cand % 2 == 0][0])
+        out[i] = c | 0x8 if (x < 0 and c != 0) else c
+    return out
+
+
+def test_mx_quantize_brute_force_and_invariants():
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((6, 256)) * 10.0 ** rng.integers(-3, 4, size=(6, 1))
+    x[2, 64:96] = 0.0                                        # an all-zero block
+    x = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    codes, e8 = QZ.mx_quantize_rows(x)
+    X = e8.astype(np.int64) - 127
+    v = x / np.repeat(np.ldexp(1.0, X), 32, axis=1)
+    assert np.array_equal(codes, _brute_e2m1(np.clip(v, -6, 6)))
+    mag = np.abs(F.e2m1_value(codes)).reshape(6, 8, 32).max(2)
+    nz = np.abs(x).reshape(6, 8, 32).max(2) > 0
+    assert np.all(np.isin(mag[nz], (4.0, 6.0))) and np.all(mag[~nz] == 0) and np.all(e8[~nz] == 127)
+    c2, e2 = QZ.mx_quantize_rows(-x)
+    assert np.array_equal(e2, e8) and np.array_equal(F.e2m1_value(c2), -F.e2m1_value(codes))
+    c3, e3 = QZ.mx_quantize_rows(x * 16.0)
+    assert np.array_equal(c3, codes) and np.array_equal(e3[nz], e8[nz] + 4)
+
+
+def test_mx_quantize_planted_mistakes():
+    g, x, a, _ = _mx_fixture()
+
+    def rule(emax=2, away=False):
+        amax = np.abs(x).max(1, keepdims=True)
+        X = np.floor(np.log2(amax)) - emax
+        v = np.clip(x / 2.0 ** X, -6, 6)
+        if away:  # ties away from zero
+            vals = F.e2m1_value(np.arange(8))
+            idx = np.array([[np.argmin(np.abs(vals - abs(t)) - 1e-9 * vals) for t in row] for row in v])
+            return np.where(v < 0, idx | 8, idx) * (idx != 0)
+        return F.e2m1_encode(v)
+
+    assert rule().tolist() == a.tolist()
+    assert rule(emax=3).tolist() != a.tolist()
+    assert rule(away=True).tolist() != a.tolist()
+
+
+def test_w4a4_gemm_hand_example_and_integer_special_case():
+    g, _, a, w = _mx_fixture()
+    r = OG.gemm_mxfp4_mxfp4(datagen.pack_u4(a), np.array(g["a_e8m0"])[:, None], datagen.pack_u4(w),
+                            np.array(g["w_e8m0"])[:, None])
+    assert r["c64"].tolist() == g["c"]
+    # with every scale 2^0, 4 C = (2 e2m1(qa)) . (2 e2m1(qw))^T, an integer matmul
+    rng = np.random.default_rng(22)
+    qa = rng.integers(0, 16, size=(5, 64), dtype=np.uint8)
+    qw = rng.integers(0, 16, size=(7, 64), dtype=np.uint8)
+    ia = (2 * F.e2m1_value(qa)).astype(np.int64)
+    iw = (2 * F.e2m1_value(qw)).astype(np.int64)
+    one = np.full((5, 2), 127)
+    r = OG.gemm_mxfp4_mxfp4(datagen.pack_u4(qa), one, datagen.pack_u4(qw), np.full((7, 2), 127))
+    assert np.array_equal(r["c64"] * 4, (ia @ iw.T).astype(np.float64))
