@@ -31,7 +31,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "hq.h")
 HQ_OK, HQ_ERR_INVALID_ARG, HQ_ERR_UNSUPPORTED, HQ_ERR_WORKSPACE, HQ_ERR_HIP, HQ_ERR_INTERNAL = range(6)
 F16, BF16, F32, FP8_E4M3, INT8, U4, FP4_E2M1, E8M0, I32 = range(9)
 ZP_NONE, ZP_FIXED, ZP_PER_GROUP_U4 = range(3)
-ASCALE_NONE, ASCALE_PER_TOKEN_F32 = range(2)
+ASCALE_NONE, ASCALE_PER_TOKEN_F32, ASCALE_MX_E8M0 = range(3)
 GEMM_DENSE, GEMM_GROUPED = range(2)
 EPI_NONE, EPI_SILU_MUL, EPI_SILU_MUL_QFP8, EPI_TOPK_COMBINE, EPI_I32_ACC = range(5)
 
@@ -97,6 +97,12 @@ def w4a8_mxfp4(out: str = "bf16") -> QuantDesc:
     return QuantDesc(FP4_E2M1, 4, 32, E8M0, ZP_NONE, 0, FP8_E4M3, ASCALE_PER_TOKEN_F32, _DT[out])
 
 
+def w4a4_mxfp4(out: str = "bf16") -> QuantDesc:
+    """MXFP4 weights x MXFP4 activations (E2M1 codes packed two per byte along
+    K, E8M0 block scales [m, K/32] passed as a_scale)."""
+    return QuantDesc(FP4_E2M1, 4, 32, E8M0, ZP_NONE, 0, FP4_E2M1, ASCALE_MX_E8M0, _DT[out])
+
+
 # ---------------------------------------------------------------- library --
 _lib = None
 
@@ -128,6 +134,7 @@ _SIGS = {
                                       ctypes.c_void_p]),
     "hq_quantize_per_token": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int] +
                               [ctypes.c_void_p] * 4),
+    "hq_quantize_mxfp4": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int] + [ctypes.c_void_p] * 4),
     "hq_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_size_t, ctypes.c_void_p]),
@@ -275,12 +282,16 @@ class Plan:
              out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
         """out[m, n] = A . W_deq^T (see include/hq.h, hq_gemm)."""
         _dev(a, "a"), _dev(w, "w"), _dev(meta, "meta")
+        act4 = self.quant.act == FP4_E2M1
         if a_scale is not None:
             _dev(a_scale, "a_scale")
-            if a_scale.dtype != torch.float32:
-                raise ValueError("a_scale must be float32")
+            if a_scale.dtype != (torch.uint8 if act4 else torch.float32):
+                raise ValueError("a_scale must be uint8 E8M0 [m, k/32] (MXFP4 activations) or float32 [m]")
         m = a.shape[0]
-        if a.dim() != 2 or a.shape[1] != self.k:
+        if act4:  # MXFP4 codes two per byte: [m, k/2] bytes (or [m, k/8] int32 words)
+            if a.dim() != 2 or a.shape[1] * a.element_size() != self.k // 2:
+                raise ValueError(f"a must hold [m, {self.k // 2}] bytes of packed MXFP4 codes")
+        elif a.dim() != 2 or a.shape[1] != self.k:
             raise ValueError(f"a must be [m, {self.k}]")
         if out is None:
             if self.epi == EPI_I32_ACC:
@@ -327,6 +338,27 @@ def quantize_per_token(x: torch.Tensor, out: str = "fp8", codes: Optional[torch.
                                        FP8_E4M3 if out == "fp8" else INT8, _ptr(x), _ptr(codes), _ptr(scales),
                                        _stream_ptr(x.device)))
     return codes, scales
+
+
+def quantize_mxfp4(x: torch.Tensor, codes: Optional[torch.Tensor] = None, e8m0: Optional[torch.Tensor] = None):
+    """MXFP4 block quantisation of fp16 / bf16 activations [m, k] (see
+    hq_quantize_mxfp4).  Returns (codes uint8 [m, k/2], e8m0 uint8 [m, k/32]),
+    the (a, a_scale) of a W4A4 GEMM."""
+    _dev(x, "x")
+    if x.dim() != 2 or x.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("x must be fp16 / bf16 [m, k]")
+    m, k = x.shape
+    if codes is None:
+        codes = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
+    if e8m0 is None:
+        e8m0 = torch.empty((m, k // 32), dtype=torch.uint8, device=x.device)
+    _dev(codes, "codes"), _dev(e8m0, "e8m0")
+    if codes.numel() * codes.element_size() != m * (k // 2) or e8m0.numel() != m * (k // 32) or \
+            e8m0.dtype != torch.uint8:
+        raise ValueError("codes must hold [m, k/2] bytes and e8m0 be uint8 [m, k/32]")
+    _check(lib().hq_quantize_mxfp4(m, k, BF16 if x.dtype == torch.bfloat16 else F16, _ptr(x), _ptr(codes),
+                                   _ptr(e8m0), _stream_ptr(x.device)))
+    return codes, e8m0
 
 
 # ------------------------------------------------------------------- MoE --

@@ -84,8 +84,14 @@ hq_status classify(const hq_quant_desc& q, int* fmt) {
     if (q.group_size != 32) return fail(HQ_ERR_UNSUPPORTED, "MXFP4 needs block size 32");
     if (q.scale != HQ_E8M0) return fail(HQ_ERR_UNSUPPORTED, "MXFP4 needs E8M0 block scales");
     if (q.zp != HQ_ZP_NONE) return fail(HQ_ERR_UNSUPPORTED, "MXFP4 has no zero point");
+    if (q.act == HQ_FP4_E2M1) {
+      if (q.act_scale != HQ_ASCALE_MX_E8M0)
+        return fail(HQ_ERR_UNSUPPORTED, "MXFP4 activations need E8M0 block scales (HQ_ASCALE_MX_E8M0)");
+      *fmt = hq::FMT_F44;
+      return HQ_OK;
+    }
     if (q.act != HQ_FP8_E4M3 || q.act_scale != HQ_ASCALE_PER_TOKEN_F32)
-      return fail(HQ_ERR_UNSUPPORTED, "MXFP4 weights are implemented with fp8 e4m3 per-token activations");
+      return fail(HQ_ERR_UNSUPPORTED, "MXFP4 weights take fp8 e4m3 per-token or MXFP4 activations");
     *fmt = hq::FMT_F4;
     return HQ_OK;
   }
@@ -99,6 +105,7 @@ const char* fmt_name(int fmt) {
     case hq::FMT_I8: return "w4a8-int8";
     case hq::FMT_Q8: return "w4a8-fp8";
     case hq::FMT_F4: return "w4a8-mxfp4";
+    case hq::FMT_F44: return "w4a4-mxfp4";
   }
   return "?";
 }
@@ -139,7 +146,7 @@ Exec choose_exec(const hq_plan* p, int64_t m) {
     e.tl.nbw = (N % 256 == 0 && m >= 512 && p->fmt == FMT_W16F16) ? 4 : 2;
     int stages = 3;
     if (!act16 && m >= 512) {
-      if (p->fmt == FMT_F4) {
+      if (mx_weights(p->fmt)) {
         stages = 4;
       } else {
         e.tl.bm = 64;
@@ -226,8 +233,10 @@ hq_status check_exec(const hq_plan* p, const hq::Exec& e) {
       // load pipeline: stages x (tile_m rows x one group of A) in LDS, and the
       // loads of stages - 2 groups in flight within the 6-bit wait counter
       const bool act16 = p->fmt == hq::FMT_W16F16 || p->fmt == hq::FMT_W16BF16;
-      const int rowb = act16 ? 256 : 128;
-      const int lps = e.tl.bm * rowb / 1024 / 4 + e.tl.nbw * (p->fmt == hq::FMT_F4 ? 2 : 3);
+      const bool act4 = p->fmt == hq::FMT_F44;
+      const int rowb = act16 ? 256 : (act4 ? 64 : 128);
+      const int lps = e.tl.bm * rowb / 1024 / 4 + e.tl.nbw * (hq::mx_weights(p->fmt) ? 2 : 3) +
+                      (act4 ? e.tl.bm / 16 : 0);
       if (e.tl.stages < 2 || e.tl.stages > 5) return fail(HQ_ERR_INVALID_ARG, "tiled kernel: stages must be 2..5");
       if (e.tl.stages * e.tl.bm * rowb > 160 * 1024 || lps * (e.tl.stages - 2) >= 64)
         return fail(HQ_ERR_INVALID_ARG, "tiled kernel: too many stages for this tile");
@@ -342,7 +351,7 @@ hq_status hq_plan_create(const hq_layer_desc* layer, const hq_compute* compute, 
     p->fmt = fmt;
     const int64_t N = layer->n, K = layer->k, G = K / 128;
     p->w_bytes_per_expert = (size_t)(N * K / 2);
-    if (fmt == hq::FMT_F4) {
+    if (hq::mx_weights(fmt)) {
       p->scale_region_bytes = 0;
       p->meta_bytes_per_expert = (size_t)(N * K / 32);
     } else {
@@ -405,7 +414,7 @@ hq_status hq_repacked_bytes(const hq_plan* p, size_t* w_bytes, size_t* meta_byte
 static hq_status check_repack_args(const hq_plan* p, const void* codes, const void* scales, const void* zx,
                                    const void* w_out, const void* meta_out) {
   if (!p || !codes || !w_out || !meta_out) return fail(HQ_ERR_INVALID_ARG, "null argument");
-  if (p->fmt == hq::FMT_F4) {
+  if (hq::mx_weights(p->fmt)) {
     if (!zx) return fail(HQ_ERR_INVALID_ARG, "MXFP4 repack needs the E8M0 scales");
   } else {
     if (!scales) return fail(HQ_ERR_INVALID_ARG, "INT4 repack needs the group scales");
@@ -442,7 +451,7 @@ hq_status hq_repack_host(const hq_plan* p, const void* codes, const void* scales
     for (int64_t e = 0; e < E; ++e)
       for (int64_t i = 0; i < wpe; ++i) wo[e * wpe + i] = hq::repack_word(cw + e * wpe, K, p->fmt, i);
     uint8_t* meta = static_cast<uint8_t*>(meta_out);
-    if (p->fmt == hq::FMT_F4) {
+    if (hq::mx_weights(p->fmt)) {
       const int64_t per = N * K / 32;
       const uint8_t* src = static_cast<const uint8_t*>(zx);
       for (int64_t e = 0; e < E; ++e)
@@ -467,7 +476,7 @@ hq_status hq_repack_host(const hq_plan* p, const void* codes, const void* scales
   }
 }
 
-hq_status hq_gemm(const hq_plan* p, int64_t m, const void* a, const float* a_scale, const void* w,
+hq_status hq_gemm(const hq_plan* p, int64_t m, const void* a, const void* a_scale, const void* w,
                   const void* meta, void* out, void* ws, size_t ws_bytes, void* stream) {
   const hq::TimingEvents ev = hq::take_timing();  // consumed by this call whatever happens
   try {
@@ -479,9 +488,14 @@ hq_status hq_gemm(const hq_plan* p, int64_t m, const void* a, const float* a_sca
     if (!a || !w || !meta || !out) return fail(HQ_ERR_INVALID_ARG, "null device pointer");
     if (!aligned16(a) || !aligned16(w) || !aligned16(meta) || !aligned16(out))
       return fail(HQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+    const bool act4 = p->fmt == hq::FMT_F44;
     const bool act8 = p->fmt == hq::FMT_I8 || p->fmt == hq::FMT_Q8 || p->fmt == hq::FMT_F4;
     if (act8 && !a_scale) return fail(HQ_ERR_INVALID_ARG, "8-bit activations need a_scale");
-    if (!act8 && a_scale) return fail(HQ_ERR_INVALID_ARG, "16-bit activations take no a_scale");
+    if (act4 && !a_scale) return fail(HQ_ERR_INVALID_ARG, "MXFP4 activations need their E8M0 scales in a_scale");
+    if (act4 && !aligned16(a_scale)) return fail(HQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+    if (!act8 && !act4 && a_scale) return fail(HQ_ERR_INVALID_ARG, "16-bit activations take no a_scale");
+    const float* a_scale_f = act8 ? static_cast<const float*>(a_scale) : nullptr;
+    const uint8_t* a_e8m0 = act4 ? static_cast<const uint8_t*>(a_scale) : nullptr;
     hq::Exec e = hq::choose_exec(p, m);
     hq_status s = check_exec(p, e);
     if (s != HQ_OK) return s;
@@ -499,16 +513,17 @@ hq_status hq_gemm(const hq_plan* p, int64_t m, const void* a, const float* a_sca
                                 : nullptr;
     {
       // the kernels address A and W through 32-bit buffer ranges
-      const int64_t act_bytes = (p->fmt == hq::FMT_W16F16 || p->fmt == hq::FMT_W16BF16) ? 2 : 1;
-      if (m * K * act_bytes >= (int64_t(1) << 31) || N * K / 2 >= (int64_t(1) << 31))
+      const int64_t act_bytes2 = (p->fmt == hq::FMT_W16F16 || p->fmt == hq::FMT_W16BF16) ? 4 : (act4 ? 1 : 2);
+      if (m * K * act_bytes2 / 2 >= (int64_t(1) << 31) || N * K / 2 >= (int64_t(1) << 31))
         return fail(HQ_ERR_UNSUPPORTED, "activations and weights must each stay below 2 GiB");
     }
     if (e.kernel == hq::KER_TILED) {
       hq::TiledArgs t{};
       t.a = a;
-      t.a_scale = a_scale;
+      t.a_scale = a_scale_f;
+      t.a_e8m0 = a_e8m0;
       t.w = w;
-      if (p->fmt == hq::FMT_F4) t.e8m0 = static_cast<const uint8_t*>(meta);
+      if (hq::mx_weights(p->fmt)) t.e8m0 = static_cast<const uint8_t*>(meta);
       else t.scales = meta;
       t.zeros = zeros;
       t.out = out;
@@ -535,9 +550,10 @@ hq_status hq_gemm(const hq_plan* p, int64_t m, const void* a, const float* a_sca
     }
     hq::SkinnyArgs args{};
     args.a = a;
-    args.a_scale = a_scale;
+    args.a_scale = a_scale_f;
+    args.a_e8m0 = a_e8m0;
     args.w = w;
-    if (p->fmt == hq::FMT_F4) {
+    if (hq::mx_weights(p->fmt)) {
       args.e8m0 = static_cast<const uint8_t*>(meta);
     } else {
       args.scales = meta;
@@ -878,6 +894,24 @@ hq_status hq_quantize_per_token(int64_t m, int64_t k, hq_dtype in, hq_dtype out,
     return fail(HQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
   hq::arm_timing(ev);
   const int err = hq::launch_quantize_rows(m, k, in == HQ_BF16, out == HQ_FP8_E4M3, x, codes, scales, stream);
+  hq::arm_timing({nullptr, nullptr});
+  if (err != hipSuccess) return fail(HQ_ERR_HIP, "quantize launch: %s", hipGetErrorString((hipError_t)err));
+  return ok();
+}
+
+hq_status hq_quantize_mxfp4(int64_t m, int64_t k, hq_dtype in, const void* x, void* codes, uint8_t* e8m0,
+                            void* stream) {
+  const hq::TimingEvents ev = hq::take_timing();  // consumed by this call whatever happens
+  if (in != HQ_F16 && in != HQ_BF16) return fail(HQ_ERR_UNSUPPORTED, "input must be fp16 or bf16");
+  if (m < 0 || m > (int64_t(1) << 24)) return fail(HQ_ERR_INVALID_ARG, "m out of range [0, 2^24]");
+  if (k < 32 || k % 32 || k > (int64_t(1) << 24)) return fail(HQ_ERR_INVALID_ARG, "k must be a multiple of 32 in [32, 2^24]");
+  if (m * k > (int64_t(1) << 36)) return fail(HQ_ERR_UNSUPPORTED, "m * k above 2^36");
+  if (m == 0) return ok();
+  if (!x || !codes || !e8m0) return fail(HQ_ERR_INVALID_ARG, "null device pointer");
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(e8m0))
+    return fail(HQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  hq::arm_timing(ev);
+  const int err = hq::launch_quantize_mx(m, k, in == HQ_BF16, x, codes, e8m0, stream);
   hq::arm_timing({nullptr, nullptr});
   if (err != hipSuccess) return fail(HQ_ERR_HIP, "quantize launch: %s", hipGetErrorString((hipError_t)err));
   return ok();

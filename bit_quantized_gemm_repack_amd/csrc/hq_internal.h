@@ -62,13 +62,17 @@ enum Fmt : int {
   FMT_W16BF16 = 1, // INT4 weight, bf16 activation, bf16 MFMA
   FMT_I8 = 2,      // INT4 weight, int8 activation, int8 MFMA (exact int32)
   FMT_Q8 = 3,      // INT4 weight, fp8 activation, scaled fp8 MFMA
-  FMT_F4 = 4       // MXFP4 weight, fp8 activation, scaled fp8 x fp4 MFMA
+  FMT_F4 = 4,      // MXFP4 weight, fp8 activation, scaled fp8 x fp4 MFMA
+  FMT_F44 = 5      // MXFP4 weight, MXFP4 activation, scaled fp4 x fp4 MFMA
 };
+
+// MXFP4 weights (E2M1 codes in natural order + E8M0 block scales).
+HQ_HD constexpr inline bool mx_weights(int fmt) { return fmt == FMT_F4 || fmt == FMT_F44; }
 
 enum NibOrder : int { NIB_W16 = 0, NIB_B8 = 1, NIB_NAT = 2 };
 
 HQ_HD inline int nib_order_of(int fmt) {
-  return (fmt == FMT_W16F16 || fmt == FMT_W16BF16) ? NIB_W16 : (fmt == FMT_F4 ? NIB_NAT : NIB_B8);
+  return (fmt == FMT_W16F16 || fmt == FMT_W16BF16) ? NIB_W16 : (mx_weights(fmt) ? NIB_NAT : NIB_B8);
 }
 HQ_HD inline uint32_t nib_xor_of(int fmt) { return fmt == FMT_I8 ? 8u : 0u; }
 
@@ -192,6 +196,7 @@ Exec choose_exec(const hq_plan* p, int64_t m);
 struct SkinnyArgs {
   const void* a;
   const float* a_scale;
+  const uint8_t* a_e8m0;  // MXFP4 activations: E8M0 [M][K/32]
   const void* w;
   const void* scales;
   const uint32_t* zeros;  // nibble-packed, or null
@@ -246,6 +251,7 @@ int launch_moe_combine(const float* rows, int topk, int64_t t, int64_t n, void* 
 struct TiledArgs {
   const void* a;
   const float* a_scale;
+  const uint8_t* a_e8m0;  // MXFP4 activations: E8M0 [M][K/32]
   const void* w;
   const void* scales;
   const uint32_t* zeros;
@@ -283,6 +289,9 @@ int launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int workgr
 // and scales [m]; k a multiple of 8.
 int launch_quantize_rows(int64_t m, int64_t k, int in_bf16, int out_fp8, const void* x, void* codes, float* scales,
                          void* stream);
+// MXFP4 block quantiser: x [m, k] fp16/bf16 -> codes [m, k/2] bytes and E8M0
+// [m, k/32]; k a multiple of 32.
+int launch_quantize_mx(int64_t m, int64_t k, int in_bf16, const void* x, void* codes, uint8_t* e8m0, void* stream);
 
 // Pending timing events for the next launch on this thread (see
 // hq_time_next_launch); take_timing() returns and clears them.

@@ -44,9 +44,11 @@ namespace hq {
 template <int FMT>
 struct FmtInfo {
   static constexpr bool kAct16 = (FMT == FMT_W16F16 || FMT == FMT_W16BF16);
-  static constexpr int kAVec = kAct16 ? 4 : 2;  // 16-byte loads per lane per group
+  static constexpr bool kAct4 = (FMT == FMT_F44);  // MXFP4 activations
+  static constexpr int kAVec = kAct16 ? 4 : (kAct4 ? 1 : 2);  // 16-byte loads per lane per group
+  static constexpr int kARowB = kAct16 ? 256 : (kAct4 ? 64 : 128);  // A bytes per row per group
   static constexpr bool kRowSum = (FMT == FMT_W16F16 || FMT == FMT_W16BF16 || FMT == FMT_Q8);
-  static constexpr bool kActScale = !kAct16;
+  static constexpr bool kActScale = !kAct16 && !kAct4;  // one fp32 scale per row
 };
 
 template <int FMT, int MB, int NB>
@@ -55,6 +57,7 @@ struct Stage {
   u4_t b[NB];
   uint32_t sraw[NB];  // scale bits, or the E8M0 byte
   uint32_t zraw[NB];  // zero-point word (8 nibbles), unused with a fixed zero
+  uint32_t asc[MB];   // MXFP4 activations: the row's four E8M0 block scales of the group
 };
 
 template <int FMT>
@@ -105,7 +108,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
       return;
     }
     wbytes += ex * p.w_expert;
-    if constexpr (FMT == FMT_F4) {
+    if constexpr (mx_weights(FMT)) {
       e8 += ex * p.e8_expert;
     } else {
       scales16 += ex * p.s_expert;
@@ -134,7 +137,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   auto rsrc = [](const void* base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
   };
-  const int a_rowb = K * (FI::kAct16 ? 2 : 1);
+  const int a_rowb = FI::kAct16 ? 2 * K : (FI::kAct4 ? K / 2 : K);
   const int a_rows = (GRP == GRP_GATHER) ? p.n_slots / p.topk : p.M;
   const auto ra = rsrc(p.a, (int64_t)a_rows * a_rowb);
   const int64_t nfrag = (int64_t)(p.N / 16) * G;
@@ -143,10 +146,12 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   [[maybe_unused]] const auto rz = rsrc(zeros32 ? static_cast<const void*>(zeros32) : static_cast<const void*>(scales16),
                                         zeros32 ? nfrag * 8 : nfrag * 32);
   [[maybe_unused]] const auto re = rsrc(e8, nfrag * 64);
+  [[maybe_unused]] const auto rae = rsrc(p.a_e8m0, (int64_t)a_rows * (K / 32));
   // at or above 2^31: past every range (ranges stay below 2 GiB), and adding
   // the group offset cannot wrap
   constexpr int kOutOfRange = INT32_MIN;
   int aoff[MB];
+  [[maybe_unused]] int aeoff[MB];  // E8M0 row offset of MXFP4 activations
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int m = m0 + 16 * mb + c;
@@ -159,13 +164,14 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
     }
     // 16-bit step t: bytes 256 g + 64 t + 16 kq; 8-bit piece h: 128 g + 64 h + 16 kq
     aoff[mb] = row >= 0 ? row * a_rowb + 16 * kq : kOutOfRange;
+    aeoff[mb] = row >= 0 ? row * (K / 32) : kOutOfRange;
   }
   int woff[NB], soff[NB], zoff[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int f0 = nblk(nb) * G;
     woff[nb] = (f0 * 64 + lane) * 16;
-    soff[nb] = (FMT == FMT_F4) ? f0 * 64 + (lane & ~3) : f0 * 32 + (c >> 1) * 4;
+    soff[nb] = mx_weights(FMT) ? f0 * 64 + (lane & ~3) : f0 * 32 + (c >> 1) * 4;
     zoff[nb] = f0 * 8 + (c >> 3) * 4;
   }
 
@@ -182,6 +188,11 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           st.a[mb][t] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[mb] + 64 * t, g * 256, 0));
+      } else if constexpr (FI::kAct4) {
+        // block kq of the group: k = 32 kq + [0, 32), 16 bytes; its scale byte
+        // is byte kq of the row's group word
+        st.a[mb][0] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[mb], g * 64, 0));
+        st.asc[mb] = __builtin_amdgcn_raw_buffer_load_b32(rae, aeoff[mb], g * 4, 0);
       } else {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -192,7 +203,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
     // that no wait is needed until the stage's math.
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      if constexpr (FMT == FMT_F4) {
+      if constexpr (mx_weights(FMT)) {
         st.sraw[nb] = __builtin_amdgcn_raw_buffer_load_b32(re, soff[nb], g * 64, 0);
       } else {
         st.sraw[nb] = __builtin_amdgcn_raw_buffer_load_b32(rsc, soff[nb], g * 32, 0);
@@ -202,7 +213,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   };
   // the lane's 16-bit scale / E8M0 byte out of its metadata dword
   auto sbits = [&](const Stage<FMT, MB, NB>& st, int nb) -> uint32_t {
-    return (FMT == FMT_F4) ? (st.sraw[nb] >> (8 * (lane & 3))) & 0xFFu : (st.sraw[nb] >> (16 * (c & 1))) & 0xFFFFu;
+    return mx_weights(FMT) ? (st.sraw[nb] >> (8 * (lane & 3))) & 0xFFu : (st.sraw[nb] >> (16 * (c & 1))) & 0xFFFFu;
   };
   auto zero_of = [&](const Stage<FMT, MB, NB>& st, int nb) -> uint32_t {
     return p.zp_fixed < 0 ? (st.zraw[nb] >> (4 * (c & 7))) & 0xFu : (uint32_t)p.zp_fixed;
@@ -293,6 +304,17 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
               cat8(st.a[mb][0], st.a[mb][1]), bop, f4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 136);
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[mb][nb][r] += s * (P[r] - z * rs[mb][r]);
+        }
+      } else if constexpr (FMT == FMT_F44) {
+        // fp4 x fp4: both operands E2M1 (format 4), each with its block scales
+        const i8_t bop = i8_t{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+        const int sb = (int)sbits(st, nb);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const u4_t x = st.a[mb][0];
+          const i8_t av = i8_t{(int)x[0], (int)x[1], (int)x[2], (int)x[3], 0, 0, 0, 0};
+          const int sa = (int)((st.asc[mb] >> (8 * kq)) & 0xFFu);
+          acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bop, acc[mb][nb], 4, 4, 0, sa, 0, sb);
         }
       } else {  // FMT_F4
         const i8_t bop = i8_t{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
@@ -500,6 +522,7 @@ int launch_skinny(int fmt, const SkinnyCfg& cfg, const SkinnyArgs& a, void* stre
     case FMT_I8: return (int)launch_mb<FMT_I8>(cfg, a, grid, block, lds, s);
     case FMT_Q8: return (int)launch_mb<FMT_Q8>(cfg, a, grid, block, lds, s);
     case FMT_F4: return (int)launch_mb<FMT_F4>(cfg, a, grid, block, lds, s);
+    case FMT_F44: return (int)launch_mb<FMT_F44>(cfg, a, grid, block, lds, s);
   }
   return (int)hipErrorInvalidValue;
 }

@@ -55,7 +55,8 @@ struct TCfg {
   static constexpr int BN = WAVES * NBW * 16;
   static constexpr int MB = BM / 16;
   static constexpr bool ACT16 = (FMT == FMT_W16F16 || FMT == FMT_W16BF16);
-  static constexpr int ROWB = ACT16 ? 256 : 128;  // A bytes per row per group
+  static constexpr bool ACT4 = (FMT == FMT_F44);  // MXFP4 activations
+  static constexpr int ROWB = ACT16 ? 256 : (ACT4 ? 64 : 128);  // A bytes per row per group
   static constexpr int CHUNKS = ROWB / 16;        // 16-byte chunks per row
   static constexpr int RPS = 1024 / ROWB;         // rows per 1 KiB load segment
   static constexpr int NSEG = BM * ROWB / 1024;   // global->LDS loads per step (workgroup)
@@ -63,17 +64,21 @@ struct TCfg {
   static constexpr int STAGES = ST;  // groups in the pipeline (ST - 1 ahead of the math)
   static constexpr int STAGE_BYTES = BM * ROWB;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-  static constexpr int META = (FMT == FMT_F4) ? 1 : 2;  // metadata loads per fragment
-  static constexpr int LPS = SEGW + NBW + META * NBW;   // vector-memory loads per step per wave
+  static constexpr int META = mx_weights(FMT) ? 1 : 2;  // metadata loads per fragment
+  // vector-memory loads per step per wave (MXFP4 activations: plus one E8M0
+  // word per m-block)
+  static constexpr int LPS = SEGW + NBW + META * NBW + (ACT4 ? MB : 0);
   static_assert(SEGW * WAVES == NSEG, "tile rows must fill the loaders");
   static_assert(ST >= 2 && LPS * (ST - 2) < 64, "loads in flight exceed the counter");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds the workgroup limit");
 };
 
-// Physical 16-byte chunk of logical chunk c in row r.
-template <bool ACT16>
+// Physical 16-byte chunk of logical chunk c in row r (CH chunks per row):
+// the 16 rows an MFMA operand reads at one logical chunk land on distinct
+// banks.
+template <int CH>
 __device__ inline int swz(int r, int c) {
-  return ACT16 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+  return CH == 16 ? (c ^ (r & 15)) : (CH == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3)));
 }
 
 // s_waitcnt: at most N (< 64) vector-memory loads of this wave still in
@@ -148,7 +153,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
       return;
     }
     wbytes += ex * p.w_expert;
-    if constexpr (FMT == FMT_F4) {
+    if constexpr (mx_weights(FMT)) {
       e8 += ex * p.e8_expert;
     } else {
       scales16 += ex * p.s_expert;
@@ -176,7 +181,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
   auto rsrc = [](const void* base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
   };
-  const int a_rowb = K * (C::ACT16 ? 2 : 1);
+  const int a_rowb = C::ACT16 ? 2 * K : (C::ACT4 ? K / 2 : K);
   const int a_rows = (GRP == GRP_GATHER) ? p.n_slots / p.topk : p.M;
   const auto ra = rsrc(p.a, (int64_t)a_rows * a_rowb);
   const int64_t nfrag = (int64_t)(p.N / 16) * G;  // fragments of this weight (one expert)
@@ -185,6 +190,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
   [[maybe_unused]] const auto rz = rsrc(zeros32 ? static_cast<const void*>(zeros32) : static_cast<const void*>(scales16),
                                         zeros32 ? nfrag * 8 : nfrag * 32);
   [[maybe_unused]] const auto re = rsrc(e8, nfrag * 64);
+  [[maybe_unused]] const auto rae = rsrc(p.a_e8m0, (int64_t)a_rows * (K / 32));
 
   // Activation segment s (1 KiB of the slot) holds rows seg*RPS .. +RPS-1;
   // lane l writes physical chunk l % CHUNKS of row seg*RPS + l / CHUNKS, so it
@@ -195,7 +201,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
   for (int s = 0; s < C::SEGW; ++s) {
     const int seg = wave + C::WAVES * s;
     const int r = seg * C::RPS + lane / C::CHUNKS;
-    const int lchunk = swz<C::ACT16>(r, lane % C::CHUNKS);
+    const int lchunk = swz<C::CHUNKS>(r, lane % C::CHUNKS);
     int row;
     if constexpr (GRP == GRP_DENSE) {
       row = min(m0 + r, p.M - 1);
@@ -207,12 +213,17 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
     }
     aoff[s] = row * a_rowb + lchunk * 16;
   }
+  // MXFP4 activations: E8M0 word offsets of the rows 16 mb + c16 this lane's
+  // MFMA operands hold (dense only)
+  [[maybe_unused]] int aeoff[C::MB];
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb) aeoff[mb] = min(m0 + 16 * mb + c16, p.M - 1) * (K / 32);
   int woff[NBW], soff[NBW], zoff[NBW];
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
     const int f0 = nblk(j) * G;  // first fragment of this column block
     woff[j] = (f0 * 64 + lane) * 16;
-    soff[j] = (FMT == FMT_F4) ? f0 * 64 + (lane & ~3) : f0 * 32 + (c16 >> 1) * 4;
+    soff[j] = mx_weights(FMT) ? f0 * 64 + (lane & ~3) : f0 * 32 + (c16 >> 1) * 4;
     zoff[j] = f0 * 8 + (c16 >> 3) * 4;
   }
 
@@ -220,6 +231,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
   u4_t braw[C::STAGES][NBW];
   uint32_t sraw[C::STAGES][NBW];
   [[maybe_unused]] uint32_t zraw[C::STAGES][NBW];
+  [[maybe_unused]] uint32_t asc[C::STAGES][C::MB];  // MXFP4 activations: row scale words
 
   auto issue = [&](auto slot_c, int g) {
     constexpr int slot = decltype(slot_c)::value;
@@ -238,12 +250,16 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
     // ring is carried round the loop, which forces a wait for every load there.
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
-      if constexpr (FMT == FMT_F4) {
+      if constexpr (mx_weights(FMT)) {
         sraw[slot][j] = __builtin_amdgcn_raw_buffer_load_b32(re, soff[j], gg * 64, 0);
       } else {
         sraw[slot][j] = __builtin_amdgcn_raw_buffer_load_b32(rs, soff[j], gg * 32, 0);
         zraw[slot][j] = __builtin_amdgcn_raw_buffer_load_b32(rz, zoff[j], gg * 8, 0);
       }
+    }
+    if constexpr (C::ACT4) {
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) asc[slot][mb] = __builtin_amdgcn_raw_buffer_load_b32(rae, aeoff[mb], gg * 4, 0);
     }
   };
   auto zero_of = [&](uint32_t zw) -> uint32_t {
@@ -266,13 +282,19 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
     const int r = 16 * mb + c16;
     const uint8_t* base = lds + slot * C::STAGE_BYTES + r * C::ROWB;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const u4_t*>(base + swz<true>(r, 4 * t + kq) * 16);
+    for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const u4_t*>(base + swz<16>(r, 4 * t + kq) * 16);
   };
   auto read_a8 = [&](int slot, int mb, u4_t (&a)[2]) {
     const int r = 16 * mb + c16;
     const uint8_t* base = lds + slot * C::STAGE_BYTES + r * C::ROWB;
-    a[0] = *reinterpret_cast<const u4_t*>(base + swz<false>(r, kq) * 16);
-    a[1] = *reinterpret_cast<const u4_t*>(base + swz<false>(r, 4 + kq) * 16);
+    a[0] = *reinterpret_cast<const u4_t*>(base + swz<8>(r, kq) * 16);
+    a[1] = *reinterpret_cast<const u4_t*>(base + swz<8>(r, 4 + kq) * 16);
+  };
+  // 4-bit: block kq takes k = 32 kq + [0, 32) (chunk kq)
+  [[maybe_unused]] auto read_a4 = [&](int slot, int mb) -> u4_t {
+    const int r = 16 * mb + c16;
+    const uint8_t* base = lds + slot * C::STAGE_BYTES + r * C::ROWB;
+    return *reinterpret_cast<const u4_t*>(base + swz<4>(r, kq) * 16);
   };
 
   auto compute = [&](auto slot_c) {
@@ -303,7 +325,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
       auto read_a16t = [&](int mb, int t) -> u4_t {
         const int r = 16 * mb + c16;
         const uint8_t* base = lds + slot * C::STAGE_BYTES + r * C::ROWB;
-        return *reinterpret_cast<const u4_t*>(base + swz<true>(r, 4 * t + kq) * 16);
+        return *reinterpret_cast<const u4_t*>(base + swz<16>(r, 4 * t + kq) * 16);
       };
       u4_t b[2][NBW];
       u4_t a[2][C::MB];
@@ -411,6 +433,21 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
           for (int r = 0; r < 4; ++r) acc[mb][j][r] += sj[j] * (P[r] - zj[j] * rs[r]);
         }
       }
+    } else if constexpr (FMT == FMT_F44) {
+      // fp4 x fp4: both operands E2M1 (format 4), each with its block scales
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) {
+        const u4_t x = read_a4(slot, mb);
+        const i8_t av = i8_t{(int)x[0], (int)x[1], (int)x[2], (int)x[3], 0, 0, 0, 0};
+        const int sa = (int)((asc[slot][mb] >> (8 * kq)) & 0xFFu);
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+          const u4_t w = braw[slot][j];
+          const i8_t bv = i8_t{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+          acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mb][j], 4, 4, 0, sa, 0,
+                                                                        e8m0_of(sraw[slot][j]));
+        }
+      }
     } else {  // FMT_F4
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) {
@@ -441,7 +478,11 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
     for (int j = 0; j < NBW; ++j) {
       pin(braw[cur][j]);
       pin(sraw[cur][j]);
-      if constexpr (FMT != FMT_F4) pin(zraw[cur][j]);
+      if constexpr (!mx_weights(FMT)) pin(zraw[cur][j]);
+    }
+    if constexpr (C::ACT4) {
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) pin(asc[cur][mb]);
     }
     issue(Ahead{}, gclamp(g + ST - 1));  // into the slot every wave finished reading at step g-1
     if (g < Gl) compute(slot_c);
@@ -459,7 +500,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
   __builtin_amdgcn_s_waitcnt(0);  // no load into LDS may outlive the workgroup
 
   // ---- epilogue ---------------------------------------------------------------
-  constexpr bool ACT_SCALE = !C::ACT16;
+  constexpr bool ACT_SCALE = !C::ACT16 && !C::ACT4;
 #pragma unroll
   for (int mb = 0; mb < C::MB; ++mb) {
 #pragma unroll
@@ -570,6 +611,7 @@ int launch_tiled(int fmt, const TiledCfgRt& cfg, const TiledArgs& a, void* strea
     case FMT_I8: return (int)launch_tiled_f<FMT_I8, GRP_DENSE>(cfg, a, grid, s);
     case FMT_Q8: return (int)launch_tiled_f<FMT_Q8, GRP_DENSE>(cfg, a, grid, s);
     case FMT_F4: return (int)launch_tiled_f<FMT_F4, GRP_DENSE>(cfg, a, grid, s);
+    case FMT_F44: return (int)launch_tiled_f<FMT_F44, GRP_DENSE>(cfg, a, grid, s);
   }
   return (int)hipErrorInvalidValue;
 }

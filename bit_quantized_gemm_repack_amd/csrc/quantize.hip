@@ -123,7 +123,71 @@ __global__ void __launch_bounds__(1024) quantize_rows_kernel(const u4_t* __restr
   if (tid == 0) scales[row] = s;
 }
 
+// ---------------------------------------------------------------------------
+// MXFP4 block quantiser (activations of W4A4), after the OCP MX v1.0
+// conversion of a 32-element block: shared exponent X = floor(log2 max|v|) - 2
+// (2 = the largest E2M1 exponent), clamped to [-127, 127], X = 0 for an
+// all-zero block; elements RNE_E2M1(v / 2^X) saturated to +-6.  The scaling by
+// 2^-X is exact (ldexp), so every decision is an exact comparison.
+
+// Round-to-nearest-even fp32 -> E2M1 code, saturating at 6; -0 gives code 0.
+// Below 1 the spacing is 0.5 (code = rint(2|x|)); above, the 23-bit mantissa
+// is rounded to 1 bit (a carry moves into the exponent field).
+__device__ inline uint32_t e2m1_code_rne(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 28) & 0x8u;
+  const float a = fminf(fabsf(x), 6.f);
+  uint32_t code;
+  if (a < 1.f) {
+    code = (uint32_t)__builtin_rintf(a * 2.f);
+  } else {
+    const uint32_t bits = __float_as_uint(a);
+    const uint32_t e = (bits >> 23) - 127u + 1u;  // exponent field, bias 1
+    const uint32_t mant = bits & 0x7FFFFFu;
+    const uint32_t r = (mant + 0x1FFFFFu + ((mant >> 22) & 1u)) >> 22;  // 0..2
+    code = (e << 1) + r;
+  }
+  return code == 0 ? 0u : (sign | code);
+}
+
+// One thread per 32-element block: 64 input bytes in, 16 code bytes and one
+// E8M0 byte out (consecutive threads, consecutive blocks of a row).
+template <bool BF16>
+__global__ void __launch_bounds__(256) quantize_mx_kernel(const u4_t* __restrict__ x, int64_t nblk,
+                                                          u4_t* __restrict__ codes, uint8_t* __restrict__ e8m0) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nblk) return;
+  u4_t v[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) v[c] = __builtin_nontemporal_load(x + 4 * i + c);
+  float amax = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) amax = fmaxf(amax, chunk_absmax<BF16>(v[c]));
+  // floor(log2 amax) from the exponent field (a subnormal amax clamps to -127)
+  const int X = amax > 0.f ? max((int)(__float_as_uint(amax) >> 23) - 127 - 2, -127) : 0;
+  uint32_t w[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {  // chunk c: elements 8c .. 8c + 7 -> word c, low nibble first
+    uint32_t word = 0u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      word |= e2m1_code_rne(__builtin_amdgcn_ldexpf(elem<BF16>(v[c][j >> 1], j & 1), -X)) << (4 * j);
+    w[c] = word;
+  }
+  codes[i] = u4_t{w[0], w[1], w[2], w[3]};
+  e8m0[i] = (uint8_t)(X + 127);
+}
+
 }  // namespace
+
+int launch_quantize_mx(int64_t m, int64_t k, int in_bf16, const void* x, void* codes, uint8_t* e8m0, void* stream) {
+  const int64_t nblk = m * (k / 32);
+  const dim3 grid((unsigned)((nblk + 255) / 256)), block(256);
+  const auto xs = static_cast<const u4_t*>(x);
+  const auto cs = static_cast<u4_t*>(codes);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return in_bf16 ? (int)launch_timed(quantize_mx_kernel<true>, grid, block, 0, s, xs, nblk, cs, e8m0)
+                 : (int)launch_timed(quantize_mx_kernel<false>, grid, block, 0, s, xs, nblk, cs, e8m0);
+}
 
 int launch_quantize_rows(int64_t m, int64_t k, int in_bf16, int out_fp8, const void* x, void* codes, float* scales,
                          void* stream) {

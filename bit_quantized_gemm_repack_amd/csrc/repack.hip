@@ -76,7 +76,7 @@ int launch_repack(const hq_plan* p, const void* codes, const void* scales, const
   if (err != hipSuccess) return (int)err;
   uint8_t* meta = static_cast<uint8_t*>(meta_out);
   const size_t mpe = p->meta_bytes_per_expert;
-  if (p->fmt == FMT_F4) {
+  if (mx_weights(p->fmt)) {
     // per expert: E8M0 region only
     const int64_t per = N * K / 32;
     hipLaunchKernelGGL(repack_e8m0_kernel, grid_for(per * E), dim3(256), 0, s,

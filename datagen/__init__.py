@@ -94,6 +94,17 @@ def w4a8_mxfp4(M: int, N: int, K: int, key=(3,)):
     return {"a_codes": a_codes, "a_scale": a_scale, "codes": pack_u4(q), "e8m0": e8}
 
 
+def w4a4_mxfp4(M: int, N: int, K: int, key=(6,)):
+    """W4A4-MXFP4 inputs: E2M1 activation codes (packed like the weights) with
+    E8M0 block scales 2^-2..2^1, E2M1 weight codes with E8M0 scales 2^-8..2^-4."""
+    rng = rng_for(*key, M, N, K)
+    qa = rng.integers(0, 16, size=(M, K), dtype=np.uint8)
+    ea = (127 + rng.integers(-2, 2, size=(M, K // MX_BLOCK))).astype(np.uint8)
+    q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    e8 = (127 + rng.integers(-8, -3, size=(N, K // MX_BLOCK))).astype(np.uint8)
+    return {"a_codes": pack_u4(qa), "a_e8m0": ea, "codes": pack_u4(q), "e8m0": e8}
+
+
 def w4a8_int(M: int, N: int, K: int, key=(4,)):
     """W4A8-INT inputs: int8 per-token A, symmetric INT4 codes, fp16 scales."""
     rng = rng_for(*key, M, N, K)

@@ -93,7 +93,8 @@ typedef enum hq_zp_mode {
 
 typedef enum hq_ascale_mode {
   HQ_ASCALE_NONE = 0,         /* 16-bit activations, no scale        */
-  HQ_ASCALE_PER_TOKEN_F32 = 1 /* 8-bit codes with one fp32 per row   */
+  HQ_ASCALE_PER_TOKEN_F32 = 1, /* 8-bit codes with one fp32 per row  */
+  HQ_ASCALE_MX_E8M0 = 2        /* MXFP4 codes with an E8M0 scale per row and 32-element block */
 } hq_ascale_mode;
 
 /* The unified quantisation description: weight codes, scales, zero points
@@ -107,6 +108,10 @@ typedef enum hq_ascale_mode {
  *              act FP8_E4M3, act_scale PER_TOKEN_F32, out F16|BF16
  *   W4A8-MXFP4 w_elem FP4_E2M1, group 32, scale E8M0, zp NONE,
  *              act FP8_E4M3, act_scale PER_TOKEN_F32, out F16|BF16
+ *   W4A4-MXFP4 w_elem FP4_E2M1, group 32, scale E8M0, zp NONE,
+ *              act FP4_E2M1, act_scale MX_E8M0, out F16|BF16 (dense only;
+ *              W4A4 and MXFP4 are among the supported combinations and
+ *              formats of cocoloop.cn, format section)
  * Anything else returns HQ_ERR_UNSUPPORTED from hq_plan_create. */
 typedef struct hq_quant_desc {
   hq_dtype w_elem;
@@ -203,7 +208,10 @@ hq_status hq_repack_host(const hq_plan* plan, const void* codes, const void* sca
 
 /* Dense GEMM: out[M, N] = A[M, K] . W_deq^T.
  *   a        device [m, K] activations (act dtype of the plan)
- *   a_scale  device fp32 [m] per-row scales for 8-bit activations, else NULL
+ *   a_scale  device: fp32 [m] per-row scales for 8-bit activations; uint8
+ *            E8M0 [m, K/32] block scales for MXFP4 activations (W4A4, the
+ *            codes in `a` packed like the weights: two per byte along K, low
+ *            nibble first, i.e. [m, K/2] bytes); else NULL
  *   w, meta  device, produced by hq_repack
  *   out      device [m, N] in the plan's out dtype; with HQ_EPI_I32_ACC
  *            (W4A8-INT only) int32 [m, N, K/128] holding
@@ -213,7 +221,7 @@ hq_status hq_repack_host(const hq_plan* plan, const void* codes, const void* sca
  * m = 0 is a no-op; m > max_m is HQ_ERR_INVALID_ARG.  The kernels address
  * `a` and `w` through 32-bit buffer ranges: an `a` of 2 GiB or more, or a `w`
  * of 2 GiB or more, is HQ_ERR_UNSUPPORTED. */
-hq_status hq_gemm(const hq_plan* plan, int64_t m, const void* a, const float* a_scale,
+hq_status hq_gemm(const hq_plan* plan, int64_t m, const void* a, const void* a_scale,
                   const void* w, const void* meta, void* out, void* ws, size_t ws_bytes,
                   void* stream);
 
@@ -313,13 +321,28 @@ hq_status hq_moe_gemm(const hq_plan* plan, int64_t t, int topk, const void* a, c
 hq_status hq_quantize_per_token(int64_t m, int64_t k, hq_dtype in, hq_dtype out, const void* x, void* codes,
                                 float* scales, void* stream);
 
+/* MXFP4 block quantiser for W4A4 activations (W4A4 and MXFP4: cocoloop.cn,
+ * format section), following the OCP Microscaling v1.0 conversion of a block
+ * of 32 values: X = floor(log2(max |v|)) - 2 (2 = the largest E2M1 exponent),
+ * clamped to [-127, 127], with X = 0 for an all-zero block; each element is
+ * v / 2^X (exact) rounded to E2M1, nearest with ties to even, saturated to
+ * +-6; a value that rounds to zero gives code 0.
+ *   x      device [m, k] fp16 / bf16 (in = HQ_F16 / HQ_BF16), finite values
+ *   codes  device [m, k/2] bytes: E2M1 codes two per byte along k, low
+ *          nibble first (the `a` of a W4A4 hq_gemm), fully overwritten
+ *   e8m0   device [m, k/32] bytes: X + 127 per block (its `a_scale`)
+ * k must be a multiple of 32 (at most 2^24), m at most 2^24 and m * k at most
+ * 2^36; m = 0 is a no-op.  Honours hq_time_next_launch (one kernel). */
+hq_status hq_quantize_mxfp4(int64_t m, int64_t k, hq_dtype in, const void* x, void* codes, uint8_t* e8m0,
+                            void* stream);
+
 /* Kernel timing: the next hq_gemm, hq_moe_align, hq_moe_gemm,
- * hq_quantize_per_token or hq_stream_read call on this thread records
- * `start` (hipEvent_t, created by the caller with timing enabled) when its
- * first kernel starts and `stop` when its last kernel ends (the split-K
- * reduce, the fp8 requant or the combine's final pass included; dispatch
- * times, so no host launch overhead), and hipEventElapsedTime gives the
- * call's device duration.  The request is consumed by that call (also when
+ * hq_quantize_per_token, hq_quantize_mxfp4 or hq_stream_read call on this
+ * thread records `start` (hipEvent_t, created by the caller with timing
+ * enabled) when its first kernel starts and `stop` when its last kernel ends
+ * (the split-K reduce, the fp8 requant or the combine's final pass included;
+ * dispatch times, so no host launch overhead), and hipEventElapsedTime gives
+ * the call's device duration.  The request is consumed by that call (also when
  * it fails); passing NULL, NULL cancels a pending request. */
 hq_status hq_time_next_launch(void* start_event, void* stop_event);
 

@@ -377,3 +377,33 @@ def test_quantize_call_validation():
     assert q(4, 64, hq.F16, hq.FP8_E4M3, fake + 8, fake, fake, None) == hq.HQ_ERR_INVALID_ARG
     assert b"aligned" in L.hq_last_error()
     assert q(0, 64, hq.F16, hq.FP8_E4M3, None, None, None, None) == hq.HQ_OK  # m = 0: no-op
+
+
+def test_w4a4_plans_and_validation():
+    p = _plan(quant=hq.w4a4_mxfp4(), n=4096, k=7168, max_m=1024)
+    assert "w4a4-mxfp4" in p.describe(1) and "kernel=skinny" in p.describe(1)
+    assert "kernel=tiled" in p.describe(1024)
+    for m in (1, 64, 1024):
+        assert p.workspace_bytes(m) >= 0
+    with pytest.raises(hq.HQError):   # W4A4 is dense only
+        hq.MoePlan(512, 7168, hq.w4a4_mxfp4(), 256, 4096, "silu_mul")
+    bad = hq.QuantDesc(hq.FP4_E2M1, 4, 32, hq.E8M0, hq.ZP_NONE, 0, hq.FP4_E2M1, hq.ASCALE_PER_TOKEN_F32, hq.BF16)
+    with pytest.raises(hq.HQError):   # MXFP4 activations need E8M0 block scales
+        _plan(quant=bad)
+    # activations need their E8M0 scales
+    assert _gemm_status(p, 4, a_scale=None) == hq.HQ_ERR_INVALID_ARG
+    assert _gemm_status(p, 4, a_scale=_A16 + 4) == hq.HQ_ERR_INVALID_ARG
+
+
+def test_quantize_mxfp4_call_validation():
+    L = hq.lib()
+    fake = 1 << 20
+    q = L.hq_quantize_mxfp4
+    assert q(4, 64, hq.F32, fake, fake, fake, None) == hq.HQ_ERR_UNSUPPORTED
+    for k in (0, 16, 48, (1 << 24) + 32):
+        assert q(4, k, hq.BF16, fake, fake, fake, None) == hq.HQ_ERR_INVALID_ARG
+    assert q(-1, 64, hq.BF16, fake, fake, fake, None) == hq.HQ_ERR_INVALID_ARG
+    assert q(1 << 24, 1 << 13, hq.BF16, fake, fake, fake, None) == hq.HQ_ERR_UNSUPPORTED  # m * k above 2^36
+    assert q(4, 64, hq.BF16, None, fake, fake, None) == hq.HQ_ERR_INVALID_ARG
+    assert q(4, 64, hq.BF16, fake, fake, fake + 1, None) == hq.HQ_ERR_INVALID_ARG
+    assert q(0, 64, hq.BF16, None, None, None, None) == hq.HQ_OK
