@@ -229,6 +229,8 @@ _WORKLOAD_PROFILES = {
     "prefill": ("qgemm_tiled_prefill_w4a16_f16.md", "dense W4A16 prefill, M in {1024,4096}, N = K = 8192, fp16"),
     "w4a8": ("qgemm_w4a8_mxfp4_int8_n4096_k7168.md", "dense W4A8, M in {1,16,128,1024}, N = 4096, K = 7168, "
              "MXFP4 x fp8 and INT4 x int8"),
+    "w4a4": ("qgemm_w4a4_mxfp4_n4096_k7168.md", "dense W4A4, M in {1,16,128,1024}, N = 4096, K = 7168, "
+             "MXFP4 x MXFP4"),
     "moe": ("moe_layer_e256_top8_h7168_i256.md", "MoE layer, 256 experts, top-8, hidden 7168, intermediate 256, "
             "T in {1,32,512,4096}, bf16 and fp8 activations"),
 }
@@ -542,6 +544,7 @@ def run_quant(args):
 # ----------------------------------------------------------------------------
 FP16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
+FP4_PEAK_TFLOPS = 10100.0
 
 
 def _prefill_points(dev):
@@ -598,6 +601,32 @@ def _w4a8_points(dev):
     return pts, "quantized GEMM TFLOPS and effective HBM GB/s vs M (W4A8)", \
         "dense W4A8: M in {1,16,128,1024}, N = 4096, K = 7168; MXFP4 weights (E8M0 scales) x fp8 e4m3 " \
         "activations, and INT4 weights (fp16 scales, zero point 8) x int8 activations; bf16 output", "f8/i8"
+
+
+def _w4a4_points(dev):
+    import bit_quantized_gemm_repack_amd as hq
+    import datagen
+
+    N, K = 4096, 7168
+    pts = []
+    for M in (1, 16, 128, 1024):
+        d = datagen.w4a4_mxfp4(M, N, K)
+        plan = hq.Plan(N, K, hq.w4a4_mxfp4(), max_m=M)
+        w, meta = plan.repack(torch.from_numpy(d["codes"]).to(dev), e8m0=torch.from_numpy(d["e8m0"]).to(dev))
+        R = 64  # 64 copies of 15.6 MB: > 1 GB
+        ws_ = [(w.clone(), meta.clone()) for _ in range(R)]
+        a = torch.from_numpy(d["a_codes"]).to(dev)
+        ea = hq.mx_scales_group_major(torch.from_numpy(d["a_e8m0"])).to(dev)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = plan.workspace(M, dev)
+        byt = N * K // 2 + N * K // 32 + M * K // 2 + M * K // 32 + 2 * M * N
+        pts.append(dict(name=f"M={M} N={N} K={K}", R=R, bytes=byt, flops=2 * M * N * K, peak=FP4_PEAK_TFLOPS,
+                        plan=plan.describe(M),
+                        calls=lambda r, plan=plan, ws_=ws_, a=a, ea=ea, out=out, ws=ws:
+                        [lambda: plan.gemm(a, ws_[r][0], ws_[r][1], a_scale=ea, out=out, ws=ws)]))
+    return pts, "quantized GEMM TFLOPS and effective HBM GB/s vs M (W4A4)", \
+        "dense W4A4: M in {1,16,128,1024}, N = 4096, K = 7168; MXFP4 activations x MXFP4 weights (E2M1 codes, " \
+        "E8M0 scales per 32), bf16 output", "f4"
 
 
 def _moe_points(dev):
@@ -778,6 +807,12 @@ def _cpu_sample(workload, budget):
             t0 = time.perf_counter()
             og.gemm_w4a16(d["a"].double().numpy(), d["codes"], d["scales"].double().numpy(), 8, out_fmt="f16")
             what = "dense W4A16 M=8 rows of N = K = 8192"
+        elif workload == "w4a4":
+            M, N, K = 16, 4096, 7168
+            d = datagen.w4a4_mxfp4(M, N, K)
+            t0 = time.perf_counter()
+            og.gemm_mxfp4_mxfp4(d["a_codes"], d["a_e8m0"], d["codes"], d["e8m0"])
+            what = "W4A4-MXFP4 M=16 N=4096 K=7168"
         elif workload == "w4a8":
             M, N, K = 16, 4096, 7168
             d = datagen.w4a8_mxfp4(M, N, K)
@@ -817,9 +852,9 @@ def main():
     ap.add_argument("--rotations", type=int, default=4)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--workload", choices=("decode", "quant", "prefill", "w4a8", "moe"), default="decode",
+    ap.add_argument("--workload", choices=("decode", "quant", "prefill", "w4a8", "w4a4", "moe"), default="decode",
                     help="decode: the dense W4A16 decode sweep (default); quant: the per-token quantiser; "
-                         "prefill / w4a8 / moe: the other GEMM workloads")
+                         "prefill / w4a8 / w4a4 / moe: the other GEMM workloads")
     ap.add_argument("--write-profiles", metavar="RUN_DIR",
                     help="CPU only: write the profiles/ summaries from rocprofv3 outputs in RUN_DIR and exit")
     args = ap.parse_args()
@@ -833,8 +868,9 @@ def main():
     if args.workload == "quant":
         run_quant(args)
         return
-    if args.workload in ("prefill", "w4a8", "moe"):
-        run_points_workload(args, {"prefill": _prefill_points, "w4a8": _w4a8_points, "moe": _moe_points}[args.workload])
+    if args.workload in ("prefill", "w4a8", "w4a4", "moe"):
+        run_points_workload(args, {"prefill": _prefill_points, "w4a8": _w4a8_points, "w4a4": _w4a4_points,
+                                   "moe": _moe_points}[args.workload])
         return
 
     import bit_quantized_gemm_repack_amd as hq

@@ -99,7 +99,8 @@ def w4a8_mxfp4(out: str = "bf16") -> QuantDesc:
 
 def w4a4_mxfp4(out: str = "bf16") -> QuantDesc:
     """MXFP4 weights x MXFP4 activations (E2M1 codes packed two per byte along
-    K, E8M0 block scales [m, K/32] passed as a_scale)."""
+    K; E8M0 block scales passed as a_scale in the group-major layout
+    [K/128, m, 4], see mx_scales_group_major)."""
     return QuantDesc(FP4_E2M1, 4, 32, E8M0, ZP_NONE, 0, FP4_E2M1, ASCALE_MX_E8M0, _DT[out])
 
 
@@ -340,10 +341,17 @@ def quantize_per_token(x: torch.Tensor, out: str = "fp8", codes: Optional[torch.
     return codes, scales
 
 
+def mx_scales_group_major(e8m0_rows: torch.Tensor) -> torch.Tensor:
+    """Row-major E8M0 block scales [m, K/32] -> the group-major words
+    [K/128, m, 4] that a W4A4 GEMM reads (a copy; runs where the tensor is)."""
+    m, kb = e8m0_rows.shape
+    return e8m0_rows.reshape(m, kb // 4, 4).transpose(0, 1).contiguous()
+
+
 def quantize_mxfp4(x: torch.Tensor, codes: Optional[torch.Tensor] = None, e8m0: Optional[torch.Tensor] = None):
     """MXFP4 block quantisation of fp16 / bf16 activations [m, k] (see
-    hq_quantize_mxfp4).  Returns (codes uint8 [m, k/2], e8m0 uint8 [m, k/32]),
-    the (a, a_scale) of a W4A4 GEMM."""
+    hq_quantize_mxfp4).  Returns (codes uint8 [m, k/2], e8m0 uint8
+    [k/128, m, 4] group-major), the (a, a_scale) of a W4A4 GEMM."""
     _dev(x, "x")
     if x.dim() != 2 or x.dtype not in (torch.float16, torch.bfloat16):
         raise ValueError("x must be fp16 / bf16 [m, k]")
@@ -351,11 +359,11 @@ def quantize_mxfp4(x: torch.Tensor, codes: Optional[torch.Tensor] = None, e8m0: 
     if codes is None:
         codes = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
     if e8m0 is None:
-        e8m0 = torch.empty((m, k // 32), dtype=torch.uint8, device=x.device)
+        e8m0 = torch.empty((k // 128, m, 4), dtype=torch.uint8, device=x.device)
     _dev(codes, "codes"), _dev(e8m0, "e8m0")
     if codes.numel() * codes.element_size() != m * (k // 2) or e8m0.numel() != m * (k // 32) or \
             e8m0.dtype != torch.uint8:
-        raise ValueError("codes must hold [m, k/2] bytes and e8m0 be uint8 [m, k/32]")
+        raise ValueError("codes must hold [m, k/2] bytes and e8m0 be uint8 [k/128, m, 4]")
     _check(lib().hq_quantize_mxfp4(m, k, BF16 if x.dtype == torch.bfloat16 else F16, _ptr(x), _ptr(codes),
                                    _ptr(e8m0), _stream_ptr(x.device)))
     return codes, e8m0

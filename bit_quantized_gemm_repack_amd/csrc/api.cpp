@@ -176,11 +176,13 @@ Exec choose_exec(const hq_plan* p, int64_t m) {
   // Rules from a sweep of the decode shapes on MI355X (kernel durations):
   //   wide layers (>= 512 column blocks): 4 column blocks per workgroup;
   //   otherwise one column block per workgroup with K split over the waves;
-  //   8 waves for <= 4 rows, 4 for 5..16 rows (each wave's activation loads
-  //   grow with the rows); two groups of loads in flight per wave.
+  //   8 waves, except 4 for 5..16 rows of 16-bit activations (each wave's
+  //   activation loads grow with the rows and the element size); two groups
+  //   of loads in flight per wave.
   c.stages = 2;
   if (c.mb == 1) {
-    c.waves = m <= 4 ? 8 : 4;
+    const bool act16 = p->fmt == FMT_W16F16 || p->fmt == FMT_W16BF16;
+    c.waves = (m <= 4 || !act16) ? 8 : 4;
     if (N / 16 >= 512 && N % 64 == 0) c.nb = 4;
   } else {
     c.waves = 8;
@@ -904,7 +906,8 @@ hq_status hq_quantize_mxfp4(int64_t m, int64_t k, hq_dtype in, const void* x, vo
   const hq::TimingEvents ev = hq::take_timing();  // consumed by this call whatever happens
   if (in != HQ_F16 && in != HQ_BF16) return fail(HQ_ERR_UNSUPPORTED, "input must be fp16 or bf16");
   if (m < 0 || m > (int64_t(1) << 24)) return fail(HQ_ERR_INVALID_ARG, "m out of range [0, 2^24]");
-  if (k < 32 || k % 32 || k > (int64_t(1) << 24)) return fail(HQ_ERR_INVALID_ARG, "k must be a multiple of 32 in [32, 2^24]");
+  if (k < 128 || k % 128 || k > (int64_t(1) << 24))
+    return fail(HQ_ERR_INVALID_ARG, "k must be a multiple of 128 in [128, 2^24]");
   if (m * k > (int64_t(1) << 36)) return fail(HQ_ERR_UNSUPPORTED, "m * k above 2^36");
   if (m == 0) return ok();
   if (!x || !codes || !e8m0) return fail(HQ_ERR_INVALID_ARG, "null device pointer");

@@ -196,7 +196,7 @@ Exec choose_exec(const hq_plan* p, int64_t m);
 struct SkinnyArgs {
   const void* a;
   const float* a_scale;
-  const uint8_t* a_e8m0;  // MXFP4 activations: E8M0 [M][K/32]
+  const uint8_t* a_e8m0;  // MXFP4 activations: E8M0 words [K/128][M][4]
   const void* w;
   const void* scales;
   const uint32_t* zeros;  // nibble-packed, or null
@@ -251,7 +251,7 @@ int launch_moe_combine(const float* rows, int topk, int64_t t, int64_t n, void* 
 struct TiledArgs {
   const void* a;
   const float* a_scale;
-  const uint8_t* a_e8m0;  // MXFP4 activations: E8M0 [M][K/32]
+  const uint8_t* a_e8m0;  // MXFP4 activations: E8M0 words [K/128][M][4]
   const void* w;
   const void* scales;
   const uint32_t* zeros;
@@ -290,7 +290,7 @@ int launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int workgr
 int launch_quantize_rows(int64_t m, int64_t k, int in_bf16, int out_fp8, const void* x, void* codes, float* scales,
                          void* stream);
 // MXFP4 block quantiser: x [m, k] fp16/bf16 -> codes [m, k/2] bytes and E8M0
-// [m, k/32]; k a multiple of 32.
+// words [k/128][m][4]; k a multiple of 128.
 int launch_quantize_mx(int64_t m, int64_t k, int in_bf16, const void* x, void* codes, uint8_t* e8m0, void* stream);
 
 // Pending timing events for the next launch on this thread (see

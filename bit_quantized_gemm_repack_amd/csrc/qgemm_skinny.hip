@@ -146,7 +146,9 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   [[maybe_unused]] const auto rz = rsrc(zeros32 ? static_cast<const void*>(zeros32) : static_cast<const void*>(scales16),
                                         zeros32 ? nfrag * 8 : nfrag * 32);
   [[maybe_unused]] const auto re = rsrc(e8, nfrag * 64);
-  [[maybe_unused]] const auto rae = rsrc(p.a_e8m0, (int64_t)a_rows * (K / 32));
+  // MXFP4 activation scales, group-major words: word (g, row) holds the four
+  // E8M0 block scales of the row's group g
+  [[maybe_unused]] const auto rae = rsrc(p.a_e8m0, (int64_t)G * a_rows * 4);
   // at or above 2^31: past every range (ranges stay below 2 GiB), and adding
   // the group offset cannot wrap
   constexpr int kOutOfRange = INT32_MIN;
@@ -164,7 +166,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
     }
     // 16-bit step t: bytes 256 g + 64 t + 16 kq; 8-bit piece h: 128 g + 64 h + 16 kq
     aoff[mb] = row >= 0 ? row * a_rowb + 16 * kq : kOutOfRange;
-    aeoff[mb] = row >= 0 ? row * (K / 32) : kOutOfRange;
+    aeoff[mb] = row >= 0 ? row * 4 : kOutOfRange;
   }
   int woff[NB], soff[NB], zoff[NB];
 #pragma unroll
@@ -192,7 +194,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
         // block kq of the group: k = 32 kq + [0, 32), 16 bytes; its scale byte
         // is byte kq of the row's group word
         st.a[mb][0] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[mb], g * 64, 0));
-        st.asc[mb] = __builtin_amdgcn_raw_buffer_load_b32(rae, aeoff[mb], g * 4, 0);
+        st.asc[mb] = __builtin_amdgcn_raw_buffer_load_b32(rae, aeoff[mb], g * a_rows * 4, 0);
       } else {
 #pragma unroll
         for (int h = 0; h < 2; ++h)

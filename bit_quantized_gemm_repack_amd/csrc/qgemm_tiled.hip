@@ -190,7 +190,9 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
   [[maybe_unused]] const auto rz = rsrc(zeros32 ? static_cast<const void*>(zeros32) : static_cast<const void*>(scales16),
                                         zeros32 ? nfrag * 8 : nfrag * 32);
   [[maybe_unused]] const auto re = rsrc(e8, nfrag * 64);
-  [[maybe_unused]] const auto rae = rsrc(p.a_e8m0, (int64_t)a_rows * (K / 32));
+  // MXFP4 activation scales, group-major words: word (g, row) holds the four
+  // E8M0 block scales of the row's group g
+  [[maybe_unused]] const auto rae = rsrc(p.a_e8m0, (int64_t)G * a_rows * 4);
 
   // Activation segment s (1 KiB of the slot) holds rows seg*RPS .. +RPS-1;
   // lane l writes physical chunk l % CHUNKS of row seg*RPS + l / CHUNKS, so it
@@ -214,10 +216,11 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
     aoff[s] = row * a_rowb + lchunk * 16;
   }
   // MXFP4 activations: E8M0 word offsets of the rows 16 mb + c16 this lane's
-  // MFMA operands hold (dense only)
+  // MFMA operands hold (dense only); 16 rows of one m-block are 64
+  // contiguous bytes
   [[maybe_unused]] int aeoff[C::MB];
 #pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb) aeoff[mb] = min(m0 + 16 * mb + c16, p.M - 1) * (K / 32);
+  for (int mb = 0; mb < C::MB; ++mb) aeoff[mb] = min(m0 + 16 * mb + c16, p.M - 1) * 4;
   int woff[NBW], soff[NBW], zoff[NBW];
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
@@ -259,7 +262,8 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
     }
     if constexpr (C::ACT4) {
 #pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb) asc[slot][mb] = __builtin_amdgcn_raw_buffer_load_b32(rae, aeoff[mb], gg * 4, 0);
+      for (int mb = 0; mb < C::MB; ++mb)
+        asc[slot][mb] = __builtin_amdgcn_raw_buffer_load_b32(rae, aeoff[mb], gg * a_rows * 4, 0);
     }
   };
   auto zero_of = [&](uint32_t zw) -> uint32_t {

@@ -150,12 +150,16 @@ __device__ inline uint32_t e2m1_code_rne(float x) {
 }
 
 // One thread per 32-element block: 64 input bytes in, 16 code bytes and one
-// E8M0 byte out (consecutive threads, consecutive blocks of a row).
+// E8M0 byte out (consecutive threads, consecutive blocks of a row).  The
+// scales are stored group-major: byte j of word (g, row) is block 4 g + j of
+// the row, so that the GEMM's 16 rows of one operand read 64 contiguous bytes.
 template <bool BF16>
-__global__ void __launch_bounds__(256) quantize_mx_kernel(const u4_t* __restrict__ x, int64_t nblk,
-                                                          u4_t* __restrict__ codes, uint8_t* __restrict__ e8m0) {
+__global__ void __launch_bounds__(256) quantize_mx_kernel(const u4_t* __restrict__ x, int64_t nblk, int64_t m,
+                                                          int64_t kb, u4_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ e8m0) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= nblk) return;
+  const int64_t row = i / kb, b = i - row * kb;
   u4_t v[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) v[c] = __builtin_nontemporal_load(x + 4 * i + c);
@@ -174,7 +178,7 @@ __global__ void __launch_bounds__(256) quantize_mx_kernel(const u4_t* __restrict
     w[c] = word;
   }
   codes[i] = u4_t{w[0], w[1], w[2], w[3]};
-  e8m0[i] = (uint8_t)(X + 127);
+  e8m0[((b >> 2) * m + row) * 4 + (b & 3)] = (uint8_t)(X + 127);
 }
 
 }  // namespace
@@ -185,8 +189,9 @@ int launch_quantize_mx(int64_t m, int64_t k, int in_bf16, const void* x, void* c
   const auto xs = static_cast<const u4_t*>(x);
   const auto cs = static_cast<u4_t*>(codes);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  return in_bf16 ? (int)launch_timed(quantize_mx_kernel<true>, grid, block, 0, s, xs, nblk, cs, e8m0)
-                 : (int)launch_timed(quantize_mx_kernel<false>, grid, block, 0, s, xs, nblk, cs, e8m0);
+  const int64_t kb = k / 32;
+  return in_bf16 ? (int)launch_timed(quantize_mx_kernel<true>, grid, block, 0, s, xs, nblk, m, kb, cs, e8m0)
+                 : (int)launch_timed(quantize_mx_kernel<false>, grid, block, 0, s, xs, nblk, m, kb, cs, e8m0);
 }
 
 int launch_quantize_rows(int64_t m, int64_t k, int in_bf16, int out_fp8, const void* x, void* codes, float* scales,

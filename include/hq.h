@@ -208,10 +208,13 @@ hq_status hq_repack_host(const hq_plan* plan, const void* codes, const void* sca
 
 /* Dense GEMM: out[M, N] = A[M, K] . W_deq^T.
  *   a        device [m, K] activations (act dtype of the plan)
- *   a_scale  device: fp32 [m] per-row scales for 8-bit activations; uint8
- *            E8M0 [m, K/32] block scales for MXFP4 activations (W4A4, the
- *            codes in `a` packed like the weights: two per byte along K, low
- *            nibble first, i.e. [m, K/2] bytes); else NULL
+ *   a_scale  device: fp32 [m] per-row scales for 8-bit activations; for
+ *            MXFP4 activations (W4A4; the codes in `a` packed like the
+ *            weights, two per byte along K, low nibble first: [m, K/2]
+ *            bytes) the E8M0 block scales as group-major words uint8
+ *            [K/128][m][4], byte j of word (g, r) scaling k-block 4g + j of
+ *            row r (so that the 16 rows of one MFMA operand are 64
+ *            contiguous bytes); else NULL
  *   w, meta  device, produced by hq_repack
  *   out      device [m, N] in the plan's out dtype; with HQ_EPI_I32_ACC
  *            (W4A8-INT only) int32 [m, N, K/128] holding
@@ -330,9 +333,10 @@ hq_status hq_quantize_per_token(int64_t m, int64_t k, hq_dtype in, hq_dtype out,
  *   x      device [m, k] fp16 / bf16 (in = HQ_F16 / HQ_BF16), finite values
  *   codes  device [m, k/2] bytes: E2M1 codes two per byte along k, low
  *          nibble first (the `a` of a W4A4 hq_gemm), fully overwritten
- *   e8m0   device [m, k/32] bytes: X + 127 per block (its `a_scale`)
- * k must be a multiple of 32 (at most 2^24), m at most 2^24 and m * k at most
- * 2^36; m = 0 is a no-op.  Honours hq_time_next_launch (one kernel). */
+ *   e8m0   device bytes, X + 127 per block, in the group-major word layout
+ *          [k/128][m][4] that hq_gemm takes as the `a_scale` of W4A4
+ * k must be a multiple of 128 (at most 2^24), m at most 2^24 and m * k at
+ * most 2^36; m = 0 is a no-op.  Honours hq_time_next_launch (one kernel). */
 hq_status hq_quantize_mxfp4(int64_t m, int64_t k, hq_dtype in, const void* x, void* codes, uint8_t* e8m0,
                             void* stream);
 

@@ -399,11 +399,11 @@ def test_quantize_mxfp4_call_validation():
     L = hq.lib()
     fake = 1 << 20
     q = L.hq_quantize_mxfp4
-    assert q(4, 64, hq.F32, fake, fake, fake, None) == hq.HQ_ERR_UNSUPPORTED
-    for k in (0, 16, 48, (1 << 24) + 32):
+    assert q(4, 128, hq.F32, fake, fake, fake, None) == hq.HQ_ERR_UNSUPPORTED
+    for k in (0, 16, 32, 96, 640 + 32, (1 << 24) + 128):
         assert q(4, k, hq.BF16, fake, fake, fake, None) == hq.HQ_ERR_INVALID_ARG
-    assert q(-1, 64, hq.BF16, fake, fake, fake, None) == hq.HQ_ERR_INVALID_ARG
+    assert q(-1, 128, hq.BF16, fake, fake, fake, None) == hq.HQ_ERR_INVALID_ARG
     assert q(1 << 24, 1 << 13, hq.BF16, fake, fake, fake, None) == hq.HQ_ERR_UNSUPPORTED  # m * k above 2^36
-    assert q(4, 64, hq.BF16, None, fake, fake, None) == hq.HQ_ERR_INVALID_ARG
-    assert q(4, 64, hq.BF16, fake, fake, fake + 1, None) == hq.HQ_ERR_INVALID_ARG
-    assert q(0, 64, hq.BF16, None, None, None, None) == hq.HQ_OK
+    assert q(4, 128, hq.BF16, None, fake, fake, None) == hq.HQ_ERR_INVALID_ARG
+    assert q(4, 128, hq.BF16, fake, fake, fake + 1, None) == hq.HQ_ERR_INVALID_ARG
+    assert q(0, 128, hq.BF16, None, None, None, None) == hq.HQ_OK

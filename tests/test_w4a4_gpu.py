@@ -34,7 +34,7 @@ def _run(M, N, K, tuning=None):
     plan = hq.Plan(N, K, hq.w4a4_mxfp4(), max_m=M, tuning=tuning)
     w, meta = plan.repack(torch.from_numpy(d["codes"]).to(DEV), e8m0=torch.from_numpy(d["e8m0"]).to(DEV))
     a = torch.from_numpy(d["a_codes"]).to(DEV)
-    ea = torch.from_numpy(d["a_e8m0"]).to(DEV)
+    ea = hq.mx_scales_group_major(torch.from_numpy(d["a_e8m0"])).to(DEV)
     out = plan.gemm(a, w, meta, a_scale=ea)
     torch.cuda.synchronize()
     rows = _rows(M)
@@ -70,14 +70,16 @@ def _mx_check(x):
     ref_c, ref_e = QZ.mx_quantize_rows(x.float().numpy())
     got = codes.cpu().numpy()
     want = (ref_c[:, 0::2] | (ref_c[:, 1::2] << 4)).astype(np.uint8)
-    assert np.array_equal(e8.cpu().numpy(), ref_e), "E8M0 scales differ"
+    m = ref_e.shape[0]
+    ref_words = ref_e.reshape(m, -1, 4).transpose(1, 0, 2)   # the group-major word layout
+    assert np.array_equal(e8.cpu().numpy(), ref_words), "E8M0 scales differ"
     bad = np.argwhere(got != want)
     assert bad.size == 0, f"{len(bad)} code bytes differ, first at {bad[:4].tolist()}"
     return codes, e8
 
 
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("m,k", [(1, 32), (3, 96), (17, 7168), (256, 4096), (1024, 7168)])
+@pytest.mark.parametrize("m,k", [(1, 128), (3, 384), (17, 7168), (256, 4096), (1024, 7168)])
 def test_quantize_mxfp4_bit_exact(m, k, dt):
     _log(f"quantize mxfp4 m={m} k={k} {dt}")
     rng = np.random.default_rng(m * 7 + k)
@@ -97,9 +99,9 @@ def test_quantize_mxfp4_ties_and_extremes():
     blk[1:8] = mids
     blk[8:15] = -mids
     blk[15:22] = mids * 1.0078125                              # just above each midpoint
-    x = np.stack([blk, blk * 2.0 ** -20, blk * 2.0 ** 20, np.r_[blk[:16], 7.5, 6.5, np.zeros(14)]])
-    _mx_check(torch.from_numpy(x).to(torch.bfloat16))
-    tiny = np.zeros((1, 32))
+    x = np.concatenate([blk, blk * 2.0 ** -20, blk * 2.0 ** 20, np.r_[blk[:16], 7.5, 6.5, np.zeros(14)]])
+    _mx_check(torch.from_numpy(x[None, :]).to(torch.bfloat16))
+    tiny = np.zeros((1, 128))
     tiny[0, :4] = [1e-38, -2e-39, 3e-40, 0]                   # subnormal block maximum
     _mx_check(torch.from_numpy(tiny).to(torch.bfloat16))
 
