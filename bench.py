@@ -64,19 +64,20 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qgemm_decode_sweep_traffic.json")
 
 # sources of the kernels a decode-sweep call runs (GEMM, split-K reduce, their
 # shared headers and launch helper); the plan strings cover the host heuristic
-DECODE_KERNEL_SOURCES = ("qgemm_skinny.hip", "qgemm_tiled.hip", "splitk_reduce.hip", "device_common.h",
-                         "hq_internal.h", "launch.h")
+DECODE_KERNEL_SOURCES = ("csrc/qgemm_skinny.hip", "csrc/qgemm_tiled.hip", "csrc/qgemm_tiled_kernel.h",
+                         "csrc/splitk_reduce.hip", "csrc/device_common.h", "csrc/hq_internal.h", "csrc/launch.h",
+                         "build.py")
 
 
 def kernel_source_hash():
-    """sha256 over the sources of the decode-sweep kernels."""
+    """sha256 over the sources (and build flags) of the decode-sweep kernels."""
     import hashlib
 
-    csrc = os.path.join(ROOT, "bit_quantized_gemm_repack_amd", "csrc")
+    pkg = os.path.join(ROOT, "bit_quantized_gemm_repack_amd")
     h = hashlib.sha256()
     for name in DECODE_KERNEL_SOURCES:
         h.update(name.encode())
-        with open(os.path.join(csrc, name), "rb") as f:
+        with open(os.path.join(pkg, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 

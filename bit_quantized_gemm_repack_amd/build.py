@@ -22,6 +22,10 @@ ARCH = os.environ.get("HQ_OFFLOAD_ARCH", "gfx950")
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 COMMON = ["-O3", "-std=c++20", "-fPIC", "-I", os.path.join(ROOT, "include"), "-Wno-unused-command-line-argument"]
 DEVICE = [f"--offload-arch={ARCH}", "-mcode-object-version=5", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Matrix-instruction results in ordinary VGPRs, so that the per-group
+# epilogues read them without a v_accvgpr_read copy each; sources named
+# *_f16.hip (an fp16 k loop without per-group epilogue) keep the default.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
 def sources():
@@ -32,7 +36,7 @@ def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
     if src.endswith(".hip"):
-        cmd[1:1] = DEVICE
+        cmd[1:1] = DEVICE + ([] if src.endswith("_f16.hip") else VGPR_FORM)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
