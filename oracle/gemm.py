@@ -17,6 +17,9 @@ Readings where the pages are silent:
   before scaling; group g covers k in [G*g, G*g + G) for every row n.
 * Scales and zero points are row-major [N, K/G], n-major like the codes.
 * A symmetric INT4 weight (fixed zero 8) stands for q - 8 in [-8, 7].
+* INT8 weights (WnA16 with n = 8; the pages list INT1..INT8 widths): one
+  unsigned byte per weight with a fixed zero point (128 for the symmetric
+  case), w = (q - z) * s with group-128 scales as for INT4.
 * W4A8-INT: the int32 accumulator of one group is
   P[m,n,g] = sum_{k in g} a_q[m,k] * (q[n,k] - 8), and
   C = s_a[m] * sum_g s[n,g] * P[m,n,g].
@@ -92,6 +95,35 @@ def gemm_w4a16(a, codes, scales, zeros=None, group: int = 128, out_fmt: str = "f
     """
     a = np.asarray(a, dtype=np.float64)
     w = dequant_int4(codes, scales, zeros, group)
+    c64 = a @ w.T
+    return {"c64": c64, "c_out": rne(c64, out_fmt), "tau": tolerance(a, w), "w": w}
+
+
+def dequant_int8(codes, scales, zero: int = 128, group: int = 128) -> np.ndarray:
+    """Exact float64 weights w[n,k] = (q[n,k] - z) * s[n,k//G] for 8-bit codes.
+
+    codes  uint8 [N, K] (canonical: one byte per weight, row-major; an int32
+           [N, K/4] array of the same bytes, low byte first, is accepted)
+    scales float array-like [N, K/G]; zero the fixed zero point 0..255.
+    """
+    c = np.ascontiguousarray(codes)
+    q = (c.view(np.uint8) if c.dtype != np.uint8 else c).astype(np.int64)
+    N, K = q.shape[0], q.size // q.shape[0]
+    q = q.reshape(N, K)
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    s = np.asarray(scales, dtype=np.float64)
+    w = np.empty((N, K), dtype=np.float64)
+    for g in range(K // group):
+        ks = slice(g * group, (g + 1) * group)
+        w[:, ks] = (q[:, ks] - int(zero)) * s[:, g : g + 1]
+    return w
+
+
+def gemm_w8a16(a, codes, scales, zero: int = 128, group: int = 128, out_fmt: str = "f16"):
+    """Dense W8A16 (INT8 weights, one of the WnA16 widths): C = A . ((q - z) * s)^T, float64."""
+    a = np.asarray(a, dtype=np.float64)
+    w = dequant_int8(codes, scales, zero, group)
     c64 = a @ w.T
     return {"c64": c64, "c_out": rne(c64, out_fmt), "tau": tolerance(a, w), "w": w}
 

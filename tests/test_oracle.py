@@ -435,3 +435,35 @@ def test_planted_mistakes_are_caught(monkeypatch):
     # a wrong E2M1 exponent bias is caught by the table pin
     vals = F.e2m1_value(np.arange(16)) * 2
     assert not np.array_equal(vals, np.array(_gold("e2m1_table.json")["values"]))
+
+
+# ------------------------------------------------------------ INT8 weights --
+
+def test_int8_gemm_hand_example():
+    g = _gold("int8_gemm_2x2.json")
+    r = G.gemm_w8a16(np.array(g["a"], float), np.array(g["codes"], np.uint8), np.array(g["scales"]), g["zero"],
+                     group=g["group"])
+    assert r["c64"].tolist() == g["c"]
+    # the same bytes given as int32 words (low byte first)
+    words = np.array(g["codes"], np.uint8).view(np.int32)
+    assert np.array_equal(G.dequant_int8(words, np.array(g["scales"]), g["zero"], group=8),
+                          G.dequant_int8(np.array(g["codes"], np.uint8), np.array(g["scales"]), g["zero"], group=8))
+
+
+def test_int8_weights_agree_with_int4_on_shared_range():
+    """Codes 120..135 with zero 128 are the INT4 codes 0..15 with zero 8."""
+    rng = np.random.default_rng(31)
+    q4 = rng.integers(0, 16, size=(6, 256), dtype=np.uint8)
+    s = rng.uniform(0.005, 0.02, size=(6, 2))
+    w4 = G.dequant_int4(datagen.pack_u4(q4), s, 8)
+    w8 = G.dequant_int8((q4.astype(np.int64) + 120).astype(np.uint8), s, 128)
+    assert np.array_equal(w4, w8)
+
+
+def test_int8_integer_special_case():
+    rng = np.random.default_rng(32)
+    q = rng.integers(0, 256, size=(7, 384), dtype=np.uint8)
+    a = rng.integers(-4, 5, size=(5, 384)).astype(np.float64)
+    r = G.gemm_w8a16(a, q, np.ones((7, 3)), 128)
+    ref = a.astype(np.int64) @ (q.astype(np.int64) - 128).T
+    assert np.array_equal(r["c64"], ref.astype(np.float64))
