@@ -46,9 +46,21 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Map a quantisation description to a kernel format, or fail.
 hq_status classify(const hq_quant_desc& q, int* fmt) {
-  if (q.w_bits != 4) return fail(HQ_ERR_UNSUPPORTED, "only 4-bit weights are implemented (w_bits=%d)", q.w_bits);
   if (q.out != HQ_F16 && q.out != HQ_BF16)
     return fail(HQ_ERR_UNSUPPORTED, "output dtype must be fp16 or bf16");
+  if (q.w_elem == HQ_U8) {
+    if (q.w_bits != 8) return fail(HQ_ERR_UNSUPPORTED, "U8 weights have w_bits 8 (got %d)", q.w_bits);
+    if (q.group_size != 128) return fail(HQ_ERR_UNSUPPORTED, "INT8 weights need group_size 128 (got %d)", q.group_size);
+    if (q.scale != HQ_F16 && q.scale != HQ_BF16)
+      return fail(HQ_ERR_UNSUPPORTED, "INT8 group scales must be fp16 or bf16");
+    if (q.zp != HQ_ZP_FIXED) return fail(HQ_ERR_UNSUPPORTED, "INT8 weights are implemented with a fixed zero point");
+    if (q.zp_value < 0 || q.zp_value > 255) return fail(HQ_ERR_INVALID_ARG, "INT8 fixed zero point must be 0..255");
+    if ((q.act != HQ_F16 && q.act != HQ_BF16) || q.act_scale != HQ_ASCALE_NONE)
+      return fail(HQ_ERR_UNSUPPORTED, "INT8 weights are implemented with fp16 / bf16 activations");
+    *fmt = q.act == HQ_F16 ? hq::FMT_W8F16 : hq::FMT_W8BF16;
+    return HQ_OK;
+  }
+  if (q.w_bits != 4) return fail(HQ_ERR_UNSUPPORTED, "this weight element needs w_bits 4 (got %d)", q.w_bits);
   if (q.w_elem == HQ_U4) {
     if (q.group_size != 128) return fail(HQ_ERR_UNSUPPORTED, "INT4 weights need group_size 128 (got %d)", q.group_size);
     if (q.scale != HQ_F16 && q.scale != HQ_BF16)
@@ -102,6 +114,8 @@ const char* fmt_name(int fmt) {
   switch (fmt) {
     case hq::FMT_W16F16: return "w4a16-f16";
     case hq::FMT_W16BF16: return "w4a16-bf16";
+    case hq::FMT_W8F16: return "w8a16-f16";
+    case hq::FMT_W8BF16: return "w8a16-bf16";
     case hq::FMT_I8: return "w4a8-int8";
     case hq::FMT_Q8: return "w4a8-fp8";
     case hq::FMT_F4: return "w4a8-mxfp4";
@@ -141,9 +155,9 @@ Exec choose_exec(const hq_plan* p, int64_t m) {
     // tile shapes from a sweep on MI355X (N = 4096..8192): 16-bit activations
     // 128 x 256 at m >= 512; MXFP4 128 x 128 with a 4-group pipeline; int8
     // and fp8 x INT4 64 x 128 with a 2-group pipeline
-    const bool act16 = p->fmt == FMT_W16F16 || p->fmt == FMT_W16BF16;
+    const bool act16 = act16_fmt(p->fmt);
     e.tl.bm = m >= 512 ? 128 : 64;
-    e.tl.nbw = (N % 256 == 0 && m >= 512 && p->fmt == FMT_W16F16) ? 4 : 2;
+    e.tl.nbw = (N % 256 == 0 && m >= 512 && f16_act(p->fmt)) ? 4 : 2;
     int stages = 3;
     if (!act16 && m >= 512) {
       if (mx_weights(p->fmt)) {
@@ -181,7 +195,7 @@ Exec choose_exec(const hq_plan* p, int64_t m) {
   //   of loads in flight per wave.
   c.stages = 2;
   if (c.mb == 1) {
-    const bool act16 = p->fmt == FMT_W16F16 || p->fmt == FMT_W16BF16;
+    const bool act16 = act16_fmt(p->fmt);
     c.waves = (m <= 4 || !act16) ? 8 : 4;
     if (N / 16 >= 512 && N % 64 == 0) c.nb = 4;
   } else {
@@ -234,11 +248,11 @@ hq_status check_exec(const hq_plan* p, const hq::Exec& e) {
     {
       // load pipeline: stages x (tile_m rows x one group of A) in LDS, and the
       // loads of stages - 2 groups in flight within the 6-bit wait counter
-      const bool act16 = p->fmt == hq::FMT_W16F16 || p->fmt == hq::FMT_W16BF16;
+      const bool act16 = hq::act16_fmt(p->fmt);
       const bool act4 = p->fmt == hq::FMT_F44;
       const int rowb = act16 ? 256 : (act4 ? 64 : 128);
       const int lps = e.tl.bm * rowb / 1024 / 4 + e.tl.nbw * (hq::mx_weights(p->fmt) ? 2 : 3) +
-                      (act4 ? e.tl.bm / 16 : 0);
+                      (act4 ? e.tl.bm / 16 : 0) + (hq::w8_weights(p->fmt) ? e.tl.nbw : 0);
       if (e.tl.stages < 2 || e.tl.stages > 5) return fail(HQ_ERR_INVALID_ARG, "tiled kernel: stages must be 2..5");
       if (e.tl.stages * e.tl.bm * rowb > 160 * 1024 || lps * (e.tl.stages - 2) >= 64)
         return fail(HQ_ERR_INVALID_ARG, "tiled kernel: too many stages for this tile");
@@ -258,8 +272,9 @@ hq_status check_exec(const hq_plan* p, const hq::Exec& e) {
   if ((size_t)c.waves * c.mb * c.nb * 4 * 64 * 4 > 32768)
     return fail(HQ_ERR_INVALID_ARG, "waves * tile_m * tile_n too large for the reduction buffer");
   // register budget: these shapes would spill at two waves per SIMD
-  const bool act16 = p->fmt == hq::FMT_W16F16 || p->fmt == hq::FMT_W16BF16;
-  if ((c.stages < 8 && c.mb * c.nb * c.stages > 16) || c.mb * c.stages > 8 || (c.mb == 4 && c.nb == 2 && act16))
+  const bool act16 = hq::act16_fmt(p->fmt);
+  if ((c.stages < 8 && c.mb * c.nb * c.stages > 16) || c.mb * c.stages > 8 || (c.mb == 4 && c.nb == 2 && act16) ||
+      (hq::w8_weights(p->fmt) && c.mb * c.nb * c.stages > 8))
     return fail(HQ_ERR_INVALID_ARG, "tile_m/tile_n/stages combination exceeds the register budget");
   return HQ_OK;
 }
@@ -352,7 +367,7 @@ hq_status hq_plan_create(const hq_layer_desc* layer, const hq_compute* compute, 
     if (tuning) p->user = *tuning;
     p->fmt = fmt;
     const int64_t N = layer->n, K = layer->k, G = K / 128;
-    p->w_bytes_per_expert = (size_t)(N * K / 2);
+    p->w_bytes_per_expert = (size_t)(hq::w8_weights(fmt) ? N * K : N * K / 2);
     if (hq::mx_weights(fmt)) {
       p->scale_region_bytes = 0;
       p->meta_bytes_per_expert = (size_t)(N * K / 32);
@@ -447,11 +462,18 @@ hq_status hq_repack_host(const hq_plan* p, const void* codes, const void* scales
     hq_status s = check_repack_args(p, codes, scales, zx, w_out, meta_out);
     if (s != HQ_OK) return s;
     const int64_t N = p->layer.n, K = p->layer.k, E = p->layer.num_experts, G = K / 128;
-    const int64_t wpe = N * K / 8;
-    const uint32_t* cw = static_cast<const uint32_t*>(codes);
     uint32_t* wo = static_cast<uint32_t*>(w_out);
-    for (int64_t e = 0; e < E; ++e)
-      for (int64_t i = 0; i < wpe; ++i) wo[e * wpe + i] = hq::repack_word(cw + e * wpe, K, p->fmt, i);
+    if (hq::w8_weights(p->fmt)) {
+      const int64_t wpe8 = N * K / 4;
+      const uint8_t* cb = static_cast<const uint8_t*>(codes);
+      for (int64_t e = 0; e < E; ++e)
+        for (int64_t i = 0; i < wpe8; ++i) wo[e * wpe8 + i] = hq::repack_word8(cb + e * N * K, K, i);
+    } else {
+      const int64_t wpe = N * K / 8;
+      const uint32_t* cw = static_cast<const uint32_t*>(codes);
+      for (int64_t e = 0; e < E; ++e)
+        for (int64_t i = 0; i < wpe; ++i) wo[e * wpe + i] = hq::repack_word(cw + e * wpe, K, p->fmt, i);
+    }
     uint8_t* meta = static_cast<uint8_t*>(meta_out);
     if (hq::mx_weights(p->fmt)) {
       const int64_t per = N * K / 32;
@@ -515,8 +537,8 @@ hq_status hq_gemm(const hq_plan* p, int64_t m, const void* a, const void* a_scal
                                 : nullptr;
     {
       // the kernels address A and W through 32-bit buffer ranges
-      const int64_t act_bytes2 = (p->fmt == hq::FMT_W16F16 || p->fmt == hq::FMT_W16BF16) ? 4 : (act4 ? 1 : 2);
-      if (m * K * act_bytes2 / 2 >= (int64_t(1) << 31) || N * K / 2 >= (int64_t(1) << 31))
+      const int64_t act_bytes2 = hq::act16_fmt(p->fmt) ? 4 : (act4 ? 1 : 2);
+      if (m * K * act_bytes2 / 2 >= (int64_t(1) << 31) || (int64_t)p->w_bytes_per_expert >= (int64_t(1) << 31))
         return fail(HQ_ERR_UNSUPPORTED, "activations and weights must each stay below 2 GiB");
     }
     if (e.kernel == hq::KER_TILED) {

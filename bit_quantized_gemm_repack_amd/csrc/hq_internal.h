@@ -63,8 +63,21 @@ enum Fmt : int {
   FMT_I8 = 2,      // INT4 weight, int8 activation, int8 MFMA (exact int32)
   FMT_Q8 = 3,      // INT4 weight, fp8 activation, scaled fp8 MFMA
   FMT_F4 = 4,      // MXFP4 weight, fp8 activation, scaled fp8 x fp4 MFMA
-  FMT_F44 = 5      // MXFP4 weight, MXFP4 activation, scaled fp4 x fp4 MFMA
+  FMT_F44 = 5,     // MXFP4 weight, MXFP4 activation, scaled fp4 x fp4 MFMA
+  FMT_W8F16 = 6,   // INT8 weight, fp16 activation (two 4-bit planes), fp16 MFMA
+  FMT_W8BF16 = 7   // INT8 weight, bf16 activation (two 4-bit planes), bf16 MFMA
 };
+
+// INT8 weights: stored as two 4-bit planes (high nibbles, then low nibbles)
+// in the 16-bit operand order, so that each plane expands to exact MFMA
+// operands like an INT4 weight and q = 16 * high + low.
+HQ_HD constexpr inline bool w8_weights(int fmt) { return fmt == FMT_W8F16 || fmt == FMT_W8BF16; }
+// fp16 / bf16 activations (INT4 or INT8 weights)
+HQ_HD constexpr inline bool act16_fmt(int fmt) {
+  return fmt == FMT_W16F16 || fmt == FMT_W16BF16 || fmt == FMT_W8F16 || fmt == FMT_W8BF16;
+}
+// fp16 (rather than bf16) activations
+HQ_HD constexpr inline bool f16_act(int fmt) { return fmt == FMT_W16F16 || fmt == FMT_W8F16; }
 
 // MXFP4 weights (E2M1 codes in natural order + E8M0 block scales).
 HQ_HD constexpr inline bool mx_weights(int fmt) { return fmt == FMT_F4 || fmt == FMT_F44; }
@@ -72,7 +85,7 @@ HQ_HD constexpr inline bool mx_weights(int fmt) { return fmt == FMT_F4 || fmt ==
 enum NibOrder : int { NIB_W16 = 0, NIB_B8 = 1, NIB_NAT = 2 };
 
 HQ_HD inline int nib_order_of(int fmt) {
-  return (fmt == FMT_W16F16 || fmt == FMT_W16BF16) ? NIB_W16 : (mx_weights(fmt) ? NIB_NAT : NIB_B8);
+  return act16_fmt(fmt) ? NIB_W16 : (mx_weights(fmt) ? NIB_NAT : NIB_B8);
 }
 HQ_HD inline uint32_t nib_xor_of(int fmt) { return fmt == FMT_I8 ? 8u : 0u; }
 
@@ -110,6 +123,27 @@ HQ_HD inline uint32_t repack_word(const uint32_t* codes, int64_t K, int fmt, int
   const uint32_t x = nib_xor_of(fmt);
   uint32_t w = 0;
   for (int p = 0; p < 8; ++p) w |= (canon_code(codes, K, n, kbase + nib_koff(order, p)) ^ x) << (4 * p);
+  return w;
+}
+
+// One 32-bit word of the INT8 device layout (two 1 KiB planes per 16 x 128
+// fragment: high nibbles, then low nibbles, each in the 4-bit order of the
+// 16-bit operands): word widx of one expert's region <- canonical uint8 [N][K].
+HQ_HD inline uint32_t repack_word8(const uint8_t* codes, int64_t K, int64_t widx) {
+  const int64_t G = K / kFragK;
+  const int t = (int)(widx & 3);
+  const int lane = (int)((widx >> 2) & 63);
+  const int plane = (int)((widx >> 8) & 1);
+  const int64_t frag = widx >> 9;
+  const int64_t g = frag % G;
+  const int64_t nb = frag / G;
+  const int64_t n = nb * kFragN + (lane & 15);
+  const int64_t kbase = g * kFragK + word_kbase(NIB_W16, lane >> 4, t);
+  uint32_t w = 0;
+  for (int p = 0; p < 8; ++p) {
+    const uint32_t q = codes[n * K + kbase + nib_koff(NIB_W16, p)];
+    w |= (plane == 0 ? (q >> 4) : (q & 0xFu)) << (4 * p);
+  }
   return w;
 }
 

@@ -43,11 +43,12 @@ namespace hq {
 
 template <int FMT>
 struct FmtInfo {
-  static constexpr bool kAct16 = (FMT == FMT_W16F16 || FMT == FMT_W16BF16);
+  static constexpr bool kAct16 = act16_fmt(FMT);
+  static constexpr bool kW8 = w8_weights(FMT);  // INT8 weights: a second (low-nibble) plane
   static constexpr bool kAct4 = (FMT == FMT_F44);  // MXFP4 activations
   static constexpr int kAVec = kAct16 ? 4 : (kAct4 ? 1 : 2);  // 16-byte loads per lane per group
   static constexpr int kARowB = kAct16 ? 256 : (kAct4 ? 64 : 128);  // A bytes per row per group
-  static constexpr bool kRowSum = (FMT == FMT_W16F16 || FMT == FMT_W16BF16 || FMT == FMT_Q8);
+  static constexpr bool kRowSum = (act16_fmt(FMT) || FMT == FMT_Q8);
   static constexpr bool kActScale = !kAct16 && !kAct4;  // one fp32 scale per row
 };
 
@@ -55,6 +56,7 @@ template <int FMT, int MB, int NB>
 struct Stage {
   u4_t a[MB][FmtInfo<FMT>::kAVec];
   u4_t b[NB];
+  u4_t b2[NB];        // INT8 weights: the low-nibble plane (b holds the high one)
   uint32_t sraw[NB];  // scale bits, or the E8M0 byte
   uint32_t zraw[NB];  // zero-point word (8 nibbles), unused with a fixed zero
   uint32_t asc[MB];   // MXFP4 activations: the row's four E8M0 block scales of the group
@@ -62,7 +64,7 @@ struct Stage {
 
 template <int FMT>
 __device__ inline f4_t mfma16(u4_t a, u4_t b, f4_t c) {
-  return mfma_16x16x32<FMT == FMT_W16F16>(a, b, c);
+  return mfma_16x16x32<f16_act(FMT)>(a, b, c);
 }
 
 // GRP selects the row / weight indexing: GRP_DENSE (rows 0..M-1, one weight),
@@ -141,7 +143,8 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   const int a_rows = (GRP == GRP_GATHER) ? p.n_slots / p.topk : p.M;
   const auto ra = rsrc(p.a, (int64_t)a_rows * a_rowb);
   const int64_t nfrag = (int64_t)(p.N / 16) * G;
-  const auto rw = rsrc(wbytes, nfrag * 1024);
+  constexpr int kFragB = FI::kW8 ? 2048 : 1024;  // weight bytes per 16 x 128 fragment
+  const auto rw = rsrc(wbytes, nfrag * kFragB);
   [[maybe_unused]] const auto rsc = rsrc(scales16, nfrag * 32);
   [[maybe_unused]] const auto rz = rsrc(zeros32 ? static_cast<const void*>(zeros32) : static_cast<const void*>(scales16),
                                         zeros32 ? nfrag * 8 : nfrag * 32);
@@ -172,7 +175,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int f0 = nblk(nb) * G;
-    woff[nb] = (f0 * 64 + lane) * 16;
+    woff[nb] = f0 * kFragB + lane * 16;
     soff[nb] = mx_weights(FMT) ? f0 * 64 + (lane & ~3) : f0 * 32 + (c >> 1) * 4;
     zoff[nb] = f0 * 8 + (c >> 3) * 4;
   }
@@ -180,7 +183,12 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   auto load = [&](Stage<FMT, MB, NB>& st, int g) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      st.b[nb] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[nb], g * 1024, 2));
+      st.b[nb] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[nb], g * kFragB, 2));
+    if constexpr (FI::kW8) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        st.b2[nb] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[nb] + 1024, g * kFragB, 2));
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       // Step t of the 16-bit operand: k = 32 t + 8 kq + [0,8); piece h of the
@@ -229,8 +237,8 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
 
   auto compute = [&](const Stage<FMT, MB, NB>& st, int g) {
     [[maybe_unused]] f4_t rs[MB];
-    if constexpr (FMT == FMT_W16F16 || FMT == FMT_W16BF16) {
-      const uint32_t one2 = (FMT == FMT_W16F16) ? 0x3C003C00u : 0x3F803F80u;
+    if constexpr (FI::kAct16) {
+      const uint32_t one2 = f16_act(FMT) ? 0x3C003C00u : 0x3F803F80u;
       const u4_t ones = u4_t{one2, one2, one2, one2};
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
@@ -250,9 +258,34 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const u4_t w = st.b[nb];
-      if constexpr (FMT == FMT_W16F16 || FMT == FMT_W16BF16) {
-        const uint32_t magic = (FMT == FMT_W16F16) ? 0x64006400u : 0x43004300u;
-        const float off = (FMT == FMT_W16F16) ? 1024.f : 128.f;
+      if constexpr (FI::kW8) {
+        // q = 16 * high + low: P_h and P_l against the exact offset operands
+        // (OFF + high), (OFF + low); the row sums remove 17 OFF + z
+        const uint32_t magic = f16_act(FMT) ? 0x64006400u : 0x43004300u;
+        const float off = f16_act(FMT) ? 1024.f : 128.f;
+        const u4_t w2 = st.b2[nb];
+        f4_t Ph[MB], Pl[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) Ph[mb] = Pl[mb] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const u4_t bh = w16_operand(w[t], magic);
+          const u4_t bl = w16_operand(w2[t], magic);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            Ph[mb] = mfma16<FMT>(st.a[mb][t], bh, Ph[mb]);
+            Pl[mb] = mfma16<FMT>(st.a[mb][t], bl, Pl[mb]);
+          }
+        }
+        const float s = p.scale_bf16 ? bf16_bits_to_float(sbits(st, nb)) : f16_bits_to_float(sbits(st, nb));
+        const float cz = 17.f * off + (float)p.zp_fixed;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[mb][nb][r] += s * (16.f * Ph[mb][r] + Pl[mb][r] - cz * rs[mb][r]);
+      } else if constexpr (FI::kAct16) {
+        const uint32_t magic = f16_act(FMT) ? 0x64006400u : 0x43004300u;
+        const float off = f16_act(FMT) ? 1024.f : 128.f;
         f4_t P[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) P[mb] = f4_t{0.f, 0.f, 0.f, 0.f};
@@ -521,6 +554,8 @@ int launch_skinny(int fmt, const SkinnyCfg& cfg, const SkinnyArgs& a, void* stre
   switch (fmt) {
     case FMT_W16F16: return (int)launch_mb<FMT_W16F16>(cfg, a, grid, block, lds, s);
     case FMT_W16BF16: return (int)launch_mb<FMT_W16BF16>(cfg, a, grid, block, lds, s);
+    case FMT_W8F16: return (int)launch_mb<FMT_W8F16>(cfg, a, grid, block, lds, s);
+    case FMT_W8BF16: return (int)launch_mb<FMT_W8BF16>(cfg, a, grid, block, lds, s);
     case FMT_I8: return (int)launch_mb<FMT_I8>(cfg, a, grid, block, lds, s);
     case FMT_Q8: return (int)launch_mb<FMT_Q8>(cfg, a, grid, block, lds, s);
     case FMT_F4: return (int)launch_mb<FMT_F4>(cfg, a, grid, block, lds, s);

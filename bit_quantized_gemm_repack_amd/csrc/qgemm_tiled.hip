@@ -9,8 +9,10 @@ int launch_tiled(int fmt, const TiledCfgRt& cfg, const TiledArgs& a, void* strea
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)(a.part ? cfg.split : 1));
   switch (fmt) {
-    case FMT_W16F16: return (int)launch_tiled_f16(GRP_DENSE, cfg, a, grid, s);
+    case FMT_W16F16:
+    case FMT_W8F16: return (int)launch_tiled_f16(fmt, GRP_DENSE, cfg, a, grid, s);
     case FMT_W16BF16: return (int)launch_tiled_f<FMT_W16BF16, GRP_DENSE>(cfg, a, grid, s);
+    case FMT_W8BF16: return (int)launch_tiled_f<FMT_W8BF16, GRP_DENSE>(cfg, a, grid, s);
     case FMT_I8: return (int)launch_tiled_f<FMT_I8, GRP_DENSE>(cfg, a, grid, s);
     case FMT_Q8: return (int)launch_tiled_f<FMT_Q8, GRP_DENSE>(cfg, a, grid, s);
     case FMT_F4: return (int)launch_tiled_f<FMT_F4, GRP_DENSE>(cfg, a, grid, s);
@@ -29,13 +31,13 @@ int launch_tiled_grouped(int fmt, int mode, const TiledCfgRt& cfg, const TiledAr
   const dim3 grid((unsigned)ntiles, (unsigned)blocks);
   if (mode == GRP_GATHER) {
     switch (fmt) {
-      case FMT_W16F16: return (int)launch_tiled_f16(GRP_GATHER, cfg, a, grid, s);
+      case FMT_W16F16: return (int)launch_tiled_f16(fmt, GRP_GATHER, cfg, a, grid, s);
       case FMT_W16BF16: return (int)launch_tiled_f<FMT_W16BF16, GRP_GATHER>(cfg, a, grid, s);
       case FMT_Q8: return (int)launch_tiled_f<FMT_Q8, GRP_GATHER>(cfg, a, grid, s);
     }
   } else if (mode == GRP_SORTED) {
     switch (fmt) {
-      case FMT_W16F16: return (int)launch_tiled_f16(GRP_SORTED, cfg, a, grid, s);
+      case FMT_W16F16: return (int)launch_tiled_f16(fmt, GRP_SORTED, cfg, a, grid, s);
       case FMT_W16BF16: return (int)launch_tiled_f<FMT_W16BF16, GRP_SORTED>(cfg, a, grid, s);
       case FMT_Q8: return (int)launch_tiled_f<FMT_Q8, GRP_SORTED>(cfg, a, grid, s);
     }

@@ -56,7 +56,9 @@ struct TCfg {
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BN = WAVES * NBW * 16;
   static constexpr int MB = BM / 16;
-  static constexpr bool ACT16 = (FMT == FMT_W16F16 || FMT == FMT_W16BF16);
+  static constexpr bool ACT16 = act16_fmt(FMT);
+  static constexpr bool W8 = w8_weights(FMT);  // INT8 weights: two 1 KiB planes per fragment
+  static constexpr int FRAGB = W8 ? 2048 : 1024;
   static constexpr bool ACT4 = (FMT == FMT_F44);  // MXFP4 activations
   static constexpr int ROWB = ACT16 ? 256 : (ACT4 ? 64 : 128);  // A bytes per row per group
   static constexpr int CHUNKS = ROWB / 16;        // 16-byte chunks per row
@@ -69,10 +71,10 @@ struct TCfg {
   static constexpr int META = mx_weights(FMT) ? 1 : 2;  // metadata loads per fragment
   // vector-memory loads per step per wave (MXFP4 activations: plus one E8M0
   // word per m-block)
-  static constexpr int LPS = SEGW + NBW + META * NBW + (ACT4 ? MB : 0);
+  static constexpr int LPS = SEGW + (W8 ? 2 : 1) * NBW + META * NBW + (ACT4 ? MB : 0);
+  // the loads in flight fit the wait counter and the ring fits the LDS
+  static constexpr bool FITS = ST >= 2 && LPS * (ST - 2) < 64 && LDS_BYTES <= 160 * 1024;
   static_assert(SEGW * WAVES == NSEG, "tile rows must fill the loaders");
-  static_assert(ST >= 2 && LPS * (ST - 2) < 64, "loads in flight exceed the counter");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds the workgroup limit");
 };
 
 // Physical 16-byte chunk of logical chunk c in row r (CH chunks per row):
@@ -105,6 +107,7 @@ template <int FMT, int BM, int NBW, int GRP, int ST>
 __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses device-only builtins; the host pass needs only the stub
   using C = TCfg<FMT, BM, NBW, ST>;
+  static_assert(C::FITS, "loads in flight exceed the counter, or the ring the LDS");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -187,7 +190,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
   const int a_rows = (GRP == GRP_GATHER) ? p.n_slots / p.topk : p.M;
   const auto ra = rsrc(p.a, (int64_t)a_rows * a_rowb);
   const int64_t nfrag = (int64_t)(p.N / 16) * G;  // fragments of this weight (one expert)
-  const auto rw = rsrc(wbytes, nfrag * 1024);
+  const auto rw = rsrc(wbytes, nfrag * C::FRAGB);
   [[maybe_unused]] const auto rs = rsrc(scales16, nfrag * 32);
   [[maybe_unused]] const auto rz = rsrc(zeros32 ? static_cast<const void*>(zeros32) : static_cast<const void*>(scales16),
                                         zeros32 ? nfrag * 8 : nfrag * 32);
@@ -227,13 +230,14 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
     const int f0 = nblk(j) * G;  // first fragment of this column block
-    woff[j] = (f0 * 64 + lane) * 16;
+    woff[j] = f0 * C::FRAGB + lane * 16;
     soff[j] = mx_weights(FMT) ? f0 * 64 + (lane & ~3) : f0 * 32 + (c16 >> 1) * 4;
     zoff[j] = f0 * 8 + (c16 >> 3) * 4;
   }
 
   // ---- weight fragments + metadata of this wave, register ring ---------------
   u4_t braw[C::STAGES][NBW];
+  [[maybe_unused]] u4_t braw2[C::STAGES][NBW];  // INT8 weights: the low-nibble plane
   uint32_t sraw[C::STAGES][NBW];
   [[maybe_unused]] uint32_t zraw[C::STAGES][NBW];
   [[maybe_unused]] uint32_t asc[C::STAGES][C::MB];  // MXFP4 activations: row scale words
@@ -249,7 +253,13 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
     }
 #pragma unroll
     for (int j = 0; j < NBW; ++j)
-      braw[slot][j] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[j], gg * 1024, 2));
+      braw[slot][j] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[j], gg * C::FRAGB, 2));
+    if constexpr (C::W8) {
+#pragma unroll
+      for (int j = 0; j < NBW; ++j)
+        braw2[slot][j] =
+            __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[j] + 1024, gg * C::FRAGB, 2));
+    }
     // Metadata comes in as whole 32-bit words and the lane's byte / half-word
     // is taken out in the math: a narrow load would be zero-extended where the
     // ring is carried round the loop, which forces a wait for every load there.
@@ -279,7 +289,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
   for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
     for (int j = 0; j < NBW; ++j) acc[mb][j] = f4_t{0.f, 0.f, 0.f, 0.f};
-  [[maybe_unused]] const uint32_t magic_v = opaque_vgpr(FMT == FMT_W16F16 ? 0x64006400u : 0x43004300u);
+  [[maybe_unused]] const uint32_t magic_v = opaque_vgpr(f16_act(FMT) ? 0x64006400u : 0x43004300u);
 
   // Operand fetch of m-block mb from `slot`: row r = 16 mb + c16.
   // 16-bit: step t takes k = 32 t + 8 kq + [0,8) (chunk 4 t + kq);
@@ -305,7 +315,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 
   auto compute = [&](auto slot_c) {
     constexpr int slot = decltype(slot_c)::value;
-    if constexpr (FMT == FMT_W16F16) {
+    if constexpr (f16_act(FMT)) {
       // Per k-step t: the MB x NBW MFMAs of step t, with the dequantisation
       // of step t+1's weights interleaved between them (the MFMA pipe runs
       // 16 cycles per op; the 4-cycle VALU ops fill the gaps), then t+1.
@@ -320,11 +330,25 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
       auto deq = [&](int j, int t) -> u4_t {
         const u4_t x = w16_operand(braw[slot][j][t], magic_v);
         uint32_t y[4];
+        if constexpr (C::W8) {
+          // q = 16 * high + low: (high - 0) * 16 + (low - z), exact integers
+          const u4_t xl = w16_operand(braw2[slot][j][t], magic_v);
+          const h2_t m1024 = h2_t{(_Float16)-1024.f, (_Float16)-1024.f};
+          const h2_t k16 = h2_t{(_Float16)16.f, (_Float16)16.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          h2_t v = __builtin_bit_cast(h2_t, (uint32_t)x[r]);
-          v = (v + c2[j]) * s2[j];  // exact integer q - z, then one rounding
-          y[r] = __builtin_bit_cast(uint32_t, v);
+          for (int r = 0; r < 4; ++r) {
+            const h2_t vh = __builtin_bit_cast(h2_t, (uint32_t)x[r]) + m1024;
+            const h2_t vl = __builtin_bit_cast(h2_t, (uint32_t)xl[r]) + c2[j];
+            const h2_t v = (vh * k16 + vl) * s2[j];  // exact integer q - z, then one rounding
+            y[r] = __builtin_bit_cast(uint32_t, v);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            h2_t v = __builtin_bit_cast(h2_t, (uint32_t)x[r]);
+            v = (v + c2[j]) * s2[j];  // exact integer q - z, then one rounding
+            y[r] = __builtin_bit_cast(uint32_t, v);
+          }
         }
         return u4_t{y[0], y[1], y[2], y[3]};
       };
@@ -363,6 +387,41 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
           __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if constexpr (FMT == FMT_W8BF16) {
+      // q = 16 * high + low: P_h and P_l against (128 + high), (128 + low);
+      // the row sums remove 17 * 128 + z
+      u4_t bh[NBW][4], bl[NBW][4];
+      float sj[NBW], cj[NBW];
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) {
+        sj[j] = p.scale_bf16 ? bf16_bits_to_float(scale_bits(sraw[slot][j])) : f16_bits_to_float(scale_bits(sraw[slot][j]));
+        cj[j] = 17.f * 128.f + (float)zero_of(zraw[slot][j]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          bh[j][t] = w16_operand(braw[slot][j][t], magic_v);
+          bl[j][t] = w16_operand(braw2[slot][j][t], magic_v);
+        }
+      }
+      const u4_t ones = u4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) {
+        u4_t a[4];
+        read_a16(slot, mb, a);
+        f4_t rs = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) rs = mfma_16x16x32<false>(a[t], ones, rs);
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+          f4_t Ph = f4_t{0.f, 0.f, 0.f, 0.f}, Pl = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            Ph = mfma_16x16x32<false>(a[t], bh[j][t], Ph);
+            Pl = mfma_16x16x32<false>(a[t], bl[j][t], Pl);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[mb][j][r] += sj[j] * (16.f * Ph[r] + Pl[r] - cj[j] * rs[r]);
+        }
       }
     } else if constexpr (FMT == FMT_W16BF16) {
       u4_t bop[NBW][4];
@@ -483,6 +542,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
       pin(braw[cur][j]);
+      if constexpr (C::W8) pin(braw2[cur][j]);
       pin(sraw[cur][j]);
       if constexpr (!mx_weights(FMT)) pin(zraw[cur][j]);
     }
@@ -584,7 +644,7 @@ inline hipError_t launch_tiled_s(const TiledCfgRt& cfg, const TiledArgs& a, dim3
   if constexpr (GRP == GRP_DENSE) {
     if (cfg.stages == 2) return launch_tiled_t<FMT, BM, NBW, GRP, 2>(a, grid, s);
     if (cfg.stages == 4) return launch_tiled_t<FMT, BM, NBW, GRP, 4>(a, grid, s);
-    if constexpr (TCfg<FMT, BM, NBW, 5>::LDS_BYTES <= 160 * 1024 && TCfg<FMT, BM, NBW, 5>::LPS * 3 < 64)
+    if constexpr (TCfg<FMT, BM, NBW, 5>::FITS)
       if (cfg.stages == 5) return launch_tiled_t<FMT, BM, NBW, GRP, 5>(a, grid, s);
   }
   if (cfg.stages == 3 || cfg.stages == 0) return launch_tiled_t<FMT, BM, NBW, GRP, 3>(a, grid, s);
@@ -611,6 +671,6 @@ inline bool splits_cover_k(const TiledCfgRt& cfg, const TiledArgs& a, bool dense
 // (built with matrix-instruction results in accumulation registers, which
 // their epilogue-free k loop prefers); the other formats are built with the
 // results in ordinary VGPRs, which their per-group epilogues read.
-hipError_t launch_tiled_f16(int mode, const TiledCfgRt& cfg, const TiledArgs& a, dim3 grid, hipStream_t s);
+hipError_t launch_tiled_f16(int fmt, int mode, const TiledCfgRt& cfg, const TiledArgs& a, dim3 grid, hipStream_t s);
 
 }  // namespace hq

@@ -25,6 +25,16 @@ __global__ void repack_codes_kernel(const uint32_t* __restrict__ codes, uint32_t
   }
 }
 
+__global__ void repack_codes8_kernel(const uint8_t* __restrict__ codes, uint32_t* __restrict__ out, int64_t K,
+                                     int64_t words_per_expert, int64_t total_words) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total_words;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = i / words_per_expert;
+    const int64_t widx = i - e * words_per_expert;
+    out[i] = repack_word8(codes + e * words_per_expert * 4, K, widx);
+  }
+}
+
 __global__ void repack_scales_kernel(const uint16_t* __restrict__ scales, uint16_t* __restrict__ out,
                                      int64_t G, int64_t per_expert, int64_t total) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
@@ -68,10 +78,16 @@ int launch_repack(const hq_plan* p, const void* codes, const void* scales, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t N = p->layer.n, K = p->layer.k, E = p->layer.num_experts;
   const int64_t G = K / kFragK;
-  const int64_t wpe = N * K / 8;  // 32-bit words per expert (same count as canonical)
-  hipLaunchKernelGGL(repack_codes_kernel, grid_for(wpe * E), dim3(256), 0, s,
-                     static_cast<const uint32_t*>(codes), static_cast<uint32_t*>(w_out), K, p->fmt, wpe,
-                     wpe * E, wpe);
+  if (w8_weights(p->fmt)) {
+    const int64_t wpe8 = N * K / 4;  // 32-bit words per expert (one byte per weight)
+    hipLaunchKernelGGL(repack_codes8_kernel, grid_for(wpe8 * E), dim3(256), 0, s, static_cast<const uint8_t*>(codes),
+                       static_cast<uint32_t*>(w_out), K, wpe8, wpe8 * E);
+  } else {
+    const int64_t wpe = N * K / 8;  // 32-bit words per expert (same count as canonical)
+    hipLaunchKernelGGL(repack_codes_kernel, grid_for(wpe * E), dim3(256), 0, s,
+                       static_cast<const uint32_t*>(codes), static_cast<uint32_t*>(w_out), K, p->fmt, wpe,
+                       wpe * E, wpe);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return (int)err;
   uint8_t* meta = static_cast<uint8_t*>(meta_out);

@@ -84,6 +84,16 @@ def dense_w4a16(M: int, N: int, K: int, act: str = "f16", zp: str = "fixed", key
     return {"a": a, "codes": pack_u4(q), "scales": scales, "zeros": zeros, "act": act}
 
 
+def dense_w8a16(M: int, N: int, K: int, act: str = "bf16", key=(7,)):
+    """Dense W8A16 inputs: INT8 codes uniform over 0..255 (uint8 [N, K]), zero 128."""
+    rng = rng_for(*key, M, N, K)
+    dt = _dtype(act)
+    a = _to_dtype(rng.standard_normal((M, K)), dt)
+    q = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    scales = _to_dtype(rng.uniform(0.0005, 0.002, size=(N, K // GROUP)), dt)
+    return {"a": a, "codes": q, "scales": scales}
+
+
 def w4a8_mxfp4(M: int, N: int, K: int, key=(3,)):
     """W4A8-MXFP4 inputs: fp8 e4m3 per-token A, E2M1 codes, E8M0 block scales."""
     rng = rng_for(*key, M, N, K)

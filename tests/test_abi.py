@@ -407,3 +407,39 @@ def test_quantize_mxfp4_call_validation():
     assert q(4, 128, hq.BF16, None, fake, fake, None) == hq.HQ_ERR_INVALID_ARG
     assert q(4, 128, hq.BF16, fake, fake, fake + 1, None) == hq.HQ_ERR_INVALID_ARG
     assert q(0, 128, hq.BF16, None, None, None, None) == hq.HQ_OK
+
+
+def test_repack_w8_planes_operand_order():
+    """INT8 weights: per fragment a high-nibble plane then a low-nibble plane,
+    each in the 16-bit operand order, so 16 * high + low is the code."""
+    rng = np.random.default_rng(9)
+    q = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    p = _plan(N, K, hq.w8a16("f16"), max_m=16)
+    w, _ = p.repack_host(torch.from_numpy(q), torch.ones(N, K // 128, dtype=torch.float16))
+    fw = w.numpy().view(np.uint32).reshape(N // 16, K // 128, 2, 64, 4)
+    for nb in range(N // 16):
+        for g in range(K // 128):
+            for lane in range(0, 64, 5):
+                n = 16 * nb + lane % 16
+                for t in range(4):
+                    k0 = _k16(g, lane, t)
+                    for r in range(4):
+                        hi = (int(fw[nb, g, 0, lane, t]) >> (4 * r)) & 0x000F000F
+                        lo = (int(fw[nb, g, 1, lane, t]) >> (4 * r)) & 0x000F000F
+                        assert 16 * (hi & 0xF) + (lo & 0xF) == q[n, k0 + 2 * r]
+                        assert 16 * (hi >> 16) + (lo >> 16) == q[n, k0 + 2 * r + 1]
+
+
+def test_w8a16_plans_and_validation():
+    p = _plan(4096, 4096, hq.w8a16("bf16"), max_m=1024)
+    wb, mb = p.repacked_bytes()
+    assert wb == 4096 * 4096 and mb == 4096 * 32 * 2
+    assert "w8a16-bf16" in p.describe(1) and "kernel=tiled" in p.describe(1024)
+    with pytest.raises(hq.HQError):   # INT8 weights take a fixed zero point only
+        _plan(quant=hq.QuantDesc(hq.U8, 8, 128, hq.F16, hq.ZP_PER_GROUP_U4, 0, hq.F16, 0, hq.F16))
+    with pytest.raises(hq.HQError):   # zero point range
+        _plan(quant=hq.w8a16("f16", zp_value=256))
+    with pytest.raises(hq.HQError):   # dense only
+        hq.MoePlan(512, 7168, hq.w8a16("bf16"), 256, 4096, "silu_mul")
+    with pytest.raises(hq.HQError):   # U4 elements need w_bits 4
+        _plan(quant=hq.QuantDesc(hq.U4, 8, 128, hq.F16, hq.ZP_FIXED, 8, hq.F16, 0, hq.F16))
