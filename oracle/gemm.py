@@ -20,6 +20,9 @@ Readings where the pages are silent:
 * INT8 weights (WnA16 with n = 8; the pages list INT1..INT8 widths): one
   unsigned byte per weight with a fixed zero point (128 for the symmetric
   case), w = (q - z) * s with group-128 scales as for INT4.
+* INT2 weights (n = 2): 16 codes per int32 along K, code k = 16j + i in bits
+  [2i, 2i+2) of word j, a fixed zero point 0..3 (2 for the symmetric case),
+  w = (q - z) * s with group-128 scales.
 * W4A8-INT: the int32 accumulator of one group is
   P[m,n,g] = sum_{k in g} a_q[m,k] * (q[n,k] - 8), and
   C = s_a[m] * sum_g s[n,g] * P[m,n,g].
@@ -118,6 +121,39 @@ def dequant_int8(codes, scales, zero: int = 128, group: int = 128) -> np.ndarray
         ks = slice(g * group, (g + 1) * group)
         w[:, ks] = (q[:, ks] - int(zero)) * s[:, g : g + 1]
     return w
+
+
+def unpack_u2(words) -> np.ndarray:
+    """Unpack int32 words [..., K/16] into 2-bit codes [..., K]: code k = 16j + i
+    sits in bits [2i, 2i+2) of word j (low bits first)."""
+    w = np.ascontiguousarray(words).view(np.uint32)
+    out = np.empty(w.shape[:-1] + (w.shape[-1] * 16,), dtype=np.uint8)
+    for i in range(16):
+        out[..., i::16] = (w >> np.uint32(2 * i)) & np.uint32(0x3)
+    return out
+
+
+def dequant_int2(codes, scales, zero: int = 2, group: int = 128) -> np.ndarray:
+    """Exact float64 weights w[n,k] = (q[n,k] - z) * s[n,k//G] for 2-bit codes
+    (int32 [N, K/16] canonical packing), fixed zero point z in 0..3."""
+    q = unpack_u2(codes).astype(np.int64)
+    N, K = q.shape
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    s = np.asarray(scales, dtype=np.float64)
+    w = np.empty((N, K), dtype=np.float64)
+    for g in range(K // group):
+        ks = slice(g * group, (g + 1) * group)
+        w[:, ks] = (q[:, ks] - int(zero)) * s[:, g : g + 1]
+    return w
+
+
+def gemm_w2a16(a, codes, scales, zero: int = 2, group: int = 128, out_fmt: str = "f16"):
+    """Dense W2A16 (INT2 weights, one of the WnA16 widths): C = A . ((q - z) * s)^T, float64."""
+    a = np.asarray(a, dtype=np.float64)
+    w = dequant_int2(codes, scales, zero, group)
+    c64 = a @ w.T
+    return {"c64": c64, "c_out": rne(c64, out_fmt), "tau": tolerance(a, w), "w": w}
 
 
 def gemm_w8a16(a, codes, scales, zero: int = 128, group: int = 128, out_fmt: str = "f16"):

@@ -467,3 +467,36 @@ def test_int8_integer_special_case():
     r = G.gemm_w8a16(a, q, np.ones((7, 3)), 128)
     ref = a.astype(np.int64) @ (q.astype(np.int64) - 128).T
     assert np.array_equal(r["c64"], ref.astype(np.float64))
+
+
+# ------------------------------------------------------------ INT2 weights --
+
+def test_int2_unpack_and_gemm_hand_example():
+    g = _gold("int2_gemm_2x2.json")
+    words = np.array([int(h, 16) for h in g["packed_words_hex"]], dtype=np.uint32).view(np.int32).reshape(2, 1)
+    assert G.unpack_u2(words).tolist() == g["codes_rows"]
+    r = G.gemm_w2a16(np.array(g["a"], float), words, np.array(g["scales"]), g["zero"], group=g["group"])
+    assert r["c64"].tolist() == g["c"]
+
+
+def test_int2_unpack_every_value_every_position():
+    for pos in range(16):
+        for v in range(4):
+            word = np.array([[v << (2 * pos)]], dtype=np.uint32).view(np.int32)
+            q = G.unpack_u2(word)[0]
+            expect = [0] * 16
+            expect[pos] = v
+            assert q.tolist() == expect
+
+
+def test_int2_weights_agree_with_int4_on_shared_range():
+    """Codes 0..3 with zero 2 are the INT4 codes 6..9 with zero 8."""
+    rng = np.random.default_rng(33)
+    q2 = rng.integers(0, 4, size=(5, 256), dtype=np.uint8)
+    words = np.zeros((5, 16), np.uint32)
+    for i in range(16):
+        words |= (q2[:, i::16].astype(np.uint32) << np.uint32(2 * i))
+    s = rng.uniform(0.005, 0.02, size=(5, 2))
+    w2 = G.dequant_int2(words.view(np.int32), s, 2)
+    w4 = G.dequant_int4(datagen.pack_u4(q2 + 6), s, 8)
+    assert np.array_equal(w2, w4)
