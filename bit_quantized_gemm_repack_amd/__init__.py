@@ -29,7 +29,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "hq.h")
 
 # ------------------------------------------------------------------ enums --
 HQ_OK, HQ_ERR_INVALID_ARG, HQ_ERR_UNSUPPORTED, HQ_ERR_WORKSPACE, HQ_ERR_HIP, HQ_ERR_INTERNAL = range(6)
-F16, BF16, F32, FP8_E4M3, INT8, U4, FP4_E2M1, E8M0, I32, U8 = range(10)
+F16, BF16, F32, FP8_E4M3, INT8, U4, FP4_E2M1, E8M0, I32, U8, U2 = range(11)
 ZP_NONE, ZP_FIXED, ZP_PER_GROUP_U4 = range(3)
 ASCALE_NONE, ASCALE_PER_TOKEN_F32, ASCALE_MX_E8M0 = range(3)
 GEMM_DENSE, GEMM_GROUPED = range(2)
@@ -85,6 +85,12 @@ def w8a16(act: str = "f16", scale: Optional[str] = None, zp_value: int = 128, ou
     """INT8 (group 128, fixed zero point) weights x fp16/bf16 activations; codes
     are uint8 [N, K], one byte per weight."""
     return QuantDesc(U8, 8, 128, _DT[scale or act], ZP_FIXED, zp_value, _DT[act], ASCALE_NONE, _DT[out or act])
+
+
+def w2a16(act: str = "f16", scale: Optional[str] = None, zp_value: int = 2, out: Optional[str] = None) -> QuantDesc:
+    """INT2 (group 128, fixed zero point) weights x fp16/bf16 activations; codes
+    are int32 [N, K/16], sixteen 2-bit codes per word, lowest bits first."""
+    return QuantDesc(U2, 2, 128, _DT[scale or act], ZP_FIXED, zp_value, _DT[act], ASCALE_NONE, _DT[out or act])
 
 
 def w4a8_int(scale: str = "f16", out: str = "bf16") -> QuantDesc:

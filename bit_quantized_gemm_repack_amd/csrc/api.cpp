@@ -60,6 +60,18 @@ hq_status classify(const hq_quant_desc& q, int* fmt) {
     *fmt = q.act == HQ_F16 ? hq::FMT_W8F16 : hq::FMT_W8BF16;
     return HQ_OK;
   }
+  if (q.w_elem == HQ_U2) {
+    if (q.w_bits != 2) return fail(HQ_ERR_UNSUPPORTED, "U2 weights have w_bits 2 (got %d)", q.w_bits);
+    if (q.group_size != 128) return fail(HQ_ERR_UNSUPPORTED, "INT2 weights need group_size 128 (got %d)", q.group_size);
+    if (q.scale != HQ_F16 && q.scale != HQ_BF16)
+      return fail(HQ_ERR_UNSUPPORTED, "INT2 group scales must be fp16 or bf16");
+    if (q.zp != HQ_ZP_FIXED) return fail(HQ_ERR_UNSUPPORTED, "INT2 weights are implemented with a fixed zero point");
+    if (q.zp_value < 0 || q.zp_value > 3) return fail(HQ_ERR_INVALID_ARG, "INT2 fixed zero point must be 0..3");
+    if ((q.act != HQ_F16 && q.act != HQ_BF16) || q.act_scale != HQ_ASCALE_NONE)
+      return fail(HQ_ERR_UNSUPPORTED, "INT2 weights are implemented with fp16 / bf16 activations");
+    *fmt = q.act == HQ_F16 ? hq::FMT_W2F16 : hq::FMT_W2BF16;
+    return HQ_OK;
+  }
   if (q.w_bits != 4) return fail(HQ_ERR_UNSUPPORTED, "this weight element needs w_bits 4 (got %d)", q.w_bits);
   if (q.w_elem == HQ_U4) {
     if (q.group_size != 128) return fail(HQ_ERR_UNSUPPORTED, "INT4 weights need group_size 128 (got %d)", q.group_size);
@@ -116,6 +128,8 @@ const char* fmt_name(int fmt) {
     case hq::FMT_W16BF16: return "w4a16-bf16";
     case hq::FMT_W8F16: return "w8a16-f16";
     case hq::FMT_W8BF16: return "w8a16-bf16";
+    case hq::FMT_W2F16: return "w2a16-f16";
+    case hq::FMT_W2BF16: return "w2a16-bf16";
     case hq::FMT_I8: return "w4a8-int8";
     case hq::FMT_Q8: return "w4a8-fp8";
     case hq::FMT_F4: return "w4a8-mxfp4";
@@ -367,7 +381,7 @@ hq_status hq_plan_create(const hq_layer_desc* layer, const hq_compute* compute, 
     if (tuning) p->user = *tuning;
     p->fmt = fmt;
     const int64_t N = layer->n, K = layer->k, G = K / 128;
-    p->w_bytes_per_expert = (size_t)(hq::w8_weights(fmt) ? N * K : N * K / 2);
+    p->w_bytes_per_expert = (size_t)(hq::w8_weights(fmt) ? N * K : (hq::w2_weights(fmt) ? N * K / 4 : N * K / 2));
     if (hq::mx_weights(fmt)) {
       p->scale_region_bytes = 0;
       p->meta_bytes_per_expert = (size_t)(N * K / 32);
@@ -463,7 +477,12 @@ hq_status hq_repack_host(const hq_plan* p, const void* codes, const void* scales
     if (s != HQ_OK) return s;
     const int64_t N = p->layer.n, K = p->layer.k, E = p->layer.num_experts, G = K / 128;
     uint32_t* wo = static_cast<uint32_t*>(w_out);
-    if (hq::w8_weights(p->fmt)) {
+    if (hq::w2_weights(p->fmt)) {
+      const int64_t wpe2 = N * K / 16;
+      const uint32_t* cw = static_cast<const uint32_t*>(codes);
+      for (int64_t e = 0; e < E; ++e)
+        for (int64_t i = 0; i < wpe2; ++i) wo[e * wpe2 + i] = hq::repack_word2(cw + e * wpe2, K, i);
+    } else if (hq::w8_weights(p->fmt)) {
       const int64_t wpe8 = N * K / 4;
       const uint8_t* cb = static_cast<const uint8_t*>(codes);
       for (int64_t e = 0; e < E; ++e)

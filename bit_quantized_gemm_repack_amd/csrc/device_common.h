@@ -74,6 +74,15 @@ __device__ inline u4_t w16_operand(uint32_t x, uint32_t magic) {
               ((x >> 12) & 0x000F000Fu) | magic};
 }
 
+// One word of INT2 codes -> the 16-bit operand of MFMA step 2d + u (the word
+// holds steps 2d and 2d+1): register r = crumbs 4u + r (low half) and
+// 8 + 4u + r (high half), MAGIC + q exactly.
+__device__ inline u4_t w2_operand(uint32_t x, uint32_t magic, int u) {
+  const uint32_t y = x >> (8 * u);
+  return u4_t{(y & 0x00030003u) | magic, ((y >> 2) & 0x00030003u) | magic, ((y >> 4) & 0x00030003u) | magic,
+              ((y >> 6) & 0x00030003u) | magic};
+}
+
 // Two words of NIB_B8 codes stored as q ^ 8 -> the int8 operand (16 values)
 // holding 16 * (q - 8) exactly.
 __device__ inline i4_t i8_operand(uint32_t w0, uint32_t w1) {

@@ -65,7 +65,9 @@ enum Fmt : int {
   FMT_F4 = 4,      // MXFP4 weight, fp8 activation, scaled fp8 x fp4 MFMA
   FMT_F44 = 5,     // MXFP4 weight, MXFP4 activation, scaled fp4 x fp4 MFMA
   FMT_W8F16 = 6,   // INT8 weight, fp16 activation (two 4-bit planes), fp16 MFMA
-  FMT_W8BF16 = 7   // INT8 weight, bf16 activation (two 4-bit planes), bf16 MFMA
+  FMT_W8BF16 = 7,  // INT8 weight, bf16 activation (two 4-bit planes), bf16 MFMA
+  FMT_W2F16 = 8,   // INT2 weight, fp16 activation, fp16 MFMA
+  FMT_W2BF16 = 9   // INT2 weight, bf16 activation, bf16 MFMA
 };
 
 // INT8 weights: stored as two 4-bit planes (high nibbles, then low nibbles)
@@ -73,11 +75,14 @@ enum Fmt : int {
 // operands like an INT4 weight and q = 16 * high + low.
 HQ_HD constexpr inline bool w8_weights(int fmt) { return fmt == FMT_W8F16 || fmt == FMT_W8BF16; }
 // fp16 / bf16 activations (INT4 or INT8 weights)
+// INT2 weights: 512-byte fragments, 8 bytes per lane, 16 codes per word.
+HQ_HD constexpr inline bool w2_weights(int fmt) { return fmt == FMT_W2F16 || fmt == FMT_W2BF16; }
 HQ_HD constexpr inline bool act16_fmt(int fmt) {
-  return fmt == FMT_W16F16 || fmt == FMT_W16BF16 || fmt == FMT_W8F16 || fmt == FMT_W8BF16;
+  return fmt == FMT_W16F16 || fmt == FMT_W16BF16 || fmt == FMT_W8F16 || fmt == FMT_W8BF16 || fmt == FMT_W2F16 ||
+         fmt == FMT_W2BF16;
 }
 // fp16 (rather than bf16) activations
-HQ_HD constexpr inline bool f16_act(int fmt) { return fmt == FMT_W16F16 || fmt == FMT_W8F16; }
+HQ_HD constexpr inline bool f16_act(int fmt) { return fmt == FMT_W16F16 || fmt == FMT_W8F16 || fmt == FMT_W2F16; }
 
 // MXFP4 weights (E2M1 codes in natural order + E8M0 block scales).
 HQ_HD constexpr inline bool mx_weights(int fmt) { return fmt == FMT_F4 || fmt == FMT_F44; }
@@ -143,6 +148,29 @@ HQ_HD inline uint32_t repack_word8(const uint8_t* codes, int64_t K, int64_t widx
   for (int p = 0; p < 8; ++p) {
     const uint32_t q = codes[n * K + kbase + nib_koff(NIB_W16, p)];
     w |= (plane == 0 ? (q >> 4) : (q & 0xFu)) << (4 * p);
+  }
+  return w;
+}
+
+// One 32-bit word of the INT2 device layout (512-byte fragments, two words
+// per lane): word d of lane l holds the 16 codes of MFMA steps 2d and 2d+1;
+// crumb 4u + r (u = 0, 1; r = 0..3) is element 2r of step 2d + u and crumb
+// 8 + 4u + r element 2r + 1, so that (w >> 2(4u + r)) & 0x00030003 is operand
+// register r of step 2d + u.  Canonical int32 [N][K/16], low bits first.
+HQ_HD inline uint32_t repack_word2(const uint32_t* codes, int64_t K, int64_t widx) {
+  const int64_t G = K / kFragK;
+  const int d = (int)(widx & 1);
+  const int lane = (int)((widx >> 1) & 63);
+  const int64_t frag = widx >> 7;
+  const int64_t g = frag % G;
+  const int64_t nb = frag / G;
+  const int64_t n = nb * kFragN + (lane & 15);
+  uint32_t w = 0;
+  for (int p = 0; p < 16; ++p) {
+    const int hi = p >> 3, u = (p >> 2) & 1, r = p & 3;
+    const int64_t k = g * kFragK + 32 * (2 * d + u) + 8 * (lane >> 4) + 2 * r + hi;
+    const uint32_t q = (codes[n * (K / 16) + (k >> 4)] >> (2 * (k & 15))) & 0x3u;
+    w |= q << (2 * p);
   }
   return w;
 }

@@ -45,6 +45,7 @@ template <int FMT>
 struct FmtInfo {
   static constexpr bool kAct16 = act16_fmt(FMT);
   static constexpr bool kW8 = w8_weights(FMT);  // INT8 weights: a second (low-nibble) plane
+  static constexpr bool kW2 = w2_weights(FMT);  // INT2 weights: 8 bytes per lane per fragment
   static constexpr bool kAct4 = (FMT == FMT_F44);  // MXFP4 activations
   static constexpr int kAVec = kAct16 ? 4 : (kAct4 ? 1 : 2);  // 16-byte loads per lane per group
   static constexpr int kARowB = kAct16 ? 256 : (kAct4 ? 64 : 128);  // A bytes per row per group
@@ -143,7 +144,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   const int a_rows = (GRP == GRP_GATHER) ? p.n_slots / p.topk : p.M;
   const auto ra = rsrc(p.a, (int64_t)a_rows * a_rowb);
   const int64_t nfrag = (int64_t)(p.N / 16) * G;
-  constexpr int kFragB = FI::kW8 ? 2048 : 1024;  // weight bytes per 16 x 128 fragment
+  constexpr int kFragB = FI::kW8 ? 2048 : (FI::kW2 ? 512 : 1024);  // weight bytes per 16 x 128 fragment
   const auto rw = rsrc(wbytes, nfrag * kFragB);
   [[maybe_unused]] const auto rsc = rsrc(scales16, nfrag * 32);
   [[maybe_unused]] const auto rz = rsrc(zeros32 ? static_cast<const void*>(zeros32) : static_cast<const void*>(scales16),
@@ -175,7 +176,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int f0 = nblk(nb) * G;
-    woff[nb] = f0 * kFragB + lane * 16;
+    woff[nb] = f0 * kFragB + lane * (FI::kW2 ? 8 : 16);
     soff[nb] = mx_weights(FMT) ? f0 * 64 + (lane & ~3) : f0 * 32 + (c >> 1) * 4;
     zoff[nb] = f0 * 8 + (c >> 3) * 4;
   }
@@ -183,7 +184,12 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   auto load = [&](Stage<FMT, MB, NB>& st, int g) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      st.b[nb] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[nb], g * kFragB, 2));
+      if constexpr (FI::kW2) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rw, woff[nb], g * kFragB, 2);
+        st.b[nb] = u4_t{(uint32_t)v[0], (uint32_t)v[1], 0u, 0u};
+      } else {
+        st.b[nb] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[nb], g * kFragB, 2));
+      }
     if constexpr (FI::kW8) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
@@ -291,9 +297,14 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
         for (int mb = 0; mb < MB; ++mb) P[mb] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const uint32_t x = w[t];
-          const u4_t bop = u4_t{(x & 0x000F000Fu) | magic, ((x >> 4) & 0x000F000Fu) | magic,
-                                ((x >> 8) & 0x000F000Fu) | magic, ((x >> 12) & 0x000F000Fu) | magic};
+          u4_t bop;
+          if constexpr (FI::kW2) {
+            bop = w2_operand(w[t >> 1], magic, t & 1);
+          } else {
+            const uint32_t x = w[t];
+            bop = u4_t{(x & 0x000F000Fu) | magic, ((x >> 4) & 0x000F000Fu) | magic, ((x >> 8) & 0x000F000Fu) | magic,
+                       ((x >> 12) & 0x000F000Fu) | magic};
+          }
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) P[mb] = mfma16<FMT>(st.a[mb][t], bop, P[mb]);
         }
@@ -556,6 +567,8 @@ int launch_skinny(int fmt, const SkinnyCfg& cfg, const SkinnyArgs& a, void* stre
     case FMT_W16BF16: return (int)launch_mb<FMT_W16BF16>(cfg, a, grid, block, lds, s);
     case FMT_W8F16: return (int)launch_mb<FMT_W8F16>(cfg, a, grid, block, lds, s);
     case FMT_W8BF16: return (int)launch_mb<FMT_W8BF16>(cfg, a, grid, block, lds, s);
+    case FMT_W2F16: return (int)launch_mb<FMT_W2F16>(cfg, a, grid, block, lds, s);
+    case FMT_W2BF16: return (int)launch_mb<FMT_W2BF16>(cfg, a, grid, block, lds, s);
     case FMT_I8: return (int)launch_mb<FMT_I8>(cfg, a, grid, block, lds, s);
     case FMT_Q8: return (int)launch_mb<FMT_Q8>(cfg, a, grid, block, lds, s);
     case FMT_F4: return (int)launch_mb<FMT_F4>(cfg, a, grid, block, lds, s);

@@ -10,9 +10,11 @@ int launch_tiled(int fmt, const TiledCfgRt& cfg, const TiledArgs& a, void* strea
   const dim3 grid((unsigned)(a.tiles_m * a.tiles_n), (unsigned)(a.part ? cfg.split : 1));
   switch (fmt) {
     case FMT_W16F16:
-    case FMT_W8F16: return (int)launch_tiled_f16(fmt, GRP_DENSE, cfg, a, grid, s);
+    case FMT_W8F16:
+    case FMT_W2F16: return (int)launch_tiled_f16(fmt, GRP_DENSE, cfg, a, grid, s);
     case FMT_W16BF16: return (int)launch_tiled_f<FMT_W16BF16, GRP_DENSE>(cfg, a, grid, s);
     case FMT_W8BF16: return (int)launch_tiled_f<FMT_W8BF16, GRP_DENSE>(cfg, a, grid, s);
+    case FMT_W2BF16: return (int)launch_tiled_f<FMT_W2BF16, GRP_DENSE>(cfg, a, grid, s);
     case FMT_I8: return (int)launch_tiled_f<FMT_I8, GRP_DENSE>(cfg, a, grid, s);
     case FMT_Q8: return (int)launch_tiled_f<FMT_Q8, GRP_DENSE>(cfg, a, grid, s);
     case FMT_F4: return (int)launch_tiled_f<FMT_F4, GRP_DENSE>(cfg, a, grid, s);

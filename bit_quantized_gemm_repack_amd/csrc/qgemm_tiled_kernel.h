@@ -58,7 +58,8 @@ struct TCfg {
   static constexpr int MB = BM / 16;
   static constexpr bool ACT16 = act16_fmt(FMT);
   static constexpr bool W8 = w8_weights(FMT);  // INT8 weights: two 1 KiB planes per fragment
-  static constexpr int FRAGB = W8 ? 2048 : 1024;
+  static constexpr bool W2 = w2_weights(FMT);  // INT2 weights: 512-byte fragments, 8 bytes per lane
+  static constexpr int FRAGB = W8 ? 2048 : (W2 ? 512 : 1024);
   static constexpr bool ACT4 = (FMT == FMT_F44);  // MXFP4 activations
   static constexpr int ROWB = ACT16 ? 256 : (ACT4 ? 64 : 128);  // A bytes per row per group
   static constexpr int CHUNKS = ROWB / 16;        // 16-byte chunks per row
@@ -230,7 +231,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
     const int f0 = nblk(j) * G;  // first fragment of this column block
-    woff[j] = f0 * C::FRAGB + lane * 16;
+    woff[j] = f0 * C::FRAGB + lane * (C::W2 ? 8 : 16);
     soff[j] = mx_weights(FMT) ? f0 * 64 + (lane & ~3) : f0 * 32 + (c16 >> 1) * 4;
     zoff[j] = f0 * 8 + (c16 >> 3) * 4;
   }
@@ -252,8 +253,14 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
                                                gg * C::ROWB, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < NBW; ++j)
-      braw[slot][j] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[j], gg * C::FRAGB, 2));
+    for (int j = 0; j < NBW; ++j) {
+      if constexpr (C::W2) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rw, woff[j], gg * C::FRAGB, 2);
+        braw[slot][j] = u4_t{(uint32_t)v[0], (uint32_t)v[1], 0u, 0u};
+      } else {
+        braw[slot][j] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[j], gg * C::FRAGB, 2));
+      }
+    }
     if constexpr (C::W8) {
 #pragma unroll
       for (int j = 0; j < NBW; ++j)
@@ -328,7 +335,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
         c2[j] = h2_t{cz, cz};
       }
       auto deq = [&](int j, int t) -> u4_t {
-        const u4_t x = w16_operand(braw[slot][j][t], magic_v);
+        const u4_t x = C::W2 ? w2_operand(braw[slot][j][t >> 1], magic_v, t & 1) : w16_operand(braw[slot][j][t], magic_v);
         uint32_t y[4];
         if constexpr (C::W8) {
           // q = 16 * high + low: (high - 0) * 16 + (low - z), exact integers
@@ -423,7 +430,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
           for (int r = 0; r < 4; ++r) acc[mb][j][r] += sj[j] * (16.f * Ph[r] + Pl[r] - cj[j] * rs[r]);
         }
       }
-    } else if constexpr (FMT == FMT_W16BF16) {
+    } else if constexpr (FMT == FMT_W16BF16 || FMT == FMT_W2BF16) {
       u4_t bop[NBW][4];
       float sj[NBW], cj[NBW];
 #pragma unroll
@@ -431,7 +438,8 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
         sj[j] = p.scale_bf16 ? bf16_bits_to_float(scale_bits(sraw[slot][j])) : f16_bits_to_float(scale_bits(sraw[slot][j]));
         cj[j] = 128.f + (float)zero_of(zraw[slot][j]);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) bop[j][t] = w16_operand(braw[slot][j][t], magic_v);
+        for (int t = 0; t < 4; ++t)
+          bop[j][t] = C::W2 ? w2_operand(braw[slot][j][t >> 1], magic_v, t & 1) : w16_operand(braw[slot][j][t], magic_v);
       }
       const u4_t ones = u4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 #pragma unroll

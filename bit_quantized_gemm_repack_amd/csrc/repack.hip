@@ -35,6 +35,16 @@ __global__ void repack_codes8_kernel(const uint8_t* __restrict__ codes, uint32_t
   }
 }
 
+__global__ void repack_codes2_kernel(const uint32_t* __restrict__ codes, uint32_t* __restrict__ out, int64_t K,
+                                     int64_t words_per_expert, int64_t total_words) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total_words;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = i / words_per_expert;
+    const int64_t widx = i - e * words_per_expert;
+    out[i] = repack_word2(codes + e * words_per_expert, K, widx);
+  }
+}
+
 __global__ void repack_scales_kernel(const uint16_t* __restrict__ scales, uint16_t* __restrict__ out,
                                      int64_t G, int64_t per_expert, int64_t total) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
@@ -78,7 +88,11 @@ int launch_repack(const hq_plan* p, const void* codes, const void* scales, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t N = p->layer.n, K = p->layer.k, E = p->layer.num_experts;
   const int64_t G = K / kFragK;
-  if (w8_weights(p->fmt)) {
+  if (w2_weights(p->fmt)) {
+    const int64_t wpe2 = N * K / 16;  // 32-bit words per expert (same count as canonical)
+    hipLaunchKernelGGL(repack_codes2_kernel, grid_for(wpe2 * E), dim3(256), 0, s, static_cast<const uint32_t*>(codes),
+                       static_cast<uint32_t*>(w_out), K, wpe2, wpe2 * E);
+  } else if (w8_weights(p->fmt)) {
     const int64_t wpe8 = N * K / 4;  // 32-bit words per expert (one byte per weight)
     hipLaunchKernelGGL(repack_codes8_kernel, grid_for(wpe8 * E), dim3(256), 0, s, static_cast<const uint8_t*>(codes),
                        static_cast<uint32_t*>(w_out), K, wpe8, wpe8 * E);

@@ -22,6 +22,7 @@ import torch
 import bit_quantized_gemm_repack_amd as hq
 import datagen
 from oracle.formats import unpack_u4
+from oracle.gemm import unpack_u2
 
 
 def _plan(n=256, k=512, quant=None, max_m=64, epi="none", tuning=None):
@@ -443,3 +444,44 @@ def test_w8a16_plans_and_validation():
         hq.MoePlan(512, 7168, hq.w8a16("bf16"), 256, 4096, "silu_mul")
     with pytest.raises(hq.HQError):   # U4 elements need w_bits 4
         _plan(quant=hq.QuantDesc(hq.U4, 8, 128, hq.F16, hq.ZP_FIXED, 8, hq.F16, 0, hq.F16))
+
+
+def test_repack_w2_operand_order():
+    """INT2 weights: 512-byte fragments, two words per lane; word d holds MFMA
+    steps 2d and 2d + 1, and (word >> 2 (4u + r)) & 0x00030003 is operand
+    register r of step 2d + u (elements 2r and 2r + 1 of the lane's 8)."""
+    rng = np.random.default_rng(10)
+    words = rng.integers(0, 1 << 32, size=(N, K // 16), dtype=np.uint64).astype(np.uint32).view(np.int32)
+    q = unpack_u2(words)
+    p = _plan(N, K, hq.w2a16("f16"), max_m=16)
+    w, _ = p.repack_host(torch.from_numpy(words), torch.ones(N, K // 128, dtype=torch.float16))
+    assert w.numel() == N * K // 4
+    fw = w.numpy().view(np.uint32).reshape(N // 16, K // 128, 64, 2)
+    for nb in range(N // 16):
+        for g in range(K // 128):
+            for lane in range(0, 64, 3):
+                n = 16 * nb + lane % 16
+                for t in range(4):
+                    k0 = _k16(g, lane, t)
+                    y = int(fw[nb, g, lane, t >> 1]) >> (8 * (t & 1))
+                    for r in range(4):
+                        v = (y >> (2 * r)) & 0x00030003
+                        assert (v & 0x3) == q[n, k0 + 2 * r]
+                        assert (v >> 16) == q[n, k0 + 2 * r + 1]
+
+
+def test_w2a16_plans_and_validation():
+    p = _plan(4096, 4096, hq.w2a16("bf16"), max_m=1024)
+    wb, mb = p.repacked_bytes()
+    assert wb == 4096 * 4096 // 4 and mb == 4096 * 32 * 2
+    assert "w2a16-bf16" in p.describe(1) and "kernel=tiled" in p.describe(1024)
+    with pytest.raises(hq.HQError):   # fixed zero point only
+        _plan(quant=hq.QuantDesc(hq.U2, 2, 128, hq.F16, hq.ZP_PER_GROUP_U4, 0, hq.F16, 0, hq.F16))
+    with pytest.raises(hq.HQError):   # zero point range
+        _plan(quant=hq.w2a16("f16", zp_value=4))
+    with pytest.raises(hq.HQError):   # group 128 only
+        _plan(quant=hq.QuantDesc(hq.U2, 2, 64, hq.F16, hq.ZP_FIXED, 2, hq.F16, 0, hq.F16))
+    with pytest.raises(hq.HQError):   # U2 elements need w_bits 2
+        _plan(quant=hq.QuantDesc(hq.U2, 4, 128, hq.F16, hq.ZP_FIXED, 2, hq.F16, 0, hq.F16))
+    with pytest.raises(hq.HQError):   # dense only
+        hq.MoePlan(512, 7168, hq.w2a16("bf16"), 256, 4096, "silu_mul")
