@@ -166,13 +166,21 @@ Exec choose_exec(const hq_plan* p, int64_t m) {
   const bool tiled_auto = m > 32;
   if (tiled_ok && (u.kernel == KER_TILED || (u.kernel == 0 && tiled_auto))) {
     e.kernel = KER_TILED;
-    // tile shapes from a sweep on MI355X (N = 4096..8192): 16-bit activations
-    // 128 x 256 at m >= 512; MXFP4 128 x 128 with a 4-group pipeline; int8
-    // and fp8 x INT4 64 x 128 with a 2-group pipeline
+    // Tile shapes from sweeps on MI355X (N = 4096..16384, K = 2048..8192):
+    //   16-bit activations (INT2 / INT4 / INT8 weights): 128-row tiles from
+    //   256 rows on; fp16 128 x 256 where that still gives 192 tiles, else
+    //   128 x 128, with a 3-group pipeline; bf16 128 x 128 with a 2-group
+    //   pipeline;
+    //   MXFP4 weights x 8/4-bit activations 128 x 128 with a 4-group
+    //   pipeline; int8 and fp8 x INT4 64 x 128 with a 2-group pipeline.
     const bool act16 = act16_fmt(p->fmt);
-    e.tl.bm = m >= 512 ? 128 : 64;
-    e.tl.nbw = (N % 256 == 0 && m >= 512 && f16_act(p->fmt)) ? 4 : 2;
+    e.tl.bm = (m >= 512 || (act16 && m >= 256)) ? 128 : 64;
+    e.tl.nbw = 2;
     int stages = 3;
+    if (act16) {
+      if (f16_act(p->fmt)) e.tl.nbw = (m >= 512 && N % 256 == 0 && cdiv(mm, 128) * (N / 256) >= 192) ? 4 : 2;
+      else stages = 2;
+    }
     if (!act16 && m >= 512) {
       if (mx_weights(p->fmt)) {
         stages = 4;
@@ -191,6 +199,12 @@ Exec choose_exec(const hq_plan* p, int64_t m) {
     const int64_t tiles = e.tiles_m * e.tiles_n;
     if (u.split_k) split = u.split_k;
     else if (tiles > 0 && tiles < 256) split = std::min<int64_t>(cdiv(256, tiles), std::max<int64_t>(1, G / 2));
+    if (!u.split_k && act16) {
+      // 16-bit activations: no split from 192 tiles on, else a power of two
+      // (an even share of the groups per split)
+      if (tiles >= 192) split = 1;
+      while (split & (split - 1)) split &= split - 1;
+    }
     split = std::max<int64_t>(1, std::min<int64_t>(split, G));
     split = cdiv(G, cdiv(G, split));  // no empty split
     e.tl.split = (int)split;
@@ -220,7 +234,15 @@ Exec choose_exec(const hq_plan* p, int64_t m) {
   // column-block workgroup; 4 column blocks per workgroup cut that 4x, and
   // a 4-way K split keeps 4x the workgroups (partials summed by the reduce).
   int64_t auto_split = 1;
-  if (c.mb == 1 && m > 4 && G >= 64 && N % 64 == 0 && N / 64 >= 32) {
+  if (w8_weights(p->fmt) || w2_weights(p->fmt)) {
+    // INT8 / INT2 weights (a sweep at N = 4096..16384): two column blocks per
+    // workgroup from 384 column blocks on, four from 1024 on (INT8: for 5..16
+    // rows only), no K split
+    if (c.mb == 1) {
+      c.nb = (N / 16 >= 384 && N % 32 == 0) ? 2 : 1;
+      if (N / 16 >= 1024 && N % 64 == 0 && (w2_weights(p->fmt) || m > 4)) c.nb = 4;
+    }
+  } else if (c.mb == 1 && m > 4 && G >= 64 && N % 64 == 0 && N / 64 >= 32) {
     c.nb = 4;
     auto_split = 4;
   }
