@@ -23,6 +23,11 @@ Readings where the pages are silent:
 * INT2 weights (n = 2): 16 codes per int32 along K, code k = 16j + i in bits
   [2i, 2i+2) of word j, a fixed zero point 0..3 (2 for the symmetric case),
   w = (q - z) * s with group-128 scales.
+* INT3 weights (n = 3; GPTQ INT3 is the named case): the dense 3-bit packing
+  along K, 32 codes per 3 int32 words, code k in bits [3k, 3k+3) of the row's
+  little-endian bit stream (so codes 10 and 21 of every 32 straddle two
+  words), a fixed zero point 0..7 (4 for the symmetric case),
+  w = (q - z) * s with group-128 scales.
 * W4A8-INT: the int32 accumulator of one group is
   P[m,n,g] = sum_{k in g} a_q[m,k] * (q[n,k] - 8), and
   C = s_a[m] * sum_g s[n,g] * P[m,n,g].
@@ -146,6 +151,45 @@ def dequant_int2(codes, scales, zero: int = 2, group: int = 128) -> np.ndarray:
         ks = slice(g * group, (g + 1) * group)
         w[:, ks] = (q[:, ks] - int(zero)) * s[:, g : g + 1]
     return w
+
+
+def unpack_u3(words) -> np.ndarray:
+    """Unpack int32 words [..., 3K/32] into 3-bit codes [..., K].  The words of a
+    row form one little-endian bit stream (word j holds stream bits [32j, 32j+32),
+    lowest first) and code k is the 3-bit number at stream bits [3k, 3k+3), so
+    32 codes fill 3 words and some codes straddle two words: the dense 3-bit
+    packing along K of GPTQ INT3 checkpoints."""
+    w = np.ascontiguousarray(words).view(np.uint32)
+    if w.shape[-1] % 3:
+        raise ValueError("INT3 rows hold a multiple of 3 words (32 codes per 3 words)")
+    le = np.ascontiguousarray(w.astype("<u4")).view(np.uint8)  # bytes in stream order
+    bits = np.unpackbits(le, axis=-1, bitorder="little")  # stream bit b at index b
+    K = bits.shape[-1] // 3
+    b = bits.reshape(w.shape[:-1] + (K, 3))
+    return (b[..., 0] | (b[..., 1] << 1) | (b[..., 2] << 2)).astype(np.uint8)
+
+
+def dequant_int3(codes, scales, zero: int = 4, group: int = 128) -> np.ndarray:
+    """Exact float64 weights w[n,k] = (q[n,k] - z) * s[n,k//G] for 3-bit codes
+    (int32 [N, 3K/32] bit-stream packing), fixed zero point z in 0..7."""
+    q = unpack_u3(codes).astype(np.int64)
+    N, K = q.shape
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    s = np.asarray(scales, dtype=np.float64)
+    w = np.empty((N, K), dtype=np.float64)
+    for g in range(K // group):
+        ks = slice(g * group, (g + 1) * group)
+        w[:, ks] = (q[:, ks] - int(zero)) * s[:, g : g + 1]
+    return w
+
+
+def gemm_w3a16(a, codes, scales, zero: int = 4, group: int = 128, out_fmt: str = "f16"):
+    """Dense W3A16 (INT3 weights, one of the WnA16 widths): C = A . ((q - z) * s)^T, float64."""
+    a = np.asarray(a, dtype=np.float64)
+    w = dequant_int3(codes, scales, zero, group)
+    c64 = a @ w.T
+    return {"c64": c64, "c_out": rne(c64, out_fmt), "tau": tolerance(a, w), "w": w}
 
 
 def gemm_w2a16(a, codes, scales, zero: int = 2, group: int = 128, out_fmt: str = "f16"):

@@ -500,3 +500,48 @@ def test_int2_weights_agree_with_int4_on_shared_range():
     w2 = G.dequant_int2(words.view(np.int32), s, 2)
     w4 = G.dequant_int4(datagen.pack_u4(q2 + 6), s, 8)
     assert np.array_equal(w2, w4)
+
+
+# ------------------------------------------------------------ INT3 weights --
+
+def test_int3_unpack_and_gemm_hand_example():
+    g = _gold("int3_gemm_2x2.json")
+    words = np.array([[int(h, 16) for h in row] for row in g["packed_words_hex"]], dtype=np.uint32).view(np.int32)
+    assert G.unpack_u3(words).tolist() == g["codes_rows"]
+    r = G.gemm_w3a16(np.array(g["a"], float), words, np.array(g["scales"]), g["zero"], group=g["group"])
+    assert r["c64"].tolist() == g["c"]
+
+
+def _stream_words(rows):
+    """Test-side packer: each row of 3-bit codes as one Python integer bit
+    stream, cut into 32-bit words (lowest first)."""
+    out = []
+    for codes in rows:
+        v = 0
+        for k, q in enumerate(codes):
+            v |= int(q) << (3 * k)
+        out.append([(v >> (32 * j)) & 0xFFFFFFFF for j in range(len(codes) * 3 // 32)])
+    return np.array(out, dtype=np.uint32).view(np.int32)
+
+
+def test_int3_unpack_every_value_every_position():
+    """Each of the 8 values at each of the 32 positions of a 3-word group,
+    including the straddling positions 10 and 21."""
+    for pos in range(32):
+        for v in range(8):
+            words = np.array([[((v << (3 * pos)) >> (32 * j)) & 0xFFFFFFFF for j in range(3)]],
+                             dtype=np.uint32).view(np.int32)
+            q = G.unpack_u3(words)[0]
+            expect = [0] * 32
+            expect[pos] = v
+            assert q.tolist() == expect
+
+
+def test_int3_weights_agree_with_int4_on_shared_range():
+    """Codes 0..7 with zero 4 are the INT4 codes 4..11 with zero 8."""
+    rng = np.random.default_rng(34)
+    q3 = rng.integers(0, 8, size=(5, 256), dtype=np.uint8)
+    s = rng.uniform(0.005, 0.02, size=(5, 2))
+    w3 = G.dequant_int3(_stream_words(q3), s, 4)
+    w4 = G.dequant_int4(datagen.pack_u4(q3 + 4), s, 8)
+    assert np.array_equal(w3, w4)
