@@ -234,6 +234,7 @@ _WORKLOAD_PROFILES = {
              "MXFP4 x MXFP4"),
     "w8a16": ("qgemm_w8a16_bf16_n4096_k4096.md", "dense W8A16, M in {1,16,64,1024}, N = K = 4096, bf16"),
     "w2a16": ("qgemm_w2a16_bf16_n4096_k4096.md", "dense W2A16, M in {1,16,64,1024}, N = K = 4096, bf16"),
+    "w3a16": ("qgemm_w3a16_bf16_n4096_k4096.md", "dense W3A16, M in {1,16,64,1024}, N = K = 4096, bf16"),
     "moe": ("moe_layer_e256_top8_h7168_i256.md", "MoE layer, 256 experts, top-8, hidden 7168, intermediate 256, "
             "T in {1,32,512,4096}, bf16 and fp8 activations"),
 }
@@ -631,29 +632,30 @@ def _w8a16_points(dev):
         "zero point 128), bf16 output", "bf16"
 
 
-def _w2a16_points(dev):
+def _w2a16_points(dev, bits=2):
     import bit_quantized_gemm_repack_amd as hq
     import datagen
 
     N = K = 4096
+    gen, desc, zp = {2: (datagen.dense_w2a16, hq.w2a16, 2), 3: (datagen.dense_w3a16, hq.w3a16, 4)}[bits]
     pts = []
     for M in (1, 16, 64, 1024):
-        d = datagen.dense_w2a16(M, N, K, act="bf16")
-        plan = hq.Plan(N, K, hq.w2a16("bf16"), max_m=M)
+        d = gen(M, N, K, act="bf16")
+        plan = hq.Plan(N, K, desc("bf16"), max_m=M)
         w, meta = plan.repack(torch.from_numpy(d["codes"]).to(dev), d["scales"].to(dev))
-        R = 200  # 200 copies of 5 MB: > 1 GB
+        R = 200  # 200 copies of >= 5 MB: > 1 GB
         ws_ = [(w.clone(), meta.clone()) for _ in range(R)]
         a = d["a"].to(dev)
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         ws = plan.workspace(M, dev)
-        byt = N * K // 4 + 2 * N * (K // 128) + 2 * M * K + 2 * M * N
+        byt = N * K * bits // 8 + 2 * N * (K // 128) + 2 * M * K + 2 * M * N
         pts.append(dict(name=f"M={M} N={N} K={K}", R=R, bytes=byt, flops=2 * M * N * K, peak=FP16_PEAK_TFLOPS,
                         plan=plan.describe(M),
                         calls=lambda r, plan=plan, ws_=ws_, a=a, out=out, ws=ws:
                         [lambda: plan.gemm(a, ws_[r][0], ws_[r][1], out=out, ws=ws)]))
-    return pts, "quantized GEMM TFLOPS and effective HBM GB/s vs M (W2A16)", \
-        "dense W2A16: M in {1,16,64,1024}, N = K = 4096, bf16 activations, INT2 weights (group 128, bf16 scales, " \
-        "zero point 2), bf16 output", "bf16"
+    return pts, f"quantized GEMM TFLOPS and effective HBM GB/s vs M (W{bits}A16)", \
+        f"dense W{bits}A16: M in {{1,16,64,1024}}, N = K = 4096, bf16 activations, INT{bits} weights (group 128, " \
+        f"bf16 scales, zero point {zp}), bf16 output", "bf16"
 
 
 def _w4a4_points(dev):
@@ -872,6 +874,12 @@ def _cpu_sample(workload, budget):
             t0 = time.perf_counter()
             og.gemm_w2a16(d["a"].double().numpy(), d["codes"], d["scales"].double().numpy(), 2, out_fmt="bf16")
             what = "dense W2A16 M=8 N=K=4096"
+        elif workload == "w3a16":
+            M, N, K = 8, 4096, 4096
+            d = datagen.dense_w3a16(M, N, K, act="bf16")
+            t0 = time.perf_counter()
+            og.gemm_w3a16(d["a"].double().numpy(), d["codes"], d["scales"].double().numpy(), 4, out_fmt="bf16")
+            what = "dense W3A16 M=8 N=K=4096"
         elif workload == "w4a4":
             M, N, K = 16, 4096, 7168
             d = datagen.w4a4_mxfp4(M, N, K)
@@ -917,10 +925,10 @@ def main():
     ap.add_argument("--rotations", type=int, default=4)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--workload", choices=("decode", "quant", "prefill", "w4a8", "w4a4", "w8a16", "w2a16", "moe"),
+    ap.add_argument("--workload", choices=("decode", "quant", "prefill", "w4a8", "w4a4", "w8a16", "w2a16", "w3a16", "moe"),
                     default="decode",
                     help="decode: the dense W4A16 decode sweep (default); quant: the per-token quantiser; "
-                         "prefill / w4a8 / w4a4 / w8a16 / w2a16 / moe: the other GEMM workloads")
+                         "prefill / w4a8 / w4a4 / w8a16 / w2a16 / w3a16 / moe: the other GEMM workloads")
     ap.add_argument("--write-profiles", metavar="RUN_DIR",
                     help="CPU only: write the profiles/ summaries from rocprofv3 outputs in RUN_DIR and exit")
     args = ap.parse_args()
@@ -934,9 +942,10 @@ def main():
     if args.workload == "quant":
         run_quant(args)
         return
-    if args.workload in ("prefill", "w4a8", "w4a4", "w8a16", "w2a16", "moe"):
+    if args.workload in ("prefill", "w4a8", "w4a4", "w8a16", "w2a16", "w3a16", "moe"):
         run_points_workload(args, {"prefill": _prefill_points, "w4a8": _w4a8_points, "w4a4": _w4a4_points,
-                                   "w8a16": _w8a16_points, "w2a16": _w2a16_points, "moe": _moe_points}[args.workload])
+                                   "w8a16": _w8a16_points, "w2a16": _w2a16_points,
+                                   "w3a16": lambda dev: _w2a16_points(dev, 3), "moe": _moe_points}[args.workload])
         return
 
     import bit_quantized_gemm_repack_amd as hq

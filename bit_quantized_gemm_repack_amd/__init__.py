@@ -29,7 +29,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "hq.h")
 
 # ------------------------------------------------------------------ enums --
 HQ_OK, HQ_ERR_INVALID_ARG, HQ_ERR_UNSUPPORTED, HQ_ERR_WORKSPACE, HQ_ERR_HIP, HQ_ERR_INTERNAL = range(6)
-F16, BF16, F32, FP8_E4M3, INT8, U4, FP4_E2M1, E8M0, I32, U8, U2 = range(11)
+F16, BF16, F32, FP8_E4M3, INT8, U4, FP4_E2M1, E8M0, I32, U8, U2, U3 = range(12)
 ZP_NONE, ZP_FIXED, ZP_PER_GROUP_U4 = range(3)
 ASCALE_NONE, ASCALE_PER_TOKEN_F32, ASCALE_MX_E8M0 = range(3)
 GEMM_DENSE, GEMM_GROUPED = range(2)
@@ -91,6 +91,13 @@ def w2a16(act: str = "f16", scale: Optional[str] = None, zp_value: int = 2, out:
     """INT2 (group 128, fixed zero point) weights x fp16/bf16 activations; codes
     are int32 [N, K/16], sixteen 2-bit codes per word, lowest bits first."""
     return QuantDesc(U2, 2, 128, _DT[scale or act], ZP_FIXED, zp_value, _DT[act], ASCALE_NONE, _DT[out or act])
+
+
+def w3a16(act: str = "f16", scale: Optional[str] = None, zp_value: int = 4, out: Optional[str] = None) -> QuantDesc:
+    """INT3 (group 128, fixed zero point) weights x fp16/bf16 activations; codes
+    are int32 [N, 3K/32], the dense 3-bit packing of GPTQ INT3 along K (each
+    row one little-endian bit stream, code k in bits [3k, 3k+3))."""
+    return QuantDesc(U3, 3, 128, _DT[scale or act], ZP_FIXED, zp_value, _DT[act], ASCALE_NONE, _DT[out or act])
 
 
 def w4a8_int(scale: str = "f16", out: str = "bf16") -> QuantDesc:

@@ -60,16 +60,21 @@ hq_status classify(const hq_quant_desc& q, int* fmt) {
     *fmt = q.act == HQ_F16 ? hq::FMT_W8F16 : hq::FMT_W8BF16;
     return HQ_OK;
   }
-  if (q.w_elem == HQ_U2) {
-    if (q.w_bits != 2) return fail(HQ_ERR_UNSUPPORTED, "U2 weights have w_bits 2 (got %d)", q.w_bits);
-    if (q.group_size != 128) return fail(HQ_ERR_UNSUPPORTED, "INT2 weights need group_size 128 (got %d)", q.group_size);
+  if (q.w_elem == HQ_U2 || q.w_elem == HQ_U3) {
+    const int bits = q.w_elem == HQ_U2 ? 2 : 3;
+    if (q.w_bits != bits) return fail(HQ_ERR_UNSUPPORTED, "U%d weights have w_bits %d (got %d)", bits, bits, q.w_bits);
+    if (q.group_size != 128)
+      return fail(HQ_ERR_UNSUPPORTED, "INT%d weights need group_size 128 (got %d)", bits, q.group_size);
     if (q.scale != HQ_F16 && q.scale != HQ_BF16)
-      return fail(HQ_ERR_UNSUPPORTED, "INT2 group scales must be fp16 or bf16");
-    if (q.zp != HQ_ZP_FIXED) return fail(HQ_ERR_UNSUPPORTED, "INT2 weights are implemented with a fixed zero point");
-    if (q.zp_value < 0 || q.zp_value > 3) return fail(HQ_ERR_INVALID_ARG, "INT2 fixed zero point must be 0..3");
+      return fail(HQ_ERR_UNSUPPORTED, "INT%d group scales must be fp16 or bf16", bits);
+    if (q.zp != HQ_ZP_FIXED)
+      return fail(HQ_ERR_UNSUPPORTED, "INT%d weights are implemented with a fixed zero point", bits);
+    if (q.zp_value < 0 || q.zp_value >= (1 << bits))
+      return fail(HQ_ERR_INVALID_ARG, "INT%d fixed zero point must be 0..%d", bits, (1 << bits) - 1);
     if ((q.act != HQ_F16 && q.act != HQ_BF16) || q.act_scale != HQ_ASCALE_NONE)
-      return fail(HQ_ERR_UNSUPPORTED, "INT2 weights are implemented with fp16 / bf16 activations");
-    *fmt = q.act == HQ_F16 ? hq::FMT_W2F16 : hq::FMT_W2BF16;
+      return fail(HQ_ERR_UNSUPPORTED, "INT%d weights are implemented with fp16 / bf16 activations", bits);
+    if (bits == 2) *fmt = q.act == HQ_F16 ? hq::FMT_W2F16 : hq::FMT_W2BF16;
+    else *fmt = q.act == HQ_F16 ? hq::FMT_W3F16 : hq::FMT_W3BF16;
     return HQ_OK;
   }
   if (q.w_bits != 4) return fail(HQ_ERR_UNSUPPORTED, "this weight element needs w_bits 4 (got %d)", q.w_bits);
@@ -130,6 +135,8 @@ const char* fmt_name(int fmt) {
     case hq::FMT_W8BF16: return "w8a16-bf16";
     case hq::FMT_W2F16: return "w2a16-f16";
     case hq::FMT_W2BF16: return "w2a16-bf16";
+    case hq::FMT_W3F16: return "w3a16-f16";
+    case hq::FMT_W3BF16: return "w3a16-bf16";
     case hq::FMT_I8: return "w4a8-int8";
     case hq::FMT_Q8: return "w4a8-fp8";
     case hq::FMT_F4: return "w4a8-mxfp4";
@@ -234,13 +241,13 @@ Exec choose_exec(const hq_plan* p, int64_t m) {
   // column-block workgroup; 4 column blocks per workgroup cut that 4x, and
   // a 4-way K split keeps 4x the workgroups (partials summed by the reduce).
   int64_t auto_split = 1;
-  if (w8_weights(p->fmt) || w2_weights(p->fmt)) {
+  if (w8_weights(p->fmt) || w2_weights(p->fmt) || w3_weights(p->fmt)) {
     // INT8 / INT2 weights (a sweep at N = 4096..16384): two column blocks per
     // workgroup from 384 column blocks on, four from 1024 on (INT8: for 5..16
     // rows only), no K split
     if (c.mb == 1) {
       c.nb = (N / 16 >= 384 && N % 32 == 0) ? 2 : 1;
-      if (N / 16 >= 1024 && N % 64 == 0 && (w2_weights(p->fmt) || m > 4)) c.nb = 4;
+      if (N / 16 >= 1024 && N % 64 == 0 && (!w8_weights(p->fmt) || m > 4)) c.nb = 4;
     }
   } else if (c.mb == 1 && m > 4 && G >= 64 && N % 64 == 0 && N / 64 >= 32) {
     c.nb = 4;
@@ -288,7 +295,7 @@ hq_status check_exec(const hq_plan* p, const hq::Exec& e) {
       const bool act4 = p->fmt == hq::FMT_F44;
       const int rowb = act16 ? 256 : (act4 ? 64 : 128);
       const int lps = e.tl.bm * rowb / 1024 / 4 + e.tl.nbw * (hq::mx_weights(p->fmt) ? 2 : 3) +
-                      (act4 ? e.tl.bm / 16 : 0) + (hq::w8_weights(p->fmt) ? e.tl.nbw : 0);
+                      (act4 ? e.tl.bm / 16 : 0) + ((hq::w8_weights(p->fmt) || hq::w3_weights(p->fmt)) ? e.tl.nbw : 0);
       if (e.tl.stages < 2 || e.tl.stages > 5) return fail(HQ_ERR_INVALID_ARG, "tiled kernel: stages must be 2..5");
       if (e.tl.stages * e.tl.bm * rowb > 160 * 1024 || lps * (e.tl.stages - 2) >= 64)
         return fail(HQ_ERR_INVALID_ARG, "tiled kernel: too many stages for this tile");
@@ -403,7 +410,7 @@ hq_status hq_plan_create(const hq_layer_desc* layer, const hq_compute* compute, 
     if (tuning) p->user = *tuning;
     p->fmt = fmt;
     const int64_t N = layer->n, K = layer->k, G = K / 128;
-    p->w_bytes_per_expert = (size_t)(hq::w8_weights(fmt) ? N * K : (hq::w2_weights(fmt) ? N * K / 4 : N * K / 2));
+    p->w_bytes_per_expert = (size_t)N * (size_t)K * (size_t)hq::frag_bytes(fmt) / (size_t)(hq::kFragN * hq::kFragK);
     if (hq::mx_weights(fmt)) {
       p->scale_region_bytes = 0;
       p->meta_bytes_per_expert = (size_t)(N * K / 32);
@@ -499,7 +506,12 @@ hq_status hq_repack_host(const hq_plan* p, const void* codes, const void* scales
     if (s != HQ_OK) return s;
     const int64_t N = p->layer.n, K = p->layer.k, E = p->layer.num_experts, G = K / 128;
     uint32_t* wo = static_cast<uint32_t*>(w_out);
-    if (hq::w2_weights(p->fmt)) {
+    if (hq::w3_weights(p->fmt)) {
+      const int64_t wpe3 = N * K * 3 / 32;
+      const uint32_t* cw = static_cast<const uint32_t*>(codes);
+      for (int64_t e = 0; e < E; ++e)
+        for (int64_t i = 0; i < wpe3; ++i) wo[e * wpe3 + i] = hq::repack_word3(cw + e * wpe3, K, i);
+    } else if (hq::w2_weights(p->fmt)) {
       const int64_t wpe2 = N * K / 16;
       const uint32_t* cw = static_cast<const uint32_t*>(codes);
       for (int64_t e = 0; e < E; ++e)

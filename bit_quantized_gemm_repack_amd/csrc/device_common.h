@@ -83,6 +83,14 @@ __device__ inline u4_t w2_operand(uint32_t x, uint32_t magic, int u) {
               ((y >> 6) & 0x00030003u) | magic};
 }
 
+// One word of INT3 high bits -> the 16-bit operand of MFMA step t: register r
+// = bits 4t + r (low half) and 16 + 4t + r (high half), MAGIC + bit exactly.
+__device__ inline u4_t w1_operand(uint32_t x, uint32_t magic, int t) {
+  const uint32_t y = x >> (4 * t);
+  return u4_t{(y & 0x00010001u) | magic, ((y >> 1) & 0x00010001u) | magic, ((y >> 2) & 0x00010001u) | magic,
+              ((y >> 3) & 0x00010001u) | magic};
+}
+
 // Two words of NIB_B8 codes stored as q ^ 8 -> the int8 operand (16 values)
 // holding 16 * (q - 8) exactly.
 __device__ inline i4_t i8_operand(uint32_t w0, uint32_t w1) {

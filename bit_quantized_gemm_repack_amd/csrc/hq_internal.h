@@ -67,22 +67,34 @@ enum Fmt : int {
   FMT_W8F16 = 6,   // INT8 weight, fp16 activation (two 4-bit planes), fp16 MFMA
   FMT_W8BF16 = 7,  // INT8 weight, bf16 activation (two 4-bit planes), bf16 MFMA
   FMT_W2F16 = 8,   // INT2 weight, fp16 activation, fp16 MFMA
-  FMT_W2BF16 = 9   // INT2 weight, bf16 activation, bf16 MFMA
+  FMT_W2BF16 = 9,  // INT2 weight, bf16 activation, bf16 MFMA
+  FMT_W3F16 = 10,  // INT3 weight, fp16 activation (2-bit + 1-bit planes), fp16 MFMA
+  FMT_W3BF16 = 11  // INT3 weight, bf16 activation (2-bit + 1-bit planes), bf16 MFMA
 };
 
 // INT8 weights: stored as two 4-bit planes (high nibbles, then low nibbles)
 // in the 16-bit operand order, so that each plane expands to exact MFMA
 // operands like an INT4 weight and q = 16 * high + low.
 HQ_HD constexpr inline bool w8_weights(int fmt) { return fmt == FMT_W8F16 || fmt == FMT_W8BF16; }
-// fp16 / bf16 activations (INT4 or INT8 weights)
 // INT2 weights: 512-byte fragments, 8 bytes per lane, 16 codes per word.
 HQ_HD constexpr inline bool w2_weights(int fmt) { return fmt == FMT_W2F16 || fmt == FMT_W2BF16; }
+// INT3 weights: 768-byte fragments, a 2-bit plane of the low code bits in the
+// INT2 layout (512 bytes) then a 1-bit plane of the high bits (256 bytes, one
+// word per lane), q = 4 * high + low.
+HQ_HD constexpr inline bool w3_weights(int fmt) { return fmt == FMT_W3F16 || fmt == FMT_W3BF16; }
+// fp16 / bf16 activations (INT2, INT3, INT4 or INT8 weights)
 HQ_HD constexpr inline bool act16_fmt(int fmt) {
   return fmt == FMT_W16F16 || fmt == FMT_W16BF16 || fmt == FMT_W8F16 || fmt == FMT_W8BF16 || fmt == FMT_W2F16 ||
-         fmt == FMT_W2BF16;
+         fmt == FMT_W2BF16 || fmt == FMT_W3F16 || fmt == FMT_W3BF16;
 }
 // fp16 (rather than bf16) activations
-HQ_HD constexpr inline bool f16_act(int fmt) { return fmt == FMT_W16F16 || fmt == FMT_W8F16 || fmt == FMT_W2F16; }
+HQ_HD constexpr inline bool f16_act(int fmt) {
+  return fmt == FMT_W16F16 || fmt == FMT_W8F16 || fmt == FMT_W2F16 || fmt == FMT_W3F16;
+}
+// Weight bytes of one 16 x 128 fragment.
+HQ_HD constexpr inline int frag_bytes(int fmt) {
+  return w8_weights(fmt) ? 2048 : (w2_weights(fmt) ? 512 : (w3_weights(fmt) ? 768 : 1024));
+}
 
 // MXFP4 weights (E2M1 codes in natural order + E8M0 block scales).
 HQ_HD constexpr inline bool mx_weights(int fmt) { return fmt == FMT_F4 || fmt == FMT_F44; }
@@ -171,6 +183,50 @@ HQ_HD inline uint32_t repack_word2(const uint32_t* codes, int64_t K, int64_t wid
     const int64_t k = g * kFragK + 32 * (2 * d + u) + 8 * (lane >> 4) + 2 * r + hi;
     const uint32_t q = (codes[n * (K / 16) + (k >> 4)] >> (2 * (k & 15))) & 0x3u;
     w |= q << (2 * p);
+  }
+  return w;
+}
+
+// Code k of one row of canonical INT3 words: the row is one little-endian bit
+// stream and the code takes stream bits [3k, 3k+3) (it may straddle words).
+HQ_HD inline uint32_t code3_at(const uint32_t* row, int64_t k) {
+  const int64_t b = 3 * k;
+  const int64_t j = b >> 5;
+  const int o = (int)(b & 31);
+  uint32_t v = row[j] >> o;
+  if (o > 29) v |= row[j + 1] << (32 - o);
+  return v & 0x7u;
+}
+
+// One 32-bit word of the INT3 device layout (768-byte fragments of 192
+// words): words [0, 128) are the low two bits of every code in the INT2
+// layout (repack_word2's crumb order), words [128, 192) the high bit, one word
+// per lane: bit 4t + r is element 2r and bit 16 + 4t + r element 2r + 1 of
+// MFMA step t, so that (w >> (4t + r)) & 0x00010001 is operand register r of
+// step t.  Canonical int32 [N][3K/32], the dense 3-bit stream along K.
+HQ_HD inline uint32_t repack_word3(const uint32_t* codes, int64_t K, int64_t widx) {
+  const int64_t G = K / kFragK;
+  const int64_t frag = widx / 192;
+  const int rem = (int)(widx - frag * 192);
+  const int64_t g = frag % G;
+  const int64_t nb = frag / G;
+  const bool high = rem >= 128;
+  const int lane = high ? rem - 128 : rem >> 1;
+  const int d = rem & 1;
+  const int64_t n = nb * kFragN + (lane & 15);
+  const uint32_t* row = codes + n * (K / 32 * 3);
+  uint32_t w = 0;
+  for (int p = 0; p < (high ? 32 : 16); ++p) {
+    int64_t k;
+    if (high) {
+      const int hi = p >> 4, t = (p >> 2) & 3, r = p & 3;
+      k = g * kFragK + 32 * t + 8 * (lane >> 4) + 2 * r + hi;
+    } else {
+      const int hi = p >> 3, u = (p >> 2) & 1, r = p & 3;
+      k = g * kFragK + 32 * (2 * d + u) + 8 * (lane >> 4) + 2 * r + hi;
+    }
+    const uint32_t q = code3_at(row, k);
+    w |= (high ? (q >> 2) : (q & 0x3u)) << (high ? p : 2 * p);
   }
   return w;
 }

@@ -46,6 +46,7 @@ struct FmtInfo {
   static constexpr bool kAct16 = act16_fmt(FMT);
   static constexpr bool kW8 = w8_weights(FMT);  // INT8 weights: a second (low-nibble) plane
   static constexpr bool kW2 = w2_weights(FMT);  // INT2 weights: 8 bytes per lane per fragment
+  static constexpr bool kW3 = w3_weights(FMT);  // INT3 weights: INT2 plane (8 B) + 1-bit plane (4 B) per lane
   static constexpr bool kAct4 = (FMT == FMT_F44);  // MXFP4 activations
   static constexpr int kAVec = kAct16 ? 4 : (kAct4 ? 1 : 2);  // 16-byte loads per lane per group
   static constexpr int kARowB = kAct16 ? 256 : (kAct4 ? 64 : 128);  // A bytes per row per group
@@ -57,7 +58,7 @@ template <int FMT, int MB, int NB>
 struct Stage {
   u4_t a[MB][FmtInfo<FMT>::kAVec];
   u4_t b[NB];
-  u4_t b2[NB];        // INT8 weights: the low-nibble plane (b holds the high one)
+  u4_t b2[NB];        // INT8 weights: the low-nibble plane (b holds the high one); INT3: the high-bit word
   uint32_t sraw[NB];  // scale bits, or the E8M0 byte
   uint32_t zraw[NB];  // zero-point word (8 nibbles), unused with a fixed zero
   uint32_t asc[MB];   // MXFP4 activations: the row's four E8M0 block scales of the group
@@ -144,7 +145,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   const int a_rows = (GRP == GRP_GATHER) ? p.n_slots / p.topk : p.M;
   const auto ra = rsrc(p.a, (int64_t)a_rows * a_rowb);
   const int64_t nfrag = (int64_t)(p.N / 16) * G;
-  constexpr int kFragB = FI::kW8 ? 2048 : (FI::kW2 ? 512 : 1024);  // weight bytes per 16 x 128 fragment
+  constexpr int kFragB = frag_bytes(FMT);  // weight bytes per 16 x 128 fragment
   const auto rw = rsrc(wbytes, nfrag * kFragB);
   [[maybe_unused]] const auto rsc = rsrc(scales16, nfrag * 32);
   [[maybe_unused]] const auto rz = rsrc(zeros32 ? static_cast<const void*>(zeros32) : static_cast<const void*>(scales16),
@@ -176,7 +177,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int f0 = nblk(nb) * G;
-    woff[nb] = f0 * kFragB + lane * (FI::kW2 ? 8 : 16);
+    woff[nb] = f0 * kFragB + lane * ((FI::kW2 || FI::kW3) ? 8 : 16);
     soff[nb] = mx_weights(FMT) ? f0 * 64 + (lane & ~3) : f0 * 32 + (c >> 1) * 4;
     zoff[nb] = f0 * 8 + (c >> 3) * 4;
   }
@@ -184,7 +185,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   auto load = [&](Stage<FMT, MB, NB>& st, int g) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      if constexpr (FI::kW2) {
+      if constexpr (FI::kW2 || FI::kW3) {
         const auto v = __builtin_amdgcn_raw_buffer_load_b64(rw, woff[nb], g * kFragB, 2);
         st.b[nb] = u4_t{(uint32_t)v[0], (uint32_t)v[1], 0u, 0u};
       } else {
@@ -194,6 +195,12 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
         st.b2[nb] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[nb] + 1024, g * kFragB, 2));
+    }
+    if constexpr (FI::kW3) {
+      // the 1-bit plane: bytes [512, 768) of the fragment, one word per lane
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        st.b2[nb] = u4_t{__builtin_amdgcn_raw_buffer_load_b32(rw, woff[nb] + 512 - 4 * lane, g * kFragB, 2), 0u, 0u, 0u};
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -264,9 +271,12 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const u4_t w = st.b[nb];
-      if constexpr (FI::kW8) {
-        // q = 16 * high + low: P_h and P_l against the exact offset operands
-        // (OFF + high), (OFF + low); the row sums remove 17 OFF + z
+      if constexpr (FI::kW8 || FI::kW3) {
+        // INT8: q = 16 * high + low (two nibble planes); INT3: q = 4 * high
+        // + low (a bit plane and a crumb plane).  P_h and P_l against the
+        // exact offset operands (OFF + high), (OFF + low); the row sums
+        // remove (H + 1) OFF + z, H = 16 or 4.
+        constexpr float kH = FI::kW8 ? 16.f : 4.f;
         const uint32_t magic = f16_act(FMT) ? 0x64006400u : 0x43004300u;
         const float off = f16_act(FMT) ? 1024.f : 128.f;
         const u4_t w2 = st.b2[nb];
@@ -275,8 +285,8 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
         for (int mb = 0; mb < MB; ++mb) Ph[mb] = Pl[mb] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const u4_t bh = w16_operand(w[t], magic);
-          const u4_t bl = w16_operand(w2[t], magic);
+          const u4_t bh = FI::kW8 ? w16_operand(w[t], magic) : w1_operand(w2[0], magic, t);
+          const u4_t bl = FI::kW8 ? w16_operand(w2[t], magic) : w2_operand(w[t >> 1], magic, t & 1);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
             Ph[mb] = mfma16<FMT>(st.a[mb][t], bh, Ph[mb]);
@@ -284,11 +294,11 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
           }
         }
         const float s = p.scale_bf16 ? bf16_bits_to_float(sbits(st, nb)) : f16_bits_to_float(sbits(st, nb));
-        const float cz = 17.f * off + (float)p.zp_fixed;
+        const float cz = (kH + 1.f) * off + (float)p.zp_fixed;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[mb][nb][r] += s * (16.f * Ph[mb][r] + Pl[mb][r] - cz * rs[mb][r]);
+          for (int r = 0; r < 4; ++r) acc[mb][nb][r] += s * (kH * Ph[mb][r] + Pl[mb][r] - cz * rs[mb][r]);
       } else if constexpr (FI::kAct16) {
         const uint32_t magic = f16_act(FMT) ? 0x64006400u : 0x43004300u;
         const float off = f16_act(FMT) ? 1024.f : 128.f;
@@ -569,6 +579,8 @@ int launch_skinny(int fmt, const SkinnyCfg& cfg, const SkinnyArgs& a, void* stre
     case FMT_W8BF16: return (int)launch_mb<FMT_W8BF16>(cfg, a, grid, block, lds, s);
     case FMT_W2F16: return (int)launch_mb<FMT_W2F16>(cfg, a, grid, block, lds, s);
     case FMT_W2BF16: return (int)launch_mb<FMT_W2BF16>(cfg, a, grid, block, lds, s);
+    case FMT_W3F16: return (int)launch_mb<FMT_W3F16>(cfg, a, grid, block, lds, s);
+    case FMT_W3BF16: return (int)launch_mb<FMT_W3BF16>(cfg, a, grid, block, lds, s);
     case FMT_I8: return (int)launch_mb<FMT_I8>(cfg, a, grid, block, lds, s);
     case FMT_Q8: return (int)launch_mb<FMT_Q8>(cfg, a, grid, block, lds, s);
     case FMT_F4: return (int)launch_mb<FMT_F4>(cfg, a, grid, block, lds, s);

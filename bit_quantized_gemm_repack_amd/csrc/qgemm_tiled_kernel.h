@@ -59,7 +59,9 @@ struct TCfg {
   static constexpr bool ACT16 = act16_fmt(FMT);
   static constexpr bool W8 = w8_weights(FMT);  // INT8 weights: two 1 KiB planes per fragment
   static constexpr bool W2 = w2_weights(FMT);  // INT2 weights: 512-byte fragments, 8 bytes per lane
-  static constexpr int FRAGB = W8 ? 2048 : (W2 ? 512 : 1024);
+  static constexpr bool W3 = w3_weights(FMT);  // INT3 weights: INT2 plane + one high-bit word per lane
+  static constexpr bool TWO = W8 || W3;        // a second weight load per fragment
+  static constexpr int FRAGB = frag_bytes(FMT);
   static constexpr bool ACT4 = (FMT == FMT_F44);  // MXFP4 activations
   static constexpr int ROWB = ACT16 ? 256 : (ACT4 ? 64 : 128);  // A bytes per row per group
   static constexpr int CHUNKS = ROWB / 16;        // 16-byte chunks per row
@@ -72,7 +74,7 @@ struct TCfg {
   static constexpr int META = mx_weights(FMT) ? 1 : 2;  // metadata loads per fragment
   // vector-memory loads per step per wave (MXFP4 activations: plus one E8M0
   // word per m-block)
-  static constexpr int LPS = SEGW + (W8 ? 2 : 1) * NBW + META * NBW + (ACT4 ? MB : 0);
+  static constexpr int LPS = SEGW + (TWO ? 2 : 1) * NBW + META * NBW + (ACT4 ? MB : 0);
   // the loads in flight fit the wait counter and the ring fits the LDS
   static constexpr bool FITS = ST >= 2 && LPS * (ST - 2) < 64 && LDS_BYTES <= 160 * 1024;
   static_assert(SEGW * WAVES == NSEG, "tile rows must fill the loaders");
@@ -231,14 +233,14 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
     const int f0 = nblk(j) * G;  // first fragment of this column block
-    woff[j] = f0 * C::FRAGB + lane * (C::W2 ? 8 : 16);
+    woff[j] = f0 * C::FRAGB + lane * ((C::W2 || C::W3) ? 8 : 16);
     soff[j] = mx_weights(FMT) ? f0 * 64 + (lane & ~3) : f0 * 32 + (c16 >> 1) * 4;
     zoff[j] = f0 * 8 + (c16 >> 3) * 4;
   }
 
   // ---- weight fragments + metadata of this wave, register ring ---------------
   u4_t braw[C::STAGES][NBW];
-  [[maybe_unused]] u4_t braw2[C::STAGES][NBW];  // INT8 weights: the low-nibble plane
+  [[maybe_unused]] u4_t braw2[C::STAGES][NBW];  // INT8 weights: the low-nibble plane; INT3: the high-bit word
   uint32_t sraw[C::STAGES][NBW];
   [[maybe_unused]] uint32_t zraw[C::STAGES][NBW];
   [[maybe_unused]] uint32_t asc[C::STAGES][C::MB];  // MXFP4 activations: row scale words
@@ -254,7 +256,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
     }
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
-      if constexpr (C::W2) {
+      if constexpr (C::W2 || C::W3) {
         const auto v = __builtin_amdgcn_raw_buffer_load_b64(rw, woff[j], gg * C::FRAGB, 2);
         braw[slot][j] = u4_t{(uint32_t)v[0], (uint32_t)v[1], 0u, 0u};
       } else {
@@ -266,6 +268,13 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
       for (int j = 0; j < NBW; ++j)
         braw2[slot][j] =
             __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[j] + 1024, gg * C::FRAGB, 2));
+    }
+    if constexpr (C::W3) {
+      // the 1-bit plane: bytes [512, 768) of the fragment, one word per lane
+#pragma unroll
+      for (int j = 0; j < NBW; ++j)
+        braw2[slot][j] = u4_t{__builtin_amdgcn_raw_buffer_load_b32(rw, woff[j] + 512 - 4 * lane, gg * C::FRAGB, 2), 0u,
+                              0u, 0u};
     }
     // Metadata comes in as whole 32-bit words and the lane's byte / half-word
     // is taken out in the math: a narrow load would be zero-extended where the
@@ -335,21 +344,26 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
         c2[j] = h2_t{cz, cz};
       }
       auto deq = [&](int j, int t) -> u4_t {
-        const u4_t x = C::W2 ? w2_operand(braw[slot][j][t >> 1], magic_v, t & 1) : w16_operand(braw[slot][j][t], magic_v);
         uint32_t y[4];
-        if constexpr (C::W8) {
-          // q = 16 * high + low: (high - 0) * 16 + (low - z), exact integers
-          const u4_t xl = w16_operand(braw2[slot][j][t], magic_v);
+        if constexpr (C::TWO) {
+          // INT8: q = 16 * high + low; INT3: q = 4 * high + low;
+          // (high - 0) * H + (low - z), exact integers
+          const u4_t xh = C::W8 ? w16_operand(braw[slot][j][t], magic_v) : w1_operand(braw2[slot][j][0], magic_v, t);
+          const u4_t xl =
+              C::W8 ? w16_operand(braw2[slot][j][t], magic_v) : w2_operand(braw[slot][j][t >> 1], magic_v, t & 1);
           const h2_t m1024 = h2_t{(_Float16)-1024.f, (_Float16)-1024.f};
-          const h2_t k16 = h2_t{(_Float16)16.f, (_Float16)16.f};
+          const _Float16 H = (_Float16)(C::W8 ? 16.f : 4.f);
+          const h2_t kh = h2_t{H, H};
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const h2_t vh = __builtin_bit_cast(h2_t, (uint32_t)x[r]) + m1024;
+            const h2_t vh = __builtin_bit_cast(h2_t, (uint32_t)xh[r]) + m1024;
             const h2_t vl = __builtin_bit_cast(h2_t, (uint32_t)xl[r]) + c2[j];
-            const h2_t v = (vh * k16 + vl) * s2[j];  // exact integer q - z, then one rounding
+            const h2_t v = (vh * kh + vl) * s2[j];  // exact integer q - z, then one rounding
             y[r] = __builtin_bit_cast(uint32_t, v);
           }
         } else {
+          const u4_t x =
+              C::W2 ? w2_operand(braw[slot][j][t >> 1], magic_v, t & 1) : w16_operand(braw[slot][j][t], magic_v);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             h2_t v = __builtin_bit_cast(h2_t, (uint32_t)x[r]);
@@ -395,19 +409,22 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-    } else if constexpr (FMT == FMT_W8BF16) {
-      // q = 16 * high + low: P_h and P_l against (128 + high), (128 + low);
-      // the row sums remove 17 * 128 + z
+    } else if constexpr (FMT == FMT_W8BF16 || FMT == FMT_W3BF16) {
+      // INT8: q = 16 * high + low; INT3: q = 4 * high + low.  P_h and P_l
+      // against (128 + high), (128 + low); the row sums remove
+      // (H + 1) * 128 + z
+      constexpr float kH = C::W8 ? 16.f : 4.f;
       u4_t bh[NBW][4], bl[NBW][4];
       float sj[NBW], cj[NBW];
 #pragma unroll
       for (int j = 0; j < NBW; ++j) {
         sj[j] = p.scale_bf16 ? bf16_bits_to_float(scale_bits(sraw[slot][j])) : f16_bits_to_float(scale_bits(sraw[slot][j]));
-        cj[j] = 17.f * 128.f + (float)zero_of(zraw[slot][j]);
+        cj[j] = (kH + 1.f) * 128.f + (float)zero_of(zraw[slot][j]);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          bh[j][t] = w16_operand(braw[slot][j][t], magic_v);
-          bl[j][t] = w16_operand(braw2[slot][j][t], magic_v);
+          bh[j][t] = C::W8 ? w16_operand(braw[slot][j][t], magic_v) : w1_operand(braw2[slot][j][0], magic_v, t);
+          bl[j][t] = C::W8 ? w16_operand(braw2[slot][j][t], magic_v)
+                           : w2_operand(braw[slot][j][t >> 1], magic_v, t & 1);
         }
       }
       const u4_t ones = u4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
@@ -427,7 +444,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
             Pl = mfma_16x16x32<false>(a[t], bl[j][t], Pl);
           }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[mb][j][r] += sj[j] * (16.f * Ph[r] + Pl[r] - cj[j] * rs[r]);
+          for (int r = 0; r < 4; ++r) acc[mb][j][r] += sj[j] * (kH * Ph[r] + Pl[r] - cj[j] * rs[r]);
         }
       }
     } else if constexpr (FMT == FMT_W16BF16 || FMT == FMT_W2BF16) {
@@ -550,7 +567,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
       pin(braw[cur][j]);
-      if constexpr (C::W8) pin(braw2[cur][j]);
+      if constexpr (C::TWO) pin(braw2[cur][j]);
       pin(sraw[cur][j]);
       if constexpr (!mx_weights(FMT)) pin(zraw[cur][j]);
     }

@@ -45,6 +45,16 @@ __global__ void repack_codes2_kernel(const uint32_t* __restrict__ codes, uint32_
   }
 }
 
+__global__ void repack_codes3_kernel(const uint32_t* __restrict__ codes, uint32_t* __restrict__ out, int64_t K,
+                                     int64_t words_per_expert, int64_t total_words) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total_words;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = i / words_per_expert;
+    const int64_t widx = i - e * words_per_expert;
+    out[i] = repack_word3(codes + e * words_per_expert, K, widx);
+  }
+}
+
 __global__ void repack_scales_kernel(const uint16_t* __restrict__ scales, uint16_t* __restrict__ out,
                                      int64_t G, int64_t per_expert, int64_t total) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
@@ -88,7 +98,11 @@ int launch_repack(const hq_plan* p, const void* codes, const void* scales, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t N = p->layer.n, K = p->layer.k, E = p->layer.num_experts;
   const int64_t G = K / kFragK;
-  if (w2_weights(p->fmt)) {
+  if (w3_weights(p->fmt)) {
+    const int64_t wpe3 = N * K * 3 / 32;  // 32-bit words per expert (same count as canonical)
+    hipLaunchKernelGGL(repack_codes3_kernel, grid_for(wpe3 * E), dim3(256), 0, s, static_cast<const uint32_t*>(codes),
+                       static_cast<uint32_t*>(w_out), K, wpe3, wpe3 * E);
+  } else if (w2_weights(p->fmt)) {
     const int64_t wpe2 = N * K / 16;  // 32-bit words per expert (same count as canonical)
     hipLaunchKernelGGL(repack_codes2_kernel, grid_for(wpe2 * E), dim3(256), 0, s, static_cast<const uint32_t*>(codes),
                        static_cast<uint32_t*>(w_out), K, wpe2, wpe2 * E);

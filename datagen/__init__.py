@@ -105,6 +105,17 @@ def dense_w2a16(M: int, N: int, K: int, act: str = "bf16", key=(8,)):
     return {"a": a, "codes": words, "scales": scales}
 
 
+def dense_w3a16(M: int, N: int, K: int, act: str = "bf16", key=(9,)):
+    """Dense W3A16 inputs: uniformly random int32 words [N, 3K/32] (every 3-bit
+    code of the bit stream uniform over 0..7), zero 4."""
+    rng = rng_for(*key, M, N, K)
+    dt = _dtype(act)
+    a = _to_dtype(rng.standard_normal((M, K)), dt)
+    words = rng.integers(0, 1 << 32, size=(N, K // 32 * 3), dtype=np.uint64).astype(np.uint32).view(np.int32)
+    scales = _to_dtype(rng.uniform(0.005, 0.02, size=(N, K // GROUP)), dt)
+    return {"a": a, "codes": words, "scales": scales}
+
+
 def w4a8_mxfp4(M: int, N: int, K: int, key=(3,)):
     """W4A8-MXFP4 inputs: fp8 e4m3 per-token A, E2M1 codes, E8M0 block scales."""
     rng = rng_for(*key, M, N, K)

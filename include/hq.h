@@ -44,11 +44,15 @@
  *               INT8 weights (W8A16): uint8 [N, K], one byte per weight.
  *               INT2 weights (W2A16): int32 [N, K/16], code k = 16j + i in
  *               bits [2i, 2i+2) of word j.
+ *               INT3 weights (W3A16): int32 [N, 3K/32], the dense 3-bit
+ *               packing along K of GPTQ INT3: a row's words form one
+ *               little-endian bit stream and code k takes its bits
+ *               [3k, 3k+3) (codes may straddle two words).
  *       scales  fp16 or bf16 [N, K/G] (INT4 / INT8, G = 128): group g covers
  *               k in [G*g, G*g+G).
  *       zeros   uint8 [N, K/G] holding 0..15 (only with HQ_ZP_PER_GROUP_U4).
  *       e8m0    uint8 [N, K/32] (MXFP4): scale 2^(X-127) per 32 k.
- *     INT2 / INT4 / INT8 dequantisation is w = (q - z) * s; MXFP4 is
+ *     INT2 / INT3 / INT4 / INT8 dequantisation is w = (q - z) * s; MXFP4 is
  *     w = e2m1(q) * 2^(X-127).
  *   * Activations: row-major [M, K] fp16 / bf16, or 8-bit codes (fp8 e4m3
  *     or int8) with one fp32 scale per row (value = code * scale[m]).
@@ -87,7 +91,8 @@ typedef enum hq_dtype {
   HQ_E8M0 = 7,     /* OCP MX shared scale */
   HQ_I32 = 8,
   HQ_U8 = 9,       /* unsigned 8-bit integer code 0..255 */
-  HQ_U2 = 10       /* unsigned 2-bit integer code 0..3 */
+  HQ_U2 = 10,      /* unsigned 2-bit integer code 0..3 */
+  HQ_U3 = 11       /* unsigned 3-bit integer code 0..7 */
 } hq_dtype;
 
 typedef enum hq_zp_mode {
@@ -114,6 +119,10 @@ typedef enum hq_ascale_mode {
  *   W2A16      w_elem U2 (w_bits 2), group 128, scale F16|BF16, zp FIXED
  *              (0..3, 2 for the symmetric case), act F16|BF16, act_scale
  *              NONE, out F16|BF16 (dense only)
+ *   W3A16      w_elem U3 (w_bits 3), group 128, scale F16|BF16, zp FIXED
+ *              (0..7, 4 for the symmetric case), act F16|BF16, act_scale
+ *              NONE, out F16|BF16 (dense only; GPTQ INT3, the format
+ *              cocoloop.cn names for the compatibility route)
  *   W4A8-INT   w_elem U4, group 128, scale F16|BF16, zp FIXED (8),
  *              act INT8, act_scale PER_TOKEN_F32, out F16|BF16
  *   W4A8-FP8   w_elem U4, group 128, scale F16|BF16, zp FIXED|PER_GROUP_U4,

@@ -22,7 +22,7 @@ import torch
 import bit_quantized_gemm_repack_amd as hq
 import datagen
 from oracle.formats import unpack_u4
-from oracle.gemm import unpack_u2
+from oracle.gemm import unpack_u2, unpack_u3
 
 
 def _plan(n=256, k=512, quant=None, max_m=64, epi="none", tuning=None):
@@ -485,3 +485,45 @@ def test_w2a16_plans_and_validation():
         _plan(quant=hq.QuantDesc(hq.U2, 4, 128, hq.F16, hq.ZP_FIXED, 2, hq.F16, 0, hq.F16))
     with pytest.raises(hq.HQError):   # dense only
         hq.MoePlan(512, 7168, hq.w2a16("bf16"), 256, 4096, "silu_mul")
+
+
+def test_repack_w3_planes_operand_order():
+    """INT3 weights: 768-byte fragments, the low two bits of every code in the
+    INT2 layout (two words per lane) then the high bit, one word per lane,
+    with (word >> (4t + r)) & 0x00010001 the high bits of operand register r
+    of step t; 4 * high + low is the code of the canonical bit stream."""
+    rng = np.random.default_rng(11)
+    words = rng.integers(0, 1 << 32, size=(N, K // 32 * 3), dtype=np.uint64).astype(np.uint32).view(np.int32)
+    q = unpack_u3(words)
+    p = _plan(N, K, hq.w3a16("bf16"), max_m=16)
+    w, _ = p.repack_host(torch.from_numpy(words), torch.ones(N, K // 128, dtype=torch.bfloat16))
+    assert w.numel() == N * K * 3 // 8
+    fw = w.numpy().view(np.uint32).reshape(N // 16, K // 128, 192)
+    for nb in range(N // 16):
+        for g in range(K // 128):
+            for lane in range(0, 64, 3):
+                n = 16 * nb + lane % 16
+                hw = int(fw[nb, g, 128 + lane])
+                for t in range(4):
+                    k0 = _k16(g, lane, t)
+                    y = int(fw[nb, g, 2 * lane + (t >> 1)]) >> (8 * (t & 1))
+                    for r in range(4):
+                        lo = (y >> (2 * r)) & 0x00030003
+                        hi = (hw >> (4 * t + r)) & 0x00010001
+                        assert 4 * (hi & 1) + (lo & 3) == q[n, k0 + 2 * r]
+                        assert 4 * (hi >> 16) + (lo >> 16) == q[n, k0 + 2 * r + 1]
+
+
+def test_w3a16_plans_and_validation():
+    p = _plan(4096, 4096, hq.w3a16("f16"), max_m=1024)
+    wb, mb = p.repacked_bytes()
+    assert wb == 4096 * 4096 * 3 // 8 and mb == 4096 * 32 * 2
+    assert "w3a16-f16" in p.describe(1) and "kernel=tiled" in p.describe(1024)
+    with pytest.raises(hq.HQError):   # fixed zero point only
+        _plan(quant=hq.QuantDesc(hq.U3, 3, 128, hq.F16, hq.ZP_PER_GROUP_U4, 0, hq.F16, 0, hq.F16))
+    with pytest.raises(hq.HQError):   # zero point range
+        _plan(quant=hq.w3a16("f16", zp_value=8))
+    with pytest.raises(hq.HQError):   # U3 elements need w_bits 3
+        _plan(quant=hq.QuantDesc(hq.U3, 2, 128, hq.F16, hq.ZP_FIXED, 4, hq.F16, 0, hq.F16))
+    with pytest.raises(hq.HQError):   # dense only
+        hq.MoePlan(512, 7168, hq.w3a16("bf16"), 256, 4096, "silu_mul")
