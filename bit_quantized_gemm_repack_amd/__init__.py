@@ -16,6 +16,7 @@ Quick use::
 from __future__ import annotations
 
 import ctypes
+import json
 import os
 import re
 from dataclasses import dataclass
@@ -72,6 +73,18 @@ class Tuning(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int),
                 ("waves", ctypes.c_int), ("split_k", ctypes.c_int), ("stages", ctypes.c_int),
                 ("mfma", ctypes.c_int)]
+
+
+class AutotuneResult(ctypes.Structure):
+    _fields_ = [("best", Tuning), ("best_us", ctypes.c_float), ("current_us", ctypes.c_float),
+                ("candidates", ctypes.c_int)]
+
+
+_TUNING_FIELDS = ("kernel", "tile_m", "tile_n", "waves", "split_k", "stages")
+
+
+def _tuning_dict(t: Tuning) -> dict:
+    return {f: int(getattr(t, f)) for f in _TUNING_FIELDS}
 
 
 def w4a16(act: str = "f16", scale: Optional[str] = None, zp="fixed", zp_value: int = 8,
@@ -155,6 +168,12 @@ _SIGS = {
     "hq_quantize_per_token": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int] +
                               [ctypes.c_void_p] * 4),
     "hq_quantize_mxfp4": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int] + [ctypes.c_void_p] * 4),
+    "hq_plan_autotune": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_void_p] * 6 +
+                         [ctypes.c_size_t, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p,
+                          ctypes.POINTER(AutotuneResult)]),
+    "hq_plan_set_tuning": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(Tuning)]),
+    "hq_plan_get_tuning": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(Tuning),
+                                          ctypes.POINTER(ctypes.c_int)]),
     "hq_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_size_t, ctypes.c_void_p]),
@@ -325,6 +344,88 @@ class Plan:
         _check(lib().hq_gemm(self._h, m, _ptr(a), _ptr(a_scale), _ptr(w), _ptr(meta), _ptr(out), _ptr(ws),
                              ws_bytes, _stream_ptr(a.device)))
         return out
+
+
+    # -- measured execution choices --------------------------------------
+    def autotune(self, a: torch.Tensor, w: torch.Tensor, meta: torch.Tensor, a_scale: Optional[torch.Tensor] = None,
+                 reps: int = 10, flush_bytes: int = 512 << 20, max_ws_bytes: int = 512 << 20) -> dict:
+        """Time the candidate execution choices for m = a.shape[0] rows on these
+        buffers and install the fastest for that m (see hq_plan_autotune).
+        Returns {"tuning", "best_us", "current_us", "candidates"}."""
+        _dev(a, "a"), _dev(w, "w"), _dev(meta, "meta")
+        if a_scale is not None:
+            _dev(a_scale, "a_scale")
+        m = a.shape[0]
+        out = torch.empty((m, self.n), dtype=_TORCH_OUT.get(self.quant.out, torch.float16), device=a.device)
+        if self.epi == EPI_I32_ACC:
+            out = torch.empty((m, self.n, self.k // 128), dtype=torch.int32, device=a.device)
+        ws_bytes = min(int(max_ws_bytes), 8 * m * self.n * 4)
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=a.device)
+        res = AutotuneResult()
+        _check(lib().hq_plan_autotune(self._h, m, _ptr(a), _ptr(a_scale), _ptr(w), _ptr(meta), _ptr(out), _ptr(ws),
+                                      ws_bytes, int(reps), int(flush_bytes), _stream_ptr(a.device),
+                                      ctypes.byref(res)))
+        return {"tuning": _tuning_dict(res.best), "best_us": float(res.best_us),
+                "current_us": float(res.current_us), "candidates": int(res.candidates)}
+
+    def set_tuning(self, m: int, tuning: Optional[dict]):
+        """Install a tuning for exactly m rows (None removes m's entry)."""
+        t = None if tuning is None else Tuning(**{f: int(tuning.get(f, 0)) for f in _TUNING_FIELDS})
+        _check(lib().hq_plan_set_tuning(self._h, int(m), None if t is None else ctypes.byref(t)))
+
+    def get_tuning(self, m: int):
+        """(resolved tuning dict for m rows, whether it comes from the table)."""
+        t, flag = Tuning(), ctypes.c_int(0)
+        _check(lib().hq_plan_get_tuning(self._h, int(m), ctypes.byref(t), ctypes.byref(flag)))
+        return _tuning_dict(t), bool(flag.value)
+
+    def tuning_key(self, m: int, device) -> str:
+        """Cache key of m rows of this plan on `device`: format, shape, GPU, rows."""
+        q = self.quant
+        fmt = "-".join(str(int(getattr(q, f))) for f, _ in QuantDesc._fields_)
+        name = torch.cuda.get_device_name(torch.device(device)).replace("|", "/")
+        return f"{fmt}|epi{self.epi}|n{self.n}|k{self.k}|{name}|abi{lib().hq_abi_version()}|m{int(m)}"
+
+
+class TuningCache:
+    """Measured execution choices kept across processes: a JSON file that maps
+    Plan.tuning_key(m, device) to a resolved tuning."""
+
+    def __init__(self, path: str):
+        self.path = path
+        self.entries = {}
+        if os.path.exists(path):
+            with open(path) as f:
+                self.entries = json.load(f)
+
+    def save(self):
+        tmp = self.path + ".tmp"
+        with open(tmp, "w") as f:
+            json.dump(self.entries, f, indent=1, sort_keys=True)
+        os.replace(tmp, self.path)
+
+    def apply(self, plan: Plan, device) -> int:
+        """Install every cached tuning of this plan on `device`; returns how many."""
+        prefix = plan.tuning_key(0, device)[:-1]  # everything but the row count
+        n = 0
+        for key, t in self.entries.items():
+            if key.startswith(prefix) and key[len(prefix):].isdigit() and 1 <= int(key[len(prefix):]) <= plan.max_m:
+                plan.set_tuning(int(key[len(prefix):]), t)
+                n += 1
+        return n
+
+    def tune(self, plan: Plan, a: torch.Tensor, w: torch.Tensor, meta: torch.Tensor,
+             a_scale: Optional[torch.Tensor] = None, **kw) -> dict:
+        """The cached tuning for a's rows if there is one (installed), else an
+        autotune run whose result is installed and saved."""
+        key = plan.tuning_key(a.shape[0], a.device)
+        if key in self.entries:
+            plan.set_tuning(a.shape[0], self.entries[key])
+            return {"tuning": dict(self.entries[key]), "cached": True}
+        r = plan.autotune(a, w, meta, a_scale, **kw)
+        self.entries[key] = r["tuning"]
+        self.save()
+        return dict(r, cached=False)
 
 
 def stream_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int, nbytes: Optional[int] = None):

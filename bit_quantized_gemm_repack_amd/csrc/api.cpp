@@ -159,12 +159,18 @@ TimingEvents take_timing() {
   return t;
 }
 
-Exec choose_exec(const hq_plan* p, int64_t m) {
+static const hq_tuning* tuned_for(const hq_plan* p, int64_t m) {
+  for (const auto& t : p->tuned)
+    if (t.first == m) return &t.second;
+  return &p->user;
+}
+
+Exec choose_exec(const hq_plan* p, int64_t m, const hq_tuning* up) {
   Exec e{};
   e.kernel = KER_SKINNY;
   const int64_t N = p->layer.n;
   const int64_t G = p->layer.k / kFragK;
-  const hq_tuning& u = p->user;
+  const hq_tuning& u = up ? *up : *tuned_for(p, m);
   const int64_t mm = m > 0 ? m : 1;
   // Large M: the MFMA-bound tiled kernel (needs whole 128/256-column tiles);
   // from 33 rows on, the activation tile in LDS is shared by the four waves
@@ -553,27 +559,36 @@ hq_status hq_repack_host(const hq_plan* p, const void* codes, const void* scales
   }
 }
 
-hq_status hq_gemm(const hq_plan* p, int64_t m, const void* a, const void* a_scale, const void* w,
-                  const void* meta, void* out, void* ws, size_t ws_bytes, void* stream) {
-  const hq::TimingEvents ev = hq::take_timing();  // consumed by this call whatever happens
-  try {
-    if (!p) return fail(HQ_ERR_INVALID_ARG, "null plan");
-    if (p->compute.kind != HQ_GEMM_DENSE) return fail(HQ_ERR_INVALID_ARG, "hq_gemm needs a dense plan");
-    if (m < 0 || m > p->max_m) return fail(HQ_ERR_INVALID_ARG, "m=%lld out of range [0, %lld]", (long long)m,
-                                           (long long)p->max_m);
-    if (m == 0) return ok();
-    if (!a || !w || !meta || !out) return fail(HQ_ERR_INVALID_ARG, "null device pointer");
-    if (!aligned16(a) || !aligned16(w) || !aligned16(meta) || !aligned16(out))
-      return fail(HQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+namespace {
+
+// Argument checks of a dense call (hq_gemm, hq_plan_autotune); m >= 1.
+hq_status dense_args_check(const hq_plan* p, int64_t m, const void* a, const void* a_scale, const void* w,
+                           const void* meta, void* out) {
+  if (!p) return fail(HQ_ERR_INVALID_ARG, "null plan");
+  if (p->compute.kind != HQ_GEMM_DENSE) return fail(HQ_ERR_INVALID_ARG, "hq_gemm needs a dense plan");
+  if (m < 0 || m > p->max_m) return fail(HQ_ERR_INVALID_ARG, "m=%lld out of range [0, %lld]", (long long)m,
+                                         (long long)p->max_m);
+  if (!a || !w || !meta || !out) return fail(HQ_ERR_INVALID_ARG, "null device pointer");
+  if (!aligned16(a) || !aligned16(w) || !aligned16(meta) || !aligned16(out))
+    return fail(HQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  const bool act4 = p->fmt == hq::FMT_F44;
+  const bool act8 = p->fmt == hq::FMT_I8 || p->fmt == hq::FMT_Q8 || p->fmt == hq::FMT_F4;
+  if (act8 && !a_scale) return fail(HQ_ERR_INVALID_ARG, "8-bit activations need a_scale");
+  if (act4 && !a_scale) return fail(HQ_ERR_INVALID_ARG, "MXFP4 activations need their E8M0 scales in a_scale");
+  if (act4 && !aligned16(a_scale)) return fail(HQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  if (!act8 && !act4 && a_scale) return fail(HQ_ERR_INVALID_ARG, "16-bit activations take no a_scale");
+  return HQ_OK;
+}
+
+// One dense GEMM with the execution choice e (arguments already checked).
+hq_status dense_run(const hq_plan* p, const hq::Exec& e, int64_t m, const void* a, const void* a_scale,
+                    const void* w, const void* meta, void* out, void* ws, size_t ws_bytes, void* stream,
+                    const hq::TimingEvents& ev) {
+  {
     const bool act4 = p->fmt == hq::FMT_F44;
     const bool act8 = p->fmt == hq::FMT_I8 || p->fmt == hq::FMT_Q8 || p->fmt == hq::FMT_F4;
-    if (act8 && !a_scale) return fail(HQ_ERR_INVALID_ARG, "8-bit activations need a_scale");
-    if (act4 && !a_scale) return fail(HQ_ERR_INVALID_ARG, "MXFP4 activations need their E8M0 scales in a_scale");
-    if (act4 && !aligned16(a_scale)) return fail(HQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
-    if (!act8 && !act4 && a_scale) return fail(HQ_ERR_INVALID_ARG, "16-bit activations take no a_scale");
     const float* a_scale_f = act8 ? static_cast<const float*>(a_scale) : nullptr;
     const uint8_t* a_e8m0 = act4 ? static_cast<const uint8_t*>(a_scale) : nullptr;
-    hq::Exec e = hq::choose_exec(p, m);
     hq_status s = check_exec(p, e);
     if (s != HQ_OK) return s;
     if (e.ws_bytes > 0) {
@@ -657,6 +672,20 @@ hq_status hq_gemm(const hq_plan* p, int64_t m, const void* a, const void* a_scal
     hq::arm_timing({nullptr, nullptr});
     if (err != hipSuccess) return fail(HQ_ERR_HIP, "gemm launch: %s", hipGetErrorString((hipError_t)err));
     return ok();
+  }
+}
+
+}  // namespace
+
+hq_status hq_gemm(const hq_plan* p, int64_t m, const void* a, const void* a_scale, const void* w,
+                  const void* meta, void* out, void* ws, size_t ws_bytes, void* stream) {
+  const hq::TimingEvents ev = hq::take_timing();  // consumed by this call whatever happens
+  try {
+    if (!p) return fail(HQ_ERR_INVALID_ARG, "null plan");
+    if (m == 0 && p->compute.kind == HQ_GEMM_DENSE) return ok();
+    hq_status s = dense_args_check(p, m, a, a_scale, w, meta, out);
+    if (s != HQ_OK) return s;
+    return dense_run(p, hq::choose_exec(p, m), m, a, a_scale, w, meta, out, ws, ws_bytes, stream, ev);
   } catch (...) {
     return fail(HQ_ERR_INTERNAL, "exception in hq_gemm");
   }
@@ -993,6 +1022,227 @@ hq_status hq_quantize_mxfp4(int64_t m, int64_t k, hq_dtype in, const void* x, vo
   hq::arm_timing({nullptr, nullptr});
   if (err != hipSuccess) return fail(HQ_ERR_HIP, "quantize launch: %s", hipGetErrorString((hipError_t)err));
   return ok();
+}
+
+// ---------------------------------------------------------------------------
+// autotuning (dense plans)
+// ---------------------------------------------------------------------------
+
+}  // extern "C"
+
+namespace {
+
+// The tuning that reproduces e through choose_exec (every field explicit).
+hq_tuning resolved_tuning(const hq::Exec& e) {
+  hq_tuning t{};
+  if (e.kernel == hq::KER_TILED) {
+    t.kernel = hq::KER_TILED;
+    t.tile_m = e.tl.bm;
+    t.tile_n = 64 * e.tl.nbw;
+    t.waves = 4;
+    t.split_k = e.tl.split;
+    t.stages = e.tl.stages;
+  } else {
+    t.kernel = hq::KER_SKINNY;
+    t.tile_m = 16 * e.sk.mb;
+    t.tile_n = 16 * e.sk.nb;
+    t.waves = e.sk.waves;
+    t.split_k = e.sk.split;
+    t.stages = e.sk.stages;
+  }
+  return t;
+}
+
+bool same_tuning(const hq_tuning& a, const hq_tuning& b) {
+  return a.kernel == b.kernel && a.tile_m == b.tile_m && a.tile_n == b.tile_n && a.waves == b.waves &&
+         a.split_k == b.split_k && a.stages == b.stages;
+}
+
+// Candidate execution choices for m rows: the skinny kernel up to 64 rows
+// (row / column blocks, waves, groups in flight, K split) and the tiled
+// kernel from 17 rows on (tile shape, ring depth, K split).
+std::vector<hq_tuning> tuning_candidates(const hq_plan* p, int64_t m) {
+  std::vector<hq_tuning> c;
+  if (m <= 64) {
+    for (int mb : {1, 2, 4}) {
+      if (mb > 1 && 16 * (mb / 2) >= m) continue;  // no tile taller than the rows need
+      for (int nb : {1, 2, 4})
+        for (int waves : {4, 8})
+          for (int stages : {2, 4})
+            for (int split : {1, 2, 4}) c.push_back(hq_tuning{hq::KER_SKINNY, 16 * mb, 16 * nb, waves, split, stages, 0});
+    }
+  }
+  if (m > 16 && p->layer.n % 128 == 0 && p->compute.epi != HQ_EPI_I32_ACC) {
+    for (int bm : {64, 128})
+      for (int tn : {128, 256})
+        for (int stages : {2, 3, 4})
+          for (int split : {1, 2, 4, 8}) c.push_back(hq_tuning{hq::KER_TILED, bm, tn, 4, split, stages, 0});
+  }
+  return c;
+}
+
+void set_tuned(hq_plan* p, int64_t m, const hq_tuning& t) {
+  for (auto& e : p->tuned)
+    if (e.first == m) {
+      e.second = t;
+      return;
+    }
+  p->tuned.emplace_back(m, t);
+}
+
+}  // namespace
+
+extern "C" {
+
+hq_status hq_plan_set_tuning(hq_plan* p, int64_t m, const hq_tuning* t) {
+  try {
+    if (!p) return fail(HQ_ERR_INVALID_ARG, "null plan");
+    if (p->compute.kind != HQ_GEMM_DENSE) return fail(HQ_ERR_UNSUPPORTED, "per-m tunings are for dense plans");
+    if (m < 1 || m > p->max_m) return fail(HQ_ERR_INVALID_ARG, "m out of range [1, max_m]");
+    if (!t) {
+      for (size_t i = 0; i < p->tuned.size(); ++i)
+        if (p->tuned[i].first == m) {
+          p->tuned.erase(p->tuned.begin() + (long)i);
+          break;
+        }
+      return ok();
+    }
+    if (t->split_k < 0 || t->split_k > 64) return fail(HQ_ERR_INVALID_ARG, "split_k must be 1..64");
+    const hq::Exec e = hq::choose_exec(p, m, t);
+    hq_status s = check_exec(p, e);
+    if (s != HQ_OK) return s;
+    set_tuned(p, m, resolved_tuning(e));
+    return ok();
+  } catch (...) {
+    return fail(HQ_ERR_INTERNAL, "exception in hq_plan_set_tuning");
+  }
+}
+
+hq_status hq_plan_get_tuning(const hq_plan* p, int64_t m, hq_tuning* t, int* is_tuned) {
+  if (!p || !t) return fail(HQ_ERR_INVALID_ARG, "null argument");
+  if (m < 1 || m > p->max_m) return fail(HQ_ERR_INVALID_ARG, "m out of range [1, max_m]");
+  bool tuned = false;
+  for (const auto& e : p->tuned) tuned |= e.first == m;
+  *t = resolved_tuning(hq::choose_exec(p, m));
+  if (is_tuned) *is_tuned = tuned ? 1 : 0;
+  return ok();
+}
+
+hq_status hq_plan_autotune(hq_plan* p, int64_t m, const void* a, const void* a_scale, const void* w,
+                           const void* meta, void* out, void* ws, size_t ws_bytes, int reps, size_t flush_bytes,
+                           void* stream, hq_autotune_result* result) {
+  hq::take_timing();  // an armed pair of events is not for this call
+  void* flush = nullptr;
+  uint32_t* sink = nullptr;
+  std::vector<hipEvent_t> evs;
+  auto release = [&]() {
+    for (hipEvent_t e : evs) (void)hipEventDestroy(e);
+    if (flush) (void)hipFree(flush);
+    if (sink) (void)hipFree(sink);
+  };
+  try {
+    if (!p) return fail(HQ_ERR_INVALID_ARG, "null plan");
+    if (p->compute.kind != HQ_GEMM_DENSE) return fail(HQ_ERR_UNSUPPORTED, "autotuning is for dense plans");
+    if (m < 1) return fail(HQ_ERR_INVALID_ARG, "m must be at least 1");
+    if (reps < 1 || reps > 1000) return fail(HQ_ERR_INVALID_ARG, "reps must be 1..1000");
+    if (flush_bytes % 16 || flush_bytes > (size_t(1) << 34))
+      return fail(HQ_ERR_INVALID_ARG, "flush_bytes must be a multiple of 16, at most 16 GiB");
+    hq_status s = dense_args_check(p, m, a, a_scale, w, meta, out);
+    if (s != HQ_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (flush_bytes) {
+      // its contents do not matter: only its reads evict the caches
+      if (hipMalloc(&flush, flush_bytes) != hipSuccess || hipMalloc(reinterpret_cast<void**>(&sink), 16) != hipSuccess) {
+        release();
+        return fail(HQ_ERR_HIP, "cannot allocate the %zu-byte cache flush buffer", flush_bytes);
+      }
+    }
+    evs.resize(2 * (size_t)reps, nullptr);
+    for (auto& e : evs)
+      if (hipEventCreate(&e) != hipSuccess) {
+        e = nullptr;
+        release();
+        return fail(HQ_ERR_HIP, "hipEventCreate failed");
+      }
+    const hq::TimingEvents none{nullptr, nullptr};
+    // mean time per call of one execution choice (< 0: not runnable here)
+    auto time_exec = [&](const hq::Exec& e, float* us) -> hq_status {
+      *us = -1.f;
+      if (check_exec(p, e) != HQ_OK || e.ws_bytes > (ws ? ws_bytes : 0)) return HQ_OK;
+      hq_status r = dense_run(p, e, m, a, a_scale, w, meta, out, ws, ws_bytes, stream, none);  // warm-up
+      if (r != HQ_OK) return r;
+      for (int i = 0; i < reps; ++i) {
+        if (flush) {
+          hq::arm_timing(none);
+          if (hq::launch_stream_read(flush, flush_bytes, sink, 1024, stream) != hipSuccess)
+            return fail(HQ_ERR_HIP, "cache flush launch failed");
+        }
+        if (hipEventRecord(evs[2 * i], st) != hipSuccess) return fail(HQ_ERR_HIP, "hipEventRecord failed");
+        r = dense_run(p, e, m, a, a_scale, w, meta, out, ws, ws_bytes, stream, none);
+        if (r != HQ_OK) return r;
+        if (hipEventRecord(evs[2 * i + 1], st) != hipSuccess) return fail(HQ_ERR_HIP, "hipEventRecord failed");
+      }
+      if (hipEventSynchronize(evs[2 * reps - 1]) != hipSuccess) return fail(HQ_ERR_HIP, "hipEventSynchronize failed");
+      double tot = 0;
+      for (int i = 0; i < reps; ++i) {
+        float ms = 0;
+        if (hipEventElapsedTime(&ms, evs[2 * i], evs[2 * i + 1]) != hipSuccess)
+          return fail(HQ_ERR_HIP, "hipEventElapsedTime failed");
+        tot += ms;
+      }
+      *us = (float)(tot * 1000.0 / reps);
+      return HQ_OK;
+    };
+    const hq::Exec base = hq::choose_exec(p, m);
+    const hq_tuning base_t = resolved_tuning(base);
+    float base_us = -1.f;
+    s = time_exec(base, &base_us);
+    if (s != HQ_OK) {
+      release();
+      return s;
+    }
+    if (base_us < 0) {
+      release();
+      return fail(HQ_ERR_WORKSPACE, "the current choice for m=%lld needs %zu workspace bytes", (long long)m,
+                  base.ws_bytes);
+    }
+    hq_tuning best_t = base_t;
+    float best_us = base_us;
+    int timed = 1;
+    std::vector<hq_tuning> seen{base_t};
+    for (const hq_tuning& c : tuning_candidates(p, m)) {
+      const hq::Exec e = hq::choose_exec(p, m, &c);
+      const hq_tuning rt = resolved_tuning(e);
+      bool dup = false;
+      for (const auto& q : seen) dup |= same_tuning(q, rt);
+      if (dup) continue;
+      seen.push_back(rt);
+      float us = -1.f;
+      s = time_exec(e, &us);
+      if (s != HQ_OK) {
+        release();
+        return s;
+      }
+      if (us < 0) continue;
+      ++timed;
+      if (us < best_us) {
+        best_us = us;
+        best_t = rt;
+      }
+    }
+    release();
+    set_tuned(p, m, best_t);
+    if (result) {
+      result->best = best_t;
+      result->best_us = best_us;
+      result->current_us = base_us;
+      result->candidates = timed;
+    }
+    return ok();
+  } catch (...) {
+    release();
+    return fail(HQ_ERR_INTERNAL, "exception in hq_plan_autotune");
+  }
 }
 
 hq_status hq_stream_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups, void* stream) {

@@ -41,6 +41,8 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <utility>
+#include <vector>
 
 #include "../../include/hq.h"
 
@@ -291,6 +293,9 @@ struct hq_plan {
   hq_compute compute;
   int64_t max_m;
   hq_tuning user;  // user overrides (zero = auto)
+  // per-m execution choices installed by hq_plan_autotune / hq_plan_set_tuning
+  // (dense plans); they take the place of `user` for exactly that m
+  std::vector<std::pair<int64_t, hq_tuning>> tuned;
   int fmt;         // hq::Fmt
   size_t w_bytes_per_expert;
   size_t meta_bytes_per_expert;
@@ -308,7 +313,9 @@ struct Exec {
   size_t ws_bytes;  // total workspace: the fp32 split-K partials
 };
 
-Exec choose_exec(const hq_plan* p, int64_t m);
+// The execution choice for m rows: the heuristic with the overrides of `u`,
+// or (u == nullptr) with the plan's tuned entry for m, else its user tuning.
+Exec choose_exec(const hq_plan* p, int64_t m, const hq_tuning* u = nullptr);
 
 // Kernel launchers (defined in the .hip files).  Return a hipError_t as int.
 struct SkinnyArgs {

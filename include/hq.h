@@ -361,6 +361,53 @@ hq_status hq_quantize_per_token(int64_t m, int64_t k, hq_dtype in, hq_dtype out,
 hq_status hq_quantize_mxfp4(int64_t m, int64_t k, hq_dtype in, const void* x, void* codes, uint8_t* e8m0,
                             void* stream);
 
+/* ---- Autotuning (dense plans) ----------------------------------------
+ * The heuristic maps (format, n, k, m) to an execution choice by rules taken
+ * from sweeps; the pages list that rule-based selection among the
+ * limitations, with autotuning not yet finished (cocoloop.cn, limitations
+ * section).  These calls replace the heuristic per row count m with a
+ * measured choice.
+ *
+ * A plan keeps a table m -> hq_tuning (empty at creation).  For an m in the
+ * table, every later call on the plan (hq_gemm, hq_plan_describe,
+ * hq_plan_workspace_bytes) uses that entry in place of the plan's tuning;
+ * other m keep the heuristic.  The table is changed only by the two calls
+ * below, which must not overlap any other call that uses the plan. */
+
+typedef struct hq_autotune_result {
+  hq_tuning best;     /* the installed choice, every field resolved        */
+  float best_us;      /* its mean device time per call, microseconds       */
+  float current_us;   /* the same for the choice in force before the call  */
+  int candidates;     /* execution choices timed (the current one included) */
+} hq_autotune_result;
+
+/* Time the current choice for m rows and every other candidate that fits
+ * (skinny kernel up to 64 rows over row / column blocks, waves, groups in
+ * flight and K split; tiled kernel from 17 rows over tile shape, ring depth
+ * and K split) on the caller's buffers, exactly as hq_gemm takes them, then
+ * install the fastest for m.  Each candidate runs once untimed and `reps`
+ * times between two events on `stream` (mean taken); with flush_bytes > 0
+ * a buffer of that size is read before each timed run so that the weights
+ * come from HBM rather than the caches (use at least 2x the 256 MiB
+ * last-level cache for an HBM-bound choice).  Candidates needing more than
+ * ws_bytes of workspace are skipped (ws may be NULL: only choices without a
+ * workspace).  `out` holds the product on return.  Synchronises `stream`;
+ * allocates the flush buffer, events and a 16-byte sink with hipMalloc and
+ * frees them before returning.  `result` may be NULL. */
+hq_status hq_plan_autotune(hq_plan* plan, int64_t m, const void* a, const void* a_scale, const void* w,
+                           const void* meta, void* out, void* ws, size_t ws_bytes, int reps, size_t flush_bytes,
+                           void* stream, hq_autotune_result* result);
+
+/* Install `tuning` for exactly m rows (validated like a plan's tuning and
+ * stored resolved), or remove m's entry with tuning == NULL.  For a tuning
+ * cache kept across processes: store hq_plan_get_tuning's result, install it
+ * here in a later process. */
+hq_status hq_plan_set_tuning(hq_plan* plan, int64_t m, const hq_tuning* tuning);
+
+/* The resolved execution choice for m rows; *is_tuned (if not NULL) says
+ * whether it comes from the table. */
+hq_status hq_plan_get_tuning(const hq_plan* plan, int64_t m, hq_tuning* tuning, int* is_tuned);
+
 /* Kernel timing: the next hq_gemm, hq_moe_align, hq_moe_gemm,
  * hq_quantize_per_token, hq_quantize_mxfp4 or hq_stream_read call on this
  * thread records `start` (hipEvent_t, created by the caller with timing

@@ -527,3 +527,44 @@ def test_w3a16_plans_and_validation():
         _plan(quant=hq.QuantDesc(hq.U3, 2, 128, hq.F16, hq.ZP_FIXED, 4, hq.F16, 0, hq.F16))
     with pytest.raises(hq.HQError):   # dense only
         hq.MoePlan(512, 7168, hq.w3a16("bf16"), 256, 4096, "silu_mul")
+
+
+def test_per_m_tuning_table():
+    """hq_plan_set_tuning / hq_plan_get_tuning: an entry replaces the heuristic
+    for exactly its m (describe and workspace follow it), None removes it."""
+    p = _plan(4096, 4096, hq.w4a16("bf16"), max_m=1024)
+    heur, tuned = p.get_tuning(1)
+    assert not tuned and heur["kernel"] == 1
+    t = dict(kernel=1, tile_m=16, tile_n=32, waves=4, split_k=2, stages=4)
+    p.set_tuning(1, t)
+    got, tuned = p.get_tuning(1)
+    assert tuned and got == t
+    d = p.describe(1)
+    assert "tile_n=32 waves=4 split_k=2 stages=4" in d
+    assert p.workspace_bytes(1) == 2 * 1 * 4096 * 4
+    assert p.get_tuning(2) == (heur, False)          # other m keep the heuristic
+    p.set_tuning(300, dict(kernel=2, tile_m=128, tile_n=256, stages=2, split_k=1))
+    assert p.get_tuning(300) == (dict(kernel=2, tile_m=128, tile_n=256, waves=4, split_k=1, stages=2), True)
+    p.set_tuning(1, None)
+    assert p.get_tuning(1) == (heur, False)
+    with pytest.raises(hq.HQError):   # not a tile width
+        p.set_tuning(4, dict(kernel=1, tile_n=48))
+    with pytest.raises(hq.HQError):   # m out of range
+        p.set_tuning(1025, t)
+    with pytest.raises(hq.HQError):   # grouped plans keep their own choice
+        hq.MoePlan(512, 7168, hq.w4a16("bf16"), 256, 4096, "silu_mul").set_tuning(1, t)
+
+
+def test_autotune_argument_checks():
+    """Rejected before any device work (no GPU needed)."""
+    L = hq.lib()
+    p = _plan(256, 512, hq.w4a16("f16"), max_m=64)
+    fake = 1 << 20
+    at = L.hq_plan_autotune
+    assert at(p._h, 1, fake, None, fake, fake, fake, None, 0, 0, 0, None, None) == hq.HQ_ERR_INVALID_ARG  # reps
+    assert at(p._h, 1, fake, None, fake, fake, fake, None, 0, 5, 8, None, None) == hq.HQ_ERR_INVALID_ARG  # flush
+    assert at(p._h, 0, fake, None, fake, fake, fake, None, 0, 5, 0, None, None) == hq.HQ_ERR_INVALID_ARG  # m
+    assert at(p._h, 65, fake, None, fake, fake, fake, None, 0, 5, 0, None, None) == hq.HQ_ERR_INVALID_ARG
+    assert at(p._h, 1, None, None, fake, fake, fake, None, 0, 5, 0, None, None) == hq.HQ_ERR_INVALID_ARG
+    assert at(p._h, 1, fake, fake, fake, fake, fake, None, 0, 5, 0, None, None) == hq.HQ_ERR_INVALID_ARG  # a_scale
+    assert at(None, 1, fake, None, fake, fake, fake, None, 0, 5, 0, None, None) == hq.HQ_ERR_INVALID_ARG
