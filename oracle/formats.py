@@ -54,6 +54,15 @@ def e2m1_value(code) -> np.ndarray:
     return sign * np.where(e == 0, sub, normal)
 
 
+def mxint4_value(code) -> np.ndarray:
+    """MXINT4 element value of a 4-bit code: the code read as a two's-complement
+    integer (-8..7) times an implicit 2^-2, i.e. a 1.2 fixed-point number in
+    [-2, 1.75] -- the 4-bit form of the OCP MX integer element, whose 8-bit
+    form (MXINT8) is a two's-complement integer times 2^-6."""
+    c = np.asarray(code, dtype=np.int64)
+    return np.where(c >= 8, c - 16, c) * 0.25
+
+
 def e8m0_value(code) -> np.ndarray:
     """OCP MX E8M0 shared-scale value 2^(X-127); X = 255 decodes to NaN."""
     x = np.asarray(code, dtype=np.int64)

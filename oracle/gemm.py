@@ -28,6 +28,10 @@ Readings where the pages are silent:
   little-endian bit stream (so codes 10 and 21 of every 32 straddle two
   words), a fixed zero point 0..7 (4 for the symmetric case),
   w = (q - z) * s with group-128 scales.
+* MXINT4 weights (the pages list MXINT4 among the formats): 4-bit
+  two's-complement elements with an implicit 2^-2 (formats.mxint4_value),
+  one E8M0 scale 2^(X-127) per 32 k as for MXFP4; with fp16/bf16
+  activations C = A . W^T, W exact in float64.
 * W4A8-INT: the int32 accumulator of one group is
   P[m,n,g] = sum_{k in g} a_q[m,k] * (q[n,k] - 8), and
   C = s_a[m] * sum_g s[n,g] * P[m,n,g].
@@ -42,7 +46,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import e2m1_value, e4m3_value, e8m0_value, int8_value, rne, ulp, unpack_u4
+from .formats import e2m1_value, e4m3_value, e8m0_value, int8_value, mxint4_value, rne, ulp, unpack_u4
 
 
 def dequant_int4(codes, scales, zeros, group: int = 128) -> np.ndarray:
@@ -219,6 +223,28 @@ def mxfp4_weights(codes, e8m0, block: int = 32) -> np.ndarray:
     for b in range(K // block):
         w[:, b * block : (b + 1) * block] *= scale[:, b : b + 1]
     return w
+
+
+def mxint4_weights(codes, e8m0, block: int = 32) -> np.ndarray:
+    """w[n,k] = mxint4(q[n,k]) * 2^(E[n, k//32] - 127), exact in float64."""
+    q = unpack_u4(codes)
+    N, K = q.shape
+    scale = e8m0_value(np.asarray(e8m0))
+    if scale.shape != (N, K // block):
+        raise ValueError("E8M0 scales must be [N, K/32]")
+    w = mxint4_value(q)
+    for b in range(K // block):
+        w[:, b * block : (b + 1) * block] *= scale[:, b : b + 1]
+    return w
+
+
+def gemm_mxint4_w16(a, w_codes, e8m0, out_fmt: str = "bf16"):
+    """W4A16-MXINT4: C = A . W^T with fp16/bf16 activation values A and the
+    MXINT4 weights (mxint4_weights), float64."""
+    a = np.asarray(a, dtype=np.float64)
+    w = mxint4_weights(w_codes, e8m0)
+    c64 = a @ w.T
+    return {"c64": c64, "c_out": rne(c64, out_fmt), "tau": tolerance(a, w), "w": w}
 
 
 def gemm_mxfp4_fp8(a_codes, a_scale, w_codes, e8m0, out_fmt: str = "bf16"):

@@ -545,3 +545,37 @@ def test_int3_weights_agree_with_int4_on_shared_range():
     w3 = G.dequant_int3(_stream_words(q3), s, 4)
     w4 = G.dequant_int4(datagen.pack_u4(q3 + 4), s, 8)
     assert np.array_equal(w3, w4)
+
+
+# ---------------------------------------------------------- MXINT4 weights --
+
+def test_mxint4_hand_example():
+    g = _gold("mxint4_gemm_2x2.json")
+    words = np.array([[int(h, 16) for h in row] for row in g["packed_words_hex"]], dtype=np.uint32).view(np.int32)
+    assert F.unpack_u4(words).tolist() == g["codes_rows"]
+    r = G.gemm_mxint4_w16(np.array(g["a"], float), words, np.array(g["e8m0"], dtype=np.uint8))
+    assert r["c64"].tolist() == g["c"]
+
+
+def test_mxint4_every_code():
+    """The 16 codes are the two's-complement integers -8..7 in quarters."""
+    vals = F.mxint4_value(np.arange(16))
+    assert vals.tolist() == [0, 0.25, 0.5, 0.75, 1, 1.25, 1.5, 1.75, -2, -1.75, -1.5, -1.25, -1, -0.75, -0.5, -0.25]
+
+
+def test_mxint4_weights_agree_with_int4_group32():
+    """A two's-complement code q is the INT4 code q xor 8 with zero 8; the
+    implicit 2^-2 and the E8M0 block scale make a group-32 scale 2^(X-129)."""
+    rng = np.random.default_rng(35)
+    q = rng.integers(0, 16, size=(6, 256), dtype=np.uint8)
+    x = rng.integers(100, 140, size=(6, 8))
+    w_mx = G.mxint4_weights(datagen.pack_u4(q), x.astype(np.uint8))
+    w_i4 = G.dequant_int4(datagen.pack_u4(q ^ 8), np.ldexp(1.0, x - 129), 8, group=32)
+    assert np.array_equal(w_mx, w_i4)
+
+
+def test_mxint4_nan_scale_propagates():
+    q = np.zeros((1, 32), np.uint8)
+    q[0, 3] = 5
+    w = G.mxint4_weights(datagen.pack_u4(q), np.array([[255]], np.uint8))
+    assert np.isnan(w).all()
