@@ -235,6 +235,8 @@ _WORKLOAD_PROFILES = {
     "w8a16": ("qgemm_w8a16_bf16_n4096_k4096.md", "dense W8A16, M in {1,16,64,1024}, N = K = 4096, bf16"),
     "w2a16": ("qgemm_w2a16_bf16_n4096_k4096.md", "dense W2A16, M in {1,16,64,1024}, N = K = 4096, bf16"),
     "w3a16": ("qgemm_w3a16_bf16_n4096_k4096.md", "dense W3A16, M in {1,16,64,1024}, N = K = 4096, bf16"),
+    "mxint4": ("qgemm_w4a16_mxint4_bf16_n4096_k4096.md", "dense W4A16-MXINT4, M in {1,16,64,1024}, N = K = 4096, "
+               "bf16"),
     "moe": ("moe_layer_e256_top8_h7168_i256.md", "MoE layer, 256 experts, top-8, hidden 7168, intermediate 256, "
             "T in {1,32,512,4096}, bf16 and fp8 activations"),
 }
@@ -330,7 +332,7 @@ class Hip:
         self.L.hipEventDestroy(e)
 
 
-def make_points(dev, rotations):
+def make_points(dev, rotations, autotune=False):
     import bit_quantized_gemm_repack_amd as hq
     import datagen
 
@@ -350,6 +352,10 @@ def make_points(dev, rotations):
             a = s["data"]["a"][:M].contiguous().to(dev)
             copies = [(s["w"].clone(), s["meta"].clone()) for _ in range(rotations)]
             out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            if autotune:  # measured choice for this m in place of the heuristic (weights from HBM)
+                r = plan.autotune(a, copies[0][0], copies[0][1], reps=10, flush_bytes=512 << 20)
+                print(f"[bench] autotune M={M} N={N} K={K}: {r['current_us']:.2f} -> {r['best_us']:.2f} us "
+                      f"{r['tuning']}", file=sys.stderr, flush=True)
             ws = plan.workspace(M, dev)
             points.append(dict(M=M, N=N, K=K, plan=plan, a=a, copies=copies, out=out, ws=ws,
                                bytes=algo_bytes(M, N, K), flops=algo_flops(M, N, K)))
@@ -658,6 +664,31 @@ def _w2a16_points(dev, bits=2):
         f"bf16 scales, zero point {zp}), bf16 output", "bf16"
 
 
+def _mxint4_points(dev):
+    import bit_quantized_gemm_repack_amd as hq
+    import datagen
+
+    N = K = 4096
+    pts = []
+    for M in (1, 16, 64, 1024):
+        d = datagen.w4a16_mxint4(M, N, K, act="bf16")
+        plan = hq.Plan(N, K, hq.w4a16_mxint4("bf16"), max_m=M)
+        w, meta = plan.repack(torch.from_numpy(d["codes"]).to(dev), e8m0=torch.from_numpy(d["e8m0"]).to(dev))
+        R = 128  # 128 copies of 8.9 MB: > 1 GB
+        ws_ = [(w.clone(), meta.clone()) for _ in range(R)]
+        a = d["a"].to(dev)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = plan.workspace(M, dev)
+        byt = N * K // 2 + N * (K // 32) + 2 * M * K + 2 * M * N
+        pts.append(dict(name=f"M={M} N={N} K={K}", R=R, bytes=byt, flops=2 * M * N * K, peak=FP16_PEAK_TFLOPS,
+                        plan=plan.describe(M),
+                        calls=lambda r, plan=plan, ws_=ws_, a=a, out=out, ws=ws:
+                        [lambda: plan.gemm(a, ws_[r][0], ws_[r][1], out=out, ws=ws)]))
+    return pts, "quantized GEMM TFLOPS and effective HBM GB/s vs M (W4A16-MXINT4)", \
+        "dense W4A16-MXINT4: M in {1,16,64,1024}, N = K = 4096, bf16 activations, MXINT4 weights (one E8M0 scale " \
+        "per 32 k), bf16 output", "bf16"
+
+
 def _w4a4_points(dev):
     import bit_quantized_gemm_repack_amd as hq
     import datagen
@@ -880,6 +911,12 @@ def _cpu_sample(workload, budget):
             t0 = time.perf_counter()
             og.gemm_w3a16(d["a"].double().numpy(), d["codes"], d["scales"].double().numpy(), 4, out_fmt="bf16")
             what = "dense W3A16 M=8 N=K=4096"
+        elif workload == "mxint4":
+            M, N, K = 8, 4096, 4096
+            d = datagen.w4a16_mxint4(M, N, K, act="bf16")
+            t0 = time.perf_counter()
+            og.gemm_mxint4_w16(d["a"].double().numpy(), d["codes"], d["e8m0"], out_fmt="bf16")
+            what = "dense W4A16-MXINT4 M=8 N=K=4096"
         elif workload == "w4a4":
             M, N, K = 16, 4096, 7168
             d = datagen.w4a4_mxfp4(M, N, K)
@@ -925,10 +962,12 @@ def main():
     ap.add_argument("--rotations", type=int, default=4)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--workload", choices=("decode", "quant", "prefill", "w4a8", "w4a4", "w8a16", "w2a16", "w3a16", "moe"),
+    ap.add_argument("--autotune", action="store_true",
+                    help="decode: install a measured execution choice per point (hq_plan_autotune) first")
+    ap.add_argument("--workload", choices=("decode", "quant", "prefill", "w4a8", "w4a4", "w8a16", "w2a16", "w3a16", "mxint4", "moe"),
                     default="decode",
                     help="decode: the dense W4A16 decode sweep (default); quant: the per-token quantiser; "
-                         "prefill / w4a8 / w4a4 / w8a16 / w2a16 / w3a16 / moe: the other GEMM workloads")
+                         "prefill / w4a8 / w4a4 / w8a16 / w2a16 / w3a16 / mxint4 / moe: the other GEMM workloads")
     ap.add_argument("--write-profiles", metavar="RUN_DIR",
                     help="CPU only: write the profiles/ summaries from rocprofv3 outputs in RUN_DIR and exit")
     args = ap.parse_args()
@@ -942,10 +981,11 @@ def main():
     if args.workload == "quant":
         run_quant(args)
         return
-    if args.workload in ("prefill", "w4a8", "w4a4", "w8a16", "w2a16", "w3a16", "moe"):
+    if args.workload in ("prefill", "w4a8", "w4a4", "w8a16", "w2a16", "w3a16", "mxint4", "moe"):
         run_points_workload(args, {"prefill": _prefill_points, "w4a8": _w4a8_points, "w4a4": _w4a4_points,
                                    "w8a16": _w8a16_points, "w2a16": _w2a16_points,
-                                   "w3a16": lambda dev: _w2a16_points(dev, 3), "moe": _moe_points}[args.workload])
+                                   "w3a16": lambda dev: _w2a16_points(dev, 3), "mxint4": _mxint4_points,
+                                   "moe": _moe_points}[args.workload])
         return
 
     import bit_quantized_gemm_repack_amd as hq
@@ -955,7 +995,7 @@ def main():
     L = hq.lib()
     print(f"[bench] preparing {len(SWEEP_M) * len(SWEEP_NK)} points x {args.rotations} rotations", file=sys.stderr,
           flush=True)
-    points, shapes = make_points(dev, args.rotations)
+    points, shapes = make_points(dev, args.rotations, args.autotune)
     R = args.rotations
     step_bytes = sum(p["bytes"] for p in points)
     step_flops = sum(p["flops"] for p in points)
@@ -1053,8 +1093,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "launches_per_step": n, "step_bytes": step_bytes,
                    "step_flops": step_flops, "tflops_per_step_time": round(step_flops / (ms_per_step * 1e-3) / 1e12, 3),
-                   "weight_pool_rotations": R, "timing": "HIP graph replay per step; kernel durations from "
-                                                         "dispatch-bracketing HIP events"},
+                   "weight_pool_rotations": R, "execution_choice": "autotuned" if args.autotune else "heuristic",
+                   "timing": "HIP graph replay per step; kernel durations from dispatch-bracketing HIP events"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic([p["plan"] for p in per_point]),

@@ -30,7 +30,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "hq.h")
 
 # ------------------------------------------------------------------ enums --
 HQ_OK, HQ_ERR_INVALID_ARG, HQ_ERR_UNSUPPORTED, HQ_ERR_WORKSPACE, HQ_ERR_HIP, HQ_ERR_INTERNAL = range(6)
-F16, BF16, F32, FP8_E4M3, INT8, U4, FP4_E2M1, E8M0, I32, U8, U2, U3 = range(12)
+F16, BF16, F32, FP8_E4M3, INT8, U4, FP4_E2M1, E8M0, I32, U8, U2, U3, I4 = range(13)
 ZP_NONE, ZP_FIXED, ZP_PER_GROUP_U4 = range(3)
 ASCALE_NONE, ASCALE_PER_TOKEN_F32, ASCALE_MX_E8M0 = range(3)
 GEMM_DENSE, GEMM_GROUPED = range(2)
@@ -111,6 +111,13 @@ def w3a16(act: str = "f16", scale: Optional[str] = None, zp_value: int = 4, out:
     are int32 [N, 3K/32], the dense 3-bit packing of GPTQ INT3 along K (each
     row one little-endian bit stream, code k in bits [3k, 3k+3))."""
     return QuantDesc(U3, 3, 128, _DT[scale or act], ZP_FIXED, zp_value, _DT[act], ASCALE_NONE, _DT[out or act])
+
+
+def w4a16_mxint4(act: str = "bf16", out: Optional[str] = None) -> QuantDesc:
+    """MXINT4 weights (two's-complement 4-bit codes times 2^-2, one E8M0 scale
+    per 32 k; codes packed as INT4, scales uint8 [N, K/32]) x fp16/bf16
+    activations."""
+    return QuantDesc(I4, 4, 32, E8M0, ZP_NONE, 0, _DT[act], ASCALE_NONE, _DT[out or act])
 
 
 def w4a8_int(scale: str = "f16", out: str = "bf16") -> QuantDesc:

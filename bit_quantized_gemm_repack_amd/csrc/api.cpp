@@ -60,6 +60,15 @@ hq_status classify(const hq_quant_desc& q, int* fmt) {
     *fmt = q.act == HQ_F16 ? hq::FMT_W8F16 : hq::FMT_W8BF16;
     return HQ_OK;
   }
+  if (q.w_elem == HQ_I4) {
+    if (q.w_bits != 4) return fail(HQ_ERR_UNSUPPORTED, "MXINT4 elements have w_bits 4 (got %d)", q.w_bits);
+    if (q.group_size != 32 || q.scale != HQ_E8M0 || q.zp != HQ_ZP_NONE)
+      return fail(HQ_ERR_UNSUPPORTED, "MXINT4 weights take one E8M0 scale per 32 k and no zero point");
+    if ((q.act != HQ_F16 && q.act != HQ_BF16) || q.act_scale != HQ_ASCALE_NONE)
+      return fail(HQ_ERR_UNSUPPORTED, "MXINT4 weights are implemented with fp16 / bf16 activations");
+    *fmt = q.act == HQ_F16 ? hq::FMT_MX4F16 : hq::FMT_MX4BF16;
+    return HQ_OK;
+  }
   if (q.w_elem == HQ_U2 || q.w_elem == HQ_U3) {
     const int bits = q.w_elem == HQ_U2 ? 2 : 3;
     if (q.w_bits != bits) return fail(HQ_ERR_UNSUPPORTED, "U%d weights have w_bits %d (got %d)", bits, bits, q.w_bits);
@@ -137,6 +146,8 @@ const char* fmt_name(int fmt) {
     case hq::FMT_W2BF16: return "w2a16-bf16";
     case hq::FMT_W3F16: return "w3a16-f16";
     case hq::FMT_W3BF16: return "w3a16-bf16";
+    case hq::FMT_MX4F16: return "w4a16-mxint4-f16";
+    case hq::FMT_MX4BF16: return "w4a16-mxint4-bf16";
     case hq::FMT_I8: return "w4a8-int8";
     case hq::FMT_Q8: return "w4a8-fp8";
     case hq::FMT_F4: return "w4a8-mxfp4";
@@ -300,7 +311,7 @@ hq_status check_exec(const hq_plan* p, const hq::Exec& e) {
       const bool act16 = hq::act16_fmt(p->fmt);
       const bool act4 = p->fmt == hq::FMT_F44;
       const int rowb = act16 ? 256 : (act4 ? 64 : 128);
-      const int lps = e.tl.bm * rowb / 1024 / 4 + e.tl.nbw * (hq::mx_weights(p->fmt) ? 2 : 3) +
+      const int lps = e.tl.bm * rowb / 1024 / 4 + e.tl.nbw * (hq::e8m0_meta(p->fmt) ? 2 : 3) +
                       (act4 ? e.tl.bm / 16 : 0) + ((hq::w8_weights(p->fmt) || hq::w3_weights(p->fmt)) ? e.tl.nbw : 0);
       if (e.tl.stages < 2 || e.tl.stages > 5) return fail(HQ_ERR_INVALID_ARG, "tiled kernel: stages must be 2..5");
       if (e.tl.stages * e.tl.bm * rowb > 160 * 1024 || lps * (e.tl.stages - 2) >= 64)
@@ -417,7 +428,7 @@ hq_status hq_plan_create(const hq_layer_desc* layer, const hq_compute* compute, 
     p->fmt = fmt;
     const int64_t N = layer->n, K = layer->k, G = K / 128;
     p->w_bytes_per_expert = (size_t)N * (size_t)K * (size_t)hq::frag_bytes(fmt) / (size_t)(hq::kFragN * hq::kFragK);
-    if (hq::mx_weights(fmt)) {
+    if (hq::e8m0_meta(fmt)) {
       p->scale_region_bytes = 0;
       p->meta_bytes_per_expert = (size_t)(N * K / 32);
     } else {
@@ -480,8 +491,8 @@ hq_status hq_repacked_bytes(const hq_plan* p, size_t* w_bytes, size_t* meta_byte
 static hq_status check_repack_args(const hq_plan* p, const void* codes, const void* scales, const void* zx,
                                    const void* w_out, const void* meta_out) {
   if (!p || !codes || !w_out || !meta_out) return fail(HQ_ERR_INVALID_ARG, "null argument");
-  if (hq::mx_weights(p->fmt)) {
-    if (!zx) return fail(HQ_ERR_INVALID_ARG, "MXFP4 repack needs the E8M0 scales");
+  if (hq::e8m0_meta(p->fmt)) {
+    if (!zx) return fail(HQ_ERR_INVALID_ARG, "MXFP4 / MXINT4 repack needs the E8M0 scales");
   } else {
     if (!scales) return fail(HQ_ERR_INVALID_ARG, "INT4 repack needs the group scales");
     if (p->layer.q.zp == HQ_ZP_PER_GROUP_U4 && !zx)
@@ -534,11 +545,13 @@ hq_status hq_repack_host(const hq_plan* p, const void* codes, const void* scales
         for (int64_t i = 0; i < wpe; ++i) wo[e * wpe + i] = hq::repack_word(cw + e * wpe, K, p->fmt, i);
     }
     uint8_t* meta = static_cast<uint8_t*>(meta_out);
-    if (hq::mx_weights(p->fmt)) {
+    if (hq::e8m0_meta(p->fmt)) {
       const int64_t per = N * K / 32;
       const uint8_t* src = static_cast<const uint8_t*>(zx);
+      const bool cols = hq::mxint4_weights(p->fmt);
       for (int64_t e = 0; e < E; ++e)
-        for (int64_t i = 0; i < per; ++i) meta[e * per + i] = src[e * per + hq::e8m0_src_index(K, i)];
+        for (int64_t i = 0; i < per; ++i)
+          meta[e * per + i] = src[e * per + (cols ? hq::e8m0_cols_src_index(K, i) : hq::e8m0_src_index(K, i))];
       return ok();
     }
     const int64_t sper = N * G;
@@ -615,7 +628,7 @@ hq_status dense_run(const hq_plan* p, const hq::Exec& e, int64_t m, const void* 
       t.a_scale = a_scale_f;
       t.a_e8m0 = a_e8m0;
       t.w = w;
-      if (hq::mx_weights(p->fmt)) t.e8m0 = static_cast<const uint8_t*>(meta);
+      if (hq::e8m0_meta(p->fmt)) t.e8m0 = static_cast<const uint8_t*>(meta);
       else t.scales = meta;
       t.zeros = zeros;
       t.out = out;
@@ -645,7 +658,7 @@ hq_status dense_run(const hq_plan* p, const hq::Exec& e, int64_t m, const void* 
     args.a_scale = a_scale_f;
     args.a_e8m0 = a_e8m0;
     args.w = w;
-    if (hq::mx_weights(p->fmt)) {
+    if (hq::e8m0_meta(p->fmt)) {
       args.e8m0 = static_cast<const uint8_t*>(meta);
     } else {
       args.scales = meta;

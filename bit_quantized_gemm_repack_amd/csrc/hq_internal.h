@@ -71,7 +71,9 @@ enum Fmt : int {
   FMT_W2F16 = 8,   // INT2 weight, fp16 activation, fp16 MFMA
   FMT_W2BF16 = 9,  // INT2 weight, bf16 activation, bf16 MFMA
   FMT_W3F16 = 10,  // INT3 weight, fp16 activation (2-bit + 1-bit planes), fp16 MFMA
-  FMT_W3BF16 = 11  // INT3 weight, bf16 activation (2-bit + 1-bit planes), bf16 MFMA
+  FMT_W3BF16 = 11, // INT3 weight, bf16 activation (2-bit + 1-bit planes), bf16 MFMA
+  FMT_MX4F16 = 12, // MXINT4 weight (E8M0 per 32 k), fp16 activation, fp16 MFMA
+  FMT_MX4BF16 = 13 // MXINT4 weight (E8M0 per 32 k), bf16 activation, bf16 MFMA
 };
 
 // INT8 weights: stored as two 4-bit planes (high nibbles, then low nibbles)
@@ -84,14 +86,17 @@ HQ_HD constexpr inline bool w2_weights(int fmt) { return fmt == FMT_W2F16 || fmt
 // INT2 layout (512 bytes) then a 1-bit plane of the high bits (256 bytes, one
 // word per lane), q = 4 * high + low.
 HQ_HD constexpr inline bool w3_weights(int fmt) { return fmt == FMT_W3F16 || fmt == FMT_W3BF16; }
-// fp16 / bf16 activations (INT2, INT3, INT4 or INT8 weights)
+// MXINT4 weights: two's-complement codes stored offset by 8 (q xor 8) in the
+// 16-bit operand order, one E8M0 scale per column per 32 k, i.e. per MFMA step.
+HQ_HD constexpr inline bool mxint4_weights(int fmt) { return fmt == FMT_MX4F16 || fmt == FMT_MX4BF16; }
+// fp16 / bf16 activations (INT2, INT3, INT4, INT8 or MXINT4 weights)
 HQ_HD constexpr inline bool act16_fmt(int fmt) {
   return fmt == FMT_W16F16 || fmt == FMT_W16BF16 || fmt == FMT_W8F16 || fmt == FMT_W8BF16 || fmt == FMT_W2F16 ||
-         fmt == FMT_W2BF16 || fmt == FMT_W3F16 || fmt == FMT_W3BF16;
+         fmt == FMT_W2BF16 || fmt == FMT_W3F16 || fmt == FMT_W3BF16 || fmt == FMT_MX4F16 || fmt == FMT_MX4BF16;
 }
 // fp16 (rather than bf16) activations
 HQ_HD constexpr inline bool f16_act(int fmt) {
-  return fmt == FMT_W16F16 || fmt == FMT_W8F16 || fmt == FMT_W2F16 || fmt == FMT_W3F16;
+  return fmt == FMT_W16F16 || fmt == FMT_W8F16 || fmt == FMT_W2F16 || fmt == FMT_W3F16 || fmt == FMT_MX4F16;
 }
 // Weight bytes of one 16 x 128 fragment.
 HQ_HD constexpr inline int frag_bytes(int fmt) {
@@ -100,13 +105,15 @@ HQ_HD constexpr inline int frag_bytes(int fmt) {
 
 // MXFP4 weights (E2M1 codes in natural order + E8M0 block scales).
 HQ_HD constexpr inline bool mx_weights(int fmt) { return fmt == FMT_F4 || fmt == FMT_F44; }
+// Metadata is one E8M0 region (MXFP4 or MXINT4 weights) rather than scales + zeros.
+HQ_HD constexpr inline bool e8m0_meta(int fmt) { return mx_weights(fmt) || mxint4_weights(fmt); }
 
 enum NibOrder : int { NIB_W16 = 0, NIB_B8 = 1, NIB_NAT = 2 };
 
 HQ_HD inline int nib_order_of(int fmt) {
   return act16_fmt(fmt) ? NIB_W16 : (mx_weights(fmt) ? NIB_NAT : NIB_B8);
 }
-HQ_HD inline uint32_t nib_xor_of(int fmt) { return fmt == FMT_I8 ? 8u : 0u; }
+HQ_HD inline uint32_t nib_xor_of(int fmt) { return (fmt == FMT_I8 || mxint4_weights(fmt)) ? 8u : 0u; }
 
 // k-offset (0..7, within the 8 k of one word) held by nibble p.
 HQ_HD inline int nib_koff(int order, int p) {
@@ -263,6 +270,17 @@ HQ_HD inline int64_t e8m0_src_index(int64_t K, int64_t eidx) {
   const int64_t nb = (eidx >> 6) / G;
   const int64_t n = nb * kFragN + (lane & 15);
   return n * (K / 32) + 4 * g + (lane >> 4);
+}
+
+// Byte eidx of the MXINT4 E8M0 region [N/16][G][16 columns][4 blocks] (one
+// dword per column: the scales of its four MFMA steps) <- canonical [N][K/32].
+HQ_HD inline int64_t e8m0_cols_src_index(int64_t K, int64_t eidx) {
+  const int64_t G = K / kFragK;
+  const int t = (int)(eidx & 3);
+  const int c = (int)((eidx >> 2) & 15);
+  const int64_t g = (eidx >> 6) % G;
+  const int64_t nb = (eidx >> 6) / G;
+  return (nb * kFragN + c) * (K / 32) + 4 * g + t;
 }
 
 // ---------------------------------------------------------------------------

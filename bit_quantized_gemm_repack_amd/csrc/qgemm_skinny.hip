@@ -47,6 +47,7 @@ struct FmtInfo {
   static constexpr bool kW8 = w8_weights(FMT);  // INT8 weights: a second (low-nibble) plane
   static constexpr bool kW2 = w2_weights(FMT);  // INT2 weights: 8 bytes per lane per fragment
   static constexpr bool kW3 = w3_weights(FMT);  // INT3 weights: INT2 plane (8 B) + 1-bit plane (4 B) per lane
+  static constexpr bool kMX4 = mxint4_weights(FMT);  // MXINT4: one E8M0 scale per column per MFMA step
   static constexpr bool kAct4 = (FMT == FMT_F44);  // MXFP4 activations
   static constexpr int kAVec = kAct16 ? 4 : (kAct4 ? 1 : 2);  // 16-byte loads per lane per group
   static constexpr int kARowB = kAct16 ? 256 : (kAct4 ? 64 : 128);  // A bytes per row per group
@@ -112,7 +113,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
       return;
     }
     wbytes += ex * p.w_expert;
-    if constexpr (mx_weights(FMT)) {
+    if constexpr (e8m0_meta(FMT)) {
       e8 += ex * p.e8_expert;
     } else {
       scales16 += ex * p.s_expert;
@@ -178,7 +179,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   for (int nb = 0; nb < NB; ++nb) {
     const int f0 = nblk(nb) * G;
     woff[nb] = f0 * kFragB + lane * ((FI::kW2 || FI::kW3) ? 8 : 16);
-    soff[nb] = mx_weights(FMT) ? f0 * 64 + (lane & ~3) : f0 * 32 + (c >> 1) * 4;
+    soff[nb] = FI::kMX4 ? f0 * 64 + c * 4 : (mx_weights(FMT) ? f0 * 64 + (lane & ~3) : f0 * 32 + (c >> 1) * 4);
     zoff[nb] = f0 * 8 + (c >> 3) * 4;
   }
 
@@ -226,7 +227,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
     // that no wait is needed until the stage's math.
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      if constexpr (mx_weights(FMT)) {
+      if constexpr (e8m0_meta(FMT)) {
         st.sraw[nb] = __builtin_amdgcn_raw_buffer_load_b32(re, soff[nb], g * 64, 0);
       } else {
         st.sraw[nb] = __builtin_amdgcn_raw_buffer_load_b32(rsc, soff[nb], g * 32, 0);
@@ -250,7 +251,15 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
 
   auto compute = [&](const Stage<FMT, MB, NB>& st, int g) {
     [[maybe_unused]] f4_t rs[MB];
-    if constexpr (FI::kAct16) {
+    [[maybe_unused]] f4_t rs4[MB][4];  // MXINT4: the row sums of each MFMA step
+    if constexpr (FI::kMX4) {
+      const uint32_t one2 = f16_act(FMT) ? 0x3C003C00u : 0x3F803F80u;
+      const u4_t ones = u4_t{one2, one2, one2, one2};
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) rs4[mb][t] = mfma16<FMT>(st.a[mb][t], ones, f4_t{0.f, 0.f, 0.f, 0.f});
+    } else if constexpr (FI::kAct16) {
       const uint32_t one2 = f16_act(FMT) ? 0x3C003C00u : 0x3F803F80u;
       const u4_t ones = u4_t{one2, one2, one2, one2};
 #pragma unroll
@@ -299,6 +308,25 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[mb][nb][r] += s * (kH * Ph[mb][r] + Pl[mb][r] - cz * rs[mb][r]);
+      } else if constexpr (FI::kMX4) {
+        // one E8M0 scale per MFMA step (32 k): per step P against the offset
+        // codes OFF + (v + 8) and s_t (P - (OFF + 8) rowsum_t), s_t =
+        // 2^(X_t - 127) times the element's implicit 2^-2
+        const uint32_t magic = f16_act(FMT) ? 0x64006400u : 0x43004300u;
+        const float cz = (f16_act(FMT) ? 1024.f : 128.f) + 8.f;
+        const uint32_t xw = st.sraw[nb];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const u4_t bop = w16_operand(w[t], magic);
+          const uint32_t X = (xw >> (8 * t)) & 0xFFu;
+          const float sc = X == 255u ? __builtin_nanf("") : __builtin_amdgcn_ldexpf(1.0f, (int)X - 129);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const f4_t P = mfma16<FMT>(st.a[mb][t], bop, f4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[mb][nb][r] += sc * (P[r] - cz * rs4[mb][t][r]);
+          }
+        }
       } else if constexpr (FI::kAct16) {
         const uint32_t magic = f16_act(FMT) ? 0x64006400u : 0x43004300u;
         const float off = f16_act(FMT) ? 1024.f : 128.f;
@@ -581,6 +609,8 @@ int launch_skinny(int fmt, const SkinnyCfg& cfg, const SkinnyArgs& a, void* stre
     case FMT_W2BF16: return (int)launch_mb<FMT_W2BF16>(cfg, a, grid, block, lds, s);
     case FMT_W3F16: return (int)launch_mb<FMT_W3F16>(cfg, a, grid, block, lds, s);
     case FMT_W3BF16: return (int)launch_mb<FMT_W3BF16>(cfg, a, grid, block, lds, s);
+    case FMT_MX4F16: return (int)launch_mb<FMT_MX4F16>(cfg, a, grid, block, lds, s);
+    case FMT_MX4BF16: return (int)launch_mb<FMT_MX4BF16>(cfg, a, grid, block, lds, s);
     case FMT_I8: return (int)launch_mb<FMT_I8>(cfg, a, grid, block, lds, s);
     case FMT_Q8: return (int)launch_mb<FMT_Q8>(cfg, a, grid, block, lds, s);
     case FMT_F4: return (int)launch_mb<FMT_F4>(cfg, a, grid, block, lds, s);

@@ -71,7 +71,7 @@ struct TCfg {
   static constexpr int STAGES = ST;  // groups in the pipeline (ST - 1 ahead of the math)
   static constexpr int STAGE_BYTES = BM * ROWB;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-  static constexpr int META = mx_weights(FMT) ? 1 : 2;  // metadata loads per fragment
+  static constexpr int META = e8m0_meta(FMT) ? 1 : 2;  // metadata loads per fragment
   // vector-memory loads per step per wave (MXFP4 activations: plus one E8M0
   // word per m-block)
   static constexpr int LPS = SEGW + (TWO ? 2 : 1) * NBW + META * NBW + (ACT4 ? MB : 0);
@@ -161,7 +161,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
       return;
     }
     wbytes += ex * p.w_expert;
-    if constexpr (mx_weights(FMT)) {
+    if constexpr (e8m0_meta(FMT)) {
       e8 += ex * p.e8_expert;
     } else {
       scales16 += ex * p.s_expert;
@@ -234,7 +234,8 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
   for (int j = 0; j < NBW; ++j) {
     const int f0 = nblk(j) * G;  // first fragment of this column block
     woff[j] = f0 * C::FRAGB + lane * ((C::W2 || C::W3) ? 8 : 16);
-    soff[j] = mx_weights(FMT) ? f0 * 64 + (lane & ~3) : f0 * 32 + (c16 >> 1) * 4;
+    soff[j] = mxint4_weights(FMT) ? f0 * 64 + c16 * 4
+                                  : (mx_weights(FMT) ? f0 * 64 + (lane & ~3) : f0 * 32 + (c16 >> 1) * 4);
     zoff[j] = f0 * 8 + (c16 >> 3) * 4;
   }
 
@@ -281,7 +282,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
     // ring is carried round the loop, which forces a wait for every load there.
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
-      if constexpr (mx_weights(FMT)) {
+      if constexpr (e8m0_meta(FMT)) {
         sraw[slot][j] = __builtin_amdgcn_raw_buffer_load_b32(re, soff[j], gg * 64, 0);
       } else {
         sraw[slot][j] = __builtin_amdgcn_raw_buffer_load_b32(rs, soff[j], gg * 32, 0);
@@ -331,7 +332,40 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 
   auto compute = [&](auto slot_c) {
     constexpr int slot = decltype(slot_c)::value;
-    if constexpr (f16_act(FMT)) {
+    if constexpr (mxint4_weights(FMT)) {
+      // MXINT4: one E8M0 scale per column per MFMA step (32 k).  Per step P
+      // against the offset codes OFF + (v + 8) and s_t (P - (OFF + 8)
+      // rowsum_t), s_t = 2^(X_t - 127) times the element's implicit 2^-2.
+      constexpr bool F16 = f16_act(FMT);
+      u4_t bop[NBW][4];
+      float sc[NBW][4];
+#pragma unroll
+      for (int j = 0; j < NBW; ++j)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          bop[j][t] = w16_operand(braw[slot][j][t], magic_v);
+          const uint32_t X = (sraw[slot][j] >> (8 * t)) & 0xFFu;
+          sc[j][t] = X == 255u ? __builtin_nanf("") : __builtin_amdgcn_ldexpf(1.0f, (int)X - 129);
+        }
+      const float cz = (F16 ? 1024.f : 128.f) + 8.f;
+      const uint32_t one2 = F16 ? 0x3C003C00u : 0x3F803F80u;
+      const u4_t ones = u4_t{one2, one2, one2, one2};
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) {
+        u4_t a[4];
+        read_a16(slot, mb, a);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const f4_t rs = mfma_16x16x32<F16>(a[t], ones, f4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) {
+            const f4_t P = mfma_16x16x32<F16>(a[t], bop[j][t], f4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[mb][j][r] += sc[j][t] * (P[r] - cz * rs[r]);
+          }
+        }
+      }
+    } else if constexpr (f16_act(FMT)) {
       // Per k-step t: the MB x NBW MFMAs of step t, with the dequantisation
       // of step t+1's weights interleaved between them (the MFMA pipe runs
       // 16 cycles per op; the 4-cycle VALU ops fill the gaps), then t+1.
@@ -569,7 +603,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
       pin(braw[cur][j]);
       if constexpr (C::TWO) pin(braw2[cur][j]);
       pin(sraw[cur][j]);
-      if constexpr (!mx_weights(FMT)) pin(zraw[cur][j]);
+      if constexpr (!e8m0_meta(FMT)) pin(zraw[cur][j]);
     }
     if constexpr (C::ACT4) {
 #pragma unroll

@@ -77,12 +77,12 @@ __global__ void repack_zeros_kernel(const uint8_t* __restrict__ zeros, uint32_t*
 }
 
 __global__ void repack_e8m0_kernel(const uint8_t* __restrict__ e8, uint8_t* __restrict__ out, int64_t K,
-                                   int64_t per_expert, int64_t total) {
+                                   int64_t per_expert, int64_t total, int cols) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t e = i / per_expert;
     const int64_t eidx = i - e * per_expert;
-    out[i] = e8[e * per_expert + e8m0_src_index(K, eidx)];
+    out[i] = e8[e * per_expert + (cols ? e8m0_cols_src_index(K, eidx) : e8m0_src_index(K, eidx))];
   }
 }
 
@@ -120,11 +120,11 @@ int launch_repack(const hq_plan* p, const void* codes, const void* scales, const
   if (err != hipSuccess) return (int)err;
   uint8_t* meta = static_cast<uint8_t*>(meta_out);
   const size_t mpe = p->meta_bytes_per_expert;
-  if (mx_weights(p->fmt)) {
-    // per expert: E8M0 region only
+  if (e8m0_meta(p->fmt)) {
+    // per expert: E8M0 region only (MXINT4: one dword of four block scales per column)
     const int64_t per = N * K / 32;
     hipLaunchKernelGGL(repack_e8m0_kernel, grid_for(per * E), dim3(256), 0, s,
-                       static_cast<const uint8_t*>(zx), meta, K, per, per * E);
+                       static_cast<const uint8_t*>(zx), meta, K, per, per * E, mxint4_weights(p->fmt) ? 1 : 0);
     return (int)hipGetLastError();
   }
   // scales of every expert first, then zero points of every expert

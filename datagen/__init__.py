@@ -116,6 +116,16 @@ def dense_w3a16(M: int, N: int, K: int, act: str = "bf16", key=(9,)):
     return {"a": a, "codes": words, "scales": scales}
 
 
+def w4a16_mxint4(M: int, N: int, K: int, act: str = "bf16", key=(10,)):
+    """W4A16-MXINT4 inputs: 16-bit A, MXINT4 codes uniform over 0..15 (packed as
+    INT4), E8M0 block scales 2^-6..2^-2."""
+    rng = rng_for(*key, M, N, K)
+    a = _to_dtype(rng.standard_normal((M, K)), _dtype(act))
+    q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    e8 = (127 + rng.integers(-6, -1, size=(N, K // MX_BLOCK))).astype(np.uint8)
+    return {"a": a, "codes": pack_u4(q), "e8m0": e8}
+
+
 def w4a8_mxfp4(M: int, N: int, K: int, key=(3,)):
     """W4A8-MXFP4 inputs: fp8 e4m3 per-token A, E2M1 codes, E8M0 block scales."""
     rng = rng_for(*key, M, N, K)

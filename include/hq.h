@@ -51,9 +51,10 @@
  *       scales  fp16 or bf16 [N, K/G] (INT4 / INT8, G = 128): group g covers
  *               k in [G*g, G*g+G).
  *       zeros   uint8 [N, K/G] holding 0..15 (only with HQ_ZP_PER_GROUP_U4).
- *       e8m0    uint8 [N, K/32] (MXFP4): scale 2^(X-127) per 32 k.
+ *       e8m0    uint8 [N, K/32] (MXFP4, MXINT4): scale 2^(X-127) per 32 k.
  *     INT2 / INT3 / INT4 / INT8 dequantisation is w = (q - z) * s; MXFP4 is
- *     w = e2m1(q) * 2^(X-127).
+ *     w = e2m1(q) * 2^(X-127); MXINT4 is w = int4(q) * 2^-2 * 2^(X-127) with
+ *     int4 the two's-complement reading of the code (codes packed as INT4).
  *   * Activations: row-major [M, K] fp16 / bf16, or 8-bit codes (fp8 e4m3
  *     or int8) with one fp32 scale per row (value = code * scale[m]).
  *   * Output: row-major [M, N] fp16 / bf16, rounded to nearest even from
@@ -92,7 +93,8 @@ typedef enum hq_dtype {
   HQ_I32 = 8,
   HQ_U8 = 9,       /* unsigned 8-bit integer code 0..255 */
   HQ_U2 = 10,      /* unsigned 2-bit integer code 0..3 */
-  HQ_U3 = 11       /* unsigned 3-bit integer code 0..7 */
+  HQ_U3 = 11,      /* unsigned 3-bit integer code 0..7 */
+  HQ_I4 = 12       /* MXINT4 element: two's-complement 4-bit code, value (-8..7) * 2^-2 */
 } hq_dtype;
 
 typedef enum hq_zp_mode {
@@ -123,6 +125,9 @@ typedef enum hq_ascale_mode {
  *              (0..7, 4 for the symmetric case), act F16|BF16, act_scale
  *              NONE, out F16|BF16 (dense only; GPTQ INT3, the format
  *              cocoloop.cn names for the compatibility route)
+ *   W4A16-MXINT4 w_elem I4 (w_bits 4), group 32, scale E8M0, zp NONE,
+ *              act F16|BF16, act_scale NONE, out F16|BF16 (dense only;
+ *              MXINT4 is in the format list of cocoloop.cn, format section)
  *   W4A8-INT   w_elem U4, group 128, scale F16|BF16, zp FIXED (8),
  *              act INT8, act_scale PER_TOKEN_F32, out F16|BF16
  *   W4A8-FP8   w_elem U4, group 128, scale F16|BF16, zp FIXED|PER_GROUP_U4,

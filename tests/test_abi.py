@@ -568,3 +568,43 @@ def test_autotune_argument_checks():
     assert at(p._h, 1, None, None, fake, fake, fake, None, 0, 5, 0, None, None) == hq.HQ_ERR_INVALID_ARG
     assert at(p._h, 1, fake, fake, fake, fake, fake, None, 0, 5, 0, None, None) == hq.HQ_ERR_INVALID_ARG  # a_scale
     assert at(None, 1, fake, None, fake, fake, fake, None, 0, 5, 0, None, None) == hq.HQ_ERR_INVALID_ARG
+
+
+def test_repack_mxint4_layout():
+    """MXINT4: codes in the 16-bit operand order stored as q xor 8 (offset
+    binary), and one E8M0 dword per column per fragment holding the scales of
+    its four 32-k blocks (byte t = block 4g + t)."""
+    rng = np.random.default_rng(12)
+    q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    e8 = rng.integers(0, 256, size=(N, K // 32), dtype=np.uint8)
+    p = _plan(N, K, hq.w4a16_mxint4("bf16"), max_m=16)
+    w, meta = p.repack_host(torch.from_numpy(datagen.pack_u4(q)), e8m0=torch.from_numpy(e8))
+    assert meta.numel() == N * K // 32
+    fw = w.numpy().view(np.uint32).reshape(N // 16, K // 128, 64, 4)
+    fm = meta.numpy().reshape(N // 16, K // 128, 16, 4)
+    for nb in range(N // 16):
+        for g in range(K // 128):
+            assert np.array_equal(fm[nb, g], e8[16 * nb:16 * nb + 16, 4 * g:4 * g + 4])
+            for lane in range(0, 64, 7):
+                n = 16 * nb + lane % 16
+                for t in range(4):
+                    k0 = _k16(g, lane, t)
+                    for r in range(4):
+                        v = (int(fw[nb, g, lane, t]) >> (4 * r)) & 0x000F000F
+                        assert (v & 0xF) == q[n, k0 + 2 * r] ^ 8
+                        assert (v >> 16) == q[n, k0 + 2 * r + 1] ^ 8
+
+
+def test_mxint4_plans_and_validation():
+    p = _plan(4096, 4096, hq.w4a16_mxint4("f16"), max_m=1024)
+    wb, mb = p.repacked_bytes()
+    assert wb == 4096 * 4096 // 2 and mb == 4096 * 4096 // 32
+    assert "w4a16-mxint4-f16" in p.describe(1) and "kernel=tiled" in p.describe(1024)
+    with pytest.raises(hq.HQError):   # block 32 only
+        _plan(quant=hq.QuantDesc(hq.I4, 4, 128, hq.E8M0, hq.ZP_NONE, 0, hq.BF16, 0, hq.BF16))
+    with pytest.raises(hq.HQError):   # E8M0 scales only
+        _plan(quant=hq.QuantDesc(hq.I4, 4, 32, hq.BF16, hq.ZP_NONE, 0, hq.BF16, 0, hq.BF16))
+    with pytest.raises(hq.HQError):   # 16-bit activations only
+        _plan(quant=hq.QuantDesc(hq.I4, 4, 32, hq.E8M0, hq.ZP_NONE, 0, hq.FP8_E4M3, 1, hq.BF16))
+    with pytest.raises(hq.HQError):   # dense only
+        hq.MoePlan(512, 7168, hq.w4a16_mxint4("bf16"), 256, 4096, "silu_mul")
