@@ -32,6 +32,10 @@ Readings where the pages are silent:
   two's-complement elements with an implicit 2^-2 (formats.mxint4_value),
   one E8M0 scale 2^(X-127) per 32 k as for MXFP4; with fp16/bf16
   activations C = A . W^T, W exact in float64.
+* NVFP4 weights (the pages list NVFP4 among the formats): E2M1 elements,
+  one FP8 E4M3 scale per 16 k and one float32 scale per tensor (NVIDIA's
+  published definition of the format); w = e2m1(q) * e4m3(s_b) * s_t, exact
+  in float64; with fp16/bf16 activations C = A . W^T.
 * W4A8-INT: the int32 accumulator of one group is
   P[m,n,g] = sum_{k in g} a_q[m,k] * (q[n,k] - 8), and
   C = s_a[m] * sum_g s[n,g] * P[m,n,g].
@@ -243,6 +247,28 @@ def gemm_mxint4_w16(a, w_codes, e8m0, out_fmt: str = "bf16"):
     MXINT4 weights (mxint4_weights), float64."""
     a = np.asarray(a, dtype=np.float64)
     w = mxint4_weights(w_codes, e8m0)
+    c64 = a @ w.T
+    return {"c64": c64, "c_out": rne(c64, out_fmt), "tau": tolerance(a, w), "w": w}
+
+
+def nvfp4_weights(codes, e4m3_scales, tensor_scale, block: int = 16) -> np.ndarray:
+    """w[n,k] = e2m1(q[n,k]) * e4m3(S[n, k//16]) * s_t, exact in float64."""
+    q = unpack_u4(codes)
+    N, K = q.shape
+    sb = e4m3_value(np.asarray(e4m3_scales))
+    if sb.shape != (N, K // block):
+        raise ValueError("E4M3 block scales must be [N, K/16]")
+    w = e2m1_value(q)
+    for b in range(K // block):
+        w[:, b * block : (b + 1) * block] *= sb[:, b : b + 1]
+    return w * float(tensor_scale)
+
+
+def gemm_nvfp4_w16(a, w_codes, e4m3_scales, tensor_scale, out_fmt: str = "bf16"):
+    """W4A16-NVFP4: C = A . W^T with fp16/bf16 activation values A and the
+    NVFP4 weights (nvfp4_weights), float64."""
+    a = np.asarray(a, dtype=np.float64)
+    w = nvfp4_weights(w_codes, e4m3_scales, tensor_scale)
     c64 = a @ w.T
     return {"c64": c64, "c_out": rne(c64, out_fmt), "tau": tolerance(a, w), "w": w}
 

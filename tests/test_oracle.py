@@ -579,3 +579,35 @@ def test_mxint4_nan_scale_propagates():
     q[0, 3] = 5
     w = G.mxint4_weights(datagen.pack_u4(q), np.array([[255]], np.uint8))
     assert np.isnan(w).all()
+
+
+# ----------------------------------------------------------- NVFP4 weights --
+
+def test_nvfp4_hand_example():
+    g = _gold("nvfp4_gemm_2x2.json")
+    words = np.array([[int(h, 16) for h in row] for row in g["packed_words_hex"]], dtype=np.uint32).view(np.int32)
+    assert F.unpack_u4(words).tolist() == g["codes_rows"]
+    r = G.gemm_nvfp4_w16(np.array(g["a"], float), words, np.array(g["e4m3_scales"], dtype=np.uint8),
+                         g["tensor_scale"])
+    assert r["c64"].tolist() == g["c"]
+
+
+def test_nvfp4_agrees_with_mxfp4_on_power_of_two_scales():
+    """E4M3 scales that are powers of two, equal on both halves of every 32-block,
+    with tensor scale 1, are E8M0 block scales: the MXFP4 weights."""
+    rng = np.random.default_rng(36)
+    q = rng.integers(0, 16, size=(5, 256), dtype=np.uint8)
+    ex = rng.integers(-6, 8, size=(5, 8))            # 2^ex, all E4M3 normals
+    e4 = ((ex + 7) << 3).astype(np.uint8)            # E4M3 code of 2^ex (mantissa 0)
+    w_nv = G.nvfp4_weights(datagen.pack_u4(q), np.repeat(e4, 2, axis=1), 1.0)
+    w_mx = G.mxfp4_weights(datagen.pack_u4(q), (ex + 127).astype(np.uint8))
+    assert np.array_equal(w_nv, w_mx)
+
+
+def test_nvfp4_block_of_16_and_tensor_scale():
+    """Each 16-block takes its own scale, and the tensor scale multiplies all."""
+    q = np.full((1, 32), 0x2, np.uint8)              # E2M1 1.0 everywhere
+    w = G.nvfp4_weights(datagen.pack_u4(q), np.array([[0x38, 0x40]], np.uint8), 0.5)
+    assert w[0, :16].tolist() == [0.5] * 16 and w[0, 16:].tolist() == [1.0] * 16
+    wn = G.nvfp4_weights(datagen.pack_u4(q), np.array([[0x7F, 0x40]], np.uint8), 1.0)
+    assert np.isnan(wn[0, :16]).all() and (wn[0, 16:] == 2.0).all()
