@@ -237,6 +237,8 @@ _WORKLOAD_PROFILES = {
     "w3a16": ("qgemm_w3a16_bf16_n4096_k4096.md", "dense W3A16, M in {1,16,64,1024}, N = K = 4096, bf16"),
     "mxint4": ("qgemm_w4a16_mxint4_bf16_n4096_k4096.md", "dense W4A16-MXINT4, M in {1,16,64,1024}, N = K = 4096, "
                "bf16"),
+    "nvfp4": ("qgemm_w4a16_nvfp4_bf16_n4096_k4096.md", "dense W4A16-NVFP4, M in {1,16,64,1024}, N = K = 4096, "
+              "bf16"),
     "moe": ("moe_layer_e256_top8_h7168_i256.md", "MoE layer, 256 experts, top-8, hidden 7168, intermediate 256, "
             "T in {1,32,512,4096}, bf16 and fp8 activations"),
 }
@@ -664,26 +666,36 @@ def _w2a16_points(dev, bits=2):
         f"bf16 scales, zero point {zp}), bf16 output", "bf16"
 
 
-def _mxint4_points(dev):
+def _mxint4_points(dev, nv=False):
     import bit_quantized_gemm_repack_amd as hq
     import datagen
 
     N = K = 4096
     pts = []
     for M in (1, 16, 64, 1024):
-        d = datagen.w4a16_mxint4(M, N, K, act="bf16")
-        plan = hq.Plan(N, K, hq.w4a16_mxint4("bf16"), max_m=M)
-        w, meta = plan.repack(torch.from_numpy(d["codes"]).to(dev), e8m0=torch.from_numpy(d["e8m0"]).to(dev))
+        if nv:
+            d = datagen.w4a16_nvfp4(M, N, K, act="bf16")
+            plan = hq.Plan(N, K, hq.w4a16_nvfp4("bf16"), max_m=M)
+            w, meta = plan.repack(torch.from_numpy(d["codes"]).to(dev), torch.from_numpy(d["tscale"]).to(dev),
+                                  e8m0=torch.from_numpy(d["e4m3"]).to(dev))
+        else:
+            d = datagen.w4a16_mxint4(M, N, K, act="bf16")
+            plan = hq.Plan(N, K, hq.w4a16_mxint4("bf16"), max_m=M)
+            w, meta = plan.repack(torch.from_numpy(d["codes"]).to(dev), e8m0=torch.from_numpy(d["e8m0"]).to(dev))
         R = 128  # 128 copies of 8.9 MB: > 1 GB
         ws_ = [(w.clone(), meta.clone()) for _ in range(R)]
         a = d["a"].to(dev)
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         ws = plan.workspace(M, dev)
-        byt = N * K // 2 + N * (K // 32) + 2 * M * K + 2 * M * N
+        byt = N * K // 2 + N * (K // (16 if nv else 32)) + 2 * M * K + 2 * M * N
         pts.append(dict(name=f"M={M} N={N} K={K}", R=R, bytes=byt, flops=2 * M * N * K, peak=FP16_PEAK_TFLOPS,
                         plan=plan.describe(M),
                         calls=lambda r, plan=plan, ws_=ws_, a=a, out=out, ws=ws:
                         [lambda: plan.gemm(a, ws_[r][0], ws_[r][1], out=out, ws=ws)]))
+    if nv:
+        return pts, "quantized GEMM TFLOPS and effective HBM GB/s vs M (W4A16-NVFP4)", \
+            "dense W4A16-NVFP4: M in {1,16,64,1024}, N = K = 4096, bf16 activations, NVFP4 weights (one E4M3 scale " \
+            "per 16 k, fp32 tensor scale), bf16 output", "bf16"
     return pts, "quantized GEMM TFLOPS and effective HBM GB/s vs M (W4A16-MXINT4)", \
         "dense W4A16-MXINT4: M in {1,16,64,1024}, N = K = 4096, bf16 activations, MXINT4 weights (one E8M0 scale " \
         "per 32 k), bf16 output", "bf16"
@@ -917,6 +929,12 @@ def _cpu_sample(workload, budget):
             t0 = time.perf_counter()
             og.gemm_mxint4_w16(d["a"].double().numpy(), d["codes"], d["e8m0"], out_fmt="bf16")
             what = "dense W4A16-MXINT4 M=8 N=K=4096"
+        elif workload == "nvfp4":
+            M, N, K = 8, 4096, 4096
+            d = datagen.w4a16_nvfp4(M, N, K, act="bf16")
+            t0 = time.perf_counter()
+            og.gemm_nvfp4_w16(d["a"].double().numpy(), d["codes"], d["e4m3"], float(d["tscale"][0]), out_fmt="bf16")
+            what = "dense W4A16-NVFP4 M=8 N=K=4096"
         elif workload == "w4a4":
             M, N, K = 16, 4096, 7168
             d = datagen.w4a4_mxfp4(M, N, K)
@@ -964,10 +982,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--autotune", action="store_true",
                     help="decode: install a measured execution choice per point (hq_plan_autotune) first")
-    ap.add_argument("--workload", choices=("decode", "quant", "prefill", "w4a8", "w4a4", "w8a16", "w2a16", "w3a16", "mxint4", "moe"),
+    ap.add_argument("--workload", choices=("decode", "quant", "prefill", "w4a8", "w4a4", "w8a16", "w2a16", "w3a16", "mxint4", "nvfp4", "moe"),
                     default="decode",
                     help="decode: the dense W4A16 decode sweep (default); quant: the per-token quantiser; "
-                         "prefill / w4a8 / w4a4 / w8a16 / w2a16 / w3a16 / mxint4 / moe: the other GEMM workloads")
+                         "prefill / w4a8 / w4a4 / w8a16 / w2a16 / w3a16 / mxint4 / nvfp4 / moe: the other GEMM workloads")
     ap.add_argument("--write-profiles", metavar="RUN_DIR",
                     help="CPU only: write the profiles/ summaries from rocprofv3 outputs in RUN_DIR and exit")
     args = ap.parse_args()
@@ -981,10 +999,11 @@ def main():
     if args.workload == "quant":
         run_quant(args)
         return
-    if args.workload in ("prefill", "w4a8", "w4a4", "w8a16", "w2a16", "w3a16", "mxint4", "moe"):
+    if args.workload in ("prefill", "w4a8", "w4a4", "w8a16", "w2a16", "w3a16", "mxint4", "nvfp4", "moe"):
         run_points_workload(args, {"prefill": _prefill_points, "w4a8": _w4a8_points, "w4a4": _w4a4_points,
                                    "w8a16": _w8a16_points, "w2a16": _w2a16_points,
                                    "w3a16": lambda dev: _w2a16_points(dev, 3), "mxint4": _mxint4_points,
+                                   "nvfp4": lambda dev: _mxint4_points(dev, nv=True),
                                    "moe": _moe_points}[args.workload])
         return
 

@@ -120,6 +120,14 @@ def w4a16_mxint4(act: str = "bf16", out: Optional[str] = None) -> QuantDesc:
     return QuantDesc(I4, 4, 32, E8M0, ZP_NONE, 0, _DT[act], ASCALE_NONE, _DT[out or act])
 
 
+def w4a16_nvfp4(act: str = "bf16", out: Optional[str] = None) -> QuantDesc:
+    """NVFP4 weights (E2M1 codes packed as INT4, one E4M3 scale per 16 k as
+    uint8 [N, K/16], one fp32 tensor scale) x fp16/bf16 activations.  Repack
+    with scales = the tensor scale (float32 [1], or [E] for stacked weights)
+    and e8m0 = the E4M3 block scales."""
+    return QuantDesc(FP4_E2M1, 4, 16, FP8_E4M3, ZP_NONE, 0, _DT[act], ASCALE_NONE, _DT[out or act])
+
+
 def w4a8_int(scale: str = "f16", out: str = "bf16") -> QuantDesc:
     """INT4 (group 128, zero 8) weights x int8 per-token activations."""
     return QuantDesc(U4, 4, 128, _DT[scale], ZP_FIXED, 8, INT8, ASCALE_PER_TOKEN_F32, _DT[out])

@@ -118,6 +118,15 @@ hq_status classify(const hq_quant_desc& q, int* fmt) {
         return fail(HQ_ERR_UNSUPPORTED, "unsupported activation dtype %d for INT4 weights", (int)q.act);
     }
   }
+  if (q.w_elem == HQ_FP4_E2M1 && q.scale == HQ_FP8_E4M3) {
+    // NVFP4: E2M1 elements, one E4M3 scale per 16 k, an fp32 tensor scale
+    if (q.w_bits != 4 || q.group_size != 16 || q.zp != HQ_ZP_NONE)
+      return fail(HQ_ERR_UNSUPPORTED, "NVFP4 weights take one E4M3 scale per 16 k and no zero point");
+    if ((q.act != HQ_F16 && q.act != HQ_BF16) || q.act_scale != HQ_ASCALE_NONE)
+      return fail(HQ_ERR_UNSUPPORTED, "NVFP4 weights are implemented with fp16 / bf16 activations");
+    *fmt = q.act == HQ_F16 ? hq::FMT_NV4F16 : hq::FMT_NV4BF16;
+    return HQ_OK;
+  }
   if (q.w_elem == HQ_FP4_E2M1) {
     if (q.group_size != 32) return fail(HQ_ERR_UNSUPPORTED, "MXFP4 needs block size 32");
     if (q.scale != HQ_E8M0) return fail(HQ_ERR_UNSUPPORTED, "MXFP4 needs E8M0 block scales");
@@ -148,6 +157,8 @@ const char* fmt_name(int fmt) {
     case hq::FMT_W3BF16: return "w3a16-bf16";
     case hq::FMT_MX4F16: return "w4a16-mxint4-f16";
     case hq::FMT_MX4BF16: return "w4a16-mxint4-bf16";
+    case hq::FMT_NV4F16: return "w4a16-nvfp4-f16";
+    case hq::FMT_NV4BF16: return "w4a16-nvfp4-bf16";
     case hq::FMT_I8: return "w4a8-int8";
     case hq::FMT_Q8: return "w4a8-fp8";
     case hq::FMT_F4: return "w4a8-mxfp4";
@@ -428,7 +439,10 @@ hq_status hq_plan_create(const hq_layer_desc* layer, const hq_compute* compute, 
     p->fmt = fmt;
     const int64_t N = layer->n, K = layer->k, G = K / 128;
     p->w_bytes_per_expert = (size_t)N * (size_t)K * (size_t)hq::frag_bytes(fmt) / (size_t)(hq::kFragN * hq::kFragK);
-    if (hq::e8m0_meta(fmt)) {
+    if (hq::nvfp4_weights(fmt)) {
+      p->scale_region_bytes = 0;  // E4M3 region, then the fp32 tensor scale (16 bytes)
+      p->meta_bytes_per_expert = (size_t)(N * K / 16 + 16);
+    } else if (hq::e8m0_meta(fmt)) {
       p->scale_region_bytes = 0;
       p->meta_bytes_per_expert = (size_t)(N * K / 32);
     } else {
@@ -491,7 +505,9 @@ hq_status hq_repacked_bytes(const hq_plan* p, size_t* w_bytes, size_t* meta_byte
 static hq_status check_repack_args(const hq_plan* p, const void* codes, const void* scales, const void* zx,
                                    const void* w_out, const void* meta_out) {
   if (!p || !codes || !w_out || !meta_out) return fail(HQ_ERR_INVALID_ARG, "null argument");
-  if (hq::e8m0_meta(p->fmt)) {
+  if (hq::nvfp4_weights(p->fmt)) {
+    if (!zx || !scales) return fail(HQ_ERR_INVALID_ARG, "NVFP4 repack needs the E4M3 block scales and the tensor scale");
+  } else if (hq::e8m0_meta(p->fmt)) {
     if (!zx) return fail(HQ_ERR_INVALID_ARG, "MXFP4 / MXINT4 repack needs the E8M0 scales");
   } else {
     if (!scales) return fail(HQ_ERR_INVALID_ARG, "INT4 repack needs the group scales");
@@ -545,6 +561,17 @@ hq_status hq_repack_host(const hq_plan* p, const void* codes, const void* scales
         for (int64_t i = 0; i < wpe; ++i) wo[e * wpe + i] = hq::repack_word(cw + e * wpe, K, p->fmt, i);
     }
     uint8_t* meta = static_cast<uint8_t*>(meta_out);
+    if (hq::nvfp4_weights(p->fmt)) {
+      const int64_t per = N * K / 16;
+      const uint8_t* src = static_cast<const uint8_t*>(zx);
+      for (int64_t e = 0; e < E; ++e) {
+        uint8_t* me = meta + e * (int64_t)p->meta_bytes_per_expert;
+        for (int64_t i = 0; i < per; ++i) me[i] = src[e * per + hq::e4m3_src_index(K, i)];
+        std::memset(me + per, 0, 16);
+        std::memcpy(me + per, static_cast<const float*>(scales) + e, 4);
+      }
+      return ok();
+    }
     if (hq::e8m0_meta(p->fmt)) {
       const int64_t per = N * K / 32;
       const uint8_t* src = static_cast<const uint8_t*>(zx);
@@ -629,6 +656,8 @@ hq_status dense_run(const hq_plan* p, const hq::Exec& e, int64_t m, const void* 
       t.a_e8m0 = a_e8m0;
       t.w = w;
       if (hq::e8m0_meta(p->fmt)) t.e8m0 = static_cast<const uint8_t*>(meta);
+      if (hq::nvfp4_weights(p->fmt))
+        t.tscale = reinterpret_cast<const float*>(static_cast<const uint8_t*>(meta) + N * K / 16);
       else t.scales = meta;
       t.zeros = zeros;
       t.out = out;
@@ -660,6 +689,8 @@ hq_status dense_run(const hq_plan* p, const hq::Exec& e, int64_t m, const void* 
     args.w = w;
     if (hq::e8m0_meta(p->fmt)) {
       args.e8m0 = static_cast<const uint8_t*>(meta);
+      if (hq::nvfp4_weights(p->fmt))
+        args.tscale = reinterpret_cast<const float*>(static_cast<const uint8_t*>(meta) + N * K / 16);
     } else {
       args.scales = meta;
       args.zeros = zeros;

@@ -91,6 +91,37 @@ __device__ inline u4_t w1_operand(uint32_t x, uint32_t magic, int t) {
               ((y >> 3) & 0x00010001u) | magic};
 }
 
+// NVFP4 weights -> the 16-bit operand of one MFMA step, dequantised exactly.
+// x holds the step's 8 E2M1 codes in the 16-bit operand order (nibbles r and
+// 4 + r are elements 2r and 2r + 1); sb is the E4M3 code of their 16-k block.
+// Each value is e2m1(q) * e4m3(sb) * 2^-8: the E2M1 bits placed as an fp16
+// (sign to bit 15, exponent and mantissa to bits 9..11) are e2m1(q) * 2^-14;
+// the E4M3 bits placed as an fp16 are e4m3(sb) * 2^-8, times 2^14 exactly;
+// their product has at most 6 significant bits and lies in [2^-18, 10.5], so
+// it is exact in fp16 and, widened and truncated, in bf16.  The kernel's
+// epilogue multiplies by 2^8 and the tensor scale.  An E4M3 NaN code gives NaN.
+template <bool BF16>
+__device__ inline u4_t nvfp4_operand(uint32_t x, uint32_t sb) {
+  _Float16 S = __builtin_bit_cast(_Float16, (uint16_t)(((sb & 0x80u) << 8) | ((sb & 0x7Fu) << 7))) * (_Float16)16384.f;
+  if ((sb & 0x7Fu) == 0x7Fu) S = (_Float16)__builtin_nanf("");
+  const h2_t S2 = h2_t{S, S};
+  u4_t out;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t u = (x >> (4 * r)) & 0x000F000Fu;
+    const uint32_t bits = ((u & 0x00070007u) << 9) | ((u & 0x00080008u) << 12);
+    const h2_t v = __builtin_bit_cast(h2_t, bits) * S2;
+    if constexpr (BF16) {
+      const uint32_t lo = __builtin_bit_cast(uint32_t, (float)v[0]);
+      const uint32_t hi = __builtin_bit_cast(uint32_t, (float)v[1]);
+      out[r] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);  // the upper halves: exact bf16
+    } else {
+      out[r] = __builtin_bit_cast(uint32_t, v);
+    }
+  }
+  return out;
+}
+
 // Two words of NIB_B8 codes stored as q ^ 8 -> the int8 operand (16 values)
 // holding 16 * (q - 8) exactly.
 __device__ inline i4_t i8_operand(uint32_t w0, uint32_t w1) {

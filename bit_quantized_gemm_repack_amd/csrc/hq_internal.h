@@ -73,7 +73,9 @@ enum Fmt : int {
   FMT_W3F16 = 10,  // INT3 weight, fp16 activation (2-bit + 1-bit planes), fp16 MFMA
   FMT_W3BF16 = 11, // INT3 weight, bf16 activation (2-bit + 1-bit planes), bf16 MFMA
   FMT_MX4F16 = 12, // MXINT4 weight (E8M0 per 32 k), fp16 activation, fp16 MFMA
-  FMT_MX4BF16 = 13 // MXINT4 weight (E8M0 per 32 k), bf16 activation, bf16 MFMA
+  FMT_MX4BF16 = 13, // MXINT4 weight (E8M0 per 32 k), bf16 activation, bf16 MFMA
+  FMT_NV4F16 = 14,  // NVFP4 weight (E4M3 per 16 k + fp32 tensor scale), fp16 activation, fp16 MFMA
+  FMT_NV4BF16 = 15  // NVFP4 weight, bf16 activation, bf16 MFMA
 };
 
 // INT8 weights: stored as two 4-bit planes (high nibbles, then low nibbles)
@@ -89,14 +91,19 @@ HQ_HD constexpr inline bool w3_weights(int fmt) { return fmt == FMT_W3F16 || fmt
 // MXINT4 weights: two's-complement codes stored offset by 8 (q xor 8) in the
 // 16-bit operand order, one E8M0 scale per column per 32 k, i.e. per MFMA step.
 HQ_HD constexpr inline bool mxint4_weights(int fmt) { return fmt == FMT_MX4F16 || fmt == FMT_MX4BF16; }
-// fp16 / bf16 activations (INT2, INT3, INT4, INT8 or MXINT4 weights)
+// NVFP4 weights: E2M1 codes in the 16-bit operand order, dequantised in
+// registers (a lane's 8 k of one MFMA step lie in one 16-k block).
+HQ_HD constexpr inline bool nvfp4_weights(int fmt) { return fmt == FMT_NV4F16 || fmt == FMT_NV4BF16; }
+// fp16 / bf16 activations (INT2, INT3, INT4, INT8, MXINT4 or NVFP4 weights)
 HQ_HD constexpr inline bool act16_fmt(int fmt) {
   return fmt == FMT_W16F16 || fmt == FMT_W16BF16 || fmt == FMT_W8F16 || fmt == FMT_W8BF16 || fmt == FMT_W2F16 ||
-         fmt == FMT_W2BF16 || fmt == FMT_W3F16 || fmt == FMT_W3BF16 || fmt == FMT_MX4F16 || fmt == FMT_MX4BF16;
+         fmt == FMT_W2BF16 || fmt == FMT_W3F16 || fmt == FMT_W3BF16 || fmt == FMT_MX4F16 || fmt == FMT_MX4BF16 ||
+         fmt == FMT_NV4F16 || fmt == FMT_NV4BF16;
 }
 // fp16 (rather than bf16) activations
 HQ_HD constexpr inline bool f16_act(int fmt) {
-  return fmt == FMT_W16F16 || fmt == FMT_W8F16 || fmt == FMT_W2F16 || fmt == FMT_W3F16 || fmt == FMT_MX4F16;
+  return fmt == FMT_W16F16 || fmt == FMT_W8F16 || fmt == FMT_W2F16 || fmt == FMT_W3F16 || fmt == FMT_MX4F16 ||
+         fmt == FMT_NV4F16;
 }
 // Weight bytes of one 16 x 128 fragment.
 HQ_HD constexpr inline int frag_bytes(int fmt) {
@@ -105,8 +112,11 @@ HQ_HD constexpr inline int frag_bytes(int fmt) {
 
 // MXFP4 weights (E2M1 codes in natural order + E8M0 block scales).
 HQ_HD constexpr inline bool mx_weights(int fmt) { return fmt == FMT_F4 || fmt == FMT_F44; }
-// Metadata is one E8M0 region (MXFP4 or MXINT4 weights) rather than scales + zeros.
-HQ_HD constexpr inline bool e8m0_meta(int fmt) { return mx_weights(fmt) || mxint4_weights(fmt); }
+// Metadata is one region of byte scales (E8M0 for MXFP4 / MXINT4, E4M3 for
+// NVFP4) rather than 16-bit scales + zero points.
+HQ_HD constexpr inline bool e8m0_meta(int fmt) { return mx_weights(fmt) || mxint4_weights(fmt) || nvfp4_weights(fmt); }
+// Bytes of that region per 16 x 128 fragment.
+HQ_HD constexpr inline int byte_meta_frag(int fmt) { return nvfp4_weights(fmt) ? 128 : 64; }
 
 enum NibOrder : int { NIB_W16 = 0, NIB_B8 = 1, NIB_NAT = 2 };
 
@@ -283,6 +293,20 @@ HQ_HD inline int64_t e8m0_cols_src_index(int64_t K, int64_t eidx) {
   return (nb * kFragN + c) * (K / 32) + 4 * g + t;
 }
 
+// Byte eidx of the NVFP4 E4M3 region [N/16][G][16 columns][2 halves][4 steps]
+// (lane (c, kq) reads the dword of half kq/2: byte t is the scale of the
+// 16-k block 2t + kq/2 that its 8 k of MFMA step t fall in) <- canonical
+// [N][K/16].
+HQ_HD inline int64_t e4m3_src_index(int64_t K, int64_t eidx) {
+  const int64_t G = K / kFragK;
+  const int t = (int)(eidx & 3);
+  const int h = (int)((eidx >> 2) & 1);
+  const int c = (int)((eidx >> 3) & 15);
+  const int64_t g = (eidx >> 7) % G;
+  const int64_t nb = (eidx >> 7) / G;
+  return (nb * kFragN + c) * (K / 16) + 8 * g + 2 * t + h;
+}
+
 // ---------------------------------------------------------------------------
 // Plan
 // ---------------------------------------------------------------------------
@@ -344,6 +368,7 @@ struct SkinnyArgs {
   const void* scales;
   const uint32_t* zeros;  // nibble-packed, or null
   const uint8_t* e8m0;
+  const float* tscale;  // NVFP4: the fp32 tensor scale (device)
   void* out;
   float* part;       // [split][M][N] fp32 partials (split > 1)
   int M, N, K, G;
@@ -399,6 +424,7 @@ struct TiledArgs {
   const void* scales;
   const uint32_t* zeros;
   const uint8_t* e8m0;
+  const float* tscale;  // NVFP4: the fp32 tensor scale (device)
   void* out;
   int M, N, K, G;
   int zp_fixed;

@@ -48,6 +48,7 @@ struct FmtInfo {
   static constexpr bool kW2 = w2_weights(FMT);  // INT2 weights: 8 bytes per lane per fragment
   static constexpr bool kW3 = w3_weights(FMT);  // INT3 weights: INT2 plane (8 B) + 1-bit plane (4 B) per lane
   static constexpr bool kMX4 = mxint4_weights(FMT);  // MXINT4: one E8M0 scale per column per MFMA step
+  static constexpr bool kNV4 = nvfp4_weights(FMT);   // NVFP4: E4M3 per 16 k, dequantised in registers
   static constexpr bool kAct4 = (FMT == FMT_F44);  // MXFP4 activations
   static constexpr int kAVec = kAct16 ? 4 : (kAct4 ? 1 : 2);  // 16-byte loads per lane per group
   static constexpr int kARowB = kAct16 ? 256 : (kAct4 ? 64 : 128);  // A bytes per row per group
@@ -151,7 +152,9 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   [[maybe_unused]] const auto rsc = rsrc(scales16, nfrag * 32);
   [[maybe_unused]] const auto rz = rsrc(zeros32 ? static_cast<const void*>(zeros32) : static_cast<const void*>(scales16),
                                         zeros32 ? nfrag * 8 : nfrag * 32);
-  [[maybe_unused]] const auto re = rsrc(e8, nfrag * 64);
+  [[maybe_unused]] const auto re = rsrc(e8, nfrag * byte_meta_frag(FMT));
+  // NVFP4: the operands carry e2m1 * e4m3 * 2^-8; the epilogue applies 2^8 and the tensor scale
+  [[maybe_unused]] const float nv_scale = FI::kNV4 ? 256.f * p.tscale[0] : 1.f;
   // MXFP4 activation scales, group-major words: word (g, row) holds the four
   // E8M0 block scales of the row's group g
   [[maybe_unused]] const auto rae = rsrc(p.a_e8m0, (int64_t)G * a_rows * 4);
@@ -179,7 +182,9 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   for (int nb = 0; nb < NB; ++nb) {
     const int f0 = nblk(nb) * G;
     woff[nb] = f0 * kFragB + lane * ((FI::kW2 || FI::kW3) ? 8 : 16);
-    soff[nb] = FI::kMX4 ? f0 * 64 + c * 4 : (mx_weights(FMT) ? f0 * 64 + (lane & ~3) : f0 * 32 + (c >> 1) * 4);
+    soff[nb] = FI::kNV4   ? f0 * 128 + c * 8 + (kq >> 1) * 4
+               : FI::kMX4 ? f0 * 64 + c * 4
+                          : (mx_weights(FMT) ? f0 * 64 + (lane & ~3) : f0 * 32 + (c >> 1) * 4);
     zoff[nb] = f0 * 8 + (c >> 3) * 4;
   }
 
@@ -228,7 +233,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       if constexpr (e8m0_meta(FMT)) {
-        st.sraw[nb] = __builtin_amdgcn_raw_buffer_load_b32(re, soff[nb], g * 64, 0);
+        st.sraw[nb] = __builtin_amdgcn_raw_buffer_load_b32(re, soff[nb], g * byte_meta_frag(FMT), 0);
       } else {
         st.sraw[nb] = __builtin_amdgcn_raw_buffer_load_b32(rsc, soff[nb], g * 32, 0);
         st.zraw[nb] = __builtin_amdgcn_raw_buffer_load_b32(rz, zoff[nb], g * 8, 0);
@@ -259,7 +264,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int t = 0; t < 4; ++t) rs4[mb][t] = mfma16<FMT>(st.a[mb][t], ones, f4_t{0.f, 0.f, 0.f, 0.f});
-    } else if constexpr (FI::kAct16) {
+    } else if constexpr (FI::kAct16 && !FI::kNV4) {
       const uint32_t one2 = f16_act(FMT) ? 0x3C003C00u : 0x3F803F80u;
       const u4_t ones = u4_t{one2, one2, one2, one2};
 #pragma unroll
@@ -308,6 +313,16 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[mb][nb][r] += s * (kH * Ph[mb][r] + Pl[mb][r] - cz * rs[mb][r]);
+      } else if constexpr (FI::kNV4) {
+        // weights dequantised exactly in registers (nvfp4_operand); no zero
+        // point, so no row-sum correction
+        const uint32_t sw = st.sraw[nb];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const u4_t bop = nvfp4_operand<!f16_act(FMT)>(w[t], (sw >> (8 * t)) & 0xFFu);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = mfma16<FMT>(st.a[mb][t], bop, acc[mb][nb]);
+        }
       } else if constexpr (FI::kMX4) {
         // one E8M0 scale per MFMA step (32 k): per step P against the offset
         // codes OFF + (v + 8) and s_t (P - (OFF + 8) rowsum_t), s_t =
@@ -491,6 +506,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
     }
     if (m >= p.M) continue;
     if (FI::kActScale) v *= p.a_scale[m];
+    if constexpr (FI::kNV4) v *= nv_scale;
     if (S == 1) {
       const uint16_t o = p.out_bf16 ? float_to_bf16_bits(v) : float_to_f16_bits(v);
       static_cast<uint16_t*>(p.out)[(int64_t)m * p.N + n] = o;
@@ -611,6 +627,8 @@ int launch_skinny(int fmt, const SkinnyCfg& cfg, const SkinnyArgs& a, void* stre
     case FMT_W3BF16: return (int)launch_mb<FMT_W3BF16>(cfg, a, grid, block, lds, s);
     case FMT_MX4F16: return (int)launch_mb<FMT_MX4F16>(cfg, a, grid, block, lds, s);
     case FMT_MX4BF16: return (int)launch_mb<FMT_MX4BF16>(cfg, a, grid, block, lds, s);
+    case FMT_NV4F16: return (int)launch_mb<FMT_NV4F16>(cfg, a, grid, block, lds, s);
+    case FMT_NV4BF16: return (int)launch_mb<FMT_NV4BF16>(cfg, a, grid, block, lds, s);
     case FMT_I8: return (int)launch_mb<FMT_I8>(cfg, a, grid, block, lds, s);
     case FMT_Q8: return (int)launch_mb<FMT_Q8>(cfg, a, grid, block, lds, s);
     case FMT_F4: return (int)launch_mb<FMT_F4>(cfg, a, grid, block, lds, s);

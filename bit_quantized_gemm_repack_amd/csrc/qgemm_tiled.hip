@@ -19,6 +19,8 @@ int launch_tiled(int fmt, const TiledCfgRt& cfg, const TiledArgs& a, void* strea
     case FMT_W3BF16: return (int)launch_tiled_f<FMT_W3BF16, GRP_DENSE>(cfg, a, grid, s);
     case FMT_MX4F16: return (int)launch_tiled_f<FMT_MX4F16, GRP_DENSE>(cfg, a, grid, s);
     case FMT_MX4BF16: return (int)launch_tiled_f<FMT_MX4BF16, GRP_DENSE>(cfg, a, grid, s);
+    case FMT_NV4F16: return (int)launch_tiled_f16(fmt, GRP_DENSE, cfg, a, grid, s);
+    case FMT_NV4BF16: return (int)launch_tiled_f<FMT_NV4BF16, GRP_DENSE>(cfg, a, grid, s);
     case FMT_I8: return (int)launch_tiled_f<FMT_I8, GRP_DENSE>(cfg, a, grid, s);
     case FMT_Q8: return (int)launch_tiled_f<FMT_Q8, GRP_DENSE>(cfg, a, grid, s);
     case FMT_F4: return (int)launch_tiled_f<FMT_F4, GRP_DENSE>(cfg, a, grid, s);

@@ -197,7 +197,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
   [[maybe_unused]] const auto rs = rsrc(scales16, nfrag * 32);
   [[maybe_unused]] const auto rz = rsrc(zeros32 ? static_cast<const void*>(zeros32) : static_cast<const void*>(scales16),
                                         zeros32 ? nfrag * 8 : nfrag * 32);
-  [[maybe_unused]] const auto re = rsrc(e8, nfrag * 64);
+  [[maybe_unused]] const auto re = rsrc(e8, nfrag * byte_meta_frag(FMT));
   // MXFP4 activation scales, group-major words: word (g, row) holds the four
   // E8M0 block scales of the row's group g
   [[maybe_unused]] const auto rae = rsrc(p.a_e8m0, (int64_t)G * a_rows * 4);
@@ -234,8 +234,9 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
   for (int j = 0; j < NBW; ++j) {
     const int f0 = nblk(j) * G;  // first fragment of this column block
     woff[j] = f0 * C::FRAGB + lane * ((C::W2 || C::W3) ? 8 : 16);
-    soff[j] = mxint4_weights(FMT) ? f0 * 64 + c16 * 4
-                                  : (mx_weights(FMT) ? f0 * 64 + (lane & ~3) : f0 * 32 + (c16 >> 1) * 4);
+    soff[j] = nvfp4_weights(FMT)    ? f0 * 128 + c16 * 8 + (kq >> 1) * 4
+              : mxint4_weights(FMT) ? f0 * 64 + c16 * 4
+                                    : (mx_weights(FMT) ? f0 * 64 + (lane & ~3) : f0 * 32 + (c16 >> 1) * 4);
     zoff[j] = f0 * 8 + (c16 >> 3) * 4;
   }
 
@@ -283,7 +284,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
       if constexpr (e8m0_meta(FMT)) {
-        sraw[slot][j] = __builtin_amdgcn_raw_buffer_load_b32(re, soff[j], gg * 64, 0);
+        sraw[slot][j] = __builtin_amdgcn_raw_buffer_load_b32(re, soff[j], gg * byte_meta_frag(FMT), 0);
       } else {
         sraw[slot][j] = __builtin_amdgcn_raw_buffer_load_b32(rs, soff[j], gg * 32, 0);
         zraw[slot][j] = __builtin_amdgcn_raw_buffer_load_b32(rz, zoff[j], gg * 8, 0);
@@ -378,6 +379,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
         c2[j] = h2_t{cz, cz};
       }
       auto deq = [&](int j, int t) -> u4_t {
+        if constexpr (nvfp4_weights(FMT)) return nvfp4_operand<false>(braw[slot][j][t], (sraw[slot][j] >> (8 * t)) & 0xFFu);
         uint32_t y[4];
         if constexpr (C::TWO) {
           // INT8: q = 16 * high + low; INT3: q = 4 * high + low;
@@ -480,6 +482,22 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[mb][j][r] += sj[j] * (kH * Ph[r] + Pl[r] - cj[j] * rs[r]);
         }
+      }
+    } else if constexpr (FMT == FMT_NV4BF16) {
+      // weights dequantised exactly in registers (nvfp4_operand), no zero point
+      u4_t bop[NBW][4];
+#pragma unroll
+      for (int j = 0; j < NBW; ++j)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) bop[j][t] = nvfp4_operand<true>(braw[slot][j][t], (sraw[slot][j] >> (8 * t)) & 0xFFu);
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) {
+        u4_t a[4];
+        read_a16(slot, mb, a);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) acc[mb][j] = mfma_16x16x32<false>(a[t], bop[j][t], acc[mb][j]);
       }
     } else if constexpr (FMT == FMT_W16BF16 || FMT == FMT_W2BF16) {
       u4_t bop[NBW][4];
@@ -633,7 +651,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
       const int m = m0 + 16 * mb + 4 * kq + r;
       if constexpr (GRP == GRP_DENSE) {
         if (m >= p.M) continue;
-        const float sa = ACT_SCALE ? p.a_scale[m] : 1.f;
+        const float sa = ACT_SCALE ? p.a_scale[m] : (nvfp4_weights(FMT) ? 256.f * p.tscale[0] : 1.f);
         if (p.part) {
           float* prow = p.part + ((int64_t)split * p.M + m) * p.N;
 #pragma unroll

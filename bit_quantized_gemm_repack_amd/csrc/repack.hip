@@ -86,6 +86,22 @@ __global__ void repack_e8m0_kernel(const uint8_t* __restrict__ e8, uint8_t* __re
   }
 }
 
+// NVFP4 metadata per expert: the E4M3 region (e4m3_src_index), then the fp32
+// tensor scale of that expert and 12 zero bytes.
+__global__ void repack_nvfp4_meta_kernel(const uint8_t* __restrict__ e4, const float* __restrict__ tscale,
+                                         uint8_t* __restrict__ out, int64_t K, int64_t per, int64_t mpe,
+                                         int64_t total) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = i / mpe;
+    const int64_t idx = i - e * mpe;
+    uint8_t v = 0;
+    if (idx < per) v = e4[e * per + e4m3_src_index(K, idx)];
+    else if (idx < per + 4) v = reinterpret_cast<const uint8_t*>(tscale + e)[idx - per];
+    out[i] = v;
+  }
+}
+
 static dim3 grid_for(int64_t n) {
   int64_t b = (n + 255) / 256;
   if (b > 65536) b = 65536;
@@ -120,6 +136,13 @@ int launch_repack(const hq_plan* p, const void* codes, const void* scales, const
   if (err != hipSuccess) return (int)err;
   uint8_t* meta = static_cast<uint8_t*>(meta_out);
   const size_t mpe = p->meta_bytes_per_expert;
+  if (nvfp4_weights(p->fmt)) {
+    const int64_t per = N * K / 16;
+    const int64_t mpe = (int64_t)p->meta_bytes_per_expert;
+    hipLaunchKernelGGL(repack_nvfp4_meta_kernel, grid_for(mpe * E), dim3(256), 0, s, static_cast<const uint8_t*>(zx),
+                       static_cast<const float*>(scales), meta, K, per, mpe, mpe * E);
+    return (int)hipGetLastError();
+  }
   if (e8m0_meta(p->fmt)) {
     // per expert: E8M0 region only (MXINT4: one dword of four block scales per column)
     const int64_t per = N * K / 32;

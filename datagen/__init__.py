@@ -126,6 +126,16 @@ def w4a16_mxint4(M: int, N: int, K: int, act: str = "bf16", key=(10,)):
     return {"a": a, "codes": pack_u4(q), "e8m0": e8}
 
 
+def w4a16_nvfp4(M: int, N: int, K: int, act: str = "bf16", key=(11,)):
+    """W4A16-NVFP4 inputs: 16-bit A, E2M1 codes uniform over 0..15, positive E4M3
+    block scales with exponents 2^-4..2^0 and any mantissa, tensor scale 0.75."""
+    rng = rng_for(*key, M, N, K)
+    a = _to_dtype(rng.standard_normal((M, K)), _dtype(act))
+    q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    e4 = ((rng.integers(3, 8, size=(N, K // 16)) << 3) | rng.integers(0, 8, size=(N, K // 16))).astype(np.uint8)
+    return {"a": a, "codes": pack_u4(q), "e4m3": e4, "tscale": np.array([0.75], np.float32)}
+
+
 def w4a8_mxfp4(M: int, N: int, K: int, key=(3,)):
     """W4A8-MXFP4 inputs: fp8 e4m3 per-token A, E2M1 codes, E8M0 block scales."""
     rng = rng_for(*key, M, N, K)

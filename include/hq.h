@@ -52,9 +52,13 @@
  *               k in [G*g, G*g+G).
  *       zeros   uint8 [N, K/G] holding 0..15 (only with HQ_ZP_PER_GROUP_U4).
  *       e8m0    uint8 [N, K/32] (MXFP4, MXINT4): scale 2^(X-127) per 32 k.
+ *       NVFP4   codes as MXFP4 (E2M1); block scales uint8 E4M3 [N, K/16],
+ *               one per 16 k, passed where the zero points go; the fp32
+ *               tensor scale (one float per expert) passed as `scales`.
  *     INT2 / INT3 / INT4 / INT8 dequantisation is w = (q - z) * s; MXFP4 is
  *     w = e2m1(q) * 2^(X-127); MXINT4 is w = int4(q) * 2^-2 * 2^(X-127) with
- *     int4 the two's-complement reading of the code (codes packed as INT4).
+ *     int4 the two's-complement reading of the code (codes packed as INT4);
+ *     NVFP4 is w = e2m1(q) * e4m3(S[n, k/16]) * s_tensor.
  *   * Activations: row-major [M, K] fp16 / bf16, or 8-bit codes (fp8 e4m3
  *     or int8) with one fp32 scale per row (value = code * scale[m]).
  *   * Output: row-major [M, N] fp16 / bf16, rounded to nearest even from
@@ -128,6 +132,9 @@ typedef enum hq_ascale_mode {
  *   W4A16-MXINT4 w_elem I4 (w_bits 4), group 32, scale E8M0, zp NONE,
  *              act F16|BF16, act_scale NONE, out F16|BF16 (dense only;
  *              MXINT4 is in the format list of cocoloop.cn, format section)
+ *   W4A16-NVFP4 w_elem FP4_E2M1 (w_bits 4), group 16, scale FP8_E4M3,
+ *              zp NONE, act F16|BF16, act_scale NONE, out F16|BF16 (dense
+ *              only; NVFP4 as NVIDIA publishes it, named by the same page)
  *   W4A8-INT   w_elem U4, group 128, scale F16|BF16, zp FIXED (8),
  *              act INT8, act_scale PER_TOKEN_F32, out F16|BF16
  *   W4A8-FP8   w_elem U4, group 128, scale F16|BF16, zp FIXED|PER_GROUP_U4,

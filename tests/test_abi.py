@@ -608,3 +608,49 @@ def test_mxint4_plans_and_validation():
         _plan(quant=hq.QuantDesc(hq.I4, 4, 32, hq.E8M0, hq.ZP_NONE, 0, hq.FP8_E4M3, 1, hq.BF16))
     with pytest.raises(hq.HQError):   # dense only
         hq.MoePlan(512, 7168, hq.w4a16_mxint4("bf16"), 256, 4096, "silu_mul")
+
+
+def test_repack_nvfp4_layout():
+    """NVFP4: E2M1 codes in the 16-bit operand order (unchanged), the E4M3
+    scales as [N/16][G][16 columns][2 halves][4 steps] bytes (byte t of half h
+    = block 8g + 2t + h) and the fp32 tensor scale after them."""
+    rng = np.random.default_rng(13)
+    q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    e4 = rng.integers(0, 256, size=(N, K // 16), dtype=np.uint8)
+    p = _plan(N, K, hq.w4a16_nvfp4("bf16"), max_m=16)
+    w, meta = p.repack_host(torch.from_numpy(datagen.pack_u4(q)), torch.tensor([0.375], dtype=torch.float32),
+                            e8m0=torch.from_numpy(e4))
+    assert meta.numel() == N * K // 16 + 16
+    fm = meta.numpy()[:N * K // 16].reshape(N // 16, K // 128, 16, 2, 4)
+    assert meta.numpy()[N * K // 16:N * K // 16 + 4].view(np.float32)[0] == 0.375
+    fw = w.numpy().view(np.uint32).reshape(N // 16, K // 128, 64, 4)
+    for nb in range(N // 16):
+        for g in range(K // 128):
+            for c in range(16):
+                for h in range(2):
+                    for t in range(4):
+                        assert fm[nb, g, c, h, t] == e4[16 * nb + c, 8 * g + 2 * t + h]
+            for lane in range(0, 64, 7):
+                n = 16 * nb + lane % 16
+                for t in range(4):
+                    k0 = _k16(g, lane, t)
+                    assert (k0 % 128) // 16 == 2 * t + (lane // 16) // 2   # the lane's 8 k in one block
+                    for r in range(4):
+                        v = (int(fw[nb, g, lane, t]) >> (4 * r)) & 0x000F000F
+                        assert (v & 0xF) == q[n, k0 + 2 * r] and (v >> 16) == q[n, k0 + 2 * r + 1]
+
+
+def test_nvfp4_plans_and_validation():
+    p = _plan(4096, 4096, hq.w4a16_nvfp4("f16"), max_m=1024)
+    wb, mb = p.repacked_bytes()
+    assert wb == 4096 * 4096 // 2 and mb == 4096 * 4096 // 16 + 16
+    assert "w4a16-nvfp4-f16" in p.describe(1) and "kernel=tiled" in p.describe(1024)
+    with pytest.raises(hq.HQError):   # block 16 only
+        _plan(quant=hq.QuantDesc(hq.FP4_E2M1, 4, 32, hq.FP8_E4M3, hq.ZP_NONE, 0, hq.BF16, 0, hq.BF16))
+    with pytest.raises(hq.HQError):   # 16-bit activations only
+        _plan(quant=hq.QuantDesc(hq.FP4_E2M1, 4, 16, hq.FP8_E4M3, hq.ZP_NONE, 0, hq.FP8_E4M3, 1, hq.BF16))
+    with pytest.raises(hq.HQError):   # dense only
+        hq.MoePlan(512, 7168, hq.w4a16_nvfp4("bf16"), 256, 4096, "silu_mul")
+    L = hq.lib()
+    fake = 1 << 20
+    assert L.hq_repack_host(p._h, fake, None, fake, fake, fake) == hq.HQ_ERR_INVALID_ARG   # no tensor scale
