@@ -493,7 +493,14 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
             store_out(p.out, (int64_t)m * half + n, act, p.out_bf16);
           } else {
             p.f32_out[(int64_t)m * half + n] = act;
-            atomicMax(p.row_amax + m, __float_as_uint(fabsf(act)));
+            // the 16 lanes l >> 4 = const hold this row's 16 columns (and
+            // skip or keep the row together): their maximum |act| (as bits:
+            // unsigned order, NaN on top), then one atomic per row, not 16
+            // on one address
+            uint32_t amax = __float_as_uint(fabsf(act));
+#pragma unroll
+            for (int d = 1; d < 16; d <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, d, 64));
+            if ((l & 15) == 0) atomicMax(p.row_amax + m, amax);
           }
         } else {
           store_out(p.out, (int64_t)m * p.N + n, v * sa, p.out_bf16);
