@@ -785,7 +785,7 @@ def _moe_points(dev):
 
             pts.append(dict(name=f"{act} T={T} (experts hit {hit})", R=R, bytes=byt, flops=flops,
                             peak=FP16_PEAK_TFLOPS if act == "bf16" else FP8_PEAK_TFLOPS,
-                            plan=f"block_m={bm} gate_up: {p1.describe(T)} | down: {p2.describe(T)}", calls=calls))
+                            plan=f"gate_up: {p1.describe(T, topk)} | down: {p2.describe(T, topk)}", calls=calls))
     return pts, "MoE layer TFLOPS and effective HBM GB/s vs T", \
         "MoE layer on one GPU's tensor-parallel share: 256 experts, top-8, hidden 7168, intermediate 256; " \
         "align + gate_up (SiLU * up; bf16, or fp8 requant for W4A8-FP8) + down with the top-k combine; INT4 " \

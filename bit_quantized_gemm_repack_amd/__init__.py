@@ -536,6 +536,10 @@ class MoePlan(Plan):
                  tuning: Optional[dict] = None):
         super().__init__(n, k, quant, max_m=max_t, epi=epi, kind="grouped", num_experts=num_experts, tuning=tuning)
 
+    def describe(self, t: int, topk: int = 1) -> str:
+        """The kernel a grouped call with t tokens of topk slots launches."""
+        return super().describe(int(t) * int(topk))
+
     def block_m(self, t: int, topk: int) -> int:
         v = ctypes.c_int()
         _check(lib().hq_moe_block_m(self._h, int(t), int(topk), ctypes.byref(v)))

@@ -468,9 +468,12 @@ hq_status hq_plan_destroy(hq_plan* plan) {
   return ok();
 }
 
+static hq_status describe_grouped(const hq_plan* p, int64_t slots, char* buf, size_t len);
+
 hq_status hq_plan_describe(const hq_plan* p, int64_t m, char* buf, size_t len) {
   if (!p || !buf || len == 0) return fail(HQ_ERR_INVALID_ARG, "null argument");
   if (m < 1) m = 1;
+  if (p->compute.kind == HQ_GEMM_GROUPED) return describe_grouped(p, m, buf, len);
   hq::Exec e = hq::choose_exec(p, m);
   if (e.kernel == hq::KER_TILED) {
     snprintf(buf, len,
@@ -795,6 +798,33 @@ static MoeChoice moe_choice(const hq_plan* p, int64_t t, int topk) {
   return c;
 }
 
+// The kernel a grouped call with `slots` routed slots (t * topk) launches, as
+// hq_moe_gemm picks it: the choice depends on t and topk only through their
+// product (slots per expert).
+static bool moe_uses_smallk(const hq_plan* p, int bm) {
+  return p->compute.epi == HQ_EPI_TOPK_COMBINE && p->user.kernel == 0 &&
+         hq::smallk_supported(p->fmt, bm / 16, (int)(p->layer.k / 128)) && (bm == 16 || bm == 64);
+}
+
+static hq_status describe_grouped(const hq_plan* p, int64_t slots, char* buf, size_t len) {
+  const MoeChoice mc = moe_choice(p, slots, 1);
+  const long long n = (long long)p->layer.n, k = (long long)p->layer.k;
+  if (moe_uses_smallk(p, mc.bm)) {
+    snprintf(buf, len, "kernel=grouped-smallk fmt=%s slots=%lld n=%lld k=%lld experts=%d block_m=%d", fmt_name(p->fmt),
+             (long long)slots, n, k, p->layer.num_experts, mc.bm);
+  } else if (mc.tiled) {
+    snprintf(buf, len, "kernel=grouped-tiled fmt=%s slots=%lld n=%lld k=%lld experts=%d block_m=%d tile_n=%d stages=%d",
+             fmt_name(p->fmt), (long long)slots, n, k, p->layer.num_experts, mc.bm, 64 * mc.tl.nbw, mc.tl.stages);
+  } else {
+    snprintf(buf, len,
+             "kernel=grouped-skinny fmt=%s slots=%lld n=%lld k=%lld experts=%d block_m=%d tile_n=%d waves=%d "
+             "stages=%d",
+             fmt_name(p->fmt), (long long)slots, n, k, p->layer.num_experts, mc.bm, 16 * mc.sk.nb, mc.sk.waves,
+             mc.sk.stages);
+  }
+  return ok();
+}
+
 hq_status hq_moe_block_m(const hq_plan* p, int64_t t, int topk, int* block_m) {
   if (!p || !block_m) return fail(HQ_ERR_INVALID_ARG, "null argument");
   if (p->compute.kind != HQ_GEMM_GROUPED) return fail(HQ_ERR_INVALID_ARG, "not a grouped plan");
@@ -924,8 +954,7 @@ hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, cons
     hq::arm_timing({ev.start, second ? nullptr : ev.stop});
     // the down projection with a short K: activations resident in registers,
     // weights streamed over all columns (16- and 64-row blocks)
-    const bool smallk = epi == HQ_EPI_TOPK_COMBINE && p->user.kernel == 0 &&
-                        hq::smallk_supported(p->fmt, bm / 16, (int)G) && (bm == 16 || bm == 64);
+    const bool smallk = moe_uses_smallk(p, bm);
     if (smallk) {
       hq::SkinnyArgs s{};
       s.a = a;

@@ -210,7 +210,8 @@ const char* hq_last_error(void);
 hq_status hq_plan_create(const hq_layer_desc* layer, const hq_compute* compute, int64_t max_m,
                          const hq_tuning* tuning, hq_plan** out);
 hq_status hq_plan_destroy(hq_plan* plan);
-/* Human-readable description of the plan's execution choice. */
+/* Human-readable description of the plan's execution choice for m rows; for
+ * a grouped plan, m is the number of routed slots (t * topk) of a call. */
 hq_status hq_plan_describe(const hq_plan* plan, int64_t m, char* buf, size_t len);
 
 /* Workspace a call with m rows needs, in bytes (0 if none): the fp32 partial

@@ -313,6 +313,13 @@ def test_moe_block_choice():
         with pytest.raises(hq.HQError) as e:
             hq.MoePlan(n, 7168, q, 256, 64, "silu_mul", tuning=bad)
         assert e.value.status == hq.HQ_ERR_UNSUPPORTED, bad
+    # the description names the kernel the grouped call launches
+    assert "kernel=grouped-skinny" in p.describe(32, 8) and "block_m=16" in p.describe(32, 8)
+    assert "kernel=grouped-tiled" in p.describe(4096, 8) and "block_m=64" in p.describe(4096, 8)
+    down = hq.MoePlan(7168, 256, q, 256, 8192, "topk_combine")
+    assert "kernel=grouped-smallk" in down.describe(32, 8) and "kernel=grouped-smallk" in down.describe(4096, 8)
+    assert "kernel=grouped-tiled" in hq.MoePlan(7168, 256, q, 256, 8192, "topk_combine",
+                                                tuning=dict(kernel=2)).describe(4096, 8)
     # the workspace follows the block size of the call
     pq = hq.MoePlan(512, 7168, hq.w4a8_fp8(), 256, 8192, "silu_mul_qfp8")
     b = ctypes.c_size_t()
