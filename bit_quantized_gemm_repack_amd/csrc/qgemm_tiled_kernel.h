@@ -35,7 +35,7 @@
 //   * Grouped mode (MoE): grid y walks the expert-aligned blocks of BM slots,
 //     rows are gathered by token (gate_up) or taken in aligned order (down);
 //     epilogues as in the skinny kernel (SiLU * mul, fp32 + row max for the
-//     fp8 requant, weighted atomic combine into tokens).
+//     fp8 requant, each slot's weighted fp32 row for the combine kernel).
 #pragma once
 
 #include <hip/hip_ext.h>
