@@ -23,6 +23,10 @@ Timings
     sources it was taken on are unchanged (source hash), else null.
   * cpu_baseline: the CPU oracle (oracle/, float64 dequantise + GEMM) on a
     bounded sample of the same points, on this host's cores.
+  * ceilings: what a plain streaming read (the library's probe, no
+    arithmetic) attains on this GPU: over 1 GiB, and over each point's packed
+    weights from the same rotating pool, with the GEMMs' achieved bandwidth
+    as a fraction of the latter.
 
 Algorithmic bytes per GEMM: N*K/2 (codes) + 2*N*K/128 (bf16 scales) +
 N*K/256 (4-bit zeros) + 2*M*K (A) + 2*M*N (C).  Flops: 2*M*N*K.
@@ -385,6 +389,46 @@ def check_point(points, shapes):
     return float(ratio.max())
 
 
+def measure_ceilings(points, hip, L, R, steps):
+    """Attainable-bandwidth references measured with the library's plain
+    streaming-read probe (16-byte loads, no arithmetic): a 1 GiB read, and a
+    read of each point's packed weights (the bulk of its bytes) from the same
+    rotating pool, timed with the same dispatch-bracketing events as the
+    GEMMs.  The best of three grid sizes is kept."""
+    import bit_quantized_gemm_repack_amd as hq
+
+    dev = points[0]["a"].device
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def timed_read(buf, nbytes, wgs, reps):
+        evs = [(hip.event(), hip.event()) for _ in range(reps)]
+        for i in range(reps):
+            hq._check(L.hq_time_next_launch(*evs[i]))
+            hq.stream_read(buf[i % len(buf)], sink, wgs, nbytes)
+        torch.cuda.synchronize()
+        ms = sorted(hip.elapsed_ms(a, b) for a, b in evs)
+        for a, b in evs:
+            hip.destroy(a)
+            hip.destroy(b)
+        return ms[len(ms) // 2] * 1e3
+
+    big = [torch.empty(1 << 30, dtype=torch.uint8, device=dev)]
+    big_us = min(timed_read(big, 1 << 30, w, 10) for w in (1024, 2048, 4096))
+    del big
+    point_us = []
+    for p in points:
+        bufs = [c[0] for c in p["copies"]]
+        nb = bufs[0].numel() * bufs[0].element_size() // 16 * 16
+        point_us.append(round(min(timed_read(bufs, nb, w, max(8, min(steps, 40))) for w in (512, 1024, 2048)), 3))
+    wbytes = sum(c["copies"][0][0].numel() * c["copies"][0][0].element_size() // 16 * 16 for c in points)
+    return {"stream_read_1GiB_GBps": round((1 << 30) / (big_us * 1e-6) / 1e9, 1),
+            "same_bytes_read_GBps": round(wbytes / (sum(point_us) * 1e-6) / 1e9, 1),
+            "what": "plain streaming reads by the library's probe: 1 GiB, and each point's packed weights "
+                    "(the bulk of its bytes) from the same rotating pool; roofline.achieved / same_bytes_read_GBps "
+                    "= frac_of_same_bytes_read",
+            "point_read_us": point_us}
+
+
 def cpu_baseline(budget_s: float):
     """Time the CPU oracle on points of the sweep until ~budget_s seconds."""
     import datagen
@@ -544,6 +588,7 @@ def run_quant(args):
                      "kernel": "hq::quantize_rows_kernel", "mean_kernel_us": round(mean_us, 3),
                      "mean_algorithmic_bytes": int(step_bytes / n)},
         "cpu_baseline": cpu,
+        "ceilings": dict(ceilings, frac_of_same_bytes_read=round(achieved / ceilings["same_bytes_read_GBps"], 4)),
         "points": per_point,
     }
     print(json.dumps(line), flush=True)
@@ -1086,6 +1131,9 @@ def main():
     mean_kernel_us = tot_k_ms / launches * 1e3
     mean_bytes = step_bytes / n
     achieved = mean_bytes / (mean_kernel_us * 1e-6) / 1e9
+    ceilings = measure_ceilings(points, hip, L, R, args.steps)
+    for pp, us in zip(per_point, ceilings.pop("point_read_us")):
+        pp["plain_read_of_weights_us"] = us
 
     cpu = None
     if not args.no_cpu:
@@ -1121,6 +1169,7 @@ def main():
                                "(+ hq::splitk_reduce_kernel where K is split)",
                      "mean_kernel_us": round(mean_kernel_us, 3), "mean_algorithmic_bytes": int(mean_bytes)},
         "cpu_baseline": cpu,
+        "ceilings": dict(ceilings, frac_of_same_bytes_read=round(achieved / ceilings["same_bytes_read_GBps"], 4)),
         "points": per_point,
     }
     print(json.dumps(line), flush=True)
