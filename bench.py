@@ -389,6 +389,34 @@ def check_point(points, shapes):
     return float(ratio.max())
 
 
+def gpu_state():
+    """Clock and power state of the GPU as amd-smi reports it right after the
+    timed region (a child process; None where the tool is unavailable)."""
+    import subprocess
+
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--power", "--json"], capture_output=True,
+                           text=True, timeout=30)
+        if r.returncode != 0:
+            return None
+        d = json.loads(r.stdout)
+        d = d.get("gpu_data", d) if isinstance(d, dict) else d
+        d = d[0] if isinstance(d, list) and d else d
+        clk, pw = d.get("clock", {}), d.get("power", {})
+        gfx = [v["clk"]["value"] for k, v in clk.items() if k.startswith("gfx") and isinstance(v.get("clk"), dict)]
+        mem = [v["clk"]["value"] for k, v in clk.items() if k.startswith("mem") and isinstance(v.get("clk"), dict)]
+        out = {"gfx_clk_mhz_mean": round(sum(gfx) / len(gfx), 1) if gfx else None,
+               "gfx_clk_max_mhz": next((v["max_clk"]["value"] for k, v in clk.items()
+                                        if k.startswith("gfx") and isinstance(v.get("max_clk"), dict)), None),
+               "mem_clk_mhz": mem[0] if mem else None,
+               "clk_locked": next((v.get("clk_locked") for k, v in clk.items() if k.startswith("gfx")), None),
+               "socket_power_w": (pw.get("socket_power") or {}).get("value") if isinstance(pw, dict) else None,
+               "when": "amd-smi right after the timed region"}
+        return out
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+
+
 def measure_ceilings(points, hip, L, R, steps):
     """Attainable-bandwidth references measured with the library's plain
     streaming-read probe (16-byte loads, no arithmetic): a 1 GiB read, and a
@@ -589,6 +617,7 @@ def run_quant(args):
                      "mean_algorithmic_bytes": int(step_bytes / n)},
         "cpu_baseline": cpu,
         "ceilings": dict(ceilings, frac_of_same_bytes_read=round(achieved / ceilings["same_bytes_read_GBps"], 4)),
+        "gpu_state": state,
         "points": per_point,
     }
     print(json.dumps(line), flush=True)
@@ -1131,6 +1160,7 @@ def main():
     mean_kernel_us = tot_k_ms / launches * 1e3
     mean_bytes = step_bytes / n
     achieved = mean_bytes / (mean_kernel_us * 1e-6) / 1e9
+    state = gpu_state()
     ceilings = measure_ceilings(points, hip, L, R, args.steps)
     for pp, us in zip(per_point, ceilings.pop("point_read_us")):
         pp["plain_read_of_weights_us"] = us
@@ -1170,6 +1200,7 @@ def main():
                      "mean_kernel_us": round(mean_kernel_us, 3), "mean_algorithmic_bytes": int(mean_bytes)},
         "cpu_baseline": cpu,
         "ceilings": dict(ceilings, frac_of_same_bytes_read=round(achieved / ceilings["same_bytes_read_GBps"], 4)),
+        "gpu_state": state,
         "points": per_point,
     }
     print(json.dumps(line), flush=True)
