@@ -417,6 +417,31 @@ def gpu_state():
         return None
 
 
+def mfma_ceilings(hip, L, dev):
+    """Sustained matrix-core rate (TFLOP/s or TOP/s) of every operand type the
+    GEMMs use, from the library's register-only probe (hq_mfma_peak): median of
+    five launches of 1024 workgroups, timed with dispatch-bracketing events."""
+    import bit_quantized_gemm_repack_amd as hq
+
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    kinds = {"f16": hq.PEAK_F16, "bf16": hq.PEAK_BF16, "fp8": hq.PEAK_FP8, "fp8_fp4": hq.PEAK_FP8_FP4,
+             "fp4": hq.PEAK_FP4, "int8": hq.PEAK_INT8}
+    out = {}
+    for name, k in kinds.items():
+        hq.mfma_peak(k, sink, 1024, 200)  # warm-up (clock ramp)
+        rates = []
+        for _ in range(5):
+            a, b = hip.event(), hip.event()
+            hq._check(L.hq_time_next_launch(a, b))
+            fl = hq.mfma_peak(k, sink, 1024, 2000)
+            torch.cuda.synchronize()
+            rates.append(fl / (hip.elapsed_ms(a, b) * 1e-3) / 1e12)
+            hip.destroy(a)
+            hip.destroy(b)
+        out[name] = round(float(np.median(rates)), 1)
+    return out
+
+
 def measure_ceilings(points, hip, L, R, steps):
     """Attainable-bandwidth references measured with the library's plain
     streaming-read probe (16-byte loads, no arithmetic): a 1 GiB read, and a
@@ -650,7 +675,7 @@ def _prefill_points(dev):
         ws = plan.workspace(M, dev)
         byt = N * K // 2 + 2 * N * (K // 128) + 2 * M * K + 2 * M * N
         pts.append(dict(name=f"M={M} N={N} K={K}", R=R, bytes=byt, flops=2 * M * N * K, peak=FP16_PEAK_TFLOPS,
-                        plan=plan.describe(M),
+                        mfma="f16", plan=plan.describe(M),
                         calls=lambda r, plan=plan, ws_=ws_, a_=a_, out=out, ws=ws:
                         [lambda: plan.gemm(a_[r % 4], ws_[r][0], ws_[r][1], out=out, ws=ws)]))
     return pts, "quantized GEMM TFLOPS vs M (dense W4A16 prefill)", \
@@ -680,7 +705,7 @@ def _w4a8_points(dev):
             meta_b = N * K // 32 if kind == "mxfp4" else 2 * N * (K // 128)
             byt = N * K // 2 + meta_b + M * K + 4 * M + 2 * M * N
             pts.append(dict(name=f"{kind} M={M} N={N} K={K}", R=R, bytes=byt, flops=2 * M * N * K,
-                            peak=FP8_PEAK_TFLOPS, plan=plan.describe(M),
+                            peak=FP8_PEAK_TFLOPS, mfma="fp8_fp4" if kind == "mxfp4" else "int8", plan=plan.describe(M),
                             calls=lambda r, plan=plan, ws_=ws_, a=a, sa=sa, out=out, ws=ws:
                             [lambda: plan.gemm(a, ws_[r][0], ws_[r][1], a_scale=sa, out=out, ws=ws)]))
         del d
@@ -859,6 +884,7 @@ def _moe_points(dev):
 
             pts.append(dict(name=f"{act} T={T} (experts hit {hit})", R=R, bytes=byt, flops=flops,
                             peak=FP16_PEAK_TFLOPS if act == "bf16" else FP8_PEAK_TFLOPS,
+                            mfma="bf16" if act == "bf16" else "fp8",
                             plan=f"gate_up: {p1.describe(T, topk)} | down: {p2.describe(T, topk)}", calls=calls))
     return pts, "MoE layer TFLOPS and effective HBM GB/s vs T", \
         "MoE layer on one GPU's tensor-parallel share: 256 experts, top-8, hidden 7168, intermediate 256; " \
@@ -942,11 +968,17 @@ def run_points_workload(args, builder):
         shares.append(us)
     step_bytes = sum(p["bytes"] for p in pts)
     step_flops = sum(p["flops"] for p in pts)
+    ceil = mfma_ceilings(hip, L, dev)
+    for p, q in zip(points, pts):
+        kind = q.get("mfma") or {FP16_PEAK_TFLOPS: "bf16", FP8_PEAK_TFLOPS: "fp8", FP4_PEAK_TFLOPS: "fp4"}[q["peak"]]
+        p["mfma_type"] = kind
+        p["frac_of_measured_mfma"] = round(p["TFLOPS"] / ceil[kind], 4)
     dom = int(np.argmax(shares))
     dp, dq = points[dom], pts[dom]
     if dp["bound"] == "mfma":
         roof = {"bound": "mfma", "achieved": dp["TFLOPS"], "peak": dq["peak"], "unit": "TFLOP/s",
-                "frac": dp["mfma_frac"]}
+                "frac": dp["mfma_frac"], "measured_peak": ceil[dp["mfma_type"]],
+                "frac_of_measured_peak": dp["frac_of_measured_mfma"]}
     else:
         roof = {"bound": "hbm", "achieved": dp["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dp["hbm_frac"]}
     roof.update({"traffic": None, "point": dp["point"], "kernel_us": dp["kernel_us"]})
@@ -962,7 +994,7 @@ def run_points_workload(args, builder):
                        "step_flops": step_flops, "gbps_per_step_time": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                        "timing": "HIP graph replay per step; per-point time = sum of its calls' "
                                  "dispatch-bracketing HIP events, median over the steps"},
-            "roofline": roof, "cpu_baseline": cpu, "points": points}
+            "roofline": roof, "cpu_baseline": cpu, "mfma_ceilings_TFLOPS": ceil, "points": points}
     print(json.dumps(line), flush=True)
 
 

@@ -35,6 +35,7 @@ ZP_NONE, ZP_FIXED, ZP_PER_GROUP_U4 = range(3)
 ASCALE_NONE, ASCALE_PER_TOKEN_F32, ASCALE_MX_E8M0 = range(3)
 GEMM_DENSE, GEMM_GROUPED = range(2)
 EPI_NONE, EPI_SILU_MUL, EPI_SILU_MUL_QFP8, EPI_TOPK_COMBINE, EPI_I32_ACC = range(5)
+PEAK_F16, PEAK_BF16, PEAK_FP8, PEAK_FP8_FP4, PEAK_FP4, PEAK_INT8 = range(6)
 
 _DT = {"f16": F16, "bf16": BF16, "fp8": FP8_E4M3, "int8": INT8}
 _EPI = {"none": EPI_NONE, "silu_mul": EPI_SILU_MUL, "silu_mul_qfp8": EPI_SILU_MUL_QFP8,
@@ -180,6 +181,8 @@ _SIGS = {
                     [ctypes.c_size_t, ctypes.c_void_p]),
     "hq_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
                                       ctypes.c_void_p]),
+    "hq_mfma_peak": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]),
     "hq_quantize_per_token": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int] +
                               [ctypes.c_void_p] * 4),
     "hq_quantize_mxfp4": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int] + [ctypes.c_void_p] * 4),
@@ -448,6 +451,16 @@ def stream_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int, nbytes: 
     _dev(buf, "buf"), _dev(sink, "sink")
     n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
     _check(lib().hq_stream_read(_ptr(buf), n, _ptr(sink), int(workgroups), _stream_ptr(buf.device)))
+
+
+def mfma_peak(kind: int, sink: torch.Tensor, workgroups: int = 1024, iters: int = 2000) -> float:
+    """Matrix-core throughput probe (see hq_mfma_peak): one launch of `kind`
+    (PEAK_F16 .. PEAK_INT8) on the stream of `sink`; returns its operations."""
+    _dev(sink, "sink")
+    fl = ctypes.c_double()
+    _check(lib().hq_mfma_peak(int(kind), int(workgroups), int(iters), _ptr(sink), ctypes.byref(fl),
+                              _stream_ptr(sink.device)))
+    return fl.value
 
 
 def quantize_per_token(x: torch.Tensor, out: str = "fp8", codes: Optional[torch.Tensor] = None,

@@ -1318,6 +1318,18 @@ hq_status hq_plan_autotune(hq_plan* p, int64_t m, const void* a, const void* a_s
   }
 }
 
+hq_status hq_mfma_peak(int type, int workgroups, int iters, uint32_t* sink, double* flops, void* stream) {
+  if (!sink) return fail(HQ_ERR_INVALID_ARG, "null sink");
+  if (type < HQ_PEAK_F16 || type > HQ_PEAK_INT8) return fail(HQ_ERR_INVALID_ARG, "unknown matrix type %d", type);
+  if (workgroups < 1 || workgroups > (1 << 20)) return fail(HQ_ERR_INVALID_ARG, "workgroups out of range");
+  if (iters < 1 || iters > (1 << 24)) return fail(HQ_ERR_INVALID_ARG, "iters out of range");
+  if (flops) *flops = hq::mfma_peak_flops(type, workgroups, iters);
+  int err = hq::launch_mfma_peak(type, workgroups, iters, sink, stream);  // takes the armed events
+  hq::arm_timing({nullptr, nullptr});
+  if (err != hipSuccess) return fail(HQ_ERR_HIP, "matrix probe launch: %s", hipGetErrorString((hipError_t)err));
+  return ok();
+}
+
 hq_status hq_stream_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups, void* stream) {
   if (!buf || !sink) return fail(HQ_ERR_INVALID_ARG, "null argument");
   if (bytes % 16 || !aligned16(buf)) return fail(HQ_ERR_INVALID_ARG, "buffer must be 16-byte aligned and sized");

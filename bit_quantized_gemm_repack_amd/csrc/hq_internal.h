@@ -454,6 +454,8 @@ int launch_tiled_grouped(int fmt, int mode, const TiledCfgRt& cfg, const TiledAr
 // out[i] = round(sum_s part[s * mn + i]) in index order (fp16 / bf16 out).
 int launch_splitk_reduce(const float* part, int splits, int64_t mn, void* out, int out_bf16, void* stream);
 int launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups, void* stream);
+int launch_mfma_peak(int dtype, int workgroups, int iters, uint32_t* sink, void* stream);
+double mfma_peak_flops(int dtype, int workgroups, int iters);
 // Per-row quantiser: x [m, k] fp16/bf16 -> codes [m, k] (fp8 e4m3 or int8)
 // and scales [m]; k a multiple of 8.
 int launch_quantize_rows(int64_t m, int64_t k, int in_bf16, int out_fp8, const void* x, void* codes, float* scales,

@@ -437,6 +437,20 @@ hq_status hq_time_next_launch(void* start_event, void* stop_event);
  * practically never written.  Honours hq_time_next_launch. */
 hq_status hq_stream_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups, void* stream);
 
+/* Matrix-core throughput probe (measurement helper, not part of the GEMM):
+ * `workgroups` workgroups of 4 waves each run `iters` rounds of 4 independent
+ * 16 x 16 matrix instructions of one operand type on register values, with
+ * no memory traffic.  The types are those the GEMMs use: fp16 and bf16
+ * (16x16x32), fp8 e4m3 x fp8, fp8 x fp4 e2m1 and fp4 x fp4 (the scaled
+ * 16x16x128 form, unit scales) and int8 (16x16x64, int32 results).
+ * *flops (if not NULL) receives the operations of the launch (2 * 16 * 16 * K
+ * per instruction); with the duration from hq_time_next_launch it gives the
+ * rate the chip sustains for that type.  `sink` is a device uint32 that is
+ * practically never written.  workgroups in [1, 2^20], iters in [1, 2^24]. */
+typedef enum { HQ_PEAK_F16 = 0, HQ_PEAK_BF16 = 1, HQ_PEAK_FP8 = 2, HQ_PEAK_FP8_FP4 = 3, HQ_PEAK_FP4 = 4,
+               HQ_PEAK_INT8 = 5 } hq_peak_type;
+hq_status hq_mfma_peak(int type, int workgroups, int iters, uint32_t* sink, double* flops, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

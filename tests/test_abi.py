@@ -661,3 +661,13 @@ def test_nvfp4_plans_and_validation():
     L = hq.lib()
     fake = 1 << 20
     assert L.hq_repack_host(p._h, fake, None, fake, fake, fake) == hq.HQ_ERR_INVALID_ARG   # no tensor scale
+
+
+def test_mfma_probe_validation():
+    # argument checks happen before any launch (no GPU needed)
+    L = hq.lib()
+    fake = ctypes.c_void_p(256)
+    fl = ctypes.c_double()
+    for kind, wg, it in ((-1, 1, 1), (6, 1, 1), (0, 0, 1), (0, 1 << 21, 1), (0, 1, 0), (0, 1, (1 << 24) + 1)):
+        assert L.hq_mfma_peak(kind, wg, it, fake, ctypes.byref(fl), None) == hq.HQ_ERR_INVALID_ARG, (kind, wg, it)
+    assert L.hq_mfma_peak(0, 1, 1, None, ctypes.byref(fl), None) == hq.HQ_ERR_INVALID_ARG
