@@ -391,9 +391,13 @@ def check_point(points, shapes):
 
 def gpu_state():
     """Clock and power state of the GPU as amd-smi reports it right after the
-    timed region (a child process; None where the tool is unavailable)."""
+    timed region (a child process; None where the tool is unavailable, and
+    under a profiler, whose preloaded library would attach the child to the GPU
+    before it starts the tool's interpreter)."""
     import subprocess
 
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
+        return None
     try:
         r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--power", "--json"], capture_output=True,
                            text=True, timeout=30)

@@ -422,7 +422,7 @@ hq_status hq_plan_set_tuning(hq_plan* plan, int64_t m, const hq_tuning* tuning);
 hq_status hq_plan_get_tuning(const hq_plan* plan, int64_t m, hq_tuning* tuning, int* is_tuned);
 
 /* Kernel timing: the next hq_gemm, hq_moe_align, hq_moe_gemm,
- * hq_quantize_per_token, hq_quantize_mxfp4 or hq_stream_read call on this
+ * hq_quantize_per_token, hq_quantize_mxfp4, hq_stream_read or hq_mfma_peak call on this
  * thread records `start` (hipEvent_t, created by the caller with timing
  * enabled) when its first kernel starts and `stop` when its last kernel ends
  * (the split-K reduce, the fp8 requant or the combine's final pass included;
