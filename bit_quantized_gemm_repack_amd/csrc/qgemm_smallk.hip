@@ -22,6 +22,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "hq_internal.h"
@@ -60,12 +61,38 @@ __global__ void __launch_bounds__(256) qgemm_smallk(SkinnyArgs p) {
   const uint32_t* zsrc = p.zeros ? p.zeros + ex * p.z_expert : reinterpret_cast<const uint32_t*>(scales16);
   const int K = p.K;
 
+  // output rows of this lane: slot ids and weights (topk_w times the row scale)
+  int oid[MB][4];
+  float of[MB][4];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = m0 + 16 * mb + 4 * kq + r;
+      const int id = p.sorted_ids[m];
+      oid[mb][r] = id;
+      of[mb][r] = id < p.n_slots ? p.topk_w[id] * (ACT16 ? 1.f : p.a_scale[m]) : 0.f;
+    }
+  // m-blocks up to the last one that holds a slot (an expert's slots come
+  // first in its aligned segment, so a block's padding rows usually fill its
+  // last m-blocks): the others need no operands, products or stores
+  uint32_t live = 0;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    bool any = false;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) any |= oid[mb][r] < p.n_slots;
+    if (__builtin_amdgcn_ballot_w64(any) != 0) live |= 1u << mb;
+  }
+  const int nlive = live ? 32 - __builtin_clz(live) : 0;
+
   // ---- the block's activation operands and row sums, once ----------------
   // 16-bit step t of group g: k = 128 g + 32 t + 8 kq + [0,8); 8-bit piece h:
   // k = 128 g + 64 h + 16 kq + [0,16).
   u4_t a[MB][AV];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
+    if (mb >= nlive) break;
     const int64_t row = m0 + 16 * mb + c;  // aligned rows: the down GEMM's input rows
     if constexpr (ACT16) {
       const uint16_t* ar = static_cast<const uint16_t*>(p.a) + row * K + 8 * kq;
@@ -79,7 +106,8 @@ __global__ void __launch_bounds__(256) qgemm_smallk(SkinnyArgs p) {
   }
   f4_t rs[MB][G];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int mb = 0; mb < MB; ++mb) {
+    if (mb >= nlive) break;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       if constexpr (ACT16) {
@@ -96,18 +124,7 @@ __global__ void __launch_bounds__(256) qgemm_smallk(SkinnyArgs p) {
             cat8(a[mb][2 * g], a[mb][2 * g + 1]), ones, f4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
       }
     }
-  // output rows of this lane: slot ids and weights (topk_w times the row scale)
-  int oid[MB][4];
-  float of[MB][4];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + 16 * mb + 4 * kq + r;
-      const int id = p.sorted_ids[m];
-      oid[mb][r] = id;
-      of[mb][r] = id < p.n_slots ? p.topk_w[id] * (ACT16 ? 1.f : p.a_scale[m]) : 0.f;
-    }
+  }
 
   // ---- column blocks of this wave, D blocks of loads in flight ------------
   const int n_my = (cb1 - cb0 - wave + 3) / 4;  // blocks cb0 + wave + 4 i
@@ -128,10 +145,11 @@ __global__ void __launch_bounds__(256) qgemm_smallk(SkinnyArgs p) {
       st.z[g] = zsrc[rec * 2 + (c >> 3)];
     }
   };
-  auto compute = [&](const St& st, int cb) {
-    f4_t acc[MB];
+  auto compute = [&](auto L_c, const St& st, int cb) {
+    constexpr int L = decltype(L_c)::value;  // live m-blocks
+    f4_t acc[L];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb] = f4_t{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < L; ++mb) acc[mb] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const uint32_t sb = (st.s[g] >> (16 * (c & 1))) & 0xFFFFu;
@@ -140,24 +158,24 @@ __global__ void __launch_bounds__(256) qgemm_smallk(SkinnyArgs p) {
       if constexpr (ACT16) {
         const uint32_t magic = (FMT == FMT_W16F16) ? 0x64006400u : 0x43004300u;
         const float cz = ((FMT == FMT_W16F16) ? 1024.f : 128.f) + (float)z;
-        f4_t P[MB];
+        f4_t P[L];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) P[mb] = f4_t{0.f, 0.f, 0.f, 0.f};
+        for (int mb = 0; mb < L; ++mb) P[mb] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const u4_t bop = w16_operand(st.w[g][t], magic);
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) P[mb] = mfma_16x16x32<FMT == FMT_W16F16>(a[mb][4 * g + t], bop, P[mb]);
+          for (int mb = 0; mb < L; ++mb) P[mb] = mfma_16x16x32<FMT == FMT_W16F16>(a[mb][4 * g + t], bop, P[mb]);
         }
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < L; ++mb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[mb][r] += s * (P[mb][r] - cz * rs[mb][g][r]);
       } else {
         const i8_t bop = q8_operand(st.w[g]);
         const float zf = (float)z;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
+        for (int mb = 0; mb < L; ++mb) {
           // codes 0x00..0x0F are q * 2^-9 in e4m3; block scale 2^9 (E8M0 136) undoes it
           const f4_t P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               cat8(a[mb][2 * g], a[mb][2 * g + 1]), bop, f4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 136);
@@ -168,20 +186,30 @@ __global__ void __launch_bounds__(256) qgemm_smallk(SkinnyArgs p) {
     }
     const int n = cb * 16 + c;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < L; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (oid[mb][r] < p.n_slots) p.f32_out[(int64_t)oid[mb][r] * p.N + n] = acc[mb][r] * of[mb][r];
   };
-  St st[D];
+  auto run = [&](auto L_c) {
+    St st[D];
 #pragma unroll
-  for (int d = 0; d < D; ++d) load(st[d], cb_of(d));
-  for (int i = 0; i < n_my; i += D) {
+    for (int d = 0; d < D; ++d) load(st[d], cb_of(d));
+    for (int i = 0; i < n_my; i += D) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-      if (i + d < n_my) compute(st[d], cb0 + wave + 4 * (i + d));
-      load(st[d], cb_of(i + d + D));
+      for (int d = 0; d < D; ++d) {
+        if (i + d < n_my) compute(L_c, st[d], cb0 + wave + 4 * (i + d));
+        load(st[d], cb_of(i + d + D));
+      }
     }
+  };
+  if constexpr (MB == 4) {
+    if (nlive <= 1) run(std::integral_constant<int, 1>{});
+    else if (nlive == 2) run(std::integral_constant<int, 2>{});
+    else if (nlive == 3) run(std::integral_constant<int, 3>{});
+    else run(std::integral_constant<int, 4>{});
+  } else {
+    run(std::integral_constant<int, MB>{});
   }
 }
 
