@@ -36,11 +36,11 @@ gemm     dense W4A16, W4A8 (MXFP4 x FP8 and INT4 x INT8), W4A4 (MXFP4 x
 moe      the grouped MoE layer: align invariants, gate_up + SiLU*mul (+ fp8
          requant), down + top-k combine.
 quant    the per-token (per-row) activation quantiser that feeds W4A8:
-         s = max|x| / Q, codes = RNE(x * (1/s)) as fp8 e4m3 or int8; and the
+         s = max|x| / Q, codes = RNE(x / s) as fp8 e4m3 or int8; and the
          MXFP4 block quantiser (OCP MX v1.0) of W4A4 activations.
 
-Parity status: every function is pinned by tests/test_oracle.py and
-tests/test_quant_oracle.py against
+Parity status: every function is pinned by tests/test_oracle.py,
+tests/test_quant_oracle.py and tests/test_moe_oracle.py against
 hand-worked examples (tests/golden), code tables derived from the format
 definitions, torch's fp8 decoders, exact rational brute force and
 invariants.  No function is "parity unpinned".

@@ -77,10 +77,12 @@ def check_align(topk_ids, num_experts: int, block_m: int, sorted_ids, block_expe
 
 
 def silu(x):
+    """SiLU(x) = x * sigmoid(x) = x / (1 + e^-x), float64."""
     return x / (1.0 + np.exp(-x))
 
 
 def silu_grad(x):
+    """d/dx SiLU(x) = sigmoid(x) (1 + x (1 - sigmoid(x))), float64."""
     s = 1.0 / (1.0 + np.exp(-x))
     return s * (1.0 + x * (1.0 - s))
 
@@ -116,9 +118,18 @@ def gate_up(rows_a, row_expert, w1_codes, w1_scales, inter: int):
     g, u = h[:, :inter], h[:, inter:]
     tg, tu = tau_h[:, :inter], tau_h[:, inter:]
     act = silu(g) * u
-    tau_act = (np.abs(silu_grad(g) * u) * tg + np.abs(silu(g)) * tu
-               + 1.1 * tg * tu + 0.25 * tg * tg * (np.abs(u) + tu))
-    return {"g": g, "u": u, "act": act, "tau_g": tg, "tau_u": tu, "tau_act": tau_act}
+    return {"g": g, "u": u, "act": act, "tau_g": tg, "tau_u": tu, "tau_act": act_bound(g, u, tg, tu)}
+
+
+def act_bound(g, u, tg, tu):
+    """Bound on |SiLU(g + dg)(u + du) - SiLU(g) u| over |dg| <= tg, |du| <= tu.
+
+    Writing the difference as [SiLU(g + dg) - SiLU(g)](u + du) + SiLU(g) du
+    and expanding SiLU to second order with |SiLU''| <= 1/2 and |SiLU'| <= 1.1:
+    |SiLU'(g) u| tg + |SiLU(g)| tu + 1.1 tg tu + (1/4) tg^2 (|u| + tu).
+    """
+    return (np.abs(silu_grad(g) * u) * tg + np.abs(silu(g)) * tu
+            + 1.1 * tg * tu + 0.25 * tg * tg * (np.abs(u) + tu))
 
 
 def requant_fp8_rows(act):

@@ -10,23 +10,19 @@ Reading (the plainest symmetric per-row rule, listed with the others in the
 design notes): for each row r of x,
 
     s[r]    = max_j |x[r, j]| / Q          (s[r] = 1 when the row is all zero)
-    inv[r]  = 1 / s[r]
-    code    = RNE(x[r, j] * inv[r])        saturated to [-Q, Q]
+    code    = RNE(x[r, j] / s[r])          saturated to [-Q, Q]
 
 with Q = 448 and an OCP e4m3 ("fn") code for FP8, Q = 127 and a
-two's-complement int8 code for INT8, so that code * s[r] approximates x.
+two's-complement int8 code for INT8, so that code * s[r] approximates x.  The
+quotient is the correctly rounded float32 division (one rounding), the same
+rule the fused requantisation of the MoE gate_up output follows.  A negative
+value that rounds to zero gives code 0 (no -0).
 
-The quotient is taken as a product with the row's reciprocal scale, the form
-production per-token quantisers use (one multiply per element instead of a
-division); code * s still approximates x within half a code step plus a few
-float32 roundings.  A negative value that rounds to zero gives code 0 (no -0).
-
-Precision.  The scale, its reciprocal and the product decide integer codes,
-so the oracle takes them in IEEE float32, the precision the GPU kernel
-computes in (numpy's float32 division and multiplication are correctly
-rounded); the rounding of the float32 product to the code grid is then exact
-(formats.rne / rint in float64 on a float32 value).  Inputs are fp16 / bf16
-values, hence exact in float32.
+Precision.  The scale and the quotient decide integer codes, so the oracle
+takes them in IEEE float32, the precision the GPU kernel computes in (numpy's
+float32 division is correctly rounded); the rounding of the float32 quotient
+to the code grid is then exact (formats.rne / rint in float64 on a float32
+value).  Inputs are fp16 / bf16 values, hence exact in float32.
 """
 from __future__ import annotations
 
@@ -52,8 +48,7 @@ def quantize_rows(x, out: str):
     q = np.float32(Q_FP8 if out == "fp8" else Q_INT8)
     amax = np.max(np.abs(x32), axis=1) if x32.shape[1] else np.zeros(x32.shape[0], np.float32)
     s = np.where(amax > 0, amax / q, np.float32(1.0)).astype(np.float32)
-    inv = (np.float32(1.0) / s).astype(np.float32)        # float32 reciprocal, correctly rounded
-    v = (x32 * inv[:, None]).astype(np.float32)           # float32 product, correctly rounded
+    v = (x32 / s[:, None]).astype(np.float32)             # float32 quotient, correctly rounded
     v64 = np.clip(v.astype(np.float64), -float(q), float(q))
     if out == "fp8":
         return e4m3_encode(v64), s
@@ -69,7 +64,7 @@ def dequantize_rows(codes, scales, out: str) -> np.ndarray:
 
 def step_bound(x, scales, out: str) -> np.ndarray:
     """Half a code step at |x / s| times s: the rounding error bound of one
-    element (plus 2^-22 relative for the float32 reciprocal and product)."""
+    element (plus 2^-22 relative for the float32 quotient)."""
     s = np.asarray(scales, dtype=np.float64)[:, None]
     v = np.abs(np.asarray(x, dtype=np.float64)) / s
     half = 0.5 * ulp(np.minimum(v, Q_FP8), "e4m3") if out == "fp8" else np.full_like(v, 0.5)

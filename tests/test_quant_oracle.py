@@ -67,11 +67,36 @@ def test_quant_hand_examples():
     assert c.tolist() == g["int8"]["codes"]
 
 
+def test_quant_division_hand_examples():
+    # quotients at or next to a rounding tie, where a correctly rounded float32
+    # division and a product with a rounded reciprocal give different codes
+    g = _gold()
+    c, s = QZ.quantize_rows(np.array(g["fp8_division"]["x"], np.float32), "fp8")
+    assert s.tolist() == g["fp8_division"]["scales"]
+    assert c.tolist() == [[int(h, 16) for h in row] for row in g["fp8_division"]["codes_hex"]]
+    c, s = QZ.quantize_rows(np.array(g["int8_division"]["x"], np.float32), "int8")
+    assert s.tolist() == g["int8_division"]["scales"]
+    assert c.tolist() == g["int8_division"]["codes"]
+
+
+def test_quant_quotient_against_exact_rationals():
+    # the float32 quotient the codes come from is the correctly rounded one:
+    # within half a float32 ulp of the exact rational x / s, on every element
+    from fractions import Fraction
+    x = _rows(21, m=6, k=64)
+    for out in ("fp8", "int8"):
+        _, s = QZ.quantize_rows(x, out)
+        v = (x / s[:, None]).astype(np.float32)
+        for (r, c), q in np.ndenumerate(v):
+            exact = Fraction(float(x[r, c])) / Fraction(float(s[r]))
+            half = Fraction(float(np.spacing(np.float32(abs(q))))) / 2
+            assert abs(Fraction(float(q)) - exact) <= half
+
+
 def test_quant_fp8_codes_match_torch_cast_and_brute_force():
     x = _rows(11)
     codes, s = QZ.quantize_rows(x, "fp8")
-    inv = (np.float32(1) / s).astype(np.float32)
-    v = (x * inv[:, None]).astype(np.float32)                  # the float32 product the rule rounds
+    v = (x / s[:, None]).astype(np.float32)                    # the float32 quotient the rule rounds
     ref = torch.from_numpy(np.clip(v, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     neg_zero = (ref == 0x80)
     assert np.array_equal(codes, np.where(neg_zero, 0, ref))
@@ -82,7 +107,7 @@ def test_quant_fp8_codes_match_torch_cast_and_brute_force():
 def test_quant_int8_codes_match_brute_force():
     x = _rows(12, dtype=torch.float16)
     codes, s = QZ.quantize_rows(x, "int8")
-    v = (x * (np.float32(1) / s)[:, None]).astype(np.float32).astype(np.float64)
+    v = (x / s[:, None]).astype(np.float32).astype(np.float64)
     assert np.array_equal(codes.astype(np.int64), _brute_int(v).astype(np.int64))
 
 
@@ -117,11 +142,12 @@ def test_quant_planted_mistakes_are_caught():
     want_f = [[int(h, 16) for h in row] for row in g["fp8"]["codes_hex"]]
     want_i = g["int8"]["codes"]
 
-    def rule(x, out, q=None, absmax=True, rnd=np.rint):
+    def rule(x, out, q=None, absmax=True, rnd=np.rint, recip=False):
         q = np.float32(q if q is not None else (448.0 if out == "fp8" else 127.0))
         m = np.max(np.abs(x) if absmax else x, axis=1)
         s = np.where(m > 0, m / q, np.float32(1)).astype(np.float32)
-        v = np.clip((x * (np.float32(1) / s)[:, None]).astype(np.float64), -float(q), float(q))
+        den = (x * (np.float32(1) / s)[:, None]) if recip else (x / s[:, None])
+        v = np.clip(den.astype(np.float32).astype(np.float64), -float(q), float(q))
         if out == "fp8":
             return F.e4m3_encode(v).tolist()
         return np.clip(rnd(v), -127, 127).astype(np.int64).tolist()
@@ -131,6 +157,13 @@ def test_quant_planted_mistakes_are_caught():
     assert rule(xi, "int8", rnd=lambda v: np.floor(v + 0.5)) != want_i   # ties away from zero / up
     assert rule(xi, "int8", rnd=np.trunc) != want_i            # truncation
     assert rule(xf, "fp8", q=240.0) != want_f                  # e4m3 "fnuz"-style range
+    # quotient as a product with the rounded reciprocal: caught by the division rows
+    xd = np.array(g["fp8_division"]["x"], np.float32)
+    wd = [[int(h, 16) for h in row] for row in g["fp8_division"]["codes_hex"]]
+    assert rule(xd, "fp8") == wd and rule(xd, "fp8", recip=True) != wd
+    xdi = np.array(g["int8_division"]["x"], np.float32)
+    assert rule(xdi, "int8") == g["int8_division"]["codes"]
+    assert rule(xdi, "int8", recip=True) != g["int8_division"]["codes"]
     neg = np.array([[-896, 1, -2, 0.5, 0, 0, 0, 0]], np.float32)
     c, s = QZ.quantize_rows(neg, "fp8")
     assert s.tolist() == [2.0] and rule(neg, "fp8", absmax=False) != c.tolist()   # max without abs
