@@ -861,18 +861,15 @@ hq_status hq_moe_align(int64_t t, int topk, int num_experts, int block_m, const 
 }
 
 struct MoeWs {
-  size_t act32, amax, rows, total;
+  size_t act32, rows, total;
 };
 
 static MoeWs moe_ws(const hq_plan* p, int64_t t, int topk) {
   MoeWs w{};
   const int64_t mp = moe_max_padded(t, topk, p->layer.num_experts, moe_choice(p, t, topk).bm);
-  if (p->compute.epi == HQ_EPI_SILU_MUL_QFP8) {
-    w.act32 = align256((size_t)mp * (size_t)(p->layer.n / 2) * 4);
-    w.amax = align256((size_t)mp * 4);
-  }
+  if (p->compute.epi == HQ_EPI_SILU_MUL_QFP8) w.act32 = align256((size_t)mp * (size_t)(p->layer.n / 2) * 4);
   if (p->compute.epi == HQ_EPI_TOPK_COMBINE) w.rows = align256((size_t)t * topk * (size_t)p->layer.n * 4);
-  w.total = w.act32 + w.amax + w.rows;
+  w.total = w.act32 + w.rows;
   return w;
 }
 
@@ -929,14 +926,12 @@ hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, cons
     uint8_t* wsb = static_cast<uint8_t*>(ws);
     int mode = hq::GRP_GATHER, gepi = hq::GEPI_PLAIN;
     float* f32_out = nullptr;
-    uint32_t* row_amax = nullptr;
     switch (epi) {
       case HQ_EPI_NONE: gepi = hq::GEPI_PLAIN; break;
       case HQ_EPI_SILU_MUL: gepi = hq::GEPI_SILU; break;
       case HQ_EPI_SILU_MUL_QFP8:
         gepi = hq::GEPI_SILU_F32;
         f32_out = reinterpret_cast<float*>(wsb);
-        row_amax = reinterpret_cast<uint32_t*>(wsb + mw.act32);
         break;
       case HQ_EPI_TOPK_COMBINE:
         gepi = hq::GEPI_COMBINE;
@@ -1011,7 +1006,6 @@ hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, cons
       s.s_expert = (int64_t)(N * G);
       s.z_expert = (int64_t)((N / 16) * G * 2);
       s.f32_out = f32_out;
-      s.row_amax = row_amax;
       err = hq::launch_tiled_grouped(p->fmt, mode, mc.tl, s, blocks, stream);
     } else {
       hq::SkinnyArgs s{};
@@ -1042,12 +1036,11 @@ hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, cons
       s.z_expert = (int64_t)((N / 16) * G * 2);
       s.e8_expert = (int64_t)(N * K / 32);
       s.f32_out = f32_out;
-      s.row_amax = row_amax;
       err = hq::launch_skinny_grouped(p->fmt, mode, mc.sk, s, blocks, stream);
     }
     hq::arm_timing({nullptr, ev.stop});
     if (err == hipSuccess && epi == HQ_EPI_SILU_MUL_QFP8)
-      err = hq::launch_moe_requant(f32_out, row_amax, sorted_ids, num_padded, n_slots, (int)(N / 2),
+      err = hq::launch_moe_requant(f32_out, sorted_ids, num_padded, n_slots, (int)(N / 2),
                                    std::min<int64_t>(mp, (int64_t)bm * t * topk), static_cast<uint8_t*>(out),
                                    out_scale, stream);
     if (err == hipSuccess && epi == HQ_EPI_TOPK_COMBINE)

@@ -391,7 +391,6 @@ struct SkinnyArgs {
   int64_t z_expert;             // zero-point words per expert
   int64_t e8_expert;            // E8M0 bytes per expert
   float* f32_out;               // gate_up fp32 act (QFP8) or down weighted slot rows [n_slots][N]
-  uint32_t* row_amax;           // gate_up QFP8: per aligned row max |act| (float bits)
 };
 
 // Grouped epilogues (SkinnyArgs::epi / TiledArgs::epi).
@@ -411,8 +410,8 @@ int launch_skinny_grouped(int fmt, int mode, const SkinnyCfg& cfg, const SkinnyA
                           void* stream);
 int launch_moe_align(int64_t t, int topk, int num_experts, int block_m, const int32_t* ids, int32_t* sorted_ids,
                      int32_t* block_expert, int32_t* num_padded, void* stream);
-int launch_moe_requant(const float* act32, uint32_t* row_amax, const int32_t* sorted_ids, const int32_t* num_padded,
-                       int n_slots, int inter, int64_t max_rows, uint8_t* codes, float* scales, void* stream);
+int launch_moe_requant(const float* act32, const int32_t* sorted_ids, const int32_t* num_padded, int n_slots,
+                       int inter, int64_t max_rows, uint8_t* codes, float* scales, void* stream);
 // y[t][n] = RNE(sum over the token's topk weighted slot rows), rows [t*topk][n] fp32
 int launch_moe_combine(const float* rows, int topk, int64_t t, int64_t n, void* y, int out_bf16, void* stream);
 
@@ -444,7 +443,6 @@ struct TiledArgs {
   int half_nblk;
   int64_t w_expert, s_expert, z_expert, e8_expert;
   float* f32_out;
-  uint32_t* row_amax;
 };
 
 int launch_tiled(int fmt, const TiledCfgRt& cfg, const TiledArgs& a, void* stream);

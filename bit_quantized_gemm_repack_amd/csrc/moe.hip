@@ -85,10 +85,13 @@ __global__ void __launch_bounds__(1024) moe_align_kernel(const int32_t* __restri
   }
 }
 
-// One wave per aligned row: s = max|act| / 448 (1 for an all-zero row),
-// codes = RNE_e4m3(act / s).  Resets the row maximum for the next call.
+// One wave per aligned row of the fp32 activations the gate_up epilogue
+// stored: s = max|act| / 448 (1 for an all-zero row), codes = RNE_e4m3(act /
+// s) with a correctly rounded fp32 quotient, saturated to +-448 -- the rule of
+// the standalone per-token quantiser (quantize.hip).  The row maximum is
+// formed here from the stored row (two passes over 4 * inter bytes, the
+// second from the cache), so no state carries over between calls.
 __global__ void __launch_bounds__(256) moe_requant_kernel(const float* __restrict__ act32,
-                                                          uint32_t* __restrict__ row_amax,
                                                           const int32_t* __restrict__ sorted_ids,
                                                           const int32_t* __restrict__ num_padded, int n_slots,
                                                           int inter, int64_t max_rows, uint8_t* __restrict__ codes,
@@ -97,16 +100,14 @@ __global__ void __launch_bounds__(256) moe_requant_kernel(const float* __restric
   const int lane = threadIdx.x & 63;
   if (row >= max_rows || row >= *num_padded) return;
   if (sorted_ids[row] >= n_slots) return;
-  const float amax = __uint_as_float(row_amax[row]);
+  const float* a = act32 + row * inter;
+  float amax = 0.f;
+  for (int col = lane; col < inter; col += 64) amax = fmaxf(amax, fabsf(a[col]));
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 64));
   const float s = amax > 0.f ? amax / 448.f : 1.f;
-  for (int col = lane; col < inter; col += 64) {
-    const float v = act32[row * inter + col] / s;
-    codes[row * inter + col] = (uint8_t)e4m3_code_rne(v);
-  }
-  if (lane == 0) {
-    scales[row] = s;
-    row_amax[row] = 0u;
-  }
+  for (int col = lane; col < inter; col += 64) codes[row * inter + col] = (uint8_t)e4m3_code_rne(a[col] / s);
+  if (lane == 0) scales[row] = s;
 }
 
 // The combine: y[t, n] = RNE(sum_j rows[t * topk + j][n]) over the token's
@@ -140,12 +141,12 @@ int launch_moe_align(int64_t t, int topk, int num_experts, int block_m, const in
                            (int)(t * topk), num_experts, block_m, sorted_ids, block_expert, num_padded);
 }
 
-int launch_moe_requant(const float* act32, uint32_t* row_amax, const int32_t* sorted_ids, const int32_t* num_padded,
-                       int n_slots, int inter, int64_t max_rows, uint8_t* codes, float* scales, void* stream) {
+int launch_moe_requant(const float* act32, const int32_t* sorted_ids, const int32_t* num_padded, int n_slots,
+                       int inter, int64_t max_rows, uint8_t* codes, float* scales, void* stream) {
   const int64_t blocks = (max_rows + 3) / 4;
   return (int)launch_timed(moe_requant_kernel, dim3((unsigned)blocks), dim3(256), 0,
-                           static_cast<hipStream_t>(stream), act32, row_amax, sorted_ids, num_padded, n_slots, inter,
-                           max_rows, codes, scales);
+                           static_cast<hipStream_t>(stream), act32, sorted_ids, num_padded, n_slots, inter, max_rows,
+                           codes, scales);
 }
 
 int launch_moe_combine(const float* rows, int topk, int64_t t, int64_t n, void* y, int out_bf16, void* stream) {

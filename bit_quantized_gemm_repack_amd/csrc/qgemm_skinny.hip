@@ -492,15 +492,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
           if (p.epi == GEPI_SILU) {
             store_out(p.out, (int64_t)m * half + n, act, p.out_bf16);
           } else {
-            p.f32_out[(int64_t)m * half + n] = act;
-            // the 16 lanes l >> 4 = const hold this row's 16 columns (and
-            // skip or keep the row together): their maximum |act| (as bits:
-            // unsigned order, NaN on top), then one atomic per row, not 16
-            // on one address
-            uint32_t amax = __float_as_uint(fabsf(act));
-#pragma unroll
-            for (int d = 1; d < 16; d <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, d, 64));
-            if ((l & 15) == 0) atomicMax(p.row_amax + m, amax);
+            p.f32_out[(int64_t)m * half + n] = act;  // requantised to fp8 by moe_requant_kernel
           }
         } else {
           store_out(p.out, (int64_t)m * p.N + n, v * sa, p.out_bf16);

@@ -669,29 +669,13 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
           const float sa = ACT_SCALE ? p.a_scale[tok] : 1.f;
           if (paired) {
             const int half = p.N / 2;
-            // |act| as bits: unsigned order is the order of the magnitudes,
-            // with NaN above every number
-            uint32_t amax = 0u;
 #pragma unroll
             for (int j = 0; j < NBW / 2; ++j) {
               const float gv = acc[mb][j][r] * sa;
               const float act = gv / (1.f + expf(-gv)) * (acc[mb][j + NBW / 2][r] * sa);
               const int64_t o = (int64_t)m * half + nblk(j) * 16 + c16;
-              if (p.epi == GEPI_SILU) {
-                store_out(p.out, o, act, p.out_bf16);
-              } else {
-                p.f32_out[o] = act;
-                amax = max(amax, __float_as_uint(fabsf(act)));
-              }
-            }
-            if (p.epi != GEPI_SILU) {
-              // the 16 lanes of one kq hold this row's columns of the tile (all
-              // of them skip or keep the row together): their maximum, then
-              // one atomic per row instead of one per element, which would
-              // serialise 16 lanes on one address
-#pragma unroll
-              for (int d = 1; d < 16; d <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, d, 64));
-              if (c16 == 0) atomicMax(p.row_amax + m, amax);
+              if (p.epi == GEPI_SILU) store_out(p.out, o, act, p.out_bf16);
+              else p.f32_out[o] = act;  // requantised to fp8 by moe_requant_kernel
             }
           } else {
 #pragma unroll

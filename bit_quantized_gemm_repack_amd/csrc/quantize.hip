@@ -4,14 +4,14 @@
 // The pages name W4A8 (4-bit weights, 8-bit activations: INT8 or FP8, with
 // MXFP4 weights taking FP8 activations) but not how the activations are
 // quantised (Humming page on news.ditty.ir, summary; cocoloop.cn, format
-// section).  The rule here is the plainest symmetric per-row form, with the
-// quotient taken as a product with the reciprocal scale:
+// section).  The rule here is the plainest symmetric per-row form:
 //   s[m]      = max_k |x[m,k]| / Q   (fp32; s = 1 for an all-zero row)
-//   inv       = 1 / s[m]             (fp32, correctly rounded)
-//   code[m,k] = RNE(x[m,k] * inv)    (fp32 product, saturated to +-Q)
+//   code[m,k] = RNE(x[m,k] / s[m])   (correctly rounded fp32 quotient,
+//                                     saturated to +-Q)
 // with Q = 448 and an OCP e4m3fn code for FP8 (a negative value that rounds
 // to zero gives code 0), Q = 127 and a two's-complement byte for INT8, so
-// that code * s[m] approximates x[m,k].
+// that code * s[m] approximates x[m,k].  The fused requantisation of the MoE
+// gate_up output (moe.hip) follows the same rule.
 //
 // Layout: x [m, k] fp16/bf16 row-major, codes [m, k] bytes, scales [m] fp32.
 // One workgroup per row: every thread loads its 16-byte chunks of the row
@@ -52,12 +52,13 @@ __device__ inline float chunk_absmax(u4_t v) {
   return m;
 }
 
-// Eight quantised bytes of one chunk, little-endian in two words.
+// Eight quantised bytes of one chunk, little-endian in two words.  The
+// quotient is the correctly rounded fp32 division (hipcc's default for '/').
 template <bool BF16, bool FP8>
-__device__ inline uint2 chunk_codes(u4_t v, float inv) {
+__device__ inline uint2 chunk_codes(u4_t v, float s) {
   float f[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) f[j] = elem<BF16>(v[j >> 1], j & 1) * inv;
+  for (int j = 0; j < 8; ++j) f[j] = elem<BF16>(v[j >> 1], j & 1) / s;
   uint32_t w[2];
   if constexpr (FP8) {
 #pragma unroll
@@ -113,13 +114,12 @@ __global__ void __launch_bounds__(1024) quantize_rows_kernel(const u4_t* __restr
   for (int w = 1; w < (nt >> 6); ++w) amax = fmaxf(amax, wmax[w]);
 
   const float s = amax > 0.f ? amax / (FP8 ? 448.f : 127.f) : 1.f;
-  const float inv = 1.f / s;
 #pragma unroll
   for (int i = 0; i < kCache; ++i) {
     const int64_t c = tid + (int64_t)i * nt;
-    if (c < k8) cr[c] = chunk_codes<BF16, FP8>(v[i], inv);
+    if (c < k8) cr[c] = chunk_codes<BF16, FP8>(v[i], s);
   }
-  for (int64_t c = tid + (int64_t)kCache * nt; c < k8; c += nt) cr[c] = chunk_codes<BF16, FP8>(xr[c], inv);
+  for (int64_t c = tid + (int64_t)kCache * nt; c < k8; c += nt) cr[c] = chunk_codes<BF16, FP8>(xr[c], s);
   if (tid == 0) scales[row] = s;
 }
 

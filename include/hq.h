@@ -304,10 +304,16 @@ hq_status hq_moe_align(int64_t t, int topk, int num_experts, int block_m, const 
  *                             sorted_ids[r] / topk of `a` [t, k];
  *                             out[max_padded, n/2] (plan out dtype) =
  *                             SiLU(h[:, :n/2]) * h[:, n/2:].
- *   epi HQ_EPI_SILU_MUL_QFP8  as above, then per-row fp8 e4m3 requant:
- *                             out = uint8 codes [max_padded, n/2], out_scale =
- *                             fp32 [max_padded], s = max|act| / 448 (1 for an
- *                             all-zero row), codes = RNE(act / s).
+ *   epi HQ_EPI_SILU_MUL_QFP8  as above, then per-row fp8 e4m3 requant by the
+ *                             rule of hq_quantize_per_token: out = uint8
+ *                             codes [max_padded, n/2], out_scale = fp32
+ *                             [max_padded], s = max|act| / 448 (1 for an
+ *                             all-zero row), codes = RNE(act / s) with a
+ *                             correctly rounded fp32 quotient, saturated to
+ *                             +-448.  act is the fp32 value the epilogue
+ *                             forms; after the call the first
+ *                             max_padded * n/2 * 4 bytes of ws hold those
+ *                             fp32 rows (rows of padding slots unspecified).
  *   epi HQ_EPI_TOPK_COMBINE   down: row r of `a` [max_padded, k] is the
  *                             intermediate of slot sorted_ids[r];
  *                             out = y [t, n] (plan out dtype),
@@ -323,10 +329,12 @@ hq_status hq_moe_align(int64_t t, int topk, int num_experts, int block_m, const 
  * per aligned row for down), else NULL.  topk_w: device fp32 [t, topk]
  * (TOPK_COMBINE only).  Rows of padding slots (and, for gate_up, of slots
  * with an out-of-range expert id) are left unwritten.  ws: the workspace of
- * hq_moe_workspace_bytes (the fp8 requant's fp32 rows and row maxima, or the
- * combine's t*topk weighted slot rows), zero-filled once before first use
- * (the row maxima are re-armed by every call).  As for hq_gemm, activations
- * or one expert's weights of 2 GiB or more are HQ_ERR_UNSUPPORTED. */
+ * hq_moe_workspace_bytes (the fp8 requant's fp32 rows, or the combine's
+ * t*topk weighted slot rows); every call writes what it reads, so its
+ * contents need no initialisation and no state carries over between calls
+ * (two calls that overlap in time must not share one workspace).  As for
+ * hq_gemm, activations or one expert's weights of 2 GiB or more are
+ * HQ_ERR_UNSUPPORTED. */
 hq_status hq_moe_workspace_bytes(const hq_plan* plan, int64_t t, int topk, size_t* bytes);
 hq_status hq_moe_gemm(const hq_plan* plan, int64_t t, int topk, const void* a, const float* a_scale,
                       const int32_t* sorted_ids, const int32_t* block_expert, const int32_t* num_padded,
@@ -338,12 +346,10 @@ hq_status hq_moe_gemm(const hq_plan* plan, int64_t t, int topk, const void* a, c
  * 8-bit activations with one fp32 scale per row (W4A8: INT8 or FP8
  * activations, FP8 for MXFP4 weights -- Humming page on news.ditty.ir,
  * summary; cocoloop.cn, format section).  The pages do not say how the
- * activations are quantised; this is the plain symmetric per-row rule, with
- * the quotient taken as a product with the reciprocal scale:
+ * activations are quantised; this is the plain symmetric per-row rule:
  *   scales[r]  = max_j |x[r, j]| / Q, computed in fp32 (1 for an all-zero row)
- *   codes[r,j] = x[r, j] * (1 / scales[r]), reciprocal and product in fp32
- *                (each correctly rounded), rounded to nearest even and
- *                saturated to +-Q
+ *   codes[r,j] = x[r, j] / scales[r], the correctly rounded fp32 quotient,
+ *                rounded to nearest even and saturated to +-Q
  * with Q = 448 and OCP e4m3fn codes (out = HQ_FP8_E4M3; -0 gives code 0) or
  * Q = 127 and two's-complement int8 codes (out = HQ_INT8; -128 is never
  * produced).  The (codes, scales) pair is what hq_gemm takes as (a, a_scale).

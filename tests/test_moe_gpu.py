@@ -17,6 +17,7 @@ import bit_quantized_gemm_repack_amd as hq
 import datagen
 from oracle import gemm as og
 from oracle import moe as om
+from oracle import quant as oq
 from oracle.formats import e4m3_value
 
 pytestmark = pytest.mark.gpu
@@ -145,8 +146,26 @@ def run_layer(layer, T, act, topk, key=(5,), sample=None, masked=0.0):
         assert ok.all(), f"gate_up act: {(~ok).sum()} bad, max err/tau {ratio.max():.3g}"
         act_rows = act_gpu
     else:
-        dq = e4m3_value(codes.cpu().numpy()[rows]) * scl.cpu().numpy()[rows, None].astype(np.float64)
-        bound = om.fp8_rows_bound(dq, scl.cpu().numpy()[rows], gu["act"], gu["tau_act"])
+        codes_h, scl_h = codes.cpu().numpy()[rows], scl.cpu().numpy()[rows]
+        # the fp32 act rows the epilogue formed (the first max_padded * I * 4
+        # bytes of the workspace) against the oracle's act
+        mp = sid.numel()
+        ws = p1.moe_workspace(T, topk, a.device)
+        act32 = ws[: mp * I * 4].view(torch.float32).view(mp, I).cpu().numpy()[rows]
+        err32 = np.abs(act32.astype(np.float64) - gu["act"])
+        assert (err32 <= gu["tau_act"] + 2.0 ** -20 * np.abs(gu["act"])).all(), \
+            f"gate_up fp32 act: {(err32 > gu['tau_act']).sum()} bad"
+        # the requant follows the per-token quantiser's rule bit for bit on those rows
+        qc, qs = oq.quantize_rows(act32, "fp8")
+        assert np.array_equal(codes_h, qc), f"fp8 requant codes: {(codes_h != qc).sum()} differ from the rule"
+        assert np.array_equal(scl_h, qs), "fp8 requant scales differ from the rule"
+        # the scale against the oracle act's row maximum (a stale or inflated
+        # maximum would miss this)
+        s64 = np.abs(gu["act"]).max(1) / 448.0
+        slack = (gu["tau_act"] + 2.0 ** -20 * np.abs(gu["act"])).max(1) / 448.0 + 2.0 ** -22 * s64
+        assert (np.abs(scl_h - s64) <= slack).all(), "fp8 requant scale off the oracle's row maximum"
+        dq = e4m3_value(codes_h) * scl_h[:, None].astype(np.float64)
+        bound = om.fp8_rows_bound(dq, scl_h, gu["act"], gu["tau_act"])
         err = np.abs(dq - gu["act"])
         assert (err <= bound).all(), f"fp8 requant: {(err > bound).sum()} bad"
         act_rows = dq
@@ -208,10 +227,19 @@ def test_small_layer_masked_experts(small_layer, small_layer_tiled, T, topk, til
 
 
 def test_small_layer_repeat_calls_reuse_workspace(small_layer):
-    # the fp32 combine accumulators and row maxima re-arm themselves: calls
-    # in a row on the same workspace all pass
+    # calls in a row on the same plans and workspace all pass: nothing a call
+    # leaves in the workspace is read by the next one
     for act in ("fp8", "bf16", "fp8"):
         run_layer(small_layer, 64, act, 2, key=(13,))
+
+
+@pytest.mark.parametrize("tiled", [False, True])
+def test_fp8_requant_with_fewer_tokens_than_the_call_before(small_layer, small_layer_tiled, tiled):
+    # a large call fills the workspace, then smaller ones (other t, topk, block
+    # size) reuse it: their scales must come from their own rows
+    lay = small_layer_tiled if tiled else small_layer
+    for T, topk in ((400, 3), (5, 8), (1, 2), (64, 2)):
+        run_layer(lay, T, "fp8", topk, key=(29,))
 
 
 @pytest.fixture(scope="module")
