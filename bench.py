@@ -375,50 +375,119 @@ def run_step(points, r):
         p["plan"].gemm(p["a"], w, meta, out=p["out"], ws=p["ws"])
 
 
-def check_point(points, shapes):
-    """Spot check of one point against the CPU oracle (sampled rows)."""
+def check_points(points, shapes):
+    """Every point's last timed output against the CPU oracle: all rows of
+    each point (the M = 64 oracle result of a shape covers its smaller M, whose
+    activations are its first rows).  Returns the largest err / tau and the
+    fraction of outputs within the literal tau (without the output format's
+    half ulp)."""
     from oracle import gemm as og
 
-    p = next(q for q in points if q["M"] == 16 and q["N"] == 4096 and q["K"] == 4096)
-    d = shapes[(4096, 4096)]["data"]
-    ref = og.gemm_w4a16(d["a"][:16].double().numpy(), d["codes"], d["scales"].double().numpy(), d["zeros"],
-                        out_fmt="bf16")
-    ok, _, ratio = og.check(p["out"].double().cpu().numpy(), ref["c64"], ref["tau"], "bf16")
-    if not ok.all():
-        raise SystemExit(f"bench: output check failed ({int((~ok).sum())} outputs, max err/tau {ratio.max():.3g})")
-    return float(ratio.max())
+    refs = {}
+    worst, lit_ok, total = 0.0, 0, 0
+    for p in points:
+        key = (p["N"], p["K"])
+        if key not in refs:
+            d = shapes[key]["data"]
+            refs[key] = og.gemm_w4a16(d["a"].double().numpy(), d["codes"], d["scales"].double().numpy(),
+                                      d["zeros"], out_fmt="bf16")
+        ref = refs[key]
+        M = p["M"]
+        ok, lit, ratio = og.check(p["out"].double().cpu().numpy(), ref["c64"][:M], ref["tau"][:M], "bf16")
+        if not ok.all():
+            raise SystemExit(f"bench: output check failed at M={M} N={p['N']} K={p['K']} "
+                             f"({int((~ok).sum())} outputs, max err/tau {ratio.max():.3g})")
+        worst = max(worst, float(ratio.max()))
+        lit_ok += int(lit.sum())
+        total += lit.size
+    return worst, lit_ok / total, total
 
 
-def gpu_state():
-    """Clock and power state of the GPU as amd-smi reports it right after the
-    timed region (a child process; None where the tool is unavailable, and
-    under a profiler, whose preloaded library would attach the child to the GPU
-    before it starts the tool's interpreter)."""
-    import subprocess
+class GpuStateSampler:
+    """The GPU's shader clock and power, read in this process from the amdgpu
+    driver's sysfs files (pp_dpm_sclk: the level marked '*' is the current
+    one; hwmon power1_average or power1_input, microwatts) by a thread that
+    samples every `period` seconds while the timed replays run.  No child
+    process is started.  The card is the one whose PCI address matches
+    torch's device 0; None where the files are not readable."""
 
-    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
-        return None
-    try:
-        r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--power", "--json"], capture_output=True,
-                           text=True, timeout=30)
-        if r.returncode != 0:
+    def __init__(self, period=0.001):
+        import glob
+        import threading
+
+        self.period = period
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+        self.card = None
+        try:
+            pr = torch.cuda.get_device_properties(0)
+            want = (int(pr.pci_domain_id), int(pr.pci_bus_id), int(pr.pci_device_id))
+        except Exception:  # pragma: no cover
+            want = None
+        for dev_dir in sorted(glob.glob("/sys/class/drm/card*/device")):
+            try:
+                bdf = os.path.basename(os.path.realpath(dev_dir))  # dddd:bb:dd.f
+                dom, bus, rest = bdf.split(":")
+                key = (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16))
+            except ValueError:
+                continue
+            if (want is None or key == want) and os.path.exists(os.path.join(dev_dir, "pp_dpm_sclk")):
+                self.card = dev_dir
+                break
+        self.power_file = None
+        if self.card:
+            for name in ("power1_average", "power1_input"):
+                hits = sorted(glob.glob(os.path.join(self.card, "hwmon", "hwmon*", name)))
+                if hits:
+                    self.power_file = hits[0]
+                    break
+
+    def _read(self):
+        clk = pw = None
+        try:
+            with open(os.path.join(self.card, "pp_dpm_sclk")) as f:
+                for line in f:
+                    if "*" in line:
+                        clk = float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz"))
+        except (OSError, ValueError, IndexError):
+            pass
+        if self.power_file:
+            try:
+                with open(self.power_file) as f:
+                    pw = int(f.read().strip()) / 1e6
+            except (OSError, ValueError):
+                pass
+        return clk, pw
+
+    def _run(self):
+        while not self._stop.is_set():
+            self.samples.append(self._read())
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+
+        if self.card:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+
+    def summary(self):
+        if not self.card:
             return None
-        d = json.loads(r.stdout)
-        d = d.get("gpu_data", d) if isinstance(d, dict) else d
-        d = d[0] if isinstance(d, list) and d else d
-        clk, pw = d.get("clock", {}), d.get("power", {})
-        gfx = [v["clk"]["value"] for k, v in clk.items() if k.startswith("gfx") and isinstance(v.get("clk"), dict)]
-        mem = [v["clk"]["value"] for k, v in clk.items() if k.startswith("mem") and isinstance(v.get("clk"), dict)]
-        out = {"gfx_clk_mhz_mean": round(sum(gfx) / len(gfx), 1) if gfx else None,
-               "gfx_clk_max_mhz": next((v["max_clk"]["value"] for k, v in clk.items()
-                                        if k.startswith("gfx") and isinstance(v.get("max_clk"), dict)), None),
-               "mem_clk_mhz": mem[0] if mem else None,
-               "clk_locked": next((v.get("clk_locked") for k, v in clk.items() if k.startswith("gfx")), None),
-               "socket_power_w": (pw.get("socket_power") or {}).get("value") if isinstance(pw, dict) else None,
-               "when": "amd-smi right after the timed region"}
-        return out
-    except (OSError, ValueError, subprocess.SubprocessError):
-        return None
+        clks = [c for c, _ in self.samples if c is not None]
+        pws = [w for _, w in self.samples if w is not None]
+        return {"gfx_clk_mhz_mean": round(float(np.mean(clks)), 1) if clks else None,
+                "gfx_clk_mhz_min": min(clks) if clks else None, "gfx_clk_mhz_max": max(clks) if clks else None,
+                "power_w_mean": round(float(np.mean(pws)), 1) if pws else None, "samples": len(self.samples),
+                "source": f"{self.card}/pp_dpm_sclk and {self.power_file}",
+                "when": "sampled in-process every ~1 ms during the timed graph replays"}
 
 
 def mfma_ceilings(hip, L, dev):
@@ -576,11 +645,12 @@ def run_quant(args):
         graphs[i % R].replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(args.steps):
-        graphs[i % R].replay()
-    e1.record()
-    torch.cuda.synchronize()
+    with GpuStateSampler() as smp:
+        e0.record()
+        for i in range(args.steps):
+            graphs[i % R].replay()
+        e1.record()
+        torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
     print(f"[bench] graph steps: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
@@ -645,8 +715,7 @@ def run_quant(args):
                      "kernel": "hq::quantize_rows_kernel", "mean_kernel_us": round(mean_us, 3),
                      "mean_algorithmic_bytes": int(step_bytes / n)},
         "cpu_baseline": cpu,
-        "ceilings": dict(ceilings, frac_of_same_bytes_read=round(achieved / ceilings["same_bytes_read_GBps"], 4)),
-        "gpu_state": state,
+        "gpu_state": smp.summary(),
         "points": per_point,
     }
     print(json.dumps(line), flush=True)
@@ -662,13 +731,13 @@ FP8_PEAK_TFLOPS = 5000.0
 FP4_PEAK_TFLOPS = 10100.0
 
 
-def _prefill_points(dev):
+def _prefill_points(dev, Ms=(1024, 4096)):
     import bit_quantized_gemm_repack_amd as hq
     import datagen
 
     N = K = 8192
     pts = []
-    for M in (1024, 4096):
+    for M in Ms:
         d = datagen.dense_w4a16(M, N, K, act="f16", zp="fixed", key=(3,))
         plan = hq.Plan(N, K, hq.w4a16("f16"), max_m=M)
         w, meta = plan.repack(torch.from_numpy(d["codes"]).to(dev), d["scales"].to(dev))
@@ -678,8 +747,16 @@ def _prefill_points(dev):
         out = torch.empty((M, N), dtype=torch.float16, device=dev)
         ws = plan.workspace(M, dev)
         byt = N * K // 2 + 2 * N * (K // 128) + 2 * M * K + 2 * M * N
+        def check(out=out, d=d, M=M):
+            from oracle import gemm as og
+
+            rows = np.sort(np.random.default_rng(M).choice(M, 8, replace=False))
+            ref = og.gemm_w4a16(d["a"][rows].double().numpy(), d["codes"], d["scales"].double().numpy(), 8,
+                                out_fmt="f16")
+            return og.check(out[rows].double().cpu().numpy(), ref["c64"], ref["tau"], "f16")
+
         pts.append(dict(name=f"M={M} N={N} K={K}", R=R, bytes=byt, flops=2 * M * N * K, peak=FP16_PEAK_TFLOPS,
-                        mfma="f16", plan=plan.describe(M),
+                        mfma="f16", plan=plan.describe(M), check=check,
                         calls=lambda r, plan=plan, ws_=ws_, a_=a_, out=out, ws=ws:
                         [lambda: plan.gemm(a_[r % 4], ws_[r][0], ws_[r][1], out=out, ws=ws)]))
     return pts, "quantized GEMM TFLOPS vs M (dense W4A16 prefill)", \
@@ -687,14 +764,14 @@ def _prefill_points(dev):
         "scales, zero point 8), fp16 output", "f16"
 
 
-def _w4a8_points(dev):
+def _w4a8_points(dev, Ms=(1, 16, 128, 1024), kinds=("mxfp4", "int")):
     import bit_quantized_gemm_repack_amd as hq
     import datagen
 
     N, K = 4096, 7168
     pts = []
-    for kind in ("mxfp4", "int"):
-        for M in (1, 16, 128, 1024):
+    for kind in kinds:
+        for M in Ms:
             d = datagen.w4a8_mxfp4(M, N, K) if kind == "mxfp4" else datagen.w4a8_int(M, N, K)
             plan = hq.Plan(N, K, hq.w4a8_mxfp4() if kind == "mxfp4" else hq.w4a8_int(), max_m=M)
             if kind == "mxfp4":
@@ -708,9 +785,20 @@ def _w4a8_points(dev):
             ws = plan.workspace(M, dev)
             meta_b = N * K // 32 if kind == "mxfp4" else 2 * N * (K // 128)
             byt = N * K // 2 + meta_b + M * K + 4 * M + 2 * M * N
+            def check(out=out, d=d, M=M, kind=kind):
+                from oracle import gemm as og
+
+                rows = np.sort(np.random.default_rng(M).choice(M, min(M, 8), replace=False))
+                ac, asc = d["a_codes"].numpy()[rows], d["a_scale"].numpy()[rows]
+                if kind == "mxfp4":
+                    ref = og.gemm_mxfp4_fp8(ac, asc, d["codes"], d["e8m0"])
+                else:
+                    ref = og.gemm_int4_int8(ac, asc, d["codes"], d["scales"].double().numpy())
+                return og.check(out[rows].double().cpu().numpy(), ref["c64"], ref["tau"], "bf16")
+
             pts.append(dict(name=f"{kind} M={M} N={N} K={K}", R=R, bytes=byt, flops=2 * M * N * K,
                             peak=FP8_PEAK_TFLOPS, mfma="fp8_fp4" if kind == "mxfp4" else "int8", plan=plan.describe(M),
-                            calls=lambda r, plan=plan, ws_=ws_, a=a, sa=sa, out=out, ws=ws:
+                            check=check, calls=lambda r, plan=plan, ws_=ws_, a=a, sa=sa, out=out, ws=ws:
                             [lambda: plan.gemm(a, ws_[r][0], ws_[r][1], a_scale=sa, out=out, ws=ws)]))
         del d
     return pts, "quantized GEMM TFLOPS and effective HBM GB/s vs M (W4A8)", \
@@ -830,14 +918,14 @@ def _w4a4_points(dev):
         "E8M0 scales per 32), bf16 output", "f4"
 
 
-def _moe_points(dev):
+def _moe_points(dev, Ts=(1, 32, 512, 4096), acts=("bf16", "fp8")):
     import bit_quantized_gemm_repack_amd as hq
     import datagen
 
     E, H, I, topk = 256, 7168, 256, 8
     wts = datagen.moe_weights(E, H, I, key=(5,))
     pts = []
-    for act in ("bf16", "fp8"):
+    for act in acts:
         q = hq.w4a16("bf16", scale="f16") if act == "bf16" else hq.w4a8_fp8(scale="f16")
         p1 = hq.MoePlan(2 * I, H, q, E, 4096, "silu_mul" if act == "bf16" else "silu_mul_qfp8")
         p2 = hq.MoePlan(H, I, q, E, 4096, "topk_combine")
@@ -845,7 +933,7 @@ def _moe_points(dev):
         w2, m2 = p2.repack(torch.from_numpy(wts["w2"]).to(dev), wts["s2"].to(dev))
         R = 2  # two copies of the 727 MB expert weights: > 1 GB
         cp = [(w1, m1, w2, m2)] + [(w1.clone(), m1.clone(), w2.clone(), m2.clone()) for _ in range(R - 1)]
-        for T in (1, 32, 512, 4096):
+        for T in Ts:
             rt = datagen.moe_routing(T)
             x = datagen.moe_activations(T, act=act)
             ids = torch.from_numpy(rt["topk_ids"]).to(dev)
@@ -896,6 +984,94 @@ def _moe_points(dev):
         "weights (group 128, fp16 scales, zero point 8); T in {1,32,512,4096}", "bf16/f8"
 
 
+def graph_time_point(p, steps, warmup):
+    """Mean time of one pass of the point's calls, in ms: one HIP graph per
+    weight copy of the rotating pool, replayed back to back between two events
+    on the replay stream (the launch gaps inside a graph included)."""
+    R = p["R"]
+    for r in range(min(R, 2)):
+        for c in p["calls"](r):
+            c()
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        for c in p["calls"](0):
+            c()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    graphs = []
+    for r in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in p["calls"](r):
+                c()
+        graphs.append(g)
+    for i in range(max(warmup, 2)):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        graphs[i % R].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del graphs
+    return e0.elapsed_time(e1) / steps
+
+
+def eager_call_times(p, steps, hip, L):
+    """Median device duration of each of the point's calls (dispatch-bracketing
+    events, eager launches), in us: the split of a multi-call point."""
+    import bit_quantized_gemm_repack_amd as hq
+
+    n = len(p["calls"](0))
+    times = [[] for _ in range(n)]
+    for i in range(steps):
+        pend = []
+        for j, c in enumerate(p["calls"](i % p["R"])):
+            a, b = hip.event(), hip.event()
+            hq._check(L.hq_time_next_launch(a, b))
+            c()
+            pend.append((j, a, b))
+        torch.cuda.synchronize()
+        for j, a, b in pend:
+            times[j].append(hip.elapsed_ms(a, b) * 1e3)
+            hip.destroy(a)
+            hip.destroy(b)
+    return [round(float(np.median(t)), 3) for t in times]
+
+
+def point_result(p, ms, ceil=None):
+    """Per-point figures from its graph-replay time `ms`."""
+    us = ms * 1e3
+    t_hbm = p["bytes"] / (HBM_PEAK_GBS * 1e3)
+    t_mfma = p["flops"] / (p["peak"] * 1e6)
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    r = {"point": p["name"], "us": round(us, 3), "GBps": round(p["bytes"] / us / 1e3, 1),
+         "TFLOPS": round(p["flops"] / us / 1e6, 2), "bound": bound, "roofline_frac": round(max(t_hbm, t_mfma) / us, 4),
+         "mfma_frac": round(t_mfma / us, 4), "hbm_frac": round(t_hbm / us, 4), "bytes": p["bytes"],
+         "flops": p["flops"], "plan": p["plan"]}
+    kind = p.get("mfma") or {FP16_PEAK_TFLOPS: "bf16", FP8_PEAK_TFLOPS: "fp8", FP4_PEAK_TFLOPS: "fp4"}[p["peak"]]
+    r["mfma_type"] = kind
+    if ceil:
+        r["frac_of_measured_mfma"] = round(r["TFLOPS"] / ceil[kind], 4)
+    if bound == "mfma":
+        r["roofline"] = {"bound": "mfma", "achieved": r["TFLOPS"], "peak": p["peak"], "unit": "TFLOP/s",
+                         "frac": r["mfma_frac"], "traffic": None}
+    else:
+        r["roofline"] = {"bound": "hbm", "achieved": r["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": r["hbm_frac"], "traffic": None}
+    if p.get("check"):
+        ok, lit, ratio = p["check"]()
+        if not ok.all():
+            raise SystemExit(f"bench: output check of {p['name']} failed ({int((~ok).sum())} outputs, "
+                             f"max err/tau {ratio.max():.3g})")
+        r["spot_check"] = {"rows": int(ok.shape[0]), "max_err_over_tau": round(float(ratio.max()), 4),
+                           "literal_tau_pass_frac": round(float(lit.mean()), 6)}
+    return r
+
+
 def run_points_workload(args, builder):
     import bit_quantized_gemm_repack_amd as hq
 
@@ -904,102 +1080,75 @@ def run_points_workload(args, builder):
     L = hq.lib()
     print(f"[bench] preparing the {args.workload} workload", file=sys.stderr, flush=True)
     pts, metric, workload, dtype = builder(dev)
-    R = max(p["R"] for p in pts)
-
-    def step(r):
+    ceil = mfma_ceilings(hip, L, dev)
+    points, step_ms = [], 0.0
+    with GpuStateSampler() as smp:
         for p in pts:
-            for c in p["calls"](r % p["R"]):
-                c()
-
-    for i in range(max(1, args.warmup)):
-        step(i)
-    torch.cuda.synchronize()
-    graphs = []
-    st = torch.cuda.Stream()
-    st.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(st):
-        step(0)
-    torch.cuda.current_stream().wait_stream(st)
-    torch.cuda.synchronize()
-    for r in range(R):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(r)
-        graphs.append(g)
-    for i in range(args.warmup):
-        graphs[i % R].replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(args.steps):
-        graphs[i % R].replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
-    print(f"[bench] graph steps: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
-
-    # per-point durations: the sum of the point's calls, each bracketed by events
-    times = {j: [] for j in range(len(pts))}
-    for i in range(args.steps):
-        pend = []
-        for j, p in enumerate(pts):
-            for c in p["calls"](i % p["R"]):
-                a, b = hip.event(), hip.event()
-                hq._check(L.hq_time_next_launch(a, b))
-                c()
-                pend.append((j, i, a, b))
-        torch.cuda.synchronize()
-        per = {}
-        for j, _, a, b in pend:
-            per[j] = per.get(j, 0.0) + hip.elapsed_ms(a, b)
-            hip.destroy(a)
-            hip.destroy(b)
-        for j, v in per.items():
-            times[j].append(v)
-    points, shares = [], []
-    for j, p in enumerate(pts):
-        ms = np.array(times[j])
-        us = float(np.median(ms)) * 1e3
-        t_hbm = p["bytes"] / (HBM_PEAK_GBS * 1e3)
-        t_mfma = p["flops"] / (p["peak"] * 1e6)
-        bound = "hbm" if t_hbm >= t_mfma else "mfma"
-        points.append({"point": p["name"], "kernel_us": round(us, 3),
-                       "kernel_us_p10": round(float(np.percentile(ms, 10)) * 1e3, 3),
-                       "kernel_us_p90": round(float(np.percentile(ms, 90)) * 1e3, 3),
-                       "GBps": round(p["bytes"] / us / 1e3, 1), "TFLOPS": round(p["flops"] / us / 1e6, 2),
-                       "bound": bound, "roofline_frac": round(max(t_hbm, t_mfma) / us, 4),
-                       "mfma_frac": round(t_mfma / us, 4), "hbm_frac": round(t_hbm / us, 4), "plan": p["plan"]})
-        shares.append(us)
+            ms = graph_time_point(p, args.steps, args.warmup)
+            step_ms += ms
+            r = point_result(p, ms, ceil)
+            if len(p["calls"](0)) > 1:
+                r["calls_us_eager"] = eager_call_times(p, min(args.steps, 20), hip, L)
+            points.append(r)
+            print(f"[bench] {p['name']}: {r['us']:.1f} us ({r['bound']} {r['roofline_frac']:.3f})", file=sys.stderr,
+                  flush=True)
     step_bytes = sum(p["bytes"] for p in pts)
     step_flops = sum(p["flops"] for p in pts)
-    ceil = mfma_ceilings(hip, L, dev)
-    for p, q in zip(points, pts):
-        kind = q.get("mfma") or {FP16_PEAK_TFLOPS: "bf16", FP8_PEAK_TFLOPS: "fp8", FP4_PEAK_TFLOPS: "fp4"}[q["peak"]]
-        p["mfma_type"] = kind
-        p["frac_of_measured_mfma"] = round(p["TFLOPS"] / ceil[kind], 4)
-    dom = int(np.argmax(shares))
-    dp, dq = points[dom], pts[dom]
-    if dp["bound"] == "mfma":
-        roof = {"bound": "mfma", "achieved": dp["TFLOPS"], "peak": dq["peak"], "unit": "TFLOP/s",
-                "frac": dp["mfma_frac"], "measured_peak": ceil[dp["mfma_type"]],
-                "frac_of_measured_peak": dp["frac_of_measured_mfma"]}
-    else:
-        roof = {"bound": "hbm", "achieved": dp["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dp["hbm_frac"]}
-    roof.update({"traffic": None, "point": dp["point"], "kernel_us": dp["kernel_us"]})
-
+    dom = int(np.argmax([q["us"] for q in points]))
+    roof = dict(points[dom]["roofline"], point=points[dom]["point"], us=points[dom]["us"])
+    if roof["bound"] == "mfma":
+        roof["measured_peak"] = ceil[points[dom]["mfma_type"]]
+        roof["frac_of_measured_peak"] = points[dom]["frac_of_measured_mfma"]
     cpu = None
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         cpu = _cpu_sample(args.workload, args.cpu_budget)
-    line = {"metric": metric, "value": round(step_flops / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+    line = {"metric": metric, "value": round(step_flops / (step_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
             "config": {"workload": workload, "points_per_step": len(pts), "step_bytes": step_bytes,
-                       "step_flops": step_flops, "gbps_per_step_time": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-                       "timing": "HIP graph replay per step; per-point time = sum of its calls' "
-                                 "dispatch-bracketing HIP events, median over the steps"},
-            "roofline": roof, "cpu_baseline": cpu, "mfma_ceilings_TFLOPS": ceil, "points": points}
+                       "step_flops": step_flops, "gbps_per_step_time": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
+                       "timing": "per point: HIP graph replays of its calls, one graph per weight copy, events "
+                                 "around the replays; the step is the sum over the points"},
+            "roofline": roof, "cpu_baseline": cpu, "mfma_ceilings_TFLOPS": ceil, "gpu_state": smp.summary(),
+            "points": points}
     print(json.dumps(line), flush=True)
+
+
+# The MFMA-bound and MoE targets measured beside the decode line (bench.py
+# with no --workload): each entry is one point of another workload, timed by
+# graph replay like the decode step, with its roofline, an output check on
+# sampled rows where the oracle is cheap, and a bounded CPU-oracle sample.
+EXTRA = (("prefill_f16_M4096", "prefill", lambda dev: _prefill_points(dev, Ms=(4096,))),
+         ("w4a8_mxfp4_fp8_M1024", "w4a8", lambda dev: _w4a8_points(dev, Ms=(1024,), kinds=("mxfp4",))),
+         ("w4a8_int4_int8_M1024", "w4a8int", lambda dev: _w4a8_points(dev, Ms=(1024,), kinds=("int",))),
+         ("moe_bf16_T4096", "moe", lambda dev: _moe_points(dev, Ts=(4096,), acts=("bf16",))),
+         ("moe_fp8_T4096", "moe", lambda dev: _moe_points(dev, Ts=(4096,), acts=("fp8",))))
+
+
+def measure_extra(args, dev, hip, L, cpu_budget):
+    ceil = mfma_ceilings(hip, L, dev)
+    out = {"mfma_ceilings_TFLOPS": ceil}
+    for name, cpu_kind, builder in EXTRA:
+        print(f"[bench] extra: {name}", file=sys.stderr, flush=True)
+        pts, _, workload, dtype = builder(dev)
+        p = pts[0]
+        steps = max(10, min(args.steps, 50))
+        r = point_result(p, graph_time_point(p, steps, min(args.warmup, 5)), ceil)
+        if len(p["calls"](0)) > 1:
+            r["calls_us_eager"] = eager_call_times(p, 10, hip, L)
+        r["workload"] = workload
+        r["dtype"] = dtype
+        r["steps"] = steps
+        if cpu_budget > 0:
+            r["cpu_baseline"] = _cpu_sample(cpu_kind, cpu_budget)
+        out[name] = r
+        print(f"[bench] extra {name}: {r['us']:.1f} us ({r['bound']} {r['roofline_frac']:.3f})", file=sys.stderr,
+              flush=True)
+        del pts, p
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
 
 
 def _cpu_sample(workload, budget):
@@ -1057,6 +1206,12 @@ def _cpu_sample(workload, budget):
             t0 = time.perf_counter()
             og.gemm_mxfp4_fp8(d["a_codes"].numpy(), d["a_scale"].numpy(), d["codes"], d["e8m0"])
             what = "W4A8-MXFP4 M=16 N=4096 K=7168"
+        elif workload == "w4a8int":
+            M, N, K = 16, 4096, 7168
+            d = datagen.w4a8_int(M, N, K)
+            t0 = time.perf_counter()
+            og.gemm_int4_int8(d["a_codes"].numpy(), d["a_scale"].numpy(), d["codes"], d["scales"].double().numpy())
+            what = "W4A8-INT4xINT8 M=16 N=4096 K=7168"
         else:
             from oracle import moe as om
 
@@ -1090,6 +1245,8 @@ def main():
     ap.add_argument("--rotations", type=int, default=4)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="decode: skip the prefill / W4A8 / MoE points reported in 'extra'")
     ap.add_argument("--autotune", action="store_true",
                     help="decode: install a measured execution choice per point (hq_plan_autotune) first")
     ap.add_argument("--workload", choices=("decode", "quant", "prefill", "w4a8", "w4a4", "w8a16", "w2a16", "w3a16", "mxint4", "nvfp4", "moe"),
@@ -1153,18 +1310,19 @@ def main():
 
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    e0.record()
-    for i in range(args.steps):
-        graphs[i % R].replay()
-    e1.record()
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t_wall) * 1e3
+    with GpuStateSampler() as smp:
+        t_wall = time.perf_counter()
+        e0.record()
+        for i in range(args.steps):
+            graphs[i % R].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t_wall) * 1e3
     ms_per_step = e0.elapsed_time(e1) / args.steps
     print(f"[bench] graph steps: {ms_per_step * 1e3:.1f} us/step (wall {wall_ms / args.steps * 1e3:.1f})",
           file=sys.stderr, flush=True)
 
-    # --- per-kernel durations (events around each dispatch) ------------------
+    # --- per-call durations, eager (dispatch-bracketing events) -------------
     n = len(points)
     evs = [(hip.event(), hip.event()) for _ in range(args.steps * n)]
     torch.cuda.synchronize()
@@ -1177,11 +1335,9 @@ def main():
             p["plan"].gemm(p["a"], w, meta, out=p["out"], ws=p["ws"])
     torch.cuda.synchronize()
     per_point = []
-    tot_k_ms = 0.0
     for j, p in enumerate(points):
         ms = [hip.elapsed_ms(*evs[i * n + j]) for i in range(args.steps)]
         us = float(np.mean(ms)) * 1e3
-        tot_k_ms += float(np.sum(ms))
         gbs = p["bytes"] / (us * 1e-6) / 1e9
         per_point.append({"M": p["M"], "N": p["N"], "K": p["K"], "kernel_us": round(us, 3),
                           "kernel_us_p10": round(float(np.percentile(ms, 10)) * 1e3, 3),
@@ -1192,25 +1348,37 @@ def main():
     for a, b in evs:
         hip.destroy(a)
         hip.destroy(b)
-    launches = args.steps * n
-    mean_kernel_us = tot_k_ms / launches * 1e3
-    mean_bytes = step_bytes / n
-    achieved = mean_bytes / (mean_kernel_us * 1e-6) / 1e9
-    state = gpu_state()
     ceilings = measure_ceilings(points, hip, L, R, args.steps)
     for pp, us in zip(per_point, ceilings.pop("point_read_us")):
         pp["plain_read_of_weights_us"] = us
 
-    cpu = None
-    if not args.no_cpu:
-        # the CPU oracle leg: a spot check of the timed launches' output, then its timing
-        max_ratio = check_point(points, shapes)
-        print(f"[bench] spot check against the oracle ok (max err/tau {max_ratio:.3g}); timing the CPU oracle",
-              file=sys.stderr, flush=True)
-        cpu = cpu_baseline(args.cpu_budget)
-        cpu["spot_check_max_err_over_tau"] = round(max_ratio, 4)
-
+    # the roofline of the step: algorithmic bytes of the twelve calls over the
+    # graph-replayed step time (events around the timed replays on the replay
+    # stream), i.e. the mean call of the step with its launch gap included
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    mean_call_us = ms_per_step * 1e3 / n
+    roof = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(value / HBM_PEAK_GBS, 4), "traffic": measured_traffic([p["plan"] for p in per_point]),
+            "kernel": "hq_gemm calls of the sweep: hq::qgemm_skinny / hq::qgemm_tiled",
+            "mean_call_us": round(mean_call_us, 3), "mean_algorithmic_bytes": int(step_bytes / n),
+            "timing": "graph-replayed step: events around the timed replays; mean call = step / 12"}
+
+    cpu = None
+    extra = None
+    if not args.no_cpu:
+        # the CPU oracle leg: every point's timed output against the oracle, then its timing
+        max_ratio, lit_frac, n_out = check_points(points, shapes)
+        print(f"[bench] output check against the oracle ok ({n_out} outputs, max err/tau {max_ratio:.3g}, "
+              f"literal-tau pass fraction {lit_frac:.4f}); timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(args.cpu_budget)
+        cpu["check"] = {"outputs": n_out, "max_err_over_tau": round(max_ratio, 4),
+                        "literal_tau_pass_frac": round(lit_frac, 6)}
+    del points, shapes, graphs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        extra = measure_extra(args, dev, hip, L, 0 if args.no_cpu else 2.5)
+
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -1227,17 +1395,14 @@ def main():
         "config": {"workload": WORKLOAD, "launches_per_step": n, "step_bytes": step_bytes,
                    "step_flops": step_flops, "tflops_per_step_time": round(step_flops / (ms_per_step * 1e-3) / 1e12, 3),
                    "weight_pool_rotations": R, "execution_choice": "autotuned" if args.autotune else "heuristic",
-                   "timing": "HIP graph replay per step; kernel durations from dispatch-bracketing HIP events"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic([p["plan"] for p in per_point]),
-                     "kernel": "hq_gemm calls of the sweep: hq::qgemm_skinny / hq::qgemm_tiled "
-                               "(+ hq::splitk_reduce_kernel where K is split)",
-                     "mean_kernel_us": round(mean_kernel_us, 3), "mean_algorithmic_bytes": int(mean_bytes)},
+                   "timing": "HIP graph replay per step; per-call durations in 'points' from dispatch-bracketing "
+                             "HIP events on eager launches"},
+        "roofline": roof,
         "cpu_baseline": cpu,
-        "ceilings": dict(ceilings, frac_of_same_bytes_read=round(achieved / ceilings["same_bytes_read_GBps"], 4)),
-        "gpu_state": state,
+        "ceilings": dict(ceilings, frac_of_same_bytes_read=round(value / ceilings["same_bytes_read_GBps"], 4)),
+        "gpu_state": smp.summary(),
         "points": per_point,
+        "extra": extra,
     }
     print(json.dumps(line), flush=True)
 

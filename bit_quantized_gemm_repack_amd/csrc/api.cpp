@@ -198,7 +198,14 @@ Exec choose_exec(const hq_plan* p, int64_t m, const hq_tuning* up) {
   // from 33 rows on, the activation tile in LDS is shared by the four waves
   // instead of being re-read by every 16-column workgroup.
   const bool tiled_ok = p->compute.epi != HQ_EPI_I32_ACC && N % 128 == 0;
-  const bool tiled_auto = m > 32;
+  // 33..64 rows of 16-bit activations (INT4 weights): 16-row x 64-column skinny blocks with
+  // no K split while they fill the chip at most once (N/64 * ceil(m/16) <=
+  // 256 workgroups); a sweep of the decode shapes on MI355X put them ahead of
+  // the split tiled kernel there (N = K = 4096: 9.7 against 14.8 us; K =
+  // 14336: even) and behind it for wider layers (N = 14336: 28 against 24 us)
+  const bool skinny_mid = (p->fmt == FMT_W16F16 || p->fmt == FMT_W16BF16) && m > 32 && m <= 64 && N % 64 == 0 && (N / 64) * cdiv(mm, 16) <= 256 &&
+                          p->compute.kind == HQ_GEMM_DENSE;
+  const bool tiled_auto = m > 32 && !skinny_mid;
   if (tiled_ok && (u.kernel == KER_TILED || (u.kernel == 0 && tiled_auto))) {
     e.kernel = KER_TILED;
     // Tile shapes from sweeps on MI355X (N = 4096..16384, K = 2048..8192):
@@ -250,6 +257,10 @@ Exec choose_exec(const hq_plan* p, int64_t m, const hq_tuning* up) {
   SkinnyCfg c{};
   c.mb = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
   c.nb = 1;
+  if (skinny_mid && u.kernel == 0) {
+    c.mb = 1;
+    c.nb = 4;
+  }
   // Rules from a sweep of the decode shapes on MI355X (kernel durations):
   //   wide layers (>= 512 column blocks): 4 column blocks per workgroup;
   //   otherwise one column block per workgroup with K split over the waves;
@@ -277,7 +288,7 @@ Exec choose_exec(const hq_plan* p, int64_t m, const hq_tuning* up) {
       c.nb = (N / 16 >= 384 && N % 32 == 0) ? 2 : 1;
       if (N / 16 >= 1024 && N % 64 == 0 && (!w8_weights(p->fmt) || m > 4)) c.nb = 4;
     }
-  } else if (c.mb == 1 && m > 4 && G >= 64 && N % 64 == 0 && N / 64 >= 32) {
+  } else if (c.mb == 1 && m > 4 && m <= 32 && G >= 64 && N % 64 == 0 && N / 64 >= 32) {
     c.nb = 4;
     auto_split = 4;
   }

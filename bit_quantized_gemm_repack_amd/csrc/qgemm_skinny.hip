@@ -253,6 +253,9 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f4_t{0.f, 0.f, 0.f, 0.f};
+  // the 16-bit operands' exponent pattern, held in a VGPR so that each
+  // unpacked register is one v_and_or_b32 (mask literal, magic register)
+  [[maybe_unused]] const uint32_t magic_v = opaque_vgpr(f16_act(FMT) ? 0x64006400u : 0x43004300u);
 
   auto compute = [&](const Stage<FMT, MB, NB>& st, int g) {
     [[maybe_unused]] f4_t rs[MB];
@@ -291,7 +294,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
         // exact offset operands (OFF + high), (OFF + low); the row sums
         // remove (H + 1) OFF + z, H = 16 or 4.
         constexpr float kH = FI::kW8 ? 16.f : 4.f;
-        const uint32_t magic = f16_act(FMT) ? 0x64006400u : 0x43004300u;
+        const uint32_t magic = magic_v;
         const float off = f16_act(FMT) ? 1024.f : 128.f;
         const u4_t w2 = st.b2[nb];
         f4_t Ph[MB], Pl[MB];
@@ -327,7 +330,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
         // one E8M0 scale per MFMA step (32 k): per step P against the offset
         // codes OFF + (v + 8) and s_t (P - (OFF + 8) rowsum_t), s_t =
         // 2^(X_t - 127) times the element's implicit 2^-2
-        const uint32_t magic = f16_act(FMT) ? 0x64006400u : 0x43004300u;
+        const uint32_t magic = magic_v;
         const float cz = (f16_act(FMT) ? 1024.f : 128.f) + 8.f;
         const uint32_t xw = st.sraw[nb];
 #pragma unroll
@@ -343,21 +346,14 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
           }
         }
       } else if constexpr (FI::kAct16) {
-        const uint32_t magic = f16_act(FMT) ? 0x64006400u : 0x43004300u;
+        const uint32_t magic = magic_v;
         const float off = f16_act(FMT) ? 1024.f : 128.f;
         f4_t P[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) P[mb] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          u4_t bop;
-          if constexpr (FI::kW2) {
-            bop = w2_operand(w[t >> 1], magic, t & 1);
-          } else {
-            const uint32_t x = w[t];
-            bop = u4_t{(x & 0x000F000Fu) | magic, ((x >> 4) & 0x000F000Fu) | magic, ((x >> 8) & 0x000F000Fu) | magic,
-                       ((x >> 12) & 0x000F000Fu) | magic};
-          }
+          const u4_t bop = FI::kW2 ? w2_operand(w[t >> 1], magic, t & 1) : w16_operand(w[t], magic);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) P[mb] = mfma16<FMT>(st.a[mb][t], bop, P[mb]);
         }

@@ -145,6 +145,9 @@ __global__ void __launch_bounds__(256) qgemm_smallk(SkinnyArgs p) {
       st.z[g] = zsrc[rec * 2 + (c >> 3)];
     }
   };
+  // the 16-bit operands' exponent pattern in a VGPR: one v_and_or_b32 per
+  // unpacked register (mask literal, magic register)
+  [[maybe_unused]] const uint32_t magic_v = opaque_vgpr((FMT == FMT_W16F16) ? 0x64006400u : 0x43004300u);
   auto compute = [&](auto L_c, const St& st, int cb) {
     constexpr int L = decltype(L_c)::value;  // live m-blocks
     f4_t acc[L];
@@ -156,7 +159,7 @@ __global__ void __launch_bounds__(256) qgemm_smallk(SkinnyArgs p) {
       const float s = p.scale_bf16 ? bf16_bits_to_float(sb) : f16_bits_to_float(sb);
       const uint32_t z = p.zp_fixed < 0 ? (st.z[g] >> (4 * (c & 7))) & 0xFu : (uint32_t)p.zp_fixed;
       if constexpr (ACT16) {
-        const uint32_t magic = (FMT == FMT_W16F16) ? 0x64006400u : 0x43004300u;
+        const uint32_t magic = magic_v;
         const float cz = ((FMT == FMT_W16F16) ? 1024.f : 128.f) + (float)z;
         f4_t P[L];
 #pragma unroll
