@@ -871,6 +871,27 @@ hq_status hq_moe_align(int64_t t, int topk, int num_experts, int block_m, const 
   }
 }
 
+// Columns of N per small-K down launch.  Each launch stores its slots'
+// weighted fp32 rows (t * topk * cols * 4 bytes) and the combine of the same
+// columns reads them back, so the window bounds the workspace.  Windows cost
+// time: each launch re-loads every block's activations and row sums (measured
+// on MI355X at t = 4096, N = 7168: seven 1024-column windows took the down +
+// combine from 640 to 870 us although the combine's reads then hit the last-
+// level cache), so a window covers all of N up to 1 GiB of rows.  Equal
+// windows, each a multiple of 64 columns.
+static constexpr int64_t kCombineWindowBytes = int64_t(1) << 30;
+
+static int64_t moe_down_cols(const hq_plan* p, int64_t t, int topk, int bm) {
+  const int64_t N = p->layer.n;
+  if (!moe_uses_smallk(p, bm) || t * topk <= 0) return N;
+  int64_t c = kCombineWindowBytes / (t * topk * 4) / 64 * 64;
+  if (c >= N) return N;
+  c = std::max<int64_t>(c, 64);
+  const int64_t n = cdiv(N, c);
+  c = cdiv(cdiv(N, n), 64) * 64;
+  return std::min(c, N);
+}
+
 struct MoeWs {
   size_t act32, rows, total;
 };
@@ -879,7 +900,8 @@ static MoeWs moe_ws(const hq_plan* p, int64_t t, int topk) {
   MoeWs w{};
   const int64_t mp = moe_max_padded(t, topk, p->layer.num_experts, moe_choice(p, t, topk).bm);
   if (p->compute.epi == HQ_EPI_SILU_MUL_QFP8) w.act32 = align256((size_t)mp * (size_t)(p->layer.n / 2) * 4);
-  if (p->compute.epi == HQ_EPI_TOPK_COMBINE) w.rows = align256((size_t)t * topk * (size_t)p->layer.n * 4);
+  if (p->compute.epi == HQ_EPI_TOPK_COMBINE)
+    w.rows = align256((size_t)t * topk * (size_t)moe_down_cols(p, t, topk, moe_choice(p, t, topk).bm) * 4);
   w.total = w.act32 + w.rows;
   return w;
 }
@@ -988,7 +1010,22 @@ hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, cons
       s.s_expert = (int64_t)(N * G);
       s.z_expert = (int64_t)((N / 16) * G * 2);
       s.f32_out = f32_out;
-      err = hq::launch_smallk_grouped(p->fmt, bm / 16, s, blocks, stream);
+      // column windows: down GEMM, then the combine of the same columns
+      const int64_t cols = moe_down_cols(p, t, topk, bm);
+      err = hipSuccess;
+      for (int64_t c0 = 0; c0 < N && err == hipSuccess; c0 += cols) {
+        const int64_t nc = std::min(cols, N - c0);
+        s.col0 = (int)c0;
+        s.ncol = (int)nc;
+        hq::arm_timing({c0 == 0 ? ev.start : nullptr, nullptr});
+        err = hq::launch_smallk_grouped(p->fmt, bm / 16, s, blocks, stream);
+        if (err != hipSuccess) break;
+        hq::arm_timing({nullptr, c0 + nc >= N ? ev.stop : nullptr});
+        err = hq::launch_moe_combine(f32_out, topk, t, N, c0, nc, out, p->layer.q.out == HQ_BF16, stream);
+      }
+      hq::arm_timing({nullptr, nullptr});
+      if (err != hipSuccess) return fail(HQ_ERR_HIP, "grouped gemm launch: %s", hipGetErrorString((hipError_t)err));
+      return ok();
     } else if (mc.tiled) {
       hq::TiledArgs s{};
       s.a = a;
@@ -1055,7 +1092,7 @@ hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, cons
                                    std::min<int64_t>(mp, (int64_t)bm * t * topk), static_cast<uint8_t*>(out),
                                    out_scale, stream);
     if (err == hipSuccess && epi == HQ_EPI_TOPK_COMBINE)
-      err = hq::launch_moe_combine(f32_out, topk, t, N, out, p->layer.q.out == HQ_BF16, stream);
+      err = hq::launch_moe_combine(f32_out, topk, t, N, 0, N, out, p->layer.q.out == HQ_BF16, stream);
     hq::arm_timing({nullptr, nullptr});
     if (err != hipSuccess) return fail(HQ_ERR_HIP, "grouped gemm launch: %s", hipGetErrorString((hipError_t)err));
     return ok();

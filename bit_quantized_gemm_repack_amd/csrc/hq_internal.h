@@ -391,6 +391,9 @@ struct SkinnyArgs {
   int64_t z_expert;             // zero-point words per expert
   int64_t e8_expert;            // E8M0 bytes per expert
   float* f32_out;               // gate_up fp32 act (QFP8) or down weighted slot rows [n_slots][N]
+  // small-K down GEMM: this launch covers columns [col0, col0 + ncol) of N
+  // and stores slot rows [n_slots][ncol] (0, 0: all of N)
+  int col0, ncol;
 };
 
 // Grouped epilogues (SkinnyArgs::epi / TiledArgs::epi).
@@ -413,7 +416,10 @@ int launch_moe_align(int64_t t, int topk, int num_experts, int block_m, const in
 int launch_moe_requant(const float* act32, const int32_t* sorted_ids, const int32_t* num_padded, int n_slots,
                        int inter, int64_t max_rows, uint8_t* codes, float* scales, void* stream);
 // y[t][n] = RNE(sum over the token's topk weighted slot rows), rows [t*topk][n] fp32
-int launch_moe_combine(const float* rows, int topk, int64_t t, int64_t n, void* y, int out_bf16, void* stream);
+// y[t][col0 + c] = RNE(sum over the token's topk weighted slot rows), rows
+// [t*topk][ncol] fp32 (summed in slot order), c < ncol; y row stride n.
+int launch_moe_combine(const float* rows, int topk, int64_t t, int64_t n, int64_t col0, int64_t ncol, void* y,
+                       int out_bf16, void* stream);
 
 struct TiledArgs {
   const void* a;

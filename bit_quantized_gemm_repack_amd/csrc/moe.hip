@@ -35,9 +35,18 @@ __global__ void __launch_bounds__(1024) moe_align_kernel(const int32_t* __restri
     cur[e] = 0;
   }
   __syncthreads();
-  for (int i = tid; i < n_slots; i += blockDim.x) {
-    const int e = ids[i];
-    atomicAdd(&cnt[(e >= 0 && e < E) ? e : E], 1);
+  // ids are read in batches of kBatch per thread, all loads of a batch in
+  // flight before its LDS atomics (one load per iteration would wait a full
+  // memory latency per id)
+  constexpr int kBatch = 8;
+  const int nt = blockDim.x;
+  for (int base = tid; base < n_slots; base += kBatch * nt) {
+    int ev[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) ev[u] = base + u * nt < n_slots ? ids[base + u * nt] : 0;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (base + u * nt < n_slots) atomicAdd(&cnt[(ev[u] >= 0 && ev[u] < E) ? ev[u] : E], 1);
   }
   __syncthreads();
   // padded sizes, then an inclusive scan over the segments by the first wave
@@ -77,11 +86,17 @@ __global__ void __launch_bounds__(1024) moe_align_kernel(const int32_t* __restri
     block_expert[b] = lo < E ? lo : -1;
   }
   __syncthreads();  // sentinel fill (global) before the scatter in this workgroup
-  for (int i = tid; i < n_slots; i += blockDim.x) {
-    const int e0 = ids[i];
-    const int e = (e0 >= 0 && e0 < E) ? e0 : E;
-    const int pos = off[e] + atomicAdd(&cur[e], 1);
-    sorted_ids[pos] = i;
+  for (int base = tid; base < n_slots; base += kBatch * nt) {
+    int ev[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) ev[u] = base + u * nt < n_slots ? ids[base + u * nt] : 0;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (base + u * nt >= n_slots) continue;
+      const int e = (ev[u] >= 0 && ev[u] < E) ? ev[u] : E;
+      const int pos = off[e] + atomicAdd(&cur[e], 1);
+      sorted_ids[pos] = base + u * nt;
+    }
   }
 }
 
@@ -110,17 +125,19 @@ __global__ void __launch_bounds__(256) moe_requant_kernel(const float* __restric
   if (lane == 0) scales[row] = s;
 }
 
-// The combine: y[t, n] = RNE(sum_j rows[t * topk + j][n]) over the token's
-// topk slot rows (each already weighted), summed in slot order; four outputs
-// per thread (n is a multiple of 64).
+// The combine: y[t, col0 + c] = RNE(sum_j rows[t * topk + j][c]) over the
+// token's topk slot rows (each already weighted; rows of ncol columns, the
+// down GEMM's column window), summed in slot order; four outputs per thread
+// (ncol and col0 are multiples of 4).
 __global__ void __launch_bounds__(256) moe_combine_kernel(const float4* __restrict__ rows, int topk, int64_t n4,
-                                                          int64_t elems4, uint2* __restrict__ y, int out_bf16) {
+                                                          int64_t col04, int64_t ncol4, int64_t elems4,
+                                                          uint2* __restrict__ y, int out_bf16) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < elems4; i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = i / n4, c = i - t * n4;
-    const float4* r = rows + t * topk * n4 + c;
+    const int64_t t = i / ncol4, c = i - t * ncol4;
+    const float4* r = rows + t * topk * ncol4 + c;
     float4 v = r[0];
     for (int j = 1; j < topk; ++j) {
-      const float4 w = r[(int64_t)j * n4];
+      const float4 w = r[(int64_t)j * ncol4];
       v.x += w.x;
       v.y += w.y;
       v.z += w.z;
@@ -130,7 +147,7 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(const float4* __restri
     const uint32_t h1 = out_bf16 ? float_to_bf16_bits(v.y) : float_to_f16_bits(v.y);
     const uint32_t h2 = out_bf16 ? float_to_bf16_bits(v.z) : float_to_f16_bits(v.z);
     const uint32_t h3 = out_bf16 ? float_to_bf16_bits(v.w) : float_to_f16_bits(v.w);
-    y[i] = uint2{h0 | (h1 << 16), h2 | (h3 << 16)};
+    y[t * n4 + col04 + c] = uint2{h0 | (h1 << 16), h2 | (h3 << 16)};
   }
 }
 
@@ -149,14 +166,16 @@ int launch_moe_requant(const float* act32, const int32_t* sorted_ids, const int3
                            codes, scales);
 }
 
-int launch_moe_combine(const float* rows, int topk, int64_t t, int64_t n, void* y, int out_bf16, void* stream) {
-  const int64_t elems4 = t * n / 4;
+int launch_moe_combine(const float* rows, int topk, int64_t t, int64_t n, int64_t col0, int64_t ncol, void* y,
+                       int out_bf16, void* stream) {
+  if (n % 4 || col0 % 4 || ncol % 4 || col0 < 0 || col0 + ncol > n) return (int)hipErrorInvalidValue;
+  const int64_t elems4 = t * ncol / 4;
   int64_t blocks = (elems4 + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;
   return (int)launch_timed(moe_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
-                           reinterpret_cast<const float4*>(rows), topk, n / 4, elems4, static_cast<uint2*>(y),
-                           out_bf16);
+                           reinterpret_cast<const float4*>(rows), topk, n / 4, col0 / 4, ncol / 4, elems4,
+                           static_cast<uint2*>(y), out_bf16);
 }
 
 }  // namespace hq

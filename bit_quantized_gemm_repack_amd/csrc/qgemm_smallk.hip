@@ -35,13 +35,17 @@ __global__ void __launch_bounds__(256) qgemm_smallk(SkinnyArgs p) {
   constexpr bool ACT16 = (FMT == FMT_W16F16 || FMT == FMT_W16BF16);
   constexpr int AV = ACT16 ? 4 * G : 2 * G;  // 16-byte activation operands per m-block
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar column offsets
   const int c = lane & 15;
   const int kq = lane >> 4;
   const int b = blockIdx.y;
   const int m0 = b * 16 * MB;
   if (m0 >= *p.num_padded) return;
-  const int nblocks = p.N / 16;
+  // this launch's column window: blocks [cbase, cbase + nblocks) of N; slot
+  // rows are stored window-local, [n_slots][ncol]
+  const int ncol = p.ncol ? p.ncol : p.N;
+  const int cbase = p.col0 / 16;
+  const int nblocks = ncol / 16;
   const int per_chunk = (nblocks + gridDim.x - 1) / gridDim.x;
   const int cb0 = blockIdx.x * per_chunk;
   const int cb1 = min(nblocks, cb0 + per_chunk);
@@ -52,7 +56,7 @@ __global__ void __launch_bounds__(256) qgemm_smallk(SkinnyArgs p) {
     for (int e = threadIdx.x; e < 16 * MB * (cb1 - cb0) * 16; e += blockDim.x) {
       const int r = e / ((cb1 - cb0) * 16), cc = e - r * ((cb1 - cb0) * 16);
       const int id = p.sorted_ids[m0 + r];
-      if (id < p.n_slots) p.f32_out[(int64_t)id * p.N + cb0 * 16 + cc] = 0.f;
+      if (id < p.n_slots) p.f32_out[(int64_t)id * ncol + cb0 * 16 + cc] = 0.f;
     }
     return;
   }
@@ -61,9 +65,14 @@ __global__ void __launch_bounds__(256) qgemm_smallk(SkinnyArgs p) {
   const uint32_t* zsrc = p.zeros ? p.zeros + ex * p.z_expert : reinterpret_cast<const uint32_t*>(scales16);
   const int K = p.K;
 
-  // output rows of this lane: slot ids and weights (topk_w times the row scale)
+  // output rows of this lane: slot ids, weights (topk_w times the row scale)
+  // and the byte offset of (row, column c) in the window's slot rows; a
+  // padding row gets an offset past the buffer range, so its stores are
+  // dropped by the range check instead of a branch.  The rows of one window
+  // stay below 2 GiB (the host caps a window at 1 GiB).
   int oid[MB][4];
   float of[MB][4];
+  int ooff[MB][4];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -72,7 +81,10 @@ __global__ void __launch_bounds__(256) qgemm_smallk(SkinnyArgs p) {
       const int id = p.sorted_ids[m];
       oid[mb][r] = id;
       of[mb][r] = id < p.n_slots ? p.topk_w[id] * (ACT16 ? 1.f : p.a_scale[m]) : 0.f;
+      ooff[mb][r] = id < p.n_slots ? (id * ncol + c) * 4 : INT32_MIN;
     }
+  const auto rout = __builtin_amdgcn_make_buffer_rsrc(p.f32_out, (short)0, (int)((int64_t)p.n_slots * ncol * 4),
+                                                      0x00020000);
   // m-blocks up to the last one that holds a slot (an expert's slots come
   // first in its aligned segment, so a block's padding rows usually fill its
   // last m-blocks): the others need no operands, products or stores
@@ -135,12 +147,13 @@ __global__ void __launch_bounds__(256) qgemm_smallk(SkinnyArgs p) {
     uint32_t z[G];
   };
   auto cb_of = [&](int i) { return i < n_my ? cb0 + wave + 4 * i : cb_last; };
-  auto load = [&](St& st, int cb) {
+  auto load = [&](St& st, int cbl) {
+    const int64_t cb = cbase + cbl;  // column block of N
 #pragma unroll
-    for (int g = 0; g < G; ++g) st.w[g] = __builtin_nontemporal_load(wfr + ((int64_t)cb * G + g) * 64 + lane);
+    for (int g = 0; g < G; ++g) st.w[g] = __builtin_nontemporal_load(wfr + (cb * G + g) * 64 + lane);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int64_t rec = (int64_t)cb * G + g;
+      const int64_t rec = cb * G + g;
       st.s[g] = reinterpret_cast<const uint32_t*>(scales16)[(rec * 16 + c) >> 1];
       st.z[g] = zsrc[rec * 2 + (c >> 3)];
     }
@@ -187,12 +200,12 @@ __global__ void __launch_bounds__(256) qgemm_smallk(SkinnyArgs p) {
         }
       }
     }
-    const int n = cb * 16 + c;
+    // column block cb of the window: a scalar byte offset on every row
 #pragma unroll
     for (int mb = 0; mb < L; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (oid[mb][r] < p.n_slots) p.f32_out[(int64_t)oid[mb][r] * p.N + n] = acc[mb][r] * of[mb][r];
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[mb][r] * of[mb][r]), rout, ooff[mb][r], cb * 64, 0);
   };
   auto run = [&](auto L_c) {
     St st[D];
@@ -237,11 +250,14 @@ bool smallk_supported(int fmt, int mb, int G) {
 }
 
 int launch_smallk_grouped(int fmt, int mb, const SkinnyArgs& a, int64_t blocks, void* stream) {
-  if (!smallk_supported(fmt, mb, a.G) || a.epi != GEPI_COMBINE || a.N % 16 || a.K != 128 * a.G)
+  const int ncol = a.ncol ? a.ncol : a.N;
+  if (!smallk_supported(fmt, mb, a.G) || a.epi != GEPI_COMBINE || a.N % 16 || a.K != 128 * a.G || ncol % 16 ||
+      a.col0 % 16 || a.col0 < 0 || a.col0 + ncol > a.N)
     return (int)hipErrorInvalidValue;
-  // column chunks: about 2048 workgroups in all, at least one column block per wave
-  const int64_t nblocks = a.N / 16;
-  int64_t chunks = (2048 + blocks - 1) / blocks;
+  // column chunks of the window: about 1024 workgroups per launch, at least
+  // one column block per wave
+  const int64_t nblocks = ncol / 16;
+  int64_t chunks = (1024 + blocks - 1) / blocks;
   chunks = std::max<int64_t>(1, std::min<int64_t>(chunks, nblocks / 4));
   const dim3 grid((unsigned)chunks, (unsigned)blocks);
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -50,6 +50,17 @@ def test_align_out_of_range_ids():
         om.check_align(ids, 4, bm, sid.cpu().numpy(), bexp.cpu().numpy(), npad.cpu().numpy())
 
 
+def test_align_extreme_ids():
+    _log("moe align extreme ids")
+    # any id outside [0, E) belongs to the trailing segment, including the
+    # int32 extremes
+    ids = np.array([[0, np.iinfo(np.int32).min], [3, np.iinfo(np.int32).max], [2, -1]] * 50, dtype=np.int32)
+    for bm in (16, 64):
+        sid, bexp, npad = hq.moe_align(torch.from_numpy(ids).to(DEV), 4, bm)
+        torch.cuda.synchronize()
+        om.check_align(ids, 4, bm, sid.cpu().numpy(), bexp.cpu().numpy(), npad.cpu().numpy())
+
+
 def test_align_degenerate_cases():
     _log("moe align degenerate")
     # every slot on one expert; one expert only; block of 64
@@ -73,15 +84,15 @@ class Layer:
     """Weights on the GPU (repacked for both activation types) + host copies.
     `tuning` (same for both GEMMs) forces a kernel / block size."""
 
-    def __init__(self, E, H, I, key, tuning=None):
+    def __init__(self, E, H, I, key, tuning=None, max_t=4096):
         self.E, self.H, self.I = E, H, I
         wts = datagen.moe_weights(E, H, I, key=key)
         self.w = wts
         self.dev = {}
         for act in ("bf16", "fp8"):
-            p1 = hq.MoePlan(2 * I, H, _quant(act), E, 4096, "silu_mul" if act == "bf16" else "silu_mul_qfp8",
+            p1 = hq.MoePlan(2 * I, H, _quant(act), E, max_t, "silu_mul" if act == "bf16" else "silu_mul_qfp8",
                             tuning=tuning)
-            p2 = hq.MoePlan(H, I, _quant(act), E, 4096, "topk_combine", tuning=tuning)
+            p2 = hq.MoePlan(H, I, _quant(act), E, max_t, "topk_combine", tuning=tuning)
             w1, m1 = p1.repack(torch.from_numpy(wts["w1"]).to(DEV), wts["s1"].to(DEV))
             w2, m2 = p2.repack(torch.from_numpy(wts["w2"]).to(DEV), wts["s2"].to(DEV))
             self.dev[act] = (p1, p2, w1, m1, w2, m2)
@@ -240,6 +251,15 @@ def test_fp8_requant_with_fewer_tokens_than_the_call_before(small_layer, small_l
     lay = small_layer_tiled if tiled else small_layer
     for T, topk in ((400, 3), (5, 8), (1, 2), (64, 2)):
         run_layer(lay, T, "fp8", topk, key=(29,))
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp8"])
+def test_small_layer_many_slots_column_windows(act):
+    # 524288 routed slots of 1024 columns: the down GEMM and the combine run
+    # in two column windows (the weighted slot rows of one window stay within
+    # 1 GiB of workspace), checked on sampled tokens
+    lay = Layer(8, 1024, 128, key=(31,), max_t=65536, tuning=dict(tile_m=64))
+    run_layer(lay, 65536, act, 8, key=(37,), sample=24)
 
 
 @pytest.fixture(scope="module")
