@@ -36,6 +36,9 @@ ASCALE_NONE, ASCALE_PER_TOKEN_F32, ASCALE_MX_E8M0 = range(3)
 GEMM_DENSE, GEMM_GROUPED = range(2)
 EPI_NONE, EPI_SILU_MUL, EPI_SILU_MUL_QFP8, EPI_TOPK_COMBINE, EPI_I32_ACC = range(5)
 PEAK_F16, PEAK_BF16, PEAK_FP8, PEAK_FP8_FP4, PEAK_FP4, PEAK_INT8 = range(6)
+MFMA_AUTO, MFMA_F16, MFMA_BF16, MFMA_FP8, MFMA_INT8, MFMA_FP8_FP4, MFMA_FP4 = range(7)
+_MFMA = {None: MFMA_AUTO, "auto": MFMA_AUTO, "f16": MFMA_F16, "bf16": MFMA_BF16, "fp8": MFMA_FP8,
+         "int8": MFMA_INT8, "fp8xfp4": MFMA_FP8_FP4, "fp4": MFMA_FP4}
 
 _DT = {"f16": F16, "bf16": BF16, "fp8": FP8_E4M3, "int8": INT8}
 _EPI = {"none": EPI_NONE, "silu_mul": EPI_SILU_MUL, "silu_mul_qfp8": EPI_SILU_MUL_QFP8,
@@ -67,7 +70,7 @@ class LayerDesc(ctypes.Structure):
 
 
 class Compute(ctypes.Structure):
-    _fields_ = [("kind", ctypes.c_int), ("epi", ctypes.c_int)]
+    _fields_ = [("kind", ctypes.c_int), ("epi", ctypes.c_int), ("mfma_in", ctypes.c_int)]
 
 
 class Tuning(ctypes.Structure):
@@ -243,28 +246,69 @@ def _stream_ptr(device) -> int:
 
 
 _TORCH_OUT = {F16: torch.float16, BF16: torch.bfloat16}
+_DT_NAME = {F16: "f16", BF16: "bf16", FP8_E4M3: "fp8", INT8: "int8", FP4_E2M1: "mxfp4"}
 
 
 # ------------------------------------------------------------------ plan --
+def _as16(q: QuantDesc) -> QuantDesc:
+    """The same weights with 16-bit activations (the output dtype's type)."""
+    act = q.out if q.out in (F16, BF16) else BF16
+    return QuantDesc(q.w_elem, q.w_bits, q.group_size, q.scale, q.zp, q.zp_value, act, ASCALE_NONE, q.out)
+
+
 class Plan:
-    """A layer description + execution choice (owns an hq_plan)."""
+    """A layer description + execution choice (owns an hq_plan).
+
+    mfma_in names the matrix-instruction operand type ('f16', 'bf16', 'fp8',
+    'int8', 'fp8xfp4', 'fp4'; None: the description's).  When the library
+    cannot run the description (HQ_ERR_UNSUPPORTED) and its activations are 8-
+    or 4-bit, the plan is built again for the same weights with 16-bit
+    activations -- the pages' fallback to a higher-precision compute type
+    (Humming page on news.ditty.ir, summary) -- unless fallback=False.  Then
+    `fallback` holds the reason, `quant` the description that runs and
+    `requested_quant` the one asked for; `linear` takes 16-bit activations
+    either way."""
 
     def __init__(self, n: int, k: int, quant: QuantDesc, max_m: int, epi: str = "none",
-                 kind: str = "dense", num_experts: int = 1, tuning: Optional[dict] = None):
+                 kind: str = "dense", num_experts: int = 1, tuning: Optional[dict] = None,
+                 mfma_in: Optional[str] = None, fallback: bool = True):
         L = lib()
         self.n, self.k, self.max_m, self.num_experts = int(n), int(k), int(max_m), int(num_experts)
+        self.requested_quant = quant
         self.quant = quant
+        self.fallback = None
         self.epi = _EPI[epi]
-        layer = LayerDesc(self.n, self.k, self.num_experts, quant)
-        comp = Compute(GEMM_DENSE if kind == "dense" else GEMM_GROUPED, self.epi)
+        if mfma_in not in _MFMA:
+            raise ValueError(f"mfma_in must be one of {sorted(k for k in _MFMA if k)}")
         tun = None
         if tuning:
             tun = Tuning(**{key: int(v) for key, v in tuning.items()})
-        handle = ctypes.c_void_p()
-        _check(L.hq_plan_create(ctypes.byref(layer), ctypes.byref(comp), self.max_m,
-                                ctypes.byref(tun) if tun is not None else None, ctypes.byref(handle)))
+
+        def create(q, mi):
+            layer = LayerDesc(self.n, self.k, self.num_experts, q)
+            comp = Compute(GEMM_DENSE if kind == "dense" else GEMM_GROUPED, self.epi, mi)
+            h = ctypes.c_void_p()
+            _check(L.hq_plan_create(ctypes.byref(layer), ctypes.byref(comp), self.max_m,
+                                    ctypes.byref(tun) if tun is not None else None, ctypes.byref(h)))
+            return h
+
+        try:
+            handle = create(quant, _MFMA[mfma_in])
+        except HQError as e:
+            if not fallback or e.status != HQ_ERR_UNSUPPORTED or quant.act in (F16, BF16) or \
+                    self.epi == EPI_I32_ACC:
+                raise
+            q16 = _as16(quant)
+            try:
+                handle = create(q16, MFMA_AUTO)
+            except HQError:
+                raise e from None
+            self.quant = q16
+            self.fallback = (f"{_DT_NAME.get(quant.act, quant.act)} activations requested: {e}; running "
+                             f"{_DT_NAME[q16.act]} activations")
         self._h = handle
         self._ws = {}
+        self._act_buf = {}
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -286,7 +330,8 @@ class Plan:
     def describe(self, m: int) -> str:
         buf = ctypes.create_string_buffer(512)
         _check(lib().hq_plan_describe(self._h, int(m), buf, 512))
-        return buf.value.decode()
+        d = buf.value.decode()
+        return d if self.fallback is None else f"{d} fallback=16-bit-activations ({self.fallback})"
 
     def workspace(self, m: int, device) -> Optional[torch.Tensor]:
         """A zero-initialised workspace kept per device (reused across calls;
@@ -363,6 +408,40 @@ class Plan:
                              ws_bytes, _stream_ptr(a.device)))
         return out
 
+
+    def linear(self, x: torch.Tensor, w: torch.Tensor, meta: torch.Tensor, out: Optional[torch.Tensor] = None,
+               ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """out = x . W_deq^T for 16-bit activations x [m, k]: a plan that runs
+        8-bit activations quantises x per token first (hq_quantize_per_token:
+        fp8 e4m3 or int8), one that runs MXFP4 activations block-quantises it
+        (hq_quantize_mxfp4), a 16-bit plan -- including one that fell back --
+        multiplies x as it is.  Every step is a library kernel on x's stream;
+        the activation codes live in a buffer kept per device and m."""
+        _dev(x, "x")
+        if x.dtype not in (torch.float16, torch.bfloat16) or x.dim() != 2 or x.shape[1] != self.k:
+            raise ValueError(f"x must be fp16 / bf16 [m, {self.k}]")
+        q = self.quant
+        if q.act in (F16, BF16):
+            if x.dtype != _TORCH_OUT[q.act]:
+                raise ValueError(f"this plan multiplies {_DT_NAME[q.act]} activations")
+            return self.gemm(x, w, meta, out=out, ws=ws)
+        m = x.shape[0]
+        key = (x.device, m)
+        buf = self._act_buf.get(key)
+        if q.act == FP4_E2M1:
+            if buf is None:
+                buf = (torch.empty((m, self.k // 2), dtype=torch.uint8, device=x.device),
+                       torch.empty((self.k // 128, m, 4), dtype=torch.uint8, device=x.device))
+                self._act_buf[key] = buf
+            codes, sc = quantize_mxfp4(x, codes=buf[0], e8m0=buf[1])
+        else:
+            kind = "fp8" if q.act == FP8_E4M3 else "int8"
+            if buf is None:
+                buf = (torch.empty((m, self.k), dtype=torch.uint8 if kind == "fp8" else torch.int8, device=x.device),
+                       torch.empty(m, dtype=torch.float32, device=x.device))
+                self._act_buf[key] = buf
+            codes, sc = quantize_per_token(x, kind, codes=buf[0], scales=buf[1])
+        return self.gemm(codes, w, meta, a_scale=sc, out=out, ws=ws)
 
     # -- measured execution choices --------------------------------------
     def autotune(self, a: torch.Tensor, w: torch.Tensor, meta: torch.Tensor, a_scale: Optional[torch.Tensor] = None,
@@ -546,8 +625,9 @@ class MoePlan(Plan):
     'silu_mul_qfp8' (gate_up), 'topk_combine' (down) or 'none'."""
 
     def __init__(self, n: int, k: int, quant: QuantDesc, num_experts: int, max_t: int, epi: str,
-                 tuning: Optional[dict] = None):
-        super().__init__(n, k, quant, max_m=max_t, epi=epi, kind="grouped", num_experts=num_experts, tuning=tuning)
+                 tuning: Optional[dict] = None, mfma_in: Optional[str] = None, fallback: bool = False):
+        super().__init__(n, k, quant, max_m=max_t, epi=epi, kind="grouped", num_experts=num_experts, tuning=tuning,
+                         mfma_in=mfma_in, fallback=fallback)
 
     def describe(self, t: int, topk: int = 1) -> str:
         """The kernel a grouped call with t tokens of topk slots launches."""

@@ -167,6 +167,30 @@ const char* fmt_name(int fmt) {
   return "?";
 }
 
+// The matrix-instruction operand type a kernel format runs on.
+hq_mfma_in implied_mfma(int fmt) {
+  switch (fmt) {
+    case hq::FMT_I8: return HQ_MFMA_INT8;
+    case hq::FMT_Q8: return HQ_MFMA_FP8;
+    case hq::FMT_F4: return HQ_MFMA_FP8_FP4;
+    case hq::FMT_F44: return HQ_MFMA_FP4;
+  }
+  return hq::f16_act(fmt) ? HQ_MFMA_F16 : HQ_MFMA_BF16;
+}
+
+const char* mfma_name(hq_mfma_in t) {
+  switch (t) {
+    case HQ_MFMA_AUTO: return "auto";
+    case HQ_MFMA_F16: return "f16";
+    case HQ_MFMA_BF16: return "bf16";
+    case HQ_MFMA_FP8: return "fp8";
+    case HQ_MFMA_INT8: return "int8";
+    case HQ_MFMA_FP8_FP4: return "fp8xfp4";
+    case HQ_MFMA_FP4: return "fp4";
+  }
+  return "?";
+}
+
 bool valid_pow(int v) { return v == 1 || v == 2 || v == 4; }
 
 }  // namespace
@@ -406,6 +430,11 @@ hq_status hq_plan_create(const hq_layer_desc* layer, const hq_compute* compute, 
     int fmt = 0;
     hq_status s = classify(layer->q, &fmt);
     if (s != HQ_OK) return s;
+    if (compute->mfma_in < HQ_MFMA_AUTO || compute->mfma_in > HQ_MFMA_FP4)
+      return fail(HQ_ERR_INVALID_ARG, "unknown matrix-instruction type %d", (int)compute->mfma_in);
+    if (compute->mfma_in != HQ_MFMA_AUTO && compute->mfma_in != implied_mfma(fmt))
+      return fail(HQ_ERR_UNSUPPORTED, "%s runs on the %s matrix instruction, not %s", fmt_name(fmt),
+                  mfma_name(implied_mfma(fmt)), mfma_name(compute->mfma_in));
     switch (compute->epi) {
       case HQ_EPI_NONE: break;
       case HQ_EPI_I32_ACC:
@@ -488,17 +517,19 @@ hq_status hq_plan_describe(const hq_plan* p, int64_t m, char* buf, size_t len) {
   hq::Exec e = hq::choose_exec(p, m);
   if (e.kernel == hq::KER_TILED) {
     snprintf(buf, len,
-             "kernel=tiled fmt=%s m=%lld n=%lld k=%lld tile_m=%d tile_n=%d waves=4 split_k=%d grid=%lldx%d ws=%zu",
-             fmt_name(p->fmt), (long long)m, (long long)p->layer.n, (long long)p->layer.k, e.tl.bm, 64 * e.tl.nbw,
-             e.tl.split, (long long)(e.tiles_m * e.tiles_n), e.tl.split, e.ws_bytes);
+             "kernel=tiled fmt=%s mfma=%s m=%lld n=%lld k=%lld tile_m=%d tile_n=%d waves=4 split_k=%d grid=%lldx%d "
+             "ws=%zu",
+             fmt_name(p->fmt), mfma_name(implied_mfma(p->fmt)), (long long)m, (long long)p->layer.n,
+             (long long)p->layer.k, e.tl.bm, 64 * e.tl.nbw, e.tl.split, (long long)(e.tiles_m * e.tiles_n), e.tl.split,
+             e.ws_bytes);
     return ok();
   }
   snprintf(buf, len,
-           "kernel=skinny fmt=%s m=%lld n=%lld k=%lld tile_m=%d tile_n=%d waves=%d split_k=%d stages=%d "
+           "kernel=skinny fmt=%s mfma=%s m=%lld n=%lld k=%lld tile_m=%d tile_n=%d waves=%d split_k=%d stages=%d "
            "grid=%lldx%dx%lld ws=%zu",
-           fmt_name(p->fmt), (long long)m, (long long)p->layer.n, (long long)p->layer.k, 16 * e.sk.mb,
-           16 * e.sk.nb, e.sk.waves, e.sk.split, e.sk.stages, (long long)e.tiles_n, e.sk.split,
-           (long long)e.tiles_m, e.ws_bytes);
+           fmt_name(p->fmt), mfma_name(implied_mfma(p->fmt)), (long long)m, (long long)p->layer.n,
+           (long long)p->layer.k, 16 * e.sk.mb, 16 * e.sk.nb, e.sk.waves, e.sk.split, e.sk.stages,
+           (long long)e.tiles_n, e.sk.split, (long long)e.tiles_m, e.ws_bytes);
   return ok();
 }
 

@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define HQ_ABI_VERSION 1
+#define HQ_ABI_VERSION 2
 
 typedef enum hq_status {
   HQ_OK = 0,
@@ -175,10 +175,33 @@ typedef enum hq_epilogue {
   HQ_EPI_I32_ACC = 4        /* W4A8-INT debug: per-group int32 accumulators */
 } hq_epilogue;
 
-/* Compute config: which GEMM and which epilogue. */
+/* Operand type of the matrix instruction a plan runs on.  The quantisation
+ * description fixes it (16-bit activations: HQ_MFMA_F16 / HQ_MFMA_BF16;
+ * INT4 x int8: HQ_MFMA_INT8; INT4 x fp8: HQ_MFMA_FP8; MXFP4 x fp8:
+ * HQ_MFMA_FP8_FP4; MXFP4 x MXFP4: HQ_MFMA_FP4); HQ_MFMA_AUTO takes that
+ * type, any other value must name it. */
+typedef enum hq_mfma_in {
+  HQ_MFMA_AUTO = 0,
+  HQ_MFMA_F16 = 1,
+  HQ_MFMA_BF16 = 2,
+  HQ_MFMA_FP8 = 3,
+  HQ_MFMA_INT8 = 4,
+  HQ_MFMA_FP8_FP4 = 5,
+  HQ_MFMA_FP4 = 6
+} hq_mfma_in;
+
+/* Compute config: which GEMM, which epilogue, and the matrix-instruction
+ * operand type (the pages' compute config: the GEMM type a layer runs as,
+ * Humming page on news.ditty.ir, summary).  A request this library cannot
+ * run (an operand type other than the description's, a combination without
+ * a kernel) is HQ_ERR_UNSUPPORTED from hq_plan_create; the pages' answer to
+ * a compute type the GPU lacks is to run the layer at a higher precision
+ * (same page, summary), which the Python binding does by building the plan
+ * again with 16-bit activations. */
 typedef struct hq_compute {
   hq_gemm_kind kind;
   hq_epilogue epi;
+  hq_mfma_in mfma_in;
 } hq_compute;
 
 /* Tuning config (execution choice, kept apart from the description).
@@ -201,7 +224,11 @@ const char* hq_status_str(hq_status s);
 /* Message of the last failed call on this thread ("" if none). */
 const char* hq_last_error(void);
 
-/* Validate a layer + compute description and pick an execution choice.
+/* Validate a layer + compute description and pick an execution choice --
+ * the pages' layer config (shapes, data types), compute config (GEMM type)
+ * and tuning config (tile, pipeline, matrix instruction), the last chosen by
+ * a rule-based heuristic (Humming page on news.ditty.ir, summary; cocoloop.cn,
+ * limits section: tuning is heuristic).
  * max_m bounds the rows (tokens) a later call may pass.  `tuning` may be
  * NULL (heuristic, the rule-based selection the pages describe); non-zero
  * fields override it.  On success *out owns a host object released with
@@ -214,7 +241,10 @@ hq_status hq_plan_destroy(hq_plan* plan);
  * a grouped plan, m is the number of routed slots (t * topk) of a call. */
 hq_status hq_plan_describe(const hq_plan* plan, int64_t m, char* buf, size_t len);
 
-/* Workspace a call with m rows needs, in bytes (0 if none): the fp32 partial
+/* Workspace a call with m rows needs, in bytes (0 if none) -- memory the
+ * execution choice adds to the layer description, kept apart from it as the
+ * pages keep the tuning config apart from the layer config (Humming page on
+ * news.ditty.ir, summary): the fp32 partial
  * tiles [split][m][n] when K is split over workgroups (a second kernel of the
  * same call sums them in split order, so results are deterministic).  Its
  * contents need no initialisation.  Two calls that overlap in time must not
@@ -222,12 +252,16 @@ hq_status hq_plan_describe(const hq_plan* plan, int64_t m, char* buf, size_t len
 hq_status hq_plan_workspace_bytes(const hq_plan* plan, int64_t m, size_t* bytes);
 
 /* Sizes of the repacked (device-layout) weight: w_bytes for the codes,
- * meta_bytes for scales + zero points (or E8M0 scales).  For a grouped
+ * meta_bytes for scales + zero points (or E8M0 scales) -- the weight, scale
+ * and zero point held as separate parameters of the one standard format
+ * (Humming page on news.ditty.ir, summary; aube.news: INT4 stores one weight
+ * in 4 bits).  For a grouped
  * plan both cover all experts. */
 hq_status hq_repacked_bytes(const hq_plan* plan, size_t* w_bytes, size_t* meta_bytes);
 
 /* Offline repack (the format conversion into the library's standard
- * layout): canonical codes / scales / zeros-or-e8m0 (see above; for a
+ * layout that the pages describe for every supported format: Humming page on
+ * news.ditty.ir, summary): canonical codes / scales / zeros-or-e8m0 (see above; for a
  * grouped plan each is stacked [E, ...]) -> the device layout, which places
  * the 4-bit codes in gfx950 MFMA operand order.  All pointers are device
  * pointers; the work is a kernel on `stream`.  `zeros_or_e8m0` is NULL for
@@ -240,7 +274,10 @@ hq_status hq_repack(const hq_plan* plan, const void* codes, const void* scales,
 hq_status hq_repack_host(const hq_plan* plan, const void* codes, const void* scales,
                          const void* zeros_or_e8m0, void* w_out, void* meta_out);
 
-/* Dense GEMM: out[M, N] = A[M, K] . W_deq^T.
+/* Dense GEMM: out[M, N] = A[M, K] . W_deq^T, the weights dequantised inside
+ * the kernel from their packed codes (the mixed-precision GEMM of the pages:
+ * Humming page on news.ditty.ir, summary -- WnA16, W4A8 including MXFP4 x
+ * FP8, W4A4; cocoloop.cn, format section and speed-up table, dense rows).
  *   a        device [m, K] activations (act dtype of the plan)
  *   a_scale  device: fp32 [m] per-row scales for 8-bit activations; for
  *            MXFP4 activations (W4A4; the codes in `a` packed like the

@@ -25,8 +25,10 @@ from oracle.formats import unpack_u4
 from oracle.gemm import unpack_u2, unpack_u3
 
 
-def _plan(n=256, k=512, quant=None, max_m=64, epi="none", tuning=None):
-    return hq.Plan(n, k, quant if quant is not None else hq.w4a16(), max_m=max_m, epi=epi, tuning=tuning)
+def _plan(n=256, k=512, quant=None, max_m=64, epi="none", tuning=None, fallback=False):
+    # the C rejection path: no binding-level fallback unless asked for
+    return hq.Plan(n, k, quant if quant is not None else hq.w4a16(), max_m=max_m, epi=epi, tuning=tuning,
+                   fallback=fallback)
 
 
 def test_library_exports_every_header_function():
@@ -49,7 +51,7 @@ def test_library_has_no_undefined_internal_symbols():
 
 def test_abi_version_and_status_strings():
     L = hq.lib()
-    assert L.hq_abi_version() == 1
+    assert L.hq_abi_version() == 2
     assert L.hq_status_str(0) == b"HQ_OK"
     assert L.hq_status_str(3) == b"HQ_ERR_WORKSPACE"
 
@@ -81,6 +83,57 @@ def test_plan_validation(kw, status):
         _plan(**kw)
     assert e.value.status == status
     assert hq.lib().hq_last_error().decode()
+
+
+NVFP4_FP8 = hq.QuantDesc(hq.FP4_E2M1, 4, 16, hq.FP8_E4M3, hq.ZP_NONE, 0, hq.FP8_E4M3, hq.ASCALE_PER_TOKEN_F32, hq.BF16)
+MXINT4_FP8 = hq.QuantDesc(hq.I4, 4, 32, hq.E8M0, hq.ZP_NONE, 0, hq.FP8_E4M3, hq.ASCALE_PER_TOKEN_F32, hq.BF16)
+INT4U4_I8 = hq.QuantDesc(hq.U4, 4, 128, hq.F16, hq.ZP_PER_GROUP_U4, 0, hq.INT8, hq.ASCALE_PER_TOKEN_F32, hq.F16)
+
+
+def test_mfma_in_must_name_the_descriptions_type():
+    for q, mi in ((hq.w4a16("bf16"), "bf16"), (hq.w4a16("f16"), "f16"), (hq.w4a8_int(), "int8"),
+                  (hq.w4a8_fp8(), "fp8"), (hq.w4a8_mxfp4(), "fp8xfp4"), (hq.w4a4_mxfp4(), "fp4")):
+        p = hq.Plan(4096, 4096, q, max_m=16, mfma_in=mi, fallback=False)
+        assert f"mfma={mi}" in p.describe(16) and p.fallback is None
+        other = "f16" if mi != "f16" else "bf16"
+        with pytest.raises(hq.HQError) as e:
+            hq.Plan(4096, 4096, q, max_m=16, mfma_in=other, fallback=False)
+        assert e.value.status == hq.HQ_ERR_UNSUPPORTED and "matrix instruction" in str(e.value)
+    # an out-of-range value through the C ABI
+    L = hq.lib()
+    layer = hq.LayerDesc(4096, 4096, 1, hq.w4a16())
+    h = ctypes.c_void_p()
+    assert L.hq_plan_create(ctypes.byref(layer), ctypes.byref(hq.Compute(0, 0, 7)), 16, None,
+                            ctypes.byref(h)) == hq.HQ_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("q, runs", [(NVFP4_FP8, "w4a16-nvfp4-bf16"), (MXINT4_FP8, "w4a16-mxint4-bf16"),
+                                     (INT4U4_I8, "w4a16-f16")])
+def test_unsupported_compute_type_falls_back_to_16_bit_activations(q, runs):
+    # the C library rejects the description ...
+    with pytest.raises(hq.HQError) as e:
+        hq.Plan(4096, 4096, q, max_m=64, fallback=False)
+    assert e.value.status == hq.HQ_ERR_UNSUPPORTED
+    # ... and the binding builds the same weights with 16-bit activations
+    p = hq.Plan(4096, 4096, q, max_m=64)
+    assert p.fallback and p.requested_quant is q
+    assert p.quant.act == q.out and p.quant.act_scale == hq.ASCALE_NONE
+    assert (p.quant.w_elem, p.quant.group_size, p.quant.scale, p.quant.zp) == (q.w_elem, q.group_size, q.scale, q.zp)
+    d = p.describe(16)
+    assert f"fmt={runs}" in d and "fallback=16-bit-activations" in d
+    # a requested instruction type the description cannot use falls back too
+    p2 = hq.Plan(4096, 4096, hq.w4a8_int(), max_m=64, mfma_in="fp8")
+    assert p2.fallback and "fmt=w4a16-bf16" in p2.describe(1)
+
+
+def test_fallback_never_hides_other_errors():
+    with pytest.raises(hq.HQError) as e:   # invalid argument: no fallback
+        hq.Plan(250, 4096, hq.w4a8_int(), max_m=64)
+    assert e.value.status == hq.HQ_ERR_UNSUPPORTED and "N must be a multiple" in str(e.value)
+    with pytest.raises(hq.HQError):        # no 16-bit kernel for MXFP4 weights either: the original error
+        hq.Plan(4096, 4096, hq.w4a8_mxfp4(), max_m=64, mfma_in="int8")
+    with pytest.raises(hq.HQError):        # 16-bit activations were asked for: nothing higher to fall to
+        hq.Plan(4096, 4096, hq.w4a16("bf16"), max_m=64, mfma_in="fp8")
 
 
 def test_grouped_epilogue_on_dense_plan_rejected():
