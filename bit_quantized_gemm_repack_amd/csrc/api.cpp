@@ -780,6 +780,33 @@ hq_status hq_gemm(const hq_plan* p, int64_t m, const void* a, const void* a_scal
   }
 }
 
+hq_status hq_gemm_noalloc(const hq_plan* p, int64_t m, const void* a, const void* a_scale, const void* w,
+                          const void* meta, void* out, void* stream) {
+  const hq::TimingEvents ev = hq::take_timing();  // consumed by this call whatever happens
+  try {
+    if (!p) return fail(HQ_ERR_INVALID_ARG, "null plan");
+    if (m == 0 && p->compute.kind == HQ_GEMM_DENSE) return ok();
+    hq_status s = dense_args_check(p, m, a, a_scale, w, meta, out);
+    if (s != HQ_OK) return s;
+    const hq::Exec e = hq::choose_exec(p, m);
+    if (e.ws_bytes > hq::kNoAllocScratchBytes)
+      return fail(HQ_ERR_WORKSPACE,
+                  "this call's split-K partials need %zu bytes, above the %zu-byte library scratch of "
+                  "hq_gemm_noalloc (use hq_gemm with a workspace, or a tuning with a smaller K split)",
+                  e.ws_bytes, hq::kNoAllocScratchBytes);
+    void* scratch = nullptr;
+    if (e.ws_bytes > 0) {
+      const int err = hq::noalloc_scratch(&scratch);
+      if (err != hipSuccess)
+        return fail(HQ_ERR_HIP, "library scratch lookup: %s", hipGetErrorString((hipError_t)err));
+    }
+    return dense_run(p, e, m, a, a_scale, w, meta, out, scratch, e.ws_bytes > 0 ? hq::kNoAllocScratchBytes : 0,
+                     stream, ev);
+  } catch (...) {
+    return fail(HQ_ERR_INTERNAL, "exception in hq_gemm_noalloc");
+  }
+}
+
 // ---------------------------------------------------------------------------
 // grouped (MoE)
 // ---------------------------------------------------------------------------

@@ -457,6 +457,10 @@ int launch_tiled_grouped(int fmt, int mode, const TiledCfgRt& cfg, const TiledAr
                          void* stream);
 // out[i] = round(sum_s part[s * mn + i]) in index order (fp16 / bf16 out).
 int launch_splitk_reduce(const float* part, int splits, int64_t mn, void* out, int out_bf16, void* stream);
+// Size of the library-owned device scratch of hq_gemm_noalloc, and its address
+// on the current device (looked up once per device; a hipError_t).
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+int noalloc_scratch(void** ptr);
 int launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups, void* stream);
 int launch_mfma_peak(int dtype, int workgroups, int iters, uint32_t* sink, void* stream);
 double mfma_peak_flops(int dtype, int workgroups, int iters);

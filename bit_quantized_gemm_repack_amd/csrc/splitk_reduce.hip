@@ -4,6 +4,8 @@
 // needed, and the result does not depend on which workgroup finished first.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "device_common.h"
 #include "hq_internal.h"
 #include "launch.h"
@@ -28,6 +30,39 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float4* __rest
     const uint32_t h3 = out_bf16 ? float_to_bf16_bits(v.w) : float_to_f16_bits(v.w);
     out[i] = uint2{h0 | (h1 << 16), h2 | (h3 << 16)};
   }
+}
+
+// ---------------------------------------------------------------------------
+// Library-owned scratch for hq_gemm_noalloc: the split-K partials of a call
+// that must not allocate live in this file-scope device array (each GPU the
+// library runs on holds its own copy until the process ends).  In host code
+// the name `scratch` is only a host-side stand-in, never a device address:
+// the address is looked up once per device with hipGetSymbolAddress, with
+// that device current, and only that address is handed to kernels.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int noalloc_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (!p) return (int)hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return (int)hipSuccess;
 }
 
 int launch_splitk_reduce(const float* part, int splits, int64_t mn, void* out, int out_bf16, void* stream) {

@@ -299,6 +299,22 @@ hq_status hq_gemm(const hq_plan* plan, int64_t m, const void* a, const void* a_s
                   const void* w, const void* meta, void* out, void* ws, size_t ws_bytes,
                   void* stream);
 
+/* hq_gemm for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It runs the same kernels as hq_gemm with the same plan
+ * and execution choice; the split-K partials (the only scratch a dense call
+ * needs) live in a 16 MiB device array owned by the library, one per GPU,
+ * held until the process ends.  A call whose partials exceed 16 MiB (see
+ * hq_plan_workspace_bytes) returns HQ_ERR_WORKSPACE before any launch.  The
+ * call allocates nothing (no hipMalloc / hipFree); the first call on a device
+ * looks the array's address up once (thread-safe).  Every call on one GPU
+ * shares that GPU's array and overwrites what it reads, so nothing needs
+ * clearing, but calls that overlap in time on one GPU (several streams or
+ * threads) race on it: serialise them, or use hq_gemm with workspaces of
+ * their own.  Arguments and results as hq_gemm. */
+hq_status hq_gemm_noalloc(const hq_plan* plan, int64_t m, const void* a, const void* a_scale, const void* w,
+                          const void* meta, void* out, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Grouped (mixture-of-experts) path.  The pages describe a separate MoE
  * backend with its own "Grouped" GEMM path run with W4A16 or W4A8 weights
