@@ -6,8 +6,8 @@ Layer: one GPU's tensor-parallel share of a DeepSeek-style layer -- 256
 experts, top-8 of softmax(router logits ~ N(0,1)), hidden 7168, expert
 intermediate 256 (gate_up N=512 K=7168; down N=7168 K=256), INT4 weights with
 group 128, fp16 scales and zero point 8, activations bf16 or fp8 e4m3 with
-per-token scales -- for T in {1, 32, 512, 4096} tokens (sampled tokens at the
-larger T), plus a small layer checked on every token.
+per-token scales -- for T in {1, 32, 512, 4096} tokens (every token at T = 512,
+sampled tokens at T = 4096), plus small layers checked on every token.
 """
 import numpy as np
 import pytest
@@ -272,6 +272,12 @@ def full_layer():
 @pytest.mark.parametrize("T", [1, 32, 512, 4096])
 def test_full_layer(full_layer, T, act):
     run_layer(full_layer, T, act, TOPK, sample=12)
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp8"])
+def test_full_layer_t512_every_token(full_layer, act):
+    # all 512 tokens (4096 routed slots, every expert hit), stage by stage
+    run_layer(full_layer, 512, act, TOPK, sample=None)
 
 
 @pytest.mark.parametrize("act", ["bf16", "fp8"])
