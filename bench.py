@@ -641,6 +641,8 @@ def run_quant(args):
         with torch.cuda.graph(gr):
             step(r)
         graphs.append(gr)
+    for gr in graphs:  # a graph's first launch uploads it: once each, before the warm-up steps
+        gr.replay()
     for i in range(args.warmup):
         graphs[i % R].replay()
     torch.cuda.synchronize()
@@ -985,9 +987,11 @@ def _moe_points(dev, Ts=(1, 32, 512, 4096), acts=("bf16", "fp8")):
 
 
 def graph_time_point(p, steps, warmup):
-    """Mean time of one pass of the point's calls, in ms: one HIP graph per
-    weight copy of the rotating pool, replayed back to back between two events
-    on the replay stream (the launch gaps inside a graph included)."""
+    """Mean time of one pass of the point's calls, in ms: one HIP graph holds a
+    pass over every weight copy of the rotating pool (R passes back to back,
+    so the weights of consecutive passes are cold in the last-level cache),
+    replayed between two events on the replay stream; the launch gaps inside
+    the graph are included, the host's per-graph launch is amortised over R."""
     R = p["R"]
     for r in range(min(R, 2)):
         for c in p["calls"](r):
@@ -1000,24 +1004,24 @@ def graph_time_point(p, steps, warmup):
             c()
     torch.cuda.current_stream().wait_stream(st)
     torch.cuda.synchronize()
-    graphs = []
-    for r in range(R):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for r in range(R):
             for c in p["calls"](r):
                 c()
-        graphs.append(g)
-    for i in range(max(warmup, 2)):
-        graphs[i % R].replay()
+    g.replay()  # the first launch uploads the graph
+    for _ in range(max(1, -(-warmup // R))):
+        g.replay()
     torch.cuda.synchronize()
+    reps = max(1, -(-steps // R))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(steps):
-        graphs[i % R].replay()
+    for _ in range(reps):
+        g.replay()
     e1.record()
     torch.cuda.synchronize()
-    del graphs
-    return e0.elapsed_time(e1) / steps
+    del g
+    return e0.elapsed_time(e1) / (reps * R)
 
 
 def eager_call_times(p, steps, hip, L):
@@ -1108,8 +1112,8 @@ def run_points_workload(args, builder):
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
             "config": {"workload": workload, "points_per_step": len(pts), "step_bytes": step_bytes,
                        "step_flops": step_flops, "gbps_per_step_time": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
-                       "timing": "per point: HIP graph replays of its calls, one graph per weight copy, events "
-                                 "around the replays; the step is the sum over the points"},
+                       "timing": "per point: one HIP graph of its calls over every weight copy of the pool, "
+                                 "events around the replays; the step is the sum over the points"},
             "roofline": roof, "cpu_baseline": cpu, "mfma_ceilings_TFLOPS": ceil, "gpu_state": smp.summary(),
             "points": points}
     print(json.dumps(line), flush=True)
@@ -1304,6 +1308,8 @@ def main():
         with torch.cuda.graph(g):
             run_step(points, r)
         graphs.append(g)
+    for g in graphs:  # a graph's first launch uploads it: once each, before the warm-up steps
+        g.replay()
     for i in range(args.warmup):
         graphs[i % R].replay()
     torch.cuda.synchronize()

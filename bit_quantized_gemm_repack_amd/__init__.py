@@ -76,7 +76,7 @@ class Compute(ctypes.Structure):
 class Tuning(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int),
                 ("waves", ctypes.c_int), ("split_k", ctypes.c_int), ("stages", ctypes.c_int),
-                ("mfma", ctypes.c_int)]
+                ("mfma", ctypes.c_int), ("tile_group", ctypes.c_int)]
 
 
 class AutotuneResult(ctypes.Structure):
@@ -84,7 +84,7 @@ class AutotuneResult(ctypes.Structure):
                 ("candidates", ctypes.c_int)]
 
 
-_TUNING_FIELDS = ("kernel", "tile_m", "tile_n", "waves", "split_k", "stages")
+_TUNING_FIELDS = ("kernel", "tile_m", "tile_n", "waves", "split_k", "stages", "tile_group")
 
 
 def _tuning_dict(t: Tuning) -> dict:

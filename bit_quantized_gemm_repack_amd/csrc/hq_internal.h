@@ -318,6 +318,7 @@ struct TiledCfgRt {
   int nbw;    // 16-column blocks per wave (2, 4); tile width = 64 * nbw
   int split;   // K split over workgroups (dense; partials + reduce kernel)
   int stages;  // groups in the load pipeline (3; dense also 4, 5)
+  int gm;      // launch order (dense): row tiles per group, the group's tiles column by column
 };
 
 struct SkinnyCfg {
@@ -436,6 +437,7 @@ struct TiledArgs {
   int scale_bf16;
   int out_bf16;
   int tiles_m, tiles_n;
+  int group_m;  // dense launch order: row tiles per group (>= 1)
   int gps;      // groups per split (dense)
   float* part;  // [split][M][N] fp32 partials, or null (no split)
   // ---- grouped (MoE) mode: the same fields as SkinnyArgs ----

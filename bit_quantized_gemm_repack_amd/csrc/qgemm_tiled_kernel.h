@@ -72,6 +72,10 @@ struct TCfg {
   static constexpr int STAGE_BYTES = BM * ROWB;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static constexpr int META = e8m0_meta(FMT) ? 1 : 2;  // metadata loads per fragment
+  // Cache policy of the weight loads: default (temporal).  The row tiles of
+  // one launch-order group run side by side on one XCD and read the same
+  // weight columns, so the fragments must stay in that XCD's L2.
+  static constexpr int WPOL = 0;
   // vector-memory loads per step per wave (MXFP4 activations: plus one E8M0
   // word per m-block)
   static constexpr int LPS = SEGW + (TWO ? 2 : 1) * NBW + META * NBW + (ACT4 ? MB : 0);
@@ -128,12 +132,20 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
   int tm, tn;
   if constexpr (GRP == GRP_DENSE) {
     // XCD-aware order: ids dealt round-robin to the 8 XCDs get consecutive
-    // logical tiles (same rows) on each XCD.
+    // logical tiles on each XCD.  Logical tiles run in groups of group_m row
+    // tiles, each group column by column, so the tiles one XCD holds at a time
+    // form a block (group_m rows x a few columns) that shares both its
+    // activation rows and its weight columns through that XCD's L2.
     const int nwg = gridDim.x;
     int lid = blockIdx.x;
     if ((nwg & 7) == 0) lid = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
-    tm = lid / p.tiles_n;
-    tn = lid - tm * p.tiles_n;
+    const int per = p.group_m * p.tiles_n;  // tiles per group
+    const int grp = lid / per;
+    const int first = grp * p.group_m;
+    const int gsz = min(p.tiles_m - first, p.group_m);
+    const int r = lid - grp * per;
+    tm = first + r % gsz;
+    tn = r / gsz;
   } else {
     tn = blockIdx.x;
     tm = blockIdx.y;
@@ -259,23 +271,23 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
       if constexpr (C::W2 || C::W3) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rw, woff[j], gg * C::FRAGB, 2);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rw, woff[j], gg * C::FRAGB, C::WPOL);
         braw[slot][j] = u4_t{(uint32_t)v[0], (uint32_t)v[1], 0u, 0u};
       } else {
-        braw[slot][j] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[j], gg * C::FRAGB, 2));
+        braw[slot][j] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[j], gg * C::FRAGB, C::WPOL));
       }
     }
     if constexpr (C::W8) {
 #pragma unroll
       for (int j = 0; j < NBW; ++j)
         braw2[slot][j] =
-            __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[j] + 1024, gg * C::FRAGB, 2));
+            __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[j] + 1024, gg * C::FRAGB, C::WPOL));
     }
     if constexpr (C::W3) {
       // the 1-bit plane: bytes [512, 768) of the fragment, one word per lane
 #pragma unroll
       for (int j = 0; j < NBW; ++j)
-        braw2[slot][j] = u4_t{__builtin_amdgcn_raw_buffer_load_b32(rw, woff[j] + 512 - 4 * lane, gg * C::FRAGB, 2), 0u,
+        braw2[slot][j] = u4_t{__builtin_amdgcn_raw_buffer_load_b32(rw, woff[j] + 512 - 4 * lane, gg * C::FRAGB, C::WPOL), 0u,
                               0u, 0u};
     }
     // Metadata comes in as whole 32-bit words and the lane's byte / half-word
@@ -329,6 +341,21 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
     const int r = 16 * mb + c16;
     const uint8_t* base = lds + slot * C::STAGE_BYTES + r * C::ROWB;
     return *reinterpret_cast<const u4_t*>(base + swz<4>(r, kq) * 16);
+  };
+  // 8- and 4-bit activations: the operands of every m-block of the step are
+  // read into registers of their own before the first MFMA, so the LDS
+  // latency is paid once per step rather than once per m-block (reading
+  // into reused registers would serialise each read behind the MFMAs of the
+  // m-block before).
+  [[maybe_unused]] auto read_step8 = [&](int slot, u4_t (&a)[C::MB][2]) {
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) read_a8(slot, mb, a[mb]);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  [[maybe_unused]] auto read_step4 = [&](int slot, u4_t (&a)[C::MB]) {
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) a[mb] = read_a4(slot, mb);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   auto compute = [&](auto slot_c) {
@@ -536,15 +563,15 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
         bop[j][0] = i8_operand(braw[slot][j][0], braw[slot][j][1]);
         bop[j][1] = i8_operand(braw[slot][j][2], braw[slot][j][3]);
       }
+      u4_t a8[C::MB][2];
+      read_step8(slot, a8);
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) {
-        u4_t a[2];
-        read_a8(slot, mb, a);
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
           i4_t P = i4_t{0, 0, 0, 0};
-          P = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i4_t, a[0]), bop[j][0], P, 0, 0, 0);
-          P = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i4_t, a[1]), bop[j][1], P, 0, 0, 0);
+          P = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i4_t, a8[mb][0]), bop[j][0], P, 0, 0, 0);
+          P = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i4_t, a8[mb][1]), bop[j][1], P, 0, 0, 0);
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[mb][j][r] += sj[j] * (float)P[r];
         }
@@ -560,11 +587,11 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
       }
       const i8_t ones = i8_t{0x38383838, 0x38383838, 0x38383838, 0x38383838,
                              0x38383838, 0x38383838, 0x38383838, 0x38383838};
+      u4_t a8[C::MB][2];
+      read_step8(slot, a8);
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) {
-        u4_t a[2];
-        read_a8(slot, mb, a);
-        const i8_t av = cat8(a[0], a[1]);
+        const i8_t av = cat8(a8[mb][0], a8[mb][1]);
         const f4_t rs = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, ones, f4_t{0.f, 0.f, 0.f, 0.f}, 0, 0,
                                                                          0, 127, 0, 127);
 #pragma unroll
@@ -577,9 +604,11 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
       }
     } else if constexpr (FMT == FMT_F44) {
       // fp4 x fp4: both operands E2M1 (format 4), each with its block scales
+      u4_t a4[C::MB];
+      read_step4(slot, a4);
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) {
-        const u4_t x = read_a4(slot, mb);
+        const u4_t x = a4[mb];
         const i8_t av = i8_t{(int)x[0], (int)x[1], (int)x[2], (int)x[3], 0, 0, 0, 0};
         const int sa = (int)((asc[slot][mb] >> (8 * kq)) & 0xFFu);
 #pragma unroll
@@ -591,11 +620,11 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
         }
       }
     } else {  // FMT_F4
+      u4_t a8[C::MB][2];
+      read_step8(slot, a8);
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) {
-        u4_t a[2];
-        read_a8(slot, mb, a);
-        const i8_t av = cat8(a[0], a[1]);
+        const i8_t av = cat8(a8[mb][0], a8[mb][1]);
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
           const u4_t w = braw[slot][j];

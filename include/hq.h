@@ -215,6 +215,10 @@ typedef struct hq_tuning {
   int stages;  /* skinny: 128-k groups in flight per wave (2, 4, 8);
                   tiled: groups in the LDS / register ring (2..5)          */
   int mfma;    /* 16 (16x16 MFMA); reserved for 32                         */
+  int tile_group; /* tiled kernel launch order: row tiles per group (1 = row
+                    by row); each group is walked column by column, so an XCD
+                    works on a block of tiles that shares activations and
+                    weights in its L2 (0 = the library's choice)          */
 } hq_tuning;
 
 typedef struct hq_plan hq_plan;

@@ -598,13 +598,14 @@ def test_per_m_tuning_table():
     t = dict(kernel=1, tile_m=16, tile_n=32, waves=4, split_k=2, stages=4)
     p.set_tuning(1, t)
     got, tuned = p.get_tuning(1)
-    assert tuned and got == t
+    assert tuned and got == dict(t, tile_group=0)   # no launch-order groups on the skinny kernel
     d = p.describe(1)
     assert "tile_n=32 waves=4 split_k=2 stages=4" in d
     assert p.workspace_bytes(1) == 2 * 1 * 4096 * 4
     assert p.get_tuning(2) == (heur, False)          # other m keep the heuristic
     p.set_tuning(300, dict(kernel=2, tile_m=128, tile_n=256, stages=2, split_k=1))
-    assert p.get_tuning(300) == (dict(kernel=2, tile_m=128, tile_n=256, waves=4, split_k=1, stages=2), True)
+    assert p.get_tuning(300) == (dict(kernel=2, tile_m=128, tile_n=256, waves=4, split_k=1, stages=2, tile_group=8),
+                                 True)
     p.set_tuning(1, None)
     assert p.get_tuning(1) == (heur, False)
     with pytest.raises(hq.HQError):   # not a tile width
@@ -724,3 +725,16 @@ def test_mfma_probe_validation():
     for kind, wg, it in ((-1, 1, 1), (6, 1, 1), (0, 0, 1), (0, 1 << 21, 1), (0, 1, 0), (0, 1, (1 << 24) + 1)):
         assert L.hq_mfma_peak(kind, wg, it, fake, ctypes.byref(fl), None) == hq.HQ_ERR_INVALID_ARG, (kind, wg, it)
     assert L.hq_mfma_peak(0, 1, 1, None, ctypes.byref(fl), None) == hq.HQ_ERR_INVALID_ARG
+
+
+
+def test_tile_group_choice_and_validation():
+    """The tiled kernel's launch order: groups of tile_group row tiles walked
+    column by column (8 unless a tuning says otherwise), 1..64."""
+    p = _plan(quant=hq.w4a8_mxfp4(), n=4096, k=7168, max_m=1024)
+    assert "tile_group=8" in p.describe(1024) and p.get_tuning(1024)[0]["tile_group"] == 8
+    q = _plan(quant=hq.w4a16("f16"), n=512, k=1024, max_m=256, tuning=dict(kernel=2, tile_group=3))
+    assert "tile_group=3" in q.describe(256)
+    for bad in (-1, 65):
+        with pytest.raises(hq.HQError):
+            _plan(quant=hq.w4a16("f16"), n=512, k=1024, max_m=256, tuning=dict(kernel=2, tile_group=bad))

@@ -297,6 +297,23 @@ def test_tiled_split_k_w4a8_formats():
         _assert_ok(out.double().cpu().numpy(), ref, "bf16", "split w4a8-mxfp4")
 
 
+@pytest.mark.parametrize("group", [1, 3, 8, 64])
+def test_tiled_launch_order(group):
+    # every tile computed once whatever the launch order: 5 x 6 tiles of 64 x 128
+    # (a partial last row tile, a partial last group for 3 and 8, one group for 64)
+    M, N, K = 300, 768, 1024
+    _log(f"tiled launch order tile_group={group}")
+    d = datagen.w4a8_mxfp4(M, N, K)
+    plan = hq.Plan(N, K, hq.w4a8_mxfp4(), max_m=M, tuning=dict(kernel=2, tile_m=64, tile_n=128, tile_group=group))
+    assert f"tile_group={group}" in plan.describe(M)
+    w, meta = plan.repack(torch.from_numpy(d["codes"]).to(DEV), e8m0=torch.from_numpy(d["e8m0"]).to(DEV))
+    out = plan.gemm(d["a_codes"].to(DEV), w, meta, a_scale=d["a_scale"].to(DEV))
+    torch.cuda.synchronize()
+    ref = og.gemm_mxfp4_fp8(d["a_codes"].numpy(), d["a_scale"].numpy(), d["codes"], d["e8m0"])
+    _assert_ok(out.double().cpu().numpy(), ref, "bf16", f"launch order {group}")
+    run_w4a16(M, N, K, act="f16", zp="fixed", tuning=dict(kernel=2, tile_m=128, tile_n=256, tile_group=group))
+
+
 @pytest.mark.parametrize("tuning", [dict(kernel=2, tile_m=64, tile_n=256), dict(kernel=2, tile_m=128, tile_n=256),
                                     dict(kernel=2, tile_m=128, tile_n=128)])
 def test_tiled_w4a8(tuning):
