@@ -538,21 +538,36 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
           bop[j][t] = C::W2 ? w2_operand(braw[slot][j][t >> 1], magic_v, t & 1) : w16_operand(braw[slot][j][t], magic_v);
       }
       const u4_t ones = u4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+      // Two m-blocks at a time, k-step outer: the 2 (NBW + 1) accumulator
+      // chains (row sums and products) advance one MFMA each per k-step, so
+      // consecutive MFMAs never wait on each other's results.
+      constexpr int PAIR = C::MB >= 2 ? 2 : 1;
 #pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb) {
-        u4_t a[4];
-        read_a16(slot, mb, a);
-        f4_t rs = f4_t{0.f, 0.f, 0.f, 0.f};
+      for (int mb0 = 0; mb0 < C::MB; mb0 += PAIR) {
+        u4_t a[PAIR][4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) rs = mfma_16x16x32<false>(a[t], ones, rs);
+        for (int u = 0; u < PAIR; ++u) read_a16(slot, mb0 + u, a[u]);
+        f4_t rs[PAIR], P[PAIR][NBW];
 #pragma unroll
-        for (int j = 0; j < NBW; ++j) {
-          f4_t P = f4_t{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < PAIR; ++u) {
+          rs[u] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int t = 0; t < 4; ++t) P = mfma_16x16x32<false>(a[t], bop[j][t], P);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[mb][j][r] += sj[j] * (P[r] - cj[j] * rs[r]);
+          for (int j = 0; j < NBW; ++j) P[u][j] = f4_t{0.f, 0.f, 0.f, 0.f};
         }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int u = 0; u < PAIR; ++u) {
+            rs[u] = mfma_16x16x32<false>(a[u][t], ones, rs[u]);
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) P[u][j] = mfma_16x16x32<false>(a[u][t], bop[j][t], P[u][j]);
+          }
+#pragma unroll
+        for (int u = 0; u < PAIR; ++u)
+#pragma unroll
+          for (int j = 0; j < NBW; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[mb0 + u][j][r] += sj[j] * (P[u][j][r] - cj[j] * rs[u][r]);
       }
     } else if constexpr (FMT == FMT_I8) {
       i4_t bop[NBW][2];
