@@ -79,6 +79,11 @@ class Tuning(ctypes.Structure):
                 ("mfma", ctypes.c_int), ("tile_group", ctypes.c_int)]
 
 
+class JitStats(ctypes.Structure):
+    _fields_ = [("compiles", ctypes.c_int64), ("disk_hits", ctypes.c_int64), ("memory_hits", ctypes.c_int64),
+                ("launches", ctypes.c_int64), ("compile_seconds", ctypes.c_double), ("load_seconds", ctypes.c_double)]
+
+
 class AutotuneResult(ctypes.Structure):
     _fields_ = [("best", Tuning), ("best_us", ctypes.c_float), ("current_us", ctypes.c_float),
                 ("candidates", ctypes.c_int)]
@@ -200,7 +205,20 @@ _SIGS = {
                                ctypes.c_size_t, ctypes.c_void_p]),
     "hq_gemm_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_void_p] * 5 +
                         [ctypes.c_void_p]),
+    "hq_plan_set_jit": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_char_p]),
+    "hq_jit_cache_key": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_char_p, ctypes.c_char_p,
+                                        ctypes.c_size_t]),
+    "hq_jit_get_stats": (ctypes.c_int, [ctypes.POINTER(JitStats)]),
+    "hq_jit_prepare": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_char_p]),
 }
+
+
+def jit_stats() -> dict:
+    """Counters of the run-time specialisation since the library was loaded
+    (hq_jit_get_stats)."""
+    st = JitStats()
+    _check(lib().hq_jit_get_stats(ctypes.byref(st)))
+    return {f: getattr(st, f) for f, _ in JitStats._fields_}
 
 
 def lib():
@@ -466,6 +484,25 @@ class Plan:
                                       ctypes.byref(res)))
         return {"tuning": _tuning_dict(res.best), "best_us": float(res.best_us),
                 "current_us": float(res.current_us), "candidates": int(res.candidates)}
+
+    def set_jit(self, enable: bool = True, cache_dir: Optional[str] = None):
+        """Run-time specialised kernels for this dense plan (hq_plan_set_jit):
+        each call's shape compiled once by hipRTC, code objects cached on disk
+        under cache_dir (None: the library's default directory)."""
+        _check(lib().hq_plan_set_jit(self._h, 1 if enable else 0,
+                                     None if cache_dir is None else os.fsencode(cache_dir)))
+
+    def jit_cache_key(self, m: int, arch: str = "gfx950") -> str:
+        """The code-object cache key of the kernel a call with m rows runs under
+        run-time specialisation (hq_jit_cache_key; host only)."""
+        buf = ctypes.create_string_buffer(128)
+        _check(lib().hq_jit_cache_key(self._h, int(m), arch.encode(), buf, len(buf)))
+        return buf.value.decode()
+
+    def jit_prepare(self, m: int, arch: str = "gfx950"):
+        """Compile the m-row kernel of run-time specialisation into the plan's
+        code-object cache without a device (hq_jit_prepare)."""
+        _check(lib().hq_jit_prepare(self._h, int(m), arch.encode()))
 
     def set_tuning(self, m: int, tuning: Optional[dict]):
         """Install a tuning for exactly m rows (None removes m's entry)."""

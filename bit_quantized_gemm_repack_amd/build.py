@@ -26,6 +26,8 @@ DEVICE = [f"--offload-arch={ARCH}", "-mcode-object-version=5", "-Xclang", "-targ
 # epilogues read them without a v_accvgpr_read copy each; sources named
 # *_f16.hip (an fp16 k loop without per-group epilogue) keep the default.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+# hipRTC for the run-time specialised kernels (hq_plan_set_jit)
+LINK = ["-lhiprtc"]
 
 
 def sources():
@@ -49,7 +51,7 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *DEVICE, "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, *DEVICE, "-shared", "-fPIC", "-o", tmp, *objs, *LINK]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")

@@ -17,6 +17,7 @@
 #include <string>
 
 #include "hq_internal.h"
+#include "jit.h"
 
 namespace {
 
@@ -727,7 +728,12 @@ hq_status dense_run(const hq_plan* p, const hq::Exec& e, int64_t m, const void* 
       t.gps = (int)cdiv(G, e.tl.split);
       t.part = e.tl.split > 1 ? static_cast<float*>(ws) : nullptr;
       hq::arm_timing({ev.start, e.tl.split > 1 ? nullptr : ev.stop});
-      int err = hq::launch_tiled(p->fmt, e.tl, t, stream);
+      std::string jit_err;
+      int err = p->jit ? hq::jit::launch_tiled(p, e.tl, t, stream, &jit_err) : hq::launch_tiled(p->fmt, e.tl, t, stream);
+      if (!jit_err.empty()) {
+        hq::arm_timing({nullptr, nullptr});
+        return fail(HQ_ERR_UNSUPPORTED, "%s", jit_err.c_str());
+      }
       if (err == hipSuccess && e.tl.split > 1) {
         hq::arm_timing({nullptr, ev.stop});
         err = hq::launch_splitk_reduce(t.part, e.tl.split, m * N, out, t.out_bf16, stream);
@@ -762,7 +768,12 @@ hq_status dense_run(const hq_plan* p, const hq::Exec& e, int64_t m, const void* 
     args.gps = (int)cdiv(G, e.sk.split);
     const bool reduce = e.ws_bytes > 0;
     hq::arm_timing({ev.start, reduce ? nullptr : ev.stop});
-    int err = hq::launch_skinny(p->fmt, e.sk, args, stream);
+    std::string jit_err;
+    int err = p->jit ? hq::jit::launch_skinny(p, e.sk, args, stream, &jit_err) : hq::launch_skinny(p->fmt, e.sk, args, stream);
+    if (!jit_err.empty()) {
+      hq::arm_timing({nullptr, nullptr});
+      return fail(HQ_ERR_UNSUPPORTED, "%s", jit_err.c_str());
+    }
     if (err == hipSuccess && reduce) {
       hq::arm_timing({nullptr, ev.stop});
       err = hq::launch_splitk_reduce(args.part, e.sk.split, m * N, out, args.out_bf16, stream);
@@ -1307,6 +1318,69 @@ hq_status hq_plan_get_tuning(const hq_plan* p, int64_t m, hq_tuning* t, int* is_
   for (const auto& e : p->tuned) tuned |= e.first == m;
   *t = resolved_tuning(hq::choose_exec(p, m));
   if (is_tuned) *is_tuned = tuned ? 1 : 0;
+  return ok();
+}
+
+hq_status hq_plan_set_jit(hq_plan* p, int enable, const char* cache_dir) {
+  if (!p) return fail(HQ_ERR_INVALID_ARG, "null plan");
+  if (enable != 0 && enable != 1) return fail(HQ_ERR_INVALID_ARG, "enable must be 0 or 1");
+  if (p->compute.kind != HQ_GEMM_DENSE)
+    return fail(HQ_ERR_UNSUPPORTED, "run-time specialisation covers dense plans only");
+  if (cache_dir && std::strlen(cache_dir) >= sizeof(p->jit_dir))
+    return fail(HQ_ERR_INVALID_ARG, "cache directory path longer than %zu bytes", sizeof(p->jit_dir) - 1);
+  p->jit = enable;
+  std::snprintf(p->jit_dir, sizeof(p->jit_dir), "%s", cache_dir ? cache_dir : "");
+  return ok();
+}
+
+hq_status hq_jit_cache_key(const hq_plan* p, int64_t m, const char* arch, char* key, size_t key_bytes) {
+  try {
+    if (!p || !arch || !key) return fail(HQ_ERR_INVALID_ARG, "null argument");
+    if (p->compute.kind != HQ_GEMM_DENSE)
+      return fail(HQ_ERR_UNSUPPORTED, "run-time specialisation covers dense plans only");
+    if (m < 1 || m > p->max_m) return fail(HQ_ERR_INVALID_ARG, "m out of range [1, max_m]");
+    const hq::Exec e = hq::choose_exec(p, m);
+    const int64_t N = p->layer.n, K = p->layer.k;
+    const hq::jit::Spec sp = e.kernel == hq::KER_TILED ? hq::jit::tiled_spec(p->fmt, e.tl, m, N, K)
+                                                        : hq::jit::skinny_spec(p->fmt, e.sk, m, N, K);
+    const std::string k = hq::jit::cache_key(sp, arch);
+    if (key_bytes < k.size() + 1) return fail(HQ_ERR_INVALID_ARG, "key buffer shorter than %zu bytes", k.size() + 1);
+    std::memcpy(key, k.c_str(), k.size() + 1);
+    return ok();
+  } catch (...) {
+    return fail(HQ_ERR_INTERNAL, "exception in hq_jit_cache_key");
+  }
+}
+
+hq_status hq_jit_prepare(const hq_plan* p, int64_t m, const char* arch) {
+  try {
+    if (!p || !arch) return fail(HQ_ERR_INVALID_ARG, "null argument");
+    if (p->compute.kind != HQ_GEMM_DENSE)
+      return fail(HQ_ERR_UNSUPPORTED, "run-time specialisation covers dense plans only");
+    if (m < 1 || m > p->max_m) return fail(HQ_ERR_INVALID_ARG, "m out of range [1, max_m]");
+    const hq::Exec e = hq::choose_exec(p, m);
+    const int64_t N = p->layer.n, K = p->layer.k;
+    const hq::jit::Spec sp = e.kernel == hq::KER_TILED ? hq::jit::tiled_spec(p->fmt, e.tl, m, N, K)
+                                                        : hq::jit::skinny_spec(p->fmt, e.sk, m, N, K);
+    std::string err;
+    const int r = hq::jit::prepare(p, sp, arch, &err);
+    if (r == 1) return fail(HQ_ERR_UNSUPPORTED, "%s", err.c_str());
+    if (r != 0) return fail(HQ_ERR_INTERNAL, "%s", err.c_str());
+    return ok();
+  } catch (...) {
+    return fail(HQ_ERR_INTERNAL, "exception in hq_jit_prepare");
+  }
+}
+
+hq_status hq_jit_get_stats(hq_jit_stats* stats) {
+  if (!stats) return fail(HQ_ERR_INVALID_ARG, "null argument");
+  const hq::jit::Stats s = hq::jit::stats();
+  stats->compiles = s.compiles;
+  stats->disk_hits = s.disk_hits;
+  stats->memory_hits = s.memory_hits;
+  stats->launches = s.launches;
+  stats->compile_seconds = s.compile_seconds;
+  stats->load_seconds = s.load_seconds;
   return ok();
 }
 

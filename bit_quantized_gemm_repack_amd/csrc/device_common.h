@@ -3,7 +3,9 @@
 // fragment layout (hq_internal.h) was designed for.
 #pragma once
 
+#ifndef __HIPCC_RTC__  // the run-time compiler includes the HIP runtime itself
 #include <hip/hip_runtime.h>
+#endif
 
 #include <cstdint>
 

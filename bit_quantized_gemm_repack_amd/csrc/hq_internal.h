@@ -39,12 +39,14 @@
 // A grouped (MoE) weight is E such layouts one after the other.
 #pragma once
 
-#include <cstddef>
 #include <cstdint>
 #include <utility>
+#ifndef __HIPCC_RTC__  // the run-time compiler sees the device-side definitions only
+#include <cstddef>
 #include <vector>
 
 #include "../../include/hq.h"
+#endif
 
 #if defined(__HIPCC__)
 #define HQ_HD __host__ __device__
@@ -331,6 +333,7 @@ struct SkinnyCfg {
 
 }  // namespace hq
 
+#ifndef __HIPCC_RTC__
 struct hq_plan {
   hq_layer_desc layer;
   hq_compute compute;
@@ -343,10 +346,14 @@ struct hq_plan {
   size_t w_bytes_per_expert;
   size_t meta_bytes_per_expert;
   size_t scale_region_bytes;  // per expert, before the zero / e8m0 region
+  int jit;                    // kernels specialised at run time for each call's shape (hq_plan_set_jit)
+  char jit_dir[512];          // code-object cache directory ("" = the default)
 };
+#endif  // __HIPCC_RTC__
 
 namespace hq {
 
+#ifndef __HIPCC_RTC__
 // Resolved execution choice for one call with m rows.
 struct Exec {
   int kernel;
@@ -359,8 +366,10 @@ struct Exec {
 // The execution choice for m rows: the heuristic with the overrides of `u`,
 // or (u == nullptr) with the plan's tuned entry for m, else its user tuning.
 Exec choose_exec(const hq_plan* p, int64_t m, const hq_tuning* u = nullptr);
+#endif  // __HIPCC_RTC__
 
-// Kernel launchers (defined in the .hip files).  Return a hipError_t as int.
+// Kernel arguments (passed by value) and launchers (defined in the .hip
+// files; they return a hipError_t as int).
 struct SkinnyArgs {
   const void* a;
   const float* a_scale;
@@ -403,6 +412,7 @@ enum GroupedEpi : int { GEPI_PLAIN = 0, GEPI_SILU = 1, GEPI_SILU_F32 = 2, GEPI_C
 // token (gate_up), 2 rows in aligned order (down).
 enum GroupedMode : int { GRP_DENSE = 0, GRP_GATHER = 1, GRP_SORTED = 2 };
 
+#ifndef __HIPCC_RTC__
 int launch_skinny(int fmt, const SkinnyCfg& cfg, const SkinnyArgs& a, void* stream);
 // Grouped down GEMM for short K (K = 128 G): blocks of 16 mb aligned rows,
 // combine rows out.  Supported: fp16 / bf16 / fp8 activations, mb 1 with
@@ -421,6 +431,7 @@ int launch_moe_requant(const float* act32, const int32_t* sorted_ids, const int3
 // [t*topk][ncol] fp32 (summed in slot order), c < ncol; y row stride n.
 int launch_moe_combine(const float* rows, int topk, int64_t t, int64_t n, int64_t col0, int64_t ncol, void* y,
                        int out_bf16, void* stream);
+#endif  // __HIPCC_RTC__
 
 struct TiledArgs {
   const void* a;
@@ -453,6 +464,7 @@ struct TiledArgs {
   float* f32_out;
 };
 
+#ifndef __HIPCC_RTC__
 int launch_tiled(int fmt, const TiledCfgRt& cfg, const TiledArgs& a, void* stream);
 // Grouped launch: grid (n tiles, aligned blocks of bm rows).
 int launch_tiled_grouped(int fmt, int mode, const TiledCfgRt& cfg, const TiledArgs& a, int64_t blocks,
@@ -485,5 +497,6 @@ TimingEvents take_timing();
 void arm_timing(TimingEvents t);
 int launch_repack(const hq_plan* p, const void* codes, const void* scales, const void* zx,
                   void* w_out, void* meta_out, void* stream);
+#endif  // __HIPCC_RTC__
 
 }  // namespace hq

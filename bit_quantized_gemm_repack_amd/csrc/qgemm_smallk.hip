@@ -35,6 +35,11 @@ __global__ void __launch_bounds__(256) qgemm_smallk(SkinnyArgs p) {
   constexpr bool ACT16 = (FMT == FMT_W16F16 || FMT == FMT_W16BF16);
   constexpr int AV = ACT16 ? 4 * G : 2 * G;  // 16-byte activation operands per m-block
   const int lane = threadIdx.x & 63;
+  // E8M0 block scales 2^0 and 2^9 for the scaled matrix instruction, held in
+  // VGPRs: the instruction reads its scales from VGPRs only, and a uniform
+  // constant left to the compiler may be placed in a scalar register.
+  [[maybe_unused]] const int e8_one = (int)opaque_vgpr(127u);
+  [[maybe_unused]] const int e8_nine = (int)opaque_vgpr(136u);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar column offsets
   const int c = lane & 15;
   const int kq = lane >> 4;
@@ -133,7 +138,7 @@ __global__ void __launch_bounds__(256) qgemm_smallk(SkinnyArgs p) {
         const i8_t ones = i8_t{0x38383838, 0x38383838, 0x38383838, 0x38383838,
                                0x38383838, 0x38383838, 0x38383838, 0x38383838};
         rs[mb][g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            cat8(a[mb][2 * g], a[mb][2 * g + 1]), ones, f4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+            cat8(a[mb][2 * g], a[mb][2 * g + 1]), ones, f4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, e8_one, 0, e8_one);
       }
     }
   }
@@ -194,7 +199,7 @@ __global__ void __launch_bounds__(256) qgemm_smallk(SkinnyArgs p) {
         for (int mb = 0; mb < L; ++mb) {
           // codes 0x00..0x0F are q * 2^-9 in e4m3; block scale 2^9 (E8M0 136) undoes it
           const f4_t P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              cat8(a[mb][2 * g], a[mb][2 * g + 1]), bop, f4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 136);
+              cat8(a[mb][2 * g], a[mb][2 * g + 1]), bop, f4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, e8_one, 0, e8_nine);
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[mb][r] += s * (P[r] - zf * rs[mb][g][r]);
         }

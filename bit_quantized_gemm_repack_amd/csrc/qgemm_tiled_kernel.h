@@ -38,15 +38,19 @@
 //     fp8 requant, each slot's weighted fp32 row for the combine kernel).
 #pragma once
 
+#ifndef __HIPCC_RTC__  // the run-time compiler takes the kernel only (hq_plan_set_jit)
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
+#endif
 
 #include <type_traits>
 #include <utility>
 
 #include "device_common.h"
 #include "hq_internal.h"
+#ifndef __HIPCC_RTC__
 #include "launch.h"
+#endif
 
 namespace hq {
 
@@ -110,19 +114,32 @@ __device__ inline void pin(T& x) {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int FMT, int BM, int NBW, int GRP, int ST>
+// MC, NC, KC: the call's M, N and K as compile-time constants (run-time
+// specialisation, hq_plan_set_jit); 0 takes them from the arguments.  SL:
+// the stage ring is a static LDS array (a run-time compiled module has no
+// dynamic-LDS attribute to raise), not the launch's dynamic LDS.
+template <int FMT, int BM, int NBW, int GRP, int ST, int MC = 0, int NC = 0, int KC = 0, int SL = 0>
 __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses device-only builtins; the host pass needs only the stub
   using C = TCfg<FMT, BM, NBW, ST>;
   static_assert(C::FITS, "loads in flight exceed the counter, or the ring the LDS");
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+  uint8_t* lds;
+  if constexpr (SL) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds_st[C::LDS_BYTES];
+    lds = lds_st;
+  } else {
+    lds = lds_dyn;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int c16 = lane & 15;
   const int kq = lane >> 4;
-  const int G = p.G;
-  const int K = p.K;
+  const int M = MC ? MC : p.M;
+  const int N = NC ? NC : p.N;
+  const int K = KC ? KC : p.K;
+  const int G = KC ? KC / 128 : p.G;
   // Split K (dense only): grid y picks a range of p.gps groups; the fp32
   // partial tiles are summed by a second kernel.
   const int split = (GRP == GRP_DENSE) ? (int)blockIdx.y : 0;
@@ -167,7 +184,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
         for (int e = tid; e < BM * C::BN; e += C::THREADS) {
           const int r = e / C::BN, cc = e - r * C::BN;
           const int id = p.sorted_ids[m0 + r];
-          if (id < p.n_slots) p.f32_out[(int64_t)id * p.N + tn * C::BN + cc] = 0.f;
+          if (id < p.n_slots) p.f32_out[(int64_t)id * N + tn * C::BN + cc] = 0.f;
         }
       }
       return;
@@ -202,9 +219,9 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
   };
   const int a_rowb = C::ACT16 ? 2 * K : (C::ACT4 ? K / 2 : K);
-  const int a_rows = (GRP == GRP_GATHER) ? p.n_slots / p.topk : p.M;
+  const int a_rows = (GRP == GRP_GATHER) ? p.n_slots / p.topk : M;
   const auto ra = rsrc(p.a, (int64_t)a_rows * a_rowb);
-  const int64_t nfrag = (int64_t)(p.N / 16) * G;  // fragments of this weight (one expert)
+  const int64_t nfrag = (int64_t)(N / 16) * G;  // fragments of this weight (one expert)
   const auto rw = rsrc(wbytes, nfrag * C::FRAGB);
   [[maybe_unused]] const auto rs = rsrc(scales16, nfrag * 32);
   [[maybe_unused]] const auto rz = rsrc(zeros32 ? static_cast<const void*>(zeros32) : static_cast<const void*>(scales16),
@@ -226,7 +243,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
     const int lchunk = swz<C::CHUNKS>(r, lane % C::CHUNKS);
     int row;
     if constexpr (GRP == GRP_DENSE) {
-      row = min(m0 + r, p.M - 1);
+      row = min(m0 + r, M - 1);
     } else if constexpr (GRP == GRP_GATHER) {
       const int id = p.sorted_ids[m0 + r];
       row = id < p.n_slots ? id / p.topk : 0;
@@ -240,7 +257,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
   // contiguous bytes
   [[maybe_unused]] int aeoff[C::MB];
 #pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb) aeoff[mb] = min(m0 + 16 * mb + c16, p.M - 1) * 4;
+  for (int mb = 0; mb < C::MB; ++mb) aeoff[mb] = min(m0 + 16 * mb + c16, M - 1) * 4;
   int woff[NBW], soff[NBW], zoff[NBW];
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
@@ -320,6 +337,11 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 #pragma unroll
     for (int j = 0; j < NBW; ++j) acc[mb][j] = f4_t{0.f, 0.f, 0.f, 0.f};
   [[maybe_unused]] const uint32_t magic_v = opaque_vgpr(f16_act(FMT) ? 0x64006400u : 0x43004300u);
+  // E8M0 block scales 2^0 and 2^9 for the scaled matrix instruction, held in
+  // VGPRs: the instruction reads its scales from VGPRs only, and a uniform
+  // constant left to the compiler may be placed in a scalar register.
+  [[maybe_unused]] const int e8_one = (int)opaque_vgpr(127u);
+  [[maybe_unused]] const int e8_nine = (int)opaque_vgpr(136u);
 
   // Operand fetch of m-block mb from `slot`: row r = 16 mb + c16.
   // 16-bit: step t takes k = 32 t + 8 kq + [0,8) (chunk 4 t + kq);
@@ -538,10 +560,13 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
           bop[j][t] = C::W2 ? w2_operand(braw[slot][j][t >> 1], magic_v, t & 1) : w16_operand(braw[slot][j][t], magic_v);
       }
       const u4_t ones = u4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-      // Two m-blocks at a time, k-step outer: the 2 (NBW + 1) accumulator
-      // chains (row sums and products) advance one MFMA each per k-step, so
-      // consecutive MFMAs never wait on each other's results.
-      constexpr int PAIR = C::MB >= 2 ? 2 : 1;
+      // k-step outer over PAIR m-blocks: the PAIR (NBW + 1) accumulator chains
+      // (row sums and products) advance one MFMA each per k-step, so
+      // consecutive MFMAs never wait on each other's results.  Two m-blocks
+      // for two column blocks per wave; with four, one m-block already has
+      // five chains, and a pair would not fit the registers of two waves per
+      // SIMD.
+      constexpr int PAIR = (C::MB >= 2 && NBW <= 2) ? 2 : 1;
 #pragma unroll
       for (int mb0 = 0; mb0 < C::MB; mb0 += PAIR) {
         u4_t a[PAIR][4];
@@ -608,11 +633,11 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
       for (int mb = 0; mb < C::MB; ++mb) {
         const i8_t av = cat8(a8[mb][0], a8[mb][1]);
         const f4_t rs = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, ones, f4_t{0.f, 0.f, 0.f, 0.f}, 0, 0,
-                                                                         0, 127, 0, 127);
+                                                                         0, e8_one, 0, e8_one);
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
           const f4_t P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bop[j], f4_t{0.f, 0.f, 0.f, 0.f},
-                                                                          0, 0, 0, 127, 0, 136);
+                                                                          0, 0, 0, e8_one, 0, e8_nine);
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[mb][j][r] += sj[j] * (P[r] - zj[j] * rs[r]);
         }
@@ -644,7 +669,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
         for (int j = 0; j < NBW; ++j) {
           const u4_t w = braw[slot][j];
           const i8_t bv = i8_t{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
-          acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mb][j], 0, 4, 0, 127, 0,
+          acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mb][j], 0, 4, 0, e8_one, 0,
                                                                         e8m0_of(sraw[slot][j]));
         }
       }
@@ -694,17 +719,17 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
     for (int r = 0; r < 4; ++r) {
       const int m = m0 + 16 * mb + 4 * kq + r;
       if constexpr (GRP == GRP_DENSE) {
-        if (m >= p.M) continue;
+        if (m >= M) continue;
         const float sa = ACT_SCALE ? p.a_scale[m] : (nvfp4_weights(FMT) ? 256.f * p.tscale[0] : 1.f);
         if (p.part) {
-          float* prow = p.part + ((int64_t)split * p.M + m) * p.N;
+          float* prow = p.part + ((int64_t)split * M + m) * N;
 #pragma unroll
           for (int j = 0; j < NBW; ++j) prow[nblk(j) * 16 + c16] = acc[mb][j][r] * sa;
           continue;
         }
 #pragma unroll
         for (int j = 0; j < NBW; ++j)
-          store_out(p.out, (int64_t)m * p.N + nblk(j) * 16 + c16, acc[mb][j][r] * sa, p.out_bf16);
+          store_out(p.out, (int64_t)m * N + nblk(j) * 16 + c16, acc[mb][j][r] * sa, p.out_bf16);
       } else {
         const int id = p.sorted_ids[m];
         if (id >= p.n_slots) continue;
@@ -712,7 +737,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
         if constexpr (GRP == GRP_GATHER) {
           const float sa = ACT_SCALE ? p.a_scale[tok] : 1.f;
           if (paired) {
-            const int half = p.N / 2;
+            const int half = N / 2;
 #pragma unroll
             for (int j = 0; j < NBW / 2; ++j) {
               const float gv = acc[mb][j][r] * sa;
@@ -724,11 +749,11 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
           } else {
 #pragma unroll
             for (int j = 0; j < NBW; ++j)
-              store_out(p.out, (int64_t)m * p.N + nblk(j) * 16 + c16, acc[mb][j][r] * sa, p.out_bf16);
+              store_out(p.out, (int64_t)m * N + nblk(j) * 16 + c16, acc[mb][j][r] * sa, p.out_bf16);
           }
         } else {
           const float sa = (ACT_SCALE ? p.a_scale[m] : 1.f) * p.topk_w[id];
-          float* row = p.f32_out + (int64_t)id * p.N;  // this slot's weighted row
+          float* row = p.f32_out + (int64_t)id * N;  // this slot's weighted row
 #pragma unroll
           for (int j = 0; j < NBW; ++j) row[nblk(j) * 16 + c16] = acc[mb][j][r] * sa;
         }
@@ -738,6 +763,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 #endif
 }
 
+#ifndef __HIPCC_RTC__
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
@@ -789,5 +815,7 @@ inline bool splits_cover_k(const TiledCfgRt& cfg, const TiledArgs& a, bool dense
 // their epilogue-free k loop prefers); the other formats are built with the
 // results in ordinary VGPRs, which their per-group epilogues read.
 hipError_t launch_tiled_f16(int fmt, int mode, const TiledCfgRt& cfg, const TiledArgs& a, dim3 grid, hipStream_t s);
+
+#endif  // __HIPCC_RTC__
 
 }  // namespace hq

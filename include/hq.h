@@ -484,6 +484,56 @@ hq_status hq_plan_set_tuning(hq_plan* plan, int64_t m, const hq_tuning* tuning);
  * whether it comes from the table. */
 hq_status hq_plan_get_tuning(const hq_plan* plan, int64_t m, hq_tuning* tuning, int* is_tuned);
 
+/* Run-time specialisation (the pages compile each layer's kernel at run time
+ * for its shape and keep the compiled kernels in a cache: "Humming:
+ * open-source kernel library for quantized inference", news.ditty.ir,
+ * summary; news.cocoloop.cn, limitations section, compile-speed paragraph).
+ * With enable = 1, every hq_gemm on this dense plan runs its kernel compiled
+ * by hipRTC with the call's M, N and K, the format and the resolved execution
+ * choice (heuristic or tuning table) as compile-time constants.  The first
+ * call of a shape on a device compiles it (about a second, host time, on the
+ * calling thread) or loads it from the code-object cache: `cache_dir` (NULL or
+ * "": $HQ_JIT_CACHE_DIR, else $XDG_CACHE_HOME/hq_jit, else
+ * $HOME/.cache/hq_jit), one file per hq_jit_cache_key, written atomically;
+ * an unwritable directory only means the next process compiles again.  The
+ * kernel sources are read from the csrc directory next to the library.
+ * Later calls of the shape launch the loaded kernel (modules stay loaded until
+ * the process ends).  A compile failure makes hq_gemm return
+ * HQ_ERR_UNSUPPORTED with the compiler's log in hq_last_error.  enable = 0
+ * goes back to the precompiled kernels.  Dense plans only; not thread-safe
+ * against concurrent calls on the same plan (like every setter). */
+hq_status hq_plan_set_jit(hq_plan* plan, int enable, const char* cache_dir);
+
+/* The cache key of the kernel hq_gemm runs for m rows under run-time
+ * specialisation on architecture `arch` (e.g. "gfx950"): a NUL-terminated
+ * string of at most 63 characters ("hq-<kernel>-<arch>-<64-bit hex hash>")
+ * that changes with the kernel sources, the compile options, the format, the
+ * shape and the execution choice.  Host only (no device call). */
+hq_status hq_jit_cache_key(const hq_plan* plan, int64_t m, const char* arch, char* key, size_t key_bytes);
+
+/* Compile the kernel hq_gemm would run for m rows under run-time
+ * specialisation, for architecture `arch`, into the plan's code-object cache
+ * directory (hq_plan_set_jit's cache_dir; the plan need not have run-time
+ * specialisation enabled), unless a valid code object is there already.
+ * Needs no device: a cache can be filled ahead of time on another machine.
+ * HQ_ERR_UNSUPPORTED with the compiler's log if the compile fails,
+ * HQ_ERR_INTERNAL if the cache file cannot be written. */
+hq_status hq_jit_prepare(const hq_plan* plan, int64_t m, const char* arch);
+
+/* Counters of the run-time specialisation since the library was loaded:
+ * hipRTC compiles, code objects loaded from the disk cache, launches that found
+ * the kernel already loaded, kernel launches, and the host seconds spent
+ * compiling and loading. */
+typedef struct hq_jit_stats {
+  int64_t compiles;
+  int64_t disk_hits;
+  int64_t memory_hits;
+  int64_t launches;
+  double compile_seconds;
+  double load_seconds;
+} hq_jit_stats;
+hq_status hq_jit_get_stats(hq_jit_stats* stats);
+
 /* Kernel timing: the next hq_gemm, hq_moe_align, hq_moe_gemm,
  * hq_quantize_per_token, hq_quantize_mxfp4, hq_stream_read or hq_mfma_peak call on this
  * thread records `start` (hipEvent_t, created by the caller with timing
