@@ -68,7 +68,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qgemm_decode_sweep_traffic.json")
 
 # sources of the kernels a decode-sweep call runs (GEMM, split-K reduce, their
 # shared headers and launch helper); the plan strings cover the host heuristic
-DECODE_KERNEL_SOURCES = ("csrc/qgemm_skinny.hip", "csrc/qgemm_tiled.hip", "csrc/qgemm_tiled_kernel.h",
+DECODE_KERNEL_SOURCES = ("csrc/qgemm_skinny.hip", "csrc/qgemm_skinny_kernel.h", "csrc/qgemm_tiled.hip",
+                         "csrc/qgemm_tiled_kernel.h",
                          "csrc/splitk_reduce.hip", "csrc/device_common.h", "csrc/hq_internal.h", "csrc/launch.h",
                          "build.py")
 
@@ -153,7 +154,7 @@ def write_profiles(run_dir):
                             plan=plans[j]))
         tot += fb + wb
     cmd = "cd /tmp && rocprofv3 --pmc {c} --output-format csv -d <repo>/gpurun_out/{d} -o {o} -- " \
-          "python3 <repo>/bench.py --steps 3 --warmup 1 --no-cpu"
+          "python3 <repo>/bench.py --steps 3 --warmup 1 --no-cpu --no-extra"
     traffic = {"source_sha256": kernel_source_hash(), "hbm_bytes_per_call": int(tot / n),
                "algorithmic_bytes_per_call": int(sum(algo_bytes(*p) for p in pts) / n),
                "fetch_scale": round(fetch_scale, 4), "write_scale": 1.0,
@@ -187,7 +188,7 @@ def write_profiles(run_dir):
          "uint4 zero points, bf16 output; every call reads its own copy of the weights from a rotating pool (> 1 GB).",
          "", "Kernel trace (from the repository root on the GPU host):", "", "```",
          "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <repo>/gpurun_out/prof_bench -o bench -- \\",
-         "    python3 <repo>/bench.py --steps 20 --warmup 5 --no-cpu",
+         "    python3 <repo>/bench.py --steps 20 --warmup 5 --no-cpu --no-extra",
          "python3 bench.py --write-profiles gpurun_out      # this file and the traffic summary, on the CPU", "```", "",
          "`bench_kernel_stats.csv`, library kernels (every dispatch of the run: eager warm-up, graph replays, "
          "event-timed pass):", "", "| kernel | calls | total ns | average ns | min ns | max ns |", "|---|---|---|---|---|---|"]
@@ -198,10 +199,12 @@ def write_profiles(run_dir):
     L += ["", f"hq_gemm calls in the trace (GEMM dispatch start to the end of its split-K reduce, where there is one): "
               f"the traced run's event-timed pass (its last {len(timed)} calls) averages {mean_timed:.2f} us per call, "
               f"its graph replays {sum(graph) / len(graph):.2f} us, all {len(calls)} calls {sum(dur) / len(dur):.2f} us "
-              f"(the first passes run on cold caches and workspaces).  The bench's own dispatch-bracketing events in "
-              f"the default run (below) give {b['roofline']['mean_kernel_us']:.2f} us per call "
-              f"({100 * (b['roofline']['mean_kernel_us'] / mean_timed - 1):+.1f} % against the traced timed pass, "
-              f"which carries the profiler's overhead).", "",
+              f"(the first passes run on cold caches and workspaces).  The default run below gives "
+              f"{b['roofline']['mean_call_us']:.2f} us per call over its graph-replayed step (the roofline's figure, "
+              f"{100 * (b['roofline']['mean_call_us'] / (sum(graph) / len(graph)) - 1):+.1f} % against the traced "
+              f"graph replays, which carry the profiler's overhead) and "
+              f"{sum(q['kernel_us'] for q in b['points']) / len(b['points']):.2f} us per call from its "
+              f"dispatch-bracketing events.", "",
           f"Bench line (default `python3 bench.py`): {b['value']} GB/s over the step ({b['ms_per_step'] * 1e3:.1f} us "
           f"per step of {n} graph-replayed calls); roofline achieved {b['roofline']['achieved']} GB/s = "
           f"{100 * b['roofline']['frac']:.1f} % of 8 TB/s; CPU oracle {b['cpu_baseline']['value']:.3f} GB/s on "
@@ -286,15 +289,86 @@ def _write_workload_profiles(run_dir, rows):
                         L.append(f"| {p['M']} | {p['out']} | {p['kernel_us']:.2f} | {p['GBps']:.0f} | "
                                  f"{100 * p['hbm_frac']:.1f} |")
                 else:
-                    L += ["| point | us (median) | p10 | p90 | GB/s | TFLOP/s | bound | % of bound | plan |",
-                          "|---|---|---|---|---|---|---|---|---|"]
+                    L += ["Per point: one graph over the point's whole weight pool, the mean pass (us).", "",
+                          "| point | us | GB/s | TFLOP/s | bound | % of bound | plan |",
+                          "|---|---|---|---|---|---|---|"]
                     for p in b["points"]:
-                        L.append(f"| {p['point']} | {p['kernel_us']:.1f} | {p['kernel_us_p10']:.1f} | "
-                                 f"{p['kernel_us_p90']:.1f} | {p['GBps']:.0f} | {p['TFLOPS']:.1f} | {p['bound']} | "
-                                 f"{100 * p['roofline_frac']:.1f} | {p['plan']} |")
+                        L.append(f"| {p['point']} | {p['us']:.1f} | {p['GBps']:.0f} | {p['TFLOPS']:.1f} | "
+                                 f"{p['bound']} | {100 * p['roofline_frac']:.1f} | {p['plan']} |")
         with open(os.path.join(ROOT, "profiles", fname), "w") as f:
             f.write("\n".join(L) + "\n")
         print(f"wrote profiles/{fname}")
+    _write_counter_profiles(run_dir, rows)
+
+
+# Two SQ counter passes of a workload's bench (rocprofv3 collects at most
+# eight SQ counters per pass): sq_<w>_1 and sq_<w>_2 in the run directory.
+SQ_PASSES = ("SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY "
+             "SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU",
+             "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_INSTS_VMEM_RD SQ_INST_LEVEL_VMEM "
+             "SQ_ACTIVE_INST_LDS SQ_WAVES")
+
+
+def _write_counter_profiles(run_dir, rows):
+    """profiles/<workload file>_sq_counters.md: per library kernel, the mean of
+    each SQ counter over its dispatches, and the derived figures."""
+    import collections
+
+    for w, (fname, what) in _WORKLOAD_PROFILES.items():
+        paths = [os.path.join(run_dir, f"sq_{w}_{i}", f"c_counter_collection.csv") for i in (1, 2)]
+        if not all(os.path.exists(x) for x in paths):
+            continue
+        agg = collections.defaultdict(lambda: collections.defaultdict(list))
+        for i in (1, 2):
+            for r in rows(f"sq_{w}_{i}/c_counter_collection.csv"):
+                k = r["Kernel_Name"].split("(")[0]
+                if "hq::" in k:
+                    agg[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        L = [f"# SQ counters: {what}", "", "Two counter passes of the workload's bench (from the repository root on the "
+             "GPU host), then this summary on the CPU:", "", "```"]
+        for i, c in enumerate(SQ_PASSES, 1):
+            L.append(f"cd /tmp && rocprofv3 --pmc {c} --output-format csv -d <repo>/gpurun_out/sq_{w}_{i} -o c -- "
+                     f"python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu")
+        means = {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in agg.items()}
+
+        def busy_ratio(m):
+            return m.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / max(m.get("SQ_BUSY_CYCLES", 0.0), 1.0)
+
+        # the register-only matrix-core probe of each operand type, from the same run
+        probe = {int(k.split("<")[1].split(">")[0]): busy_ratio(m) for k, m in means.items()
+                 if "mfma_peak_kernel<" in k}
+        # kernel format (first template argument) -> probe type (f16 0, bf16 1, fp8 2, fp8 x fp4 3, fp4 4, int8 5)
+        fmt_probe = {0: 0, 1: 1, 2: 5, 3: 2, 4: 3, 5: 4}
+        L += ["python3 bench.py --write-profiles gpurun_out", "```", "",
+              "Per kernel, the means over its dispatches, as unit-free ratios: VALU instructions per MFMA; LDS bank "
+              "conflicts per LDS instruction; the share of the waves' time spent waiting (SQ_WAIT_ANY / "
+              "SQ_WAVE_CYCLES) and issuing (SQ_ACTIVE_INST_ANY / SQ_WAVE_CYCLES); and the matrix cores' busy time "
+              "relative to the SQ's busy time (SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CYCLES), also as a fraction of the "
+              "same ratio for the library's register-only matrix-core probe of the kernel's operand type in the "
+              "same run (`mfma_peak_kernel<type>`, types f16 0, bf16 1, fp8 2, fp8 x fp4 3, fp4 4, int8 5).", "",
+              "| kernel | dispatches | waves | MFMA instr | VALU / MFMA | bank conflicts / LDS instr | waiting share | "
+              "issuing share | MFMA busy / SQ busy | of the probe's |",
+              "|---|---|---|---|---|---|---|---|---|---|"]
+        for k, m in sorted(means.items()):
+            n = max(len(v) for v in agg[k].values())
+            wc = max(m.get("SQ_WAVE_CYCLES", 0.0), 1.0)
+            mf = m.get("SQ_INSTS_MFMA", 0.0)
+            vpm = f"{m.get('SQ_INSTS_VALU', 0.0) / mf:.2f}" if mf else "-"
+            bc = m.get("SQ_LDS_BANK_CONFLICT", 0.0) / max(m.get("SQ_INSTS_LDS", 0.0), 1.0)
+            br = busy_ratio(m)
+            rel = "-"
+            if ("qgemm" in k or "smallk" in k) and "<" in k:
+                fmt = int(k.split("<")[1].split(",")[0])
+                ptype = fmt_probe.get(fmt, 0 if fmt % 2 == 0 else 1)
+                if probe.get(ptype):
+                    rel = f"{br / probe[ptype]:.2f}"
+            L.append(f"| `{k[:80]}` | {n} | {m.get('SQ_WAVES', 0.0):.0f} | {mf:.0f} | {vpm} | {bc:.3f} | "
+                     f"{m.get('SQ_WAIT_ANY', 0.0) / wc:.2f} | {m.get('SQ_ACTIVE_INST_ANY', 0.0) / wc:.2f} | {br:.3f} | "
+                     f"{rel} |")
+        out = fname.replace(".md", "_sq_counters.md")
+        with open(os.path.join(ROOT, "profiles", out), "w") as f:
+            f.write("\n".join(L) + "\n")
+        print(f"wrote profiles/{out}")
 
 
 def algo_bytes(M, N, K):
