@@ -90,10 +90,13 @@ struct TCfg {
 
 // Physical 16-byte chunk of logical chunk c in row r (CH chunks per row):
 // the 16 rows an MFMA operand reads at one logical chunk land on distinct
-// banks.
+// banks.  Measured with SQ_LDS_BANK_CONFLICT on gfx950: for 64-byte rows
+// (MXFP4 activations) the XOR with (r >> 1) & 3 reads without conflicts,
+// where (r >> 2) & 3, r & 3 and (r ^ (r >> 2)) & 3 each cost four conflict
+// cycles per 16-byte read.
 template <int CH>
 __device__ inline int swz(int r, int c) {
-  return CH == 16 ? (c ^ (r & 15)) : (CH == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3)));
+  return CH == 16 ? (c ^ (r & 15)) : (CH == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 1) & 3)));
 }
 
 // s_waitcnt: at most N (< 64) vector-memory loads of this wave still in
