@@ -994,12 +994,13 @@ def _w4a4_points(dev):
         "E8M0 scales per 32), bf16 output", "f4"
 
 
-def _moe_points(dev, Ts=(1, 32, 512, 4096), acts=("bf16", "fp8")):
+def _moe_points(dev, Ts=(1, 32, 512, 4096), acts=("bf16", "fp8"), slot_Ts=(1, 4, 8, 32)):
     import bit_quantized_gemm_repack_amd as hq
     import datagen
 
     E, H, I, topk = 256, 7168, 256, 8
     wts = datagen.moe_weights(E, H, I, key=(5,))
+    per_expert = 2 * I * H // 2 + 2 * (2 * I) * (H // 128) + H * I // 2 + 2 * H * (I // 128)
     pts = []
     for act in acts:
         q = hq.w4a16("bf16", scale="f16") if act == "bf16" else hq.w4a8_fp8(scale="f16")
@@ -1007,13 +1008,27 @@ def _moe_points(dev, Ts=(1, 32, 512, 4096), acts=("bf16", "fp8")):
         p2 = hq.MoePlan(H, I, q, E, 4096, "topk_combine")
         w1, m1 = p1.repack(torch.from_numpy(wts["w1"]).to(dev), wts["s1"].to(dev))
         w2, m2 = p2.repack(torch.from_numpy(wts["w2"]).to(dev), wts["s2"].to(dev))
-        R = 2  # two copies of the 727 MB expert weights: > 1 GB
-        cp = [(w1, m1, w2, m2)] + [(w1.clone(), m1.clone(), w2.clone(), m2.clone()) for _ in range(R - 1)]
+        C = 2  # two copies of the 727 MB expert weights: > 1 GB
+        cp = [(w1, m1, w2, m2)] + [(w1.clone(), m1.clone(), w2.clone(), m2.clone()) for _ in range(C - 1)]
+        abytes = 2 if act == "bf16" else 1
+
+        def routings(T):
+            # A pass touches only its routed experts' weights: at small T
+            # those of one routing would stay in the 256 MB last-level cache
+            # from pass to pass, so the passes cycle through several routings
+            # (and both weight copies) until a graph touches >= 600 MB.
+            first = datagen.moe_routing(T)
+            hit0 = int(np.unique(first["topk_ids"]).size)
+            n = int(min(16, max(1, -(-600e6 // (C * hit0 * per_expert)))))
+            rts = [first] + [datagen.moe_routing(T, key=(5, j)) for j in range(1, n)]
+            hit = float(np.mean([np.unique(rt["topk_ids"]).size for rt in rts]))
+            ids = [torch.from_numpy(rt["topk_ids"]).to(dev) for rt in rts]
+            tw = [torch.from_numpy(rt["topk_w"]).to(dev) for rt in rts]
+            return n, hit, ids, tw
+
         for T in Ts:
-            rt = datagen.moe_routing(T)
+            n_rt, hit, ids, tw = routings(T)
             x = datagen.moe_activations(T, act=act)
-            ids = torch.from_numpy(rt["topk_ids"]).to(dev)
-            tw = torch.from_numpy(rt["topk_w"]).to(dev)
             xa = (x["x"] if act == "bf16" else x["x_codes"]).to(dev)
             xs = None if act == "bf16" else x["x_scale"].to(dev)
             bm = p1.block_m(T, topk)
@@ -1025,39 +1040,77 @@ def _moe_points(dev, Ts=(1, 32, 512, 4096), acts=("bf16", "fp8")):
             iscale = None if act == "bf16" else torch.empty(mp, dtype=torch.float32, device=dev)
             y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
             ws1, ws2 = p1.moe_workspace(T, topk, dev), p2.moe_workspace(T, topk, dev)
-            hit = int(np.unique(rt["topk_ids"]).size)
-            wbytes = hit * (2 * I * H // 2 + 2 * (2 * I) * (H // 128) + H * I // 2 + 2 * H * (I // 128))
-            abytes = 2 if act == "bf16" else 1
-            # A once (+ scale), the intermediate written once and read once, y once
-            byt = wbytes + T * H * abytes + (4 * T if act == "fp8" else 0) + 2 * T * topk * I * abytes + 2 * T * H
+            # weights of the experts hit (mean over the routings), A once (+
+            # scale), the intermediate written once and read once, y once
+            byt = int(hit * per_expert) + T * H * abytes + (4 * T if act == "fp8" else 0) + \
+                2 * T * topk * I * abytes + 2 * T * H
             flops = 2 * T * topk * (2 * I * H + H * I)
 
             def calls(r, cp=cp, ids=ids, tw=tw, xa=xa, xs=xs, bm=bm, sid=sid, bex=bex, npad=npad, inter=inter,
-                      iscale=iscale, y=y, ws1=ws1, ws2=ws2, T=T, p1=p1, p2=p2, act=act):
-                w1_, m1_, w2_, m2_ = cp[r]
+                      iscale=iscale, y=y, ws1=ws1, ws2=ws2, T=T, p1=p1, p2=p2):
+                w1_, m1_, w2_, m2_ = cp[r % C]
+                ids_, tw_ = ids[r // C], tw[r // C]
                 L = hq.lib()
 
                 def align():
-                    hq._check(L.hq_moe_align(T, topk, E, bm, hq._ptr(ids), hq._ptr(sid), hq._ptr(bex),
-                                             hq._ptr(npad), hq._stream_ptr(ids.device)))
+                    hq._check(L.hq_moe_align(T, topk, E, bm, hq._ptr(ids_), hq._ptr(sid), hq._ptr(bex),
+                                             hq._ptr(npad), hq._stream_ptr(ids_.device)))
 
                 def gate_up():
                     p1.moe_gemm(xa, T, topk, sid, bex, npad, w1_, m1_, a_scale=xs, out=inter, out_scale=iscale,
                                 ws=ws1)
 
                 def down():
-                    p2.moe_gemm(inter, T, topk, sid, bex, npad, w2_, m2_, a_scale=iscale, topk_w=tw, out=y, ws=ws2)
+                    p2.moe_gemm(inter, T, topk, sid, bex, npad, w2_, m2_, a_scale=iscale, topk_w=tw_, out=y, ws=ws2)
 
                 return [align, gate_up, down]
 
-            pts.append(dict(name=f"{act} T={T} (experts hit {hit})", R=R, bytes=byt, flops=flops,
-                            peak=FP16_PEAK_TFLOPS if act == "bf16" else FP8_PEAK_TFLOPS,
+            pts.append(dict(name=f"{act} T={T} (experts hit {hit:.0f}, {n_rt} routings)", R=C * n_rt, bytes=byt,
+                            flops=flops, peak=FP16_PEAK_TFLOPS if act == "bf16" else FP8_PEAK_TFLOPS,
                             mfma="bf16" if act == "bf16" else "fp8",
                             plan=f"gate_up: {p1.describe(T, topk)} | down: {p2.describe(T, topk)}", calls=calls))
+        for T in slot_Ts:
+            # the unaligned path: rows indexed by routed slot, no align launch
+            n_rt, hit, ids, tw = routings(T)
+            x = datagen.moe_activations(T, act=act)
+            xa = (x["x"] if act == "bf16" else x["x_codes"]).to(dev)
+            xs = None if act == "bf16" else x["x_scale"].to(dev)
+            S = T * topk
+            inter = torch.empty((S, I), dtype=torch.bfloat16 if act == "bf16" else torch.uint8, device=dev)
+            iscale = None if act == "bf16" else torch.empty(S, dtype=torch.float32, device=dev)
+            y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+            ws1 = p1.moe_workspace(T, topk, dev) if act == "fp8" else None
+            # the experts hit once each (an expert picked by two slots is read
+            # twice, from the cache the second time: not counted), A, the slot
+            # rows written and read, y
+            byt = int(hit * per_expert) + T * H * abytes + (4 * T if act == "fp8" else 0) + \
+                2 * S * I * abytes + 2 * T * H
+            flops = 2 * S * (2 * I * H + H * I)
+
+            def calls(r, cp=cp, ids=ids, tw=tw, xa=xa, xs=xs, inter=inter, iscale=iscale, y=y, ws1=ws1, T=T,
+                      p1=p1, p2=p2):
+                w1_, m1_, w2_, m2_ = cp[r % C]
+                ids_, tw_ = ids[r // C], tw[r // C]
+
+                def gate_up():
+                    p1.moe_gemm_by_slot(xa, T, topk, ids_, w1_, m1_, a_scale=xs, out=inter, out_scale=iscale,
+                                        ws=ws1)
+
+                def down():
+                    p2.moe_gemm_by_slot(inter, T, topk, ids_, w2_, m2_, a_scale=iscale, topk_w=tw_, out=y)
+
+                return [gate_up, down]
+
+            pts.append(dict(name=f"{act} T={T} by slot (experts hit {hit:.0f}, {n_rt} routings)", R=C * n_rt,
+                            bytes=byt, flops=flops, peak=FP16_PEAK_TFLOPS if act == "bf16" else FP8_PEAK_TFLOPS,
+                            mfma="bf16" if act == "bf16" else "fp8",
+                            plan="gate_up + down by slot (skinny kernel, slot and token modes)", calls=calls))
     return pts, "MoE layer TFLOPS and effective HBM GB/s vs T", \
         "MoE layer on one GPU's tensor-parallel share: 256 experts, top-8, hidden 7168, intermediate 256; " \
         "align + gate_up (SiLU * up; bf16, or fp8 requant for W4A8-FP8) + down with the top-k combine; INT4 " \
-        "weights (group 128, fp16 scales, zero point 8); T in {1,32,512,4096}", "bf16/f8"
+        "weights (group 128, fp16 scales, zero point 8); T in {1,32,512,4096}; the unaligned by-slot path " \
+        "(gate_up + down, no align) at T in {1,4,8,32}; small T cycles through routings so passes stay cold", \
+        "bf16/f8"
 
 
 def graph_time_point(p, steps, warmup):
@@ -1200,8 +1253,9 @@ def run_points_workload(args, builder):
 EXTRA = (("prefill_f16_M4096", "prefill", lambda dev: _prefill_points(dev, Ms=(4096,))),
          ("w4a8_mxfp4_fp8_M1024", "w4a8", lambda dev: _w4a8_points(dev, Ms=(1024,), kinds=("mxfp4",))),
          ("w4a8_int4_int8_M1024", "w4a8int", lambda dev: _w4a8_points(dev, Ms=(1024,), kinds=("int",))),
-         ("moe_bf16_T4096", "moe", lambda dev: _moe_points(dev, Ts=(4096,), acts=("bf16",))),
-         ("moe_fp8_T4096", "moe", lambda dev: _moe_points(dev, Ts=(4096,), acts=("fp8",))))
+         ("moe_bf16_T4096", "moe", lambda dev: _moe_points(dev, Ts=(4096,), acts=("bf16",), slot_Ts=())),
+         ("moe_fp8_T4096", "moe", lambda dev: _moe_points(dev, Ts=(4096,), acts=("fp8",), slot_Ts=())),
+         ("moe_bf16_T1_by_slot", "moe", lambda dev: _moe_points(dev, Ts=(), acts=("bf16",), slot_Ts=(1,))))
 
 
 def measure_extra(args, dev, hip, L, cpu_budget):

@@ -187,6 +187,8 @@ _SIGS = {
                                               ctypes.POINTER(ctypes.c_size_t)]),
     "hq_moe_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int] + [ctypes.c_void_p] * 11 +
                     [ctypes.c_size_t, ctypes.c_void_p]),
+    "hq_moe_gemm_by_slot": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int] + [ctypes.c_void_p] * 9 +
+                            [ctypes.c_size_t, ctypes.c_void_p]),
     "hq_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
                                       ctypes.c_void_p]),
     "hq_mfma_peak": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
@@ -719,4 +721,34 @@ class MoePlan(Plan):
         _check(lib().hq_moe_gemm(self._h, int(t), int(topk), _ptr(a), _ptr(a_scale), _ptr(sorted_ids),
                                  _ptr(block_expert), _ptr(num_padded), _ptr(topk_w), _ptr(w), _ptr(meta), _ptr(out),
                                  _ptr(out_scale), _ptr(ws), ws_bytes, _stream_ptr(dev)))
+        return (out, out_scale) if self.epi == EPI_SILU_MUL_QFP8 else out
+
+    def moe_gemm_by_slot(self, a: torch.Tensor, t: int, topk: int, topk_ids: torch.Tensor, w: torch.Tensor,
+                         meta: torch.Tensor, a_scale=None, topk_w=None, out=None, out_scale=None, ws=None):
+        """hq_moe_gemm_by_slot: the grouped GEMM with rows indexed by routed
+        slot (no alignment).  gate_up returns [t*topk, n/2] (fp8: codes and
+        per-slot scales); down takes those slot rows and returns y [t, n]."""
+        for x, nm in ((a, "a"), (topk_ids, "topk_ids"), (w, "w"), (meta, "meta")):
+            _dev(x, nm)
+        dev = a.device
+        slots = int(t) * int(topk)
+        if topk_ids.numel() < slots:
+            raise ValueError(f"topk_ids holds {topk_ids.numel()} ids, t * topk = {slots}")
+        if out is None:
+            if self.epi == EPI_TOPK_COMBINE:
+                out = torch.empty((t, self.n), dtype=_TORCH_OUT[self.quant.out], device=dev)
+            elif self.epi == EPI_SILU_MUL_QFP8:
+                out = torch.empty((slots, self.n // 2), dtype=torch.uint8, device=dev)
+            elif self.epi == EPI_SILU_MUL:
+                out = torch.empty((slots, self.n // 2), dtype=_TORCH_OUT[self.quant.out], device=dev)
+            else:
+                out = torch.empty((slots, self.n), dtype=_TORCH_OUT[self.quant.out], device=dev)
+        if self.epi == EPI_SILU_MUL_QFP8 and out_scale is None:
+            out_scale = torch.empty(slots, dtype=torch.float32, device=dev)
+        if ws is None and self.epi == EPI_SILU_MUL_QFP8:
+            ws = self.moe_workspace(t, topk, dev)
+        ws_bytes = 0 if ws is None else ws.numel()
+        _check(lib().hq_moe_gemm_by_slot(self._h, int(t), int(topk), _ptr(a), _ptr(a_scale), _ptr(topk_ids),
+                                         _ptr(topk_w), _ptr(w), _ptr(meta), _ptr(out), _ptr(out_scale), _ptr(ws),
+                                         ws_bytes, _stream_ptr(dev)))
         return (out, out_scale) if self.epi == EPI_SILU_MUL_QFP8 else out

@@ -474,8 +474,9 @@ hq_status hq_plan_create(const hq_layer_desc* layer, const hq_compute* compute, 
           return fail(HQ_ERR_UNSUPPORTED, "the skinny grouped kernel uses 16- or 32-row blocks");
         if (tuning->kernel == hq::KER_TILED && (tm == 16 || tm == 32))
           return fail(HQ_ERR_UNSUPPORTED, "the tiled grouped kernel uses 64- or 128-row blocks");
-        if (tn != 0 && tn != 128 && tn != 256)
-          return fail(HQ_ERR_UNSUPPORTED, "grouped tile_n must be 128 or 256");
+        if (tn != 0 && tn != 16 && tn != 32 && tn != 64 && tn != 128 && tn != 256)
+          return fail(HQ_ERR_UNSUPPORTED, "grouped tile_n must be 128 or 256 (tiled), 16, 32 or 64 (by slot)");
+        if (tuning->waves < 0 || tuning->waves > 16) return fail(HQ_ERR_UNSUPPORTED, "grouped waves must be 1..16");
         if (tn != 0 && layer->n % tn) return fail(HQ_ERR_UNSUPPORTED, "n must be a multiple of tile_n");
       }
     }
@@ -877,7 +878,7 @@ static MoeChoice moe_choice(const hq_plan* p, int64_t t, int topk) {
   }
   c.bm = u.tile_m >= 64 ? u.tile_m : (per_expert >= 192.0 ? 128 : 64);
   int nbw;
-  if (u.tile_n) nbw = u.tile_n / 64;
+  if (u.tile_n >= 128) nbw = u.tile_n / 64;  // smaller tile_n values are the by-slot kernel's
   else nbw = (N % 256 == 0) ? 4 : 2;
   if (N % (64 * nbw)) nbw = 2;
   c.tl.bm = c.bm;
@@ -1176,6 +1177,121 @@ hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, cons
     return ok();
   } catch (...) {
     return fail(HQ_ERR_INTERNAL, "exception in hq_moe_gemm");
+  }
+}
+
+hq_status hq_moe_gemm_by_slot(const hq_plan* p, int64_t t, int topk, const void* a, const float* a_scale,
+                              const int32_t* topk_ids, const float* topk_w, const void* w, const void* meta,
+                              void* out, float* out_scale, void* ws, size_t ws_bytes, void* stream) {
+  const hq::TimingEvents ev = hq::take_timing();  // consumed by this call whatever happens
+  try {
+    if (!p) return fail(HQ_ERR_INVALID_ARG, "null plan");
+    if (p->compute.kind != HQ_GEMM_GROUPED) return fail(HQ_ERR_INVALID_ARG, "hq_moe_gemm_by_slot needs a grouped plan");
+    if (t < 0 || t > p->max_m) return fail(HQ_ERR_INVALID_ARG, "t out of range [0, max_m]");
+    if (topk < 1 || topk > 64) return fail(HQ_ERR_INVALID_ARG, "topk must be 1..64");
+    if (t == 0) return ok();
+    if (t * topk > 65535) return fail(HQ_ERR_UNSUPPORTED, "t * topk must be at most 65535 on this path");
+    if (!a || !topk_ids || !w || !meta || !out) return fail(HQ_ERR_INVALID_ARG, "null device pointer");
+    if (!aligned16(a) || !aligned16(w) || !aligned16(meta) || !aligned16(out))
+      return fail(HQ_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+    const bool act8 = p->fmt == hq::FMT_Q8;
+    if (act8 && !a_scale) return fail(HQ_ERR_INVALID_ARG, "8-bit activations need a_scale");
+    if (!act8 && a_scale) return fail(HQ_ERR_INVALID_ARG, "16-bit activations take no a_scale");
+    const int epi = p->compute.epi;
+    if (epi == HQ_EPI_TOPK_COMBINE && !topk_w) return fail(HQ_ERR_INVALID_ARG, "the combine needs topk_w");
+    if (epi == HQ_EPI_SILU_MUL_QFP8 && !out_scale) return fail(HQ_ERR_INVALID_ARG, "fp8 requant needs out_scale");
+    const int64_t N = p->layer.n, K = p->layer.k, G = K / 128, E = p->layer.num_experts;
+    const int n_slots = (int)(t * topk);
+    const bool token = epi == HQ_EPI_TOPK_COMBINE;
+    const size_t need = epi == HQ_EPI_SILU_MUL_QFP8 ? align256((size_t)n_slots * (size_t)(N / 2) * 4) : 0;
+    if (need > 0) {
+      if (!ws) return fail(HQ_ERR_WORKSPACE, "this call needs %zu workspace bytes", need);
+      if (ws_bytes < need) return fail(HQ_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, need);
+      if (!aligned16(ws)) return fail(HQ_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    }
+    {
+      // 32-bit buffer ranges: the activation rows, and one expert's weights
+      // (token mode: all experts' weights and scales, the step picks one)
+      const int64_t act_bytes = act8 ? 1 : 2;
+      const int64_t wexp = (int64_t)p->w_bytes_per_expert;
+      if ((token ? n_slots : t) * K * act_bytes >= (int64_t(1) << 31) ||
+          (token ? E * wexp : wexp) >= (int64_t(1) << 31) || (token ? E * N * G * 2 : 0) >= (int64_t(1) << 31))
+        return fail(HQ_ERR_UNSUPPORTED, "activations or the weights one launch addresses must stay below 2 GiB");
+    }
+    hq::SkinnyCfg c{};
+    c.mb = 1;
+    c.stages = 2;
+    c.split = 1;
+    {
+      // defaults measured on MI355X at H = 7168, I = 256, topk 8; the plan's
+      // tile_n (16, 32, 64) and waves (1..16) override them where they fit
+      const hq_tuning& u = p->user;
+      const bool paired = !token && (epi == HQ_EPI_SILU_MUL || epi == HQ_EPI_SILU_MUL_QFP8);
+      c.nb = 2;
+      if (u.tile_n == 16 || u.tile_n == 32 || u.tile_n == 64) c.nb = u.tile_n / 16;
+      if (paired && c.nb < 2) c.nb = 2;
+      while (c.nb > 1 && (paired ? (N / 2) % (16 * (c.nb / 2)) : N % (16 * c.nb))) c.nb /= 2;
+      if (paired && c.nb < 2) return fail(HQ_ERR_UNSUPPORTED, "gate_up needs n / 2 to be a multiple of 16");
+      const int64_t steps = token ? topk * G : G;
+      c.waves = (u.waves >= 1 && u.waves <= 16) ? u.waves : (int)std::min<int64_t>(8, steps);
+    }
+    const uint32_t* zeros = p->layer.q.zp == HQ_ZP_PER_GROUP_U4
+                                ? reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(meta) +
+                                                                    p->scale_region_bytes * (size_t)E)
+                                : nullptr;
+    int gepi = hq::GEPI_PLAIN;
+    float* f32_out = nullptr;
+    switch (epi) {
+      case HQ_EPI_NONE: gepi = hq::GEPI_PLAIN; break;
+      case HQ_EPI_SILU_MUL: gepi = hq::GEPI_SILU; break;
+      case HQ_EPI_SILU_MUL_QFP8:
+        gepi = hq::GEPI_SILU_F32;
+        f32_out = static_cast<float*>(ws);
+        break;
+      case HQ_EPI_TOPK_COMBINE: gepi = hq::GEPI_COMBINE; break;
+      default: return fail(HQ_ERR_INVALID_ARG, "unsupported grouped epilogue");
+    }
+    hq::SkinnyArgs s{};
+    s.a = a;
+    s.a_scale = a_scale;
+    s.w = w;
+    s.scales = meta;
+    s.zeros = zeros;
+    s.out = out;
+    s.M = token ? (int)t : n_slots;
+    s.N = (int)N;
+    s.K = (int)K;
+    s.G = (int)(token ? topk * G : G);  // token mode: topk slots of K / 128 groups each
+    s.gps = s.G;
+    s.ge = (int)G;
+    s.zp_fixed = p->layer.q.zp == HQ_ZP_FIXED ? p->layer.q.zp_value : -1;
+    s.scale_bf16 = p->layer.q.scale == HQ_BF16;
+    s.out_bf16 = p->layer.q.out == HQ_BF16;
+    s.topk_ids = topk_ids;
+    s.num_experts = (int)E;
+    s.topk_w = topk_w;
+    s.topk = topk;
+    s.n_slots = n_slots;
+    s.epi = gepi;
+    s.half_nblk = (int)(N / 2 / 16);
+    s.w_expert = (int64_t)p->w_bytes_per_expert;
+    s.s_expert = (int64_t)(N * G);
+    s.z_expert = (int64_t)((N / 16) * G * 2);
+    s.e8_expert = (int64_t)(N * K / 32);
+    s.f32_out = f32_out;
+    const bool requant = epi == HQ_EPI_SILU_MUL_QFP8;
+    hq::arm_timing({ev.start, requant ? nullptr : ev.stop});
+    int err = hq::launch_skinny_byslot(p->fmt, token ? hq::GRP_TOKEN : hq::GRP_SLOT, c, s, token ? t : n_slots,
+                                       stream);
+    hq::arm_timing({nullptr, ev.stop});
+    if (err == hipSuccess && requant)
+      err = hq::launch_moe_requant(f32_out, nullptr, nullptr, n_slots, (int)(N / 2), n_slots,
+                                   static_cast<uint8_t*>(out), out_scale, stream);
+    hq::arm_timing({nullptr, nullptr});
+    if (err != hipSuccess) return fail(HQ_ERR_HIP, "grouped gemm launch: %s", hipGetErrorString((hipError_t)err));
+    return ok();
+  } catch (...) {
+    return fail(HQ_ERR_INTERNAL, "exception in hq_moe_gemm_by_slot");
   }
 }
 

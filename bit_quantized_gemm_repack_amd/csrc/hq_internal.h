@@ -404,13 +404,22 @@ struct SkinnyArgs {
   // small-K down GEMM: this launch covers columns [col0, col0 + ncol) of N
   // and stores slot rows [n_slots][ncol] (0, 0: all of N)
   int col0, ncol;
+  // slot / token modes: the routing and the experts' layout
+  const int32_t* topk_ids;  // [t][topk]
+  int num_experts;
+  int ge;                   // groups per expert (token mode: G = topk * ge)
 };
 
 // Grouped epilogues (SkinnyArgs::epi / TiledArgs::epi).
 enum GroupedEpi : int { GEPI_PLAIN = 0, GEPI_SILU = 1, GEPI_SILU_F32 = 2, GEPI_COMBINE = 3 };
 // Grouped kernel modes (template parameter): 0 dense, 1 rows gathered by
 // token (gate_up), 2 rows in aligned order (down).
-enum GroupedMode : int { GRP_DENSE = 0, GRP_GATHER = 1, GRP_SORTED = 2 };
+// 3 (skinny kernel, few tokens): block z is routed slot z, its expert read from
+// topk_ids, its row token z / topk, gate_up output row z; 4 (skinny kernel,
+// few tokens): block z is token z, the k loop walks its topk slots' rows and
+// experts (groups g: slot g / ge, group g % ge), the top-k weight folded into
+// each group's scale, so the workgroup's reduction is the combine.
+enum GroupedMode : int { GRP_DENSE = 0, GRP_GATHER = 1, GRP_SORTED = 2, GRP_SLOT = 3, GRP_TOKEN = 4 };
 
 #ifndef __HIPCC_RTC__
 int launch_skinny(int fmt, const SkinnyCfg& cfg, const SkinnyArgs& a, void* stream);
@@ -422,11 +431,17 @@ int launch_smallk_grouped(int fmt, int mb, const SkinnyArgs& a, int64_t blocks, 
 // Grouped launch: grid.z = blocks of the aligned array (max_padded / (16 mb)).
 int launch_skinny_grouped(int fmt, int mode, const SkinnyCfg& cfg, const SkinnyArgs& a, int64_t blocks,
                           void* stream);
+// Unaligned grouped launch (GRP_SLOT: grid.z = routed slots; GRP_TOKEN:
+// grid.z = tokens): mb 1, stages 2, up to 16 waves; fp16 / bf16 / fp8
+// activations.
+int launch_skinny_byslot(int fmt, int mode, const SkinnyCfg& cfg, const SkinnyArgs& a, int64_t blocks,
+                         void* stream);
 int launch_moe_align(int64_t t, int topk, int num_experts, int block_m, const int32_t* ids, int32_t* sorted_ids,
                      int32_t* block_expert, int32_t* num_padded, void* stream);
+// Per-row fp8 requantisation of the gate_up epilogue's fp32 rows; with null
+// sorted_ids and num_padded the rows are the slots themselves (max_rows of them).
 int launch_moe_requant(const float* act32, const int32_t* sorted_ids, const int32_t* num_padded, int n_slots,
                        int inter, int64_t max_rows, uint8_t* codes, float* scales, void* stream);
-// y[t][n] = RNE(sum over the token's topk weighted slot rows), rows [t*topk][n] fp32
 // y[t][col0 + c] = RNE(sum over the token's topk weighted slot rows), rows
 // [t*topk][ncol] fp32 (summed in slot order), c < ncol; y row stride n.
 int launch_moe_combine(const float* rows, int topk, int64_t t, int64_t n, int64_t col0, int64_t ncol, void* y,

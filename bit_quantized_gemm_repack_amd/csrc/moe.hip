@@ -105,7 +105,9 @@ __global__ void __launch_bounds__(1024) moe_align_kernel(const int32_t* __restri
 // s) with a correctly rounded fp32 quotient, saturated to +-448 -- the rule of
 // the standalone per-token quantiser (quantize.hip).  The row maximum is
 // formed here from the stored row (two passes over 4 * inter bytes, the
-// second from the cache), so no state carries over between calls.
+// second from the cache), so no state carries over between calls.  Rows are
+// aligned positions (padding skipped), or slots when sorted_ids and
+// num_padded are null.
 __global__ void __launch_bounds__(256) moe_requant_kernel(const float* __restrict__ act32,
                                                           const int32_t* __restrict__ sorted_ids,
                                                           const int32_t* __restrict__ num_padded, int n_slots,
@@ -113,8 +115,8 @@ __global__ void __launch_bounds__(256) moe_requant_kernel(const float* __restric
                                                           float* __restrict__ scales) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (row >= max_rows || row >= *num_padded) return;
-  if (sorted_ids[row] >= n_slots) return;
+  if (row >= max_rows || (num_padded && row >= *num_padded)) return;
+  if (sorted_ids && sorted_ids[row] >= n_slots) return;
   const float* a = act32 + row * inter;
   float amax = 0.f;
   for (int col = lane; col < inter; col += 64) amax = fmaxf(amax, fabsf(a[col]));

@@ -97,6 +97,44 @@ int launch_skinny_grouped(int fmt, int mode, const SkinnyCfg& cfg, const SkinnyA
   return (int)hipErrorInvalidValue;
 }
 
+// Slot and token modes (no alignment): one row per block, up to 16 waves.
+template <int FMT, int GRP>
+static hipError_t launch_byslot_t(const SkinnyCfg& cfg, const SkinnyArgs& a, dim3 grid, dim3 block, size_t lds,
+                                  hipStream_t s) {
+  if (cfg.stages != 2 || cfg.mb != 1 || cfg.waves > 16) return hipErrorInvalidValue;
+  if constexpr (GRP == GRP_TOKEN)
+    if (cfg.nb == 1) return launch_kernel(qgemm_skinny<FMT, 1, 1, 2, 1024, GRP>, grid, block, lds, s, a);
+  if (cfg.nb == 2) return launch_kernel(qgemm_skinny<FMT, 1, 2, 2, 1024, GRP>, grid, block, lds, s, a);
+  if (cfg.nb == 4) return launch_kernel(qgemm_skinny<FMT, 1, 4, 2, 1024, GRP>, grid, block, lds, s, a);
+  return hipErrorInvalidValue;
+}
+
+int launch_skinny_byslot(int fmt, int mode, const SkinnyCfg& cfg, const SkinnyArgs& a, int64_t blocks,
+                         void* stream) {
+  if (a.G < 1 || a.gps != a.G || cfg.split != 1 || blocks < 1 || blocks > 65535) return (int)hipErrorInvalidValue;
+  if (mode != GRP_SLOT && mode != GRP_TOKEN) return (int)hipErrorInvalidValue;
+  const bool paired = mode == GRP_SLOT && (a.epi == GEPI_SILU || a.epi == GEPI_SILU_F32);
+  if (paired && cfg.nb < 2) return (int)hipErrorInvalidValue;
+  const int ntiles = paired ? (a.N / 2) / (16 * (cfg.nb / 2)) : a.N / (16 * cfg.nb);
+  dim3 grid(ntiles, 1, (unsigned)blocks);
+  dim3 block(64 * cfg.waves);
+  const size_t lds = (size_t)cfg.waves * cfg.mb * cfg.nb * 4 * 64 * sizeof(float);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool slot = mode == GRP_SLOT;
+  switch (fmt) {
+    case FMT_W16F16:
+      return (int)(slot ? launch_byslot_t<FMT_W16F16, GRP_SLOT>(cfg, a, grid, block, lds, s)
+                        : launch_byslot_t<FMT_W16F16, GRP_TOKEN>(cfg, a, grid, block, lds, s));
+    case FMT_W16BF16:
+      return (int)(slot ? launch_byslot_t<FMT_W16BF16, GRP_SLOT>(cfg, a, grid, block, lds, s)
+                        : launch_byslot_t<FMT_W16BF16, GRP_TOKEN>(cfg, a, grid, block, lds, s));
+    case FMT_Q8:
+      return (int)(slot ? launch_byslot_t<FMT_Q8, GRP_SLOT>(cfg, a, grid, block, lds, s)
+                        : launch_byslot_t<FMT_Q8, GRP_TOKEN>(cfg, a, grid, block, lds, s));
+  }
+  return (int)hipErrorInvalidValue;
+}
+
 int launch_skinny(int fmt, const SkinnyCfg& cfg, const SkinnyArgs& a, void* stream) {
   // every split holds at least one group, and the splits cover K
   if (a.G < 1 || a.gps < 1 || (int64_t)(cfg.split - 1) * a.gps >= a.G || (int64_t)cfg.split * a.gps < a.G)

@@ -66,6 +66,7 @@ struct Stage {
   uint32_t sraw[NB];  // scale bits, or the E8M0 byte
   uint32_t zraw[NB];  // zero-point word (8 nibbles), unused with a fixed zero
   uint32_t asc[MB];   // MXFP4 activations: the row's four E8M0 block scales of the group
+  float gw;           // token mode: the step's top-k weight (times its slot row's scale)
 };
 
 template <int FMT>
@@ -75,8 +76,13 @@ __device__ inline f4_t mfma16(u4_t a, u4_t b, f4_t c) {
 
 // GRP selects the row / weight indexing: GRP_DENSE (rows 0..M-1, one weight),
 // GRP_GATHER (MoE gate_up: block z of the expert-aligned slot array, rows are
-// the slots' tokens, weights of the block's expert) or GRP_SORTED (MoE down:
-// rows are the aligned slots themselves).
+// the slots' tokens, weights of the block's expert), GRP_SORTED (MoE down:
+// rows are the aligned slots themselves), GRP_SLOT (gate_up without the
+// alignment: block z is routed slot z, one row, its token's activations
+// against its expert's weights, output row z) or GRP_TOKEN (down and combine
+// in one: block z is token z and its k loop runs over the token's topk slots
+// in turn, each slot's activation row against that slot's expert, the top-k
+// weight folded into the group scale, so the row sum is the combined output).
 // MC, NC, KC: the call's M, N and K as compile-time constants (run-time
 // specialisation, hq_plan_set_jit); 0 takes them from the arguments.  SL:
 // the reduction buffer is a static LDS array sized for MAXT threads (a
@@ -107,7 +113,32 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   const uint32_t* zeros32 = p.zeros;
   const uint8_t* e8 = p.e8m0;
   [[maybe_unused]] bool paired = false;
-  if constexpr (GRP != GRP_DENSE) {
+  if constexpr (GRP == GRP_SLOT) {
+    // one routed slot per block: its expert straight from the routing
+    const int slot = blockIdx.z;
+    const int ex = p.topk_ids[slot];
+    paired = p.epi == GEPI_SILU || p.epi == GEPI_SILU_F32;
+    if (ex < 0 || ex >= p.num_experts) {
+      // out-of-range expert: a zero output row (the token-mode down weights it by zero)
+      const int width = paired ? N / 2 : N, cols = (paired ? NB / 2 : NB) * 16;
+      for (int e = threadIdx.x; e < cols; e += blockDim.x) {
+        const int64_t o = (int64_t)slot * width + nt * cols + e;
+        if (p.epi == GEPI_SILU_F32) p.f32_out[o] = 0.f;
+        else store_out(p.out, o, 0.f, p.out_bf16);
+      }
+      return;
+    }
+    wbytes += (int64_t)ex * p.w_expert;
+    if constexpr (e8m0_meta(FMT)) {
+      e8 += (int64_t)ex * p.e8_expert;
+    } else {
+      scales16 += (int64_t)ex * p.s_expert;
+      if (zeros32) zeros32 += (int64_t)ex * p.z_expert;
+    }
+  } else if constexpr (GRP == GRP_TOKEN) {
+    // the expert changes along k: addressed per step (below); 16-bit scales only
+    static_assert(!e8m0_meta(FMT), "token mode takes formats with 16-bit group scales");
+  } else if constexpr (GRP != GRP_DENSE) {
     if (m0 >= *p.num_padded) return;
     const int64_t ex = p.block_expert[blockIdx.z];
     if (ex < 0) {
@@ -132,7 +163,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
     paired = GRP == GRP_GATHER && (p.epi == GEPI_SILU || p.epi == GEPI_SILU_F32);
   }
   auto nblk = [&](int nb) -> int {
-    if constexpr (GRP == GRP_GATHER) {
+    if constexpr (GRP == GRP_GATHER || GRP == GRP_SLOT) {
       if (paired) return nb < NB / 2 ? nt * (NB / 2) + nb : p.half_nblk + nt * (NB / 2) + (nb - NB / 2);
     }
     return nt * NB + nb;
@@ -153,14 +184,20 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
   };
   const int a_rowb = FI::kAct16 ? 2 * K : (FI::kAct4 ? K / 2 : K);
-  const int a_rows = (GRP == GRP_GATHER) ? p.n_slots / p.topk : M;
+  // activation rows: tokens (gate_up modes), slot rows (token mode), else M
+  const int a_rows = (GRP == GRP_GATHER || GRP == GRP_SLOT) ? p.n_slots / p.topk
+                                                            : (GRP == GRP_TOKEN ? p.n_slots : M);
   const auto ra = rsrc(p.a, (int64_t)a_rows * a_rowb);
-  const int64_t nfrag = (int64_t)(N / 16) * G;
+  const int GW = GRP == GRP_TOKEN ? p.ge : G;  // groups of one expert's weight
+  const int64_t nfrag = (int64_t)(N / 16) * GW;
   constexpr int kFragB = frag_bytes(FMT);  // weight bytes per 16 x 128 fragment
-  const auto rw = rsrc(wbytes, nfrag * kFragB);
-  [[maybe_unused]] const auto rsc = rsrc(scales16, nfrag * 32);
+  // token mode reads every expert's layout (the step picks one): ranges over all of them
+  const int64_t n_exp = GRP == GRP_TOKEN ? p.num_experts : 1;
+  const auto rw = rsrc(wbytes, GRP == GRP_TOKEN ? n_exp * p.w_expert : nfrag * kFragB);
+  [[maybe_unused]] const auto rsc = rsrc(scales16, GRP == GRP_TOKEN ? n_exp * p.s_expert * 2 : nfrag * 32);
   [[maybe_unused]] const auto rz = rsrc(zeros32 ? static_cast<const void*>(zeros32) : static_cast<const void*>(scales16),
-                                        zeros32 ? nfrag * 8 : nfrag * 32);
+                                        zeros32 ? (GRP == GRP_TOKEN ? n_exp * p.z_expert * 4 : nfrag * 8)
+                                                : (GRP == GRP_TOKEN ? n_exp * p.s_expert * 2 : nfrag * 32));
   [[maybe_unused]] const auto re = rsrc(e8, nfrag * byte_meta_frag(FMT));
   // NVFP4: the operands carry e2m1 * e4m3 * 2^-8; the epilogue applies 2^8 and the tensor scale
   [[maybe_unused]] const float nv_scale = FI::kNV4 ? 256.f * p.tscale[0] : 1.f;
@@ -178,6 +215,10 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
     int row = -1;
     if constexpr (GRP == GRP_DENSE) {
       row = m < M ? m : -1;
+    } else if constexpr (GRP == GRP_SLOT) {
+      row = (mb == 0 && c == 0) ? (int)blockIdx.z / p.topk : -1;  // row 0: the slot's token
+    } else if constexpr (GRP == GRP_TOKEN) {
+      row = (mb == 0 && c == 0) ? 0 : -1;  // row 0; the step's slot row is a scalar offset
     } else {
       const int id = p.sorted_ids[m];
       if (id < p.n_slots) row = (GRP == GRP_GATHER) ? id / p.topk : m;
@@ -189,7 +230,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   int woff[NB], soff[NB], zoff[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int f0 = nblk(nb) * G;
+    const int f0 = nblk(nb) * GW;
     woff[nb] = f0 * kFragB + lane * ((FI::kW2 || FI::kW3) ? 8 : 16);
     soff[nb] = FI::kNV4   ? f0 * 128 + c * 8 + (kq >> 1) * 4
                : FI::kMX4 ? f0 * 64 + c * 4
@@ -198,24 +239,39 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   }
 
   auto load = [&](Stage<FMT, MB, NB>& st, int g) {
+    // scalar (per-step) offsets: weight fragment, scales, zero points, activations
+    int sw = g * kFragB, ss = g * 32, sz = g * 8, sa16 = g * 256, sa8 = g * 128;
+    if constexpr (GRP == GRP_TOKEN) {
+      const int j = g / p.ge, gin = g - j * p.ge;
+      const int slot = (int)blockIdx.z * p.topk + j;
+      const int e = p.topk_ids[slot];
+      const bool ok = e >= 0 && e < p.num_experts;
+      const int eu = ok ? e : 0;  // an out-of-range expert reads expert 0, weighted by zero
+      sw = eu * (int)p.w_expert + gin * kFragB;
+      ss = eu * (int)p.s_expert * 2 + gin * 32;
+      sz = eu * (int)p.z_expert * 4 + gin * 8;
+      sa16 = slot * a_rowb + gin * 256;
+      sa8 = slot * a_rowb + gin * 128;
+      st.gw = ok ? p.topk_w[slot] * (FI::kActScale ? p.a_scale[slot] : 1.f) : 0.f;
+    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
       if constexpr (FI::kW2 || FI::kW3) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rw, woff[nb], g * kFragB, 2);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rw, woff[nb], sw, 2);
         st.b[nb] = u4_t{(uint32_t)v[0], (uint32_t)v[1], 0u, 0u};
       } else {
-        st.b[nb] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[nb], g * kFragB, 2));
+        st.b[nb] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[nb], sw, 2));
       }
     if constexpr (FI::kW8) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        st.b2[nb] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[nb] + 1024, g * kFragB, 2));
+        st.b2[nb] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[nb] + 1024, sw, 2));
     }
     if constexpr (FI::kW3) {
       // the 1-bit plane: bytes [512, 768) of the fragment, one word per lane
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        st.b2[nb] = u4_t{__builtin_amdgcn_raw_buffer_load_b32(rw, woff[nb] + 512 - 4 * lane, g * kFragB, 2), 0u, 0u, 0u};
+        st.b2[nb] = u4_t{__builtin_amdgcn_raw_buffer_load_b32(rw, woff[nb] + 512 - 4 * lane, sw, 2), 0u, 0u, 0u};
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -225,7 +281,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
       if constexpr (FI::kAct16) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          st.a[mb][t] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[mb] + 64 * t, g * 256, 0));
+          st.a[mb][t] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[mb] + 64 * t, sa16, 0));
       } else if constexpr (FI::kAct4) {
         // block kq of the group: k = 32 kq + [0, 32), 16 bytes; its scale byte
         // is byte kq of the row's group word
@@ -234,7 +290,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
       } else {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          st.a[mb][h] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[mb] + 64 * h, g * 128, 0));
+          st.a[mb][h] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[mb] + 64 * h, sa8, 0));
       }
     }
     // Metadata comes in as whole dwords, decoded only at compute time, so
@@ -244,8 +300,8 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
       if constexpr (e8m0_meta(FMT)) {
         st.sraw[nb] = __builtin_amdgcn_raw_buffer_load_b32(re, soff[nb], g * byte_meta_frag(FMT), 0);
       } else {
-        st.sraw[nb] = __builtin_amdgcn_raw_buffer_load_b32(rsc, soff[nb], g * 32, 0);
-        st.zraw[nb] = __builtin_amdgcn_raw_buffer_load_b32(rz, zoff[nb], g * 8, 0);
+        st.sraw[nb] = __builtin_amdgcn_raw_buffer_load_b32(rsc, soff[nb], ss, 0);
+        st.zraw[nb] = __builtin_amdgcn_raw_buffer_load_b32(rz, zoff[nb], sz, 0);
       }
     }
   };
@@ -271,6 +327,12 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   [[maybe_unused]] const int e8_one = (int)opaque_vgpr(127u);
   [[maybe_unused]] const int e8_nine = (int)opaque_vgpr(136u);
 
+  // token mode: the step's top-k weight (and slot row scale) times the group scale
+  auto gfac = [&](const Stage<FMT, MB, NB>& st) -> float {
+    if constexpr (GRP == GRP_TOKEN) return st.gw;
+    (void)st;
+    return 1.f;
+  };
   auto compute = [&](const Stage<FMT, MB, NB>& st, int g) {
     [[maybe_unused]] f4_t rs[MB];
     [[maybe_unused]] f4_t rs4[MB][4];  // MXINT4: the row sums of each MFMA step
@@ -324,7 +386,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
             Pl[mb] = mfma16<FMT>(st.a[mb][t], bl, Pl[mb]);
           }
         }
-        const float s = p.scale_bf16 ? bf16_bits_to_float(sbits(st, nb)) : f16_bits_to_float(sbits(st, nb));
+        const float s = gfac(st) * (p.scale_bf16 ? bf16_bits_to_float(sbits(st, nb)) : f16_bits_to_float(sbits(st, nb)));
         const float cz = (kH + 1.f) * off + (float)p.zp_fixed;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -371,7 +433,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) P[mb] = mfma16<FMT>(st.a[mb][t], bop, P[mb]);
         }
-        const float s = p.scale_bf16 ? bf16_bits_to_float(sbits(st, nb)) : f16_bits_to_float(sbits(st, nb));
+        const float s = gfac(st) * (p.scale_bf16 ? bf16_bits_to_float(sbits(st, nb)) : f16_bits_to_float(sbits(st, nb)));
         const float cz = off + (float)zero_of(st, nb);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -382,7 +444,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
                              (int)((w[1] << 4) & 0xF0F0F0F0u), (int)(w[1] & 0xF0F0F0F0u)};
         const i4_t b1 = i4_t{(int)((w[2] << 4) & 0xF0F0F0F0u), (int)(w[2] & 0xF0F0F0F0u),
                              (int)((w[3] << 4) & 0xF0F0F0F0u), (int)(w[3] & 0xF0F0F0F0u)};
-        const float s16 = 0.0625f * (p.scale_bf16 ? bf16_bits_to_float(sbits(st, nb)) : f16_bits_to_float(sbits(st, nb)));
+        const float s16 = gfac(st) * 0.0625f * (p.scale_bf16 ? bf16_bits_to_float(sbits(st, nb)) : f16_bits_to_float(sbits(st, nb)));
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           i4_t P = i4_t{0, 0, 0, 0};
@@ -404,7 +466,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
                               (int)(w[1] & 0x0F0F0F0Fu), (int)((w[1] >> 4) & 0x0F0F0F0Fu),
                               (int)(w[2] & 0x0F0F0F0Fu), (int)((w[2] >> 4) & 0x0F0F0F0Fu),
                               (int)(w[3] & 0x0F0F0F0Fu), (int)((w[3] >> 4) & 0x0F0F0F0Fu)};
-        const float s = p.scale_bf16 ? bf16_bits_to_float(sbits(st, nb)) : f16_bits_to_float(sbits(st, nb));
+        const float s = gfac(st) * (p.scale_bf16 ? bf16_bits_to_float(sbits(st, nb)) : f16_bits_to_float(sbits(st, nb)));
         const float z = (float)zero_of(st, nb);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -492,12 +554,20 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
     const int mb = (idx >> 2) / NB;
     const int m = m0 + 16 * mb + 4 * (l >> 4) + r;
     const int n = nblk(nb) * 16 + (l & 15);
+    if constexpr (GRP == GRP_TOKEN) {
+      // row 0 is the token: the top-k weights are in, the sum over its slots is done
+      if (m != m0) continue;
+      store_out(p.out, (int64_t)blockIdx.z * N + n, v, p.out_bf16);
+      continue;
+    }
     if constexpr (GRP != GRP_DENSE) {
-      // m is the row of the aligned slot array; padding slots are dropped
-      const int id = p.sorted_ids[m];
+      // m is the row of the aligned slot array (slot mode: row 0 is the
+      // block's slot); padding slots are dropped
+      const int id = GRP == GRP_SLOT ? (m == m0 ? (int)blockIdx.z : p.n_slots) : p.sorted_ids[m];
       if (id >= p.n_slots) continue;
       const int tok = id / p.topk;
-      if constexpr (GRP == GRP_GATHER) {
+      const int64_t orow = GRP == GRP_SLOT ? id : m;  // output row: the slot (slot mode) or the aligned row
+      if constexpr (GRP == GRP_GATHER || GRP == GRP_SLOT) {
         const float sa = FI::kActScale ? p.a_scale[tok] : 1.f;
         if (paired) {
           if (nb >= NB / 2) continue;
@@ -507,12 +577,12 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
           const float act = gv / (1.f + expf(-gv)) * (u * sa);  // SiLU(gate) * up
           const int half = N / 2;
           if (p.epi == GEPI_SILU) {
-            store_out(p.out, (int64_t)m * half + n, act, p.out_bf16);
+            store_out(p.out, orow * half + n, act, p.out_bf16);
           } else {
-            p.f32_out[(int64_t)m * half + n] = act;  // requantised to fp8 by moe_requant_kernel
+            p.f32_out[orow * half + n] = act;  // requantised to fp8 by moe_requant_kernel
           }
         } else {
-          store_out(p.out, (int64_t)m * N + n, v * sa, p.out_bf16);
+          store_out(p.out, orow * N + n, v * sa, p.out_bf16);
         }
       } else {
         const float sa = FI::kActScale ? p.a_scale[m] : 1.f;

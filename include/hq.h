@@ -398,6 +398,37 @@ hq_status hq_moe_gemm(const hq_plan* plan, int64_t t, int topk, const void* a, c
                       const float* topk_w, const void* w, const void* meta, void* out, float* out_scale,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* The same grouped GEMMs without the alignment, for decode-sized t: the rows
+ * are the routed slots themselves (slot s = t*topk index tok*topk + j, expert
+ * topk_ids[s]), so no hq_moe_align call precedes them and a layer is two
+ * launches (three with the fp8 requant).  Same plan, weights, metadata and
+ * epilogue semantics as hq_moe_gemm (MoE path of the pages as cited above):
+ *   topk_ids  device int32 [t, topk]; ids outside [0, num_experts) are
+ *             allowed and contribute zero
+ *   gate_up   (HQ_EPI_SILU_MUL / _QFP8 / NONE): `a` [t, k] (token rows),
+ *             out [t*topk, n/2] (or [t*topk, n] for NONE) indexed by slot;
+ *             a slot with an out-of-range id gets a zero row (fp8: zero
+ *             codes, scale 1).  _QFP8: out_scale fp32 [t*topk]; ws holds
+ *             the fp32 rows, align256(t*topk * n/2 * 4) bytes, after the
+ *             call (hq_moe_workspace_bytes is always enough).
+ *   down      (HQ_EPI_TOPK_COMBINE): `a` [t*topk, k] slot rows (the gate_up
+ *             output), a_scale fp32 [t*topk] for fp8 rows; out = y [t, n],
+ *             y[tok] = sum_j topk_w[tok, j] * (a[tok*topk + j] . W_e^T),
+ *             summed in one fp32 accumulator per output (each slot's top-k
+ *             weight folded into its group scales) and rounded once; no
+ *             workspace.  Deterministic run to run; the sum order differs
+ *             from hq_moe_gemm's, so the two agree to fp32 rounding.
+ * Every block reads its slot's (token's) expert weights directly, so an
+ * expert picked by several slots is read once per slot: the aligned path is
+ * the one for large t.  t * topk <= 65535; in down mode all experts' weights
+ * (and their scales) must stay below 2 GiB, in gate_up mode one expert's.
+ * The plan's tuning tile_n (16, 32 or 64 columns per workgroup; at least 32
+ * for gate_up) and waves (1..16) override the defaults where set.  Honours
+ * hq_time_next_launch (first launch to last). */
+hq_status hq_moe_gemm_by_slot(const hq_plan* plan, int64_t t, int topk, const void* a, const float* a_scale,
+                              const int32_t* topk_ids, const float* topk_w, const void* w, const void* meta,
+                              void* out, float* out_scale, void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Per-token activation quantiser: the step before a W4A8 GEMM, which takes
  * 8-bit activations with one fp32 scale per row (W4A8: INT8 or FP8

@@ -360,8 +360,8 @@ def test_moe_block_choice():
     assert hq.MoePlan(512, 7168, q, 256, 64, "silu_mul", tuning=dict(kernel=2)).block_m(1, 8) == 64
     assert hq.MoePlan(512, 7168, q, 256, 8192, "silu_mul", tuning=dict(kernel=1)).block_m(4096, 8) == 16
     assert hq.MoePlan(512, 7168, q, 256, 8192, "silu_mul", tuning=dict(tile_m=32)).block_m(4096, 8) == 32
-    for bad in (dict(tile_m=48), dict(kernel=1, tile_m=64), dict(kernel=2, tile_m=32), dict(tile_n=64),
-                dict(tile_n=256, tile_m=64)):
+    for bad in (dict(tile_m=48), dict(kernel=1, tile_m=64), dict(kernel=2, tile_m=32), dict(tile_n=96),
+                dict(tile_n=256, tile_m=64), dict(waves=17)):
         n = 384 if bad.get("tile_n") == 256 else 512
         with pytest.raises(hq.HQError) as e:
             hq.MoePlan(n, 7168, q, 256, 64, "silu_mul", tuning=bad)
@@ -419,6 +419,46 @@ def test_moe_call_validation():
     assert L.hq_moe_gemm(p._h, 4, 8, *args(w=A + 8), 1 << 30, None) == hq.HQ_ERR_INVALID_ARG  # misaligned
     pq = hq.MoePlan(512, 7168, hq.w4a8_fp8(), 256, 64, "silu_mul_qfp8")
     assert L.hq_moe_gemm(pq._h, 4, 8, *args(a_scale=A), 1 << 30, None) == hq.HQ_ERR_INVALID_ARG  # no out_scale
+
+
+def test_moe_by_slot_call_validation():
+    """Argument checks of hq_moe_gemm_by_slot run before any launch (no GPU needed)."""
+    L = hq.lib()
+    A = 0x10000
+    p = hq.MoePlan(7168, 256, hq.w4a16("bf16", scale="f16"), 256, 64, "topk_combine")
+    # pointer arguments: a, a_scale, topk_ids, topk_w, w, meta, out, out_scale, ws
+    def args(**kw):
+        names = ["a", "a_scale", "topk_ids", "topk_w", "w", "meta", "out", "out_scale", "ws"]
+        d = {n: A for n in names}
+        d["a_scale"] = d["out_scale"] = d["ws"] = None
+        d.update(kw)
+        return [d[n] for n in names]
+    f = L.hq_moe_gemm_by_slot
+    assert f(None, 1, 8, *args(), 0, None) == hq.HQ_ERR_INVALID_ARG
+    assert f(p._h, 0, 8, *args(a=None), 0, None) == hq.HQ_OK                    # t = 0: nothing to do
+    assert f(p._h, 1, 8, *args(topk_w=None), 0, None) == hq.HQ_ERR_INVALID_ARG   # the combine needs weights
+    assert f(p._h, 1, 8, *args(topk_ids=None), 0, None) == hq.HQ_ERR_INVALID_ARG
+    assert f(p._h, 1, 8, *args(a_scale=A), 0, None) == hq.HQ_ERR_INVALID_ARG     # 16-bit rows take no scale
+    assert f(p._h, 65, 8, *args(), 0, None) == hq.HQ_ERR_INVALID_ARG             # t > max_t
+    assert f(p._h, 1, 0, *args(), 0, None) == hq.HQ_ERR_INVALID_ARG              # topk
+    assert f(p._h, 1, 65, *args(), 0, None) == hq.HQ_ERR_INVALID_ARG
+    assert f(p._h, 1, 8, *args(out=A + 8), 0, None) == hq.HQ_ERR_INVALID_ARG     # misaligned
+    big = hq.MoePlan(7168, 256, hq.w4a16("bf16", scale="f16"), 256, 1 << 14, "topk_combine")
+    assert f(big._h, 1 << 14, 8, *args(), 0, None) == hq.HQ_ERR_UNSUPPORTED     # t * topk > 65535
+    dense = hq.Plan(512, 256, hq.w4a16("bf16"), max_m=4)
+    assert f(dense._h, 1, 8, *args(), 0, None) == hq.HQ_ERR_INVALID_ARG
+    pq = hq.MoePlan(512, 7168, hq.w4a8_fp8(), 256, 64, "silu_mul_qfp8")
+    need = 4 * 8 * 256 * 4                                                       # t * topk rows of n/2 fp32
+    assert f(pq._h, 4, 8, *args(a_scale=None, out_scale=A, ws=A), need, None) == hq.HQ_ERR_INVALID_ARG
+    assert f(pq._h, 4, 8, *args(a_scale=A, out_scale=None, ws=A), need, None) == hq.HQ_ERR_INVALID_ARG
+    assert f(pq._h, 4, 8, *args(a_scale=A, out_scale=A, ws=None), need, None) == hq.HQ_ERR_WORKSPACE
+    assert f(pq._h, 4, 8, *args(a_scale=A, out_scale=A, ws=A), need - 1, None) == hq.HQ_ERR_WORKSPACE
+    # the aligned path's workspace is always enough for the same t and topk
+    b = ctypes.c_size_t()
+    assert L.hq_moe_workspace_bytes(pq._h, 4, 8, ctypes.byref(b)) == 0 and b.value >= need
+    # all experts' weights in one buffer range (down mode): 2 GiB or more is refused
+    huge = hq.MoePlan(8192, 2048, hq.w4a16("bf16", scale="f16"), 512, 64, "topk_combine")
+    assert f(huge._h, 1, 8, *args(), 0, None) == hq.HQ_ERR_UNSUPPORTED
 
 
 def test_quantize_call_validation():

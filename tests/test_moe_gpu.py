@@ -7,7 +7,9 @@ experts, top-8 of softmax(router logits ~ N(0,1)), hidden 7168, expert
 intermediate 256 (gate_up N=512 K=7168; down N=7168 K=256), INT4 weights with
 group 128, fp16 scales and zero point 8, activations bf16 or fp8 e4m3 with
 per-token scales -- for T in {1, 32, 512, 4096} tokens (every token at T = 512,
-sampled tokens at T = 4096), plus small layers checked on every token.
+sampled tokens at T = 4096), plus small layers checked on every token.  The
+unaligned path (hq_moe_gemm_by_slot: rows indexed by routed slot) is checked
+the same way at decode-sized T.
 """
 import numpy as np
 import pytest
@@ -189,6 +191,80 @@ def run_layer(layer, T, act, topk, key=(5,), sample=None, masked=0.0):
     return ratio.max()
 
 
+def run_layer_by_slot(layer, T, act, topk, key=(5,), sample=None, masked=0.0, ws=None):
+    """gate_up -> down through hq_moe_gemm_by_slot (rows indexed by routed slot,
+    no alignment); every stage checked against the oracle on the GPU's own
+    input to it, for all tokens or a sample.  Slots with an out-of-range
+    expert id must give a zero gate_up row and add nothing to y."""
+    E, H, I = layer.E, layer.H, layer.I
+    _log(f"moe by-slot E={E} H={H} I={I} T={T} topk={topk} act={act} masked={masked}")
+    r = datagen.moe_routing(T, E=E, topk=topk, key=key)
+    if masked:
+        rng = np.random.default_rng(98)
+        ids = r["topk_ids"].copy()
+        hit = rng.random(ids.shape) < masked
+        ids[hit] = np.where(rng.random(ids.shape) < 0.5, -1, E + 3)[hit]
+        r = dict(r, topk_ids=ids)
+    x = datagen.moe_activations(T, H=H, act=act, key=key)
+    p1, p2, w1, m1, w2, m2 = layer.dev[act]
+    ids = torch.from_numpy(r["topk_ids"]).to(DEV)
+    tw = torch.from_numpy(r["topk_w"]).to(DEV)
+    S = T * topk
+    if act == "bf16":
+        act_out = p1.moe_gemm_by_slot(x["x"].to(DEV), T, topk, ids, w1, m1)
+        y = p2.moe_gemm_by_slot(act_out, T, topk, ids, w2, m2, topk_w=tw)
+    else:
+        if ws is None:
+            ws = p1.moe_workspace(T, topk, DEV)
+        codes, scl = p1.moe_gemm_by_slot(x["x_codes"].to(DEV), T, topk, ids, w1, m1, a_scale=x["x_scale"].to(DEV),
+                                         ws=ws)
+        y = p2.moe_gemm_by_slot(codes, T, topk, ids, w2, m2, a_scale=scl, topk_w=tw)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (T, H)
+
+    toks = np.arange(T) if sample is None or T <= sample else \
+        np.sort(np.random.default_rng(T).choice(T, sample, replace=False))
+    slots = (toks[:, None] * topk + np.arange(topk)[None, :]).reshape(-1)
+    flat = r["topk_ids"].reshape(-1)
+    valid = (flat[slots] >= 0) & (flat[slots] < E)
+    vs, bad = slots[valid], slots[~valid]
+    row_tok, row_exp = vs // topk, flat[vs]
+    if act == "bf16":
+        xa = x["x"].double().numpy()[row_tok]
+    else:
+        xa = e4m3_value(x["x_codes"].numpy()[row_tok]) * x["x_scale"].numpy()[row_tok, None].astype(np.float64)
+    gu = om.gate_up(xa, row_exp, layer.w["w1"], layer.w["s1"].double().numpy(), I)
+    if act == "bf16":
+        assert tuple(act_out.shape) == (S, I)
+        out_h = act_out.double().cpu().numpy()
+        act_rows = out_h[vs]
+        ok, _, ratio = og.check(act_rows, gu["act"], gu["tau_act"], "bf16")
+        assert ok.all(), f"gate_up act: {(~ok).sum()} bad, max err/tau {ratio.max():.3g}"
+        assert (out_h[bad] == 0).all(), "rows of out-of-range slots must be zero"
+    else:
+        assert tuple(codes.shape) == (S, I) and tuple(scl.shape) == (S,)
+        codes_a, scl_a = codes.cpu().numpy(), scl.cpu().numpy()
+        act32_a = ws[: S * I * 4].view(torch.float32).view(S, I).cpu().numpy()
+        act32, codes_h, scl_h = act32_a[vs], codes_a[vs], scl_a[vs]
+        err32 = np.abs(act32.astype(np.float64) - gu["act"])
+        assert (err32 <= gu["tau_act"] + 2.0 ** -20 * np.abs(gu["act"])).all(), \
+            f"gate_up fp32 act: {(err32 > gu['tau_act']).sum()} bad"
+        qc, qs = oq.quantize_rows(act32, "fp8")
+        assert np.array_equal(codes_h, qc), f"fp8 requant codes: {(codes_h != qc).sum()} differ from the rule"
+        assert np.array_equal(scl_h, qs), "fp8 requant scales differ from the rule"
+        assert (codes_a[bad] == 0).all() and (scl_a[bad] == 1.0).all(), "out-of-range slots: zero codes, scale 1"
+        dq = e4m3_value(codes_h) * scl_h[:, None].astype(np.float64)
+        bound = om.fp8_rows_bound(dq, scl_h, gu["act"], gu["tau_act"])
+        assert (np.abs(dq - gu["act"]) <= bound).all(), "fp8 requant off the oracle's act"
+        act_rows = dq
+    dc = om.down_combine(act_rows, row_tok, r["topk_w"].reshape(-1)[vs], row_exp, layer.w["w2"],
+                         layer.w["s2"].double().numpy(), T)
+    y_gpu = y.double().cpu().numpy()[toks]
+    ok, _, ratio = og.check(y_gpu, dc["y64"][toks], dc["tau_y"][toks], "bf16")
+    assert ok.all(), f"down+combine by slot: {(~ok).sum()} bad, max err/tau {ratio.max():.3g}"
+    return ratio.max()
+
+
 @pytest.fixture(scope="module")
 def small_layer():
     return Layer(8, 512, 128, key=(7,))
@@ -262,6 +338,33 @@ def test_small_layer_many_slots_column_windows(act):
     run_layer(lay, 65536, act, 8, key=(37,), sample=24)
 
 
+@pytest.mark.parametrize("act", ["bf16", "fp8"])
+@pytest.mark.parametrize("T,topk", [(1, 2), (1, 8), (3, 8), (37, 2), (200, 3)])
+def test_small_layer_by_slot(small_layer, T, topk, act):
+    run_layer_by_slot(small_layer, T, act, topk, key=(41,))
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp8"])
+@pytest.mark.parametrize("T,topk", [(1, 8), (40, 3)])
+def test_small_layer_by_slot_masked_experts(small_layer, T, topk, act):
+    run_layer_by_slot(small_layer, T, act, topk, key=(43,), masked=0.3)
+
+
+@pytest.mark.parametrize("tun", [dict(tile_n=16, waves=1), dict(tile_n=32, waves=16), dict(tile_n=64, waves=5)],
+                         ids=["n16w1", "n32w16", "n64w5"])
+@pytest.mark.parametrize("act", ["bf16", "fp8"])
+def test_small_layer_by_slot_tunings(tun, act):
+    # every column-block width and wave count the by-slot kernels take
+    run_layer_by_slot(Layer(8, 512, 128, key=(7,), tuning=tun), 6, act, 4, key=(47,))
+
+
+def test_by_slot_fp8_workspace_reuse(small_layer):
+    # one workspace across calls of falling size: each call's scales come from its own rows
+    ws = small_layer.dev["fp8"][0].moe_workspace(64, 8, DEV)
+    for T, topk in ((64, 8), (5, 3), (1, 8), (2, 2)):
+        run_layer_by_slot(small_layer, T, "fp8", topk, key=(53,), ws=ws)
+
+
 @pytest.fixture(scope="module")
 def full_layer():
     _log("generating the 256-expert layer")
@@ -272,6 +375,18 @@ def full_layer():
 @pytest.mark.parametrize("T", [1, 32, 512, 4096])
 def test_full_layer(full_layer, T, act):
     run_layer(full_layer, T, act, TOPK, sample=12)
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp8"])
+@pytest.mark.parametrize("T", [1, 2, 4, 8, 32])
+def test_full_layer_by_slot(full_layer, T, act):
+    # decode-sized batches through the unaligned path, every token
+    run_layer_by_slot(full_layer, T, act, TOPK)
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp8"])
+def test_full_layer_by_slot_masked(full_layer, act):
+    run_layer_by_slot(full_layer, 4, act, TOPK, key=(59,), masked=0.25)
 
 
 @pytest.mark.parametrize("act", ["bf16", "fp8"])
