@@ -247,7 +247,7 @@ _WORKLOAD_PROFILES = {
     "nvfp4": ("qgemm_w4a16_nvfp4_bf16_n4096_k4096.md", "dense W4A16-NVFP4, M in {1,16,64,1024}, N = K = 4096, "
               "bf16"),
     "moe": ("moe_layer_e256_top8_h7168_i256.md", "MoE layer, 256 experts, top-8, hidden 7168, intermediate 256, "
-            "T in {1,32,512,4096}, bf16 and fp8 activations"),
+            "T in {1,32,512,4096} (aligned) and {1,4,8,32} (by slot), bf16 and fp8 activations"),
 }
 
 

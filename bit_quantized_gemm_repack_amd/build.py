@@ -27,7 +27,7 @@ DEVICE = [f"--offload-arch={ARCH}", "-mcode-object-version=5", "-Xclang", "-targ
 # *_f16.hip (an fp16 k loop without per-group epilogue) keep the default.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 # hipRTC for the run-time specialised kernels (hq_plan_set_jit)
-LINK = ["-lhiprtc"]
+LINK = ["-lhiprtc", "-Wl,-z,defs"]  # every symbol resolved at link time
 
 
 def sources():

@@ -951,19 +951,20 @@ hq_status hq_moe_align(int64_t t, int topk, int num_experts, int block_m, const 
 }
 
 // Columns of N per small-K down launch.  Each launch stores its slots'
-// weighted fp32 rows (t * topk * cols * 4 bytes) and the combine of the same
+// weighted bf16 rows (t * topk * cols * 2 bytes) and the combine of the same
 // columns reads them back, so the window bounds the workspace.  Windows cost
 // time: each launch re-loads every block's activations and row sums (measured
-// on MI355X at t = 4096, N = 7168: seven 1024-column windows took the down +
-// combine from 640 to 870 us although the combine's reads then hit the last-
-// level cache), so a window covers all of N up to 1 GiB of rows.  Equal
+// on MI355X at t = 4096, N = 7168, with fp32 rows: seven 1024-column windows
+// took the down + combine from 640 to 870 us although the combine's reads
+// then hit the last-level cache), so a window covers all of N up to 1 GiB of
+// rows.  Equal
 // windows, each a multiple of 64 columns.
 static constexpr int64_t kCombineWindowBytes = int64_t(1) << 30;
 
 static int64_t moe_down_cols(const hq_plan* p, int64_t t, int topk, int bm) {
   const int64_t N = p->layer.n;
   if (!moe_uses_smallk(p, bm) || t * topk <= 0) return N;
-  int64_t c = kCombineWindowBytes / (t * topk * 4) / 64 * 64;
+  int64_t c = kCombineWindowBytes / (t * topk * 2) / 64 * 64;
   if (c >= N) return N;
   c = std::max<int64_t>(c, 64);
   const int64_t n = cdiv(N, c);
@@ -980,7 +981,7 @@ static MoeWs moe_ws(const hq_plan* p, int64_t t, int topk) {
   const int64_t mp = moe_max_padded(t, topk, p->layer.num_experts, moe_choice(p, t, topk).bm);
   if (p->compute.epi == HQ_EPI_SILU_MUL_QFP8) w.act32 = align256((size_t)mp * (size_t)(p->layer.n / 2) * 4);
   if (p->compute.epi == HQ_EPI_TOPK_COMBINE)
-    w.rows = align256((size_t)t * topk * (size_t)moe_down_cols(p, t, topk, moe_choice(p, t, topk).bm) * 4);
+    w.rows = align256((size_t)t * topk * (size_t)moe_down_cols(p, t, topk, moe_choice(p, t, topk).bm) * 2);
   w.total = w.act32 + w.rows;
   return w;
 }
@@ -1025,9 +1026,11 @@ hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, cons
     const int bm = mc.bm;
     const int64_t mp = moe_max_padded(t, topk, p->layer.num_experts, bm);
     {
-      // the kernels address A and one expert's W through 32-bit buffer ranges
+      // the kernels address A (token rows for gate_up, aligned rows for the
+      // down GEMM) and one expert's W through 32-bit buffer ranges
       const int64_t act_bytes = (p->fmt == hq::FMT_W16F16 || p->fmt == hq::FMT_W16BF16) ? 2 : 1;
-      if (std::max<int64_t>(mp, t) * K * act_bytes >= (int64_t(1) << 31) || N * K / 2 >= (int64_t(1) << 31))
+      const int64_t a_rows = epi == HQ_EPI_TOPK_COMBINE ? mp : t;
+      if (a_rows * K * act_bytes >= (int64_t(1) << 31) || N * K / 2 >= (int64_t(1) << 31))
         return fail(HQ_ERR_UNSUPPORTED, "activations and one expert's weights must each stay below 2 GiB");
     }
     const uint32_t* zeros = p->layer.q.zp == HQ_ZP_PER_GROUP_U4
@@ -1038,6 +1041,7 @@ hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, cons
     uint8_t* wsb = static_cast<uint8_t*>(ws);
     int mode = hq::GRP_GATHER, gepi = hq::GEPI_PLAIN;
     float* f32_out = nullptr;
+    uint16_t* rows16 = nullptr;
     switch (epi) {
       case HQ_EPI_NONE: gepi = hq::GEPI_PLAIN; break;
       case HQ_EPI_SILU_MUL: gepi = hq::GEPI_SILU; break;
@@ -1048,7 +1052,7 @@ hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, cons
       case HQ_EPI_TOPK_COMBINE:
         gepi = hq::GEPI_COMBINE;
         mode = hq::GRP_SORTED;
-        f32_out = reinterpret_cast<float*>(wsb);
+        rows16 = reinterpret_cast<uint16_t*>(wsb);
         break;
       default: return fail(HQ_ERR_INVALID_ARG, "unsupported grouped epilogue");
     }
@@ -1089,6 +1093,7 @@ hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, cons
       s.s_expert = (int64_t)(N * G);
       s.z_expert = (int64_t)((N / 16) * G * 2);
       s.f32_out = f32_out;
+      s.rows16 = rows16;
       // column windows: down GEMM, then the combine of the same columns
       const int64_t cols = moe_down_cols(p, t, topk, bm);
       err = hipSuccess;
@@ -1100,7 +1105,7 @@ hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, cons
         err = hq::launch_smallk_grouped(p->fmt, bm / 16, s, blocks, stream);
         if (err != hipSuccess) break;
         hq::arm_timing({nullptr, c0 + nc >= N ? ev.stop : nullptr});
-        err = hq::launch_moe_combine(f32_out, topk, t, N, c0, nc, out, p->layer.q.out == HQ_BF16, stream);
+        err = hq::launch_moe_combine(rows16, topk, t, N, c0, nc, out, p->layer.q.out == HQ_BF16, stream);
       }
       hq::arm_timing({nullptr, nullptr});
       if (err != hipSuccess) return fail(HQ_ERR_HIP, "grouped gemm launch: %s", hipGetErrorString((hipError_t)err));
@@ -1133,6 +1138,7 @@ hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, cons
       s.s_expert = (int64_t)(N * G);
       s.z_expert = (int64_t)((N / 16) * G * 2);
       s.f32_out = f32_out;
+      s.rows16 = rows16;
       err = hq::launch_tiled_grouped(p->fmt, mode, mc.tl, s, blocks, stream);
     } else {
       hq::SkinnyArgs s{};
@@ -1163,6 +1169,7 @@ hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, cons
       s.z_expert = (int64_t)((N / 16) * G * 2);
       s.e8_expert = (int64_t)(N * K / 32);
       s.f32_out = f32_out;
+      s.rows16 = rows16;
       err = hq::launch_skinny_grouped(p->fmt, mode, mc.sk, s, blocks, stream);
     }
     hq::arm_timing({nullptr, ev.stop});
@@ -1171,7 +1178,7 @@ hq_status hq_moe_gemm(const hq_plan* p, int64_t t, int topk, const void* a, cons
                                    std::min<int64_t>(mp, (int64_t)bm * t * topk), static_cast<uint8_t*>(out),
                                    out_scale, stream);
     if (err == hipSuccess && epi == HQ_EPI_TOPK_COMBINE)
-      err = hq::launch_moe_combine(f32_out, topk, t, N, 0, N, out, p->layer.q.out == HQ_BF16, stream);
+      err = hq::launch_moe_combine(rows16, topk, t, N, 0, N, out, p->layer.q.out == HQ_BF16, stream);
     hq::arm_timing({nullptr, nullptr});
     if (err != hipSuccess) return fail(HQ_ERR_HIP, "grouped gemm launch: %s", hipGetErrorString((hipError_t)err));
     return ok();

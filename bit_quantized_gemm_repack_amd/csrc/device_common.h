@@ -22,13 +22,9 @@ typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 __device__ inline float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
 __device__ inline float f16_bits_to_float(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); }
 
-// Round-to-nearest-even fp32 -> bf16 bits (a NaN stays a quiet NaN).
-__device__ inline uint16_t float_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+// Round-to-nearest-even fp32 -> bf16 bits: the hardware conversion (one
+// v_cvt_pk_bf16_f32 on gfx950, round to nearest even, a NaN gives a quiet NaN).
+__device__ inline uint16_t float_to_bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 // Round-to-nearest-even fp32 -> fp16 bits (the hardware conversion).
 __device__ inline uint16_t float_to_f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 

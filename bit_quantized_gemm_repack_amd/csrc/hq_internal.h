@@ -400,7 +400,8 @@ struct SkinnyArgs {
   int64_t s_expert;             // scale elements per expert
   int64_t z_expert;             // zero-point words per expert
   int64_t e8_expert;            // E8M0 bytes per expert
-  float* f32_out;               // gate_up fp32 act (QFP8) or down weighted slot rows [n_slots][N]
+  float* f32_out;               // gate_up fp32 act (QFP8)
+  uint16_t* rows16;             // down: weighted slot rows, bf16 [n_slots][N] (small K: [n_slots][ncol])
   // small-K down GEMM: this launch covers columns [col0, col0 + ncol) of N
   // and stores slot rows [n_slots][ncol] (0, 0: all of N)
   int col0, ncol;
@@ -443,8 +444,8 @@ int launch_moe_align(int64_t t, int topk, int num_experts, int block_m, const in
 int launch_moe_requant(const float* act32, const int32_t* sorted_ids, const int32_t* num_padded, int n_slots,
                        int inter, int64_t max_rows, uint8_t* codes, float* scales, void* stream);
 // y[t][col0 + c] = RNE(sum over the token's topk weighted slot rows), rows
-// [t*topk][ncol] fp32 (summed in slot order), c < ncol; y row stride n.
-int launch_moe_combine(const float* rows, int topk, int64_t t, int64_t n, int64_t col0, int64_t ncol, void* y,
+// [t*topk][ncol] bf16 (summed in fp32 in slot order), c < ncol; y row stride n.
+int launch_moe_combine(const uint16_t* rows, int topk, int64_t t, int64_t n, int64_t col0, int64_t ncol, void* y,
                        int out_bf16, void* stream);
 #endif  // __HIPCC_RTC__
 
@@ -476,7 +477,8 @@ struct TiledArgs {
   int epi;
   int half_nblk;
   int64_t w_expert, s_expert, z_expert, e8_expert;
-  float* f32_out;
+  float* f32_out;    // gate_up fp32 act (QFP8)
+  uint16_t* rows16;  // down: weighted slot rows, bf16 [n_slots][N]
 };
 
 #ifndef __HIPCC_RTC__

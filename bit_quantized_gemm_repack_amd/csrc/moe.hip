@@ -117,33 +117,46 @@ __global__ void __launch_bounds__(256) moe_requant_kernel(const float* __restric
   const int lane = threadIdx.x & 63;
   if (row >= max_rows || (num_padded && row >= *num_padded)) return;
   if (sorted_ids && sorted_ids[row] >= n_slots) return;
-  const float* a = act32 + row * inter;
+  // four consecutive values per lane and access (inter is a multiple of 4)
+  const float4* a = reinterpret_cast<const float4*>(act32 + row * inter);
+  uint32_t* q = reinterpret_cast<uint32_t*>(codes + row * inter);
+  const int n4 = inter >> 2;
   float amax = 0.f;
-  for (int col = lane; col < inter; col += 64) amax = fmaxf(amax, fabsf(a[col]));
+  for (int c = lane; c < n4; c += 64) {
+    const float4 v = a[c];
+    amax = fmaxf(fmaxf(amax, fabsf(v.x)), fmaxf(fmaxf(fabsf(v.y), fabsf(v.z)), fabsf(v.w)));
+  }
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 64));
   const float s = amax > 0.f ? amax / 448.f : 1.f;
-  for (int col = lane; col < inter; col += 64) codes[row * inter + col] = (uint8_t)e4m3_code_rne(a[col] / s);
+  for (int c = lane; c < n4; c += 64) {
+    const float4 v = a[c];
+    q[c] = e4m3_code_rne(v.x / s) | (e4m3_code_rne(v.y / s) << 8) | (e4m3_code_rne(v.z / s) << 16) |
+           (e4m3_code_rne(v.w / s) << 24);
+  }
   if (lane == 0) scales[row] = s;
 }
 
 // The combine: y[t, col0 + c] = RNE(sum_j rows[t * topk + j][c]) over the
-// token's topk slot rows (each already weighted; rows of ncol columns, the
-// down GEMM's column window), summed in slot order; four outputs per thread
-// (ncol and col0 are multiples of 4).
-__global__ void __launch_bounds__(256) moe_combine_kernel(const float4* __restrict__ rows, int topk, int64_t n4,
+// token's topk slot rows (each already weighted and rounded to bf16; rows of
+// ncol columns, the down GEMM's column window), summed in fp32 in slot order;
+// four outputs per thread (ncol and col0 are multiples of 4).
+__global__ void __launch_bounds__(256) moe_combine_kernel(const uint2* __restrict__ rows, int topk, int64_t n4,
                                                           int64_t col04, int64_t ncol4, int64_t elems4,
                                                           uint2* __restrict__ y, int out_bf16) {
+  auto lo = [](uint32_t b) { return __uint_as_float(b << 16); };
+  auto hi = [](uint32_t b) { return __uint_as_float(b & 0xFFFF0000u); };
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < elems4; i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t t = i / ncol4, c = i - t * ncol4;
-    const float4* r = rows + t * topk * ncol4 + c;
-    float4 v = r[0];
+    const uint2* r = rows + t * topk * ncol4 + c;
+    const uint2 w0 = r[0];
+    float4 v = make_float4(lo(w0.x), hi(w0.x), lo(w0.y), hi(w0.y));
     for (int j = 1; j < topk; ++j) {
-      const float4 w = r[(int64_t)j * ncol4];
-      v.x += w.x;
-      v.y += w.y;
-      v.z += w.z;
-      v.w += w.w;
+      const uint2 w = r[(int64_t)j * ncol4];
+      v.x += lo(w.x);
+      v.y += hi(w.x);
+      v.z += lo(w.y);
+      v.w += hi(w.y);
     }
     const uint32_t h0 = out_bf16 ? float_to_bf16_bits(v.x) : float_to_f16_bits(v.x);
     const uint32_t h1 = out_bf16 ? float_to_bf16_bits(v.y) : float_to_f16_bits(v.y);
@@ -162,13 +175,14 @@ int launch_moe_align(int64_t t, int topk, int num_experts, int block_m, const in
 
 int launch_moe_requant(const float* act32, const int32_t* sorted_ids, const int32_t* num_padded, int n_slots,
                        int inter, int64_t max_rows, uint8_t* codes, float* scales, void* stream) {
+  if (inter % 4 || max_rows < 1) return (int)hipErrorInvalidValue;
   const int64_t blocks = (max_rows + 3) / 4;
   return (int)launch_timed(moe_requant_kernel, dim3((unsigned)blocks), dim3(256), 0,
                            static_cast<hipStream_t>(stream), act32, sorted_ids, num_padded, n_slots, inter, max_rows,
                            codes, scales);
 }
 
-int launch_moe_combine(const float* rows, int topk, int64_t t, int64_t n, int64_t col0, int64_t ncol, void* y,
+int launch_moe_combine(const uint16_t* rows, int topk, int64_t t, int64_t n, int64_t col0, int64_t ncol, void* y,
                        int out_bf16, void* stream) {
   if (n % 4 || col0 % 4 || ncol % 4 || col0 < 0 || col0 + ncol > n) return (int)hipErrorInvalidValue;
   const int64_t elems4 = t * ncol / 4;
@@ -176,7 +190,7 @@ int launch_moe_combine(const float* rows, int topk, int64_t t, int64_t n, int64_
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;
   return (int)launch_timed(moe_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
-                           reinterpret_cast<const float4*>(rows), topk, n / 4, col0 / 4, ncol / 4, elems4,
+                           reinterpret_cast<const uint2*>(rows), topk, n / 4, col0 / 4, ncol / 4, elems4,
                            static_cast<uint2*>(y), out_bf16);
 }
 

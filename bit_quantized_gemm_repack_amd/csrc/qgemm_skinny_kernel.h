@@ -148,7 +148,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
         for (int e = threadIdx.x; e < 16 * MB * NB * 16; e += blockDim.x) {
           const int r = e / (NB * 16), cc = e - r * (NB * 16);
           const int id = p.sorted_ids[m0 + r];
-          if (id < p.n_slots) p.f32_out[(int64_t)id * N + (nt * NB + cc / 16) * 16 + (cc & 15)] = 0.f;
+          if (id < p.n_slots) p.rows16[(int64_t)id * N + (nt * NB + cc / 16) * 16 + (cc & 15)] = 0;
         }
       }
       return;
@@ -586,7 +586,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
         }
       } else {
         const float sa = FI::kActScale ? p.a_scale[m] : 1.f;
-        p.f32_out[(int64_t)id * N + n] = v * sa * p.topk_w[id];  // this slot's weighted row
+        p.rows16[(int64_t)id * N + n] = float_to_bf16_bits(v * sa * p.topk_w[id]);  // this slot's weighted row
       }
       continue;
     }

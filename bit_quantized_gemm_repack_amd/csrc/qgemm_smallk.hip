@@ -4,8 +4,8 @@
 //
 // The down GEMM of one GPU's share of the layer has K = 256 (two groups) and
 // N = 7168: the reduction is too short for a K-split or a K-pipelined tile to
-// amortise its start-up, and the output (one fp32 row per routed slot) is
-// larger than the weights.  So here
+// amortise its start-up, and the output (one row per routed slot) is larger
+// than the weights.  So here
 //   * a workgroup takes one expert-aligned block of 16 MB rows and a chunk of
 //     the columns; each of its 4 waves holds the block's activation operands
 //     for the whole of K in registers (loaded once), together with the row
@@ -18,7 +18,9 @@
 //       o[m, n] = sum_g s[n,g] (P_g[m,n] - (OFF + z[n,g]) rowsum_g(a[m, :]))
 //     (fp8 activations: OFF = 0, codes q * 2^-9 undone by the MFMA's block
 //     scale, times the row scale);
-//   * the epilogue stores topk_w * o as the slot's row for the combine.
+//   * the epilogue stores topk_w * o, rounded to bf16, as the slot's row for
+//     the combine (half the traffic of fp32 rows, which at 32k routed slots
+//     outweigh every other operand of the layer).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -61,7 +63,7 @@ __global__ void __launch_bounds__(256) qgemm_smallk(SkinnyArgs p) {
     for (int e = threadIdx.x; e < 16 * MB * (cb1 - cb0) * 16; e += blockDim.x) {
       const int r = e / ((cb1 - cb0) * 16), cc = e - r * ((cb1 - cb0) * 16);
       const int id = p.sorted_ids[m0 + r];
-      if (id < p.n_slots) p.f32_out[(int64_t)id * ncol + cb0 * 16 + cc] = 0.f;
+      if (id < p.n_slots) p.rows16[(int64_t)id * ncol + cb0 * 16 + cc] = 0;
     }
     return;
   }
@@ -86,9 +88,9 @@ __global__ void __launch_bounds__(256) qgemm_smallk(SkinnyArgs p) {
       const int id = p.sorted_ids[m];
       oid[mb][r] = id;
       of[mb][r] = id < p.n_slots ? p.topk_w[id] * (ACT16 ? 1.f : p.a_scale[m]) : 0.f;
-      ooff[mb][r] = id < p.n_slots ? (id * ncol + c) * 4 : INT32_MIN;
+      ooff[mb][r] = id < p.n_slots ? (id * ncol + c) * 2 : INT32_MIN;
     }
-  const auto rout = __builtin_amdgcn_make_buffer_rsrc(p.f32_out, (short)0, (int)((int64_t)p.n_slots * ncol * 4),
+  const auto rout = __builtin_amdgcn_make_buffer_rsrc(p.rows16, (short)0, (int)((int64_t)p.n_slots * ncol * 2),
                                                       0x00020000);
   // m-blocks up to the last one that holds a slot (an expert's slots come
   // first in its aligned segment, so a block's padding rows usually fill its
@@ -210,7 +212,8 @@ __global__ void __launch_bounds__(256) qgemm_smallk(SkinnyArgs p) {
     for (int mb = 0; mb < L; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[mb][r] * of[mb][r]), rout, ooff[mb][r], cb * 64, 0);
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)float_to_bf16_bits(acc[mb][r] * of[mb][r]), rout, ooff[mb][r],
+                                              cb * 32, 0);
   };
   auto run = [&](auto L_c) {
     St st[D];

@@ -187,7 +187,7 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
         for (int e = tid; e < BM * C::BN; e += C::THREADS) {
           const int r = e / C::BN, cc = e - r * C::BN;
           const int id = p.sorted_ids[m0 + r];
-          if (id < p.n_slots) p.f32_out[(int64_t)id * N + tn * C::BN + cc] = 0.f;
+          if (id < p.n_slots) p.rows16[(int64_t)id * N + tn * C::BN + cc] = 0;
         }
       }
       return;
@@ -756,9 +756,9 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
           }
         } else {
           const float sa = (ACT_SCALE ? p.a_scale[m] : 1.f) * p.topk_w[id];
-          float* row = p.f32_out + (int64_t)id * N;  // this slot's weighted row
+          uint16_t* row = p.rows16 + (int64_t)id * N;  // this slot's weighted row, rounded to bf16
 #pragma unroll
-          for (int j = 0; j < NBW; ++j) row[nblk(j) * 16 + c16] = acc[mb][j][r] * sa;
+          for (int j = 0; j < NBW; ++j) row[nblk(j) * 16 + c16] = float_to_bf16_bits(acc[mb][j][r] * sa);
         }
       }
     }

@@ -375,11 +375,12 @@ hq_status hq_moe_align(int64_t t, int topk, int num_experts, int block_m, const 
  *                             intermediate of slot sorted_ids[r];
  *                             out = y [t, n] (plan out dtype),
  *                             y[tok] = sum_j topk_w[tok, j] * (a_row . W_e^T):
- *                             each slot's weighted fp32 row goes to the
- *                             workspace, then a second kernel sums a token's
- *                             topk rows in slot order and rounds once, so the
- *                             result is deterministic.  Slots with an
- *                             out-of-range expert id contribute zero.
+ *                             each slot's weighted row, rounded to bf16, goes
+ *                             to the workspace, then a second kernel sums a
+ *                             token's topk rows in fp32 in slot order and
+ *                             rounds once, so the result is deterministic.
+ *                             Slots with an out-of-range expert id
+ *                             contribute zero.
  *   epi HQ_EPI_NONE           gate_up rows without the activation: out
  *                             [max_padded, n] (plan out dtype).
  * a_scale: per-row fp32 scales of 8-bit activations (per token for gate_up,
@@ -387,7 +388,7 @@ hq_status hq_moe_align(int64_t t, int topk, int num_experts, int block_m, const 
  * (TOPK_COMBINE only).  Rows of padding slots (and, for gate_up, of slots
  * with an out-of-range expert id) are left unwritten.  ws: the workspace of
  * hq_moe_workspace_bytes (the fp8 requant's fp32 rows, or the combine's
- * t*topk weighted slot rows); every call writes what it reads, so its
+ * t*topk weighted bf16 slot rows); every call writes what it reads, so its
  * contents need no initialisation and no state carries over between calls
  * (two calls that overlap in time must not share one workspace).  As for
  * hq_gemm, activations or one expert's weights of 2 GiB or more are

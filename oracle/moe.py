@@ -21,6 +21,9 @@ Readings (listed with the rest in the design notes):
   sum over slots: y_t = sum_j w[t,j] * (act_{t,j} . W2_{e_j}^T), rounded to bf16.
 * Each stage is checked on the GPU's own input to that stage, so that a one-ulp
   flip in a requantised code does not cascade into the next stage.
+* Where the weighted slot rows are stored in bf16 before the sum over a
+  token's slots, each is a GEMM output with its own output rounding, and the
+  bound on y grows by that rounding (``rows_rounding_bound``).
 
 Align ("moe_align") has many correct results (any order inside an expert's
 segment); ``check_align`` verifies the invariants rather than an array.
@@ -157,22 +160,45 @@ def fp8_rows_bound(dq_gpu, scale_gpu, act64, tau_act):
     return tau_act + 0.5 * ulp(mag, "e4m3") * s + 2.0 ** -20 * np.abs(act64)
 
 
-def down_combine(act_rows, row_token, row_weight, row_expert, w2_codes, w2_scales, T: int):
+def rows_rounding_bound(o, tau_o, weight, topk: int, fmt: str = "bf16"):
+    """Bound on what rounding each weighted slot row to ``fmt`` adds to y.
+
+    Reading: where the down GEMM stores its per-slot rows in a 16-bit format
+    before the sum over the token's slots, those rows are GEMM outputs like
+    any other and carry their own output rounding (the tolerance rule is per
+    output of a GEMM with fp16/bf16 outputs).  The GPU's weighted row is
+    x = fl32(w * o_gpu) with |o_gpu - o| <= tau_o, so |x| <= B = |w| (|o| +
+    tau_o) (1 + 2^-23); rounding x to ``fmt`` moves it by at most half the
+    format's spacing at B, and the fp32 sum of topk such rows in slot order
+    adds at most topk 2^-23 B per row.  Returns that per-row bound, [R, N].
+    """
+    o = np.asarray(o, dtype=np.float64)
+    B = np.abs(np.asarray(weight, dtype=np.float64))[:, None] * (np.abs(o) + tau_o) * (1.0 + 2.0 ** -23)
+    return 0.5 * ulp(B, fmt) + topk * 2.0 ** -23 * B
+
+
+def down_combine(act_rows, row_token, row_weight, row_expert, w2_codes, w2_scales, T: int, rows_fmt=None,
+                 topk: int = 8):
     """Second expert GEMM, top-k weighting and combine, float64.
 
     act_rows float64 [R, I] (the GPU's own act values), row_token / row_weight
     / row_expert [R].  Returns dict(y64, tau_y) with tau_y = sum_j |w_j| tau_o
-    (without the output half-ulp, which ``gemm.check`` adds).
+    (without the output half-ulp, which ``gemm.check`` adds), plus, when the
+    weighted rows are stored in ``rows_fmt`` before the sum, the sum over the
+    token's rows of ``rows_rounding_bound``.
     """
     o, tau_o = grouped_gemm(act_rows, row_expert, w2_codes, w2_scales)
     H = o.shape[1]
     y = np.zeros((T, H))
     ty = np.zeros((T, H))
     wr = np.asarray(row_weight, dtype=np.float64)
+    extra = rows_rounding_bound(o, tau_o, wr, topk, rows_fmt) if rows_fmt else None
     for r in range(o.shape[0]):
         t = int(row_token[r])
         y[t] += wr[r] * o[r]
         ty[t] += abs(wr[r]) * tau_o[r]
+        if extra is not None:
+            ty[t] += extra[r]
     return {"y64": y, "tau_y": ty, "o": o, "tau_o": tau_o}
 
 

@@ -391,8 +391,9 @@ def test_moe_sizes_and_workspace():
     mp = hq.moe_max_padded(32, 8, 256, 16)
     assert b.value >= mp * 256 * 4
     pc = hq.MoePlan(7168, 256, hq.w4a16("bf16", scale="f16"), 256, 4096, "topk_combine")
-    # the combine's weighted slot rows: t * topk rows of n fp32
-    assert hq.lib().hq_moe_workspace_bytes(pc._h, 32, 8, ctypes.byref(b)) == 0 and b.value >= 32 * 8 * 7168 * 4
+    # the combine's weighted slot rows: t * topk rows of n bf16
+    assert hq.lib().hq_moe_workspace_bytes(pc._h, 32, 8, ctypes.byref(b)) == 0 and b.value >= 32 * 8 * 7168 * 2
+    assert b.value < 32 * 8 * 7168 * 2 + 256
 
 
 def test_moe_call_validation():

@@ -183,8 +183,9 @@ def run_layer(layer, T, act, topk, key=(5,), sample=None, masked=0.0):
         assert (err <= bound).all(), f"fp8 requant: {(err > bound).sum()} bad"
         act_rows = dq
     # down + combine: oracle on the GPU's act rows, for the sampled tokens
+    # the aligned path stores each weighted slot row in bf16 before the combine
     dc = om.down_combine(act_rows, row_tok, r["topk_w"].reshape(-1)[slot], row_exp, layer.w["w2"],
-                         layer.w["s2"].double().numpy(), T)
+                         layer.w["s2"].double().numpy(), T, rows_fmt="bf16", topk=topk)
     y_gpu = y.double().cpu().numpy()[toks]
     ok, _, ratio = og.check(y_gpu, dc["y64"][toks], dc["tau_y"][toks], "bf16")
     assert ok.all(), f"down+combine: {(~ok).sum()} bad, max err/tau {ratio.max():.3g}"
@@ -331,10 +332,10 @@ def test_fp8_requant_with_fewer_tokens_than_the_call_before(small_layer, small_l
 
 @pytest.mark.parametrize("act", ["bf16", "fp8"])
 def test_small_layer_many_slots_column_windows(act):
-    # 524288 routed slots of 1024 columns: the down GEMM and the combine run
-    # in two column windows (the weighted slot rows of one window stay within
-    # 1 GiB of workspace), checked on sampled tokens
-    lay = Layer(8, 1024, 128, key=(31,), max_t=65536, tuning=dict(tile_m=64))
+    # 524288 routed slots of 2048 columns: the down GEMM and the combine run
+    # in two column windows (the weighted bf16 slot rows of one window stay
+    # within 1 GiB of workspace), checked on sampled tokens
+    lay = Layer(8, 2048, 128, key=(31,), max_t=65536, tuning=dict(tile_m=64))
     run_layer(lay, 65536, act, 8, key=(37,), sample=24)
 
 

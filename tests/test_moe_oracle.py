@@ -152,6 +152,69 @@ def test_fp8_rows_bound_covers_perturbed_requant():
     assert np.all(np.abs(dq - act) <= b)
 
 
+def _combine_bf16_rows(o_gpu, w, topk):
+    # the aligned path's combine, simulated: x = fl32(w * o), rounded to bf16,
+    # then summed in fp32 over each token's topk rows in slot order
+    x = (np.float32(1) * w.astype(np.float32)[:, None] * o_gpu.astype(np.float32)).astype(np.float64)
+    r = F.rne(x, "bf16").astype(np.float32)
+    T = r.shape[0] // topk
+    y = r[0::topk].copy()
+    for j in range(1, topk):
+        y = (y + r[j::topk]).astype(np.float32)
+    return y.astype(np.float64).reshape(T, -1)
+
+
+def test_rows_rounding_bound_covers_simulated_combine():
+    rng = np.random.default_rng(10)
+    topk, T, N = 8, 64, 96
+    o = rng.standard_normal((T * topk, N)) * np.exp(rng.uniform(-6, 6, (T * topk, 1)))
+    tau = np.abs(o) * rng.uniform(0, 1e-3, o.shape)
+    w = rng.uniform(0, 1, T * topk)
+    o_gpu = o + rng.uniform(-1, 1, o.shape) * tau
+    y = _combine_bf16_rows(o_gpu, w, topk)
+    exact = (w[:, None] * o).reshape(T, topk, N).sum(1)
+    bound = (np.abs(w)[:, None] * tau + MO.rows_rounding_bound(o, tau, w, topk)).reshape(T, topk, N).sum(1)
+    assert np.all(np.abs(y - exact) <= bound)
+
+
+def test_rows_rounding_bound_at_midpoints_and_binade_crossings():
+    # a row value exactly halfway between two bf16 values rounds by half a
+    # spacing; a GPU value pushed over a power of two by its GEMM error is
+    # rounded on the coarser grid above it
+    topk = 1
+    mid = 1.0 + 3.0 * 2.0 ** -8                            # halfway between 1 + 2^-7 and 1 + 2^-6: rounds up
+    o = np.array([[1.0 + 2.0 ** -8, mid - 0.02, 3.0 * 2.0 ** -9 + 1.0]])
+    tau = np.array([[0.0, 0.02, 0.0]])
+    o_gpu = np.array([[1.0 + 2.0 ** -8, mid, 3.0 * 2.0 ** -9 + 1.0]])
+    w = np.array([1.0])
+    y = _combine_bf16_rows(o_gpu, w, topk)
+    err = np.abs(y - w[:, None] * o)
+    bound = np.abs(w)[:, None] * tau + MO.rows_rounding_bound(o, tau, w, topk)
+    assert np.all(err <= bound)
+    assert err[0, 0] == 2.0 ** -8                          # the half spacing is reached
+    # planted: the spacing taken at |w o| instead of the bound on the GPU value
+    planted = np.abs(w)[:, None] * tau + 0.5 * F.ulp(np.abs(w)[:, None] * np.abs(o), "bf16")
+    assert not np.all(err <= planted)
+    # planted: no rounding term at all
+    assert not np.all(err <= np.abs(w)[:, None] * tau + topk * 2.0 ** -23 * np.abs(o))
+
+
+def test_down_combine_rows_fmt_adds_the_rounding_term():
+    g = _gold("moe_tiny.json")
+    lay = _tiny_layer(g)
+    gu = MO.gate_up(lay["rows_a"], lay["row_exp"], lay["w1"], lay["s1"], g["I"])
+    plain = MO.down_combine(gu["act"], lay["row_tok"], lay["row_w"], lay["row_exp"], lay["w2"], lay["s2"], lay["T"])
+    rounded = MO.down_combine(gu["act"], lay["row_tok"], lay["row_w"], lay["row_exp"], lay["w2"], lay["s2"],
+                              lay["T"], rows_fmt="bf16", topk=lay["topk"])
+    assert np.array_equal(plain["y64"], rounded["y64"])
+    extra = MO.rows_rounding_bound(plain["o"], plain["tau_o"], lay["row_w"], lay["topk"])
+    want = plain["tau_y"].copy()
+    for r, t in enumerate(lay["row_tok"]):
+        want[t] += extra[r]
+    assert np.allclose(rounded["tau_y"], want, rtol=0, atol=0)
+    assert np.all(rounded["tau_y"][np.abs(plain["y64"]) > 0] > plain["tau_y"][np.abs(plain["y64"]) > 0])
+
+
 def test_fp8_scale_matches_row_maximum():
     rng = np.random.default_rng(9)
     act = rng.standard_normal((16, 256))
