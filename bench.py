@@ -307,6 +307,13 @@ SQ_PASSES = ("SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ
              "SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU",
              "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_INSTS_VMEM_RD SQ_INST_LEVEL_VMEM "
              "SQ_ACTIVE_INST_LDS SQ_WAVES")
+# memory side, for the weight-streaming decode kernels (a third pass where it was taken)
+MEM_PASS = ("TCP_TCC_READ_REQ_LATENCY_sum TCP_TCC_READ_REQ_sum TCP_PENDING_STALL_CYCLES_sum "
+            "TCP_READ_TAGCONFLICT_STALL_CYCLES_sum TA_BUSY_avr TA_ADDR_STALLED_BY_TC_CYCLES_sum TCC_HIT_sum TCC_MISS_sum "
+            "GRBM_GUI_ACTIVE SQ_WAVES")
+# workloads whose counter passes run with other flags than the per-workload bench
+_COUNTER_ONLY = {"decode": ("qgemm_decode_sweep_w4a16_bf16.md", "dense W4A16 decode sweep, bf16, uint4 zero points, "
+                            "M in {1,4,16,64} x (N,K) in {(4096,4096),(14336,4096),(4096,14336)}", "--no-extra")}
 
 
 def _write_counter_profiles(run_dir, rows):
@@ -314,21 +321,31 @@ def _write_counter_profiles(run_dir, rows):
     each SQ counter over its dispatches, and the derived figures."""
     import collections
 
-    for w, (fname, what) in _WORKLOAD_PROFILES.items():
+    todo = {w: (fname, what, "") for w, (fname, what) in _WORKLOAD_PROFILES.items()}
+    todo.update(_COUNTER_ONLY)
+    for w, (fname, what, flags) in todo.items():
         paths = [os.path.join(run_dir, f"sq_{w}_{i}", f"c_counter_collection.csv") for i in (1, 2)]
         if not all(os.path.exists(x) for x in paths):
             continue
+        mem = os.path.exists(os.path.join(run_dir, f"sq_{w}_3", "c_counter_collection.csv"))
         agg = collections.defaultdict(lambda: collections.defaultdict(list))
         for i in (1, 2):
             for r in rows(f"sq_{w}_{i}/c_counter_collection.csv"):
                 k = r["Kernel_Name"].split("(")[0]
                 if "hq::" in k:
                     agg[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
-        L = [f"# SQ counters: {what}", "", "Two counter passes of the workload's bench (from the repository root on the "
-             "GPU host), then this summary on the CPU:", "", "```"]
-        for i, c in enumerate(SQ_PASSES, 1):
+        magg = collections.defaultdict(lambda: collections.defaultdict(list))
+        if mem:
+            for r in rows(f"sq_{w}_3/c_counter_collection.csv"):
+                k = r["Kernel_Name"].split("(")[0]
+                if "hq::" in k:
+                    magg[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        L = [f"# SQ counters: {what}", "", f"{3 if mem else 2} counter passes of the workload's bench (from the "
+             "repository root on the GPU host), then this summary on the CPU:", "", "```"]
+        extra = f" {flags}" if flags else ""
+        for i, c in enumerate(SQ_PASSES + ((MEM_PASS,) if mem else ()), 1):
             L.append(f"cd /tmp && rocprofv3 --pmc {c} --output-format csv -d <repo>/gpurun_out/sq_{w}_{i} -o c -- "
-                     f"python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu")
+                     f"python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu{extra}")
         means = {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in agg.items()}
 
         def busy_ratio(m):
@@ -365,10 +382,55 @@ def _write_counter_profiles(run_dir, rows):
             L.append(f"| `{k[:80]}` | {n} | {m.get('SQ_WAVES', 0.0):.0f} | {mf:.0f} | {vpm} | {bc:.3f} | "
                      f"{m.get('SQ_WAIT_ANY', 0.0) / wc:.2f} | {m.get('SQ_ACTIVE_INST_ANY', 0.0) / wc:.2f} | {br:.3f} | "
                      f"{rel} |")
+        if mem:
+            L += _memory_table(magg, run_dir, w)
         out = fname.replace(".md", "_sq_counters.md")
         with open(os.path.join(ROOT, "profiles", out), "w") as f:
             f.write("\n".join(L) + "\n")
         print(f"wrote profiles/{out}")
+
+
+def _memory_table(magg, run_dir, w):
+    """The memory-side pass, per kernel: L1 -> L2 read latency, L2 hit rate,
+    and the shares of the texture units' busy time lost to cache stalls, with
+    the plain streaming read of the same run as the reference."""
+    cus = 256
+    try:
+        import csv
+        with open(os.path.join(run_dir, f"sq_{w}_3", "c_agent_info.csv")) as f:
+            for r in csv.DictReader(f):
+                if int(r.get("cu_count", 0) or 0) > 0:
+                    cus = int(r["cu_count"])
+    except (OSError, ValueError, KeyError):
+        pass
+    L = ["", "Memory-side pass (third command), per kernel, the means over its dispatches:",
+         "* L1 -> L2 read latency: TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ, cycles per read request;",
+         "* L2 hit rate: TCC_HIT / (TCC_HIT + TCC_MISS);",
+         f"* as shares of the texture units' busy cycles ({cus} x TA_BUSY_avr, one unit per CU): cycles the L1 "
+         "stalled with its pending-miss tracking full (TCP_PENDING_STALL_CYCLES), on read tag conflicts "
+         "(TCP_READ_TAGCONFLICT_STALL_CYCLES), and cycles the address path waited on the L1 "
+         "(TA_ADDR_STALLED_BY_TC_CYCLES);",
+         "* TA busy: TA_BUSY_avr / GRBM_GUI_ACTIVE, relative to the same ratio of the plain streaming read "
+         "(`stream_read_kernel`) in the same run.", "",
+         "| kernel | dispatches | L1 -> L2 latency (cycles) | L2 hit rate | pending-miss stall | tag-conflict stall | "
+         "address stalled by L1 | TA busy vs the plain read |", "|---|---|---|---|---|---|---|---|"]
+    means = {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in magg.items()}
+
+    def ta_busy(m):
+        return m.get("TA_BUSY_avr", 0.0) / max(m.get("GRBM_GUI_ACTIVE", 0.0), 1.0)
+
+    ref = next((ta_busy(m) for k, m in means.items() if "stream_read_kernel" in k), 0.0)
+    for k, m in sorted(means.items()):
+        n = max(len(v) for v in magg[k].values())
+        lat = m.get("TCP_TCC_READ_REQ_LATENCY_sum", 0.0) / max(m.get("TCP_TCC_READ_REQ_sum", 0.0), 1.0)
+        h, mi = m.get("TCC_HIT_sum", 0.0), m.get("TCC_MISS_sum", 0.0)
+        hit = f"{h / (h + mi):.2f}" if h + mi > 0 else "-"
+        tb = max(cus * m.get("TA_BUSY_avr", 0.0), 1.0)
+        rel = f"{ta_busy(m) / ref:.2f}" if ref > 0 else "-"
+        L.append(f"| `{k[:80]}` | {n} | {lat:.0f} | {hit} | {m.get('TCP_PENDING_STALL_CYCLES_sum', 0.0) / tb:.2f} | "
+                 f"{m.get('TCP_READ_TAGCONFLICT_STALL_CYCLES_sum', 0.0) / tb:.2f} | "
+                 f"{m.get('TA_ADDR_STALLED_BY_TC_CYCLES_sum', 0.0) / tb:.2f} | {rel} |")
+    return L
 
 
 def algo_bytes(M, N, K):
