@@ -247,7 +247,7 @@ _WORKLOAD_PROFILES = {
     "nvfp4": ("qgemm_w4a16_nvfp4_bf16_n4096_k4096.md", "dense W4A16-NVFP4, M in {1,16,64,1024}, N = K = 4096, "
               "bf16"),
     "moe": ("moe_layer_e256_top8_h7168_i256.md", "MoE layer, 256 experts, top-8, hidden 7168, intermediate 256, "
-            "T in {1,32,512,4096} (aligned) and {1,4,8,32} (by slot), bf16 and fp8 activations"),
+            "T in {1,4,8,32,512,4096} (aligned) and {1,4,8,32} (by slot), bf16 and fp8 activations"),
 }
 
 
@@ -1056,7 +1056,7 @@ def _w4a4_points(dev):
         "E8M0 scales per 32), bf16 output", "f4"
 
 
-def _moe_points(dev, Ts=(1, 32, 512, 4096), acts=("bf16", "fp8"), slot_Ts=(1, 4, 8, 32)):
+def _moe_points(dev, Ts=(1, 4, 8, 32, 512, 4096), acts=("bf16", "fp8"), slot_Ts=(1, 4, 8, 32)):
     import bit_quantized_gemm_repack_amd as hq
     import datagen
 
@@ -1170,7 +1170,7 @@ def _moe_points(dev, Ts=(1, 32, 512, 4096), acts=("bf16", "fp8"), slot_Ts=(1, 4,
     return pts, "MoE layer TFLOPS and effective HBM GB/s vs T", \
         "MoE layer on one GPU's tensor-parallel share: 256 experts, top-8, hidden 7168, intermediate 256; " \
         "align + gate_up (SiLU * up; bf16, or fp8 requant for W4A8-FP8) + down with the top-k combine; INT4 " \
-        "weights (group 128, fp16 scales, zero point 8); T in {1,32,512,4096}; the unaligned by-slot path " \
+        "weights (group 128, fp16 scales, zero point 8); T in {1,4,8,32,512,4096}; the unaligned by-slot path " \
         "(gate_up + down, no align) at T in {1,4,8,32}; small T cycles through routings so passes stay cold", \
         "bf16/f8"
 
