@@ -359,6 +359,46 @@ def test_small_layer_by_slot_tunings(tun, act):
     run_layer_by_slot(Layer(8, 512, 128, key=(7,), tuning=tun), 6, act, 4, key=(47,))
 
 
+@pytest.mark.parametrize("act", ["bf16", "fp8"])
+def test_small_layer_plain_epilogue_aligned_and_by_slot(small_layer, act):
+    # the grouped GEMM without an activation (epilogue "none"): rows x_tok . W1_e^T of
+    # every slot, by aligned position and by slot; a masked slot gives no aligned row
+    # and a zero row by slot
+    lay = small_layer
+    E, H, I, T, topk = lay.E, lay.H, lay.I, 9, 3
+    _log(f"moe plain epilogue T={T} topk={topk} act={act}")
+    r = datagen.moe_routing(T, E=E, topk=topk, key=(61,))
+    ids_h = r["topk_ids"].copy()
+    ids_h[0, 1] = -1
+    x = datagen.moe_activations(T, H=H, act=act, key=(61,))
+    w1, m1 = lay.dev[act][2], lay.dev[act][3]
+    p = hq.MoePlan(2 * I, H, _quant(act), E, 4096, "none")
+    ids = torch.from_numpy(ids_h).to(DEV)
+    a = (x["x"] if act == "bf16" else x["x_codes"]).to(DEV)
+    xs = None if act == "bf16" else x["x_scale"].to(DEV)
+    sid, bex, npad = hq.moe_align(ids, E, p.block_m(T, topk))
+    out_al = p.moe_gemm(a, T, topk, sid, bex, npad, w1, m1, a_scale=xs)
+    out_sl = p.moe_gemm_by_slot(a, T, topk, ids, w1, m1, a_scale=xs)
+    torch.cuda.synchronize()
+    if act == "bf16":
+        xt = x["x"].double().numpy()
+    else:
+        xt = e4m3_value(x["x_codes"].numpy()) * x["x_scale"].numpy()[:, None].astype(np.float64)
+    flat = ids_h.reshape(-1)
+    slots = np.nonzero((flat >= 0) & (flat < E))[0]
+    o, tau = om.grouped_gemm(xt[slots // topk], flat[slots], lay.w["w1"], lay.w["s1"].double().numpy())
+    sl = out_sl.double().cpu().numpy()
+    assert sl.shape == (T * topk, 2 * I)
+    ok, _, ratio = og.check(sl[slots], o, tau, "bf16")
+    assert ok.all(), f"by slot: {(~ok).sum()} bad, max err/tau {ratio.max():.3g}"
+    assert (sl[~np.isin(np.arange(T * topk), slots)] == 0).all()
+    sid_h = sid.cpu().numpy()
+    pos = {int(v): i for i, v in enumerate(sid_h[: int(npad.cpu()[0])]) if v < T * topk}
+    al = out_al.double().cpu().numpy()[[pos[int(v)] for v in slots]]
+    ok, _, ratio = og.check(al, o, tau, "bf16")
+    assert ok.all(), f"aligned: {(~ok).sum()} bad, max err/tau {ratio.max():.3g}"
+
+
 def test_by_slot_fp8_workspace_reuse(small_layer):
     # one workspace across calls of falling size: each call's scales come from its own rows
     ws = small_layer.dev["fp8"][0].moe_workspace(64, 8, DEV)
