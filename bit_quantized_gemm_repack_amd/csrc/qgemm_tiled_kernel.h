@@ -32,15 +32,19 @@
 //     (times the row scale); a second kernel sums the splits in index order.
 //   * Dense tiles are ordered so that the workgroups the hardware places on
 //     one XCD (consecutive ids modulo 8) share the same activation rows.
-//   * Grouped mode (MoE): grid y walks the expert-aligned blocks of BM slots,
-//     rows are gathered by token (gate_up) or taken in aligned order (down);
-//     epilogues as in the skinny kernel (SiLU * mul, fp32 + row max for the
-//     fp8 requant, each slot's weighted fp32 row for the combine kernel).
+//   * Grouped mode (MoE): a persistent grid of resident workgroups walks the
+//     (expert-aligned block of BM slots, column tile) pairs up to the used
+//     length of the aligned array; rows are gathered by token (gate_up) or
+//     taken in aligned order (down); epilogues as in the skinny kernel (SiLU *
+//     mul, fp32 rows for the fp8 requant, each slot's weighted bf16 row for
+//     the combine kernel).
 #pragma once
 
 #ifndef __HIPCC_RTC__  // the run-time compiler takes the kernel only (hq_plan_set_jit)
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #endif
 
 #include <type_traits>
@@ -117,23 +121,14 @@ __device__ inline void pin(T& x) {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// MC, NC, KC: the call's M, N and K as compile-time constants (run-time
-// specialisation, hq_plan_set_jit); 0 takes them from the arguments.  SL:
-// the stage ring is a static LDS array (a run-time compiled module has no
-// dynamic-LDS attribute to raise), not the launch's dynamic LDS.
-template <int FMT, int BM, int NBW, int GRP, int ST, int MC = 0, int NC = 0, int KC = 0, int SL = 0>
-__global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
+// One BM x BN tile (row tile tm, column tile tn) of the GEMM; `lds` is the
+// workgroup's stage ring.  MC, NC, KC: the call's M, N and K as compile-time
+// constants (run-time specialisation, hq_plan_set_jit); 0 takes them from the
+// arguments.
+template <int FMT, int BM, int NBW, int GRP, int ST, int MC, int NC, int KC>
+__device__ __forceinline__ void qgemm_tiled_tile(const TiledArgs& p, uint8_t* lds, int tm, int tn) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses device-only builtins; the host pass needs only the stub
   using C = TCfg<FMT, BM, NBW, ST>;
-  static_assert(C::FITS, "loads in flight exceed the counter, or the ring the LDS");
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
-  uint8_t* lds;
-  if constexpr (SL) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds_st[C::LDS_BYTES];
-    lds = lds_st;
-  } else {
-    lds = lds_dyn;
-  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -148,28 +143,6 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
   const int split = (GRP == GRP_DENSE) ? (int)blockIdx.y : 0;
   const int gb = split * p.gps;                   // first group of this split
   const int Gl = min(G - gb, p.gps);              // groups of this split (>= 1)
-
-  int tm, tn;
-  if constexpr (GRP == GRP_DENSE) {
-    // XCD-aware order: ids dealt round-robin to the 8 XCDs get consecutive
-    // logical tiles on each XCD.  Logical tiles run in groups of group_m row
-    // tiles, each group column by column, so the tiles one XCD holds at a time
-    // form a block (group_m rows x a few columns) that shares both its
-    // activation rows and its weight columns through that XCD's L2.
-    const int nwg = gridDim.x;
-    int lid = blockIdx.x;
-    if ((nwg & 7) == 0) lid = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
-    const int per = p.group_m * p.tiles_n;  // tiles per group
-    const int grp = lid / per;
-    const int first = grp * p.group_m;
-    const int gsz = min(p.tiles_m - first, p.group_m);
-    const int r = lid - grp * per;
-    tm = first + r % gsz;
-    tn = r / gsz;
-  } else {
-    tn = blockIdx.x;
-    tm = blockIdx.y;
-  }
   const int m0 = tm * BM;
 
   const uint8_t* wbytes = static_cast<const uint8_t*>(p.w);
@@ -766,6 +739,57 @@ __global__ void __launch_bounds__(256) qgemm_tiled(TiledArgs p) {
 #endif
 }
 
+// The kernel.  SL: the stage ring is a static LDS array (a run-time compiled
+// module has no dynamic-LDS attribute to raise), not the launch's dynamic
+// LDS.  Grouped 64-row tiles are held to two waves per SIMD (the persistent
+// loop below must not cost the tile its occupancy).
+template <int FMT, int BM, int NBW, int GRP, int ST, int MC = 0, int NC = 0, int KC = 0, int SL = 0>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((GRP != GRP_DENSE && BM == 64) ? 2 : 1)))
+qgemm_tiled(TiledArgs p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using C = TCfg<FMT, BM, NBW, ST>;
+  static_assert(C::FITS, "loads in flight exceed the counter, or the ring the LDS");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+  uint8_t* lds;
+  if constexpr (SL) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds_st[C::LDS_BYTES];
+    lds = lds_st;
+  } else {
+    lds = lds_dyn;
+  }
+  if constexpr (GRP == GRP_DENSE) {
+    // XCD-aware order: ids dealt round-robin to the 8 XCDs get consecutive
+    // logical tiles on each XCD.  Logical tiles run in groups of group_m row
+    // tiles, each group column by column, so the tiles one XCD holds at a time
+    // form a block (group_m rows x a few columns) that shares both its
+    // activation rows and its weight columns through that XCD's L2.
+    const int nwg = gridDim.x;
+    int lid = blockIdx.x;
+    if ((nwg & 7) == 0) lid = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+    const int per = p.group_m * p.tiles_n;  // tiles per group
+    const int grp = lid / per;
+    const int first = grp * p.group_m;
+    const int gsz = min(p.tiles_m - first, p.group_m);
+    const int r = lid - grp * per;
+    qgemm_tiled_tile<FMT, BM, NBW, GRP, ST, MC, NC, KC>(p, lds, first + r % gsz, r / gsz);
+  } else {
+    // Grouped: persistent.  The launch holds as many workgroups as the chip
+    // keeps resident (at most one per tile); each takes the (aligned block,
+    // column tile) pairs blockIdx.x, blockIdx.x + gridDim.x, ... up to the
+    // used length of the aligned array, read here, so that no workgroup is
+    // spent on the padding the host had to allow for.  Consecutive pairs share
+    // a block (one expert's weights, the same activation rows).
+    const int used = min(p.tiles_m, (*p.num_padded + BM - 1) / BM);
+    const int total = used * p.tiles_n;
+    for (int t = blockIdx.x; t < total; t += gridDim.x) {
+      const int tm = t / p.tiles_n;
+      qgemm_tiled_tile<FMT, BM, NBW, GRP, ST, MC, NC, KC>(p, lds, tm, t - tm * p.tiles_n);
+      __syncthreads();  // every wave is done with the stage ring before the next tile refills it
+    }
+  }
+#endif
+}
+
 #ifndef __HIPCC_RTC__
 // ---------------------------------------------------------------------------
 // dispatch
@@ -781,6 +805,28 @@ inline hipError_t launch_tiled_t(const TiledArgs& a, dim3 grid, hipStream_t s) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_done = true;
+  }
+  if constexpr (GRP != GRP_DENSE) {
+    // grouped launches are persistent: grid (column tiles, aligned blocks)
+    // becomes as many workgroups as the chip keeps resident, at most one per
+    // tile (the same count on every MI355X, so kept per instantiation)
+    static int resident = 0;
+    if (!resident) {
+      int dev = 0, cus = 0, per = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, reinterpret_cast<const void*>(kern), C::THREADS,
+                                                         (size_t)C::LDS_BYTES);
+      if (e != hipSuccess) return e;
+      resident = std::max(1, cus) * std::max(1, per);
+    }
+    TiledArgs b = a;
+    b.tiles_n = (int)grid.x;
+    b.tiles_m = (int)grid.y;
+    const int64_t tiles = (int64_t)grid.x * grid.y;
+    const dim3 pg((unsigned)std::min<int64_t>(tiles, resident));
+    return launch_timed(kern, pg, dim3(C::THREADS), (size_t)C::LDS_BYTES, s, b);
   }
   return launch_timed(kern, grid, dim3(C::THREADS), (size_t)C::LDS_BYTES, s, a);
 }
