@@ -752,3 +752,43 @@ class MoePlan(Plan):
                                          _ptr(topk_w), _ptr(w), _ptr(meta), _ptr(out), _ptr(out_scale), _ptr(ws),
                                          ws_bytes, _stream_ptr(dev)))
         return (out, out_scale) if self.epi == EPI_SILU_MUL_QFP8 else out
+
+
+# Routed slots (t * topk) up to which moe_layer takes the unaligned by-slot
+# path: measured on MI355X (256 experts, top 8, H = 7168, I = 256) it is the
+# faster one up to 32 slots and level with the aligned path at 64, where an
+# expert picked by several slots starts to be read once per slot.
+MOE_BY_SLOT_MAX_SLOTS = 64
+
+
+def moe_uses_by_slot(t: int, topk: int) -> bool:
+    """Whether moe_layer runs a call of t tokens routed to topk experts each
+    through hq_moe_gemm_by_slot (else the aligned hq_moe_align + hq_moe_gemm)."""
+    return 0 < int(t) * int(topk) <= MOE_BY_SLOT_MAX_SLOTS
+
+
+def moe_layer(gate_up: "MoePlan", down: "MoePlan", x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
+              w1: torch.Tensor, m1: torch.Tensor, w2: torch.Tensor, m2: torch.Tensor, x_scale=None,
+              by_slot: Optional[bool] = None) -> torch.Tensor:
+    """One MoE layer, y [t, n_down]: gate_up (SiLU * up, or with the fp8
+    requant) then down with the top-k combine, on the by-slot path for
+    decode-sized calls (moe_uses_by_slot) and the aligned path otherwise;
+    `by_slot` forces one.  x: [t, k] activations (fp8 codes with x_scale for
+    W4A8); topk_ids int32 / topk_w fp32 [t, topk] on the GPU."""
+    t, topk = topk_ids.shape
+    if down.epi != EPI_TOPK_COMBINE or gate_up.epi not in (EPI_SILU_MUL, EPI_SILU_MUL_QFP8):
+        raise ValueError("moe_layer takes a gate_up plan (silu_mul / silu_mul_qfp8) and a topk_combine plan")
+    fp8 = gate_up.epi == EPI_SILU_MUL_QFP8
+    if by_slot is None:
+        by_slot = moe_uses_by_slot(t, topk)
+    if by_slot:
+        r = gate_up.moe_gemm_by_slot(x, t, topk, topk_ids, w1, m1, a_scale=x_scale)
+        act, scl = r if fp8 else (r, None)
+        return down.moe_gemm_by_slot(act, t, topk, topk_ids, w2, m2, a_scale=scl, topk_w=topk_w)
+    bm = gate_up.block_m(t, topk)
+    if down.block_m(t, topk) != bm:
+        raise ValueError("the gate_up and down plans must share one alignment block size (equal tuning)")
+    sid, bex, npad = moe_align(topk_ids, gate_up.num_experts, bm)
+    r = gate_up.moe_gemm(x, t, topk, sid, bex, npad, w1, m1, a_scale=x_scale)
+    act, scl = r if fp8 else (r, None)
+    return down.moe_gemm(act, t, topk, sid, bex, npad, w2, m2, a_scale=scl, topk_w=topk_w)

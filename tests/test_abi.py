@@ -462,6 +462,18 @@ def test_moe_by_slot_call_validation():
     assert f(huge._h, 1, 8, *args(), 0, None) == hq.HQ_ERR_UNSUPPORTED
 
 
+def test_moe_layer_path_choice():
+    """Host logic: moe_layer takes the by-slot path up to 64 routed slots."""
+    assert hq.moe_uses_by_slot(1, 8) and hq.moe_uses_by_slot(8, 8) and hq.moe_uses_by_slot(32, 2)
+    assert not hq.moe_uses_by_slot(9, 8) and not hq.moe_uses_by_slot(4096, 8) and not hq.moe_uses_by_slot(0, 8)
+    q = hq.w4a16("bf16", scale="f16")
+    g = hq.MoePlan(512, 7168, q, 256, 64, "silu_mul")
+    d = hq.MoePlan(7168, 256, q, 256, 64, "topk_combine")
+    ids = torch.zeros((1, 8), dtype=torch.int32)
+    with pytest.raises(ValueError):                       # plans in the wrong roles
+        hq.moe_layer(d, g, None, ids, None, None, None, None, None)
+
+
 def test_quantize_call_validation():
     """Argument checks of hq_quantize_per_token run before any launch (no GPU needed)."""
     L = hq.lib()

@@ -399,6 +399,36 @@ def test_small_layer_plain_epilogue_aligned_and_by_slot(small_layer, act):
     assert ok.all(), f"aligned: {(~ok).sum()} bad, max err/tau {ratio.max():.3g}"
 
 
+@pytest.mark.parametrize("act", ["bf16", "fp8"])
+@pytest.mark.parametrize("T,topk", [(2, 8), (40, 3)])
+def test_moe_layer_helper_matches_its_path(small_layer, T, topk, act):
+    # hq.moe_layer picks the by-slot path for few routed slots, the aligned one
+    # otherwise, and returns what the explicit calls of that path return
+    lay = small_layer
+    _log(f"moe_layer helper T={T} topk={topk} act={act}")
+    r = datagen.moe_routing(T, E=lay.E, topk=topk, key=(67,))
+    x = datagen.moe_activations(T, H=lay.H, act=act, key=(67,))
+    p1, p2, w1, m1, w2, m2 = lay.dev[act]
+    ids = torch.from_numpy(r["topk_ids"]).to(DEV)
+    tw = torch.from_numpy(r["topk_w"]).to(DEV)
+    a = (x["x"] if act == "bf16" else x["x_codes"]).to(DEV)
+    xs = None if act == "bf16" else x["x_scale"].to(DEV)
+    y = hq.moe_layer(p1, p2, a, ids, tw, w1, m1, w2, m2, x_scale=xs)
+    by_slot = hq.moe_uses_by_slot(T, topk)
+    assert by_slot == (T * topk <= 64)
+    if by_slot:
+        res = p1.moe_gemm_by_slot(a, T, topk, ids, w1, m1, a_scale=xs)
+        act_out, scl = res if act == "fp8" else (res, None)
+        ref = p2.moe_gemm_by_slot(act_out, T, topk, ids, w2, m2, a_scale=scl, topk_w=tw)
+    else:
+        sid, bex, npad = hq.moe_align(ids, lay.E, p1.block_m(T, topk))
+        res = p1.moe_gemm(a, T, topk, sid, bex, npad, w1, m1, a_scale=xs)
+        act_out, scl = res if act == "fp8" else (res, None)
+        ref = p2.moe_gemm(act_out, T, topk, sid, bex, npad, w2, m2, a_scale=scl, topk_w=tw)
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref)
+
+
 def test_by_slot_fp8_workspace_reuse(small_layer):
     # one workspace across calls of falling size: each call's scales come from its own rows
     ws = small_layer.dev["fp8"][0].moe_workspace(64, 8, DEV)
