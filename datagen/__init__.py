@@ -192,8 +192,8 @@ def moe_routing(T: int, E: int = 256, topk: int = 8, key=(5,)):
 def moe_activations(T: int, H: int = 7168, act: str = "bf16", key=(5,)):
     rng = rng_for(*key, T, H, 2)
     x = rng.standard_normal((T, H))
-    if act == "bf16":
-        return {"x": _to_dtype(x, torch.bfloat16)}
+    if act in ("bf16", "f16"):
+        return {"x": _to_dtype(x, torch.bfloat16 if act == "bf16" else torch.float16)}
     codes, s = quant_per_token(torch.from_numpy(x.astype(np.float32)), "fp8")
     return {"x_codes": codes, "x_scale": s}
 

@@ -79,20 +79,29 @@ def test_align_degenerate_cases():
 # --------------------------------------------------------- layer pipeline --
 
 def _quant(act):
-    return hq.w4a16("bf16", scale="f16") if act == "bf16" else hq.w4a8_fp8(scale="f16")
+    if act in ("bf16", "f16"):
+        return hq.w4a16(act, scale="f16")
+    return hq.w4a8_fp8(scale="f16")
+
+
+def _out_fmt(act):
+    return "f16" if act == "f16" else "bf16"
+
+
+ACTS = ("bf16", "fp8", "f16")
 
 
 class Layer:
     """Weights on the GPU (repacked for both activation types) + host copies.
     `tuning` (same for both GEMMs) forces a kernel / block size."""
 
-    def __init__(self, E, H, I, key, tuning=None, max_t=4096):
+    def __init__(self, E, H, I, key, tuning=None, max_t=4096, acts=ACTS):
         self.E, self.H, self.I = E, H, I
         wts = datagen.moe_weights(E, H, I, key=key)
         self.w = wts
         self.dev = {}
-        for act in ("bf16", "fp8"):
-            p1 = hq.MoePlan(2 * I, H, _quant(act), E, max_t, "silu_mul" if act == "bf16" else "silu_mul_qfp8",
+        for act in acts:
+            p1 = hq.MoePlan(2 * I, H, _quant(act), E, max_t, "silu_mul_qfp8" if act == "fp8" else "silu_mul",
                             tuning=tuning)
             p2 = hq.MoePlan(H, I, _quant(act), E, max_t, "topk_combine", tuning=tuning)
             w1, m1 = p1.repack(torch.from_numpy(wts["w1"]).to(DEV), wts["s1"].to(DEV))
@@ -121,7 +130,7 @@ def run_layer(layer, T, act, topk, key=(5,), sample=None, masked=0.0):
     bm = p1.block_m(T, topk)
     assert p2.block_m(T, topk) == bm
     sid, bexp, npad = hq.moe_align(ids, E, bm)
-    if act == "bf16":
+    if act != "fp8":
         a = x["x"].to(DEV)
         act_out = p1.moe_gemm(a, T, topk, sid, bexp, npad, w1, m1)
         y = p2.moe_gemm(act_out, T, topk, sid, bexp, npad, w2, m2, topk_w=torch.from_numpy(r["topk_w"]).to(DEV))
@@ -148,14 +157,14 @@ def run_layer(layer, T, act, topk, key=(5,), sample=None, masked=0.0):
     row_exp = bexp_h[rows // bm]
 
     # gate_up: oracle on the GPU's stage input (the same x)
-    if act == "bf16":
+    if act != "fp8":
         xa = x["x"].double().numpy()[row_tok]
     else:
         xa = e4m3_value(x["x_codes"].numpy()[row_tok]) * x["x_scale"].numpy()[row_tok, None].astype(np.float64)
     gu = om.gate_up(xa, row_exp, layer.w["w1"], layer.w["s1"].double().numpy(), I)
-    if act == "bf16":
+    if act != "fp8":
         act_gpu = act_out.double().cpu().numpy()[rows]
-        ok, _, ratio = og.check(act_gpu, gu["act"], gu["tau_act"], "bf16")
+        ok, _, ratio = og.check(act_gpu, gu["act"], gu["tau_act"], _out_fmt(act))
         assert ok.all(), f"gate_up act: {(~ok).sum()} bad, max err/tau {ratio.max():.3g}"
         act_rows = act_gpu
     else:
@@ -187,7 +196,7 @@ def run_layer(layer, T, act, topk, key=(5,), sample=None, masked=0.0):
     dc = om.down_combine(act_rows, row_tok, r["topk_w"].reshape(-1)[slot], row_exp, layer.w["w2"],
                          layer.w["s2"].double().numpy(), T, rows_fmt="bf16", topk=topk)
     y_gpu = y.double().cpu().numpy()[toks]
-    ok, _, ratio = og.check(y_gpu, dc["y64"][toks], dc["tau_y"][toks], "bf16")
+    ok, _, ratio = og.check(y_gpu, dc["y64"][toks], dc["tau_y"][toks], _out_fmt(act))
     assert ok.all(), f"down+combine: {(~ok).sum()} bad, max err/tau {ratio.max():.3g}"
     return ratio.max()
 
@@ -211,7 +220,7 @@ def run_layer_by_slot(layer, T, act, topk, key=(5,), sample=None, masked=0.0, ws
     ids = torch.from_numpy(r["topk_ids"]).to(DEV)
     tw = torch.from_numpy(r["topk_w"]).to(DEV)
     S = T * topk
-    if act == "bf16":
+    if act != "fp8":
         act_out = p1.moe_gemm_by_slot(x["x"].to(DEV), T, topk, ids, w1, m1)
         y = p2.moe_gemm_by_slot(act_out, T, topk, ids, w2, m2, topk_w=tw)
     else:
@@ -230,16 +239,16 @@ def run_layer_by_slot(layer, T, act, topk, key=(5,), sample=None, masked=0.0, ws
     valid = (flat[slots] >= 0) & (flat[slots] < E)
     vs, bad = slots[valid], slots[~valid]
     row_tok, row_exp = vs // topk, flat[vs]
-    if act == "bf16":
+    if act != "fp8":
         xa = x["x"].double().numpy()[row_tok]
     else:
         xa = e4m3_value(x["x_codes"].numpy()[row_tok]) * x["x_scale"].numpy()[row_tok, None].astype(np.float64)
     gu = om.gate_up(xa, row_exp, layer.w["w1"], layer.w["s1"].double().numpy(), I)
-    if act == "bf16":
+    if act != "fp8":
         assert tuple(act_out.shape) == (S, I)
         out_h = act_out.double().cpu().numpy()
         act_rows = out_h[vs]
-        ok, _, ratio = og.check(act_rows, gu["act"], gu["tau_act"], "bf16")
+        ok, _, ratio = og.check(act_rows, gu["act"], gu["tau_act"], _out_fmt(act))
         assert ok.all(), f"gate_up act: {(~ok).sum()} bad, max err/tau {ratio.max():.3g}"
         assert (out_h[bad] == 0).all(), "rows of out-of-range slots must be zero"
     else:
@@ -261,7 +270,7 @@ def run_layer_by_slot(layer, T, act, topk, key=(5,), sample=None, masked=0.0, ws
     dc = om.down_combine(act_rows, row_tok, r["topk_w"].reshape(-1)[vs], row_exp, layer.w["w2"],
                          layer.w["s2"].double().numpy(), T)
     y_gpu = y.double().cpu().numpy()[toks]
-    ok, _, ratio = og.check(y_gpu, dc["y64"][toks], dc["tau_y"][toks], "bf16")
+    ok, _, ratio = og.check(y_gpu, dc["y64"][toks], dc["tau_y"][toks], _out_fmt(act))
     assert ok.all(), f"down+combine by slot: {(~ok).sum()} bad, max err/tau {ratio.max():.3g}"
     return ratio.max()
 
@@ -271,7 +280,7 @@ def small_layer():
     return Layer(8, 512, 128, key=(7,))
 
 
-@pytest.mark.parametrize("act", ["bf16", "fp8"])
+@pytest.mark.parametrize("act", ACTS)
 @pytest.mark.parametrize("T,topk", [(1, 2), (37, 2), (200, 3), (5, 8)])
 def test_small_layer_all_tokens(small_layer, T, topk, act):
     run_layer(small_layer, T, act, topk, key=(11,))
@@ -301,7 +310,7 @@ def small_layer_tiled(request):
     return Layer(8, 512, 128, key=(7,), tuning=TILED[request.param])
 
 
-@pytest.mark.parametrize("act", ["bf16", "fp8"])
+@pytest.mark.parametrize("act", ACTS)
 @pytest.mark.parametrize("T,topk", [(3, 2), (200, 3), (700, 2)])
 def test_small_layer_tiled(small_layer_tiled, T, topk, act):
     run_layer(small_layer_tiled, T, act, topk, key=(17,))
@@ -339,7 +348,7 @@ def test_small_layer_many_slots_column_windows(act):
     run_layer(lay, 65536, act, 8, key=(37,), sample=24)
 
 
-@pytest.mark.parametrize("act", ["bf16", "fp8"])
+@pytest.mark.parametrize("act", ACTS)
 @pytest.mark.parametrize("T,topk", [(1, 2), (1, 8), (3, 8), (37, 2), (200, 3)])
 def test_small_layer_by_slot(small_layer, T, topk, act):
     run_layer_by_slot(small_layer, T, act, topk, key=(41,))
@@ -374,13 +383,13 @@ def test_small_layer_plain_epilogue_aligned_and_by_slot(small_layer, act):
     w1, m1 = lay.dev[act][2], lay.dev[act][3]
     p = hq.MoePlan(2 * I, H, _quant(act), E, 4096, "none")
     ids = torch.from_numpy(ids_h).to(DEV)
-    a = (x["x"] if act == "bf16" else x["x_codes"]).to(DEV)
-    xs = None if act == "bf16" else x["x_scale"].to(DEV)
+    a = (x["x"] if act != "fp8" else x["x_codes"]).to(DEV)
+    xs = None if act != "fp8" else x["x_scale"].to(DEV)
     sid, bex, npad = hq.moe_align(ids, E, p.block_m(T, topk))
     out_al = p.moe_gemm(a, T, topk, sid, bex, npad, w1, m1, a_scale=xs)
     out_sl = p.moe_gemm_by_slot(a, T, topk, ids, w1, m1, a_scale=xs)
     torch.cuda.synchronize()
-    if act == "bf16":
+    if act != "fp8":
         xt = x["x"].double().numpy()
     else:
         xt = e4m3_value(x["x_codes"].numpy()) * x["x_scale"].numpy()[:, None].astype(np.float64)
@@ -389,13 +398,13 @@ def test_small_layer_plain_epilogue_aligned_and_by_slot(small_layer, act):
     o, tau = om.grouped_gemm(xt[slots // topk], flat[slots], lay.w["w1"], lay.w["s1"].double().numpy())
     sl = out_sl.double().cpu().numpy()
     assert sl.shape == (T * topk, 2 * I)
-    ok, _, ratio = og.check(sl[slots], o, tau, "bf16")
+    ok, _, ratio = og.check(sl[slots], o, tau, _out_fmt(act))
     assert ok.all(), f"by slot: {(~ok).sum()} bad, max err/tau {ratio.max():.3g}"
     assert (sl[~np.isin(np.arange(T * topk), slots)] == 0).all()
     sid_h = sid.cpu().numpy()
     pos = {int(v): i for i, v in enumerate(sid_h[: int(npad.cpu()[0])]) if v < T * topk}
     al = out_al.double().cpu().numpy()[[pos[int(v)] for v in slots]]
-    ok, _, ratio = og.check(al, o, tau, "bf16")
+    ok, _, ratio = og.check(al, o, tau, _out_fmt(act))
     assert ok.all(), f"aligned: {(~ok).sum()} bad, max err/tau {ratio.max():.3g}"
 
 
@@ -411,8 +420,8 @@ def test_moe_layer_helper_matches_its_path(small_layer, T, topk, act):
     p1, p2, w1, m1, w2, m2 = lay.dev[act]
     ids = torch.from_numpy(r["topk_ids"]).to(DEV)
     tw = torch.from_numpy(r["topk_w"]).to(DEV)
-    a = (x["x"] if act == "bf16" else x["x_codes"]).to(DEV)
-    xs = None if act == "bf16" else x["x_scale"].to(DEV)
+    a = (x["x"] if act != "fp8" else x["x_codes"]).to(DEV)
+    xs = None if act != "fp8" else x["x_scale"].to(DEV)
     y = hq.moe_layer(p1, p2, a, ids, tw, w1, m1, w2, m2, x_scale=xs)
     by_slot = hq.moe_uses_by_slot(T, topk)
     assert by_slot == (T * topk <= 64)
@@ -475,7 +484,7 @@ def test_full_layer_tiled_128_rows(full_layer, act):
     for a in ("bf16", "fp8"):
         _, _, w1, m1, w2, m2 = full_layer.dev[a]
         tun = dict(kernel=2, tile_m=128, tile_n=256)
-        p1 = hq.MoePlan(2 * tl.I, tl.H, _quant(a), tl.E, 4096, "silu_mul" if a == "bf16" else "silu_mul_qfp8",
+        p1 = hq.MoePlan(2 * tl.I, tl.H, _quant(a), tl.E, 4096, "silu_mul_qfp8" if a == "fp8" else "silu_mul",
                         tuning=tun)
         p2 = hq.MoePlan(tl.H, tl.I, _quant(a), tl.E, 4096, "topk_combine", tuning=tun)
         tl.dev[a] = (p1, p2, w1, m1, w2, m2)
