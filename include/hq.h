@@ -74,7 +74,10 @@
 extern "C" {
 #endif
 
-#define HQ_ABI_VERSION 2
+/* 3: hq_tuning gained tile_group; run-time specialisation (hq_plan_set_jit,
+ * hq_jit_*) and hq_moe_gemm_by_slot added; the combine's workspace rows are
+ * bf16 */
+#define HQ_ABI_VERSION 3
 
 typedef enum hq_status {
   HQ_OK = 0,

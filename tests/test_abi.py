@@ -51,7 +51,7 @@ def test_library_has_no_undefined_internal_symbols():
 
 def test_abi_version_and_status_strings():
     L = hq.lib()
-    assert L.hq_abi_version() == 2
+    assert L.hq_abi_version() == 3
     assert L.hq_status_str(0) == b"HQ_OK"
     assert L.hq_status_str(3) == b"HQ_ERR_WORKSPACE"
 
