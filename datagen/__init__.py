@@ -198,11 +198,13 @@ def moe_activations(T: int, H: int = 7168, act: str = "bf16", key=(5,)):
     return {"x_codes": codes, "x_scale": s}
 
 
-def moe_weights(E: int = 256, H: int = 7168, I: int = 256, key=(5,), experts=None):
+def moe_weights(E: int = 256, H: int = 7168, I: int = 256, key=(5,), experts=None, zp: str = "fixed"):
     """Expert weights, drawn expert by expert.  W1 [E, 2I, H/8], W2 [E, H, I/8].
 
     ``experts`` restricts the draw to a subset (others left zero) while keeping
     every drawn expert identical to a full draw: each expert has its own seed.
+    zp "u4" adds per-group uint4 zero points z1 [E, 2I, H/128], z2 [E, H, I/128]
+    (uniform 6..9, drawn after the codes and scales from a seed of their own).
     """
     w1 = np.zeros((E, 2 * I, H // 8), dtype=np.int32)
     s1 = torch.zeros((E, 2 * I, H // GROUP), dtype=torch.float16)
@@ -214,4 +216,13 @@ def moe_weights(E: int = 256, H: int = 7168, I: int = 256, key=(5,), experts=Non
         s1[e] = _to_dtype(rng.uniform(0.005, 0.02, size=(2 * I, H // GROUP)), torch.float16)
         w2[e] = pack_u4(rng.integers(0, 16, size=(H, I), dtype=np.uint8))
         s2[e] = _to_dtype(rng.uniform(0.005, 0.02, size=(H, I // GROUP)), torch.float16)
-    return {"w1": w1, "s1": s1, "w2": w2, "s2": s2}
+    out = {"w1": w1, "s1": s1, "w2": w2, "s2": s2}
+    if zp == "u4":
+        z1 = np.zeros((E, 2 * I, H // GROUP), dtype=np.uint8)
+        z2 = np.zeros((E, H, I // GROUP), dtype=np.uint8)
+        for e in range(E) if experts is None else sorted(set(int(x) for x in experts)):
+            rng = rng_for(*key, E, H, I, 4, e)
+            z1[e] = rng.integers(6, 10, size=(2 * I, H // GROUP), dtype=np.uint8)
+            z2[e] = rng.integers(6, 10, size=(H, I // GROUP), dtype=np.uint8)
+        out.update(z1=z1, z2=z2)
+    return out

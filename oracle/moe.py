@@ -96,6 +96,7 @@ def grouped_gemm(rows_a, row_expert, codes, scales, zeros=8, group: int = 128):
     rows_a     float64 [R, K]   activation values of each (token, slot) row
     row_expert int [R]          expert of each row
     codes      int32 [E, N, K/8], scales [E, N, K/G]
+    zeros      a fixed zero point, or per-group zero points [E, N, K/G]
     """
     rows_a = np.asarray(rows_a, dtype=np.float64)
     R, K = rows_a.shape
@@ -104,20 +105,20 @@ def grouped_gemm(rows_a, row_expert, codes, scales, zeros=8, group: int = 128):
     tau = np.zeros((R, N))
     for e in np.unique(row_expert):
         sel = np.nonzero(row_expert == e)[0]
-        w = dequant_int4(codes[e], scales[e], zeros, group)
+        w = dequant_int4(codes[e], scales[e], zeros if np.isscalar(zeros) else np.asarray(zeros)[e], group)
         out[sel] = rows_a[sel] @ w.T
         tau[sel] = tolerance(rows_a[sel], w)
     return out, tau
 
 
-def gate_up(rows_a, row_expert, w1_codes, w1_scales, inter: int):
+def gate_up(rows_a, row_expert, w1_codes, w1_scales, inter: int, w1_zeros=8):
     """First expert GEMM + SiLU*mul, float64, with first-order bounds.
 
     Returns dict(g, u, act, tau_g, tau_u, tau_act) where tau_act bounds
     |act(g + dg, u + du) - act(g, u)| for |dg| <= tau_g, |du| <= tau_u
     (first-order terms plus the Taylor remainder, SiLU'' being <= 1/2).
     """
-    h, tau_h = grouped_gemm(rows_a, row_expert, w1_codes, w1_scales)
+    h, tau_h = grouped_gemm(rows_a, row_expert, w1_codes, w1_scales, w1_zeros)
     g, u = h[:, :inter], h[:, inter:]
     tg, tu = tau_h[:, :inter], tau_h[:, inter:]
     act = silu(g) * u
@@ -178,7 +179,7 @@ def rows_rounding_bound(o, tau_o, weight, topk: int, fmt: str = "bf16"):
 
 
 def down_combine(act_rows, row_token, row_weight, row_expert, w2_codes, w2_scales, T: int, rows_fmt=None,
-                 topk: int = 8):
+                 topk: int = 8, w2_zeros=8):
     """Second expert GEMM, top-k weighting and combine, float64.
 
     act_rows float64 [R, I] (the GPU's own act values), row_token / row_weight
@@ -187,7 +188,7 @@ def down_combine(act_rows, row_token, row_weight, row_expert, w2_codes, w2_scale
     weighted rows are stored in ``rows_fmt`` before the sum, the sum over the
     token's rows of ``rows_rounding_bound``.
     """
-    o, tau_o = grouped_gemm(act_rows, row_expert, w2_codes, w2_scales)
+    o, tau_o = grouped_gemm(act_rows, row_expert, w2_codes, w2_scales, w2_zeros)
     H = o.shape[1]
     y = np.zeros((T, H))
     ty = np.zeros((T, H))

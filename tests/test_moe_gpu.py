@@ -78,10 +78,10 @@ def test_align_degenerate_cases():
 
 # --------------------------------------------------------- layer pipeline --
 
-def _quant(act):
+def _quant(act, zp="fixed"):
     if act in ("bf16", "f16"):
-        return hq.w4a16(act, scale="f16")
-    return hq.w4a8_fp8(scale="f16")
+        return hq.w4a16(act, scale="f16", zp=zp)
+    return hq.w4a8_fp8(scale="f16", zp=zp)
 
 
 def _out_fmt(act):
@@ -95,17 +95,21 @@ class Layer:
     """Weights on the GPU (repacked for both activation types) + host copies.
     `tuning` (same for both GEMMs) forces a kernel / block size."""
 
-    def __init__(self, E, H, I, key, tuning=None, max_t=4096, acts=ACTS):
+    def __init__(self, E, H, I, key, tuning=None, max_t=4096, acts=ACTS, zp="fixed"):
         self.E, self.H, self.I = E, H, I
-        wts = datagen.moe_weights(E, H, I, key=key)
+        wts = datagen.moe_weights(E, H, I, key=key, zp=zp)
         self.w = wts
+        # the oracle's zero points: fixed 8, or the per-group arrays
+        self.z1, self.z2 = (wts["z1"], wts["z2"]) if zp == "u4" else (8, 8)
         self.dev = {}
         for act in acts:
-            p1 = hq.MoePlan(2 * I, H, _quant(act), E, max_t, "silu_mul_qfp8" if act == "fp8" else "silu_mul",
+            p1 = hq.MoePlan(2 * I, H, _quant(act, zp), E, max_t, "silu_mul_qfp8" if act == "fp8" else "silu_mul",
                             tuning=tuning)
-            p2 = hq.MoePlan(H, I, _quant(act), E, max_t, "topk_combine", tuning=tuning)
-            w1, m1 = p1.repack(torch.from_numpy(wts["w1"]).to(DEV), wts["s1"].to(DEV))
-            w2, m2 = p2.repack(torch.from_numpy(wts["w2"]).to(DEV), wts["s2"].to(DEV))
+            p2 = hq.MoePlan(H, I, _quant(act, zp), E, max_t, "topk_combine", tuning=tuning)
+            z1 = torch.from_numpy(wts["z1"]).to(DEV) if zp == "u4" else None
+            z2 = torch.from_numpy(wts["z2"]).to(DEV) if zp == "u4" else None
+            w1, m1 = p1.repack(torch.from_numpy(wts["w1"]).to(DEV), wts["s1"].to(DEV), z1)
+            w2, m2 = p2.repack(torch.from_numpy(wts["w2"]).to(DEV), wts["s2"].to(DEV), z2)
             self.dev[act] = (p1, p2, w1, m1, w2, m2)
         torch.cuda.synchronize()
 
@@ -161,7 +165,7 @@ def run_layer(layer, T, act, topk, key=(5,), sample=None, masked=0.0):
         xa = x["x"].double().numpy()[row_tok]
     else:
         xa = e4m3_value(x["x_codes"].numpy()[row_tok]) * x["x_scale"].numpy()[row_tok, None].astype(np.float64)
-    gu = om.gate_up(xa, row_exp, layer.w["w1"], layer.w["s1"].double().numpy(), I)
+    gu = om.gate_up(xa, row_exp, layer.w["w1"], layer.w["s1"].double().numpy(), I, w1_zeros=layer.z1)
     if act != "fp8":
         act_gpu = act_out.double().cpu().numpy()[rows]
         ok, _, ratio = og.check(act_gpu, gu["act"], gu["tau_act"], _out_fmt(act))
@@ -194,7 +198,7 @@ def run_layer(layer, T, act, topk, key=(5,), sample=None, masked=0.0):
     # down + combine: oracle on the GPU's act rows, for the sampled tokens
     # the aligned path stores each weighted slot row in bf16 before the combine
     dc = om.down_combine(act_rows, row_tok, r["topk_w"].reshape(-1)[slot], row_exp, layer.w["w2"],
-                         layer.w["s2"].double().numpy(), T, rows_fmt="bf16", topk=topk)
+                         layer.w["s2"].double().numpy(), T, rows_fmt="bf16", topk=topk, w2_zeros=layer.z2)
     y_gpu = y.double().cpu().numpy()[toks]
     ok, _, ratio = og.check(y_gpu, dc["y64"][toks], dc["tau_y"][toks], _out_fmt(act))
     assert ok.all(), f"down+combine: {(~ok).sum()} bad, max err/tau {ratio.max():.3g}"
@@ -243,7 +247,7 @@ def run_layer_by_slot(layer, T, act, topk, key=(5,), sample=None, masked=0.0, ws
         xa = x["x"].double().numpy()[row_tok]
     else:
         xa = e4m3_value(x["x_codes"].numpy()[row_tok]) * x["x_scale"].numpy()[row_tok, None].astype(np.float64)
-    gu = om.gate_up(xa, row_exp, layer.w["w1"], layer.w["s1"].double().numpy(), I)
+    gu = om.gate_up(xa, row_exp, layer.w["w1"], layer.w["s1"].double().numpy(), I, w1_zeros=layer.z1)
     if act != "fp8":
         assert tuple(act_out.shape) == (S, I)
         out_h = act_out.double().cpu().numpy()
@@ -268,7 +272,7 @@ def run_layer_by_slot(layer, T, act, topk, key=(5,), sample=None, masked=0.0, ws
         assert (np.abs(dq - gu["act"]) <= bound).all(), "fp8 requant off the oracle's act"
         act_rows = dq
     dc = om.down_combine(act_rows, row_tok, r["topk_w"].reshape(-1)[vs], row_exp, layer.w["w2"],
-                         layer.w["s2"].double().numpy(), T)
+                         layer.w["s2"].double().numpy(), T, w2_zeros=layer.z2)
     y_gpu = y.double().cpu().numpy()[toks]
     ok, _, ratio = og.check(y_gpu, dc["y64"][toks], dc["tau_y"][toks], _out_fmt(act))
     assert ok.all(), f"down+combine by slot: {(~ok).sum()} bad, max err/tau {ratio.max():.3g}"
@@ -284,6 +288,34 @@ def small_layer():
 @pytest.mark.parametrize("T,topk", [(1, 2), (37, 2), (200, 3), (5, 8)])
 def test_small_layer_all_tokens(small_layer, T, topk, act):
     run_layer(small_layer, T, act, topk, key=(11,))
+
+
+@pytest.fixture(scope="module")
+def small_layer_zp():
+    # per-group uint4 zero points (6..9) on every expert
+    return Layer(8, 512, 128, key=(9,), zp="u4")
+
+
+@pytest.fixture(scope="module")
+def small_layer_zp_tiled():
+    return Layer(8, 512, 128, key=(9,), zp="u4", tuning=dict(kernel=2, tile_m=64, tile_n=256))
+
+
+@pytest.mark.parametrize("act", ACTS)
+@pytest.mark.parametrize("T,topk", [(1, 2), (37, 2), (5, 8)])
+def test_small_layer_group_zero_points(small_layer_zp, T, topk, act):
+    run_layer(small_layer_zp, T, act, topk, key=(79,))
+
+
+@pytest.mark.parametrize("act", ACTS)
+def test_small_layer_group_zero_points_tiled(small_layer_zp_tiled, act):
+    run_layer(small_layer_zp_tiled, 200, act, 3, key=(83,))
+
+
+@pytest.mark.parametrize("act", ACTS)
+@pytest.mark.parametrize("T,topk", [(1, 8), (6, 4)])
+def test_small_layer_group_zero_points_by_slot(small_layer_zp, T, topk, act):
+    run_layer_by_slot(small_layer_zp, T, act, topk, key=(89,), masked=0.2 if T > 1 else 0.0)
 
 
 @pytest.fixture(scope="module")
@@ -395,7 +427,7 @@ def test_small_layer_plain_epilogue_aligned_and_by_slot(small_layer, act):
         xt = e4m3_value(x["x_codes"].numpy()) * x["x_scale"].numpy()[:, None].astype(np.float64)
     flat = ids_h.reshape(-1)
     slots = np.nonzero((flat >= 0) & (flat < E))[0]
-    o, tau = om.grouped_gemm(xt[slots // topk], flat[slots], lay.w["w1"], lay.w["s1"].double().numpy())
+    o, tau = om.grouped_gemm(xt[slots // topk], flat[slots], lay.w["w1"], lay.w["s1"].double().numpy(), lay.z1)
     sl = out_sl.double().cpu().numpy()
     assert sl.shape == (T * topk, 2 * I)
     ok, _, ratio = og.check(sl[slots], o, tau, _out_fmt(act))
@@ -480,6 +512,7 @@ def test_full_layer_tiled_128_rows(full_layer, act):
     # T = 4096 again with the other tiled block size (and 256-column tiles)
     tl = Layer.__new__(Layer)
     tl.E, tl.H, tl.I, tl.w = full_layer.E, full_layer.H, full_layer.I, full_layer.w
+    tl.z1, tl.z2 = full_layer.z1, full_layer.z2
     tl.dev = {}
     for a in ("bf16", "fp8"):
         _, _, w1, m1, w2, m2 = full_layer.dev[a]

@@ -264,6 +264,29 @@ def _run_tiny(g):
     return gu, dc
 
 
+def test_grouped_gemm_per_expert_zero_points_by_hand():
+    # per-group zero points of each expert, element by element in plain Python
+    rng = np.random.default_rng(12)
+    E, N, K = 2, 3, 256
+    q = rng.integers(0, 16, size=(E, N, K)).astype(np.uint8)
+    z = rng.integers(6, 10, size=(E, N, K // 128)).astype(np.uint8)
+    z[1] = 15 - z[0]                                   # the experts' zero points differ
+    s = rng.uniform(0.5, 2.0, size=(E, N, K // 128))
+    a = rng.standard_normal((4, K))
+    ex = np.array([0, 1, 1, 0])
+    got, _ = MO.grouped_gemm(a, ex, _pack(q), s, z)
+    for r in range(4):
+        e = int(ex[r])
+        for n in range(N):
+            want = 0.0
+            for k in range(K):
+                want += float(a[r, k]) * (int(q[e, n, k]) - int(z[e, n, k // 128])) * float(s[e, n, k // 128])
+            assert abs(got[r, n] - want) <= 1e-12 * (1 + abs(want))
+    # planted: one expert's zero points for every expert
+    wrong, _ = MO.grouped_gemm(a, ex, _pack(q), s, np.broadcast_to(z[0], z.shape))
+    assert not np.allclose(wrong[ex == 1], got[ex == 1])
+
+
 def test_moe_tiny_layer_by_hand():
     g = _gold("moe_tiny.json")
     gu, dc = _run_tiny(g)
