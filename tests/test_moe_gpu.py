@@ -78,10 +78,10 @@ def test_align_degenerate_cases():
 
 # --------------------------------------------------------- layer pipeline --
 
-def _quant(act, zp="fixed"):
+def _quant(act, zp="fixed", scale="f16"):
     if act in ("bf16", "f16"):
-        return hq.w4a16(act, scale="f16", zp=zp)
-    return hq.w4a8_fp8(scale="f16", zp=zp)
+        return hq.w4a16(act, scale=scale, zp=zp)
+    return hq.w4a8_fp8(scale=scale, zp=zp)
 
 
 def _out_fmt(act):
@@ -95,17 +95,19 @@ class Layer:
     """Weights on the GPU (repacked for both activation types) + host copies.
     `tuning` (same for both GEMMs) forces a kernel / block size."""
 
-    def __init__(self, E, H, I, key, tuning=None, max_t=4096, acts=ACTS, zp="fixed"):
+    def __init__(self, E, H, I, key, tuning=None, max_t=4096, acts=ACTS, zp="fixed", scale="f16"):
         self.E, self.H, self.I = E, H, I
         wts = datagen.moe_weights(E, H, I, key=key, zp=zp)
+        if scale == "bf16":  # the scales as bf16 values (rounded once; the oracle reads the same values)
+            wts["s1"], wts["s2"] = wts["s1"].to(torch.bfloat16), wts["s2"].to(torch.bfloat16)
         self.w = wts
         # the oracle's zero points: fixed 8, or the per-group arrays
         self.z1, self.z2 = (wts["z1"], wts["z2"]) if zp == "u4" else (8, 8)
         self.dev = {}
         for act in acts:
-            p1 = hq.MoePlan(2 * I, H, _quant(act, zp), E, max_t, "silu_mul_qfp8" if act == "fp8" else "silu_mul",
-                            tuning=tuning)
-            p2 = hq.MoePlan(H, I, _quant(act, zp), E, max_t, "topk_combine", tuning=tuning)
+            p1 = hq.MoePlan(2 * I, H, _quant(act, zp, scale), E, max_t,
+                            "silu_mul_qfp8" if act == "fp8" else "silu_mul", tuning=tuning)
+            p2 = hq.MoePlan(H, I, _quant(act, zp, scale), E, max_t, "topk_combine", tuning=tuning)
             z1 = torch.from_numpy(wts["z1"]).to(DEV) if zp == "u4" else None
             z2 = torch.from_numpy(wts["z2"]).to(DEV) if zp == "u4" else None
             w1, m1 = p1.repack(torch.from_numpy(wts["w1"]).to(DEV), wts["s1"].to(DEV), z1)
@@ -297,6 +299,17 @@ def small_layer_zp():
 
 
 @pytest.fixture(scope="module")
+def small_layer_bf16_scales():
+    return Layer(8, 512, 128, key=(10,), scale="bf16", zp="u4")
+
+
+@pytest.mark.parametrize("act", ACTS)
+def test_small_layer_bf16_scales_aligned_and_by_slot(small_layer_bf16_scales, act):
+    run_layer(small_layer_bf16_scales, 40, act, 2, key=(97,))
+    run_layer_by_slot(small_layer_bf16_scales, 3, act, 8, key=(97,))
+
+
+@pytest.fixture(scope="module")
 def small_layer_zp_tiled():
     return Layer(8, 512, 128, key=(9,), zp="u4", tuning=dict(kernel=2, tile_m=64, tile_n=256))
 
@@ -381,7 +394,7 @@ def test_small_layer_many_slots_column_windows(act):
 
 
 @pytest.mark.parametrize("act", ACTS)
-@pytest.mark.parametrize("T,topk", [(1, 2), (1, 8), (3, 8), (37, 2), (200, 3)])
+@pytest.mark.parametrize("T,topk", [(1, 2), (1, 8), (3, 8), (37, 2), (200, 3), (1, 1), (9, 1)])
 def test_small_layer_by_slot(small_layer, T, topk, act):
     run_layer_by_slot(small_layer, T, act, topk, key=(41,))
 
