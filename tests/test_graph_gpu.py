@@ -80,8 +80,8 @@ class _Moe:
         self.E, self.H, self.I, self.act = E, H, I, act
         q = hq.w4a16("bf16", scale="f16") if act == "bf16" else hq.w4a8_fp8(scale="f16")
         wts = datagen.moe_weights(E, H, I, key=(73,))
-        self.p1 = hq.MoePlan(2 * I, H, q, E, 256, "silu_mul" if act == "bf16" else "silu_mul_qfp8")
-        self.p2 = hq.MoePlan(H, I, q, E, 256, "topk_combine")
+        self.p1 = hq.MoePlan(2 * I, H, q, E, 512, "silu_mul" if act == "bf16" else "silu_mul_qfp8")
+        self.p2 = hq.MoePlan(H, I, q, E, 512, "topk_combine")
         self.w1, self.m1 = self.p1.repack(torch.from_numpy(wts["w1"]).to(DEV), wts["s1"].to(DEV))
         self.w2, self.m2 = self.p2.repack(torch.from_numpy(wts["w2"]).to(DEV), wts["s2"].to(DEV))
 
@@ -97,10 +97,13 @@ class _Moe:
 
 
 @pytest.mark.parametrize("act", ["bf16", "fp8"])
-def test_graph_moe_layer_aligned(act):
-    T, topk = 24, 2
+@pytest.mark.parametrize("T,topk", [(24, 2), (400, 2)], ids=["skinny", "tiled"])
+def test_graph_moe_layer_aligned(act, T, topk):
+    # 24 tokens take the weight-streaming kernels, 400 (100 slots per expert)
+    # the persistent tiled gate_up and the small-K down
     _log(f"graph moe aligned T={T} topk={topk} act={act}")
     m = _Moe(act)
+    assert ("grouped-tiled" in m.p1.describe(T, topk)) == (T == 400)
     E, I = m.E, m.I
     bm = m.p1.block_m(T, topk)
     mp = hq.moe_max_padded(T, topk, E, bm)
