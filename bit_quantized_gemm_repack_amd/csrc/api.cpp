@@ -225,11 +225,14 @@ Exec choose_exec(const hq_plan* p, int64_t m, const hq_tuning* up) {
   const bool tiled_ok = p->compute.epi != HQ_EPI_I32_ACC && N % 128 == 0;
   // 33..64 rows of 16-bit activations (INT4 weights): 16-row x 64-column skinny blocks with
   // no K split while they fill the chip at most once (N/64 * ceil(m/16) <=
-  // 256 workgroups); a sweep of the decode shapes on MI355X put them ahead of
-  // the split tiled kernel there (N = K = 4096: 9.7 against 14.8 us; K =
-  // 14336: even) and behind it for wider layers (N = 14336: 28 against 24 us)
+  // 256 workgroups) and at most 64 groups along K; a sweep of the decode
+  // shapes on MI355X put them ahead of the split tiled kernel at N = K = 4096
+  // (10.0 against 15.3 us) and behind it for wider layers (N = 14336: 28
+  // against 24 us) and for longer K (K = 14336: 26.3 against 22.0 us for the
+  // tiled kernel with an 8-way split, whose activation tile each workgroup
+  // reads once instead of once per 16-row block)
   const bool skinny_mid = (p->fmt == FMT_W16F16 || p->fmt == FMT_W16BF16) && m > 32 && m <= 64 && N % 64 == 0 && (N / 64) * cdiv(mm, 16) <= 256 &&
-                          p->compute.kind == HQ_GEMM_DENSE;
+                          G <= 64 && p->compute.kind == HQ_GEMM_DENSE;
   const bool tiled_auto = m > 32 && !skinny_mid;
   if (tiled_ok && (u.kernel == KER_TILED || (u.kernel == 0 && tiled_auto))) {
     e.kernel = KER_TILED;
