@@ -55,6 +55,9 @@ __device__ inline i8_t cat8(u4_t x, u4_t y) {
   return r;
 }
 
+// LDS address operand of the direct global->LDS buffer loads.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 // A value the compiler cannot see through (kept in a VGPR).  Passing the
 // magic exponent of w16_operand this way lets each register be one
 // v_and_or_b32 (mask from an SGPR, magic from a VGPR): with both constants

@@ -409,6 +409,10 @@ struct SkinnyArgs {
   const int32_t* topk_ids;  // [t][topk]
   int num_experts;
   int ge;                   // groups per expert (token mode: G = topk * ge)
+  // dense 16-bit activations, one 16-row block per workgroup: bytes per row of
+  // the workgroup's activation slab copied into LDS once (0: each wave loads
+  // its groups' activations from global memory)
+  int a_pitch;
 };
 
 // Grouped epilogues (SkinnyArgs::epi / TiledArgs::epi).

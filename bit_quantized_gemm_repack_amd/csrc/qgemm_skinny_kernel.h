@@ -16,6 +16,11 @@
 //     Each wave keeps STAGES groups of loads in flight ahead of its math.
 //   * Activations are read per lane as one contiguous 32 / 64-byte run of a
 //     row (L2 / L1 resident; rows beyond M are clamped, their results dropped).
+//     Dense 16-bit activations of a few rows may instead be copied once into
+//     LDS (AS = 1: the block's rows over its split's K range, while the first
+//     weight loads are in flight) and read from there: per group, four 64-lane
+//     global loads of which only the lanes of rows below M carry data would
+//     otherwise take as much address-unit time as the weight loads.
 //   * Per group the 4-bit codes become MFMA operands with one mask (+ one
 //     shift) per register and no float arithmetic: the MFMA sees the exact
 //     integers (OFF + q) (16-bit formats: OFF = 1024 for fp16, 128 for bf16),
@@ -69,6 +74,14 @@ struct Stage {
   float gw;           // token mode: the step's top-k weight (times its slot row's scale)
 };
 
+// s_waitcnt: at most N (< 64) vector-memory loads of this wave in flight
+// (LDS and scalar counters not waited on).
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 template <int FMT>
 __device__ inline f4_t mfma16(u4_t a, u4_t b, f4_t c) {
   return mfma_16x16x32<f16_act(FMT)>(a, b, c);
@@ -87,8 +100,10 @@ __device__ inline f4_t mfma16(u4_t a, u4_t b, f4_t c) {
 // specialisation, hq_plan_set_jit); 0 takes them from the arguments.  SL:
 // the reduction buffer is a static LDS array sized for MAXT threads (a
 // run-time compiled module has no dynamic-LDS attribute to raise), not the
-// launch's dynamic LDS.
-template <int FMT, int MB, int NB, int STAGES, int MAXT, int GRP, int MC = 0, int NC = 0, int KC = 0, int SL = 0>
+// launch's dynamic LDS.  AS: the activation slab is staged in LDS behind the
+// reduction buffer (dense 16-bit activations, one row block; a_pitch > 0).
+template <int FMT, int MB, int NB, int STAGES, int MAXT, int GRP, int MC = 0, int NC = 0, int KC = 0, int SL = 0,
+          int AS = 0>
 __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the body uses device-only builtins; the host pass needs only the stub
   using FI = FmtInfo<FMT>;
@@ -204,6 +219,14 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   // MXFP4 activation scales, group-major words: word (g, row) holds the four
   // E8M0 block scales of the row's group g
   [[maybe_unused]] const auto rae = rsrc(p.a_e8m0, (int64_t)G * a_rows * 4);
+  // Staged activations (AS): the block's rows over this split's groups sit in
+  // LDS behind the reduction buffer, row r at r * a_pitch, group g at
+  // (g - g_beg) * 256 bytes.
+  static_assert(!AS || (GRP == GRP_DENSE && FI::kAct16 && MB == 1 && !SL), "staged activations: dense, 16-bit, one row block");
+  [[maybe_unused]] const int blk_rows = min(16, M - m0);
+  extern __shared__ float red_dyn[];
+  [[maybe_unused]] uint8_t* const a_lds =
+      reinterpret_cast<uint8_t*>(red_dyn) + (size_t)W * (MB * NB * 4) * 64 * sizeof(float);
   // at or above 2^31: past every range (ranges stay below 2 GiB), and adding
   // the group offset cannot wrap
   constexpr int kOutOfRange = INT32_MIN;
@@ -509,16 +532,89 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   // barriers): the wait before stage d's math then counts the loads of the
   // later stages, on the first pass as in the loop.
   Stage<FMT, MB, NB> st[STAGES];
+  if constexpr (AS) {
+    // weights and metadata of group g (dense: no per-step expert)
+    auto load_wm = [&](Stage<FMT, MB, NB>& s_, int g) {
 #pragma unroll
-  for (int d = 0; d < STAGES; ++d) {
-    load(st[d], group_of(d));
+      for (int nb = 0; nb < NB; ++nb)
+        if constexpr (FI::kW2 || FI::kW3) {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b64(rw, woff[nb], g * kFragB, 2);
+          s_.b[nb] = u4_t{(uint32_t)v[0], (uint32_t)v[1], 0u, 0u};
+        } else {
+          s_.b[nb] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[nb], g * kFragB, 2));
+        }
+      if constexpr (FI::kW8) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          s_.b2[nb] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[nb] + 1024, g * kFragB, 2));
+      }
+      if constexpr (FI::kW3) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          s_.b2[nb] = u4_t{__builtin_amdgcn_raw_buffer_load_b32(rw, woff[nb] + 512 - 4 * lane, g * kFragB, 2), 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        if constexpr (e8m0_meta(FMT)) {
+          s_.sraw[nb] = __builtin_amdgcn_raw_buffer_load_b32(re, soff[nb], g * byte_meta_frag(FMT), 0);
+        } else {
+          s_.sraw[nb] = __builtin_amdgcn_raw_buffer_load_b32(rsc, soff[nb], g * 32, 0);
+          s_.zraw[nb] = __builtin_amdgcn_raw_buffer_load_b32(rz, zoff[nb], g * 8, 0);
+        }
+      }
+    };
+    constexpr int kWMLoads = NB * (1 + ((FI::kW8 || FI::kW3) ? 1 : 0) + (e8m0_meta(FMT) ? 1 : 2));
+    // group g's operand of this lane's row, zero for rows past M
+    auto load_a_lds = [&](Stage<FMT, MB, NB>& s_, int g) {
+      const uint8_t* src = a_lds + c * p.a_pitch + (g - g_beg) * 256 + 16 * kq;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        s_.a[0][t] = c < blk_rows ? *reinterpret_cast<const u4_t*>(src + 64 * t) : u4_t{0u, 0u, 0u, 0u};
+    };
+    // The slab: blk_rows rows x ceil(span / 1 KiB) chunks, each one 64-lane
+    // 16-byte load straight into LDS (a row's last chunk may run past this
+    // split's groups into the row's padding; past the buffer it reads zeros).
+    const int nch = ((g_end - g_beg) * 256 + 1023) >> 10;
+    for (int idx = wave; idx < blk_rows * nch; idx += W) {
+      const int r = idx / nch, ch = idx - r * nch;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(a_lds + r * p.a_pitch + ch * 1024), 16,
+                                               (m0 + r) * a_rowb + 16 * lane, g_beg * 256 + ch * 1024, 0, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
-  }
-  for (int i = 0; i < n_it; i += STAGES) {
 #pragma unroll
     for (int d = 0; d < STAGES; ++d) {
-      if (i + d < n_it) compute(st[d], my_first + (i + d) * W);
-      load(st[d], group_of(i + d + STAGES));
+      load_wm(st[d], group_of(d));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // The slab copies went out first: with at most the prologue's weight and
+    // metadata loads still in flight, this wave's copies have landed (loads
+    // complete in order); the barrier then covers every wave's.
+    static_assert(STAGES * kWMLoads < 64, "prologue loads exceed the counter");
+    wait_vm<STAGES * kWMLoads>();
+    __syncthreads();
+#pragma unroll
+    for (int d = 0; d < STAGES; ++d) load_a_lds(st[d], group_of(d));
+    for (int i = 0; i < n_it; i += STAGES) {
+#pragma unroll
+      for (int d = 0; d < STAGES; ++d) {
+        if (i + d < n_it) compute(st[d], my_first + (i + d) * W);
+        const int gn = group_of(i + d + STAGES);
+        load_wm(st[d], gn);
+        load_a_lds(st[d], gn);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < STAGES; ++d) {
+      load(st[d], group_of(d));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int i = 0; i < n_it; i += STAGES) {
+#pragma unroll
+      for (int d = 0; d < STAGES; ++d) {
+        if (i + d < n_it) compute(st[d], my_first + (i + d) * W);
+        load(st[d], group_of(i + d + STAGES));
+      }
     }
   }
 
@@ -526,7 +622,6 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
 
   // ---- reduce the W partial accumulators of this workgroup (fixed order) ----
   constexpr int E = MB * NB * 4;
-  extern __shared__ float red_dyn[];
   float* red;  // [W][E][64]
   if constexpr (SL) {
     __shared__ float red_st[(MAXT / 64) * E * 64];

@@ -119,8 +119,6 @@ __device__ inline void pin(T& x) {
   asm volatile("; pin %0" : "+v"(x));
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 // One BM x BN tile (row tile tm, column tile tn) of the GEMM; `lds` is the
 // workgroup's stage ring.  MC, NC, KC: the call's M, N and K as compile-time
 // constants (run-time specialisation, hq_plan_set_jit); 0 takes them from the

@@ -90,6 +90,19 @@ def test_tuning_knobs(tuning):
     run_w4a16(16, 512, 2048, act="f16", zp="fixed", tuning=tuning)
 
 
+@pytest.mark.parametrize("tuning", [
+    None, dict(split_k=2), dict(split_k=3), dict(split_k=16), dict(waves=4), dict(waves=16), dict(stages=4),
+    dict(tile_n=32), dict(tile_n=64), dict(tile_n=64, stages=4, split_k=2),
+])
+@pytest.mark.parametrize("M", [1, 3, 4])
+def test_staged_activations(M, tuning):
+    # up to 4 rows of 16-bit activations are copied into LDS once per
+    # workgroup: split ranges whose byte span is not a whole KiB (K = 640, five
+    # groups; uneven splits), every wave count, ring depth and column width
+    run_w4a16(M, 256, 640, act="bf16", zp="u4", tuning=tuning)
+    run_w4a16(M, 512, 2048, act="f16", zp="fixed", tuning=tuning)
+
+
 def test_m_zero_is_noop_and_calls_repeat():
     N, K = 256, 1024
     d, ref = w4a16_case(16, N, K, "bf16", "u4")
