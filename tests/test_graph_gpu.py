@@ -1,5 +1,6 @@
 """HIP-graph capture of the library's calls, the way a decode loop runs them:
-a decode GEMM with a K split (GEMM + split-K reduce), the aligned MoE layer
+decode GEMMs (with a K split: GEMM + split-K reduce; with staged activation
+rows), the aligned MoE layer
 (align, gate_up with the fp8 requant, down, combine) and the by-slot MoE layer.
 Each sequence is captured once and replayed several times; before every replay
 new inputs are copied into the captured input buffers, the program does eager
@@ -53,12 +54,15 @@ def _replay_and_check(capture_calls, set_inputs, outputs, eager_calls, eager_out
     del g
 
 
-def test_graph_decode_gemm_with_k_split():
-    M, N, K = 16, 4096, 14336
+@pytest.mark.parametrize("M", [16, 1])
+def test_graph_decode_gemm(M):
+    # M = 16 takes the K split and its reduce; M = 1 the activation rows staged
+    # in LDS (a slab of 28 KiB behind the reduction buffer)
+    N, K = 4096, 14336
     _log(f"graph decode gemm M={M} N={N} K={K}")
     d = datagen.dense_w4a16(M, N, K, act="bf16", zp="u4", key=(71,))
     p = hq.Plan(N, K, hq.w4a16(act="bf16", zp="u4"), max_m=M)
-    assert "split_k=1 " not in p.describe(M) + " "       # this shape takes the K split and its reduce
+    assert ("split_k=1 " not in p.describe(M) + " ") == (M == 16)
     w, meta = p.repack(torch.from_numpy(d["codes"]).to(DEV), d["scales"].to(DEV), torch.from_numpy(d["zeros"]).to(DEV))
     a = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
     out, ref = (torch.empty((M, N), dtype=torch.bfloat16, device=DEV) for _ in range(2))
