@@ -169,6 +169,13 @@ template <int FMT, int GRP>
 static hipError_t launch_byslot_t(const SkinnyCfg& cfg, const SkinnyArgs& a, dim3 grid, dim3 block, size_t lds,
                                   hipStream_t s) {
   if (cfg.stages != 2 || cfg.mb != 1 || cfg.waves > 16) return hipErrorInvalidValue;
+  if constexpr (GRP == GRP_SLOT && act16_fmt(FMT)) {
+    if (a.a_pitch > 0) {  // the slot's token row staged in LDS
+      if (cfg.nb == 2) return launch_kernel(qgemm_skinny<FMT, 1, 2, 2, 1024, GRP, 0, 0, 0, 0, 1>, grid, block, lds, s, a);
+      if (cfg.nb == 4) return launch_kernel(qgemm_skinny<FMT, 1, 4, 2, 1024, GRP, 0, 0, 0, 0, 1>, grid, block, lds, s, a);
+      return hipErrorInvalidValue;
+    }
+  }
   if constexpr (GRP == GRP_TOKEN)
     if (cfg.nb == 1) return launch_kernel(qgemm_skinny<FMT, 1, 1, 2, 1024, GRP>, grid, block, lds, s, a);
   if (cfg.nb == 2) return launch_kernel(qgemm_skinny<FMT, 1, 2, 2, 1024, GRP>, grid, block, lds, s, a);
@@ -185,19 +192,33 @@ int launch_skinny_byslot(int fmt, int mode, const SkinnyCfg& cfg, const SkinnyAr
   const int ntiles = paired ? (a.N / 2) / (16 * (cfg.nb / 2)) : a.N / (16 * cfg.nb);
   dim3 grid(ntiles, 1, (unsigned)blocks);
   dim3 block(64 * cfg.waves);
-  const size_t lds = (size_t)cfg.waves * cfg.mb * cfg.nb * 4 * 64 * sizeof(float);
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  size_t lds = (size_t)cfg.waves * cfg.mb * cfg.nb * 4 * 64 * sizeof(float);
   const bool slot = mode == GRP_SLOT;
+  // slot mode, 16-bit activations: the slot's token row over all of K staged
+  // in LDS behind the reduction buffer (as the dense calls of a few rows),
+  // while it leaves room for the workgroups each CU has to hold
+  SkinnyArgs b = a;
+  b.a_pitch = 0;
+  if (slot && act16_fmt(fmt) && (cfg.nb == 2 || cfg.nb == 4)) {
+    const int64_t pitch = ((int64_t)a.G * 256 + 1023) / 1024 * 1024 + 16;
+    static const int cus = device_cus();
+    const int64_t per_cu = ((int64_t)ntiles * blocks + cus - 1) / cus;
+    if (((int64_t)lds + pitch) * per_cu <= kSkinnyMaxLds) {
+      b.a_pitch = (int)pitch;
+      lds += (size_t)pitch;
+    }
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
   switch (fmt) {
     case FMT_W16F16:
-      return (int)(slot ? launch_byslot_t<FMT_W16F16, GRP_SLOT>(cfg, a, grid, block, lds, s)
-                        : launch_byslot_t<FMT_W16F16, GRP_TOKEN>(cfg, a, grid, block, lds, s));
+      return (int)(slot ? launch_byslot_t<FMT_W16F16, GRP_SLOT>(cfg, b, grid, block, lds, s)
+                        : launch_byslot_t<FMT_W16F16, GRP_TOKEN>(cfg, b, grid, block, lds, s));
     case FMT_W16BF16:
-      return (int)(slot ? launch_byslot_t<FMT_W16BF16, GRP_SLOT>(cfg, a, grid, block, lds, s)
-                        : launch_byslot_t<FMT_W16BF16, GRP_TOKEN>(cfg, a, grid, block, lds, s));
+      return (int)(slot ? launch_byslot_t<FMT_W16BF16, GRP_SLOT>(cfg, b, grid, block, lds, s)
+                        : launch_byslot_t<FMT_W16BF16, GRP_TOKEN>(cfg, b, grid, block, lds, s));
     case FMT_Q8:
-      return (int)(slot ? launch_byslot_t<FMT_Q8, GRP_SLOT>(cfg, a, grid, block, lds, s)
-                        : launch_byslot_t<FMT_Q8, GRP_TOKEN>(cfg, a, grid, block, lds, s));
+      return (int)(slot ? launch_byslot_t<FMT_Q8, GRP_SLOT>(cfg, b, grid, block, lds, s)
+                        : launch_byslot_t<FMT_Q8, GRP_TOKEN>(cfg, b, grid, block, lds, s));
   }
   return (int)hipErrorInvalidValue;
 }

@@ -16,9 +16,10 @@
 //     Each wave keeps STAGES groups of loads in flight ahead of its math.
 //   * Activations are read per lane as one contiguous 32 / 64-byte run of a
 //     row (L2 / L1 resident; rows beyond M are clamped, their results dropped).
-//     Dense 16-bit activations of a few rows may instead be copied once into
-//     LDS (AS = 1: the block's rows over its split's K range, while the first
-//     weight loads are in flight) and read from there: per group, four 64-lane
+//     Dense 16-bit activations of a few rows, and a routed slot's token row
+//     in slot mode, may instead be copied once into LDS (AS = 1: the block's
+//     rows over its split's K range, while the first weight loads are in
+//     flight) and read from there: per group, four 64-lane
 //     global loads of which only the lanes of rows below M carry data would
 //     otherwise take as much address-unit time as the weight loads.
 //   * Per group the 4-bit codes become MFMA operands with one mask (+ one
@@ -101,7 +102,8 @@ __device__ inline f4_t mfma16(u4_t a, u4_t b, f4_t c) {
 // the reduction buffer is a static LDS array sized for MAXT threads (a
 // run-time compiled module has no dynamic-LDS attribute to raise), not the
 // launch's dynamic LDS.  AS: the activation slab is staged in LDS behind the
-// reduction buffer (dense 16-bit activations, one row block; a_pitch > 0).
+// reduction buffer (16-bit activations, one row block, dense or slot mode;
+// a_pitch > 0).
 template <int FMT, int MB, int NB, int STAGES, int MAXT, int GRP, int MC = 0, int NC = 0, int KC = 0, int SL = 0,
           int AS = 0>
 __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
@@ -222,8 +224,11 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
   // Staged activations (AS): the block's rows over this split's groups sit in
   // LDS behind the reduction buffer, row r at r * a_pitch, group g at
   // (g - g_beg) * 256 bytes.
-  static_assert(!AS || (GRP == GRP_DENSE && FI::kAct16 && MB == 1 && !SL), "staged activations: dense, 16-bit, one row block");
-  [[maybe_unused]] const int blk_rows = min(16, M - m0);
+  static_assert(!AS || ((GRP == GRP_DENSE || GRP == GRP_SLOT) && FI::kAct16 && MB == 1 && !SL),
+                "staged activations: dense or slot mode, 16-bit, one row block");
+  // rows of the block (slot mode: the slot's token, operand row 0)
+  [[maybe_unused]] const int blk_rows = GRP == GRP_SLOT ? 1 : min(16, M - m0);
+  [[maybe_unused]] auto act_row = [&](int r) { return GRP == GRP_SLOT ? (int)blockIdx.z / p.topk : m0 + r; };
   extern __shared__ float red_dyn[];
   [[maybe_unused]] uint8_t* const a_lds =
       reinterpret_cast<uint8_t*>(red_dyn) + (size_t)W * (MB * NB * 4) * 64 * sizeof(float);
@@ -578,7 +583,7 @@ __global__ void __launch_bounds__(MAXT) qgemm_skinny(SkinnyArgs p) {
     for (int idx = wave; idx < blk_rows * nch; idx += W) {
       const int r = idx / nch, ch = idx - r * nch;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(a_lds + r * p.a_pitch + ch * 1024), 16,
-                                               (m0 + r) * a_rowb + 16 * lane, g_beg * 256 + ch * 1024, 0, 0);
+                                               act_row(r) * a_rowb + 16 * lane, g_beg * 256 + ch * 1024, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
