@@ -52,9 +52,6 @@ static int device_cus() {
   return cus > 0 ? cus : 256;
 }
 
-// Instantiated shapes: up to 8 waves per workgroup (256 VGPRs per lane) for
-// every (tile_m, tile_n, stages), and 16 waves (128 VGPRs per lane) for one
-// column block of up to 16 rows.
 // Vector-memory loads of weights and metadata per group and wave.
 constexpr int wm_loads(int fmt, int nb) {
   return nb * (1 + ((w8_weights(fmt) || w3_weights(fmt)) ? 1 : 0) + (e8m0_meta(fmt) ? 1 : 2));
@@ -74,6 +71,10 @@ static hipError_t launch_staged(const SkinnyArgs& a, dim3 grid, dim3 block, size
   return hipErrorInvalidValue;
 }
 
+// Instantiated shapes: up to 8 waves per workgroup (256 VGPRs per lane) for
+// every (tile_m, tile_n, stages), and 16 waves (128 VGPRs per lane) for one
+// column block of up to 16 rows; the staged-activation variants of the
+// one-row-block shapes with 2 or 4 stages.
 template <int FMT, int MB, int NB>
 static hipError_t launch_t(const SkinnyCfg& cfg, const SkinnyArgs& a, dim3 grid, dim3 block, size_t lds,
                            hipStream_t s) {
