@@ -758,13 +758,21 @@ class MoePlan(Plan):
 # path: measured on MI355X (256 experts, top 8, H = 7168, I = 256) it is the
 # faster one up to 32 slots and level with the aligned path at 64, where an
 # expert picked by several slots starts to be read once per slot.
+# routed slots up to which moe_layer takes the by-slot path: the measured
+# crossover on MI355X (256 experts, top 8, H = 7168, I = 256) lies between 64
+# and 256 slots for 16-bit activations (T = 8: 49.5 against 54.2 us aligned),
+# and between 32 and 64 for fp8 ones (T = 4: 32.0 against 36.5 us, T = 8:
+# 54.3 against 50.9 us)
 MOE_BY_SLOT_MAX_SLOTS = 64
+MOE_BY_SLOT_MAX_SLOTS_FP8 = 32
 
 
-def moe_uses_by_slot(t: int, topk: int) -> bool:
+def moe_uses_by_slot(t: int, topk: int, fp8: bool = False) -> bool:
     """Whether moe_layer runs a call of t tokens routed to topk experts each
-    through hq_moe_gemm_by_slot (else the aligned hq_moe_align + hq_moe_gemm)."""
-    return 0 < int(t) * int(topk) <= MOE_BY_SLOT_MAX_SLOTS
+    (fp8: W4A8-FP8 activations) through hq_moe_gemm_by_slot (else the aligned
+    hq_moe_align + hq_moe_gemm)."""
+    limit = MOE_BY_SLOT_MAX_SLOTS_FP8 if fp8 else MOE_BY_SLOT_MAX_SLOTS
+    return 0 < int(t) * int(topk) <= limit
 
 
 def moe_layer(gate_up: "MoePlan", down: "MoePlan", x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
@@ -780,7 +788,7 @@ def moe_layer(gate_up: "MoePlan", down: "MoePlan", x: torch.Tensor, topk_ids: to
         raise ValueError("moe_layer takes a gate_up plan (silu_mul / silu_mul_qfp8) and a topk_combine plan")
     fp8 = gate_up.epi == EPI_SILU_MUL_QFP8
     if by_slot is None:
-        by_slot = moe_uses_by_slot(t, topk)
+        by_slot = moe_uses_by_slot(t, topk, fp8)
     if by_slot:
         r = gate_up.moe_gemm_by_slot(x, t, topk, topk_ids, w1, m1, a_scale=x_scale)
         act, scl = r if fp8 else (r, None)
