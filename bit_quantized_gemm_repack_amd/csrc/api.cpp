@@ -308,10 +308,17 @@ Exec choose_exec(const hq_plan* p, int64_t m, const hq_tuning* up) {
     c.waves = (m <= 4 || !act16) ? 8 : 4;
     if (N / 16 >= 512 && N % 64 == 0) c.nb = 4;
     // one row of 16-bit INT4 activations (staged in LDS, so a wave's loads
-    // are its weights and metadata only) over long K: 16 waves per column
-    // block (N = 4096, K = 14336 on MI355X: 9.44-9.63 -> 9.11-9.24 us in
-    // three alternating runs on one host)
-    if (m == 1 && (p->fmt == FMT_W16F16 || p->fmt == FMT_W16BF16) && c.nb == 1 && G >= 64) c.waves = 16;
+    // are its weights and metadata only): 16 waves per column block over
+    // long K, and two column blocks of 4 waves on wide layers (three
+    // alternating runs on one MI355X host: N = 4096, K = 14336 9.44-9.63 ->
+    // 9.11-9.24 us; N = 14336, K = 4096 9.10-9.19 -> 8.78-8.94 us)
+    if (m == 1 && (p->fmt == FMT_W16F16 || p->fmt == FMT_W16BF16)) {
+      if (c.nb == 1 && G >= 64) c.waves = 16;
+      if (c.nb == 4 && N % 32 == 0) {
+        c.nb = 2;
+        c.waves = 4;
+      }
+    }
   } else {
     c.waves = 8;
   }
