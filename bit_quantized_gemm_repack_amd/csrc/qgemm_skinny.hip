@@ -173,7 +173,6 @@ static hipError_t launch_byslot_t(const SkinnyCfg& cfg, const SkinnyArgs& a, dim
   if constexpr (GRP == GRP_SLOT && act16_fmt(FMT)) {
     if (a.a_pitch > 0) {  // the slot's token row staged in LDS
       if (cfg.nb == 2) return launch_kernel(qgemm_skinny<FMT, 1, 2, 2, 1024, GRP, 0, 0, 0, 0, 1>, grid, block, lds, s, a);
-      if (cfg.nb == 4) return launch_kernel(qgemm_skinny<FMT, 1, 4, 2, 1024, GRP, 0, 0, 0, 0, 1>, grid, block, lds, s, a);
       return hipErrorInvalidValue;
     }
   }
@@ -195,12 +194,14 @@ int launch_skinny_byslot(int fmt, int mode, const SkinnyCfg& cfg, const SkinnyAr
   dim3 block(64 * cfg.waves);
   size_t lds = (size_t)cfg.waves * cfg.mb * cfg.nb * 4 * 64 * sizeof(float);
   const bool slot = mode == GRP_SLOT;
-  // slot mode, 16-bit activations: the slot's token row over all of K staged
-  // in LDS behind the reduction buffer (as the dense calls of a few rows),
-  // while it leaves room for the workgroups each CU has to hold
+  // slot mode, 16-bit activations, two column blocks (the gate and up block
+  // pair; with four, the staged form of the 1024-thread kernel spills): the
+  // slot's token row over all of K staged in LDS behind the reduction buffer
+  // (as the dense calls of a few rows), while it leaves room for the
+  // workgroups each CU has to hold
   SkinnyArgs b = a;
   b.a_pitch = 0;
-  if (slot && act16_fmt(fmt) && (cfg.nb == 2 || cfg.nb == 4)) {
+  if (slot && act16_fmt(fmt) && cfg.nb == 2) {
     const int64_t pitch = ((int64_t)a.G * 256 + 1023) / 1024 * 1024 + 16;
     static const int cus = device_cus();
     const int64_t per_cu = ((int64_t)ntiles * blocks + cus - 1) / cus;
