@@ -1256,10 +1256,12 @@ hq_status hq_moe_gemm_by_slot(const hq_plan* p, int64_t t, int topk, const void*
       if (paired && c.nb < 2) return fail(HQ_ERR_UNSUPPORTED, "gate_up needs n / 2 to be a multiple of 16");
       const int64_t steps = token ? topk * G : G;
       c.waves = (u.waves >= 1 && u.waves <= 16) ? u.waves : (int)std::min<int64_t>(8, steps);
-      // gate_up with 16-bit activations (token rows staged in LDS): 4 waves
-      // from 9 routed slots on (bf16, T = 4 / 8: 13.8 -> 13.5 and 24.2 ->
-      // 23.1 us; at T = 1, 8 waves: 8.0 against 9.7 us)
-      if (!token && !(u.waves >= 1 && u.waves <= 16) && hq::act16_fmt(p->fmt) && t * topk > 8) c.waves = 4;
+      // gate_up: 4 waves from 9 routed slots on (two alternating runs on one
+      // MI355X host, the whole layer by slot at T = 4 / 8: bf16 28.7-28.9 ->
+      // 28.5-28.6 and 50.0-50.3 -> 48.9-49.1 us, fp8 32.1-32.2 -> 31.4-31.6
+      // and 54.5-55.2 -> 53.0-53.2 us; at T = 1, 8 waves: gate_up 8.0
+      // against 9.7 us)
+      if (!token && !(u.waves >= 1 && u.waves <= 16) && t * topk > 8) c.waves = 4;
     }
     const uint32_t* zeros = p->layer.q.zp == HQ_ZP_PER_GROUP_U4
                                 ? reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(meta) +
