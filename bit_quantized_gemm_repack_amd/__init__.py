@@ -760,11 +760,10 @@ class MoePlan(Plan):
 # expert picked by several slots starts to be read once per slot.
 # routed slots up to which moe_layer takes the by-slot path: the measured
 # crossover on MI355X (256 experts, top 8, H = 7168, I = 256) lies between 64
-# and 256 slots for 16-bit activations (T = 8: 49.5 against 54.2 us aligned),
-# and between 32 and 64 for fp8 ones (T = 4: 32.0 against 36.5 us, T = 8:
-# 54.3 against 50.9 us)
+# and 256 slots for both activation types (T = 8: bf16 43.5 against 54.2 us
+# aligned, fp8 46.1 against 50.9 us; T = 32 by slot is the slower one)
 MOE_BY_SLOT_MAX_SLOTS = 64
-MOE_BY_SLOT_MAX_SLOTS_FP8 = 32
+MOE_BY_SLOT_MAX_SLOTS_FP8 = 64
 
 
 def moe_uses_by_slot(t: int, topk: int, fp8: bool = False) -> bool:

@@ -1262,6 +1262,14 @@ hq_status hq_moe_gemm_by_slot(const hq_plan* p, int64_t t, int topk, const void*
       // and 54.5-55.2 -> 53.0-53.2 us; at T = 1, 8 waves: gate_up 8.0
       // against 9.7 us)
       if (!token && !(u.waves >= 1 && u.waves <= 16) && t * topk > 8) c.waves = 4;
+      // down + combine: from 9 routed slots on, 4 column blocks of 4 waves
+      // (one host, T = 4 / 8: bf16 14.4 -> 13.5 and 24.5 -> 18.6 us, fp8 15.2
+      // -> 11.6 and 26.7 -> 18.0 us; at T = 1, 2 blocks of 8 waves: 5.9
+      // against 9.2 us)
+      if (token && t * topk > 8) {
+        if (!u.tile_n && N % 64 == 0) c.nb = 4;
+        if (!(u.waves >= 1 && u.waves <= 16)) c.waves = 4;
+      }
     }
     const uint32_t* zeros = p->layer.q.zp == HQ_ZP_PER_GROUP_U4
                                 ? reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(meta) +

@@ -469,7 +469,7 @@ def test_moe_layer_helper_matches_its_path(small_layer, T, topk, act):
     xs = None if act != "fp8" else x["x_scale"].to(DEV)
     y = hq.moe_layer(p1, p2, a, ids, tw, w1, m1, w2, m2, x_scale=xs)
     by_slot = hq.moe_uses_by_slot(T, topk, act == "fp8")
-    assert by_slot == (T * topk <= (32 if act == "fp8" else 64))
+    assert by_slot == (T * topk <= 64)
     if by_slot:
         res = p1.moe_gemm_by_slot(a, T, topk, ids, w1, m1, a_scale=xs)
         act_out, scl = res if act == "fp8" else (res, None)
