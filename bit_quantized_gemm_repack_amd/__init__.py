@@ -759,11 +759,11 @@ class MoePlan(Plan):
 # faster one up to 32 slots and level with the aligned path at 64, where an
 # expert picked by several slots starts to be read once per slot.
 # routed slots up to which moe_layer takes the by-slot path: the measured
-# crossover on MI355X (256 experts, top 8, H = 7168, I = 256) lies between 64
-# and 256 slots for both activation types (T = 8: bf16 43.5 against 54.2 us
-# aligned, fp8 46.1 against 50.9 us; T = 32 by slot is the slower one)
-MOE_BY_SLOT_MAX_SLOTS = 64
-MOE_BY_SLOT_MAX_SLOTS_FP8 = 64
+# crossover on MI355X (256 experts, top 8, H = 7168, I = 256, graph-timed
+# layers): bf16 by slot against aligned 60.7 / 71.0 us at T = 12 and 82.9 /
+# 85.4 us at T = 16; fp8 64.0 / 66.3 us at T = 12 and 78.0 / 76.3 us at T = 16
+MOE_BY_SLOT_MAX_SLOTS = 128
+MOE_BY_SLOT_MAX_SLOTS_FP8 = 96
 
 
 def moe_uses_by_slot(t: int, topk: int, fp8: bool = False) -> bool:

@@ -463,11 +463,11 @@ def test_moe_by_slot_call_validation():
 
 
 def test_moe_layer_path_choice():
-    """Host logic: moe_layer takes the by-slot path up to 64 routed slots, for
-    16-bit and fp8 activations alike."""
-    assert hq.moe_uses_by_slot(1, 8) and hq.moe_uses_by_slot(8, 8) and hq.moe_uses_by_slot(32, 2)
-    assert not hq.moe_uses_by_slot(9, 8) and not hq.moe_uses_by_slot(4096, 8) and not hq.moe_uses_by_slot(0, 8)
-    assert hq.moe_uses_by_slot(8, 8, fp8=True) and not hq.moe_uses_by_slot(9, 8, fp8=True)
+    """Host logic: moe_layer takes the by-slot path up to 128 routed slots (96
+    with fp8 activations)."""
+    assert hq.moe_uses_by_slot(1, 8) and hq.moe_uses_by_slot(16, 8) and hq.moe_uses_by_slot(64, 2)
+    assert not hq.moe_uses_by_slot(17, 8) and not hq.moe_uses_by_slot(4096, 8) and not hq.moe_uses_by_slot(0, 8)
+    assert hq.moe_uses_by_slot(12, 8, fp8=True) and not hq.moe_uses_by_slot(13, 8, fp8=True)
     q = hq.w4a16("bf16", scale="f16")
     g = hq.MoePlan(512, 7168, q, 256, 64, "silu_mul")
     d = hq.MoePlan(7168, 256, q, 256, 64, "topk_combine")
